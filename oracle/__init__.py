@@ -1,0 +1,150 @@
+"""Plain float64 CPU oracle for the block selected inverse (chain, star, tree).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product path never imports this
+package, and this package shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (scalar loops, no BLAS), which states the
+recurrences and the passages of the gabp-sparse-inv 0.3.2 project page they
+follow.  This module only marshals numpy arrays.  Inputs are float64; a float32
+run is checked by widening the float32 inputs it consumed.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+OK, INVALID_ARG, BAD_TREE = 0, 1, 2
+
+
+def compile_oracle(src: str, out: str) -> str:
+    """Compile an oracle source to a shared library (plain -O2, no fast-math)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                           "-fno-fast-math", "-o", tmp, src, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(_LIB):
+        compile_oracle(SOURCE, _LIB)
+    return _LIB
+
+
+def load(path: str | None = None):
+    """Load the oracle library (or a variant of it at `path`)."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    if path is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        path = _LIB
+    lib = ctypes.CDLL(os.path.abspath(path))
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    lib.oracle_chain.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, vp]
+    lib.oracle_star.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_tree.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_tree_depths.argtypes = [i64, vp, vp]
+    for f in (lib.oracle_chain, lib.oracle_star, lib.oracle_tree, lib.oracle_tree_depths):
+        f.restype = ctypes.c_int
+    if path == _LIB:
+        _lib = lib
+    return lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data if a.size else None
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def chain(diag, lower, lib=None):
+    """Selected inverse of block-tridiagonal chains.
+
+    diag [B,L,b,b], lower [B,L-1,b,b] with lower[i] = A_{i+1,i}.
+    Returns (G_diag [B,L,b,b], G_lower [B,L-1,b,b], logdet [B], info [B]).
+    """
+    lib = lib or load()
+    diag, lower = _f64(diag), _f64(lower)
+    B, L, b = diag.shape[0], diag.shape[1], diag.shape[2]
+    assert lower.shape == (B, L - 1, b, b)
+    Gd = np.empty_like(diag)
+    Gl = np.empty_like(lower)
+    ld = np.empty(B)
+    info = np.empty(B, np.int32)
+    rc = lib.oracle_chain(B, L, b, _p(diag), _p(lower), _p(Gd), _p(Gl), _p(ld), _p(info))
+    if rc:
+        raise OracleError("oracle_chain status %d" % rc)
+    return Gd, Gl, ld, info
+
+
+def star(center, leaves, coupling, lib=None):
+    """Selected inverse of block-arrowhead matrices.
+
+    center [B,b,b], leaves [B,K,b,b], coupling [B,K,b,b] with
+    coupling[j] = A_{j,0}.  Returns (G_center, G_leaf, G_cross, logdet, info)
+    with G_cross[j] = (A^-1)_{j,0}.
+    """
+    lib = lib or load()
+    center, leaves, coupling = _f64(center), _f64(leaves), _f64(coupling)
+    B, K, b = leaves.shape[0], leaves.shape[1], leaves.shape[2]
+    assert center.shape == (B, b, b) and coupling.shape == leaves.shape
+    Gc = np.empty_like(center)
+    Gl = np.empty_like(leaves)
+    Gx = np.empty_like(coupling)
+    ld = np.empty(B)
+    info = np.empty(B, np.int32)
+    rc = lib.oracle_star(B, K, b, _p(center), _p(leaves), _p(coupling), _p(Gc), _p(Gl),
+                         _p(Gx), _p(ld), _p(info))
+    if rc:
+        raise OracleError("oracle_star status %d" % rc)
+    return Gc, Gl, Gx, ld, info
+
+
+def tree(parent, diag, edge, lib=None):
+    """Selected inverse of a tree-structured SPD matrix.
+
+    parent [n] (root = -1), diag [n,b,b], edge [n,b,b] with
+    edge[v] = A_{parent(v),v}.  Returns (G_diag, G_edge, logdet, info) with
+    G_edge[v] = (A^-1)_{parent(v),v} and a zero root slot.
+    """
+    lib = lib or load()
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    diag, edge = _f64(diag), _f64(edge)
+    n, b = diag.shape[0], diag.shape[1]
+    assert parent.shape == (n,) and edge.shape == diag.shape
+    Gd = np.empty_like(diag)
+    Ge = np.empty_like(edge)
+    ld = np.empty(1)
+    info = np.empty(1, np.int32)
+    rc = lib.oracle_tree(n, b, _p(parent), _p(diag), _p(edge), _p(Gd), _p(Ge), _p(ld),
+                         _p(info))
+    if rc:
+        raise OracleError("oracle_tree status %d" % rc)
+    return Gd, Ge, float(ld[0]), int(info[0])
+
+
+def tree_depths(parent, lib=None):
+    lib = lib or load()
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    d = np.empty(parent.shape[0], np.int32)
+    rc = lib.oracle_tree_depths(parent.shape[0], _p(parent), _p(d))
+    if rc:
+        raise OracleError("invalid tree (status %d)" % rc)
+    return d

@@ -1,0 +1,424 @@
+/*
+ * oracle.c -- plain, slow float64 reference for the selected inverse of
+ * block-structured SPD matrices whose block graph is a tree (chain = path,
+ * star = depth 1, general rooted tree).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this code; the product path never
+ * calls it and shares no code with it.
+ *
+ * What is computed (gabp-sparse-inv 0.3.2 project page, opening paragraphs
+ * and section "Implemented and tested kernels"): only the blocks of A^-1 on
+ * A's own block pattern -- every diagonal block and every pattern edge --
+ * plus log det A, without forming the dense inverse.  On a tree the method is
+ * a two-pass schedule: a collect pass (leaves -> root) that is a block LDL^T /
+ * Cholesky elimination, and a distribute pass (root -> leaves) that is the
+ * Takahashi back-recursion; the page states the two views agree.  The log
+ * determinant comes from the same factorization (same page, "Statement of
+ * need" and the tree_logdet / junction_logdet passage in the junction-tree
+ * section).
+ *
+ * Notation.  For a non-root node v with parent p:
+ *     E_v = A_{p,v}                     (the off-diagonal block)
+ *     S_v = D_v - sum_{children c} E_c S_c^{-1} E_c^T      (Schur pivot)
+ *     R_v = chol(S_v),  S_v = R_v R_v^T, R_v lower triangular
+ *     X_v = E_v S_v^{-1}
+ * collect:    S_p -= E_v S_v^{-1} E_v^T  (= Y^T Y with Y = R_v^{-1} E_v^T)
+ * root:       G_rr = S_r^{-1}
+ * distribute: G_{p,v} = -G_pp X_v
+ *             G_vv    = S_v^{-1} - X_v^T G_{p,v}
+ * log det A = sum_v 2 sum_k ln (R_v)_kk.
+ *
+ * Layouts (Quickstart section of the same page): blocks are b x b,
+ * row-major, contiguous.
+ *   chain: diag[B][L], lower[B][L-1] with lower[i] = A_{i+1,i};
+ *          G_diag[i] = (A^-1)_{ii}, G_lower[i] = (A^-1)_{i+1,i}.
+ *          The chain is the path rooted at its last block.
+ *   star:  center[B], leaves[B][K], coupling[B][K] with coupling[j] = A_{j,0}
+ *          (centre = block 0, leaf j = block j+1);
+ *          G_center = (A^-1)_00, G_leaf[j] = (A^-1)_jj, G_cross[j] = (A^-1)_{j,0}.
+ *   tree:  parent[n] (root = -1), diag[n], edge[n] with edge[v] = A_{parent(v),v};
+ *          G_diag[v] = (A^-1)_vv, G_edge[v] = (A^-1)_{parent(v),v}, root slot 0.
+ * Only the lower triangle of each diagonal input block is read.
+ *
+ * Failure: if a Schur pivot is not positive definite (Cholesky finds a
+ * diagonal that is not > 0, NaN included), info = 1 + that block's index in
+ * the caller's numbering (chain: block i -> i+1; star: centre -> 1, leaf j ->
+ * j+2; tree: node v -> v+1), the matrix's outputs are filled with NaN and its
+ * logdet is NaN.  This mirrors the "not positive definite -> error"
+ * convention of the sparsax page (Features list).
+ *
+ * Plain C, scalar loops, no BLAS; OpenMP only across independent matrices.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_API __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------ primitives */
+
+/* Cholesky S = R R^T of a symmetric block, reading the lower triangle of S.
+ * R is lower triangular with zeros above the diagonal.  Returns 0 on
+ * success, 1 if a pivot is not > 0 (NaN included). */
+static int chol(int b, const double *S, double *R) {
+  memset(R, 0, sizeof(double) * (size_t)b * b);
+  for (int j = 0; j < b; ++j) {
+    double d = S[j * b + j];
+    for (int k = 0; k < j; ++k) d -= R[j * b + k] * R[j * b + k];
+    if (!(d > 0.0)) return 1;
+    const double rjj = sqrt(d);
+    R[j * b + j] = rjj;
+    for (int i = j + 1; i < b; ++i) {
+      double s = S[i * b + j];
+      for (int k = 0; k < j; ++k) s -= R[i * b + k] * R[j * b + k];
+      R[i * b + j] = s / rjj;
+    }
+  }
+  return 0;
+}
+
+/* Solve R Y = Bm (R lower triangular) by forward substitution, column by
+ * column.  Bm, Y are b x b. */
+static void trsm_L(int b, const double *R, const double *Bm, double *Y) {
+  for (int c = 0; c < b; ++c)
+    for (int i = 0; i < b; ++i) {
+      double s = Bm[i * b + c];
+      for (int k = 0; k < i; ++k) s -= R[i * b + k] * Y[k * b + c];
+      Y[i * b + c] = s / R[i * b + i];
+    }
+}
+
+/* Solve R^T Y = Bm (R lower triangular) by back substitution. */
+static void trsm_LT(int b, const double *R, const double *Bm, double *Y) {
+  for (int c = 0; c < b; ++c)
+    for (int i = b - 1; i >= 0; --i) {
+      double s = Bm[i * b + c];
+      for (int k = i + 1; k < b; ++k) s -= R[k * b + i] * Y[k * b + c];
+      Y[i * b + c] = s / R[i * b + i];
+    }
+}
+
+/* S^{-1} = R^{-T} R^{-1}: W = R^{-1} by forward substitution on the identity,
+ * then the full product W^T W, deliberately NOT symmetrised. */
+static void inv_from_chol(int b, const double *R, double *Sinv) {
+  double *I = (double *)calloc((size_t)b * b, sizeof(double));
+  double *W = (double *)malloc(sizeof(double) * (size_t)b * b);
+  for (int i = 0; i < b; ++i) I[i * b + i] = 1.0;
+  trsm_L(b, R, I, W);
+  for (int r = 0; r < b; ++r)
+    for (int c = 0; c < b; ++c) {
+      double s = 0.0;
+      for (int k = 0; k < b; ++k) s += W[k * b + r] * W[k * b + c];
+      Sinv[r * b + c] = s;
+    }
+  free(I);
+  free(W);
+}
+
+/* ln det S = 2 sum_k ln R_kk */
+static double logdet_chol(int b, const double *R) {
+  double s = 0.0;
+  for (int k = 0; k < b; ++k) s += log(R[k * b + k]);
+  return 2.0 * s;
+}
+
+static void transpose(int b, const double *Bm, double *T) {
+  for (int r = 0; r < b; ++r)
+    for (int c = 0; c < b; ++c) T[c * b + r] = Bm[r * b + c];
+}
+
+/* Out = P Q */
+static void matmul(int b, const double *P, const double *Q, double *Out) {
+  for (int r = 0; r < b; ++r)
+    for (int c = 0; c < b; ++c) {
+      double s = 0.0;
+      for (int k = 0; k < b; ++k) s += P[r * b + k] * Q[k * b + c];
+      Out[r * b + c] = s;
+    }
+}
+
+/* Out = P^T Q */
+static void matmul_tn(int b, const double *P, const double *Q, double *Out) {
+  for (int r = 0; r < b; ++r)
+    for (int c = 0; c < b; ++c) {
+      double s = 0.0;
+      for (int k = 0; k < b; ++k) s += P[k * b + r] * Q[k * b + c];
+      Out[r * b + c] = s;
+    }
+}
+
+static void fill_nan(double *p, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) p[i] = NAN;
+}
+
+/* One collect step for a non-root node: from R_v (chol of S_v) and the edge
+ * block E = A_{p,v}, subtract E S_v^{-1} E^T from the parent's pivot S_p and
+ * return X_v = E S_v^{-1}.  Work arrays: Et, Y, Z (b x b each). */
+static void collect_edge(int b, const double *R, const double *E, double *Sp, double *X,
+                         double *Et, double *Y, double *Z) {
+  transpose(b, E, Et);    /* E^T                      */
+  trsm_L(b, R, Et, Y);    /* Y = R^{-1} E^T           */
+  for (int r = 0; r < b; ++r)
+    for (int c = 0; c < b; ++c) {
+      double s = 0.0;
+      for (int k = 0; k < b; ++k) s += Y[k * b + r] * Y[k * b + c];
+      Sp[r * b + c] -= s; /* S_p -= Y^T Y = E S^{-1} E^T */
+    }
+  trsm_LT(b, R, Y, Z);    /* Z = S^{-1} E^T           */
+  transpose(b, Z, X);     /* X = E S^{-1}             */
+}
+
+/* One distribute step: G_{p,v} = -G_pp X_v ; G_vv = S_v^{-1} - X_v^T G_{p,v}. */
+static void distribute_edge(int b, const double *Gpp, const double *X, const double *R,
+                            double *Gpv, double *Gvv, double *Sinv, double *T) {
+  matmul(b, Gpp, X, Gpv);
+  for (int64_t e = 0; e < (int64_t)b * b; ++e) Gpv[e] = -Gpv[e];
+  inv_from_chol(b, R, Sinv);
+  matmul_tn(b, X, Gpv, T);
+  for (int64_t e = 0; e < (int64_t)b * b; ++e) Gvv[e] = Sinv[e] - T[e];
+}
+
+/* ----------------------------------------------------------------- chain */
+
+/* Block-tridiagonal chain (item "Chain" of "Implemented and tested kernels":
+ * block LDL^T factorisation plus Takahashi back-recursion; the chain is the
+ * path tree rooted at its last block, per the root-invariance remark of the
+ * Quickstart section).  Batch loop over B independent matrices. */
+ORACLE_API int oracle_chain(int64_t B, int64_t L, int b, const double *diag,
+                            const double *lower, double *G_diag, double *G_lower,
+                            double *logdet, int32_t *info) {
+  if (B < 0 || L < 1 || b < 1 || !diag || !G_diag || !logdet || !info) return 1;
+  if (L > 1 && (!lower || !G_lower)) return 1;
+  const int64_t bb = (int64_t)b * b;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t m = 0; m < B; ++m) {
+    const double *D = diag + m * L * bb;
+    const double *C = lower + m * (L - 1) * bb;
+    double *Gd = G_diag + m * L * bb;
+    double *Gl = G_lower + m * (L - 1) * bb;
+    double *R = (double *)malloc(sizeof(double) * L * bb); /* R_i, i < L   */
+    double *X = (double *)malloc(sizeof(double) * L * bb); /* X_i, i < L-1 */
+    double *S = (double *)malloc(sizeof(double) * bb);
+    double *w = (double *)malloc(sizeof(double) * 4 * bb);
+    double ld = 0.0;
+    int32_t fail = 0;
+    memcpy(S, D, sizeof(double) * bb); /* S_0 = D_0 */
+    for (int64_t i = 0; i < L; ++i) {
+      if (chol(b, S, R + i * bb)) {
+        fail = (int32_t)(i + 1);
+        break;
+      }
+      ld += logdet_chol(b, R + i * bb);
+      if (i == L - 1) break;
+      /* next pivot starts from D_{i+1}; parent of i is i+1, E_i = lower[i] */
+      memcpy(S, D + (i + 1) * bb, sizeof(double) * bb);
+      collect_edge(b, R + i * bb, C + i * bb, S, X + i * bb, w, w + bb, w + 2 * bb);
+    }
+    if (fail) {
+      info[m] = fail;
+      logdet[m] = NAN;
+      fill_nan(Gd, L * bb);
+      if (L > 1) fill_nan(Gl, (L - 1) * bb);
+    } else {
+      info[m] = 0;
+      logdet[m] = ld;
+      inv_from_chol(b, R + (L - 1) * bb, Gd + (L - 1) * bb); /* root closure */
+      for (int64_t i = L - 2; i >= 0; --i)
+        distribute_edge(b, Gd + (i + 1) * bb, X + i * bb, R + i * bb, Gl + i * bb,
+                        Gd + i * bb, w, w + bb);
+    }
+    free(R);
+    free(X);
+    free(S);
+    free(w);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ star */
+
+/* Block arrowhead (item "Star": one centre coupled to K leaves with no
+ * leaf-leaf coupling, leaves eliminated first).  The centre is the parent of
+ * every leaf, so E_j = A_{0,j} = coupling[j]^T.  Leaves are eliminated in
+ * index order. */
+ORACLE_API int oracle_star(int64_t B, int64_t K, int b, const double *center,
+                           const double *leaves, const double *coupling, double *G_center,
+                           double *G_leaf, double *G_cross, double *logdet, int32_t *info) {
+  if (B < 0 || K < 0 || b < 1 || !center || !G_center || !logdet || !info) return 1;
+  if (K > 0 && (!leaves || !coupling || !G_leaf || !G_cross)) return 1;
+  const int64_t bb = (int64_t)b * b;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t m = 0; m < B; ++m) {
+    const double *Dl = leaves + m * K * bb;
+    const double *F = coupling + m * K * bb;
+    double *Gc = G_center + m * bb;
+    double *Gl = G_leaf + m * K * bb;
+    double *Gx = G_cross + m * K * bb;
+    double *R = (double *)malloc(sizeof(double) * (K + 1) * bb); /* leaves, then centre */
+    double *X = (double *)malloc(sizeof(double) * (K > 0 ? K : 1) * bb);
+    double *S0 = (double *)malloc(sizeof(double) * bb);
+    double *w = (double *)malloc(sizeof(double) * 5 * bb);
+    double ld = 0.0;
+    int32_t fail = 0;
+    memcpy(S0, center + m * bb, sizeof(double) * bb);
+    for (int64_t j = 0; j < K; ++j) {
+      if (chol(b, Dl + j * bb, R + j * bb)) { /* a leaf has no children: S_j = D_j */
+        fail = (int32_t)(j + 2);
+        break;
+      }
+      ld += logdet_chol(b, R + j * bb);
+      transpose(b, F + j * bb, w + 3 * bb); /* E_j = A_{0,j} = coupling[j]^T */
+      collect_edge(b, R + j * bb, w + 3 * bb, S0, X + j * bb, w, w + bb, w + 2 * bb);
+    }
+    if (!fail && chol(b, S0, R + K * bb)) fail = 1;
+    if (fail) {
+      info[m] = fail;
+      logdet[m] = NAN;
+      fill_nan(Gc, bb);
+      if (K > 0) {
+        fill_nan(Gl, K * bb);
+        fill_nan(Gx, K * bb);
+      }
+    } else {
+      info[m] = 0;
+      ld += logdet_chol(b, R + K * bb);
+      logdet[m] = ld;
+      inv_from_chol(b, R + K * bb, Gc);
+      for (int64_t j = 0; j < K; ++j) {
+        /* w+3bb receives G_{0,j}; the output wants G_{j,0} = G_{0,j}^T */
+        distribute_edge(b, Gc, X + j * bb, R + j * bb, w + 3 * bb, Gl + j * bb, w, w + bb);
+        transpose(b, w + 3 * bb, Gx + j * bb);
+      }
+    }
+    free(R);
+    free(X);
+    free(S0);
+    free(w);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ tree */
+
+/* Validate a parent array and compute depths.  Returns 0 and fills depth[] and
+ * *root on success; 2 if the array is not a single rooted tree (not exactly
+ * one root, an index out of range, or a cycle). */
+static int tree_depths(int64_t n, const int32_t *parent, int32_t *depth, int64_t *root) {
+  int64_t r = -1;
+  for (int64_t v = 0; v < n; ++v) {
+    const int32_t p = parent[v];
+    if (p == -1) {
+      if (r >= 0) return 2;
+      r = v;
+    } else if (p < 0 || p >= n || p == v) {
+      return 2;
+    }
+  }
+  if (r < 0) return 2;
+  for (int64_t v = 0; v < n; ++v) depth[v] = -1;
+  depth[r] = 0;
+  int64_t *stack = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n + 1));
+  for (int64_t v = 0; v < n; ++v) {
+    /* walk up until a node of known depth; more than n steps means a cycle */
+    int64_t top = 0, u = v;
+    while (depth[u] < 0) {
+      if (top > n) {
+        free(stack);
+        return 2;
+      }
+      stack[top++] = u;
+      u = parent[u];
+    }
+    int32_t d = depth[u];
+    while (top > 0) depth[stack[--top]] = ++d;
+  }
+  free(stack);
+  *root = r;
+  return 0;
+}
+
+/* Arbitrary rooted tree (item "Tree": a parent array and one edge block per
+ * non-root node; collect leaves -> root, then distribute root -> leaves).
+ * Collect visits depths from the deepest up to 0, nodes of one depth in
+ * increasing index (so a parent's children, which share a depth, are
+ * subtracted in increasing index); distribute visits depths 1, 2, ... */
+ORACLE_API int oracle_tree(int64_t n, int b, const int32_t *parent, const double *diag,
+                           const double *edge, double *G_diag, double *G_edge, double *logdet,
+                           int32_t *info) {
+  if (n < 1 || b < 1 || !parent || !diag || !edge || !G_diag || !G_edge || !logdet || !info)
+    return 1;
+  const int64_t bb = (int64_t)b * b;
+  int32_t *depth = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+  int64_t root = -1;
+  if (tree_depths(n, parent, depth, &root)) {
+    free(depth);
+    return 2;
+  }
+  int32_t H = 0;
+  for (int64_t v = 0; v < n; ++v)
+    if (depth[v] > H) H = depth[v];
+  /* nodes bucketed by depth, increasing index within a depth */
+  int64_t *cnt = (int64_t *)calloc((size_t)H + 2, sizeof(int64_t));
+  for (int64_t v = 0; v < n; ++v) cnt[depth[v] + 1]++;
+  for (int32_t d = 0; d <= H; ++d) cnt[d + 1] += cnt[d];
+  int64_t *order = (int64_t *)malloc(sizeof(int64_t) * (size_t)n);
+  int64_t *fillp = (int64_t *)malloc(sizeof(int64_t) * ((size_t)H + 1));
+  for (int32_t d = 0; d <= H; ++d) fillp[d] = cnt[d];
+  for (int64_t v = 0; v < n; ++v) order[fillp[depth[v]]++] = v;
+
+  double *S = (double *)malloc(sizeof(double) * n * bb);
+  double *R = (double *)malloc(sizeof(double) * n * bb);
+  double *X = (double *)malloc(sizeof(double) * n * bb);
+  double *w = (double *)malloc(sizeof(double) * 4 * bb);
+  memcpy(S, diag, sizeof(double) * n * bb); /* S_v starts at D_v */
+  double ld = 0.0;
+  int32_t fail = 0;
+  for (int32_t d = H; d >= 0 && !fail; --d)
+    for (int64_t k = cnt[d]; k < cnt[d + 1]; ++k) {
+      const int64_t v = order[k];
+      if (chol(b, S + v * bb, R + v * bb)) {
+        fail = (int32_t)(v + 1);
+        break;
+      }
+      ld += logdet_chol(b, R + v * bb);
+      if (v != root)
+        collect_edge(b, R + v * bb, edge + v * bb, S + (int64_t)parent[v] * bb, X + v * bb,
+                     w, w + bb, w + 2 * bb);
+    }
+  if (fail) {
+    *info = fail;
+    *logdet = NAN;
+    fill_nan(G_diag, n * bb);
+    fill_nan(G_edge, n * bb);
+  } else {
+    *info = 0;
+    *logdet = ld;
+    inv_from_chol(b, R + root * bb, G_diag + root * bb);
+    for (int32_t d = 1; d <= H; ++d)
+      for (int64_t k = cnt[d]; k < cnt[d + 1]; ++k) {
+        const int64_t v = order[k];
+        distribute_edge(b, G_diag + (int64_t)parent[v] * bb, X + v * bb, R + v * bb,
+                        G_edge + v * bb, G_diag + v * bb, w, w + bb);
+      }
+    memset(G_edge + root * bb, 0, sizeof(double) * bb);
+  }
+  free(depth);
+  free(cnt);
+  free(order);
+  free(fillp);
+  free(S);
+  free(R);
+  free(X);
+  free(w);
+  return 0;
+}
+
+/* Depth of every node of a valid tree (host helper for the tests); returns 0,
+ * or 2 for an invalid parent array. */
+ORACLE_API int oracle_tree_depths(int64_t n, const int32_t *parent, int32_t *depth) {
+  int64_t root;
+  if (n < 1 || !parent || !depth) return 1;
+  return tree_depths(n, parent, depth, &root);
+}

@@ -1,0 +1,193 @@
+"""Seeded synthetic SPD block inputs (chain, star, tree) shared by the oracle
+tests and the GPU path.
+
+Input construction only: nothing here computes any part of the selected
+inverse.  Values come from a counter-based generator (Philox4x32-10, Salmon et
+al., SC 2011) so any single matrix of a batch can be regenerated on its own;
+``spdgen.c`` states the recipe.  The workload shapes follow the batched
+generators of the gabp-sparse-inv 0.3.2 project page (Quickstart section:
+``random_spd_chain`` / ``random_spd_star`` / ``random_spd_tree``), with
+explicit Gershgorin diagonal loads so that lambda_min(A) >= diag_load.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "spdgen.c")
+_LIB = os.path.join(_HERE, "libspdgen.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``libspdgen.so`` in place with gcc (OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        u64, i64, i32, dbl = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        vp = ctypes.c_void_p
+        lib.spdgen_chain.argtypes = [u64, i64, i64, i64, i32, dbl, vp, vp]
+        lib.spdgen_star.argtypes = [u64, i64, i64, i64, i32, dbl, vp, vp, vp]
+        lib.spdgen_random_recursive_tree.argtypes = [u64, i64, vp]
+        lib.spdgen_tree.argtypes = [u64, i64, i32, dbl, vp, vp, vp]
+        lib.spdgen_normal.argtypes = [u64, ctypes.c_uint32, u64, u64]
+        lib.spdgen_normal.restype = dbl
+        lib.spdgen_philox4x32_10.argtypes = [vp, vp, vp]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def philox4x32_10(ctr, key):
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, np.uint32)
+    _load().spdgen_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def normal(seed: int, stream: int, mat: int, e: int) -> float:
+    return _load().spdgen_normal(seed, stream, mat, e)
+
+
+def chain(B: int, L: int, b: int, seed: int = 0, diag_load: float = 2.0, m0: int = 0,
+          out=None):
+    """Block-tridiagonal SPD chains [m0, m0+B) of a seeded batch.
+
+    Returns ``diag [B,L,b,b]`` and ``lower [B,L-1,b,b]`` (float64) with
+    ``lower[i] = A_{i+1,i}``.
+    """
+    if out is None:
+        diag = np.empty((B, L, b, b), np.float64)
+        lower = np.empty((B, max(L - 1, 0), b, b), np.float64)
+    else:
+        diag, lower = out
+    _load().spdgen_chain(seed, m0, B, L, b, diag_load, _ptr(diag), _ptr(lower))
+    return diag, lower
+
+
+def star(B: int, K: int, b: int, seed: int = 0, diag_load: float = 2.0, m0: int = 0):
+    """Block-arrowhead SPD matrices [m0, m0+B).
+
+    Returns ``center [B,b,b]``, ``leaves [B,K,b,b]`` and ``coupling [B,K,b,b]``
+    with ``coupling[j] = A_{j,0}`` (leaf row, centre column).
+    """
+    center = np.empty((B, b, b), np.float64)
+    leaves = np.empty((B, K, b, b), np.float64)
+    coupling = np.empty((B, K, b, b), np.float64)
+    _load().spdgen_star(seed, m0, B, K, b, diag_load, _ptr(center), _ptr(leaves),
+                        _ptr(coupling))
+    return center, leaves, coupling
+
+
+def random_recursive_tree(n: int, seed: int = 1) -> np.ndarray:
+    """parent[0] = -1, parent[v] uniform over [0, v)."""
+    parent = np.empty(n, np.int32)
+    _load().spdgen_random_recursive_tree(seed, n, _ptr(parent))
+    return parent
+
+
+def path_tree(n: int) -> np.ndarray:
+    """Path rooted at node 0: parent[v] = v - 1."""
+    return np.arange(-1, n - 1, dtype=np.int32)
+
+
+def star_tree(n: int) -> np.ndarray:
+    """Depth-1 tree: node 0 is the root, every other node its child."""
+    p = np.zeros(n, np.int32)
+    p[0] = -1
+    return p
+
+
+def balanced_tree(n: int, arity: int = 2) -> np.ndarray:
+    """Complete `arity`-ary tree in heap order."""
+    p = (np.arange(n, dtype=np.int64) - 1) // arity
+    p[0] = -1
+    return p.astype(np.int32)
+
+
+def tree(parent: np.ndarray, b: int, seed: int = 1, diag_load: float = 2.0):
+    """Tree-structured SPD values for ``parent`` (one matrix).
+
+    Returns ``diag [n,b,b]`` and ``edge [n,b,b]`` with
+    ``edge[v] = A_{parent(v),v}`` and a zero root slot.
+    """
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    n = parent.shape[0]
+    diag = np.empty((n, b, b), np.float64)
+    edge = np.empty((n, b, b), np.float64)
+    _load().spdgen_tree(seed, n, b, diag_load, _ptr(parent), _ptr(diag), _ptr(edge))
+    return diag, edge
+
+
+# --------------------------------------------------------------- workloads
+# The five synthetic workloads the hot path is measured and checked on.
+WORKLOADS = {
+    "chain_b4_single": dict(kind="chain", B=1, L=8, b=4, seed=0, diag_load=2.0,
+                            dtypes=("f64",)),
+    "chain_b16_batched": dict(kind="chain", B=4096, L=64, b=16, seed=0, diag_load=2.0,
+                              dtypes=("f64", "f32")),
+    "chain_b32_long": dict(kind="chain", B=64, L=16384, b=32, seed=0, diag_load=1.0,
+                           dtypes=("f64",)),
+    "star_b32": dict(kind="star", B=256, K=1024, b=32, seed=0, diag_load=2.0,
+                     dtypes=("f64",)),
+    "tree_b8_random": dict(kind="tree", n=262144, b=8, seed=1, diag_load=2.0,
+                           dtypes=("f64", "f32")),
+}
+
+
+def to_dense_chain(diag: np.ndarray, lower: np.ndarray) -> np.ndarray:
+    """Assemble one chain (diag [L,b,b], lower [L-1,b,b]) as a dense matrix."""
+    L, b = diag.shape[0], diag.shape[1]
+    A = np.zeros((L * b, L * b))
+    for i in range(L):
+        A[i * b:(i + 1) * b, i * b:(i + 1) * b] = diag[i]
+    for i in range(L - 1):
+        A[(i + 1) * b:(i + 2) * b, i * b:(i + 1) * b] = lower[i]
+        A[i * b:(i + 1) * b, (i + 1) * b:(i + 2) * b] = lower[i].T
+    return A
+
+
+def to_dense_star(center: np.ndarray, leaves: np.ndarray, coupling: np.ndarray) -> np.ndarray:
+    """Assemble one star; the centre is block 0 and leaf j is block j+1."""
+    K, b = leaves.shape[0], leaves.shape[1]
+    A = np.zeros(((K + 1) * b, (K + 1) * b))
+    A[:b, :b] = center
+    for j in range(K):
+        s = (j + 1) * b
+        A[s:s + b, s:s + b] = leaves[j]
+        A[s:s + b, :b] = coupling[j]
+        A[:b, s:s + b] = coupling[j].T
+    return A
+
+
+def to_dense_tree(parent: np.ndarray, diag: np.ndarray, edge: np.ndarray) -> np.ndarray:
+    """Assemble one tree matrix; node v is block v."""
+    n, b = diag.shape[0], diag.shape[1]
+    A = np.zeros((n * b, n * b))
+    for v in range(n):
+        A[v * b:(v + 1) * b, v * b:(v + 1) * b] = diag[v]
+        p = int(parent[v])
+        if p >= 0:
+            A[p * b:(p + 1) * b, v * b:(v + 1) * b] = edge[v]
+            A[v * b:(v + 1) * b, p * b:(p + 1) * b] = edge[v].T
+    return A
