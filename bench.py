@@ -1,0 +1,216 @@
+"""Benchmark of the selected inverse on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dtype f64|f32]
+
+One step = one call of the C ABI over one batch of synthetic input already
+resident in HBM (all collect, root and distribute work of every matrix).
+Default workload: 4096 block-tridiagonal chains of 64 blocks of 16 (float64;
+the float32 run is reported alongside).  Prints ONE JSON line.
+
+Metric: nominal selected-inverse GFLOP/s (7 b^3 per non-root block, b^3 per
+root, never the executed count) and block-rows/s; roofline fraction of the
+dominant kernel against MI355X HBM bandwidth (8 TB/s) on compulsory bytes
+(every input block read once, every output block written once).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP64_PEAK_TFLOPS = 78.6
+FP32_PEAK_TFLOPS = 157.3
+
+
+def nominal_flops(kind, cfg):
+    b = cfg["b"]
+    if kind == "chain":
+        return cfg["B"] * (7 * b ** 3 * (cfg["L"] - 1) + b ** 3)
+    if kind == "star":
+        return cfg["B"] * (7 * b ** 3 * cfg["K"] + b ** 3)
+    return 7 * b ** 3 * (cfg["n"] - 1) + b ** 3
+
+
+def compulsory_bytes(kind, cfg, w):
+    """Input blocks read once + output blocks written once + logdet (f64) +
+    info (int32) (+ parent indices for the tree)."""
+    b2 = cfg["b"] ** 2
+    if kind == "chain":
+        return cfg["B"] * ((4 * cfg["L"] - 2) * b2 * w + 8 + 4)
+    if kind == "star":
+        return cfg["B"] * ((4 * cfg["K"] + 2) * b2 * w + 8 + 4)
+    return (4 * cfg["n"] - 1) * b2 * w + 4 * cfg["n"] + 8 + 4
+
+
+def block_rows(kind, cfg):
+    if kind == "chain":
+        return cfg["B"] * cfg["L"]
+    if kind == "star":
+        return cfg["B"] * (cfg["K"] + 1)
+    return cfg["n"]
+
+
+def make_inputs(kind, cfg, dt, dev):
+    import numpy as np
+    import torch
+    import spdgen
+    if kind == "chain":
+        d, l = spdgen.chain(cfg["B"], cfg["L"], cfg["b"], seed=cfg["seed"],
+                            diag_load=cfg["diag_load"])
+        return [torch.from_numpy(x).to(dev).to(dt) for x in (d, l)], None
+    if kind == "star":
+        arrs = spdgen.star(cfg["B"], cfg["K"], cfg["b"], seed=cfg["seed"],
+                           diag_load=cfg["diag_load"])
+        return [torch.from_numpy(x).to(dev).to(dt) for x in arrs], None
+    parent = spdgen.random_recursive_tree(cfg["n"], cfg["seed"])
+    d, e = spdgen.tree(parent, cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
+    return [torch.from_numpy(x).to(dev).to(dt) for x in (d, e)], np.asarray(parent)
+
+
+def run_gpu(kind, cfg, dtname, steps, warmup):
+    import torch
+    import sparse_spd_selected_amd as ssa
+    ssa.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    dt = torch.float64 if dtname == "f64" else torch.float32
+    inputs, parent = make_inputs(kind, cfg, dt, dev)
+    if kind == "chain":
+        call = lambda: ssa.chain(*inputs)
+    elif kind == "star":
+        call = lambda: ssa.star(*inputs)
+    else:
+        plan = ssa.tree_plan(parent, cfg["b"], dt, dev)
+        call = lambda: ssa.tree(parent, *inputs, plan=plan)
+    for _ in range(warmup):
+        out = call()
+    torch.cuda.synchronize()
+    del out
+    stream = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        out = call()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = [a.elapsed_time(b) for a, b in evs]
+    return {"wall_s": wall, "ev_ms": ev_ms}
+
+
+def cpu_baseline(kind, cfg):
+    """The float64 oracle, as it stands, on a bounded sample of the workload."""
+    import numpy as np
+    import oracle
+    import spdgen
+    lib = oracle.load()
+    if kind == "chain":
+        Bs = cfg["B"] if cfg["B"] * cfg["L"] * cfg["b"] ** 3 <= 4e9 else max(1, int(4e9 // (cfg["L"] * cfg["b"] ** 3)))
+        d, l = spdgen.chain(Bs, cfg["L"], cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
+        t0 = time.perf_counter()
+        oracle.chain(d, l, lib=lib)
+        t = time.perf_counter() - t0
+        sub = dict(cfg, B=Bs)
+        sample = "%d of %d chains (L=%d, b=%d), float64" % (Bs, cfg["B"], cfg["L"], cfg["b"])
+    elif kind == "star":
+        Bs = min(cfg["B"], 16)
+        arrs = spdgen.star(Bs, cfg["K"], cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
+        t0 = time.perf_counter()
+        oracle.star(*arrs, lib=lib)
+        t = time.perf_counter() - t0
+        sub = dict(cfg, B=Bs)
+        sample = "%d of %d stars (K=%d, b=%d), float64" % (Bs, cfg["B"], cfg["K"], cfg["b"])
+    else:
+        parent = spdgen.random_recursive_tree(cfg["n"], cfg["seed"])
+        d, e = spdgen.tree(parent, cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
+        t0 = time.perf_counter()
+        oracle.tree(parent, d, e, lib=lib)
+        t = time.perf_counter() - t0
+        sub = cfg
+        sample = "the whole tree (n=%d, b=%d), float64, single thread" % (cfg["n"], cfg["b"])
+    gflops = nominal_flops(kind, sub) / t / 1e9
+    cores = 1 if kind == "tree" else int(lib.oracle_num_threads())
+    return {"value": round(gflops, 3), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": sample, "seconds": round(t, 3),
+            "block_rows_per_s": round(block_rows(kind, sub) / t, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="chain_b16_batched")
+    ap.add_argument("--dtype", default=None, help="f64 or f32 (default: the workload's first)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-second-dtype", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
+              "(batches shard across GPUs with no communication; see DESIGN.md)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import spdgen
+    cfg = dict(spdgen.WORKLOADS[args.workload])
+    kind = cfg.pop("kind")
+    dtypes = cfg.pop("dtypes")
+    dtname = args.dtype or dtypes[0]
+    w = 8 if dtname == "f64" else 4
+
+    res = run_gpu(kind, cfg, dtname, args.steps, args.warmup)
+    ev = sorted(res["ev_ms"])
+    ms_mean = sum(res["ev_ms"]) / len(ev)
+    ms_step = res["wall_s"] * 1e3 / args.steps
+    F = nominal_flops(kind, cfg)
+    nbytes = compulsory_bytes(kind, cfg, w)
+    gflops = F / (ms_step * 1e-3) / 1e9
+    achieved_gbs = nbytes / (ms_mean * 1e-3) / 1e9
+    peak_t = FP64_PEAK_TFLOPS if dtname == "f64" else FP32_PEAK_TFLOPS
+    out = {
+        "metric": "selected-inverse GFLOP/s and block-rows/s (fp64/fp32), % of MI355X roofline",
+        "value": round(gflops, 3),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtname,
+        "data": "synthetic (seeded Philox SPD blocks)",
+        "config": dict({"workload": args.workload, "pattern": kind}, **cfg),
+        "block_rows_per_s": round(block_rows(kind, cfg) / (ms_step * 1e-3), 1),
+        "kernel_ms": {"mean": round(ms_mean, 4), "median": round(ev[len(ev) // 2], 4),
+                      "min": round(ev[0], 4)},
+        "flop_frac_of_peak": round(gflops / (peak_t * 1e3), 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": nbytes},
+    }
+    if not args.no_second_dtype and len(dtypes) > 1 and args.dtype is None:
+        other = dtypes[1]
+        r2 = run_gpu(kind, cfg, other, args.steps, args.warmup)
+        ms2 = r2["wall_s"] * 1e3 / args.steps
+        ev2 = sum(r2["ev_ms"]) / len(r2["ev_ms"])
+        w2 = 8 if other == "f64" else 4
+        out[other] = {"value": round(F / (ms2 * 1e-3) / 1e9, 3), "unit": "GFLOP/s",
+                      "ms_per_step": round(ms2, 4),
+                      "block_rows_per_s": round(block_rows(kind, cfg) / (ms2 * 1e-3), 1),
+                      "hbm_frac": round(compulsory_bytes(kind, cfg, w2) / (ev2 * 1e-3) / 1e9
+                                        / HBM_PEAK_GBS, 4)}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(kind, cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

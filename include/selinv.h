@@ -1,0 +1,155 @@
+/*
+ * selinv.h -- C ABI of the MI355X (gfx950) batched selected inverse of
+ * block-structured SPD matrices.
+ *
+ * What every entry point computes (gabp-sparse-inv 0.3.2 project page,
+ * opening paragraphs and section "Implemented and tested kernels", items
+ * Chain, Star and Tree): for an SPD matrix A whose block graph is a tree, the
+ * blocks of A^-1 that lie on A's own block pattern -- every diagonal block and
+ * every pattern edge -- and log det A, without forming the dense inverse.
+ * The work is a collect pass (block Cholesky / LDL^T Schur sweep, leaves ->
+ * root) followed by a distribute pass (Takahashi back-recursion, root ->
+ * leaves); the page identifies this two-pass schedule with Gaussian belief
+ * propagation.
+ *
+ * Conventions shared by all entry points
+ * --------------------------------------
+ * - Every array argument is a DEVICE pointer (memory of the current HIP
+ *   device), except `parent_host` of selinv_tree_plan_create.  The caller owns
+ *   all memory; the library never allocates per call.  Scratch memory comes in
+ *   through `workspace` (size from the matching *_workspace_bytes query; NULL
+ *   is allowed when that size is 0).  The workspace must be 256-byte aligned
+ *   and must not be used by another call that is still running.
+ * - Blocks are b x b, row-major, contiguous; batches are contiguous
+ *   ("leading batch dimensions", Quickstart section).  Outputs must not alias
+ *   inputs or each other.
+ * - Only the lower triangle of each diagonal input block is read (they are
+ *   taken to be symmetric).  Diagonal output blocks are written in full and
+ *   are symmetric.
+ * - `logdet` is always float64 (natural log of det A), also for the f32
+ *   entry points, which accumulate it in float64.
+ * - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *   default stream) and returns; nothing synchronises the device.
+ * - `info` (may be NULL): per matrix, 0 if every Schur pivot was positive
+ *   definite, else 1 + the index of a block whose pivot was not (NaN
+ *   included).  That matrix's outputs are then unspecified and its logdet is
+ *   NaN.  With a single bad block the index is that block; numbering is per
+ *   entry point below.  This follows the "not positive definite -> error"
+ *   convention of the sparsax page (Features list); the Python binding's
+ *   check=True turns a nonzero info into an exception.
+ * - Return value: a synchronous status (SELINV_OK or an error below) about
+ *   the arguments and the launch, not about the numerics.
+ * - Supported block sizes: 1 <= b <= 32.  Distinct calls on distinct streams
+ *   with distinct workspaces may run concurrently.
+ */
+#ifndef SELINV_H
+#define SELINV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define SELINV_API __attribute__((visibility("default")))
+#else
+#define SELINV_API
+#endif
+
+#define SELINV_OK 0
+#define SELINV_ERR_INVALID_ARG 1 /* null pointer, bad size, b unsupported, workspace too small */
+#define SELINV_ERR_BAD_TREE 2    /* parent array is not one rooted tree                        */
+#define SELINV_ERR_HIP 3         /* HIP runtime or launch error                                 */
+
+#define SELINV_MAX_B 32
+
+/* Human-readable text for a status code (static storage). */
+SELINV_API const char *selinv_strerror(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+SELINV_API int selinv_version(void);
+
+/* ------------------------------------------------------------------ chain
+ * Block-tridiagonal SPD chains (item "Chain": block LDL^T factorisation plus
+ * Takahashi back-recursion, O(L b^3) time).  Per matrix m of B:
+ *   diag    [B][L][b][b]    D_i = A_{i,i}
+ *   lower   [B][L-1][b][b]  lower[i] = A_{i+1,i}
+ *   G_diag  [B][L][b][b]    (A^-1)_{i,i}
+ *   G_lower [B][L-1][b][b]  (A^-1)_{i+1,i}
+ *   logdet  [B]             ln det A (float64)
+ *   info    [B]             0, or 1 + failing block index i
+ * L >= 1; with L == 1, lower and G_lower may be NULL. */
+SELINV_API size_t selinv_chain_workspace_bytes(int dtype_bytes, int64_t B, int64_t L, int32_t b);
+SELINV_API int selinv_chain_f64(int64_t B, int64_t L, int32_t b, const double *diag, const double *lower,
+                     double *G_diag, double *G_lower, double *logdet, int32_t *info,
+                     void *workspace, size_t workspace_bytes, void *stream);
+SELINV_API int selinv_chain_f32(int64_t B, int64_t L, int32_t b, const float *diag, const float *lower,
+                     float *G_diag, float *G_lower, double *logdet, int32_t *info,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------- star
+ * Block-arrowhead SPD matrices (item "Star": one centre block coupled to K
+ * leaf blocks, no leaf-leaf coupling; leaves are eliminated in parallel).
+ * Block 0 is the centre, leaf j is block j+1.  Per matrix m of B:
+ *   center   [B][b][b]      A_{0,0}
+ *   leaves   [B][K][b][b]   A_{j,j}
+ *   coupling [B][K][b][b]   A_{j,0} (leaf row, centre column)
+ *   G_center [B][b][b]      (A^-1)_{0,0}
+ *   G_leaf   [B][K][b][b]   (A^-1)_{j,j}
+ *   G_cross  [B][K][b][b]   (A^-1)_{j,0}
+ *   logdet   [B], info [B]  info: 1 = centre pivot, j+2 = leaf j
+ * K >= 0; with K == 0 the leaf arrays may be NULL.  The off-pattern
+ * leaf-leaf blocks of A^-1 are never formed. */
+SELINV_API size_t selinv_star_workspace_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b);
+SELINV_API int selinv_star_f64(int64_t B, int64_t K, int32_t b, const double *center, const double *leaves,
+                    const double *coupling, double *G_center, double *G_leaf, double *G_cross,
+                    double *logdet, int32_t *info, void *workspace, size_t workspace_bytes,
+                    void *stream);
+SELINV_API int selinv_star_f32(int64_t B, int64_t K, int32_t b, const float *center, const float *leaves,
+                    const float *coupling, float *G_center, float *G_leaf, float *G_cross,
+                    double *logdet, int32_t *info, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* ------------------------------------------------------------------- tree
+ * Arbitrary rooted tree (item "Tree": a parent array and one edge block per
+ * non-root node; collect leaves -> root, then distribute root -> leaves).
+ *
+ * selinv_tree_plan_create validates `parent_host` (HOST memory, n entries,
+ * exactly one -1 = the root, every other entry in [0, n), no cycle; else
+ * SELINV_ERR_BAD_TREE) and builds the depth level-set schedule once per
+ * pattern: breadth-first relabelling so that each depth level and each
+ * node's children are contiguous, level offsets and child ranges, copied to
+ * the device on `stream` (the plan owns these device arrays; the call
+ * synchronises `stream` before returning).  A plan is immutable after creation
+ * and may be shared by concurrent calls; it is specific to (n, b, dtype_bytes).
+ *
+ * selinv_tree_f64 / _f32, for the plan's tree:
+ *   diag   [n][b][b]   A_{v,v}
+ *   edge   [n][b][b]   edge[v] = A_{parent(v),v}; the root slot is ignored
+ *   G_diag [n][b][b]   (A^-1)_{v,v}
+ *   G_edge [n][b][b]   (A^-1)_{parent(v),v}; the root slot is written as 0
+ *   logdet [1], info [1]   info: v+1 for node v
+ * With several bad pivots, info names the first failure in the order
+ * (deepest depth first, increasing node index within a depth). */
+typedef struct selinv_tree_plan selinv_tree_plan;
+
+SELINV_API int selinv_tree_plan_create(const int32_t *parent_host, int64_t n, int32_t b, int dtype_bytes,
+                            void *stream, selinv_tree_plan **out);
+SELINV_API void selinv_tree_plan_destroy(selinv_tree_plan *plan);
+/* number of depth levels (tree height + 1) of a plan, or -1 for NULL */
+SELINV_API int32_t selinv_tree_plan_levels(const selinv_tree_plan *plan);
+SELINV_API size_t selinv_tree_workspace_bytes(const selinv_tree_plan *plan);
+SELINV_API int selinv_tree_f64(const selinv_tree_plan *plan, const double *diag, const double *edge,
+                    double *G_diag, double *G_edge, double *logdet, int32_t *info,
+                    void *workspace, size_t workspace_bytes, void *stream);
+SELINV_API int selinv_tree_f32(const selinv_tree_plan *plan, const float *diag, const float *edge,
+                    float *G_diag, float *G_edge, double *logdet, int32_t *info,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SELINV_H */

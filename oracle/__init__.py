@@ -55,7 +55,9 @@ def load(path: str | None = None):
     lib.oracle_star.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_tree.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_tree_depths.argtypes = [i64, vp, vp]
-    for f in (lib.oracle_chain, lib.oracle_star, lib.oracle_tree, lib.oracle_tree_depths):
+    lib.oracle_num_threads.argtypes = []
+    for f in (lib.oracle_chain, lib.oracle_star, lib.oracle_tree, lib.oracle_tree_depths,
+              lib.oracle_num_threads):
         f.restype = ctypes.c_int
     if path == _LIB:
         _lib = lib

@@ -422,3 +422,15 @@ ORACLE_API int oracle_tree_depths(int64_t n, const int32_t *parent, int32_t *dep
   if (n < 1 || !parent || !depth) return 1;
   return tree_depths(n, parent, depth, &root);
 }
+
+/* Number of OpenMP threads the batch loops use (for reporting). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+ORACLE_API int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,337 @@
+"""MI355X batched selected inverse of block-structured SPD matrices.
+
+Python binding of ``libselinv.so`` (C ABI in ``include/selinv.h``).  This
+module only marshals arguments: every step of the computation runs in the HIP
+kernels of the library.  PyTorch supplies device memory and the stream.
+
+    G_diag, G_lower, logdet = chain(diag, lower)            # block tridiagonal
+    G_center, G_leaf, G_cross, logdet = star(center, leaves, coupling)
+    G_diag, G_edge, logdet = tree(parent, diag, edge)       # any rooted tree
+
+Shapes and orientations follow the Quickstart section of the
+gabp-sparse-inv 0.3.2 page: ``lower[i] = A_{i+1,i}``, ``coupling[j] =
+A_{j,0}``, ``edge[v] = A_{parent(v),v}``; leading batch dimensions are allowed
+for the chain and star.  ``check=True`` synchronises and raises
+``NotPositiveDefinite`` if any Schur pivot failed (the "not positive definite
+-> error" convention of the sparsax page), and validates the inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import hashlib
+import os
+from collections import OrderedDict
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libselinv.so")
+
+OK, INVALID_ARG, BAD_TREE, HIP_ERROR = 0, 1, 2, 3
+MAX_B = 32
+
+_lib = None
+
+
+class SelinvError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+
+class NotPositiveDefinite(SelinvError):
+    """A Schur pivot was not positive definite (info != 0)."""
+
+
+def build():
+    """Compile libselinv.so in place (hipcc, gfx950)."""
+    from . import buildlib as _b
+    global _lib
+    _lib = None
+    return _b.build()
+
+
+def lib():
+    """The loaded C library.  Raises if it has not been built: there is no
+    fallback path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libselinv.so is not built (run sparse_spd_selected_amd.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    L.selinv_strerror.argtypes = [ctypes.c_int]
+    L.selinv_strerror.restype = ctypes.c_char_p
+    L.selinv_version.restype = ctypes.c_int
+    L.selinv_chain_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32]
+    L.selinv_chain_workspace_bytes.restype = sz
+    L.selinv_star_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32]
+    L.selinv_star_workspace_bytes.restype = sz
+    for name in ("selinv_chain_f64", "selinv_chain_f32"):
+        f = getattr(L, name)
+        f.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        f.restype = ctypes.c_int
+    for name in ("selinv_star_f64", "selinv_star_f32"):
+        f = getattr(L, name)
+        f.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        f.restype = ctypes.c_int
+    L.selinv_tree_plan_create.argtypes = [vp, i64, i32, ctypes.c_int, vp, ctypes.POINTER(vp)]
+    L.selinv_tree_plan_create.restype = ctypes.c_int
+    L.selinv_tree_plan_destroy.argtypes = [vp]
+    L.selinv_tree_plan_destroy.restype = None
+    L.selinv_tree_plan_levels.argtypes = [vp]
+    L.selinv_tree_plan_levels.restype = i32
+    L.selinv_tree_workspace_bytes.argtypes = [vp]
+    L.selinv_tree_workspace_bytes.restype = sz
+    for name in ("selinv_tree_f64", "selinv_tree_f32"):
+        f = getattr(L, name)
+        f.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        f.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _status(rc: int, what: str):
+    if rc != OK:
+        msg = lib().selinv_strerror(rc).decode()
+        raise SelinvError("%s: status %d (%s)" % (what, rc, msg))
+
+
+def _sfx(t: torch.Tensor) -> str:
+    if t.dtype == torch.float64:
+        return "f64"
+    if t.dtype == torch.float32:
+        return "f32"
+    raise TypeError("selected inverse supports float32 and float64, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return t.data_ptr() if (t is not None and t.numel()) else None
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_tensor(t, name, device, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device (got %s)" % (name, t.device))
+    if t.device != device or t.dtype != dtype:
+        raise ValueError("%s: device/dtype mismatch" % name)
+    return t.contiguous()
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # 256-byte alignment is guaranteed by the caching allocator (512 B)
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _validate_values(name, t):
+    if not torch.isfinite(t).all():
+        raise ValueError("%s has non-finite entries" % name)
+
+
+def _validate_symmetric(name, t):
+    if t.numel() and not torch.equal(t, t.transpose(-1, -2)):
+        raise ValueError("%s blocks must be exactly symmetric" % name)
+
+
+def _raise_info(info: torch.Tensor, what: str):
+    bad = info.nonzero()
+    if bad.numel():
+        idx = tuple(int(i) for i in bad[0])
+        raise NotPositiveDefinite("%s: Schur pivot not positive definite (matrix %s, info=%d)"
+                                  % (what, idx, int(info[idx])))
+
+
+# ------------------------------------------------------------------ chain
+def chain(diag: torch.Tensor, lower: torch.Tensor, check: bool = False, return_info=False):
+    """Selected inverse of block-tridiagonal SPD chains.
+
+    diag [..., L, b, b], lower [..., L-1, b, b] with lower[i] = A_{i+1,i}.
+    Returns (G_diag [..., L, b, b], G_lower [..., L-1, b, b], logdet [...]
+    float64), plus info [...] int32 when return_info.
+    """
+    dt, dev = diag.dtype, diag.device
+    diag = _check_tensor(diag, "diag", dev, dt)
+    lower = _check_tensor(lower, "lower", dev, dt)
+    sfx = _sfx(diag)
+    if diag.dim() < 3 or diag.shape[-1] != diag.shape[-2]:
+        raise ValueError("diag must be [..., L, b, b]")
+    *batch, L, b, _ = diag.shape
+    if L < 1 or b < 1 or b > MAX_B:
+        raise ValueError("need L >= 1 and 1 <= b <= %d" % MAX_B)
+    if tuple(lower.shape) != tuple(batch) + (L - 1, b, b):
+        raise ValueError("lower must be [..., L-1, b, b] matching diag")
+    if check:
+        _validate_values("diag", diag)
+        _validate_values("lower", lower)
+        _validate_symmetric("diag", diag)
+    B = 1
+    for s in batch:
+        B *= s
+    G_diag = torch.empty_like(diag)
+    G_lower = torch.empty_like(lower)
+    logdet = torch.empty(tuple(batch), dtype=torch.float64, device=dev)
+    info = torch.empty(tuple(batch), dtype=torch.int32, device=dev)
+    L_ = lib()
+    ws_bytes = L_.selinv_chain_workspace_bytes(diag.element_size(), B, L, b)
+    ws = _workspace(ws_bytes, dev)
+    with torch.cuda.device(dev):
+        rc = getattr(L_, "selinv_chain_" + sfx)(
+            B, L, b, _ptr(diag), _ptr(lower), _ptr(G_diag), _ptr(G_lower), _ptr(logdet),
+            _ptr(info), _ptr(ws), ws_bytes, _stream(dev))
+    _status(rc, "selinv_chain_" + sfx)
+    if check:
+        _raise_info(info, "chain")
+    if return_info:
+        return G_diag, G_lower, logdet, info
+    return G_diag, G_lower, logdet
+
+
+# ------------------------------------------------------------------- star
+def star(center: torch.Tensor, leaves: torch.Tensor, coupling: torch.Tensor,
+         check: bool = False, return_info=False):
+    """Selected inverse of block-arrowhead SPD matrices.
+
+    center [..., b, b], leaves [..., K, b, b], coupling [..., K, b, b] with
+    coupling[j] = A_{j,0}.  Returns (G_center, G_leaf, G_cross, logdet) with
+    G_cross[j] = (A^-1)_{j,0}.
+    """
+    dt, dev = center.dtype, center.device
+    center = _check_tensor(center, "center", dev, dt)
+    leaves = _check_tensor(leaves, "leaves", dev, dt)
+    coupling = _check_tensor(coupling, "coupling", dev, dt)
+    sfx = _sfx(center)
+    if center.dim() < 2 or center.shape[-1] != center.shape[-2]:
+        raise ValueError("center must be [..., b, b]")
+    *batch, b, _ = center.shape
+    if leaves.dim() != len(batch) + 3 or tuple(leaves.shape[:len(batch)]) != tuple(batch):
+        raise ValueError("leaves must be [..., K, b, b] matching center")
+    K = leaves.shape[len(batch)]
+    if tuple(leaves.shape) != tuple(batch) + (K, b, b) or coupling.shape != leaves.shape:
+        raise ValueError("leaves and coupling must be [..., K, b, b]")
+    if b < 1 or b > MAX_B:
+        raise ValueError("need 1 <= b <= %d" % MAX_B)
+    if check:
+        for nm, t in (("center", center), ("leaves", leaves), ("coupling", coupling)):
+            _validate_values(nm, t)
+        _validate_symmetric("center", center)
+        _validate_symmetric("leaves", leaves)
+    B = 1
+    for s in batch:
+        B *= s
+    G_center = torch.empty_like(center)
+    G_leaf = torch.empty_like(leaves)
+    G_cross = torch.empty_like(coupling)
+    logdet = torch.empty(tuple(batch), dtype=torch.float64, device=dev)
+    info = torch.empty(tuple(batch), dtype=torch.int32, device=dev)
+    L_ = lib()
+    ws_bytes = L_.selinv_star_workspace_bytes(center.element_size(), B, K, b)
+    ws = _workspace(ws_bytes, dev)
+    with torch.cuda.device(dev):
+        rc = getattr(L_, "selinv_star_" + sfx)(
+            B, K, b, _ptr(center), _ptr(leaves), _ptr(coupling), _ptr(G_center), _ptr(G_leaf),
+            _ptr(G_cross), _ptr(logdet), _ptr(info), _ptr(ws), ws_bytes, _stream(dev))
+    _status(rc, "selinv_star_" + sfx)
+    if check:
+        _raise_info(info, "star")
+    if return_info:
+        return G_center, G_leaf, G_cross, logdet, info
+    return G_center, G_leaf, G_cross, logdet
+
+
+# ------------------------------------------------------------------- tree
+class TreePlan:
+    """A validated level-set schedule for one parent array (owns device
+    memory through the C library)."""
+
+    def __init__(self, parent, b: int, dtype: torch.dtype, device):
+        import numpy as np
+        p = np.ascontiguousarray(np.asarray(parent, dtype=np.int32))
+        self.n = int(p.shape[0])
+        self.b = int(b)
+        self.dtype = dtype
+        self.device = torch.device(device)
+        h = ctypes.c_void_p()
+        esz = 8 if dtype == torch.float64 else 4
+        with torch.cuda.device(self.device):
+            rc = lib().selinv_tree_plan_create(p.ctypes.data, self.n, self.b, esz,
+                                               _stream(self.device), ctypes.byref(h))
+        _status(rc, "selinv_tree_plan_create")
+        self._h = h
+        self.levels = int(lib().selinv_tree_plan_levels(h))
+        self.workspace_bytes = int(lib().selinv_tree_workspace_bytes(h))
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.selinv_tree_plan_destroy(h)
+            self._h = None
+
+
+_PLAN_CACHE: "OrderedDict[tuple, TreePlan]" = OrderedDict()
+_PLAN_CACHE_MAX = 8
+
+
+def tree_plan(parent, b: int, dtype: torch.dtype, device) -> TreePlan:
+    """Cached plan keyed by the parent array's content and (n, b, dtype,
+    device): repeated calls on one pattern pay only for the numeric work."""
+    import numpy as np
+    if isinstance(parent, torch.Tensor):
+        parent = parent.detach().cpu().numpy()
+    p = np.ascontiguousarray(np.asarray(parent, dtype=np.int32))
+    key = (hashlib.sha1(p.tobytes()).hexdigest(), p.shape[0], int(b), dtype, str(device))
+    plan = _PLAN_CACHE.get(key)
+    if plan is None:
+        plan = TreePlan(p, b, dtype, device)
+        _PLAN_CACHE[key] = plan
+        while len(_PLAN_CACHE) > _PLAN_CACHE_MAX:
+            _PLAN_CACHE.popitem(last=False)
+    else:
+        _PLAN_CACHE.move_to_end(key)
+    return plan
+
+
+def tree(parent, diag: torch.Tensor, edge: torch.Tensor, check: bool = False,
+         return_info=False, plan: TreePlan | None = None):
+    """Selected inverse of a tree-structured SPD matrix.
+
+    parent [n] (root = -1; host array or tensor), diag [n, b, b],
+    edge [n, b, b] with edge[v] = A_{parent(v),v}.  Returns (G_diag, G_edge,
+    logdet) with G_edge[v] = (A^-1)_{parent(v),v} and a zero root slot.
+    """
+    dt, dev = diag.dtype, diag.device
+    diag = _check_tensor(diag, "diag", dev, dt)
+    edge = _check_tensor(edge, "edge", dev, dt)
+    sfx = _sfx(diag)
+    if diag.dim() != 3 or diag.shape[1] != diag.shape[2] or edge.shape != diag.shape:
+        raise ValueError("diag and edge must be [n, b, b]")
+    n, b = diag.shape[0], diag.shape[1]
+    if plan is None:
+        plan = tree_plan(parent, b, dt, dev)
+    if plan.n != n or plan.b != b or plan.dtype != dt:
+        raise ValueError("plan does not match (n, b, dtype)")
+    if check:
+        _validate_values("diag", diag)
+        _validate_symmetric("diag", diag)
+    G_diag = torch.empty_like(diag)
+    G_edge = torch.empty_like(edge)
+    logdet = torch.empty((), dtype=torch.float64, device=dev)
+    info = torch.empty((), dtype=torch.int32, device=dev)
+    ws = _workspace(plan.workspace_bytes, dev)
+    with torch.cuda.device(dev):
+        rc = getattr(lib(), "selinv_tree_" + sfx)(
+            plan.handle, _ptr(diag), _ptr(edge), _ptr(G_diag), _ptr(G_edge), logdet.data_ptr(),
+            info.data_ptr(), _ptr(ws), plan.workspace_bytes, _stream(dev))
+    _status(rc, "selinv_tree_" + sfx)
+    if check:
+        _raise_info(info.reshape(1), "tree")
+    if return_info:
+        return G_diag, G_edge, logdet, info
+    return G_diag, G_edge, logdet

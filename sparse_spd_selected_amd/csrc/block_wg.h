@@ -1,0 +1,127 @@
+// block_wg.h -- b x b block algebra shared by all threads of one workgroup,
+// blocks held in LDS (row-major).  Used by the kernels for any b <= 32; the
+// specialised kernels keep their blocks in registers instead.
+//
+// Every function starts from synchronised LDS and ends with __syncthreads(),
+// so calls can be chained without extra barriers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace selinv {
+namespace wg {
+
+__device__ inline int tid() { return threadIdx.x; }
+__device__ inline int nthreads() { return blockDim.x; }
+
+template <typename T>
+__device__ inline T qnan() {
+  return __builtin_nan("");
+}
+template <>
+__device__ inline float qnan<float>() {
+  return __builtin_nanf("");
+}
+
+// dst = src (b*b entries); either side may be global or LDS
+template <typename T>
+__device__ inline void copy(T *dst, const T *src, int bb) {
+  for (int e = tid(); e < bb; e += nthreads()) dst[e] = src[e];
+  __syncthreads();
+}
+
+// dst = sign * src
+template <typename T>
+__device__ inline void copy_scaled(T *dst, const T *src, int bb, T sign) {
+  for (int e = tid(); e < bb; e += nthreads()) dst[e] = sign * src[e];
+  __syncthreads();
+}
+
+// dst = symmetric block from the LOWER triangle of src (mirrored)
+template <typename T>
+__device__ inline void load_sym_lower(T *dst, const T *src, int b) {
+  for (int e = tid(); e < b * b; e += nthreads()) {
+    const int r = e / b, c = e % b;
+    dst[e] = r >= c ? src[r * b + c] : src[c * b + r];
+  }
+  __syncthreads();
+}
+
+template <typename T>
+__device__ inline void fill(T *dst, int bb, T v) {
+  for (int e = tid(); e < bb; e += nthreads()) dst[e] = v;
+  __syncthreads();
+}
+
+// Out = op(A) op(B), op = transpose when TA/TB.  Out must not alias A or B.
+template <typename T, bool TA, bool TB>
+__device__ inline void gemm(T *Out, const T *A, const T *B, int b) {
+  for (int e = tid(); e < b * b; e += nthreads()) {
+    const int r = e / b, c = e % b;
+    T acc = T(0);
+    for (int k = 0; k < b; ++k) {
+      const T a = TA ? A[k * b + r] : A[r * b + k];
+      const T x = TB ? B[c * b + k] : B[k * b + c];
+      acc += a * x;
+    }
+    Out[e] = acc;
+  }
+  __syncthreads();
+}
+
+// Out = Base + sign * op(A) op(B), computed on the lower triangle and
+// mirrored, so Out is exactly symmetric (for products that are symmetric in
+// exact arithmetic).  Base may be null (taken as 0) and may alias Out.
+template <typename T, bool TA, bool TB>
+__device__ inline void gemm_sym(T *Out, const T *Base, const T *A, const T *B, int b, T sign) {
+  for (int e = tid(); e < b * b; e += nthreads()) {
+    const int r = e / b, c = e % b;
+    if (r < c) continue;
+    T acc = T(0);
+    for (int k = 0; k < b; ++k) {
+      const T a = TA ? A[k * b + r] : A[r * b + k];
+      const T x = TB ? B[c * b + k] : B[k * b + c];
+      acc += a * x;
+    }
+    const T v = (Base ? Base[r * b + c] : T(0)) + sign * acc;
+    Out[r * b + c] = v;
+    Out[c * b + r] = v;
+  }
+  __syncthreads();
+}
+
+// In-place inverse of a symmetric positive definite block by the symmetric
+// Gauss-Jordan sweep, without pivoting.  Sweeping pivot k maps
+//   a_ij -> a_ij - a_ik a_kj / d   (i, j != k),   a_ik -> a_ik / d,
+//   a_kk -> -1/d,   with d = a_kk,
+// so that sweeping every pivot leaves -A^{-1}; the sign is flipped at the end.
+// Each pivot d is the diagonal of the current Schur complement (the D of an
+// LDL^T factorisation), so A is positive definite iff every d > 0 and
+// ln det A = sum_k ln d.  `col` is LDS scratch of b entries.
+// Returns 0, or 1 (uniformly across the workgroup) if a pivot is not > 0 or
+// is NaN; then A holds garbage.  *logdet receives sum ln d (float64).
+template <typename T>
+__device__ inline int spd_inverse(T *A, int b, T *col, double *logdet) {
+  double ld = 0.0;
+  for (int k = 0; k < b; ++k) {
+    const T d = A[k * b + k];
+    if (!(d > T(0))) return 1;
+    ld += log(static_cast<double>(d));
+    if (tid() < b) col[tid()] = tid() == k ? T(-1) : A[tid() * b + k];
+    __syncthreads();
+    const T inv = T(1) / d;
+    for (int e = tid(); e < b * b; e += nthreads()) {
+      const int i = e / b, j = e % b;
+      const T a = (i == k || j == k) ? T(0) : A[e];
+      A[e] = a - (col[i] * col[j]) * inv;
+    }
+    __syncthreads();
+  }
+  for (int e = tid(); e < b * b; e += nthreads()) A[e] = -A[e];
+  __syncthreads();
+  *logdet = ld;
+  return 0;
+}
+
+}  // namespace wg
+}  // namespace selinv

@@ -1,0 +1,81 @@
+// internal.h -- declarations shared by the HIP sources of libselinv (not part
+// of the public ABI; the public header is include/selinv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "selinv.h"
+
+namespace selinv {
+
+// Workspace carve-up helper: every region starts 256-byte aligned.
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+struct Carve {
+  char *base;
+  size_t off = 0;
+  explicit Carve(void *p) : base(static_cast<char *>(p)) {}
+  template <typename U>
+  U *take(size_t count) {
+    U *p = reinterpret_cast<U *>(base ? base + off : nullptr);
+    off = align_up(off + count * sizeof(U));
+    return p;
+  }
+};
+
+// Host-side tree plan: depth level sets in breadth-first order.
+//   pos    = breadth-first position (levels contiguous, each node's children
+//            contiguous in the next level, in increasing node index)
+//   node_at[pos]    original node index
+//   parent_pos[pos] position of the parent (-1 for the root, pos 0)
+//   child_beg/end[pos]  children positions [beg, end)
+//   fail_rank[pos]  rank of the node in the order (depth descending, index
+//                   ascending) used to name the first failing pivot
+//   rank_node[r]    node index of rank r
+struct TreePlanDev {
+  int32_t *node_at = nullptr;
+  int32_t *parent_pos = nullptr;
+  int32_t *child_beg = nullptr;
+  int32_t *child_end = nullptr;
+  int32_t *fail_rank = nullptr;
+  int32_t *rank_node = nullptr;
+};
+
+}  // namespace selinv
+
+struct selinv_tree_plan {
+  int64_t n = 0;
+  int32_t b = 0;
+  int dtype_bytes = 0;
+  int32_t levels = 0;
+  int64_t *level_off = nullptr;   // host, levels+1 entries
+  int32_t max_children = 0;
+  selinv::TreePlanDev dev;
+  void *dev_block = nullptr;      // one device allocation backing `dev`
+};
+
+namespace selinv {
+
+// ---------------------------------------------------------------- chain
+size_t chain_workspace_bytes(int dtype_bytes, int64_t B, int64_t L, int32_t b);
+template <typename T>
+hipError_t chain_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower, T *G_diag,
+                        T *G_lower, double *logdet, int32_t *info, void *ws, hipStream_t s);
+
+// ----------------------------------------------------------------- star
+size_t star_workspace_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b);
+template <typename T>
+hipError_t star_launch(int64_t B, int64_t K, int32_t b, const T *center, const T *leaves,
+                       const T *coupling, T *G_center, T *G_leaf, T *G_cross, double *logdet,
+                       int32_t *info, void *ws, hipStream_t s);
+
+// ----------------------------------------------------------------- tree
+size_t tree_workspace_bytes(const selinv_tree_plan *plan);
+template <typename T>
+hipError_t tree_launch(const selinv_tree_plan *plan, const T *diag, const T *edge, T *G_diag,
+                       T *G_edge, double *logdet, int32_t *info, void *ws, hipStream_t s);
+
+}  // namespace selinv

@@ -1,0 +1,116 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/*.h declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+from conftest import ROOT
+
+import sparse_spd_selected_amd as ssa
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(selinv_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssa.LIB_PATH):
+        ssa.build()
+    return ssa.lib()
+
+
+def test_header_declares_entry_points():
+    names = _declared()
+    for want in ("selinv_chain_f64", "selinv_chain_f32", "selinv_star_f64", "selinv_star_f32",
+                 "selinv_tree_f64", "selinv_tree_f32", "selinv_tree_plan_create",
+                 "selinv_tree_plan_destroy", "selinv_chain_workspace_bytes",
+                 "selinv_star_workspace_bytes", "selinv_tree_workspace_bytes", "selinv_strerror"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_and_version(lib):
+    assert lib.selinv_strerror(0) == b"ok"
+    assert b"tree" in lib.selinv_strerror(2)
+    assert lib.selinv_version() >= 100
+
+
+def test_workspace_sizes(lib):
+    assert lib.selinv_chain_workspace_bytes(8, 4096, 64, 16) >= 4096 * 64 * 2 * 256 * 8
+    assert lib.selinv_chain_workspace_bytes(3, 1, 1, 1) == 0  # bad dtype size
+    assert lib.selinv_chain_workspace_bytes(8, 1, 1, 33) == 0  # b > 32
+    assert lib.selinv_star_workspace_bytes(4, 2, 0, 4) > 0
+    assert lib.selinv_tree_workspace_bytes(None) == 0
+
+
+def _chain_call(lib, B=1, L=2, b=4, diag=1, lower=1, gd=1, gl=1, ld=1, ws=1, wsb=1 << 30):
+    p = lambda x: ctypes.c_void_p(0x1000) if x else None  # never dereferenced on error paths
+    return lib.selinv_chain_f64(B, L, b, p(diag), p(lower), p(gd), p(gl), p(ld), None, p(ws),
+                                wsb, None)
+
+
+def test_chain_argument_validation(lib):
+    assert _chain_call(lib, b=0) == ssa.INVALID_ARG
+    assert _chain_call(lib, b=33) == ssa.INVALID_ARG
+    assert _chain_call(lib, L=0) == ssa.INVALID_ARG
+    assert _chain_call(lib, B=-1) == ssa.INVALID_ARG
+    assert _chain_call(lib, diag=0) == ssa.INVALID_ARG
+    assert _chain_call(lib, lower=0) == ssa.INVALID_ARG
+    assert _chain_call(lib, ld=0) == ssa.INVALID_ARG
+    assert _chain_call(lib, wsb=16) == ssa.INVALID_ARG
+    assert _chain_call(lib, ws=0) == ssa.INVALID_ARG
+    assert _chain_call(lib, B=0) == ssa.OK  # empty batch: nothing to do
+
+
+def test_star_argument_validation(lib):
+    p = ctypes.c_void_p(0x1000)
+    assert lib.selinv_star_f32(1, 2, 0, p, p, p, p, p, p, p, None, p, 1 << 30, None) == \
+        ssa.INVALID_ARG
+    assert lib.selinv_star_f32(1, 2, 4, p, None, p, p, p, p, p, None, p, 1 << 30, None) == \
+        ssa.INVALID_ARG
+    assert lib.selinv_star_f32(1, 2, 4, p, p, p, p, p, p, p, None, p, 8, None) == ssa.INVALID_ARG
+
+
+@pytest.mark.parametrize("parent", [[-1, 0, -1], [0, 0, 1], [-1, 2, 3, 1], [-1, 0, 7],
+                                    [-1, 1]])
+def test_tree_plan_rejects_invalid_trees(lib, parent):
+    a = np.array(parent, np.int32)
+    h = ctypes.c_void_p()
+    rc = lib.selinv_tree_plan_create(a.ctypes.data, len(a), 4, 8, None, ctypes.byref(h))
+    assert rc == ssa.BAD_TREE and not h.value
+
+
+def test_tree_plan_argument_validation(lib):
+    a = np.array([-1, 0], np.int32)
+    h = ctypes.c_void_p()
+    assert lib.selinv_tree_plan_create(a.ctypes.data, 2, 0, 8, None, ctypes.byref(h)) == \
+        ssa.INVALID_ARG
+    assert lib.selinv_tree_plan_create(a.ctypes.data, 2, 4, 2, None, ctypes.byref(h)) == \
+        ssa.INVALID_ARG
+    assert lib.selinv_tree_plan_create(None, 2, 4, 8, None, ctypes.byref(h)) == ssa.INVALID_ARG
+    p = ctypes.c_void_p(0x1000)
+    assert lib.selinv_tree_f64(None, p, p, p, p, p, None, p, 1 << 30, None) == ssa.INVALID_ARG
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    d = torch.zeros(1, 2, 4, 4, dtype=torch.float64)
+    l = torch.zeros(1, 1, 4, 4, dtype=torch.float64)
+    with pytest.raises(ValueError):
+        ssa.chain(d, l)
+    with pytest.raises(TypeError):
+        ssa.chain(d.numpy(), l)
