@@ -22,6 +22,7 @@ SOURCES = [
     "abi.cpp",
     "tree_plan.cpp",
     "generic.hip",
+    "chain_b16.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

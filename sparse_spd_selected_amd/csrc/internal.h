@@ -61,6 +61,10 @@ namespace selinv {
 
 // ---------------------------------------------------------------- chain
 size_t chain_workspace_bytes(int dtype_bytes, int64_t B, int64_t L, int32_t b);
+// b = 16: one wavefront per chain on the matrix cores (chain_b16.hip)
+template <typename T>
+hipError_t chain16_launch(int64_t B, int64_t L, const T *diag, const T *lower, T *G_diag,
+                          T *G_lower, double *logdet, int32_t *info, void *ws, hipStream_t s);
 template <typename T>
 hipError_t chain_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower, T *G_diag,
                         T *G_lower, double *logdet, int32_t *info, void *ws, hipStream_t s);
