@@ -143,6 +143,19 @@ def cpu_baseline(kind, cfg):
             "block_rows_per_s": round(block_rows(kind, sub) / t, 1)}
 
 
+def copy_probe(mib, steps):
+    """A plain device-to-device copy of known size: one read and one write of
+    `mib` MiB per launch, for scaling the HBM traffic counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(max(steps, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": n * 4, "launches": max(steps, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,7 +165,13 @@ def main():
     ap.add_argument("--dtype", default=None, help="f64 or f32 (default: the workload's first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-second-dtype", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib, args.steps)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
               "(batches shard across GPUs with no communication; see DESIGN.md)" % args.gpus,

@@ -97,6 +97,56 @@ __device__ __forceinline__ Frag<T> load_sym(const T *P, int ld, int g, int j) {
   return f;
 }
 
+// Lane offsets of a symmetric block read from its lower triangle: element r
+// of lane (g, j) is P[off[r]] (row-major, leading dimension ld).
+template <typename T>
+struct SymOffsets {
+  int off[4];
+  __device__ __forceinline__ SymOffsets(int ld, int g, int j) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = row<T>(g, r);
+      off[r] = i >= j ? i * ld + j : j * ld + i;
+    }
+  }
+  __device__ __forceinline__ Frag<T> load(const T *P) const {
+    Frag<T> f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f[r] = P[off[r]];
+    return f;
+  }
+};
+
+// Packed lower triangle of a symmetric 16x16 block (136 entries, row i at
+// offset i (i + 1) / 2): the element of lane (g, j) register r sits at
+// off[r]; lanes whose element is in the upper triangle do not store it.
+constexpr int kPacked16 = 136;
+template <typename T>
+struct PackedOffsets {
+  int off[4];
+  unsigned lower_mask;  // bit r: element r lies on or below the diagonal
+  __device__ __forceinline__ PackedOffsets(int g, int j) : lower_mask(0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = row<T>(g, r);
+      const int a = i >= j ? i : j, b = i >= j ? j : i;
+      off[r] = a * (a + 1) / 2 + b;
+      if (i >= j) lower_mask |= 1u << r;
+    }
+  }
+  __device__ __forceinline__ Frag<T> load(const T *P) const {
+    Frag<T> f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f[r] = P[off[r]];
+    return f;
+  }
+  __device__ __forceinline__ void store(T *P, Frag<T> f) const {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (lower_mask & (1u << r)) P[off[r]] = f[r];
+  }
+};
+
 // O(P) row-major store
 template <typename T>
 __device__ __forceinline__ void store(T *P, int ld, Frag<T> f, int g, int j) {
@@ -136,19 +186,17 @@ __device__ __forceinline__ float rcp<float>(float d) {
   return __builtin_fmaf(x, e, x);
 }
 
-// Running product of pivots kept as mantissa * 2^exponent (no overflow for
-// any finite pivots); ln of it is taken once per block.
+// Running product of pivots kept as mantissa * 2^exponent.  Pivots are
+// multiplied in groups of four and renormalised once per group, so any four
+// consecutive pivots with magnitudes in [2^-255, 2^255] are safe; ln of the
+// product is taken once per block.
 struct PivotLog {
   double mant = 1.0;
   int expo = 0;
-  __device__ __forceinline__ void mul(double d) {
+  __device__ __forceinline__ void mul4(double d0, double d1, double d2, double d3) {
     int e;
-    const double m = frexp(d, &e);
-    mant *= m;
+    mant = frexp(mant * ((d0 * d1) * (d2 * d3)), &e);
     expo += e;
-    int e2;
-    mant = frexp(mant, &e2);
-    expo += e2;
   }
   __device__ __forceinline__ double log() const {
     return ::log(mant) + expo * 0.69314718055994530941723212145818;
@@ -169,27 +217,33 @@ template <typename T>
 __device__ __forceinline__ bool gj_inverse(Frag<T> &a, T *col, int g, int j, PivotLog &pl) {
   bool bad = false;
   const int pj = Mfma<T>::pos(j);
+#pragma unroll 1
+  for (int kq = 0; kq < 4; ++kq) {
+    double dq[4];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    if (j == k) *reinterpret_cast<Frag<T> *>(col + 4 * g) = a;
-    __syncthreads();
-    const T d = col[Mfma<T>::pos(k)];
-    Frag<T> ci = *reinterpret_cast<const Frag<T> *>(col + 4 * g);
-    T cj = col[pj];
-    __syncthreads();
-    bad |= !(d > T(0));
-    pl.mul(static_cast<double>(d));
-    const T inv = rcp<T>(d);
+    for (int kr = 0; kr < 4; ++kr) {
+      // pivot k = row(kq, kr): the element of lane group kq, register kr
+      const int k = Mfma<T>::row(kq, kr);
+      if (j == k) *reinterpret_cast<Frag<T> *>(col + 4 * g) = a;
+      __syncthreads();
+      const T d = col[4 * kq + kr];
+      Frag<T> ci = *reinterpret_cast<const Frag<T> *>(col + 4 * g);
+      T cj = col[pj];
+      __syncthreads();
+      bad |= !(d > T(0));
+      dq[kr] = static_cast<double>(d);
+      const T inv = rcp<T>(d);
+      const bool own = g == kq;  // this lane group holds row k in register kr
+      if (own) ci[kr] = T(-1);
+      if (j == k) cj = T(-1);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (row<T>(g, r) == k) ci[r] = T(-1);
-    if (j == k) cj = T(-1);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool z = (j == k) || (row<T>(g, r) == k);
-      const T t = ci[r] * inv;
-      a[r] = (z ? T(0) : a[r]) - t * cj;
+      for (int r = 0; r < 4; ++r) {
+        const bool z = (j == k) || (own && r == kr);
+        const T t = ci[r] * inv;
+        a[r] = (z ? T(0) : a[r]) - t * cj;
+      }
     }
+    pl.mul4(dq[0], dq[1], dq[2], dq[3]);
   }
   a = -a;
   return bad;
