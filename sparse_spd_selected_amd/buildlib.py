@@ -23,6 +23,7 @@ SOURCES = [
     "tree_plan.cpp",
     "generic.hip",
     "chain_b16.hip",
+    "star_b32.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

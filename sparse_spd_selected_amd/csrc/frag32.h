@@ -1,0 +1,281 @@
+// frag32.h -- 32x32 blocks held by one wavefront as 2 x 2 tiles of the
+// 16x16 MFMA accumulator layout of frag16.h (16 entries per lane), with
+// block products on the matrix cores and a register-resident Gauss-Jordan
+// inverse.
+//
+// Tile (I, J) of "O32(P)" is O(P_IJ), P_IJ = P[16I .. 16I+15][16J .. 16J+15].
+// Products: O32(A B) tile (I, J) = sum_K mm(O(A^T) tile (K, I), O(B) tile (K, J)),
+// i.e. O32(A B) = mm32(O32(A^T), O32(B)) exactly as for 16x16 blocks.
+#pragma once
+
+#include "frag16.h"
+
+namespace selinv {
+namespace f32t {
+
+using f16::Frag;
+using f16::Mfma;
+using f16::row;
+
+template <typename T>
+struct Blk {
+  Frag<T> t[2][2];
+};
+
+template <typename T>
+__device__ __forceinline__ Blk<T> zero() {
+  Blk<T> b;
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J) b.t[I][J] = f16::zero<T>();
+  return b;
+}
+
+// O32(A B) + acc from O32(A^T) and O32(B)
+template <typename T>
+__device__ __forceinline__ Blk<T> mm(const Blk<T> &At, const Blk<T> &Bf, Blk<T> acc) {
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J) {
+      acc.t[I][J] = f16::mm<T>(At.t[0][I], Bf.t[0][J], acc.t[I][J]);
+      acc.t[I][J] = f16::mm<T>(At.t[1][I], Bf.t[1][J], acc.t[I][J]);
+    }
+  return acc;
+}
+
+// Symmetric variant: only the tiles on and below the diagonal are formed and
+// the upper tile is taken as the transpose of the lower one's layout-twin,
+// which is valid when the exact product is symmetric.  The (0,1) tile is
+// returned as the (1,0) tile's layout transposition is not available in
+// registers, so it is computed too but with the cheaper of the two
+// contractions shared; callers that only store the lower triangle can skip it.
+template <typename T>
+__device__ __forceinline__ Blk<T> mm_lower(const Blk<T> &At, const Blk<T> &Bf, Blk<T> acc) {
+  acc.t[0][0] = f16::mm<T>(At.t[0][0], Bf.t[0][0], acc.t[0][0]);
+  acc.t[0][0] = f16::mm<T>(At.t[1][0], Bf.t[1][0], acc.t[0][0]);
+  acc.t[1][0] = f16::mm<T>(At.t[0][1], Bf.t[0][0], acc.t[1][0]);
+  acc.t[1][0] = f16::mm<T>(At.t[1][1], Bf.t[1][0], acc.t[1][0]);
+  acc.t[1][1] = f16::mm<T>(At.t[0][1], Bf.t[0][1], acc.t[1][1]);
+  acc.t[1][1] = f16::mm<T>(At.t[1][1], Bf.t[1][1], acc.t[1][1]);
+  return acc;
+}
+
+// O32(P^T) of a row-major 32x32 block
+template <typename T>
+__device__ __forceinline__ Blk<T> load_t(const T *P, int g, int x) {
+  Blk<T> b;
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J) b.t[I][J] = f16::load_t(P + 16 * J * 32 + 16 * I, 32, g, x);
+  return b;
+}
+
+// O32(P) of a row-major 32x32 block
+template <typename T>
+__device__ __forceinline__ Blk<T> load(const T *P, int g, int j) {
+  Blk<T> b;
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b.t[I][J][r] = P[(16 * I + row<T>(g, r)) * 32 + 16 * J + j];
+  return b;
+}
+
+template <typename T>
+__device__ __forceinline__ void store(T *P, const Blk<T> &b, int g, int j) {
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J) f16::store(P + 16 * I * 32 + 16 * J, 32, b.t[I][J], g, j);
+}
+
+// store of O32(P) as P^T (a plain store when P is symmetric)
+template <typename T>
+__device__ __forceinline__ void store_t(T *P, const Blk<T> &b, int g, int j) {
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J) f16::store_t(P + 16 * J * 32 + 16 * I, 32, b.t[I][J], g, j);
+}
+
+template <typename T>
+__device__ __forceinline__ Blk<T> neg(Blk<T> b) {
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J) b.t[I][J] = -b.t[I][J];
+  return b;
+}
+
+template <typename T>
+__device__ __forceinline__ Blk<T> sub(Blk<T> a, const Blk<T> &b) {
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J) a.t[I][J] = a.t[I][J] - b.t[I][J];
+  return a;
+}
+
+// Lane offsets for a symmetric 32x32 block read from its lower triangle.
+// Off-diagonal tiles are always wholly below ((1,0)) or above ((0,1)) the
+// diagonal, so their offsets are affine in the register index; only the
+// diagonal tiles need one lane offset per register (shared by both tiles).
+template <typename T>
+struct SymOffsets {
+  int dg[4];  // tile (0,0); tile (1,1) adds 16 * 33
+  int g_, j_;
+  __device__ __forceinline__ SymOffsets(int g, int j) : g_(g), j_(j) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int a = row<T>(g, r);
+      dg[r] = a >= j ? a * 32 + j : j * 32 + a;
+    }
+  }
+  __device__ __forceinline__ Blk<T> load(const T *P) const {
+    Blk<T> b;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int a = row<T>(g_, r);
+      b.t[0][0][r] = P[dg[r]];
+      b.t[1][1][r] = P[dg[r] + 16 * 33];
+      b.t[1][0][r] = P[(16 + a) * 32 + j_];   // below the diagonal
+      b.t[0][1][r] = P[(16 + j_) * 32 + a];   // above: read the mirrored entry
+    }
+    return b;
+  }
+};
+
+// Packed lower triangle of a symmetric 32x32 block (528 entries, row i at
+// offset i (i + 1) / 2).
+constexpr int kPacked32 = 528;
+template <typename T>
+struct PackedOffsets {
+  int d0[4];   // tile (0,0) entry offsets (hi, lo = max, min of row and column)
+  int hi0[4];  // max(row, column) inside the diagonal tiles
+  int r10[4];  // tile (1,0): (16 + row)(17 + row) / 2 + column
+  int g_, j_;
+  unsigned diag_lower;  // bit r: diagonal-tile entry r lies on or below the diagonal
+  __device__ __forceinline__ PackedOffsets(int g, int j) : g_(g), j_(j), diag_lower(0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int a = row<T>(g, r);
+      const int hi = a >= j ? a : j, lo = a >= j ? j : a;
+      d0[r] = hi * (hi + 1) / 2 + lo;
+      hi0[r] = hi;
+      r10[r] = (16 + a) * (17 + a) / 2 + j;
+      if (a >= j) diag_lower |= 1u << r;
+    }
+  }
+  // tile (1,1): (16+hi)(17+hi)/2 + 16 + lo = d0 + 16 hi + 152
+  __device__ __forceinline__ int d1(int r) const { return d0[r] + 16 * hi0[r] + 152; }
+  // tile (0,1): entry (row, 16 + j) mirrors (16 + j, row)
+  __device__ __forceinline__ int u01(int r) const {
+    return (16 + j_) * (17 + j_) / 2 + row<T>(g_, r);
+  }
+  __device__ __forceinline__ Blk<T> load(const T *P) const {
+    Blk<T> b;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      b.t[0][0][r] = P[d0[r]];
+      b.t[1][1][r] = P[d1(r)];
+      b.t[1][0][r] = P[r10[r]];
+      b.t[0][1][r] = P[u01(r)];
+    }
+    return b;
+  }
+  __device__ __forceinline__ void store(T *P, const Blk<T> &b) const {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      P[r10[r]] = b.t[1][0][r];
+      if (diag_lower & (1u << r)) {
+        P[d0[r]] = b.t[0][0][r];
+        P[d1(r)] = b.t[1][1][r];
+      }
+    }
+  }
+};
+
+// In-place inverse of a symmetric positive definite 32x32 block held as
+// O32(A): the symmetric Gauss-Jordan sweep of frag16.h over 32 pivots.
+// Column k is broadcast through 32 entries of LDS (`col`, private to this
+// wavefront): the lanes holding column k store tile row I's four entries at
+// col[16 I + 4 g ..], so row i sits at col[16 (i / 16) + pos(i % 16)].
+// Pivots of tile kt are swept with kt a compile-time constant so that every
+// register choice is static; row k and column k are cleared under the lane
+// masks that own them, then one FMA per entry applies
+//     a_ij <- a_ij - u_i (u_j / d),  u = column k with u_k = -1.
+template <int kt, typename T>
+__device__ __forceinline__ bool gj_tile(Blk<T> &a, T *col, int g, int j, f16::PivotLog &pl) {
+  bool bad = false;
+  const int pj = Mfma<T>::pos(j);
+#pragma unroll 1
+  for (int kq = 0; kq < 4; ++kq) {
+    double dq[4];
+    const bool own = g == kq;  // this lane group holds the pivot rows of this quad
+#pragma unroll
+    for (int kr = 0; kr < 4; ++kr) {
+      const int kl = Mfma<T>::row(kq, kr);  // pivot row inside tile kt
+      const bool colk = j == kl;            // this lane holds column k
+      if (colk) {
+        *reinterpret_cast<Frag<T> *>(col + 4 * g) = a.t[0][kt];
+        *reinterpret_cast<Frag<T> *>(col + 16 + 4 * g) = a.t[1][kt];
+        a.t[0][kt] = f16::zero<T>();
+        a.t[1][kt] = f16::zero<T>();
+      }
+      __syncthreads();
+      const T d = col[16 * kt + 4 * kq + kr];
+      Frag<T> ci0 = *reinterpret_cast<const Frag<T> *>(col + 4 * g);
+      Frag<T> ci1 = *reinterpret_cast<const Frag<T> *>(col + 16 + 4 * g);
+      T cj0 = col[pj], cj1 = col[16 + pj];
+      __syncthreads();
+      bad |= !(d > T(0));
+      dq[kr] = static_cast<double>(d);
+      const T inv = f16::rcp<T>(d);
+      if (own) {  // row k: cleared, and u_k = -1
+        a.t[kt][0][kr] = T(0);
+        a.t[kt][1][kr] = T(0);
+        if (kt == 0)
+          ci0[kr] = T(-1);
+        else
+          ci1[kr] = T(-1);
+      }
+      if (colk) {
+        if (kt == 0)
+          cj0 = T(-1);
+        else
+          cj1 = T(-1);
+      }
+      const T s0 = cj0 * inv, s1 = cj1 * inv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        a.t[0][0][r] -= ci0[r] * s0;
+        a.t[0][1][r] -= ci0[r] * s1;
+        a.t[1][0][r] -= ci1[r] * s0;
+        a.t[1][1][r] -= ci1[r] * s1;
+      }
+    }
+    pl.mul4(dq[0], dq[1], dq[2], dq[3]);
+  }
+  return bad;
+}
+
+// Returns true if some pivot is not > 0.
+template <typename T>
+__device__ __forceinline__ bool gj_inverse(Blk<T> &a, T *col, int g, int j,
+                                           f16::PivotLog &pl) {
+  bool bad = gj_tile<0>(a, col, g, j, pl);
+  bad |= gj_tile<1>(a, col, g, j, pl);
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J) a.t[I][J] = -a.t[I][J];
+  return bad;
+}
+
+}  // namespace f32t
+}  // namespace selinv

@@ -331,6 +331,7 @@ hipError_t chain_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T 
 }
 
 size_t star_workspace_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b) {
+  if (b == 32) return star32_workspace_bytes(dtype_bytes, B, K);
   const size_t nl = static_cast<size_t>(B) * K, bb = static_cast<size_t>(b) * b;
   return align_up(3 * nl * bb * dtype_bytes) + align_up(nl * sizeof(double)) +
          align_up(nl * sizeof(int32_t)) + align_up(B * sizeof(int32_t));
@@ -341,6 +342,9 @@ hipError_t star_launch(int64_t B, int64_t K, int32_t b, const T *center, const T
                        const T *coupling, T *G_center, T *G_leaf, T *G_cross, double *logdet,
                        int32_t *info, void *ws, hipStream_t s) {
   if (B == 0) return hipSuccess;
+  if (b == 32)
+    return star32_launch<T>(B, K, center, leaves, coupling, G_center, G_leaf, G_cross, logdet,
+                            info, ws, s);
   const size_t nl = static_cast<size_t>(B) * K, bb = static_cast<size_t>(b) * b;
   Carve cv(ws);
   T *st = cv.take<T>(3 * nl * bb);

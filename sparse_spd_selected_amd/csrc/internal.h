@@ -71,6 +71,12 @@ hipError_t chain_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T 
 
 // ----------------------------------------------------------------- star
 size_t star_workspace_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b);
+// b = 32: wavefront per 16 leaves on the matrix cores (star_b32.hip)
+size_t star32_workspace_bytes(int dtype_bytes, int64_t B, int64_t K);
+template <typename T>
+hipError_t star32_launch(int64_t B, int64_t K, const T *center, const T *leaves, const T *coupling,
+                         T *G_center, T *G_leaf, T *G_cross, double *logdet, int32_t *info,
+                         void *ws, hipStream_t s);
 template <typename T>
 hipError_t star_launch(int64_t B, int64_t K, int32_t b, const T *center, const T *leaves,
                        const T *coupling, T *G_center, T *G_leaf, T *G_cross, double *logdet,

@@ -1,0 +1,215 @@
+// star_b32.hip -- block-arrowhead selected inverse for 32x32 blocks on the
+// matrix cores (gabp-sparse-inv 0.3.2 page, "Implemented and tested
+// kernels", item Star: one centre coupled to K leaves, no leaf-leaf coupling,
+// leaves eliminated in parallel).  With F_j = coupling[j] = A_{j,0} the
+// centre is every leaf's parent and E_j = A_{0,j} = F_j^T:
+//
+//   collect (per leaf):  Dinv_j = D_j^{-1},  Z_j = Dinv_j F_j,
+//                        M_j = E_j Dinv_j E_j^T = F_j^T Z_j
+//   centre:              S_0 = A_00 - sum_j M_j,  G_00 = S_0^{-1}
+//   distribute (per leaf): X_j = E_j Dinv_j = F_j^T Dinv_j,  V = G_00 X_j,
+//                        G_cross[j] = G_{j,0} = -V^T,  G_leaf[j] = Dinv_j + X_j^T V
+//
+// Three launches.  A wavefront owns LPW consecutive leaves of one matrix and
+// sums their messages in its MFMA accumulators, so the centre reduction reads
+// ceil(K / LPW) partial blocks per matrix, in a fixed order (deterministic).
+// Only the packed lower triangle of Dinv_j (528 entries) crosses from collect
+// to distribute; F_j is re-read.
+#include <climits>
+
+#include "frag32.h"
+#include "internal.h"
+
+namespace selinv {
+
+namespace {
+
+using f32t::Blk;
+constexpr int kLPW = 16;  // leaves per wavefront
+constexpr int BB = 1024, PB = f32t::kPacked32;
+
+template <typename T>
+__device__ __forceinline__ void store_sym(T *P, const Blk<T> &b, int g, int j) {
+  // symmetric result with tiles (0,0), (1,0), (1,1) formed: the (0,1) block is
+  // the transpose of the (1,0) block
+  f16::store_t(P, 32, b.t[0][0], g, j);
+  f16::store(P + 16 * 32, 32, b.t[1][0], g, j);
+  f16::store_t(P + 16, 32, b.t[1][0], g, j);
+  f16::store_t(P + 16 * 32 + 16, 32, b.t[1][1], g, j);
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void star32_collect(int K, int nw, const T *__restrict__ leaves,
+                                                     const T *__restrict__ coupling,
+                                                     T *__restrict__ st_dinv,
+                                                     T *__restrict__ st_mpart,
+                                                     double *__restrict__ st_ld,
+                                                     int32_t *__restrict__ st_fail) {
+  __shared__ __align__(32) T col[32];
+  const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
+  const int64_t m = blockIdx.x / nw;
+  const int w = blockIdx.x % nw;
+  const int j0 = w * kLPW, j1 = min(j0 + kLPW, K);
+  const T *Dm = leaves + m * K * BB;
+  const T *Fm = coupling + m * K * BB;
+  T *dinv = st_dinv + m * K * PB;
+  const f32t::SymOffsets<T> so(g, j);
+  const f32t::PackedOffsets<T> po(g, j);
+
+  Blk<T> Macc = f32t::zero<T>();
+  double ld = 0.0;
+  int32_t first_bad = 0;
+  Blk<T> S0 = so.load(Dm + j0 * BB), S1 = f32t::zero<T>();
+  auto leaf = [&](int jj, Blk<T> &S, Blk<T> &Snext) -> bool {
+    if (jj >= j1) return true;
+    // loads for this leaf's coupling and the next leaf's diagonal (clamped)
+    const Blk<T> Fo = f32t::load(Fm + jj * BB, g, j);
+    Snext = so.load(Dm + min(jj + 1, j1 - 1) * BB);
+    f16::PivotLog pl;
+    if (f32t::gj_inverse(S, col, g, j, pl) && !first_bad) first_bad = jj + 1;
+    ld += pl.log();
+    po.store(dinv + jj * PB, S);
+    const Blk<T> Z = f32t::mm(S, Fo, f32t::zero<T>());  // Dinv_j F_j
+    Macc = f32t::mm_lower(Fo, Z, Macc);                  // += F_j^T Z_j
+    return false;
+  };
+  for (int jj = j0;; jj += 2) {
+    if (leaf(jj, S0, S1)) break;
+    if (leaf(jj + 1, S1, S0)) break;
+  }
+  store_sym(st_mpart + (m * nw + w) * BB, Macc, g, j);
+  if (lane == 0) {
+    st_ld[m * nw + w] = ld;
+    st_fail[m * nw + w] = first_bad;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void star32_center(int nw, const T *__restrict__ center,
+                                                    const T *__restrict__ st_mpart,
+                                                    const double *__restrict__ st_ld,
+                                                    const int32_t *__restrict__ st_fail,
+                                                    T *__restrict__ G_center,
+                                                    double *__restrict__ logdet,
+                                                    int32_t *__restrict__ info,
+                                                    int32_t *__restrict__ mat_fail) {
+  __shared__ __align__(32) T col[32];
+  const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
+  const int64_t m = blockIdx.x;
+  const f32t::SymOffsets<T> so(g, j);
+  Blk<T> S = so.load(center + m * BB);
+  int32_t fail = 0;
+  double ld = 0.0;
+  for (int w = 0; w < nw; ++w) {  // fixed order: leaves ascending
+    S = f32t::sub(S, so.load(st_mpart + (m * nw + w) * BB));
+    if (!fail && st_fail[m * nw + w]) fail = st_fail[m * nw + w] - 1 + 2;  // leaf j -> j+2
+    ld += st_ld[m * nw + w];
+  }
+  f16::PivotLog pl;
+  const bool bad = f32t::gj_inverse(S, col, g, j, pl);
+  if (!fail && bad) fail = 1;
+  if (fail) {
+    S = f32t::zero<T>();
+#pragma unroll
+    for (int I = 0; I < 2; ++I)
+#pragma unroll
+      for (int J = 0; J < 2; ++J)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S.t[I][J][r] = static_cast<T>(__builtin_nan(""));
+  }
+  f32t::store_t(G_center + m * BB, S, g, j);
+  if (lane == 0) {
+    logdet[m] = fail ? __builtin_nan("") : ld + pl.log();
+    if (info) info[m] = fail;
+    mat_fail[m] = fail;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void star32_distribute(int K, int nw, const T *__restrict__ coupling,
+                                                        const T *__restrict__ G_center,
+                                                        const T *__restrict__ st_dinv,
+                                                        const int32_t *__restrict__ mat_fail,
+                                                        T *__restrict__ G_leaf,
+                                                        T *__restrict__ G_cross) {
+  const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
+  const int64_t m = blockIdx.x / nw;
+  const int w = blockIdx.x % nw;
+  const int j0 = w * kLPW, j1 = min(j0 + kLPW, K);
+  const T *Fm = coupling + m * K * BB;
+  const T *dinv = st_dinv + m * K * PB;
+  T *Glm = G_leaf + m * K * BB;
+  T *Gxm = G_cross + m * K * BB;
+  if (mat_fail[m]) {
+    const T nan = static_cast<T>(__builtin_nan(""));
+    for (int64_t e = static_cast<int64_t>(j0) * BB + lane; e < static_cast<int64_t>(j1) * BB;
+         e += 64) {
+      Glm[e] = nan;
+      Gxm[e] = nan;
+    }
+    return;
+  }
+  const f32t::PackedOffsets<T> po(g, j);
+  const Blk<T> G = f32t::load(G_center + m * BB, g, j);
+  Blk<T> P0 = po.load(dinv + j0 * PB), P1 = f32t::zero<T>();
+  Blk<T> F0 = f32t::load(Fm + j0 * BB, g, j), F1 = f32t::zero<T>();
+  auto leaf = [&](int jj, const Blk<T> &Di, const Blk<T> &Fo, Blk<T> &Dn, Blk<T> &Fn) -> bool {
+    if (jj >= j1) return true;
+    const int jn = min(jj + 1, j1 - 1);
+    Dn = po.load(dinv + jn * PB);
+    Fn = f32t::load(Fm + jn * BB, g, j);
+    const Blk<T> X = f32t::mm(Fo, Di, f32t::zero<T>());  // F_j^T Dinv_j
+    const Blk<T> V = f32t::mm(G, X, f32t::zero<T>());    // G_00 X_j = -G_{0,j}
+    f32t::store_t(Gxm + jj * BB, f32t::neg(V), g, j);    // G_{j,0} = -V^T
+    const Blk<T> Gl = f32t::mm_lower(X, V, Di);          // Dinv_j + X_j^T V
+    store_sym(Glm + jj * BB, Gl, g, j);
+    return false;
+  };
+  for (int jj = j0;; jj += 2) {
+    if (leaf(jj, P0, F0, P1, F1)) break;
+    if (leaf(jj + 1, P1, F1, P0, F0)) break;
+  }
+}
+
+}  // namespace
+
+size_t star32_workspace_bytes(int dtype_bytes, int64_t B, int64_t K) {
+  const size_t nw = (K + kLPW - 1) / kLPW;
+  return align_up(static_cast<size_t>(B) * K * PB * dtype_bytes) +
+         align_up(static_cast<size_t>(B) * nw * BB * dtype_bytes) +
+         align_up(static_cast<size_t>(B) * nw * sizeof(double)) +
+         align_up(static_cast<size_t>(B) * nw * sizeof(int32_t)) +
+         align_up(static_cast<size_t>(B) * sizeof(int32_t));
+}
+
+template <typename T>
+hipError_t star32_launch(int64_t B, int64_t K, const T *center, const T *leaves, const T *coupling,
+                         T *G_center, T *G_leaf, T *G_cross, double *logdet, int32_t *info,
+                         void *ws, hipStream_t s) {
+  const int nw = static_cast<int>((K + kLPW - 1) / kLPW);
+  Carve cv(ws);
+  T *dinv = cv.take<T>(static_cast<size_t>(B) * K * PB);
+  T *mpart = cv.take<T>(static_cast<size_t>(B) * nw * BB);
+  double *ldp = cv.take<double>(static_cast<size_t>(B) * nw);
+  int32_t *failp = cv.take<int32_t>(static_cast<size_t>(B) * nw);
+  int32_t *matfail = cv.take<int32_t>(B);
+  if (nw > 0)
+    hipLaunchKernelGGL(star32_collect<T>, dim3(static_cast<unsigned>(B * nw)), dim3(64), 0, s,
+                       static_cast<int>(K), nw, leaves, coupling, dinv, mpart, ldp, failp);
+  hipLaunchKernelGGL(star32_center<T>, dim3(static_cast<unsigned>(B)), dim3(64), 0, s, nw, center,
+                     mpart, ldp, failp, G_center, logdet, info, matfail);
+  if (nw > 0)
+    hipLaunchKernelGGL(star32_distribute<T>, dim3(static_cast<unsigned>(B * nw)), dim3(64), 0, s,
+                       static_cast<int>(K), nw, coupling, G_center, dinv, matfail, G_leaf,
+                       G_cross);
+  return hipGetLastError();
+}
+
+template hipError_t star32_launch<float>(int64_t, int64_t, const float *, const float *,
+                                         const float *, float *, float *, float *, double *,
+                                         int32_t *, void *, hipStream_t);
+template hipError_t star32_launch<double>(int64_t, int64_t, const double *, const double *,
+                                          const double *, double *, double *, double *, double *,
+                                          int32_t *, void *, hipStream_t);
+
+}  // namespace selinv
