@@ -24,6 +24,7 @@ SOURCES = [
     "generic.hip",
     "chain_b16.hip",
     "star_b32.hip",
+    "chain_b32.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -166,6 +166,16 @@ __device__ __forceinline__ void store_t(T *P, int ld, Frag<T> f, int g, int j) {
   }
 }
 
+// Orders LDS accesses between the lanes of one wavefront (a wavefront
+// executes its LDS instructions in order, so a compiler-level barrier with
+// wavefront-scope fences is enough; no workgroup barrier is involved, so
+// wavefronts of one workgroup may call it different numbers of times).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <typename T>
 __device__ __forceinline__ T rcp(T d);
 
@@ -225,11 +235,11 @@ __device__ __forceinline__ bool gj_inverse(Frag<T> &a, T *col, int g, int j, Piv
       // pivot k = row(kq, kr): the element of lane group kq, register kr
       const int k = Mfma<T>::row(kq, kr);
       if (j == k) *reinterpret_cast<Frag<T> *>(col + 4 * g) = a;
-      __syncthreads();
+      wave_sync();
       const T d = col[4 * kq + kr];
       Frag<T> ci = *reinterpret_cast<const Frag<T> *>(col + 4 * g);
       T cj = col[pj];
-      __syncthreads();
+      wave_sync();
       bad |= !(d > T(0));
       dq[kr] = static_cast<double>(d);
       const T inv = rcp<T>(d);

@@ -227,12 +227,12 @@ __device__ __forceinline__ bool gj_tile(Blk<T> &a, T *col, int g, int j, f16::Pi
         a.t[0][kt] = f16::zero<T>();
         a.t[1][kt] = f16::zero<T>();
       }
-      __syncthreads();
+      f16::wave_sync();
       const T d = col[16 * kt + 4 * kq + kr];
       Frag<T> ci0 = *reinterpret_cast<const Frag<T> *>(col + 4 * g);
       Frag<T> ci1 = *reinterpret_cast<const Frag<T> *>(col + 16 + 4 * g);
       T cj0 = col[pj], cj1 = col[16 + pj];
-      __syncthreads();
+      f16::wave_sync();
       bad |= !(d > T(0));
       dq[kr] = static_cast<double>(d);
       const T inv = f16::rcp<T>(d);

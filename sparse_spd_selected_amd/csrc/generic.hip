@@ -323,6 +323,7 @@ hipError_t chain_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T 
                         T *G_lower, double *logdet, int32_t *info, void *ws, hipStream_t s) {
   if (B == 0) return hipSuccess;
   if (b == 16) return chain16_launch<T>(B, L, diag, lower, G_diag, G_lower, logdet, info, ws, s);
+  if (b == 32) return chain32_launch<T>(B, L, diag, lower, G_diag, G_lower, logdet, info, ws, s);
   const int nt = threads_for(b);
   const size_t shm = (6 * b * b + b) * sizeof(T);
   hipLaunchKernelGGL(chain_generic<T>, dim3(static_cast<unsigned>(B)), dim3(nt), shm, s, L, b,

@@ -65,6 +65,11 @@ size_t chain_workspace_bytes(int dtype_bytes, int64_t B, int64_t L, int32_t b);
 template <typename T>
 hipError_t chain16_launch(int64_t B, int64_t L, const T *diag, const T *lower, T *G_diag,
                           T *G_lower, double *logdet, int32_t *info, void *ws, hipStream_t s);
+// b = 32: two-sided sweep, one workgroup of two wavefronts per chain (chain_b32.hip)
+size_t chain32_workspace_bytes(int dtype_bytes, int64_t B, int64_t L);
+template <typename T>
+hipError_t chain32_launch(int64_t B, int64_t L, const T *diag, const T *lower, T *G_diag,
+                          T *G_lower, double *logdet, int32_t *info, void *ws, hipStream_t s);
 template <typename T>
 hipError_t chain_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower, T *G_diag,
                         T *G_lower, double *logdet, int32_t *info, void *ws, hipStream_t s);
