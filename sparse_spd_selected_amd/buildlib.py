@@ -25,6 +25,8 @@ SOURCES = [
     "chain_b16.hip",
     "star_b32.hip",
     "chain_b32.hip",
+    "tree_b8.hip",
+    "chain_small.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -126,6 +126,10 @@ void chain16_kernel(int L, const T *__restrict__ diag, const T *__restrict__ low
 
 }  // namespace
 
+size_t chain16_workspace_bytes(int dtype_bytes, int64_t B, int64_t L) {
+  return align_up(static_cast<size_t>(B) * L * f16::kPacked16 * dtype_bytes);
+}
+
 template <typename T>
 hipError_t chain16_launch(int64_t B, int64_t L, const T *diag, const T *lower, T *G_diag,
                           T *G_lower, double *logdet, int32_t *info, void *ws, hipStream_t s) {

@@ -315,6 +315,9 @@ __global__ void init_int(int32_t *p, int32_t v) { *p = v; }
 // ------------------------------------------------------------ launchers
 
 size_t chain_workspace_bytes(int dtype_bytes, int64_t B, int64_t L, int32_t b) {
+  if (b <= 8) return chain_small_workspace_bytes(dtype_bytes, B, L);
+  if (b == 16) return chain16_workspace_bytes(dtype_bytes, B, L);
+  if (b == 32) return chain32_workspace_bytes(dtype_bytes, B, L);
   return align_up(static_cast<size_t>(B) * L * 2 * b * b * dtype_bytes);
 }
 
@@ -322,6 +325,8 @@ template <typename T>
 hipError_t chain_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower, T *G_diag,
                         T *G_lower, double *logdet, int32_t *info, void *ws, hipStream_t s) {
   if (B == 0) return hipSuccess;
+  if (b <= 8)
+    return chain_small_launch<T>(B, L, b, diag, lower, G_diag, G_lower, logdet, info, ws, s);
   if (b == 16) return chain16_launch<T>(B, L, diag, lower, G_diag, G_lower, logdet, info, ws, s);
   if (b == 32) return chain32_launch<T>(B, L, diag, lower, G_diag, G_lower, logdet, info, ws, s);
   const int nt = threads_for(b);
@@ -369,6 +374,7 @@ hipError_t star_launch(int64_t B, int64_t K, int32_t b, const T *center, const T
 }
 
 size_t tree_workspace_bytes(const selinv_tree_plan *plan) {
+  if (plan->b <= 8) return tree8_workspace_bytes(plan);
   const size_t n = plan->n, bb = static_cast<size_t>(plan->b) * plan->b;
   return align_up(3 * n * bb * plan->dtype_bytes) + align_up(n * sizeof(double)) +
          align_up(n * sizeof(int32_t)) + align_up(sizeof(int32_t));
@@ -377,6 +383,7 @@ size_t tree_workspace_bytes(const selinv_tree_plan *plan) {
 template <typename T>
 hipError_t tree_launch(const selinv_tree_plan *plan, const T *diag, const T *edge, T *G_diag,
                        T *G_edge, double *logdet, int32_t *info, void *ws, hipStream_t s) {
+  if (plan->b <= 8) return tree8_launch<T>(plan, diag, edge, G_diag, G_edge, logdet, info, ws, s);
   const size_t n = plan->n;
   const int b = plan->b;
   const size_t bb = static_cast<size_t>(b) * b;

@@ -61,7 +61,14 @@ namespace selinv {
 
 // ---------------------------------------------------------------- chain
 size_t chain_workspace_bytes(int dtype_bytes, int64_t B, int64_t L, int32_t b);
+// b <= 8: eight chains per wavefront, one block row per lane (chain_small.hip)
+size_t chain_small_workspace_bytes(int dtype_bytes, int64_t B, int64_t L);
+template <typename T>
+hipError_t chain_small_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower,
+                              T *G_diag, T *G_lower, double *logdet, int32_t *info, void *ws,
+                              hipStream_t s);
 // b = 16: one wavefront per chain on the matrix cores (chain_b16.hip)
+size_t chain16_workspace_bytes(int dtype_bytes, int64_t B, int64_t L);
 template <typename T>
 hipError_t chain16_launch(int64_t B, int64_t L, const T *diag, const T *lower, T *G_diag,
                           T *G_lower, double *logdet, int32_t *info, void *ws, hipStream_t s);
@@ -89,6 +96,11 @@ hipError_t star_launch(int64_t B, int64_t K, int32_t b, const T *center, const T
 
 // ----------------------------------------------------------------- tree
 size_t tree_workspace_bytes(const selinv_tree_plan *plan);
+// b <= 8: one block row per lane, eight nodes per wavefront (tree_b8.hip)
+size_t tree8_workspace_bytes(const selinv_tree_plan *plan);
+template <typename T>
+hipError_t tree8_launch(const selinv_tree_plan *plan, const T *diag, const T *edge, T *G_diag,
+                        T *G_edge, double *logdet, int32_t *info, void *ws, hipStream_t s);
 template <typename T>
 hipError_t tree_launch(const selinv_tree_plan *plan, const T *diag, const T *edge, T *G_diag,
                        T *G_edge, double *logdet, int32_t *info, void *ws, hipStream_t s);

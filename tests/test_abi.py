@@ -50,7 +50,8 @@ def test_strerror_and_version(lib):
 
 
 def test_workspace_sizes(lib):
-    assert lib.selinv_chain_workspace_bytes(8, 4096, 64, 16) >= 4096 * 64 * 2 * 256 * 8
+    assert lib.selinv_chain_workspace_bytes(8, 4096, 64, 16) >= 4096 * 64 * 136 * 8
+    assert lib.selinv_chain_workspace_bytes(8, 3, 5, 4) >= 3 * 5 * 64 * 8  # padded 8x8 state
     assert lib.selinv_chain_workspace_bytes(3, 1, 1, 1) == 0  # bad dtype size
     assert lib.selinv_chain_workspace_bytes(8, 1, 1, 33) == 0  # b > 32
     assert lib.selinv_star_workspace_bytes(4, 2, 0, 4) > 0
