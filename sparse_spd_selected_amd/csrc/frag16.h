@@ -230,11 +230,16 @@ __device__ __forceinline__ bool gj_inverse(Frag<T> &a, T *col, int g, int j, Piv
 #pragma unroll 1
   for (int kq = 0; kq < 4; ++kq) {
     double dq[4];
+    const bool own = g == kq;  // this lane group holds the quad's pivot rows
 #pragma unroll
     for (int kr = 0; kr < 4; ++kr) {
       // pivot k = row(kq, kr): the element of lane group kq, register kr
       const int k = Mfma<T>::row(kq, kr);
-      if (j == k) *reinterpret_cast<Frag<T> *>(col + 4 * g) = a;
+      const bool colk = j == k;  // this lane holds column k
+      if (colk) {  // broadcast column k, then clear it (its new value is u_i u_k / d)
+        *reinterpret_cast<Frag<T> *>(col + 4 * g) = a;
+        a = zero<T>();
+      }
       wave_sync();
       const T d = col[4 * kq + kr];
       Frag<T> ci = *reinterpret_cast<const Frag<T> *>(col + 4 * g);
@@ -243,15 +248,13 @@ __device__ __forceinline__ bool gj_inverse(Frag<T> &a, T *col, int g, int j, Piv
       bad |= !(d > T(0));
       dq[kr] = static_cast<double>(d);
       const T inv = rcp<T>(d);
-      const bool own = g == kq;  // this lane group holds row k in register kr
-      if (own) ci[kr] = T(-1);
-      if (j == k) cj = T(-1);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool z = (j == k) || (own && r == kr);
-        const T t = ci[r] * inv;
-        a[r] = (z ? T(0) : a[r]) - t * cj;
+      if (own) {  // row k: cleared, and u_k = -1
+        a[kr] = T(0);
+        ci[kr] = T(-1);
       }
+      const T sj = (colk ? T(-1) : cj) * inv;  // u_j / d
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] -= ci[r] * sj;
     }
     pl.mul4(dq[0], dq[1], dq[2], dq[3]);
   }
