@@ -28,6 +28,35 @@ FP64_PEAK_TFLOPS = 78.6
 FP32_PEAK_TFLOPS = 157.3
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP library sources; counter-derived traffic is reported
+    only when it was measured on exactly these sources."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_spd_selected_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, dtname):
+    """HBM bytes per call from FETCH_SIZE / WRITE_SIZE counter runs (scaled by
+    the plain-copy calibration), or None when absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get("%s/%s" % (workload, dtname))
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_call")
+
+
 def nominal_flops(kind, cfg):
     b = cfg["b"]
     if kind == "chain":
@@ -213,7 +242,8 @@ def main():
         "flop_frac_of_peak": round(gflops / (peak_t * 1e3), 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes": nbytes},
+                     "traffic": measured_traffic(args.workload, dtname),
+                     "algorithmic_bytes": nbytes, "kernel_source_hash": kernel_source_hash()},
     }
     if not args.no_second_dtype and len(dtypes) > 1 and args.dtype is None:
         other = dtypes[1]
