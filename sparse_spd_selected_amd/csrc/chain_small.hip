@@ -40,15 +40,21 @@ __global__ __launch_bounds__(256) void chain_small_kernel(
   double ld = 0.0;
   int32_t fail = 0;
   r8::Row<T> S = r8::load_sym(D, b, i);
-  for (int k = 0; k < L; ++k) {
-    // inputs of the next step, in flight during this sweep (clamped in range)
-    const r8::Row<T> Ck = r8::load(C + min(k, max(L - 2, 0)) * bb, b, i);
-    const r8::Row<T> Dn = r8::load_sym(D + min(k + 1, L - 1) * bb, b, i);
+  // Collect.  C_k and D_{k+1} are loaded one step ahead; two register sets
+  // alternate (loop unrolled by two, clamped in-range indices) so that no
+  // register copy waits on a load in flight.
+  const int lc = max(L - 2, 0);
+  r8::Row<T> C0 = r8::load(C, b, i), D0 = r8::load_sym(D + min(1, L - 1) * bb, b, i);
+  r8::Row<T> C1, D1;
+  auto collect = [&](int k, const r8::Row<T> &Ck, const r8::Row<T> &Dn, r8::Row<T> &Cn,
+                     r8::Row<T> &Dnn) -> bool {
+    Cn = r8::load(C + min(k + 1, lc) * bb, b, i);
+    Dnn = r8::load_sym(D + min(k + 2, L - 1) * bb, b, i);
     f16::PivotLog pl;
     const bool bad = r8::gj_inverse(S, sa, s, i, pl);
     if (bad && !fail) fail = k + 1;
     ld += pl.log();
-    if (k == L - 1) break;
+    if (k == L - 1) return true;
     if (valid) r8::store8(st + k * 64, i, S);
     f16::wave_sync();
     sa.put(s, i, S);
@@ -58,6 +64,11 @@ __global__ __launch_bounds__(256) void chain_small_kernel(
     const r8::Row<T> M = r8::mul_t(X, sb, s, r8::zero<T>());  // X C_k^T
 #pragma unroll
     for (int c = 0; c < 8; ++c) S.v[c] = Dn.v[c] - M.v[c];
+    return false;
+  };
+  for (int k = 0;; k += 2) {
+    if (collect(k, C0, D0, C1, D1)) break;
+    if (collect(k + 1, C1, D1, C0, D0)) break;
   }
   if (fail) {
     if (valid) {
@@ -75,9 +86,15 @@ __global__ __launch_bounds__(256) void chain_small_kernel(
   }
   r8::Row<T> G = S;  // G_{L-1} = Sinv_{L-1}
   if (valid) r8::store(Gd + (L - 1) * bb, b, i, G);
-  for (int k = L - 2; k >= 0; --k) {
-    const r8::Row<T> Si = r8::load8(st + k * 64, i);
-    const r8::Row<T> Ck = r8::load(C + k * bb, b, i);
+  // Distribute, with Sinv and C of the next block in flight.
+  r8::Row<T> S0 = r8::load8(st + lc * 64, i), S1;
+  C0 = r8::load(C + lc * bb, b, i);
+  auto distribute = [&](int k, const r8::Row<T> &Si, const r8::Row<T> &Ck, r8::Row<T> &Sn,
+                        r8::Row<T> &Cn) -> bool {
+    if (k < 0) return true;
+    const int kn = max(k - 1, 0);
+    Sn = r8::load8(st + kn * 64, i);
+    Cn = r8::load(C + kn * bb, b, i);
     f16::wave_sync();
     sa.put(s, i, Si);
     f16::wave_sync();
@@ -93,6 +110,11 @@ __global__ __launch_bounds__(256) void chain_small_kernel(
       r8::store(Gl + k * bb, b, i, r8::neg(V));
       r8::store(Gd + k * bb, b, i, G);
     }
+    return false;
+  };
+  for (int k = L - 2;; k -= 2) {
+    if (distribute(k, S0, C0, S1, C1)) break;
+    if (distribute(k - 1, S1, C1, S0, C0)) break;
   }
   if (valid && i == 0) {
     logdet[m] = ld;

@@ -35,6 +35,7 @@ struct Carve {
 //   fail_rank[pos]  rank of the node in the order (depth descending, index
 //                   ascending) used to name the first failing pivot
 //   rank_node[r]    node index of rank r
+//   parent_node[pos] node index of the parent (saves a dependent lookup)
 struct TreePlanDev {
   int32_t *node_at = nullptr;
   int32_t *parent_pos = nullptr;
@@ -42,6 +43,7 @@ struct TreePlanDev {
   int32_t *child_end = nullptr;
   int32_t *fail_rank = nullptr;
   int32_t *rank_node = nullptr;
+  int32_t *parent_node = nullptr;  // node index of the parent of position p (-1 at the root)
 };
 
 }  // namespace selinv

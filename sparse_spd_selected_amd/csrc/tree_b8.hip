@@ -49,11 +49,24 @@ __global__ __launch_bounds__(256) void tree8_collect(
   }
   r8::Row<T> S = valid ? r8::load_sym(diag + v * bb, b, i) : r8::load_sym(diag, 0, i);
   bool child_failed = false;
-  for (int32_t c = cb; c < ce; ++c) {
-    const r8::Row<T> mc = r8::load8(st_m + static_cast<int64_t>(c) * 64, i);
+  // children's messages, four loads in flight at a time, subtracted in child order
+  for (int32_t c0 = cb; c0 < ce; c0 += 4) {
+    r8::Row<T> mc[4];
+    int32_t fc[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) S.v[k] -= mc.v[k];
-    child_failed |= st_fail[c] != 0;
+    for (int q = 0; q < 4; ++q) {
+      const int32_t c = min(c0 + q, ce - 1);
+      mc[q] = r8::load8(st_m + static_cast<int64_t>(c) * 64, i);
+      fc[q] = st_fail[c];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (c0 + q < ce) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) S.v[k] -= mc[q].v[k];
+        child_failed |= fc[q] != 0;
+      }
+    }
   }
   f16::PivotLog pl;
   const bool bad = r8::gj_inverse(S, sa, s, i, pl);
@@ -83,7 +96,7 @@ __global__ __launch_bounds__(256) void tree8_collect(
 template <typename T>
 __global__ __launch_bounds__(256) void tree8_distribute(
     int64_t p0, int64_t p1, int b, const int32_t *__restrict__ node_at,
-    const int32_t *__restrict__ parent_pos, const T *__restrict__ edge,
+    const int32_t *__restrict__ parent_node, const T *__restrict__ edge,
     const T *__restrict__ st_sinv, const int32_t *__restrict__ first_fail, T *__restrict__ G_diag,
     T *__restrict__ G_edge) {
   __shared__ __align__(32) T lds[kWaves][2][kSlots * 64];
@@ -97,7 +110,7 @@ __global__ __launch_bounds__(256) void tree8_distribute(
   int64_t v = 0, u = 0;
   if (valid) {
     v = node_at[p];
-    u = node_at[parent_pos[p]];
+    u = parent_node[p];
   }
   const r8::Row<T> Si = valid ? r8::load8(st_sinv + p * 64, i) : r8::zero<T>();
   const r8::Row<T> E = valid ? r8::load(edge + v * bb, b, i) : r8::zero<T>();
@@ -198,7 +211,7 @@ hipError_t tree8_launch(const selinv_tree_plan *plan, const T *diag, const T *ed
     const int64_t p0 = plan->level_off[lev], p1 = plan->level_off[lev + 1];
     const unsigned grid = static_cast<unsigned>((p1 - p0 + per_block - 1) / per_block);
     hipLaunchKernelGGL(tree8_distribute<T>, dim3(grid), dim3(256), 0, s, p0, p1, b, d.node_at,
-                       d.parent_pos, edge, st_sinv, first_fail, G_diag, G_edge);
+                       d.parent_node, edge, st_sinv, first_fail, G_diag, G_edge);
   }
   const int64_t chunk = (n + kFinishGroups - 1) / kFinishGroups;
   hipLaunchKernelGGL(tree8_ld_partial, dim3(kFinishGroups), dim3(1024), 0, s, n, chunk, st_ld,

@@ -114,8 +114,11 @@ extern "C" int selinv_tree_plan_create(const int32_t *parent_host, int64_t n, in
       rank_node[r] = static_cast<int32_t>(v);
     }
   }
-  std::vector<int32_t> fail_rank(n);
-  for (int64_t p = 0; p < n; ++p) fail_rank[p] = rank_of[node_at[p]];
+  std::vector<int32_t> fail_rank(n), parent_node(n);
+  for (int64_t p = 0; p < n; ++p) {
+    fail_rank[p] = rank_of[node_at[p]];
+    parent_node[p] = parent_host[node_at[p]];
+  }
 
   selinv_tree_plan *plan = new (std::nothrow) selinv_tree_plan();
   if (!plan) return SELINV_ERR_HIP;
@@ -132,7 +135,7 @@ extern "C" int selinv_tree_plan_create(const int32_t *parent_host, int64_t n, in
   plan->level_off[0] = 0;
   for (int32_t d = 0; d <= H; ++d) plan->level_off[d + 1] = plan->level_off[d] + level_count[d];
 
-  const size_t bytes = 6 * selinv::align_up(n * sizeof(int32_t));
+  const size_t bytes = 7 * selinv::align_up(n * sizeof(int32_t));
   if (hipMalloc(&plan->dev_block, bytes) != hipSuccess) {
     delete[] plan->level_off;
     delete plan;
@@ -146,13 +149,15 @@ extern "C" int selinv_tree_plan_create(const int32_t *parent_host, int64_t n, in
   dv.child_end = cv.take<int32_t>(n);
   dv.fail_rank = cv.take<int32_t>(n);
   dv.rank_node = cv.take<int32_t>(n);
+  dv.parent_node = cv.take<int32_t>(n);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t nb = n * sizeof(int32_t);
   hipError_t e = hipSuccess;
   const std::pair<int32_t *, const int32_t *> copies[] = {
       {dv.node_at, node_at.data()},     {dv.parent_pos, parent_pos.data()},
       {dv.child_beg, child_beg.data()}, {dv.child_end, child_end.data()},
-      {dv.fail_rank, fail_rank.data()}, {dv.rank_node, rank_node.data()}};
+      {dv.fail_rank, fail_rank.data()}, {dv.rank_node, rank_node.data()},
+      {dv.parent_node, parent_node.data()}};
   for (const auto &c : copies)
     if (e == hipSuccess) e = hipMemcpyAsync(c.first, c.second, nb, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
