@@ -18,11 +18,15 @@
  *   device), except `parent_host` of selinv_tree_plan_create.  The caller owns
  *   all memory; the library never allocates per call.  Scratch memory comes in
  *   through `workspace` (size from the matching *_workspace_bytes query; NULL
- *   is allowed when that size is 0).  The workspace must be 256-byte aligned
- *   and must not be used by another call that is still running.
+ *   is allowed when that size is 0).  The workspace must not be used by
+ *   another call that is still running.
  * - Blocks are b x b, row-major, contiguous; batches are contiguous
  *   ("leading batch dimensions", Quickstart section).  Outputs must not alias
  *   inputs or each other.
+ * - Every block array must be 16-byte aligned (allocator pointers are; a view
+ *   into a larger array is when its byte offset is a multiple of 16), and the
+ *   workspace 256-byte aligned; otherwise the call returns
+ *   SELINV_ERR_INVALID_ARG.
  * - Only the lower triangle of each diagonal input block is read (they are
  *   taken to be symmetric).  Diagonal output blocks are written in full and
  *   are symmetric.

@@ -119,7 +119,10 @@ def _check_tensor(t, name, device, dtype):
         raise ValueError("%s must be on a GPU device (got %s)" % (name, t.device))
     if t.device != device or t.dtype != dtype:
         raise ValueError("%s: device/dtype mismatch" % name)
-    return t.contiguous()
+    t = t.contiguous()
+    if t.data_ptr() % 16:  # the library takes 16-byte aligned block arrays
+        t = t.clone()
+    return t
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor:

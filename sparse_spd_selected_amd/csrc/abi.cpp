@@ -9,6 +9,11 @@ namespace {
 
 inline bool bad_b(int32_t b) { return b < 1 || b > SELINV_MAX_B; }
 
+// block arrays: 16-byte aligned (null passes; required pointers are checked
+// separately); workspace: 256-byte aligned
+inline bool misaligned(const void *p) { return reinterpret_cast<uintptr_t>(p) & 15; }
+inline bool misaligned_ws(const void *p) { return reinterpret_cast<uintptr_t>(p) & 255; }
+
 template <typename T>
 int chain_entry(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower, T *G_diag,
                 T *G_lower, double *logdet, int32_t *info, void *ws, size_t ws_bytes,
@@ -17,8 +22,10 @@ int chain_entry(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower, 
   if (B == 0) return SELINV_OK;
   if (!diag || !G_diag || !logdet) return SELINV_ERR_INVALID_ARG;
   if (L > 1 && (!lower || !G_lower)) return SELINV_ERR_INVALID_ARG;
+  if (misaligned(diag) || misaligned(G_diag) || (L > 1 && (misaligned(lower) || misaligned(G_lower))))
+    return SELINV_ERR_INVALID_ARG;
   const size_t need = selinv::chain_workspace_bytes(sizeof(T), B, L, b);
-  if (ws_bytes < need || (need && !ws)) return SELINV_ERR_INVALID_ARG;
+  if (ws_bytes < need || (need && !ws) || misaligned_ws(ws)) return SELINV_ERR_INVALID_ARG;
   const hipError_t e = selinv::chain_launch<T>(B, L, b, diag, lower, G_diag, G_lower, logdet,
                                                info, ws, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
@@ -33,8 +40,12 @@ int star_entry(int64_t B, int64_t K, int32_t b, const T *center, const T *leaves
   if (B == 0) return SELINV_OK;
   if (!center || !G_center || !logdet) return SELINV_ERR_INVALID_ARG;
   if (K > 0 && (!leaves || !coupling || !G_leaf || !G_cross)) return SELINV_ERR_INVALID_ARG;
+  if (misaligned(center) || misaligned(G_center) ||
+      (K > 0 && (misaligned(leaves) || misaligned(coupling) || misaligned(G_leaf) ||
+                 misaligned(G_cross))))
+    return SELINV_ERR_INVALID_ARG;
   const size_t need = selinv::star_workspace_bytes(sizeof(T), B, K, b);
-  if (ws_bytes < need || (need && !ws)) return SELINV_ERR_INVALID_ARG;
+  if (ws_bytes < need || (need && !ws) || misaligned_ws(ws)) return SELINV_ERR_INVALID_ARG;
   const hipError_t e =
       selinv::star_launch<T>(B, K, b, center, leaves, coupling, G_center, G_leaf, G_cross,
                              logdet, info, ws, static_cast<hipStream_t>(stream));
@@ -46,8 +57,10 @@ int tree_entry(const selinv_tree_plan *plan, const T *diag, const T *edge, T *G_
                double *logdet, int32_t *info, void *ws, size_t ws_bytes, void *stream) {
   if (!plan || plan->dtype_bytes != static_cast<int>(sizeof(T))) return SELINV_ERR_INVALID_ARG;
   if (!diag || !edge || !G_diag || !G_edge || !logdet) return SELINV_ERR_INVALID_ARG;
+  if (misaligned(diag) || misaligned(edge) || misaligned(G_diag) || misaligned(G_edge))
+    return SELINV_ERR_INVALID_ARG;
   const size_t need = selinv::tree_workspace_bytes(plan);
-  if (ws_bytes < need || (need && !ws)) return SELINV_ERR_INVALID_ARG;
+  if (ws_bytes < need || (need && !ws) || misaligned_ws(ws)) return SELINV_ERR_INVALID_ARG;
   const hipError_t e = selinv::tree_launch<T>(plan, diag, edge, G_diag, G_edge, logdet, info, ws,
                                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;

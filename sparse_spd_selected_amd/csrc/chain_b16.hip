@@ -13,10 +13,16 @@
 // with C_i = lower[i] = A_{i+1,i}.  Only Sinv_i crosses from the collect to
 // the distribute pass (workspace: its packed lower triangle, 136 entries per
 // block); C_i is re-read.
-// Every product has its left factor available as O(A^T): C_i is loaded
-// transposed (one 16/32-byte vector per lane), and Sinv_i, G are symmetric.
+//
+// Every global access is a 16-byte-per-lane vector over consecutive bytes
+// (io16.h): blocks arrive in natural order one step ahead of their use and
+// are permuted into fragments in a per-wavefront LDS tile; results leave the
+// same way.  C_i is read from its tile transposed, giving O(C_i^T), the form
+// in which it enters the products as the left factor (Sinv_i and G are
+// symmetric, so O(X) = O(X^T) for those).
 #include "frag16.h"
 #include "internal.h"
+#include "io16.h"
 
 namespace selinv {
 
@@ -33,8 +39,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SELINV_CHAIN
 void chain16_kernel(int L, const T *__restrict__ diag, const T *__restrict__ lower,
                     T *__restrict__ G_diag, T *__restrict__ G_lower, double *__restrict__ logdet,
                     int32_t *__restrict__ info, T *__restrict__ state) {
+  using Tr = io16::Traits<T>;
   constexpr int BB = 256, PB = f16::kPacked16;
-  __shared__ __align__(32) T col[16];
+  __shared__ __align__(16) T col[16];
+  __shared__ __align__(16) T tA[Tr::kTile];
+  __shared__ __align__(16) T tB[Tr::kTile];
+  __shared__ __align__(16) T tP[PB];
   const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
   const int64_t m = blockIdx.x;
   const T *D = diag + m * L * BB;
@@ -44,28 +54,29 @@ void chain16_kernel(int L, const T *__restrict__ diag, const T *__restrict__ low
   T *Gd = G_diag + m * L * BB;
   T *Gl = G_lower + m * (L - 1) * BB;
   T *st = state + m * L * PB;
-  const f16::SymOffsets<T> so(16, g, j);
-  const f16::PackedOffsets<T> po(g, j);
+  const io16::SymLanes<T> sl(g, j, lane);
 
   double ld = 0.0;
   int32_t fail = 0;
-  Frag<T> S = so.load(D);
+  Frag<T> S;
+  {
+    const io16::Nat<T> d0 = io16::load(D, lane);
+    io16::put(tA, lane, d0);
+    f16::wave_sync();
+    S = sl.get_sym(tA);
+    f16::wave_sync();
+  }
   // Collect.  The inputs of the next block (C_{i+1}, D_{i+2}) are loaded
   // while block i is swept; two register sets alternate (the loop is
-  // unrolled by two) so that no copy of an in-flight register forces an
-  // early wait on the load counter.
-  Frag<T> C0 = f16::zero<T>(), D0 = f16::zero<T>(), C1 = f16::zero<T>(), D1 = f16::zero<T>();
-  if (L > 1) {
-    C0 = f16::load_t(C, 16, g, j);
-    D0 = so.load(D + BB);
-  }
-  // The prefetch is unconditional (block indices clamped into range) so that
-  // no register merge forces a wait on loads still in flight.
-  auto collect = [&](int i, const Frag<T> &Cu, const Frag<T> &Du, Frag<T> &Cn,
-                     Frag<T> &Dn) -> bool {
-    const int ic = min(i + 1, max(L - 2, 0)), id = min(i + 2, L - 1);
-    Cn = f16::load_t(C + ic * BB, 16, g, j);
-    Dn = so.load(D + id * BB);
+  // unrolled by two) and the block indices are clamped into range, so that
+  // no register copy or merge forces an early wait on loads in flight.
+  const int lc = max(L - 2, 0);
+  io16::Nat<T> C0 = io16::load(C, lane), D0 = io16::load(D + min(1, L - 1) * BB, lane);
+  io16::Nat<T> C1, D1;
+  auto collect = [&](int i, const io16::Nat<T> &Cu, const io16::Nat<T> &Du, io16::Nat<T> &Cn,
+                     io16::Nat<T> &Dn) -> bool {
+    Cn = io16::load(C + min(i + 1, lc) * BB, lane);
+    Dn = io16::load(D + min(i + 2, L - 1) * BB, lane);
     f16::PivotLog pl;
     if (f16::gj_inverse(S, col, g, j, pl)) {
       fail = i + 1;
@@ -73,9 +84,20 @@ void chain16_kernel(int L, const T *__restrict__ diag, const T *__restrict__ low
     }
     ld += pl.log();
     if (i == L - 1) return true;
-    po.store(st + i * PB, S);
-    const Frag<T> Y = f16::mm<T>(S, Cu, f16::zero<T>());  // Sinv_i C_i^T
-    S = Du - f16::mm<T>(Cu, Y, f16::zero<T>());           // D_{i+1} - C_i Sinv_i C_i^T
+    // Sinv_i -> packed triangle in the workspace; C_i, D_{i+1} -> fragments
+    f16::wave_sync();
+    io16::put_frag(tA, g, j, S);
+    io16::put(tB, lane, Cu);
+    f16::wave_sync();
+    const io16::Nat<T> pk = sl.gather_packed(tA);
+    const Frag<T> Ct = io16::get_frag_t(tB, g, j);  // O(C_i^T)
+    f16::wave_sync();
+    io16::put(tA, lane, Du);
+    io16::store_packed(st + i * PB, lane, pk);
+    f16::wave_sync();
+    const Frag<T> Dn1 = sl.get_sym(tA);
+    const Frag<T> Y = f16::mm<T>(S, Ct, f16::zero<T>());  // Sinv_i C_i^T
+    S = Dn1 - f16::mm<T>(Ct, Y, f16::zero<T>());          // D_{i+1} - C_i Sinv_i C_i^T
     return false;
   };
   for (int i = 0;; i += 2) {
@@ -93,25 +115,35 @@ void chain16_kernel(int L, const T *__restrict__ diag, const T *__restrict__ low
     return;
   }
   Frag<T> G = S;  // G_{L-1,L-1} = Sinv_{L-1}
-  f16::store_t(Gd + (L - 1) * BB, 16, G, g, j);
+  f16::wave_sync();
+  io16::put_frag(tA, g, j, G);
+  f16::wave_sync();
+  io16::store(Gd + (L - 1) * BB, lane, io16::get(tA, lane));
   // Distribute, with the packed Sinv and C of the next block in flight (same
   // alternating register sets).
-  Frag<T> S0 = f16::zero<T>(), S1 = f16::zero<T>();
-  if (L > 1) {
-    S0 = po.load(st + (L - 2) * PB);
-    C0 = f16::load_t(C + (L - 2) * BB, 16, g, j);
-  }
-  auto distribute = [&](int i, const Frag<T> &Si, const Frag<T> &Ci, Frag<T> &Sn,
-                        Frag<T> &Cn) -> bool {
+  io16::Nat<T> S0 = io16::load_packed(st + lc * PB, lane), S1;
+  C0 = io16::load(C + lc * BB, lane);
+  auto distribute = [&](int i, const io16::Nat<T> &Sp, const io16::Nat<T> &Cu, io16::Nat<T> &Sn,
+                        io16::Nat<T> &Cn) -> bool {
     if (i < 0) return true;
     const int in = max(i - 1, 0);
-    Sn = po.load(st + in * PB);
-    Cn = f16::load_t(C + in * BB, 16, g, j);
-    const Frag<T> X = f16::mm<T>(Ci, Si, f16::zero<T>());  // C_i Sinv_i
+    Sn = io16::load_packed(st + in * PB, lane);
+    Cn = io16::load(C + in * BB, lane);
+    f16::wave_sync();
+    io16::put_packed(tP, lane, Sp);
+    io16::put(tB, lane, Cu);
+    f16::wave_sync();
+    const Frag<T> Si = sl.get_packed(tP);
+    const Frag<T> Ct = io16::get_frag_t(tB, g, j);        // O(C_i^T)
+    const Frag<T> X = f16::mm<T>(Ct, Si, f16::zero<T>());  // C_i Sinv_i
     const Frag<T> V = f16::mm<T>(G, X, f16::zero<T>());    // G_{i+1} X
-    f16::store(Gl + i * BB, 16, -V, g, j);                 // G_{i+1,i}
     G = f16::mm<T>(X, V, Si);                              // Sinv_i + X^T V
-    f16::store_t(Gd + i * BB, 16, G, g, j);
+    f16::wave_sync();
+    io16::put_frag(tA, g, j, -V);
+    io16::put_frag(tB, g, j, G);
+    f16::wave_sync();
+    io16::store(Gl + i * BB, lane, io16::get(tA, lane));  // G_{i+1,i}
+    io16::store(Gd + i * BB, lane, io16::get(tB, lane));
     return false;
   };
   for (int i = L - 2;; i -= 2) {

@@ -59,7 +59,8 @@ def test_workspace_sizes(lib):
 
 
 def _chain_call(lib, B=1, L=2, b=4, diag=1, lower=1, gd=1, gl=1, ld=1, ws=1, wsb=1 << 30):
-    p = lambda x: ctypes.c_void_p(0x1000) if x else None  # never dereferenced on error paths
+    # never dereferenced on error paths; an int above 1 is taken as the address
+    p = lambda x: ctypes.c_void_p(x if x > 1 else 0x1000) if x else None
     return lib.selinv_chain_f64(B, L, b, p(diag), p(lower), p(gd), p(gl), p(ld), None, p(ws),
                                 wsb, None)
 
@@ -75,6 +76,10 @@ def test_chain_argument_validation(lib):
     assert _chain_call(lib, wsb=16) == ssa.INVALID_ARG
     assert _chain_call(lib, ws=0) == ssa.INVALID_ARG
     assert _chain_call(lib, B=0) == ssa.OK  # empty batch: nothing to do
+    # block arrays must be 16-byte aligned, the workspace 256-byte aligned
+    assert _chain_call(lib, b=16, diag=0x1008) == ssa.INVALID_ARG
+    assert _chain_call(lib, b=3, gl=0x1004) == ssa.INVALID_ARG
+    assert _chain_call(lib, ws=0x1010) == ssa.INVALID_ARG
 
 
 def test_star_argument_validation(lib):
@@ -84,6 +89,9 @@ def test_star_argument_validation(lib):
     assert lib.selinv_star_f32(1, 2, 4, p, None, p, p, p, p, p, None, p, 1 << 30, None) == \
         ssa.INVALID_ARG
     assert lib.selinv_star_f32(1, 2, 4, p, p, p, p, p, p, p, None, p, 8, None) == ssa.INVALID_ARG
+    q = ctypes.c_void_p(0x1004)
+    assert lib.selinv_star_f32(1, 2, 4, p, q, p, p, p, p, p, None, p, 1 << 30, None) == \
+        ssa.INVALID_ARG
 
 
 @pytest.mark.parametrize("parent", [[-1, 0, -1], [0, 0, 1], [-1, 2, 3, 1], [-1, 0, 7],
