@@ -56,7 +56,7 @@ void chain16_kernel(int L, const T *__restrict__ diag, const T *__restrict__ low
   T *st = state + m * L * PB;
   const io16::SymLanes<T> sl(g, j, lane);
 
-  double ld = 0.0;
+  f16::PivotLog pl;  // product of all pivots of the chain (log taken once)
   int32_t fail = 0;
   Frag<T> S;
   {
@@ -69,21 +69,18 @@ void chain16_kernel(int L, const T *__restrict__ diag, const T *__restrict__ low
   // Collect.  The inputs of the next block (C_{i+1}, D_{i+2}) are loaded
   // while block i is swept; two register sets alternate (the loop is
   // unrolled by two) and the block indices are clamped into range, so that
-  // no register copy or merge forces an early wait on loads in flight.
+  // no register copy or merge forces an early wait on loads in flight.  The
+  // loops have a single exit: a failed pivot is recorded and the sweep runs
+  // on (its output is discarded), which keeps the waits on the prefetched
+  // registers exact.
   const int lc = max(L - 2, 0);
   io16::Nat<T> C0 = io16::load(C, lane), D0 = io16::load(D + min(1, L - 1) * BB, lane);
   io16::Nat<T> C1, D1;
   auto collect = [&](int i, const io16::Nat<T> &Cu, const io16::Nat<T> &Du, io16::Nat<T> &Cn,
-                     io16::Nat<T> &Dn) -> bool {
+                     io16::Nat<T> &Dn) {
     Cn = io16::load(C + min(i + 1, lc) * BB, lane);
     Dn = io16::load(D + min(i + 2, L - 1) * BB, lane);
-    f16::PivotLog pl;
-    if (f16::gj_inverse(S, col, g, j, pl)) {
-      fail = i + 1;
-      return true;
-    }
-    ld += pl.log();
-    if (i == L - 1) return true;
+    if (f16::gj_inverse(S, col, g, j, pl) && !fail) fail = i + 1;
     // Sinv_i -> packed triangle in the workspace; C_i, D_{i+1} -> fragments
     f16::wave_sync();
     io16::put_frag(tA, g, j, S);
@@ -98,12 +95,14 @@ void chain16_kernel(int L, const T *__restrict__ diag, const T *__restrict__ low
     const Frag<T> Dn1 = sl.get_sym(tA);
     const Frag<T> Y = f16::mm<T>(S, Ct, f16::zero<T>());  // Sinv_i C_i^T
     S = Dn1 - f16::mm<T>(Ct, Y, f16::zero<T>());          // D_{i+1} - C_i Sinv_i C_i^T
-    return false;
   };
-  for (int i = 0;; i += 2) {
-    if (collect(i, C0, D0, C1, D1)) break;
-    if (collect(i + 1, C1, D1, C0, D0)) break;
+  int i = 0;
+  for (; i + 1 < L - 1; i += 2) {
+    collect(i, C0, D0, C1, D1);
+    collect(i + 1, C1, D1, C0, D0);
   }
+  if (i < L - 1) collect(i, C0, D0, C1, D1);
+  if (f16::gj_inverse(S, col, g, j, pl) && !fail) fail = L;  // the root block
   if (fail) {
     const T nan = static_cast<T>(__builtin_nan(""));
     for (int64_t e = lane; e < static_cast<int64_t>(L) * BB; e += 64) Gd[e] = nan;
@@ -114,6 +113,7 @@ void chain16_kernel(int L, const T *__restrict__ diag, const T *__restrict__ low
     }
     return;
   }
+  const double ld = pl.log();
   Frag<T> G = S;  // G_{L-1,L-1} = Sinv_{L-1}
   f16::wave_sync();
   io16::put_frag(tA, g, j, G);
@@ -124,8 +124,7 @@ void chain16_kernel(int L, const T *__restrict__ diag, const T *__restrict__ low
   io16::Nat<T> S0 = io16::load_packed(st + lc * PB, lane), S1;
   C0 = io16::load(C + lc * BB, lane);
   auto distribute = [&](int i, const io16::Nat<T> &Sp, const io16::Nat<T> &Cu, io16::Nat<T> &Sn,
-                        io16::Nat<T> &Cn) -> bool {
-    if (i < 0) return true;
+                        io16::Nat<T> &Cn) {
     const int in = max(i - 1, 0);
     Sn = io16::load_packed(st + in * PB, lane);
     Cn = io16::load(C + in * BB, lane);
@@ -144,12 +143,13 @@ void chain16_kernel(int L, const T *__restrict__ diag, const T *__restrict__ low
     f16::wave_sync();
     io16::store(Gl + i * BB, lane, io16::get(tA, lane));  // G_{i+1,i}
     io16::store(Gd + i * BB, lane, io16::get(tB, lane));
-    return false;
   };
-  for (int i = L - 2;; i -= 2) {
-    if (distribute(i, S0, C0, S1, C1)) break;
-    if (distribute(i - 1, S1, C1, S0, C0)) break;
+  i = L - 2;
+  for (; i >= 1; i -= 2) {
+    distribute(i, S0, C0, S1, C1);
+    distribute(i - 1, S1, C1, S0, C0);
   }
+  if (i == 0) distribute(0, S0, C0, S1, C1);
   if (lane == 0) {
     logdet[m] = ld;
     if (info) info[m] = 0;
