@@ -242,19 +242,16 @@ __device__ __forceinline__ bool gj_inverse(Frag<T> &a, T *col, int g, int j, Piv
       }
       wave_sync();
       const T d = col[4 * kq + kr];
-      Frag<T> ci = *reinterpret_cast<const Frag<T> *>(col + 4 * g);
-      T cj = col[pj];
+      const Frag<T> ci = *reinterpret_cast<const Frag<T> *>(col + 4 * g);
+      const T cj = col[pj];
       wave_sync();
       bad |= !(d > T(0));
       dq[kr] = static_cast<double>(d);
       const T inv = rcp<T>(d);
-      if (own) {  // row k: cleared, and u_k = -1
-        a[kr] = T(0);
-        ci[kr] = T(-1);
-      }
       const T sj = (colk ? T(-1) : cj) * inv;  // u_j / d
 #pragma unroll
       for (int r = 0; r < 4; ++r) a[r] -= ci[r] * sj;
+      if (own) a[kr] = sj;  // row k: u_k = -1 on a cleared entry gives u_j / d
     }
     pl.mul4(dq[0], dq[1], dq[2], dq[3]);
   }

@@ -38,14 +38,17 @@ struct Nat {
   typename Traits<T>::vec c[Traits<T>::kChunks];
 };
 
-// Row-major 16x16 block (leading dimension 16) -> registers.
+// Row-major 16x16 block (leading dimension 16) -> registers.  Input and
+// output blocks are touched once per pass, so they are loaded and stored
+// non-temporally (streaming), which leaves the caches to the workspace.
 template <typename T>
 __device__ __forceinline__ Nat<T> load(const T *P, int lane) {
   using Tr = Traits<T>;
   Nat<T> n;
 #pragma unroll
   for (int c = 0; c < Tr::kChunks; ++c)
-    n.c[c] = *reinterpret_cast<const typename Tr::vec *>(P + Tr::kVec * (64 * c + lane));
+    n.c[c] = __builtin_nontemporal_load(
+        reinterpret_cast<const typename Tr::vec *>(P + Tr::kVec * (64 * c + lane)));
   return n;
 }
 
@@ -54,7 +57,8 @@ __device__ __forceinline__ void store(T *P, int lane, const Nat<T> &n) {
   using Tr = Traits<T>;
 #pragma unroll
   for (int c = 0; c < Tr::kChunks; ++c)
-    *reinterpret_cast<typename Tr::vec *>(P + Tr::kVec * (64 * c + lane)) = n.c[c];
+    __builtin_nontemporal_store(n.c[c],
+                                reinterpret_cast<typename Tr::vec *>(P + Tr::kVec * (64 * c + lane)));
 }
 
 // Tile position of natural vector v (16-byte aligned: kLd is a multiple of kVec).
