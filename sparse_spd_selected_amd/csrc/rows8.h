@@ -29,15 +29,6 @@ __device__ __forceinline__ Row<T> zero() {
   return r;
 }
 
-// Row i of a b x b row-major block (zero beyond b).
-template <typename T>
-__device__ __forceinline__ Row<T> load(const T *P, int b, int i) {
-  Row<T> r;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) r.v[k] = (i < b && k < b) ? P[i * b + k] : T(0);
-  return r;
-}
-
 // Row i of an 8 x 8 block stored densely (stride 8): two or four vector loads.
 template <typename T>
 __device__ __forceinline__ Row<T> load8(const T *P, int i) {
@@ -49,6 +40,22 @@ __device__ __forceinline__ Row<T> load8(const T *P, int i) {
   for (int k = 0; k < 4; ++k) {
     r.v[k] = a[k];
     r.v[4 + k] = c[k];
+  }
+  return r;
+}
+
+// Row i of a b x b row-major block (1 <= b <= 8; zero beyond b).  b == 8 takes vector
+// loads; otherwise every lane loads from clamped in-range addresses and
+// padding is selected afterwards (no divergent loads).
+template <typename T>
+__device__ __forceinline__ Row<T> load(const T *P, int b, int i) {
+  if (b == 8) return load8(P, i);
+  Row<T> r;
+  const int ic = min(i, b - 1);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const T x = P[ic * b + min(k, b - 1)];
+    r.v[k] = (i < b && k < b) ? x : T(0);
   }
   return r;
 }
@@ -67,16 +74,16 @@ __device__ __forceinline__ void store8(T *P, int i, const Row<T> &r) {
 }
 
 // Row i of a symmetric b x b block read from its lower triangle, identity
-// padded beyond b.
+// padded beyond b (clamped in-range addresses, padding selected afterwards).
 template <typename T>
 __device__ __forceinline__ Row<T> load_sym(const T *P, int b, int i) {
   Row<T> r;
+  const int ic = min(i, b - 1);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    if (i < b && k < b)
-      r.v[k] = k <= i ? P[i * b + k] : P[k * b + i];
-    else
-      r.v[k] = (k == i) ? T(1) : T(0);
+    const int kc = min(k, b - 1);
+    const T x = P[k <= i ? ic * b + kc : kc * b + ic];
+    r.v[k] = (i < b && k < b) ? x : ((k == i) ? T(1) : T(0));
   }
   return r;
 }
@@ -84,6 +91,18 @@ __device__ __forceinline__ Row<T> load_sym(const T *P, int b, int i) {
 // Store the first b entries of row i (rows i >= b are padding: skipped).
 template <typename T>
 __device__ __forceinline__ void store(T *P, int b, int i, const Row<T> &r) {
+  if (b == 8) {
+    typedef T v4 __attribute__((ext_vector_type(4)));
+    v4 a, c;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a[k] = r.v[k];
+      c[k] = r.v[4 + k];
+    }
+    *reinterpret_cast<v4 *>(P + i * 8) = a;
+    *reinterpret_cast<v4 *>(P + i * 8 + 4) = c;
+    return;
+  }
   if (i >= b) return;
 #pragma unroll
   for (int k = 0; k < 8; ++k)

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void tree8_collect(
     cb = child_beg[p];
     ce = child_end[p];
   }
-  r8::Row<T> S = valid ? r8::load_sym(diag + v * bb, b, i) : r8::load_sym(diag, 0, i);
+  r8::Row<T> S = r8::load_sym(diag + v * bb, b, i);  // slots past the level re-read node 0
   bool child_failed = false;
   // children's messages, four loads in flight at a time, subtracted in child order
   for (int32_t c0 = cb; c0 < ce; c0 += 4) {
