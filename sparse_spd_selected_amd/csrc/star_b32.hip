@@ -19,6 +19,7 @@
 
 #include "frag32.h"
 #include "internal.h"
+#include "io32.h"
 
 namespace selinv {
 
@@ -39,13 +40,14 @@ __device__ __forceinline__ void store_sym(T *P, const Blk<T> &b, int g, int j) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void star32_collect(int K, int nw, const T *__restrict__ leaves,
-                                                     const T *__restrict__ coupling,
-                                                     T *__restrict__ st_dinv,
-                                                     T *__restrict__ st_mpart,
-                                                     double *__restrict__ st_ld,
-                                                     int32_t *__restrict__ st_fail) {
-  __shared__ __align__(32) T col[32];
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void star32_collect(
+    int K, int nw, const T *__restrict__ leaves, const T *__restrict__ coupling,
+    T *__restrict__ st_dinv, T *__restrict__ st_mpart, double *__restrict__ st_ld,
+    int32_t *__restrict__ st_fail) {
+  using Tr = io32::Traits<T>;
+  __shared__ __align__(16) T col[32];
+  __shared__ __align__(16) T tA[Tr::kTile];
+  __shared__ __align__(16) T tB[Tr::kTile];
   const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
   const int64_t m = blockIdx.x / nw;
   const int w = blockIdx.x % nw;
@@ -53,33 +55,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   const T *Dm = leaves + m * K * BB;
   const T *Fm = coupling + m * K * BB;
   T *dinv = st_dinv + m * K * PB;
-  const f32t::SymOffsets<T> so(g, j);
-  const f32t::PackedOffsets<T> po(g, j);
+  const io32::SymLanes<T> sl(g, j, lane);
 
   Blk<T> Macc = f32t::zero<T>();
-  double ld = 0.0;
+  f16::PivotLog pl;  // product of all pivots of this wavefront's leaves
   int32_t first_bad = 0;
-  Blk<T> S0 = so.load(Dm + j0 * BB), S1 = f32t::zero<T>();
-  auto leaf = [&](int jj, Blk<T> &S, Blk<T> &Snext) -> bool {
-    if (jj >= j1) return true;
-    // loads for this leaf's coupling and the next leaf's diagonal (clamped)
-    const Blk<T> Fo = f32t::load(Fm + jj * BB, g, j);
-    Snext = so.load(Dm + min(jj + 1, j1 - 1) * BB);
-    f16::PivotLog pl;
+  Blk<T> S;
+  {
+    const io32::Nat<T> d0 = io32::load(Dm + j0 * BB, lane);
+    io32::put(tA, lane, d0);
+    f16::wave_sync();
+    S = sl.get_sym(tA);
+  }
+  // Per leaf: this leaf's coupling and the next leaf's diagonal block are
+  // loaded first and consumed after the sweep (single-exit loop).
+  for (int jj = j0; jj < j1; ++jj) {
+    const io32::Nat<T> Fn = io32::load(Fm + jj * BB, lane);
+    const io32::Nat<T> Dn = io32::load(Dm + min(jj + 1, j1 - 1) * BB, lane);
     if (f32t::gj_inverse(S, col, g, j, pl) && !first_bad) first_bad = jj + 1;
-    ld += pl.log();
-    po.store(dinv + jj * PB, S);
+    f16::wave_sync();
+    io32::put_blk(tA, g, j, S);  // Dinv_j -> packed workspace triangle
+    io32::put(tB, lane, Fn);
+    f16::wave_sync();
+    const io32::NatP<T> pk = sl.gather_packed(tA);
+    const Blk<T> Fo = io32::get_blk(tB, g, j);  // O32(F_j)
+    f16::wave_sync();
+    io32::put(tA, lane, Dn);
+    io32::store_packed(dinv + jj * PB, lane, pk);
     const Blk<T> Z = f32t::mm(S, Fo, f32t::zero<T>());  // Dinv_j F_j
     Macc = f32t::mm_lower(Fo, Z, Macc);                  // += F_j^T Z_j
-    return false;
-  };
-  for (int jj = j0;; jj += 2) {
-    if (leaf(jj, S0, S1)) break;
-    if (leaf(jj + 1, S1, S0)) break;
+    f16::wave_sync();
+    S = sl.get_sym(tA);
   }
   store_sym(st_mpart + (m * nw + w) * BB, Macc, g, j);
   if (lane == 0) {
-    st_ld[m * nw + w] = ld;
+    st_ld[m * nw + w] = pl.log();
     st_fail[m * nw + w] = first_bad;
   }
 }
@@ -126,12 +136,13 @@ __global__ __launch_bounds__(64) void star32_center(int nw, const T *__restrict_
 }
 
 template <typename T>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void star32_distribute(int K, int nw, const T *__restrict__ coupling,
-                                                        const T *__restrict__ G_center,
-                                                        const T *__restrict__ st_dinv,
-                                                        const int32_t *__restrict__ mat_fail,
-                                                        T *__restrict__ G_leaf,
-                                                        T *__restrict__ G_cross) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void star32_distribute(
+    int K, int nw, const T *__restrict__ coupling, const T *__restrict__ G_center,
+    const T *__restrict__ st_dinv, const int32_t *__restrict__ mat_fail, T *__restrict__ G_leaf,
+    T *__restrict__ G_cross) {
+  using Tr = io32::Traits<T>;
+  __shared__ __align__(16) T tA[Tr::kTile];
+  __shared__ __align__(16) T tB[Tr::kTile];
   const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
   const int64_t m = blockIdx.x / nw;
   const int w = blockIdx.x % nw;
@@ -149,25 +160,37 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     }
     return;
   }
-  const f32t::PackedOffsets<T> po(g, j);
-  const Blk<T> G = f32t::load(G_center + m * BB, g, j);
-  Blk<T> P0 = po.load(dinv + j0 * PB), P1 = f32t::zero<T>();
-  Blk<T> F0 = f32t::load(Fm + j0 * BB, g, j), F1 = f32t::zero<T>();
-  auto leaf = [&](int jj, const Blk<T> &Di, const Blk<T> &Fo, Blk<T> &Dn, Blk<T> &Fn) -> bool {
-    if (jj >= j1) return true;
+  const io32::SymLanes<T> sl(g, j, lane);
+  Blk<T> G;
+  {
+    const io32::Nat<T> gc = io32::load(G_center + m * BB, lane);
+    io32::put(tA, lane, gc);
+    f16::wave_sync();
+    G = io32::get_blk(tA, g, j);
+  }
+  // The packed Dinv and the coupling of the next leaf are loaded into the
+  // registers just freed by staging the current leaf's in LDS.
+  io32::NatP<T> Pc = io32::load_packed(dinv + j0 * PB, lane);
+  io32::Nat<T> Fc = io32::load(Fm + j0 * BB, lane);
+  for (int jj = j0; jj < j1; ++jj) {
+    f16::wave_sync();
+    io32::put_packed(tA, lane, Pc);
+    io32::put(tB, lane, Fc);
     const int jn = min(jj + 1, j1 - 1);
-    Dn = po.load(dinv + jn * PB);
-    Fn = f32t::load(Fm + jn * BB, g, j);
+    Pc = io32::load_packed(dinv + jn * PB, lane);
+    Fc = io32::load(Fm + jn * BB, lane);
+    f16::wave_sync();
+    const Blk<T> Di = sl.get_packed(tA);
+    const Blk<T> Fo = io32::get_blk(tB, g, j);
     const Blk<T> X = f32t::mm(Fo, Di, f32t::zero<T>());  // F_j^T Dinv_j
     const Blk<T> V = f32t::mm(G, X, f32t::zero<T>());    // G_00 X_j = -G_{0,j}
-    f32t::store_t(Gxm + jj * BB, f32t::neg(V), g, j);    // G_{j,0} = -V^T
     const Blk<T> Gl = f32t::mm_lower(X, V, Di);          // Dinv_j + X_j^T V
-    store_sym(Glm + jj * BB, Gl, g, j);
-    return false;
-  };
-  for (int jj = j0;; jj += 2) {
-    if (leaf(jj, P0, F0, P1, F1)) break;
-    if (leaf(jj + 1, P1, F1, P0, F0)) break;
+    f16::wave_sync();
+    io32::put_blk_t(tA, g, j, f32t::neg(V));  // G_{j,0} = -V^T
+    io32::put_sym(tB, g, j, Gl);
+    f16::wave_sync();
+    io32::store(Gxm + jj * BB, lane, io32::get(tA, lane));
+    io32::store(Glm + jj * BB, lane, io32::get(tB, lane));
   }
 }
 
