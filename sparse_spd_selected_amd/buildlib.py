@@ -24,7 +24,7 @@ SOURCES = [
     "generic.hip",
     "chain_b16.hip",
     "star_b32.hip",
-    "chain_b32.hip",
+    "chain_b32.hip", "chain_b32_seg.hip",
     "tree_b8.hip",
     "chain_small.hip",
 ]

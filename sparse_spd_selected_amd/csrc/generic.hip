@@ -317,7 +317,11 @@ __global__ void init_int(int32_t *p, int32_t v) { *p = v; }
 size_t chain_workspace_bytes(int dtype_bytes, int64_t B, int64_t L, int32_t b) {
   if (b <= 8) return chain_small_workspace_bytes(dtype_bytes, B, L);
   if (b == 16) return chain16_workspace_bytes(dtype_bytes, B, L);
-  if (b == 32) return chain32_workspace_bytes(dtype_bytes, B, L);
+  if (b == 32) {
+    const int P = chain32_segments(B, L);
+    return P ? chain32_seg_workspace_bytes(dtype_bytes, B, L, P)
+             : chain32_workspace_bytes(dtype_bytes, B, L);
+  }
   return align_up(static_cast<size_t>(B) * L * 2 * b * b * dtype_bytes);
 }
 
@@ -328,7 +332,11 @@ hipError_t chain_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T 
   if (b <= 8)
     return chain_small_launch<T>(B, L, b, diag, lower, G_diag, G_lower, logdet, info, ws, s);
   if (b == 16) return chain16_launch<T>(B, L, diag, lower, G_diag, G_lower, logdet, info, ws, s);
-  if (b == 32) return chain32_launch<T>(B, L, diag, lower, G_diag, G_lower, logdet, info, ws, s);
+  if (b == 32) {
+    const int P = chain32_segments(B, L);
+    return P ? chain32_seg_launch<T>(B, L, P, diag, lower, G_diag, G_lower, logdet, info, ws, s)
+             : chain32_launch<T>(B, L, diag, lower, G_diag, G_lower, logdet, info, ws, s);
+  }
   const int nt = threads_for(b);
   const size_t shm = (6 * b * b + b) * sizeof(T);
   hipLaunchKernelGGL(chain_generic<T>, dim3(static_cast<unsigned>(B)), dim3(nt), shm, s, L, b,

@@ -79,6 +79,14 @@ size_t chain32_workspace_bytes(int dtype_bytes, int64_t B, int64_t L);
 template <typename T>
 hipError_t chain32_launch(int64_t B, int64_t L, const T *diag, const T *lower, T *G_diag,
                           T *G_lower, double *logdet, int32_t *info, void *ws, hipStream_t s);
+// b = 32 with few chains: segment-parallel elimination (chain_b32_seg.hip);
+// chain32_segments returns the number of segments per chain, 0 = not used
+int chain32_segments(int64_t B, int64_t L);
+size_t chain32_seg_workspace_bytes(int dtype_bytes, int64_t B, int64_t L, int P);
+template <typename T>
+hipError_t chain32_seg_launch(int64_t B, int64_t L, int P, const T *diag, const T *lower,
+                              T *G_diag, T *G_lower, double *logdet, int32_t *info, void *ws,
+                              hipStream_t s);
 template <typename T>
 hipError_t chain_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower, T *G_diag,
                         T *G_lower, double *logdet, int32_t *info, void *ws, hipStream_t s);

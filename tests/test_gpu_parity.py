@@ -126,6 +126,30 @@ def test_chain_workload_b32_long(ssa):
     assert worst < 1e-9, worst
 
 
+@pytest.mark.parametrize("dt", ["f64", "f32"])
+@pytest.mark.parametrize("B,L", [(1, 64), (2, 96), (3, 130), (5, 200)])
+def test_chain_b32_segments(ssa, B, L, dt):
+    """b = 32 with few chains runs the segment-parallel elimination (8 to 25
+    segments per chain here, segments of uneven length for L = 130)."""
+    run_chain(ssa, B, L, 32, DT[dt], seed=B * 100 + L, load=1.0)
+
+
+@pytest.mark.parametrize("k", [3, 7, 8, 12, 31, 63])
+def test_chain_b32_segments_not_pd_info(ssa, k):
+    """One bad block in a segment interior (3, 12), at a separator (7, 31,
+    63 with 8 segments of 8 blocks) or first in a segment (8): the reported
+    block is the bad one, as in the sequential order."""
+    d, l = spdgen.chain(3, 64, 32, seed=5, diag_load=1.0)
+    d[1, k] = -np.eye(32)
+    d[2, k, 0, 0] = np.nan
+    _, _, ld, info = ssa.chain(_to(d, torch.float64), _to(l, torch.float64), return_info=True)
+    torch.cuda.synchronize()
+    _, _, _, Oinfo = oracle.chain(d, l)
+    assert list(Oinfo) == [0, k + 1, k + 1]
+    assert list(info.cpu().numpy()) == [0, k + 1, k + 1]
+    assert np.isnan(ld.cpu().numpy()[1:]).all() and np.isfinite(float(ld[0]))
+
+
 @pytest.mark.parametrize("k", [0, 5, 7])
 def test_chain_not_pd_info(ssa, k):
     d, l = spdgen.chain(3, 8, 4, seed=0)
