@@ -103,13 +103,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       U = f32t::mm_lower(F, Y2, U);                       // += F_i^T Sinv F_i
       F = f32t::neg(f32t::mm(Ct, Y2, f32t::zero<T>()));   // -C_i Sinv F_i
     }
-    const Blk<T> Y1 = f32t::mm(S, Ct, f32t::zero<T>());   // Sinv C_i^T
-    S = f32t::sub(Dd, f32t::mm(Ct, Y1, f32t::zero<T>()));  // D_{i+1} - C_i Sinv C_i^T
+    const Blk<T> Y1 = f32t::mm(S, Ct, f32t::zero<T>());  // Sinv C_i^T
+    // D_{i+1} - C_i Sinv C_i^T; the (1,0) tile is not formed (the blocked
+    // inverse reads only the upper off-diagonal tile)
+    S = f32t::sub(Dd, f32t::mm_upper(Ct, Y1, f32t::zero<T>()));
   }
   // separator t_s: its partial Schur block, fill block and update of t
   const int64_t q = m * P + s;
   f16::wave_sync();
-  io32::put_blk(tA, g, j, S);
+  if (ts > a)
+    io32::put_sym_u(tA, g, j, S);
+  else
+    io32::put_blk(tA, g, j, S);
   f16::wave_sync();
   io32::store_ws(r_S + q * BB, lane, io32::get(tA, lane));
   if (left) {
@@ -216,23 +221,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       const Blk<T> X2 = f32t::mm(Fb, Si, f32t::zero<T>());   // F_i^T Sinv
       V1 = f32t::mm(Gtn, X2, V1);                            // + G_{i+1,t} X2
       const Blk<T> V2 = f32t::mm(Gnt, X1, f32t::mm(Gtt, X2, f32t::zero<T>()));
-      Gii = f32t::mm(X1, V1, f32t::mm(X2, V2, Si));          // Sinv + X1^T V1 + X2^T V2
+      // Sinv + X1^T V1 + X2^T V2, lower tiles (the result is symmetric)
+      Gii = f32t::mm_lower(X1, V1, f32t::mm_lower(X2, V2, Si));
       Gtn = f32t::neg(V2);                                   // O32(G_{t,i})
     } else {
-      Gii = f32t::mm(X1, V1, Si);                            // Sinv + X1^T V1
+      Gii = f32t::mm_lower(X1, V1, Si);                      // Sinv + X1^T V1
     }
     f16::wave_sync();
     io32::put_blk(tA, g, j, f32t::neg(V1));  // G_{i+1,i}
-    io32::put_blk(tB, g, j, Gii);
+    io32::put_sym(tB, g, j, Gii);
     if (left) io32::put_blk_t(tC, g, j, Gtn);  // G_{i,t} = G_{t,i}^T
     f16::wave_sync();
     io32::store(Gl + i * BB, lane, io32::get(tA, lane));
     io32::store(Gd + i * BB, lane, io32::get(tB, lane));
+    Gnn = io32::get_blk(tB, g, j);
     if (left) {
       Gnt = io32::get_blk(tC, g, j);
       if (i == a) io32::store(Gl + (a - 1) * BB, lane, io32::get(tC, lane));
     }
-    Gnn = Gii;
   }
 }
 

@@ -62,6 +62,20 @@ __device__ __forceinline__ Blk<T> mm_lower(const Blk<T> &At, const Blk<T> &Bf, B
   return acc;
 }
 
+// The other symmetric variant: tiles (0,0), (0,1) and (1,1) are formed and
+// (1,0) is left as acc.t[1][0] (for consumers such as the blocked inverse
+// below, which reads the upper off-diagonal tile only).
+template <typename T>
+__device__ __forceinline__ Blk<T> mm_upper(const Blk<T> &At, const Blk<T> &Bf, Blk<T> acc) {
+  acc.t[0][0] = f16::mm<T>(At.t[0][0], Bf.t[0][0], acc.t[0][0]);
+  acc.t[0][0] = f16::mm<T>(At.t[1][0], Bf.t[1][0], acc.t[0][0]);
+  acc.t[0][1] = f16::mm<T>(At.t[0][0], Bf.t[0][1], acc.t[0][1]);
+  acc.t[0][1] = f16::mm<T>(At.t[1][0], Bf.t[1][1], acc.t[0][1]);
+  acc.t[1][1] = f16::mm<T>(At.t[0][1], Bf.t[0][1], acc.t[1][1]);
+  acc.t[1][1] = f16::mm<T>(At.t[1][1], Bf.t[1][1], acc.t[1][1]);
+  return acc;
+}
+
 // O32(P^T) of a row-major 32x32 block
 template <typename T>
 __device__ __forceinline__ Blk<T> load_t(const T *P, int g, int x) {

@@ -177,6 +177,21 @@ __device__ __forceinline__ void put_sym(T *tile, int g, int j, const Blk<T> &b) 
   }
 }
 
+// Write a symmetric result of which only tiles (0,0), (0,1) and (1,1) are
+// formed: the (1,0) tile is the transpose of the (0,1) tile.
+template <typename T>
+__device__ __forceinline__ void put_sym_u(T *tile, int g, int j, const Blk<T> &b) {
+  constexpr int ld = Traits<T>::kLd;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int a = row<T>(g, r);
+    tile[a * ld + j] = b.t[0][0][r];
+    tile[(16 + a) * ld + 16 + j] = b.t[1][1][r];
+    tile[a * ld + 16 + j] = b.t[0][1][r];
+    tile[(16 + j) * ld + a] = b.t[0][1][r];
+  }
+}
+
 // Per-lane LDS offsets that are not affine in (g, j):
 //   dg[r]      element r of the diagonal tiles of O32(M) read from the lower
 //              triangle of a tile (tile (1,1) adds 16 (kLd + 1))
