@@ -188,8 +188,8 @@ def copy_probe(mib, steps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="chain_b16_batched")
     ap.add_argument("--dtype", default=None, help="f64 or f32 (default: the workload's first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
