@@ -40,7 +40,7 @@ __device__ __forceinline__ void store_sym(T *P, const Blk<T> &b, int g, int j) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void star32_collect(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void star32_collect(
     int K, int nw, const T *__restrict__ leaves, const T *__restrict__ coupling,
     T *__restrict__ st_dinv, T *__restrict__ st_mpart, double *__restrict__ st_ld,
     int32_t *__restrict__ st_fail) {
