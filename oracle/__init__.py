@@ -56,8 +56,10 @@ def load(path: str | None = None):
     lib.oracle_tree.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_tree_depths.argtypes = [i64, vp, vp]
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_tree_vjp.argtypes = [i64, i32, vp, vp, vp, vp, vp, ctypes.c_double, vp, vp]
+    lib.oracle_chain_vjp.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     for f in (lib.oracle_chain, lib.oracle_star, lib.oracle_tree, lib.oracle_tree_depths,
-              lib.oracle_num_threads):
+              lib.oracle_num_threads, lib.oracle_tree_vjp, lib.oracle_chain_vjp):
         f.restype = ctypes.c_int
     if path == _LIB:
         _lib = lib
@@ -150,3 +152,67 @@ def tree_depths(parent, lib=None):
     if rc:
         raise OracleError("invalid tree (status %d)" % rc)
     return d
+
+
+# ------------------------------------------------------------------ VJPs
+# Reverse mode of the collect / distribute passes ("Differentiable selected
+# inverse" section of the gabp-sparse-inv page: the analytic two-pass
+# backward).  Cotangents: gd_bar on each G_vv (only its symmetric part
+# matters), an edge cotangent on each G_{p,v}, ld_bar on log det A.  Returns
+# the cotangents of the inputs: symmetric d_bar (for symmetric perturbations
+# of the diagonal blocks) and the edge blocks' gradients.
+
+
+def tree_vjp(parent, diag, edge, gd_bar, ge_bar, ld_bar, lib=None):
+    """-> (d_bar [n,b,b], e_bar [n,b,b] with a zero root slot)."""
+    lib = lib or load()
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    diag, edge, gd_bar, ge_bar = _f64(diag), _f64(edge), _f64(gd_bar), _f64(ge_bar)
+    n, b = diag.shape[0], diag.shape[1]
+    assert edge.shape == diag.shape == gd_bar.shape == ge_bar.shape
+    db = np.empty_like(diag)
+    eb = np.empty_like(edge)
+    rc = lib.oracle_tree_vjp(n, b, _p(parent), _p(diag), _p(edge), _p(gd_bar), _p(ge_bar),
+                             float(ld_bar), _p(db), _p(eb))
+    if rc:
+        raise OracleError("oracle_tree_vjp status %d" % rc)
+    return db, eb
+
+
+def chain_vjp(diag, lower, gd_bar, gl_bar, ld_bar, lib=None):
+    """Chains as path trees rooted at their last block.
+    -> (d_bar [B,L,b,b], l_bar [B,L-1,b,b], status [B]: 0 or 3 = not PD)."""
+    lib = lib or load()
+    diag, lower, gd_bar, gl_bar = _f64(diag), _f64(lower), _f64(gd_bar), _f64(gl_bar)
+    B, L, b = diag.shape[0], diag.shape[1], diag.shape[2]
+    ld_bar = _f64(np.broadcast_to(np.asarray(ld_bar, dtype=np.float64), (B,)))
+    db = np.empty_like(diag)
+    lb = np.empty_like(lower)
+    st = np.empty(B, np.int32)
+    rc = lib.oracle_chain_vjp(B, L, b, _p(diag), _p(lower), _p(gd_bar), _p(gl_bar), _p(ld_bar),
+                              _p(db), _p(lb), _p(st))
+    if rc:
+        raise OracleError("oracle_chain_vjp status %d" % rc)
+    return db, lb, st
+
+
+def star_vjp(center, leaves, coupling, gc_bar, gl_bar, gx_bar, ld_bar, lib=None):
+    """Stars as depth-1 trees: centre = node 0 (root), leaf j = node j + 1 with
+    E_{j+1} = A_{0,j+1} = coupling[j]^T and G_cross[j] = G_{0,j+1}^T.
+    -> (c_bar [B,b,b], leaves_bar [B,K,b,b], coupling_bar [B,K,b,b])."""
+    center, leaves, coupling = _f64(center), _f64(leaves), _f64(coupling)
+    B, K, b = leaves.shape[0], leaves.shape[1], leaves.shape[2]
+    ld_bar = np.broadcast_to(np.asarray(ld_bar, dtype=np.float64), (B,))
+    parent = np.array([-1] + [0] * K, dtype=np.int32)
+    cb = np.empty_like(center)
+    lvb = np.empty_like(leaves)
+    cpb = np.empty_like(coupling)
+    for m in range(B):
+        diag = np.concatenate([center[m][None], leaves[m]])
+        edge = np.concatenate([np.zeros((1, b, b)), np.swapaxes(coupling[m], -1, -2)])
+        gd = np.concatenate([_f64(gc_bar)[m][None], _f64(gl_bar)[m]])
+        ge = np.concatenate([np.zeros((1, b, b)), np.swapaxes(_f64(gx_bar)[m], -1, -2)])
+        db, eb = tree_vjp(parent, diag, edge, gd, ge, ld_bar[m], lib=lib)
+        cb[m], lvb[m] = db[0], db[1:]
+        cpb[m] = np.swapaxes(eb[1:], -1, -2)
+    return cb, lvb, cpb

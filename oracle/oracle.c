@@ -415,6 +415,198 @@ ORACLE_API int oracle_tree(int64_t n, int b, const int32_t *parent, const double
   return 0;
 }
 
+/* ------------------------------------------------- vector-Jacobian product */
+
+/* Reverse mode of the two passes above (the pages' "analytic two-pass
+ * backward" of selinv_tree, section "Differentiable selected inverse"): given
+ * cotangents Gd_bar[v] on G_vv, Ge_bar[v] on G_{p,v} = G_edge[v] and ld_bar on
+ * log det A, return D_bar[v] and E_bar[v] with
+ *     dL = sum_v <D_bar[v], dD_v> + sum_{v != root} <E_bar[v], dE_v>
+ * for symmetric perturbations dD_v (D_bar is symmetric; the cotangent of G_vv
+ * enters through its symmetric part, G_vv being symmetric).  Each forward
+ * step is reversed in the opposite order:
+ *   forward collect     S_v = D_v - sum_c M_c, Sinv_v = S_v^-1,
+ *                       X_v = E_v Sinv_v, M_v = X_v E_v^T, logdet += ln det S_v
+ *   forward distribute  V_v = G_pp X_v, G_{p,v} = -V_v, G_vv = Sinv_v + X_v^T V_v
+ * Reverse distribute (deepest nodes first; GG_v = total cotangent of G_vv):
+ *   Sinv_bar_v += GG_v,  X_bar_v += V_v GG_v^T,  V_bar = X_v GG_v - Ge_bar_v,
+ *   GG_p += V_bar X_v^T, X_bar_v += G_pp^T V_bar;   root: Sinv_bar_r += GG_r.
+ * Reverse collect (root first; S_bar_p known when v is visited):
+ *   M_bar = -S_bar_p,  X_bar_v += M_bar E_v,  E_bar_v = M_bar^T X_v + X_bar_v Sinv_v^T,
+ *   Sinv_bar_v += E_v^T X_bar_v,
+ *   S_bar_v = -Sinv_v^T Sinv_bar_v Sinv_v^T + ld_bar Sinv_v^T,  D_bar_v = sym(S_bar_v).
+ * Returns 0, 2 for an invalid parent array, 3 if a pivot is not positive
+ * definite (outputs NaN). */
+static void mm_nn(int b, const double *P, const double *Q, double *Out) { matmul(b, P, Q, Out); }
+static void mm_nt(int b, const double *P, const double *Q, double *Out) { /* P Q^T */
+  for (int r = 0; r < b; ++r)
+    for (int c = 0; c < b; ++c) {
+      double s = 0.0;
+      for (int k = 0; k < b; ++k) s += P[r * b + k] * Q[c * b + k];
+      Out[r * b + c] = s;
+    }
+}
+static void mm_tn(int b, const double *P, const double *Q, double *Out) { matmul_tn(b, P, Q, Out); }
+static void add_to(int64_t n, double *dst, const double *src, double sign) {
+  for (int64_t e = 0; e < n; ++e) dst[e] += sign * src[e];
+}
+
+static int tree_vjp_core(int64_t n, int b, const int32_t *parent, const double *diag,
+                         const double *edge, const double *gd_bar, const double *ge_bar,
+                         double ld_bar, double *d_bar, double *e_bar) {
+  const int64_t bb = (int64_t)b * b;
+  int32_t *depth = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+  int64_t root = -1;
+  if (tree_depths(n, parent, depth, &root)) {
+    free(depth);
+    return 2;
+  }
+  int32_t H = 0;
+  for (int64_t v = 0; v < n; ++v)
+    if (depth[v] > H) H = depth[v];
+  int64_t *cnt = (int64_t *)calloc((size_t)H + 2, sizeof(int64_t));
+  for (int64_t v = 0; v < n; ++v) cnt[depth[v] + 1]++;
+  for (int32_t d = 0; d <= H; ++d) cnt[d + 1] += cnt[d];
+  int64_t *order = (int64_t *)malloc(sizeof(int64_t) * (size_t)n);
+  int64_t *fillp = (int64_t *)malloc(sizeof(int64_t) * ((size_t)H + 1));
+  for (int32_t d = 0; d <= H; ++d) fillp[d] = cnt[d];
+  for (int64_t v = 0; v < n; ++v) order[fillp[depth[v]]++] = v;
+
+  double *S = (double *)malloc(sizeof(double) * n * bb);
+  double *R = (double *)malloc(sizeof(double) * n * bb);
+  double *X = (double *)calloc((size_t)(n * bb), sizeof(double));
+  double *Si = (double *)malloc(sizeof(double) * n * bb);
+  double *G = (double *)malloc(sizeof(double) * n * bb);
+  double *GG = (double *)malloc(sizeof(double) * n * bb);
+  double *Sib = (double *)calloc((size_t)(n * bb), sizeof(double));
+  double *Xb = (double *)calloc((size_t)(n * bb), sizeof(double));
+  double *Sb = (double *)malloc(sizeof(double) * n * bb);
+  double *w = (double *)malloc(sizeof(double) * 6 * bb);
+  double *V = w + 3 * bb, *Vb = w + 4 * bb, *T = w + 5 * bb;
+  int rc = 0;
+
+  /* forward collect: R_v, X_v */
+  memcpy(S, diag, sizeof(double) * n * bb);
+  for (int32_t d = H; d >= 0 && !rc; --d)
+    for (int64_t k = cnt[d]; k < cnt[d + 1]; ++k) {
+      const int64_t v = order[k];
+      if (chol(b, S + v * bb, R + v * bb)) {
+        rc = 3;
+        break;
+      }
+      if (v != root)
+        collect_edge(b, R + v * bb, edge + v * bb, S + (int64_t)parent[v] * bb, X + v * bb,
+                     w, w + bb, w + 2 * bb);
+    }
+  if (rc) {
+    fill_nan(d_bar, n * bb);
+    fill_nan(e_bar, n * bb);
+  } else {
+    for (int64_t v = 0; v < n; ++v) inv_from_chol(b, R + v * bb, Si + v * bb);
+    /* forward distribute: G_vv (G_{p,v} = -G_pp X_v is not needed) */
+    memcpy(G + root * bb, Si + root * bb, sizeof(double) * bb);
+    for (int32_t d = 1; d <= H; ++d)
+      for (int64_t k = cnt[d]; k < cnt[d + 1]; ++k) {
+        const int64_t v = order[k], p = parent[v];
+        mm_nn(b, G + p * bb, X + v * bb, V);          /* V = G_pp X_v */
+        mm_tn(b, X + v * bb, V, T);                   /* X^T V        */
+        for (int64_t e = 0; e < bb; ++e) G[v * bb + e] = Si[v * bb + e] + T[e];
+      }
+    /* GG_v = sym(Gd_bar_v) */
+    for (int64_t v = 0; v < n; ++v)
+      for (int r = 0; r < b; ++r)
+        for (int c = 0; c < b; ++c)
+          GG[v * bb + r * b + c] =
+              0.5 * (gd_bar[v * bb + r * b + c] + gd_bar[v * bb + c * b + r]);
+    /* reverse distribute, deepest first */
+    for (int32_t d = H; d >= 1; --d)
+      for (int64_t k = cnt[d]; k < cnt[d + 1]; ++k) {
+        const int64_t v = order[k], p = parent[v];
+        const double *Xv = X + v * bb, *Gp = G + p * bb, *GGv = GG + v * bb;
+        mm_nn(b, Gp, Xv, V);                          /* V = G_pp X_v           */
+        add_to(bb, Sib + v * bb, GGv, 1.0);            /* Sinv_bar += GG_v       */
+        mm_nt(b, V, GGv, T);                           /* V GG^T                 */
+        add_to(bb, Xb + v * bb, T, 1.0);
+        mm_nn(b, Xv, GGv, Vb);                         /* V_bar = X GG - Ge_bar  */
+        add_to(bb, Vb, ge_bar + v * bb, -1.0);
+        mm_nt(b, Vb, Xv, T);                           /* GG_p += V_bar X^T      */
+        add_to(bb, GG + p * bb, T, 1.0);
+        mm_tn(b, Gp, Vb, T);                           /* X_bar += G_pp^T V_bar  */
+        add_to(bb, Xb + v * bb, T, 1.0);
+      }
+    add_to(bb, Sib + root * bb, GG + root * bb, 1.0);
+    /* reverse collect, root first */
+    for (int32_t d = 0; d <= H; ++d)
+      for (int64_t k = cnt[d]; k < cnt[d + 1]; ++k) {
+        const int64_t v = order[k];
+        const double *Sv = Si + v * bb;
+        if (v != root) {
+          const double *Sbp = Sb + (int64_t)parent[v] * bb, *Ev = edge + v * bb, *Xv = X + v * bb;
+          double *Mb = w, *Eb = e_bar + v * bb;
+          for (int64_t e = 0; e < bb; ++e) Mb[e] = -Sbp[e];
+          mm_nn(b, Mb, Ev, T);                          /* X_bar += M_bar E       */
+          add_to(bb, Xb + v * bb, T, 1.0);
+          mm_tn(b, Mb, Xv, Eb);                         /* E_bar = M_bar^T X      */
+          mm_nt(b, Xb + v * bb, Sv, T);                 /* + X_bar Sinv^T         */
+          add_to(bb, Eb, T, 1.0);
+          mm_tn(b, Ev, Xb + v * bb, T);                 /* Sinv_bar += E^T X_bar  */
+          add_to(bb, Sib + v * bb, T, 1.0);
+        }
+        /* S_bar = -Sinv^T Sinv_bar Sinv^T + ld_bar Sinv^T */
+        double *Sbv = Sb + v * bb;
+        mm_tn(b, Sv, Sib + v * bb, T);                  /* Sinv^T Sinv_bar        */
+        mm_nt(b, T, Sv, Sbv);                           /* (...) Sinv^T           */
+        for (int r = 0; r < b; ++r)
+          for (int c = 0; c < b; ++c)
+            Sbv[r * b + c] = -Sbv[r * b + c] + ld_bar * Sv[c * b + r];
+        for (int r = 0; r < b; ++r)
+          for (int c = 0; c < b; ++c)
+            d_bar[v * bb + r * b + c] = 0.5 * (Sbv[r * b + c] + Sbv[c * b + r]);
+      }
+    memset(e_bar + root * bb, 0, sizeof(double) * bb);
+  }
+  free(depth); free(cnt); free(order); free(fillp);
+  free(S); free(R); free(X); free(Si); free(G); free(GG); free(Sib); free(Xb); free(Sb); free(w);
+  return rc;
+}
+
+ORACLE_API int oracle_tree_vjp(int64_t n, int b, const int32_t *parent, const double *diag,
+                               const double *edge, const double *gd_bar, const double *ge_bar,
+                               double ld_bar, double *d_bar, double *e_bar) {
+  if (n < 1 || b < 1 || !parent || !diag || !edge || !gd_bar || !ge_bar || !d_bar || !e_bar)
+    return 1;
+  return tree_vjp_core(n, b, parent, diag, edge, gd_bar, ge_bar, ld_bar, d_bar, e_bar);
+}
+
+/* Chains as path trees rooted at their last block (parent of i is i + 1,
+ * E_i = lower[i], G_edge[i] = G_lower[i]), one matrix after another.
+ * status[m] = 0 or 3 (not positive definite). */
+ORACLE_API int oracle_chain_vjp(int64_t B, int64_t L, int b, const double *diag,
+                                const double *lower, const double *gd_bar, const double *gl_bar,
+                                const double *ld_bar, double *d_bar, double *l_bar,
+                                int32_t *status) {
+  if (B < 0 || L < 1 || b < 1 || !diag || !gd_bar || !ld_bar || !d_bar || !status) return 1;
+  if (L > 1 && (!lower || !gl_bar || !l_bar)) return 1;
+  const int64_t bb = (int64_t)b * b;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t m = 0; m < B; ++m) {
+    int32_t *par = (int32_t *)malloc(sizeof(int32_t) * (size_t)L);
+    double *e = (double *)calloc((size_t)(L * bb), sizeof(double));
+    double *geb = (double *)calloc((size_t)(L * bb), sizeof(double));
+    double *eb = (double *)malloc(sizeof(double) * L * bb);
+    for (int64_t i = 0; i < L; ++i) par[i] = i + 1 < L ? (int32_t)(i + 1) : -1;
+    if (L > 1) {
+      memcpy(e, lower + m * (L - 1) * bb, sizeof(double) * (L - 1) * bb);
+      memcpy(geb, gl_bar + m * (L - 1) * bb, sizeof(double) * (L - 1) * bb);
+    }
+    status[m] = tree_vjp_core(L, b, par, diag + m * L * bb, e, gd_bar + m * L * bb, geb,
+                              ld_bar[m], d_bar + m * L * bb, eb);
+    if (L > 1) memcpy(l_bar + m * (L - 1) * bb, eb, sizeof(double) * (L - 1) * bb);
+    free(par); free(e); free(geb); free(eb);
+  }
+  return 0;
+}
+
 /* Depth of every node of a valid tree (host helper for the tests); returns 0,
  * or 2 for an invalid parent array. */
 ORACLE_API int oracle_tree_depths(int64_t n, const int32_t *parent, int32_t *depth) {
