@@ -494,9 +494,9 @@ static int tree_vjp_core(int64_t n, int b, const int32_t *parent, const double *
         rc = 3;
         break;
       }
-      if (v != root)
-        collect_edge(b, R + v * bb, edge + v * bb, S + (int64_t)parent[v] * bb, X + v * bb,
-                     w, w + bb, w + 2 * bb);
+      const int64_t p = parent[v];
+      if (p >= 0) collect_edge(b, R + v * bb, edge + v * bb, S + p * bb, X + v * bb, w, w + bb,
+                               w + 2 * bb);
     }
   if (rc) {
     fill_nan(d_bar, n * bb);
