@@ -152,6 +152,80 @@ SELINV_API int selinv_tree_f32(const selinv_tree_plan *plan, const float *diag, 
                     float *G_diag, float *G_edge, double *logdet, int32_t *info,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------- reverse mode (VJP)
+ * Vector-Jacobian products of the three computations above: given the
+ * cotangents of every output, the cotangents of the inputs (the analytic
+ * backward of gabp-sparse-inv 0.3.2, "Implemented and tested kernels", item
+ * Differentiable tree: a second collect / distribute pair on the same tree,
+ * O((|V| + |E|) b^3) like the forward).  Each call recomputes the forward
+ * collect internally; nothing is kept between calls, so a caller passes the
+ * same inputs it gave the forward call.
+ *
+ * Convention (the dense identity d(A^-1) = -A^-1 dA A^-1 restricted to the
+ * pattern, d log det A = <A^-1, dA>):
+ *   - the loss is L(G_diag, G_edge, logdet); the cotangent arrays have the
+ *     shapes of the forward outputs, and `logdet_bar` has one float64 per
+ *     matrix (NULL = all zero);
+ *   - a diagonal output block is symmetric, so only the symmetric part of its
+ *     cotangent matters (the call reads the whole block and uses sym(.) =
+ *     (X + X^T) / 2);
+ *   - diagonal inputs are symmetric parameters: the returned diagonal
+ *     cotangent is the symmetric block sym(dL/dA_vv), the gradient with
+ *     respect to symmetric perturbations, written in full;
+ *   - an edge input block appears in A twice (as E at (p, v) and E^T at
+ *     (v, p)); the returned edge cotangent counts both: dL/dA_{p,v} +
+ *     (dL/dA_{v,p})^T, in the orientation of the input array.
+ * info, alignment, stream, workspace and return-status conventions are those
+ * of the forward entry points; on a failed pivot the matrix's cotangents are
+ * NaN.  Outputs must not alias inputs or each other. */
+
+/* chain: diag, lower as for selinv_chain_*; G_diag_bar [B][L][b][b],
+ * G_lower_bar [B][L-1][b][b] (may be NULL when L == 1), logdet_bar [B];
+ * outputs diag_bar [B][L][b][b], lower_bar [B][L-1][b][b]; info [B]. */
+SELINV_API size_t selinv_chain_vjp_workspace_bytes(int dtype_bytes, int64_t B, int64_t L, int32_t b);
+SELINV_API int selinv_chain_vjp_f64(int64_t B, int64_t L, int32_t b, const double *diag,
+                         const double *lower, const double *G_diag_bar,
+                         const double *G_lower_bar, const double *logdet_bar, double *diag_bar,
+                         double *lower_bar, int32_t *info, void *workspace,
+                         size_t workspace_bytes, void *stream);
+SELINV_API int selinv_chain_vjp_f32(int64_t B, int64_t L, int32_t b, const float *diag,
+                         const float *lower, const float *G_diag_bar, const float *G_lower_bar,
+                         const double *logdet_bar, float *diag_bar, float *lower_bar,
+                         int32_t *info, void *workspace, size_t workspace_bytes, void *stream);
+
+/* star: center, leaves, coupling as for selinv_star_*; cotangents
+ * G_center_bar [B][b][b], G_leaf_bar [B][K][b][b], G_cross_bar [B][K][b][b]
+ * (on G_cross[j] = (A^-1)_{j,0}), logdet_bar [B]; outputs center_bar,
+ * leaves_bar, coupling_bar (on coupling[j] = A_{j,0}, counting A_{0,j} too);
+ * info [B].  With K == 0 the leaf arrays may be NULL. */
+SELINV_API size_t selinv_star_vjp_workspace_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b);
+SELINV_API int selinv_star_vjp_f64(int64_t B, int64_t K, int32_t b, const double *center,
+                        const double *leaves, const double *coupling,
+                        const double *G_center_bar, const double *G_leaf_bar,
+                        const double *G_cross_bar, const double *logdet_bar, double *center_bar,
+                        double *leaves_bar, double *coupling_bar, int32_t *info,
+                        void *workspace, size_t workspace_bytes, void *stream);
+SELINV_API int selinv_star_vjp_f32(int64_t B, int64_t K, int32_t b, const float *center,
+                        const float *leaves, const float *coupling, const float *G_center_bar,
+                        const float *G_leaf_bar, const float *G_cross_bar,
+                        const double *logdet_bar, float *center_bar, float *leaves_bar,
+                        float *coupling_bar, int32_t *info, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* tree, for a plan from selinv_tree_plan_create: cotangents G_diag_bar
+ * [n][b][b], G_edge_bar [n][b][b] (root slot ignored), logdet_bar [1];
+ * outputs diag_bar [n][b][b], edge_bar [n][b][b] (root slot written as 0);
+ * info [1] as for selinv_tree_*. */
+SELINV_API size_t selinv_tree_vjp_workspace_bytes(const selinv_tree_plan *plan);
+SELINV_API int selinv_tree_vjp_f64(const selinv_tree_plan *plan, const double *diag,
+                        const double *edge, const double *G_diag_bar, const double *G_edge_bar,
+                        const double *logdet_bar, double *diag_bar, double *edge_bar,
+                        int32_t *info, void *workspace, size_t workspace_bytes, void *stream);
+SELINV_API int selinv_tree_vjp_f32(const selinv_tree_plan *plan, const float *diag,
+                        const float *edge, const float *G_diag_bar, const float *G_edge_bar,
+                        const double *logdet_bar, float *diag_bar, float *edge_bar,
+                        int32_t *info, void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

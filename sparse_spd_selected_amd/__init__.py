@@ -86,6 +86,24 @@ def lib():
         f = getattr(L, name)
         f.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         f.restype = ctypes.c_int
+    L.selinv_chain_vjp_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32]
+    L.selinv_chain_vjp_workspace_bytes.restype = sz
+    L.selinv_star_vjp_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32]
+    L.selinv_star_vjp_workspace_bytes.restype = sz
+    L.selinv_tree_vjp_workspace_bytes.argtypes = [vp]
+    L.selinv_tree_vjp_workspace_bytes.restype = sz
+    for name in ("selinv_chain_vjp_f64", "selinv_chain_vjp_f32"):
+        f = getattr(L, name)
+        f.argtypes = [i64, i64, i32] + [vp] * 8 + [vp, sz, vp]
+        f.restype = ctypes.c_int
+    for name in ("selinv_star_vjp_f64", "selinv_star_vjp_f32"):
+        f = getattr(L, name)
+        f.argtypes = [i64, i64, i32] + [vp] * 11 + [vp, sz, vp]
+        f.restype = ctypes.c_int
+    for name in ("selinv_tree_vjp_f64", "selinv_tree_vjp_f32"):
+        f = getattr(L, name)
+        f.argtypes = [vp] * 9 + [vp, sz, vp]
+        f.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -338,3 +356,147 @@ def tree(parent, diag: torch.Tensor, edge: torch.Tensor, check: bool = False,
     if return_info:
         return G_diag, G_edge, logdet, info
     return G_diag, G_edge, logdet
+
+
+# ------------------------------------------------------- reverse mode (VJP)
+def _logdet_bar(logdet_bar, batch, dev):
+    if logdet_bar is None:
+        return None
+    t = torch.as_tensor(logdet_bar, dtype=torch.float64, device=dev)
+    return _check_tensor(t.expand(tuple(batch)), "logdet_bar", dev, torch.float64)
+
+
+def chain_vjp(diag, lower, G_diag_bar, G_lower_bar, logdet_bar=None, check=False,
+              return_info=False):
+    """Cotangents of (diag, lower) for a loss of chain(diag, lower)'s outputs.
+
+    G_diag_bar, G_lower_bar: cotangents of G_diag, G_lower (shapes of
+    diag, lower); logdet_bar: cotangent of logdet ([...] or a scalar, float64;
+    None = 0).  Returns (diag_bar, lower_bar): diag_bar is the symmetric
+    gradient with respect to the symmetric diagonal blocks, lower_bar counts
+    both appearances A_{i+1,i} and A_{i,i+1} = lower[i]^T.
+    """
+    dt, dev = diag.dtype, diag.device
+    diag = _check_tensor(diag, "diag", dev, dt)
+    lower = _check_tensor(lower, "lower", dev, dt)
+    gd = _check_tensor(G_diag_bar, "G_diag_bar", dev, dt)
+    gl = _check_tensor(G_lower_bar, "G_lower_bar", dev, dt)
+    sfx = _sfx(diag)
+    if diag.dim() < 3 or diag.shape[-1] != diag.shape[-2]:
+        raise ValueError("diag must be [..., L, b, b]")
+    *batch, L, b, _ = diag.shape
+    if L < 1 or b < 1 or b > MAX_B:
+        raise ValueError("need L >= 1 and 1 <= b <= %d" % MAX_B)
+    if tuple(lower.shape) != tuple(batch) + (L - 1, b, b):
+        raise ValueError("lower must be [..., L-1, b, b] matching diag")
+    if gd.shape != diag.shape or gl.shape != lower.shape:
+        raise ValueError("cotangents must have the shapes of G_diag and G_lower")
+    lb = _logdet_bar(logdet_bar, batch, dev)
+    if check:
+        _validate_symmetric("diag", diag)
+    B = 1
+    for s_ in batch:
+        B *= s_
+    d_bar = torch.empty_like(diag)
+    l_bar = torch.empty_like(lower)
+    info = torch.empty(tuple(batch), dtype=torch.int32, device=dev)
+    L_ = lib()
+    ws_bytes = L_.selinv_chain_vjp_workspace_bytes(diag.element_size(), B, L, b)
+    ws = _workspace(ws_bytes, dev)
+    with torch.cuda.device(dev):
+        rc = getattr(L_, "selinv_chain_vjp_" + sfx)(
+            B, L, b, _ptr(diag), _ptr(lower), _ptr(gd), _ptr(gl), _ptr(lb), _ptr(d_bar),
+            _ptr(l_bar), _ptr(info), _ptr(ws), ws_bytes, _stream(dev))
+    _status(rc, "selinv_chain_vjp_" + sfx)
+    if check:
+        _raise_info(info, "chain_vjp")
+    if return_info:
+        return d_bar, l_bar, info
+    return d_bar, l_bar
+
+
+def star_vjp(center, leaves, coupling, G_center_bar, G_leaf_bar, G_cross_bar, logdet_bar=None,
+             check=False, return_info=False):
+    """Cotangents of (center, leaves, coupling) for a loss of star(...)'s
+    outputs (G_cross[j] = (A^-1)_{j,0}; coupling_bar counts A_{j,0} and
+    A_{0,j} = coupling[j]^T)."""
+    dt, dev = center.dtype, center.device
+    center = _check_tensor(center, "center", dev, dt)
+    leaves = _check_tensor(leaves, "leaves", dev, dt)
+    coupling = _check_tensor(coupling, "coupling", dev, dt)
+    gc = _check_tensor(G_center_bar, "G_center_bar", dev, dt)
+    gleaf = _check_tensor(G_leaf_bar, "G_leaf_bar", dev, dt)
+    gx = _check_tensor(G_cross_bar, "G_cross_bar", dev, dt)
+    sfx = _sfx(center)
+    if center.dim() < 2 or center.shape[-1] != center.shape[-2]:
+        raise ValueError("center must be [..., b, b]")
+    *batch, b, _ = center.shape
+    if leaves.dim() != len(batch) + 3 or tuple(leaves.shape[:len(batch)]) != tuple(batch):
+        raise ValueError("leaves must be [..., K, b, b] matching center")
+    K = leaves.shape[len(batch)]
+    if tuple(leaves.shape) != tuple(batch) + (K, b, b) or coupling.shape != leaves.shape:
+        raise ValueError("leaves and coupling must be [..., K, b, b]")
+    if gc.shape != center.shape or gleaf.shape != leaves.shape or gx.shape != leaves.shape:
+        raise ValueError("cotangents must have the shapes of the outputs")
+    if b < 1 or b > MAX_B:
+        raise ValueError("need 1 <= b <= %d" % MAX_B)
+    lb = _logdet_bar(logdet_bar, batch, dev)
+    B = 1
+    for s_ in batch:
+        B *= s_
+    c_bar = torch.empty_like(center)
+    lv_bar = torch.empty_like(leaves)
+    cp_bar = torch.empty_like(coupling)
+    info = torch.empty(tuple(batch), dtype=torch.int32, device=dev)
+    L_ = lib()
+    ws_bytes = L_.selinv_star_vjp_workspace_bytes(center.element_size(), B, K, b)
+    ws = _workspace(ws_bytes, dev)
+    with torch.cuda.device(dev):
+        rc = getattr(L_, "selinv_star_vjp_" + sfx)(
+            B, K, b, _ptr(center), _ptr(leaves), _ptr(coupling), _ptr(gc), _ptr(gleaf), _ptr(gx),
+            _ptr(lb), _ptr(c_bar), _ptr(lv_bar), _ptr(cp_bar), _ptr(info), _ptr(ws), ws_bytes,
+            _stream(dev))
+    _status(rc, "selinv_star_vjp_" + sfx)
+    if check:
+        _raise_info(info, "star_vjp")
+    if return_info:
+        return c_bar, lv_bar, cp_bar, info
+    return c_bar, lv_bar, cp_bar
+
+
+def tree_vjp(parent, diag, edge, G_diag_bar, G_edge_bar, logdet_bar=None, check=False,
+             return_info=False, plan: TreePlan | None = None):
+    """Cotangents of (diag, edge) for a loss of tree(parent, diag, edge)'s
+    outputs; edge_bar[v] counts A_{parent(v),v} and its transpose, the root
+    slot is zero."""
+    dt, dev = diag.dtype, diag.device
+    diag = _check_tensor(diag, "diag", dev, dt)
+    edge = _check_tensor(edge, "edge", dev, dt)
+    gd = _check_tensor(G_diag_bar, "G_diag_bar", dev, dt)
+    ge = _check_tensor(G_edge_bar, "G_edge_bar", dev, dt)
+    sfx = _sfx(diag)
+    if diag.dim() != 3 or diag.shape[1] != diag.shape[2] or edge.shape != diag.shape:
+        raise ValueError("diag and edge must be [n, b, b]")
+    if gd.shape != diag.shape or ge.shape != diag.shape:
+        raise ValueError("cotangents must be [n, b, b]")
+    n, b = diag.shape[0], diag.shape[1]
+    if plan is None:
+        plan = tree_plan(parent, b, dt, dev)
+    if plan.n != n or plan.b != b or plan.dtype != dt:
+        raise ValueError("plan does not match (n, b, dtype)")
+    lb = _logdet_bar(logdet_bar, (1,), dev)
+    d_bar = torch.empty_like(diag)
+    e_bar = torch.empty_like(edge)
+    info = torch.empty((), dtype=torch.int32, device=dev)
+    ws_bytes = int(lib().selinv_tree_vjp_workspace_bytes(plan.handle))
+    ws = _workspace(ws_bytes, dev)
+    with torch.cuda.device(dev):
+        rc = getattr(lib(), "selinv_tree_vjp_" + sfx)(
+            plan.handle, _ptr(diag), _ptr(edge), _ptr(gd), _ptr(ge), _ptr(lb), _ptr(d_bar),
+            _ptr(e_bar), info.data_ptr(), _ptr(ws), ws_bytes, _stream(dev))
+    _status(rc, "selinv_tree_vjp_" + sfx)
+    if check:
+        _raise_info(info.reshape(1), "tree_vjp")
+    if return_info:
+        return d_bar, e_bar, info
+    return d_bar, e_bar

@@ -90,6 +90,55 @@ __device__ inline void gemm_sym(T *Out, const T *Base, const T *A, const T *B, i
   __syncthreads();
 }
 
+// dst = (src + src^T) / 2; dst must not alias src
+template <typename T>
+__device__ inline void sym_part(T *dst, const T *src, int b) {
+  for (int e = tid(); e < b * b; e += nthreads()) {
+    const int r = e / b, c = e % b;
+    dst[e] = T(0.5) * (src[r * b + c] + src[c * b + r]);
+  }
+  __syncthreads();
+}
+
+// Out = beta * Base + alpha * op(A) op(B), every entry.  Base may alias Out;
+// Out must not alias A or B.
+template <typename T, bool TA, bool TB>
+__device__ inline void gemm_axpby(T *Out, T beta, const T *Base, T alpha, const T *A, const T *B,
+                                  int b) {
+  for (int e = tid(); e < b * b; e += nthreads()) {
+    const int r = e / b, c = e % b;
+    T acc = T(0);
+    for (int k = 0; k < b; ++k) {
+      const T a = TA ? A[k * b + r] : A[r * b + k];
+      const T x = TB ? B[c * b + k] : B[k * b + c];
+      acc += a * x;
+    }
+    Out[e] = beta * Base[e] + alpha * acc;
+  }
+  __syncthreads();
+}
+
+// Out = Base + sign * (P + P^T) / 2 with P = op(A) op(B): the symmetric part
+// of a product that is not symmetric by itself, exactly symmetric.  Base
+// (symmetric; only its lower triangle is read) may be null or alias Out.
+template <typename T, bool TA, bool TB>
+__device__ inline void gemm_symmetrized(T *Out, const T *Base, const T *A, const T *B, int b,
+                                        T sign) {
+  for (int e = tid(); e < b * b; e += nthreads()) {
+    const int r = e / b, c = e % b;
+    if (r < c) continue;
+    T prc = T(0), pcr = T(0);
+    for (int k = 0; k < b; ++k) {
+      prc += (TA ? A[k * b + r] : A[r * b + k]) * (TB ? B[c * b + k] : B[k * b + c]);
+      pcr += (TA ? A[k * b + c] : A[c * b + k]) * (TB ? B[r * b + k] : B[k * b + r]);
+    }
+    const T v = (Base ? Base[r * b + c] : T(0)) + sign * (T(0.5) * (prc + pcr));
+    Out[r * b + c] = v;
+    Out[c * b + r] = v;
+  }
+  __syncthreads();
+}
+
 // In-place inverse of a symmetric positive definite block by the symmetric
 // Gauss-Jordan sweep, without pivoting.  Sweeping pivot k maps
 //   a_ij -> a_ij - a_ik a_kj / d   (i, j != k),   a_ik -> a_ik / d,

@@ -115,4 +115,28 @@ template <typename T>
 hipError_t tree_launch(const selinv_tree_plan *plan, const T *diag, const T *edge, T *G_diag,
                        T *G_edge, double *logdet, int32_t *info, void *ws, hipStream_t s);
 
+// ------------------------------------------- reverse mode (vjp_*.hip)
+size_t chain_vjp_workspace_bytes(int dtype_bytes, int64_t B, int64_t L, int32_t b);
+// b = 16: one wavefront per chain on the matrix cores (vjp_chain_b16.hip)
+size_t chain16_vjp_workspace_bytes(int dtype_bytes, int64_t B, int64_t L);
+template <typename T>
+hipError_t chain16_vjp_launch(int64_t B, int64_t L, const T *diag, const T *lower, const T *gd,
+                              const T *gl, const double *ld_bar, T *d_bar, T *l_bar,
+                              int32_t *info, void *ws, hipStream_t s);
+template <typename T>
+hipError_t chain_vjp_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower,
+                            const T *gd, const T *gl, const double *ld_bar, T *d_bar, T *l_bar,
+                            int32_t *info, void *ws, hipStream_t s);
+size_t star_vjp_workspace_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b);
+template <typename T>
+hipError_t star_vjp_launch(int64_t B, int64_t K, int32_t b, const T *center, const T *leaves,
+                           const T *coupling, const T *gc, const T *gleaf, const T *gcross,
+                           const double *ld_bar, T *center_bar, T *leaves_bar, T *coupling_bar,
+                           int32_t *info, void *ws, hipStream_t s);
+size_t tree_vjp_workspace_bytes(const selinv_tree_plan *plan);
+template <typename T>
+hipError_t tree_vjp_launch(const selinv_tree_plan *plan, const T *diag, const T *edge,
+                           const T *gd, const T *ge, const double *ld_bar, T *d_bar, T *e_bar,
+                           int32_t *info, void *ws, hipStream_t s);
+
 }  // namespace selinv

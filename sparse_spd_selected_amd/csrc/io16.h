@@ -61,6 +61,26 @@ __device__ __forceinline__ void store(T *P, int lane, const Nat<T> &n) {
                                 reinterpret_cast<typename Tr::vec *>(P + Tr::kVec * (64 * c + lane)));
 }
 
+// Workspace blocks are written and read back by the same kernel: ordinary
+// (temporal) accesses, so that they can stay in the caches in between.
+template <typename T>
+__device__ __forceinline__ Nat<T> load_ws(const T *P, int lane) {
+  using Tr = Traits<T>;
+  Nat<T> n;
+#pragma unroll
+  for (int c = 0; c < Tr::kChunks; ++c)
+    n.c[c] = *reinterpret_cast<const typename Tr::vec *>(P + Tr::kVec * (64 * c + lane));
+  return n;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_ws(T *P, int lane, const Nat<T> &n) {
+  using Tr = Traits<T>;
+#pragma unroll
+  for (int c = 0; c < Tr::kChunks; ++c)
+    *reinterpret_cast<typename Tr::vec *>(P + Tr::kVec * (64 * c + lane)) = n.c[c];
+}
+
 // Tile position of natural vector v (16-byte aligned: kLd is a multiple of kVec).
 template <typename T>
 __device__ __forceinline__ constexpr int nat_pos(int v) {

@@ -48,6 +48,7 @@ def _load():
         lib.spdgen_normal.argtypes = [u64, ctypes.c_uint32, u64, u64]
         lib.spdgen_normal.restype = dbl
         lib.spdgen_philox4x32_10.argtypes = [vp, vp, vp]
+        lib.spdgen_cotangent.argtypes = [u64, ctypes.c_uint32, i64, i64, i64, vp]
         _lib = lib
     return _lib
 
@@ -97,6 +98,20 @@ def star(B: int, K: int, b: int, seed: int = 0, diag_load: float = 2.0, m0: int 
     _load().spdgen_star(seed, m0, B, K, b, diag_load, _ptr(center), _ptr(leaves),
                         _ptr(coupling))
     return center, leaves, coupling
+
+
+def cotangent(shape, seed: int = 0, k: int = 0, m0: int = 0) -> np.ndarray:
+    """Standard normal array of ``shape`` (float64), seeded per leading index:
+    row m of the result depends only on (seed, k, m0 + m), so a sample of a
+    batch can be regenerated on its own.  ``k`` tells apart several arrays of
+    one call (cotangents of different outputs)."""
+    shape = tuple(int(x) for x in shape)
+    out = np.empty(shape, np.float64)
+    count = shape[0] if shape else 1
+    per = int(np.prod(shape[1:])) if len(shape) > 1 else 1
+    if out.size:
+        _load().spdgen_cotangent(seed, k, m0, count, per, _ptr(out))
+    return out
 
 
 def random_recursive_tree(n: int, seed: int = 1) -> np.ndarray:

@@ -279,3 +279,16 @@ SPDGEN_API void spdgen_tree(uint64_t seed, int64_t n, int b, double diag_load,
   }
   free(rad);
 }
+
+/* ------------------------------------------------------------ cotangents */
+
+/* Standard normal arrays for matrices [m0, m0+count), `per` numbers per
+ * matrix, from stream 16 + k (k selects one of several arrays; the streams
+ * of the SPD inputs are below 16).  Used as the cotangents that seed a
+ * vector-Jacobian product. */
+SPDGEN_API void spdgen_cotangent(uint64_t seed, uint32_t k, int64_t m0, int64_t count, int64_t per,
+                                 double *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < count; ++m)
+    normals(seed, 16u + k, (uint64_t)(m0 + m), 0, per, 1.0, out + m * per);
+}

@@ -123,3 +123,47 @@ def test_python_binding_rejects_cpu_tensors():
         ssa.chain(d, l)
     with pytest.raises(TypeError):
         ssa.chain(d.numpy(), l)
+
+
+def test_vjp_workspace_sizes(lib):
+    # b = 16: packed Sinv and P plus X^T and Z per block
+    assert lib.selinv_chain_vjp_workspace_bytes(8, 4096, 64, 16) >= 4096 * 64 * 784 * 8
+    assert lib.selinv_chain_vjp_workspace_bytes(4, 3, 5, 7) >= 3 * 5 * 4 * 49 * 4
+    assert lib.selinv_chain_vjp_workspace_bytes(8, 1, 0, 4) == 0  # L < 1
+    assert lib.selinv_star_vjp_workspace_bytes(8, 2, 3, 33) == 0
+    assert lib.selinv_star_vjp_workspace_bytes(8, 2, 3, 4) >= 5 * 6 * 16 * 8
+    assert lib.selinv_tree_vjp_workspace_bytes(None) == 0
+
+
+def _chain_vjp_call(lib, B=1, L=2, b=4, diag=1, lower=1, gd=1, gl=1, db=1, lb=1, ws=1,
+                    wsb=1 << 30):
+    p = lambda x: ctypes.c_void_p(x if x > 1 else 0x1000) if x else None
+    return lib.selinv_chain_vjp_f64(B, L, b, p(diag), p(lower), p(gd), p(gl), None, p(db),
+                                    p(lb), None, p(ws), wsb, None)
+
+
+def test_chain_vjp_argument_validation(lib):
+    assert _chain_vjp_call(lib, b=0) == ssa.INVALID_ARG
+    assert _chain_vjp_call(lib, L=0) == ssa.INVALID_ARG
+    assert _chain_vjp_call(lib, gd=0) == ssa.INVALID_ARG
+    assert _chain_vjp_call(lib, gl=0) == ssa.INVALID_ARG
+    assert _chain_vjp_call(lib, lb=0) == ssa.INVALID_ARG
+    assert _chain_vjp_call(lib, db=0) == ssa.INVALID_ARG
+    assert _chain_vjp_call(lib, wsb=64) == ssa.INVALID_ARG
+    assert _chain_vjp_call(lib, gl=0x1008) == ssa.INVALID_ARG
+    assert _chain_vjp_call(lib, ws=0x1040) == ssa.INVALID_ARG
+    assert _chain_vjp_call(lib, B=0) == ssa.OK
+
+
+def test_star_and_tree_vjp_argument_validation(lib):
+    p = ctypes.c_void_p(0x1000)
+
+    def star(b=4, leaves_bar=p, wsb=1 << 30):
+        # center, leaves, coupling, three cotangents, logdet_bar, three outputs, info
+        return lib.selinv_star_vjp_f64(1, 2, b, p, p, p, p, p, p, None, p, leaves_bar, p, None,
+                                       p, wsb, None)
+    assert star(b=0) == ssa.INVALID_ARG
+    assert star(leaves_bar=None) == ssa.INVALID_ARG
+    assert star(wsb=8) == ssa.INVALID_ARG
+    assert lib.selinv_tree_vjp_f64(None, p, p, p, p, None, p, p, None, p, 1 << 30, None) == \
+        ssa.INVALID_ARG
