@@ -27,7 +27,7 @@ SOURCES = [
     "chain_b32.hip", "chain_b32_seg.hip",
     "tree_b8.hip",
     "chain_small.hip",
-    "vjp_generic.hip", "vjp_chain_b16.hip",
+    "vjp_generic.hip", "vjp_chain_b16.hip", "vjp_star_b32.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

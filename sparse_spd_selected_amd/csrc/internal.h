@@ -128,6 +128,13 @@ hipError_t chain_vjp_launch(int64_t B, int64_t L, int32_t b, const T *diag, cons
                             const T *gd, const T *gl, const double *ld_bar, T *d_bar, T *l_bar,
                             int32_t *info, void *ws, hipStream_t s);
 size_t star_vjp_workspace_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b);
+// b = 32: wavefront per 16 leaves on the matrix cores (vjp_star_b32.hip)
+size_t star32_vjp_workspace_bytes(int dtype_bytes, int64_t B, int64_t K);
+template <typename T>
+hipError_t star32_vjp_launch(int64_t B, int64_t K, const T *center, const T *leaves,
+                             const T *coupling, const T *gc, const T *gleaf, const T *gcross,
+                             const double *ld_bar, T *center_bar, T *leaves_bar, T *coupling_bar,
+                             int32_t *info, void *ws, hipStream_t s);
 template <typename T>
 hipError_t star_vjp_launch(int64_t B, int64_t K, int32_t b, const T *center, const T *leaves,
                            const T *coupling, const T *gc, const T *gleaf, const T *gcross,

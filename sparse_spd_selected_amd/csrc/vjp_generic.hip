@@ -395,6 +395,7 @@ hipError_t chain_vjp_launch(int64_t B, int64_t L, int32_t b, const T *diag, cons
 }
 
 size_t star_vjp_workspace_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b) {
+  if (b == 32) return star32_vjp_workspace_bytes(dtype_bytes, B, K);
   const size_t nl = static_cast<size_t>(B) * K, bb = static_cast<size_t>(b) * b;
   return align_up(5 * nl * bb * dtype_bytes) + align_up(B * bb * dtype_bytes) +
          align_up(nl * sizeof(int32_t)) + align_up(B * sizeof(int32_t));
@@ -406,6 +407,9 @@ hipError_t star_vjp_launch(int64_t B, int64_t K, int32_t b, const T *center, con
                            const double *ld_bar, T *center_bar, T *leaves_bar, T *coupling_bar,
                            int32_t *info, void *ws, hipStream_t s) {
   if (B == 0) return hipSuccess;
+  if (b == 32)
+    return star32_vjp_launch<T>(B, K, center, leaves, coupling, gc, gleaf, gcross, ld_bar,
+                                center_bar, leaves_bar, coupling_bar, info, ws, s);
   const size_t nl = static_cast<size_t>(B) * K, bb = static_cast<size_t>(b) * b;
   Carve cv(ws);
   T *st = cv.take<T>(5 * nl * bb);
