@@ -141,6 +141,12 @@ hipError_t star_vjp_launch(int64_t B, int64_t K, int32_t b, const T *center, con
                            const double *ld_bar, T *center_bar, T *leaves_bar, T *coupling_bar,
                            int32_t *info, void *ws, hipStream_t s);
 size_t tree_vjp_workspace_bytes(const selinv_tree_plan *plan);
+// b <= 8: one block row per lane, eight nodes per wavefront (vjp_tree_b8.hip)
+size_t tree8_vjp_workspace_bytes(const selinv_tree_plan *plan);
+template <typename T>
+hipError_t tree8_vjp_launch(const selinv_tree_plan *plan, const T *diag, const T *edge,
+                            const T *gd, const T *ge, const double *ld_bar, T *d_bar, T *e_bar,
+                            int32_t *info, void *ws, hipStream_t s);
 template <typename T>
 hipError_t tree_vjp_launch(const selinv_tree_plan *plan, const T *diag, const T *edge,
                            const T *gd, const T *ge, const double *ld_bar, T *d_bar, T *e_bar,

@@ -432,6 +432,7 @@ hipError_t star_vjp_launch(int64_t B, int64_t K, int32_t b, const T *center, con
 }
 
 size_t tree_vjp_workspace_bytes(const selinv_tree_plan *plan) {
+  if (plan->b <= 8) return tree8_vjp_workspace_bytes(plan);
   const size_t n = plan->n, bb = static_cast<size_t>(plan->b) * plan->b;
   return align_up(6 * n * bb * plan->dtype_bytes) + align_up(n * sizeof(int32_t)) +
          align_up(sizeof(int32_t));
@@ -441,6 +442,8 @@ template <typename T>
 hipError_t tree_vjp_launch(const selinv_tree_plan *plan, const T *diag, const T *edge,
                            const T *gd, const T *ge, const double *ld_bar, T *d_bar, T *e_bar,
                            int32_t *info, void *ws, hipStream_t s) {
+  if (plan->b <= 8)
+    return tree8_vjp_launch<T>(plan, diag, edge, gd, ge, ld_bar, d_bar, e_bar, info, ws, s);
   const size_t n = plan->n;
   const int b = plan->b;
   const size_t bb = static_cast<size_t>(b) * b;
