@@ -11,6 +11,11 @@ Metric: nominal selected-inverse GFLOP/s (7 b^3 per non-root block, b^3 per
 root, never the executed count) and block-rows/s; roofline fraction of the
 dominant kernel against MI355X HBM bandwidth (8 TB/s) on compulsory bytes
 (every input block read once, every output block written once).
+
+``--op vjp`` times the reverse mode instead (one call = the vector-Jacobian
+product of every matrix of the batch, seeded normal cotangents on every
+output): nominal 22 b^3 per non-root block and 4 b^3 per root, compulsory
+bytes = inputs + cotangents read once, input cotangents written once.
 """
 from __future__ import annotations
 
@@ -57,19 +62,32 @@ def measured_traffic(workload, dtname):
     return rec.get("bytes_per_call")
 
 
-def nominal_flops(kind, cfg):
+def nominal_flops(kind, cfg, op="selinv"):
+    """Per non-root block: forward 7 b^3 (inverse b^3, X 2 b^3, symmetric M
+    b^3, V 2 b^3, symmetric G b^3); reverse mode 22 b^3 (collect: inverse b^3,
+    X 2, M 1, W 2, Z 2, N 2, P 3; distribute: Dbar X 2, G Z 2, X^T Q 2, G X 2,
+    symmetric X^T V 1).  Per root: b^3 forward, 4 b^3 reverse."""
     b = cfg["b"]
+    per, root = (7, 1) if op == "selinv" else (22, 4)
     if kind == "chain":
-        return cfg["B"] * (7 * b ** 3 * (cfg["L"] - 1) + b ** 3)
+        return cfg["B"] * (per * b ** 3 * (cfg["L"] - 1) + root * b ** 3)
     if kind == "star":
-        return cfg["B"] * (7 * b ** 3 * cfg["K"] + b ** 3)
-    return 7 * b ** 3 * (cfg["n"] - 1) + b ** 3
+        return cfg["B"] * (per * b ** 3 * cfg["K"] + root * b ** 3)
+    return per * b ** 3 * (cfg["n"] - 1) + root * b ** 3
 
 
-def compulsory_bytes(kind, cfg, w):
+def compulsory_bytes(kind, cfg, w, op="selinv"):
     """Input blocks read once + output blocks written once + logdet (f64) +
-    info (int32) (+ parent indices for the tree)."""
+    info (int32) (+ parent indices for the tree).  Reverse mode: inputs and
+    output cotangents read once, input cotangents written once, logdet_bar
+    (f64) and info."""
     b2 = cfg["b"] ** 2
+    if op == "vjp":
+        if kind == "chain":
+            return cfg["B"] * ((6 * cfg["L"] - 3) * b2 * w + 8 + 4)
+        if kind == "star":
+            return cfg["B"] * ((6 * cfg["K"] + 3) * b2 * w + 8 + 4)
+        return (6 * cfg["n"] - 2) * b2 * w + 4 * cfg["n"] + 8 + 4
     if kind == "chain":
         return cfg["B"] * ((4 * cfg["L"] - 2) * b2 * w + 8 + 4)
     if kind == "star":
@@ -102,14 +120,36 @@ def make_inputs(kind, cfg, dt, dev):
     return [torch.from_numpy(x).to(dev).to(dt) for x in (d, e)], np.asarray(parent)
 
 
-def run_gpu(kind, cfg, dtname, steps, warmup):
+def make_cotangents(kind, inputs, cfg, dt, dev):
+    """Seeded normal cotangents, one per output (orientation of the outputs:
+    the shapes of the inputs), plus logdet_bar."""
+    import torch
+    import spdgen
+    shapes = [tuple(x.shape) for x in inputs]
+    bars = [torch.from_numpy(spdgen.cotangent(sh, seed=cfg["seed"], k=i)).to(dev).to(dt)
+            for i, sh in enumerate(shapes)]
+    nb = 1 if kind == "tree" else cfg["B"]
+    lb = torch.from_numpy(spdgen.cotangent((nb,), seed=cfg["seed"], k=len(shapes))).to(dev)
+    return bars, lb
+
+
+def run_gpu(kind, cfg, dtname, steps, warmup, op="selinv"):
     import torch
     import sparse_spd_selected_amd as ssa
     ssa.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     dt = torch.float64 if dtname == "f64" else torch.float32
     inputs, parent = make_inputs(kind, cfg, dt, dev)
-    if kind == "chain":
+    if op == "vjp":
+        bars, lb = make_cotangents(kind, inputs, cfg, dt, dev)
+        if kind == "chain":
+            call = lambda: ssa.chain_vjp(*inputs, *bars, lb)
+        elif kind == "star":
+            call = lambda: ssa.star_vjp(*inputs, *bars, lb)
+        else:
+            plan = ssa.tree_plan(parent, cfg["b"], dt, dev)
+            call = lambda: ssa.tree_vjp(parent, *inputs, *bars, lb, plan=plan)
+    elif kind == "chain":
         call = lambda: ssa.chain(*inputs)
     elif kind == "star":
         call = lambda: ssa.star(*inputs)
@@ -133,6 +173,50 @@ def run_gpu(kind, cfg, dtname, steps, warmup):
     wall = time.perf_counter() - t0
     ev_ms = [a.elapsed_time(b) for a, b in evs]
     return {"wall_s": wall, "ev_ms": ev_ms}
+
+
+def cpu_baseline_vjp(kind, cfg):
+    """The float64 oracle's VJP, as it stands, on a bounded sample."""
+    import oracle
+    import spdgen
+    lib = oracle.load()
+    if kind == "chain":
+        Bs = cfg["B"] if cfg["B"] * cfg["L"] * cfg["b"] ** 3 <= 2e9 else max(1, int(2e9 // (cfg["L"] * cfg["b"] ** 3)))
+        d, l = spdgen.chain(Bs, cfg["L"], cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
+        gd = spdgen.cotangent(d.shape, seed=cfg["seed"], k=0)
+        gl = spdgen.cotangent(l.shape, seed=cfg["seed"], k=1)
+        lb = spdgen.cotangent((Bs,), seed=cfg["seed"], k=2)
+        t0 = time.perf_counter()
+        oracle.chain_vjp(d, l, gd, gl, lb, lib=lib)
+        t = time.perf_counter() - t0
+        sub = dict(cfg, B=Bs)
+        sample = "%d of %d chains (L=%d, b=%d), float64, reverse mode" % (Bs, cfg["B"], cfg["L"], cfg["b"])
+    elif kind == "star":
+        Bs = min(cfg["B"], 4)
+        c, lv, cp = spdgen.star(Bs, cfg["K"], cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
+        bars = [spdgen.cotangent(x.shape, seed=cfg["seed"], k=i) for i, x in enumerate((c, lv, cp))]
+        lb = spdgen.cotangent((Bs,), seed=cfg["seed"], k=3)
+        t0 = time.perf_counter()
+        oracle.star_vjp(c, lv, cp, *bars, lb, lib=lib)
+        t = time.perf_counter() - t0
+        sub = dict(cfg, B=Bs)
+        sample = "%d of %d stars (K=%d, b=%d), float64, reverse mode" % (Bs, cfg["B"], cfg["K"], cfg["b"])
+    else:
+        parent = spdgen.random_recursive_tree(cfg["n"], cfg["seed"])
+        d, e = spdgen.tree(parent, cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
+        gd = spdgen.cotangent(d.shape, seed=cfg["seed"], k=0)
+        ge = spdgen.cotangent(e.shape, seed=cfg["seed"], k=1)
+        lb = float(spdgen.cotangent((1,), seed=cfg["seed"], k=2)[0])
+        t0 = time.perf_counter()
+        oracle.tree_vjp(parent, d, e, gd, ge, lb, lib=lib)
+        t = time.perf_counter() - t0
+        sub = cfg
+        sample = "the whole tree (n=%d, b=%d), float64, reverse mode, single thread" % (cfg["n"], cfg["b"])
+    gflops = nominal_flops(kind, sub, "vjp") / t / 1e9
+    cores = 1 if kind == "tree" else int(lib.oracle_num_threads())
+    return {"value": round(gflops, 3), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": sample, "seconds": round(t, 3),
+            "block_rows_per_s": round(block_rows(kind, sub) / t, 1)}
 
 
 def cpu_baseline(kind, cfg):
@@ -191,6 +275,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="chain_b16_batched")
+    ap.add_argument("--op", default="selinv", choices=("selinv", "vjp"),
+                    help="selinv: the selected inverse; vjp: its reverse mode")
     ap.add_argument("--dtype", default=None, help="f64 or f32 (default: the workload's first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-second-dtype", action="store_true")
@@ -213,17 +299,22 @@ def main():
     dtname = args.dtype or dtypes[0]
     w = 8 if dtname == "f64" else 4
 
-    res = run_gpu(kind, cfg, dtname, args.steps, args.warmup)
+    op = args.op
+    res = run_gpu(kind, cfg, dtname, args.steps, args.warmup, op)
     ev = sorted(res["ev_ms"])
     ms_mean = sum(res["ev_ms"]) / len(ev)
     ms_step = res["wall_s"] * 1e3 / args.steps
-    F = nominal_flops(kind, cfg)
-    nbytes = compulsory_bytes(kind, cfg, w)
+    F = nominal_flops(kind, cfg, op)
+    nbytes = compulsory_bytes(kind, cfg, w, op)
     gflops = F / (ms_step * 1e-3) / 1e9
     achieved_gbs = nbytes / (ms_mean * 1e-3) / 1e9
     peak_t = FP64_PEAK_TFLOPS if dtname == "f64" else FP32_PEAK_TFLOPS
+    tkey = args.workload if op == "selinv" else args.workload + "+vjp"
     out = {
-        "metric": "selected-inverse GFLOP/s and block-rows/s (fp64/fp32), % of MI355X roofline",
+        "metric": ("selected-inverse GFLOP/s and block-rows/s (fp64/fp32), % of MI355X roofline"
+                   if op == "selinv" else
+                   "selected-inverse VJP GFLOP/s and block-rows/s (fp64/fp32), "
+                   "% of MI355X roofline"),
         "value": round(gflops, 3),
         "unit": "GFLOP/s",
         "n_gpus": 1,
@@ -235,29 +326,30 @@ def main():
         "vs_baseline": None,
         "dtype": dtname,
         "data": "synthetic (seeded Philox SPD blocks)",
-        "config": dict({"workload": args.workload, "pattern": kind}, **cfg),
+        "config": dict({"workload": args.workload, "pattern": kind, "op": op}, **cfg),
         "block_rows_per_s": round(block_rows(kind, cfg) / (ms_step * 1e-3), 1),
         "kernel_ms": {"mean": round(ms_mean, 4), "median": round(ev[len(ev) // 2], 4),
                       "min": round(ev[0], 4)},
         "flop_frac_of_peak": round(gflops / (peak_t * 1e3), 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.workload, dtname),
+                     "traffic": measured_traffic(tkey, dtname),
                      "algorithmic_bytes": nbytes, "kernel_source_hash": kernel_source_hash()},
     }
     if not args.no_second_dtype and len(dtypes) > 1 and args.dtype is None:
         other = dtypes[1]
-        r2 = run_gpu(kind, cfg, other, args.steps, args.warmup)
+        r2 = run_gpu(kind, cfg, other, args.steps, args.warmup, op)
         ms2 = r2["wall_s"] * 1e3 / args.steps
         ev2 = sum(r2["ev_ms"]) / len(r2["ev_ms"])
         w2 = 8 if other == "f64" else 4
         out[other] = {"value": round(F / (ms2 * 1e-3) / 1e9, 3), "unit": "GFLOP/s",
                       "ms_per_step": round(ms2, 4),
                       "block_rows_per_s": round(block_rows(kind, cfg) / (ms2 * 1e-3), 1),
-                      "hbm_frac": round(compulsory_bytes(kind, cfg, w2) / (ev2 * 1e-3) / 1e9
+                      "hbm_frac": round(compulsory_bytes(kind, cfg, w2, op) / (ev2 * 1e-3) / 1e9
                                         / HBM_PEAK_GBS, 4)}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(kind, cfg)
+        out["cpu_baseline"] = (cpu_baseline(kind, cfg) if op == "selinv"
+                               else cpu_baseline_vjp(kind, cfg))
     print(json.dumps(out), flush=True)
 
 
