@@ -58,8 +58,11 @@ def load(path: str | None = None):
     lib.oracle_num_threads.argtypes = []
     lib.oracle_tree_vjp.argtypes = [i64, i32, vp, vp, vp, vp, vp, ctypes.c_double, vp, vp]
     lib.oracle_chain_vjp.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_tree_apply.argtypes = [i64, i32, vp, vp, vp, i64, vp, vp, i32]
+    lib.oracle_chain_apply.argtypes = [i64, i64, i32, vp, vp, i64, vp, vp, i32, vp]
     for f in (lib.oracle_chain, lib.oracle_star, lib.oracle_tree, lib.oracle_tree_depths,
-              lib.oracle_num_threads, lib.oracle_tree_vjp, lib.oracle_chain_vjp):
+              lib.oracle_num_threads, lib.oracle_tree_vjp, lib.oracle_chain_vjp,
+              lib.oracle_tree_apply, lib.oracle_chain_apply):
         f.restype = ctypes.c_int
     if path == _LIB:
         _lib = lib
@@ -216,3 +219,62 @@ def star_vjp(center, leaves, coupling, gc_bar, gl_bar, gx_bar, ld_bar, lib=None)
         cb[m], lvb[m] = db[0], db[1:]
         cpb[m] = np.swapaxes(eb[1:], -1, -2)
     return cb, lvb, cpb
+
+
+# ------------------------------------------------- shared-factor siblings
+# Solve A x = y and the Gaussian sampling transform x = L^{-T} D^{-1/2} z from
+# the collect's block LDL^T factor (oracle.c states the recurrences).  Vectors
+# are [..., n, b, k]; mode "solve" or "sample".
+
+_MODES = {"solve": 0, "sample": 1}
+
+
+def tree_apply(parent, diag, edge, vec, mode, lib=None):
+    """vec [n, b, k] -> out [n, b, k]."""
+    lib = lib or load()
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    diag, edge, vec = _f64(diag), _f64(edge), _f64(vec)
+    n, b = diag.shape[0], diag.shape[1]
+    assert edge.shape == diag.shape and vec.shape[:2] == (n, b)
+    k = vec.shape[2]
+    out = np.empty_like(vec)
+    rc = lib.oracle_tree_apply(n, b, _p(parent), _p(diag), _p(edge), k, _p(vec), _p(out),
+                               _MODES[mode])
+    if rc:
+        raise OracleError("oracle_tree_apply status %d" % rc)
+    return out
+
+
+def chain_apply(diag, lower, vec, mode, lib=None):
+    """Chains as path trees rooted at their last block.  vec [B, L, b, k]
+    -> (out [B, L, b, k], status [B]: 0 or 3 = not PD)."""
+    lib = lib or load()
+    diag, lower, vec = _f64(diag), _f64(lower), _f64(vec)
+    B, L, b = diag.shape[0], diag.shape[1], diag.shape[2]
+    assert vec.shape[:3] == (B, L, b)
+    k = vec.shape[3]
+    out = np.empty_like(vec)
+    st = np.empty(B, np.int32)
+    rc = lib.oracle_chain_apply(B, L, b, _p(diag), _p(lower), k, _p(vec), _p(out),
+                                _MODES[mode], _p(st))
+    if rc:
+        raise OracleError("oracle_chain_apply status %d" % rc)
+    return out, st
+
+
+def star_apply(center, leaves, coupling, vec_center, vec_leaves, mode, lib=None):
+    """Stars as depth-1 trees (centre = node 0, leaf j = node j + 1, edge
+    E_{j+1} = coupling[j]^T).  vec_center [B, b, k], vec_leaves [B, K, b, k]
+    -> (out_center, out_leaves)."""
+    center, leaves, coupling = _f64(center), _f64(leaves), _f64(coupling)
+    B, K, b = leaves.shape[0], leaves.shape[1], leaves.shape[2]
+    parent = np.array([-1] + [0] * K, dtype=np.int32)
+    oc = np.empty_like(_f64(vec_center))
+    ol = np.empty_like(_f64(vec_leaves))
+    for m in range(B):
+        diag = np.concatenate([center[m][None], leaves[m]])
+        edge = np.concatenate([np.zeros((1, b, b)), np.swapaxes(coupling[m], -1, -2)])
+        vec = np.concatenate([_f64(vec_center)[m][None], _f64(vec_leaves)[m]])
+        out = tree_apply(parent, diag, edge, vec, mode, lib=lib)
+        oc[m], ol[m] = out[0], out[1:]
+    return oc, ol

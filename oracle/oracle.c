@@ -607,6 +607,157 @@ ORACLE_API int oracle_chain_vjp(int64_t B, int64_t L, int b, const double *diag,
   return 0;
 }
 
+/* ---------------------------------------------- shared-factor siblings */
+
+/* Solve and Gaussian sampling from the factor of the collect pass (the
+ * gabp-sparse-inv 0.3.2 page: junction_solve, tree_logdet / junction_logdet and
+ * sample_gaussian_tree passages, all reusing "the same factorization").  The
+ * collect is a block LDL^T factorisation A = L D L^T with D = blockdiag(S_v)
+ * and L_{p,v} = X_v = E_v S_v^{-1}, unit block lower triangular in any
+ * children-first order:
+ *   solve A x = y:   u = y; children first: u_p -= X_v u_v;
+ *                    w_v = S_v^{-1} u_v (two triangular solves, S_v = R_v R_v^T);
+ *                    x_root = w_root; parents first: x_v = w_v - X_v^T x_p
+ *   sample:          x = L^{-T} D^{-1/2} z with D^{-1/2}_v = R_v^{-T}, the
+ *                    upper triangular factor of S_v^{-1}; then
+ *                    Cov(x) = L^{-T} D^{-1} L^{-1} = A^{-1} for z ~ N(0, I):
+ *                    w_v = R_v^{-T} z_v, then the same parents-first sweep.
+ * Vectors are [n][b][k] (k right-hand sides, k fastest).  mode 0 = solve,
+ * 1 = sample.  Returns 0, 2 (invalid parent array) or 3 (a pivot is not
+ * positive definite: out is NaN). */
+
+/* R Y = Bm, R lower triangular, Y and Bm b x k */
+static void trsv_L(int b, int64_t k, const double *R, const double *Bm, double *Y) {
+  for (int64_t c = 0; c < k; ++c)
+    for (int i = 0; i < b; ++i) {
+      double s = Bm[i * k + c];
+      for (int t = 0; t < i; ++t) s -= R[i * b + t] * Y[t * k + c];
+      Y[i * k + c] = s / R[i * b + i];
+    }
+}
+
+/* R^T Y = Bm, R lower triangular */
+static void trsv_LT(int b, int64_t k, const double *R, const double *Bm, double *Y) {
+  for (int64_t c = 0; c < k; ++c)
+    for (int i = b - 1; i >= 0; --i) {
+      double s = Bm[i * k + c];
+      for (int t = i + 1; t < b; ++t) s -= R[t * b + i] * Y[t * k + c];
+      Y[i * k + c] = s / R[i * b + i];
+    }
+}
+
+static int tree_ldl_apply(int64_t n, int b, const int32_t *parent, const double *diag,
+                          const double *edge, int64_t k, const double *in, double *out,
+                          int mode) {
+  const int64_t bb = (int64_t)b * b, bk = (int64_t)b * k;
+  int32_t *depth = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+  int64_t root = -1;
+  if (tree_depths(n, parent, depth, &root)) {
+    free(depth);
+    return 2;
+  }
+  int32_t H = 0;
+  for (int64_t v = 0; v < n; ++v)
+    if (depth[v] > H) H = depth[v];
+  int64_t *cnt = (int64_t *)calloc((size_t)H + 2, sizeof(int64_t));
+  for (int64_t v = 0; v < n; ++v) cnt[depth[v] + 1]++;
+  for (int32_t d = 0; d <= H; ++d) cnt[d + 1] += cnt[d];
+  int64_t *order = (int64_t *)malloc(sizeof(int64_t) * (size_t)n);
+  int64_t *fillp = (int64_t *)malloc(sizeof(int64_t) * ((size_t)H + 1));
+  for (int32_t d = 0; d <= H; ++d) fillp[d] = cnt[d];
+  for (int64_t v = 0; v < n; ++v) order[fillp[depth[v]]++] = v;
+
+  double *S = (double *)malloc(sizeof(double) * n * bb);
+  double *R = (double *)malloc(sizeof(double) * n * bb);
+  double *X = (double *)calloc((size_t)(n * bb), sizeof(double));
+  double *w = (double *)malloc(sizeof(double) * n * bk);
+  double *u = (double *)malloc(sizeof(double) * n * bk);
+  double *t = (double *)malloc(sizeof(double) * bk);
+  double *ws = (double *)malloc(sizeof(double) * 3 * bb);
+  int rc = 0;
+  /* collect: R_v and X_v, deepest level first */
+  memcpy(S, diag, sizeof(double) * n * bb);
+  for (int32_t d = H; d >= 0 && !rc; --d)
+    for (int64_t q = cnt[d]; q < cnt[d + 1]; ++q) {
+      const int64_t v = order[q], p = parent[v];
+      if (chol(b, S + v * bb, R + v * bb)) {
+        rc = 3;
+        break;
+      }
+      if (p >= 0) collect_edge(b, R + v * bb, edge + v * bb, S + p * bb, X + v * bb, ws,
+                               ws + bb, ws + 2 * bb);
+    }
+  if (rc) {
+    fill_nan(out, n * bk);
+  } else {
+    if (mode == 0) {
+      memcpy(u, in, sizeof(double) * n * bk);
+      for (int32_t d = H; d >= 1; --d) /* L u = y, children first */
+        for (int64_t q = cnt[d]; q < cnt[d + 1]; ++q) {
+          const int64_t v = order[q], p = parent[v];
+          for (int i = 0; i < b; ++i)
+            for (int64_t c = 0; c < k; ++c) {
+              double s = 0.0;
+              for (int j = 0; j < b; ++j) s += X[v * bb + i * b + j] * u[v * bk + j * k + c];
+              u[p * bk + i * k + c] -= s;
+            }
+        }
+      for (int64_t v = 0; v < n; ++v) { /* D w = u */
+        trsv_L(b, k, R + v * bb, u + v * bk, t);
+        trsv_LT(b, k, R + v * bb, t, w + v * bk);
+      }
+    } else {
+      for (int64_t v = 0; v < n; ++v) trsv_LT(b, k, R + v * bb, in + v * bk, w + v * bk);
+    }
+    /* L^T x = w, parents first */
+    memcpy(out + root * bk, w + root * bk, sizeof(double) * bk);
+    for (int32_t d = 1; d <= H; ++d)
+      for (int64_t q = cnt[d]; q < cnt[d + 1]; ++q) {
+        const int64_t v = order[q], p = parent[v];
+        for (int i = 0; i < b; ++i)
+          for (int64_t c = 0; c < k; ++c) {
+            double s = 0.0;
+            for (int j = 0; j < b; ++j) s += X[v * bb + j * b + i] * out[p * bk + j * k + c];
+            out[v * bk + i * k + c] = w[v * bk + i * k + c] - s;
+          }
+      }
+  }
+  free(depth); free(cnt); free(order); free(fillp);
+  free(S); free(R); free(X); free(w); free(u); free(t); free(ws);
+  return rc;
+}
+
+ORACLE_API int oracle_tree_apply(int64_t n, int b, const int32_t *parent, const double *diag,
+                                 const double *edge, int64_t k, const double *in, double *out,
+                                 int mode) {
+  if (n < 1 || b < 1 || k < 0 || !parent || !diag || !edge || !in || !out) return 1;
+  if (mode != 0 && mode != 1) return 1;
+  return tree_ldl_apply(n, b, parent, diag, edge, k, in, out, mode);
+}
+
+/* Chains as path trees rooted at the last block, one matrix after another;
+ * status[m] = 0 or 3. */
+ORACLE_API int oracle_chain_apply(int64_t B, int64_t L, int b, const double *diag,
+                                  const double *lower, int64_t k, const double *in, double *out,
+                                  int mode, int32_t *status) {
+  if (B < 0 || L < 1 || b < 1 || k < 0 || !diag || !in || !out || !status) return 1;
+  if (L > 1 && !lower) return 1;
+  if (mode != 0 && mode != 1) return 1;
+  const int64_t bb = (int64_t)b * b, bk = (int64_t)b * k;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t m = 0; m < B; ++m) {
+    int32_t *par = (int32_t *)malloc(sizeof(int32_t) * (size_t)L);
+    double *e = (double *)calloc((size_t)(L * bb), sizeof(double));
+    for (int64_t i = 0; i < L; ++i) par[i] = i + 1 < L ? (int32_t)(i + 1) : -1;
+    if (L > 1) memcpy(e, lower + m * (L - 1) * bb, sizeof(double) * (L - 1) * bb);
+    status[m] = tree_ldl_apply(L, b, par, diag + m * L * bb, e, k, in + m * L * bk,
+                               out + m * L * bk, mode);
+    free(par);
+    free(e);
+  }
+  return 0;
+}
+
 /* Depth of every node of a valid tree (host helper for the tests); returns 0,
  * or 2 for an invalid parent array. */
 ORACLE_API int oracle_tree_depths(int64_t n, const int32_t *parent, int32_t *depth) {
