@@ -226,6 +226,106 @@ SELINV_API int selinv_tree_vjp_f32(const selinv_tree_plan *plan, const float *di
                         const double *logdet_bar, float *diag_bar, float *edge_bar,
                         int32_t *info, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ----------------------------------------------- shared-factor siblings
+ * "Factor once, do everything" (gabp-sparse-inv 0.3.2 page: tree_logdet /
+ * junction_logdet take log det A straight from the LDL^T factorization,
+ * junction_solve solves on the same pattern sharing it, and
+ * sample_gaussian_tree draws x ~ N(0, A^{-1}) reusing it).  The collect pass
+ * is a block LDL^T factorisation A = L D L^T, D = blockdiag(S_v),
+ * L_{p,v} = E_v S_v^{-1}; the *factor* calls run it once and keep the S_v^{-1}
+ * in a caller-owned buffer, and the *solve* / *sample* calls reuse it:
+ *   solve:  x = A^{-1} y (k right-hand sides at once);
+ *   sample: x = L^{-T} D^{-1/2} z with D^{-1/2}_v the upper triangular
+ *           factor U_v of S_v^{-1} (U_v U_v^T = S_v^{-1}; U_v = R_v^{-T} for
+ *           S_v = R_v R_v^T), so x ~ N(0, A^{-1}) when z ~ N(0, I).  The caller
+ *           draws z; the map z -> x is deterministic.
+ * A factor call with factor == NULL computes log det and info only (the
+ * log-det fast path).
+ *
+ * The factor buffer's layout is private to the library: size it with the
+ * matching *_factor_bytes query, keep it 16-byte aligned, and pass it only to
+ * solve / sample calls with the same sizes, dtype (and plan) and the same
+ * edge blocks as the factor call.  Where that call reported info != 0 for a
+ * matrix, that matrix's solve / sample results are unspecified.
+ * Vectors (y, z, x) are [..., n_blocks, b, k] row-major (k fastest), with no
+ * alignment requirement; x must not alias y / z.  Other conventions (stream,
+ * workspace, return status) as above. */
+
+/* chain: factor [B][L] packed blocks; y, z, x [B][L][b][k] */
+SELINV_API size_t selinv_chain_factor_bytes(int dtype_bytes, int64_t B, int64_t L, int32_t b);
+SELINV_API int selinv_chain_factor_f64(int64_t B, int64_t L, int32_t b, const double *diag,
+                            const double *lower, double *factor, double *logdet, int32_t *info,
+                            void *stream);
+SELINV_API int selinv_chain_factor_f32(int64_t B, int64_t L, int32_t b, const float *diag,
+                            const float *lower, float *factor, double *logdet, int32_t *info,
+                            void *stream);
+SELINV_API int selinv_chain_solve_f64(int64_t B, int64_t L, int32_t b, const double *lower,
+                           const double *factor, int64_t k, const double *y, double *x,
+                           void *stream);
+SELINV_API int selinv_chain_solve_f32(int64_t B, int64_t L, int32_t b, const float *lower,
+                           const float *factor, int64_t k, const float *y, float *x,
+                           void *stream);
+SELINV_API int selinv_chain_sample_f64(int64_t B, int64_t L, int32_t b, const double *lower,
+                            const double *factor, int64_t k, const double *z, double *x,
+                            void *stream);
+SELINV_API int selinv_chain_sample_f32(int64_t B, int64_t L, int32_t b, const float *lower,
+                            const float *factor, int64_t k, const float *z, float *x,
+                            void *stream);
+
+/* star: vectors split as the centre [B][b][k] and the leaves [B][K][b][k] */
+SELINV_API size_t selinv_star_factor_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b);
+SELINV_API size_t selinv_star_factor_workspace_bytes(int dtype_bytes, int64_t B, int64_t K,
+                                          int32_t b);
+SELINV_API size_t selinv_star_solve_workspace_bytes(int dtype_bytes, int64_t B, int64_t K,
+                                         int32_t b, int64_t k);
+SELINV_API int selinv_star_factor_f64(int64_t B, int64_t K, int32_t b, const double *center,
+                           const double *leaves, const double *coupling, double *factor,
+                           double *logdet, int32_t *info, void *workspace,
+                           size_t workspace_bytes, void *stream);
+SELINV_API int selinv_star_factor_f32(int64_t B, int64_t K, int32_t b, const float *center,
+                           const float *leaves, const float *coupling, float *factor,
+                           double *logdet, int32_t *info, void *workspace,
+                           size_t workspace_bytes, void *stream);
+SELINV_API int selinv_star_solve_f64(int64_t B, int64_t K, int32_t b, const double *coupling,
+                          const double *factor, int64_t k, const double *y_center,
+                          const double *y_leaves, double *x_center, double *x_leaves,
+                          void *workspace, size_t workspace_bytes, void *stream);
+SELINV_API int selinv_star_solve_f32(int64_t B, int64_t K, int32_t b, const float *coupling,
+                          const float *factor, int64_t k, const float *y_center,
+                          const float *y_leaves, float *x_center, float *x_leaves,
+                          void *workspace, size_t workspace_bytes, void *stream);
+SELINV_API int selinv_star_sample_f64(int64_t B, int64_t K, int32_t b, const double *coupling,
+                           const double *factor, int64_t k, const double *z_center,
+                           const double *z_leaves, double *x_center, double *x_leaves,
+                           void *stream);
+SELINV_API int selinv_star_sample_f32(int64_t B, int64_t K, int32_t b, const float *coupling,
+                           const float *factor, int64_t k, const float *z_center,
+                           const float *z_leaves, float *x_center, float *x_leaves,
+                           void *stream);
+
+/* tree: vectors [n][b][k] by node index */
+SELINV_API size_t selinv_tree_factor_bytes(const selinv_tree_plan *plan);
+SELINV_API size_t selinv_tree_factor_workspace_bytes(const selinv_tree_plan *plan);
+SELINV_API size_t selinv_tree_solve_workspace_bytes(const selinv_tree_plan *plan, int64_t k);
+SELINV_API int selinv_tree_factor_f64(const selinv_tree_plan *plan, const double *diag,
+                           const double *edge, double *factor, double *logdet, int32_t *info,
+                           void *workspace, size_t workspace_bytes, void *stream);
+SELINV_API int selinv_tree_factor_f32(const selinv_tree_plan *plan, const float *diag,
+                           const float *edge, float *factor, double *logdet, int32_t *info,
+                           void *workspace, size_t workspace_bytes, void *stream);
+SELINV_API int selinv_tree_solve_f64(const selinv_tree_plan *plan, const double *edge,
+                          const double *factor, int64_t k, const double *y, double *x,
+                          void *workspace, size_t workspace_bytes, void *stream);
+SELINV_API int selinv_tree_solve_f32(const selinv_tree_plan *plan, const float *edge,
+                          const float *factor, int64_t k, const float *y, float *x,
+                          void *workspace, size_t workspace_bytes, void *stream);
+SELINV_API int selinv_tree_sample_f64(const selinv_tree_plan *plan, const double *edge,
+                           const double *factor, int64_t k, const double *z, double *x,
+                           void *stream);
+SELINV_API int selinv_tree_sample_f32(const selinv_tree_plan *plan, const float *edge,
+                           const float *factor, int64_t k, const float *z, float *x,
+                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -104,6 +104,29 @@ def lib():
         f = getattr(L, name)
         f.argtypes = [vp] * 9 + [vp, sz, vp]
         f.restype = ctypes.c_int
+    q = {"selinv_chain_factor_bytes": [ctypes.c_int, i64, i64, i32],
+         "selinv_star_factor_bytes": [ctypes.c_int, i64, i64, i32],
+         "selinv_star_factor_workspace_bytes": [ctypes.c_int, i64, i64, i32],
+         "selinv_star_solve_workspace_bytes": [ctypes.c_int, i64, i64, i32, i64],
+         "selinv_tree_factor_bytes": [vp], "selinv_tree_factor_workspace_bytes": [vp],
+         "selinv_tree_solve_workspace_bytes": [vp, i64]}
+    for name, args in q.items():
+        getattr(L, name).argtypes = args
+        getattr(L, name).restype = sz
+    sigs = {"chain_factor": [i64, i64, i32, vp, vp, vp, vp, vp, vp],
+            "chain_solve": [i64, i64, i32, vp, vp, i64, vp, vp, vp],
+            "chain_sample": [i64, i64, i32, vp, vp, i64, vp, vp, vp],
+            "star_factor": [i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "star_solve": [i64, i64, i32, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp],
+            "star_sample": [i64, i64, i32, vp, vp, i64, vp, vp, vp, vp, vp],
+            "tree_factor": [vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "tree_solve": [vp, vp, vp, i64, vp, vp, vp, sz, vp],
+            "tree_sample": [vp, vp, vp, i64, vp, vp, vp]}
+    for name, args in sigs.items():
+        for sfx in ("f64", "f32"):
+            f = getattr(L, "selinv_%s_%s" % (name, sfx))
+            f.argtypes = args
+            f.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -500,3 +523,252 @@ def tree_vjp(parent, diag, edge, G_diag_bar, G_edge_bar, logdet_bar=None, check=
     if return_info:
         return d_bar, e_bar, info
     return d_bar, e_bar
+
+
+# ------------------------------------------------- shared-factor siblings
+# One collect pass (the block LDL^T factorisation A = L D L^T) kept on the
+# device, then any number of solves x = A^{-1} y and Gaussian samples
+# x = L^{-T} D^{-1/2} z ~ N(0, A^{-1}) from it; log det comes with the factor
+# (or alone, without storing one).  Vectors are [..., n_blocks, b, k].
+
+def _vec(t, name, dev, dt, shape_prefix):
+    t = _check_tensor(t, name, dev, dt)
+    if tuple(t.shape[:len(shape_prefix)]) != tuple(shape_prefix) or t.dim() != len(shape_prefix) + 1:
+        raise ValueError("%s must be %s + (k,)" % (name, tuple(shape_prefix)))
+    return t
+
+
+def _normal_like(shape, dt, dev, generator):
+    return torch.randn(shape, dtype=dt, device=dev, generator=generator)
+
+
+class ChainFactor:
+    """Factor of block-tridiagonal chains (see chain_factor)."""
+
+    def __init__(self, lower, factor, logdet, info, shape):
+        self.lower, self.factor, self.logdet, self.info = lower, factor, logdet, info
+        self.batch, self.L, self.b = shape
+
+    def _apply(self, v, name, sample):
+        dev, dt = self.factor.device, self.factor.dtype
+        B = 1
+        for s_ in self.batch:
+            B *= s_
+        v = _vec(v, name, dev, dt, tuple(self.batch) + (self.L, self.b))
+        k = v.shape[-1]
+        x = torch.empty_like(v)
+        fn = "selinv_chain_%s_%s" % ("sample" if sample else "solve", _sfx(self.factor))
+        with torch.cuda.device(dev):
+            rc = getattr(lib(), fn)(B, self.L, self.b, _ptr(self.lower), _ptr(self.factor), k,
+                                    _ptr(v), _ptr(x), _stream(dev))
+        _status(rc, fn)
+        return x
+
+    def solve(self, y):
+        """x = A^{-1} y, y [..., L, b, k]."""
+        return self._apply(y, "y", False)
+
+    def sample(self, num_samples=None, z=None, generator=None):
+        """x = L^{-T} D^{-1/2} z ~ N(0, A^{-1}); z [..., L, b, k] given, or
+        drawn with torch.randn (k = num_samples columns)."""
+        if z is None:
+            z = _normal_like(tuple(self.batch) + (self.L, self.b, num_samples or 1),
+                             self.factor.dtype, self.factor.device, generator)
+        return self._apply(z, "z", True)
+
+
+def chain_factor(diag, lower, keep_factor=True):
+    """Collect pass of block-tridiagonal chains (diag [..., L, b, b], lower
+    [..., L-1, b, b]).  Returns a ChainFactor (logdet, info, solve, sample);
+    keep_factor=False computes log det and info only."""
+    dt, dev = diag.dtype, diag.device
+    diag = _check_tensor(diag, "diag", dev, dt)
+    lower = _check_tensor(lower, "lower", dev, dt)
+    sfx = _sfx(diag)
+    if diag.dim() < 3 or diag.shape[-1] != diag.shape[-2]:
+        raise ValueError("diag must be [..., L, b, b]")
+    *batch, L, b, _ = diag.shape
+    if L < 1 or b < 1 or b > MAX_B:
+        raise ValueError("need L >= 1 and 1 <= b <= %d" % MAX_B)
+    if tuple(lower.shape) != tuple(batch) + (L - 1, b, b):
+        raise ValueError("lower must be [..., L-1, b, b] matching diag")
+    B = 1
+    for s_ in batch:
+        B *= s_
+    L_ = lib()
+    factor = None
+    if keep_factor:
+        nbytes = L_.selinv_chain_factor_bytes(diag.element_size(), B, L, b)
+        factor = torch.empty(max(nbytes // diag.element_size(), 1), dtype=dt, device=dev)
+    logdet = torch.empty(tuple(batch), dtype=torch.float64, device=dev)
+    info = torch.empty(tuple(batch), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        rc = getattr(L_, "selinv_chain_factor_" + sfx)(B, L, b, _ptr(diag), _ptr(lower),
+                                                        _ptr(factor), _ptr(logdet), _ptr(info),
+                                                        _stream(dev))
+    _status(rc, "selinv_chain_factor_" + sfx)
+    return ChainFactor(lower, factor, logdet, info, (batch, L, b))
+
+
+def chain_logdet(diag, lower, return_info=False):
+    """log det A of block-tridiagonal chains without storing a factor."""
+    f = chain_factor(diag, lower, keep_factor=False)
+    return (f.logdet, f.info) if return_info else f.logdet
+
+
+class StarFactor:
+    """Factor of block-arrowhead matrices (see star_factor)."""
+
+    def __init__(self, coupling, factor, logdet, info, shape):
+        self.coupling, self.factor, self.logdet, self.info = coupling, factor, logdet, info
+        self.batch, self.K, self.b = shape
+
+    def _apply(self, vc, vl, sample):
+        dev, dt = self.factor.device, self.factor.dtype
+        B = 1
+        for s_ in self.batch:
+            B *= s_
+        vc = _vec(vc, "center vector", dev, dt, tuple(self.batch) + (self.b,))
+        vl = _vec(vl, "leaf vector", dev, dt, tuple(self.batch) + (self.K, self.b))
+        k = vc.shape[-1]
+        if vl.shape[-1] != k:
+            raise ValueError("centre and leaf vectors need the same k")
+        xc, xl = torch.empty_like(vc), torch.empty_like(vl)
+        sfx = _sfx(self.factor)
+        with torch.cuda.device(dev):
+            if sample:
+                rc = getattr(lib(), "selinv_star_sample_" + sfx)(
+                    B, self.K, self.b, _ptr(self.coupling), _ptr(self.factor), k, _ptr(vc),
+                    _ptr(vl), _ptr(xc), _ptr(xl), _stream(dev))
+            else:
+                nb = lib().selinv_star_solve_workspace_bytes(vc.element_size(), B, self.K,
+                                                             self.b, k)
+                ws = _workspace(nb, dev)
+                rc = getattr(lib(), "selinv_star_solve_" + sfx)(
+                    B, self.K, self.b, _ptr(self.coupling), _ptr(self.factor), k, _ptr(vc),
+                    _ptr(vl), _ptr(xc), _ptr(xl), _ptr(ws), nb, _stream(dev))
+        _status(rc, "selinv_star_%s_%s" % ("sample" if sample else "solve", sfx))
+        return xc, xl
+
+    def solve(self, y_center, y_leaves):
+        """x = A^{-1} y split as the centre [..., b, k] and leaves [..., K, b, k]."""
+        return self._apply(y_center, y_leaves, False)
+
+    def sample(self, num_samples=None, z_center=None, z_leaves=None, generator=None):
+        if z_center is None:
+            k = num_samples or 1
+            dt, dev = self.factor.dtype, self.factor.device
+            z_center = _normal_like(tuple(self.batch) + (self.b, k), dt, dev, generator)
+            z_leaves = _normal_like(tuple(self.batch) + (self.K, self.b, k), dt, dev, generator)
+        return self._apply(z_center, z_leaves, True)
+
+
+def star_factor(center, leaves, coupling, keep_factor=True):
+    """Collect pass of block-arrowhead matrices; returns a StarFactor."""
+    dt, dev = center.dtype, center.device
+    center = _check_tensor(center, "center", dev, dt)
+    leaves = _check_tensor(leaves, "leaves", dev, dt)
+    coupling = _check_tensor(coupling, "coupling", dev, dt)
+    sfx = _sfx(center)
+    *batch, b, _ = center.shape
+    if leaves.dim() != len(batch) + 3 or tuple(leaves.shape[:len(batch)]) != tuple(batch):
+        raise ValueError("leaves must be [..., K, b, b] matching center")
+    K = leaves.shape[len(batch)]
+    if tuple(leaves.shape) != tuple(batch) + (K, b, b) or coupling.shape != leaves.shape:
+        raise ValueError("leaves and coupling must be [..., K, b, b]")
+    if b < 1 or b > MAX_B:
+        raise ValueError("need 1 <= b <= %d" % MAX_B)
+    B = 1
+    for s_ in batch:
+        B *= s_
+    L_ = lib()
+    factor = None
+    if keep_factor:
+        nbytes = L_.selinv_star_factor_bytes(center.element_size(), B, K, b)
+        factor = torch.empty(max(nbytes // center.element_size(), 1), dtype=dt, device=dev)
+    logdet = torch.empty(tuple(batch), dtype=torch.float64, device=dev)
+    info = torch.empty(tuple(batch), dtype=torch.int32, device=dev)
+    nb = L_.selinv_star_factor_workspace_bytes(center.element_size(), B, K, b)
+    ws = _workspace(nb, dev)
+    with torch.cuda.device(dev):
+        rc = getattr(L_, "selinv_star_factor_" + sfx)(
+            B, K, b, _ptr(center), _ptr(leaves), _ptr(coupling), _ptr(factor), _ptr(logdet),
+            _ptr(info), _ptr(ws), nb, _stream(dev))
+    _status(rc, "selinv_star_factor_" + sfx)
+    return StarFactor(coupling, factor, logdet, info, (batch, K, b))
+
+
+def star_logdet(center, leaves, coupling, return_info=False):
+    f = star_factor(center, leaves, coupling, keep_factor=False)
+    return (f.logdet, f.info) if return_info else f.logdet
+
+
+class TreeFactor:
+    """Factor of a tree-structured matrix (see tree_factor)."""
+
+    def __init__(self, plan, edge, factor, logdet, info):
+        self.plan, self.edge, self.factor, self.logdet, self.info = plan, edge, factor, logdet, info
+
+    def _apply(self, v, name, sample):
+        dev, dt = self.factor.device, self.factor.dtype
+        v = _vec(v, name, dev, dt, (self.plan.n, self.plan.b))
+        k = v.shape[-1]
+        x = torch.empty_like(v)
+        sfx = _sfx(self.factor)
+        with torch.cuda.device(dev):
+            if sample:
+                rc = getattr(lib(), "selinv_tree_sample_" + sfx)(
+                    self.plan.handle, _ptr(self.edge), _ptr(self.factor), k, _ptr(v), _ptr(x),
+                    _stream(dev))
+            else:
+                nb = int(lib().selinv_tree_solve_workspace_bytes(self.plan.handle, k))
+                ws = _workspace(nb, dev)
+                rc = getattr(lib(), "selinv_tree_solve_" + sfx)(
+                    self.plan.handle, _ptr(self.edge), _ptr(self.factor), k, _ptr(v), _ptr(x),
+                    _ptr(ws), nb, _stream(dev))
+        _status(rc, "selinv_tree_%s_%s" % ("sample" if sample else "solve", sfx))
+        return x
+
+    def solve(self, y):
+        """x = A^{-1} y, y [n, b, k]."""
+        return self._apply(y, "y", False)
+
+    def sample(self, num_samples=None, z=None, generator=None):
+        if z is None:
+            z = _normal_like((self.plan.n, self.plan.b, num_samples or 1), self.factor.dtype,
+                             self.factor.device, generator)
+        return self._apply(z, "z", True)
+
+
+def tree_factor(parent, diag, edge, keep_factor=True, plan: TreePlan | None = None):
+    """Collect pass of a tree-structured matrix; returns a TreeFactor."""
+    dt, dev = diag.dtype, diag.device
+    diag = _check_tensor(diag, "diag", dev, dt)
+    edge = _check_tensor(edge, "edge", dev, dt)
+    sfx = _sfx(diag)
+    if diag.dim() != 3 or diag.shape[1] != diag.shape[2] or edge.shape != diag.shape:
+        raise ValueError("diag and edge must be [n, b, b]")
+    n, b = diag.shape[0], diag.shape[1]
+    if plan is None:
+        plan = tree_plan(parent, b, dt, dev)
+    if plan.n != n or plan.b != b or plan.dtype != dt:
+        raise ValueError("plan does not match (n, b, dtype)")
+    factor = None
+    if keep_factor:
+        nbytes = int(lib().selinv_tree_factor_bytes(plan.handle))
+        factor = torch.empty(max(nbytes // diag.element_size(), 1), dtype=dt, device=dev)
+    logdet = torch.empty((), dtype=torch.float64, device=dev)
+    info = torch.empty((), dtype=torch.int32, device=dev)
+    nb = int(lib().selinv_tree_factor_workspace_bytes(plan.handle))
+    ws = _workspace(nb, dev)
+    with torch.cuda.device(dev):
+        rc = getattr(lib(), "selinv_tree_factor_" + sfx)(
+            plan.handle, _ptr(diag), _ptr(edge), _ptr(factor), logdet.data_ptr(),
+            info.data_ptr(), _ptr(ws), nb, _stream(dev))
+    _status(rc, "selinv_tree_factor_" + sfx)
+    return TreeFactor(plan, edge, factor, logdet, info)
+
+
+def tree_logdet(parent, diag, edge, return_info=False):
+    f = tree_factor(parent, diag, edge, keep_factor=False)
+    return (f.logdet, f.info) if return_info else f.logdet

@@ -29,6 +29,7 @@ SOURCES = [
     "chain_small.hip",
     "vjp_generic.hip", "vjp_chain_b16.hip", "vjp_star_b32.hip",
     "vjp_tree_b8.hip",
+    "shared_factor.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

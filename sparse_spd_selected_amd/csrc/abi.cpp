@@ -124,6 +124,102 @@ int tree_vjp_entry(const selinv_tree_plan *plan, const T *diag, const T *edge, c
   return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
 }
 
+template <typename T>
+int chain_factor_entry(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower, T *factor,
+                       double *logdet, int32_t *info, void *stream) {
+  if (B < 0 || L < 1 || bad_b(b) || B > 0x7fffffff) return SELINV_ERR_INVALID_ARG;
+  if (B == 0) return SELINV_OK;
+  if (!diag || !logdet || (L > 1 && !lower)) return SELINV_ERR_INVALID_ARG;
+  if (misaligned(diag) || misaligned(factor) || (L > 1 && misaligned(lower)))
+    return SELINV_ERR_INVALID_ARG;
+  const hipError_t e = selinv::chain_factor_launch<T>(B, L, b, diag, lower, factor, logdet, info,
+                                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
+}
+
+template <typename T>
+int chain_apply_entry(int64_t B, int64_t L, int32_t b, const T *lower, const T *factor,
+                      int64_t k, const T *in, T *out, bool sample, void *stream) {
+  if (B < 0 || L < 1 || bad_b(b) || k < 0 || B > 0x7fffffff || B * ((k + 15) / 16) > 0x7fffffff)
+    return SELINV_ERR_INVALID_ARG;
+  if (B == 0 || k == 0) return SELINV_OK;
+  if (!factor || !in || !out || (L > 1 && !lower)) return SELINV_ERR_INVALID_ARG;
+  if (misaligned(factor) || (L > 1 && misaligned(lower))) return SELINV_ERR_INVALID_ARG;
+  const hipError_t e = selinv::chain_apply_launch<T>(B, L, b, k, sample, lower, factor, in, out,
+                                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
+}
+
+template <typename T>
+int star_factor_entry(int64_t B, int64_t K, int32_t b, const T *center, const T *leaves,
+                      const T *coupling, T *factor, double *logdet, int32_t *info, void *ws,
+                      size_t ws_bytes, void *stream) {
+  if (B < 0 || K < 0 || bad_b(b) || B > 0x7fffffff || B * K > 0x7fffffff)
+    return SELINV_ERR_INVALID_ARG;
+  if (B == 0) return SELINV_OK;
+  if (!center || !logdet || (K > 0 && (!leaves || !coupling))) return SELINV_ERR_INVALID_ARG;
+  if (misaligned(center) || misaligned(factor) ||
+      (K > 0 && (misaligned(leaves) || misaligned(coupling))))
+    return SELINV_ERR_INVALID_ARG;
+  const size_t need = selinv::star_factor_workspace_bytes(sizeof(T), B, K, b);
+  if (ws_bytes < need || (need && !ws) || misaligned_ws(ws)) return SELINV_ERR_INVALID_ARG;
+  const hipError_t e = selinv::star_factor_launch<T>(B, K, b, center, leaves, coupling, factor,
+                                                     logdet, info, ws,
+                                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
+}
+
+template <typename T>
+int star_apply_entry(int64_t B, int64_t K, int32_t b, const T *coupling, const T *factor,
+                     int64_t k, const T *in_c, const T *in_l, T *x_c, T *x_l, void *ws,
+                     size_t ws_bytes, bool sample, void *stream) {
+  const int64_t nch = (k + 15) / 16;
+  if (B < 0 || K < 0 || bad_b(b) || k < 0 || B > 0x7fffffff || B * K > 0x7fffffff ||
+      B * (K + 1) * nch > 0x7fffffff)
+    return SELINV_ERR_INVALID_ARG;
+  if (B == 0 || k == 0) return SELINV_OK;
+  if (!factor || !in_c || !x_c || (K > 0 && (!coupling || !in_l || !x_l)))
+    return SELINV_ERR_INVALID_ARG;
+  if (misaligned(factor) || (K > 0 && misaligned(coupling))) return SELINV_ERR_INVALID_ARG;
+  const size_t need = sample ? 0 : selinv::star_apply_workspace_bytes(sizeof(T), B, K, b, k);
+  if (ws_bytes < need || (need && !ws) || (need && misaligned_ws(ws)))
+    return SELINV_ERR_INVALID_ARG;
+  const hipError_t e = selinv::star_apply_launch<T>(B, K, b, k, sample, coupling, factor, in_c,
+                                                    in_l, x_c, x_l, ws,
+                                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
+}
+
+template <typename T>
+int tree_factor_entry(const selinv_tree_plan *plan, const T *diag, const T *edge, T *factor,
+                      double *logdet, int32_t *info, void *ws, size_t ws_bytes, void *stream) {
+  if (!plan || plan->dtype_bytes != static_cast<int>(sizeof(T))) return SELINV_ERR_INVALID_ARG;
+  if (!diag || !edge || !logdet) return SELINV_ERR_INVALID_ARG;
+  if (misaligned(diag) || misaligned(edge) || misaligned(factor)) return SELINV_ERR_INVALID_ARG;
+  const size_t need = selinv::tree_factor_workspace_bytes(plan);
+  if (ws_bytes < need || (need && !ws) || misaligned_ws(ws)) return SELINV_ERR_INVALID_ARG;
+  const hipError_t e = selinv::tree_factor_launch<T>(plan, diag, edge, factor, logdet, info, ws,
+                                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
+}
+
+template <typename T>
+int tree_apply_entry(const selinv_tree_plan *plan, const T *edge, const T *factor, int64_t k,
+                     const T *in, T *out, void *ws, size_t ws_bytes, bool sample, void *stream) {
+  if (!plan || plan->dtype_bytes != static_cast<int>(sizeof(T)) || k < 0)
+    return SELINV_ERR_INVALID_ARG;
+  if (plan->n * ((k + 15) / 16) > 0x7fffffff) return SELINV_ERR_INVALID_ARG;
+  if (k == 0) return SELINV_OK;
+  if (!edge || !factor || !in || !out) return SELINV_ERR_INVALID_ARG;
+  if (misaligned(edge) || misaligned(factor)) return SELINV_ERR_INVALID_ARG;
+  const size_t need = sample ? 0 : selinv::tree_apply_workspace_bytes(plan, k);
+  if (ws_bytes < need || (need && !ws) || (need && misaligned_ws(ws)))
+    return SELINV_ERR_INVALID_ARG;
+  const hipError_t e = selinv::tree_apply_launch<T>(plan, k, sample, edge, factor, in, out, ws,
+                                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -264,6 +360,151 @@ int selinv_tree_vjp_f32(const selinv_tree_plan *plan, const float *diag, const f
                         void *workspace, size_t workspace_bytes, void *stream) {
   return tree_vjp_entry<float>(plan, diag, edge, G_diag_bar, G_edge_bar, logdet_bar, diag_bar,
                                edge_bar, info, workspace, workspace_bytes, stream);
+}
+
+size_t selinv_chain_factor_bytes(int dtype_bytes, int64_t B, int64_t L, int32_t b) {
+  if ((dtype_bytes != 4 && dtype_bytes != 8) || B < 0 || L < 1 || bad_b(b)) return 0;
+  return selinv::chain_factor_bytes(dtype_bytes, B, L, b);
+}
+
+size_t selinv_star_factor_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b) {
+  if ((dtype_bytes != 4 && dtype_bytes != 8) || B < 0 || K < 0 || bad_b(b)) return 0;
+  return selinv::star_factor_bytes(dtype_bytes, B, K, b);
+}
+
+size_t selinv_star_factor_workspace_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b) {
+  if ((dtype_bytes != 4 && dtype_bytes != 8) || B < 0 || K < 0 || bad_b(b)) return 0;
+  return selinv::star_factor_workspace_bytes(dtype_bytes, B, K, b);
+}
+
+size_t selinv_star_solve_workspace_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b,
+                                         int64_t k) {
+  if ((dtype_bytes != 4 && dtype_bytes != 8) || B < 0 || K < 0 || bad_b(b) || k < 0) return 0;
+  return selinv::star_apply_workspace_bytes(dtype_bytes, B, K, b, k);
+}
+
+size_t selinv_tree_factor_bytes(const selinv_tree_plan *plan) {
+  return plan ? selinv::tree_factor_bytes(plan) : 0;
+}
+
+size_t selinv_tree_factor_workspace_bytes(const selinv_tree_plan *plan) {
+  return plan ? selinv::tree_factor_workspace_bytes(plan) : 0;
+}
+
+size_t selinv_tree_solve_workspace_bytes(const selinv_tree_plan *plan, int64_t k) {
+  return (plan && k >= 0) ? selinv::tree_apply_workspace_bytes(plan, k) : 0;
+}
+
+int selinv_chain_factor_f64(int64_t B, int64_t L, int32_t b, const double *diag,
+                            const double *lower, double *factor, double *logdet, int32_t *info,
+                            void *stream) {
+  return chain_factor_entry<double>(B, L, b, diag, lower, factor, logdet, info, stream);
+}
+
+int selinv_chain_solve_f64(int64_t B, int64_t L, int32_t b, const double *lower, const double *factor,
+                           int64_t k, const double *y, double *x, void *stream) {
+  return chain_apply_entry<double>(B, L, b, lower, factor, k, y, x, false, stream);
+}
+
+int selinv_chain_sample_f64(int64_t B, int64_t L, int32_t b, const double *lower, const double *factor,
+                            int64_t k, const double *z, double *x, void *stream) {
+  return chain_apply_entry<double>(B, L, b, lower, factor, k, z, x, true, stream);
+}
+
+int selinv_star_factor_f64(int64_t B, int64_t K, int32_t b, const double *center, const double *leaves,
+                           const double *coupling, double *factor, double *logdet, int32_t *info,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  return star_factor_entry<double>(B, K, b, center, leaves, coupling, factor, logdet, info,
+                                workspace, workspace_bytes, stream);
+}
+
+int selinv_star_solve_f64(int64_t B, int64_t K, int32_t b, const double *coupling, const double *factor,
+                          int64_t k, const double *y_center, const double *y_leaves, double *x_center,
+                          double *x_leaves, void *workspace, size_t workspace_bytes, void *stream) {
+  return star_apply_entry<double>(B, K, b, coupling, factor, k, y_center, y_leaves, x_center,
+                               x_leaves, workspace, workspace_bytes, false, stream);
+}
+
+int selinv_star_sample_f64(int64_t B, int64_t K, int32_t b, const double *coupling,
+                           const double *factor, int64_t k, const double *z_center, const double *z_leaves,
+                           double *x_center, double *x_leaves, void *stream) {
+  return star_apply_entry<double>(B, K, b, coupling, factor, k, z_center, z_leaves, x_center,
+                               x_leaves, nullptr, 0, true, stream);
+}
+
+int selinv_tree_factor_f64(const selinv_tree_plan *plan, const double *diag, const double *edge,
+                           double *factor, double *logdet, int32_t *info, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  return tree_factor_entry<double>(plan, diag, edge, factor, logdet, info, workspace,
+                                workspace_bytes, stream);
+}
+
+int selinv_tree_solve_f64(const selinv_tree_plan *plan, const double *edge, const double *factor,
+                          int64_t k, const double *y, double *x, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  return tree_apply_entry<double>(plan, edge, factor, k, y, x, workspace, workspace_bytes, false,
+                               stream);
+}
+
+int selinv_tree_sample_f64(const selinv_tree_plan *plan, const double *edge, const double *factor,
+                           int64_t k, const double *z, double *x, void *stream) {
+  return tree_apply_entry<double>(plan, edge, factor, k, z, x, nullptr, 0, true, stream);
+}
+
+int selinv_chain_factor_f32(int64_t B, int64_t L, int32_t b, const float *diag,
+                            const float *lower, float *factor, double *logdet, int32_t *info,
+                            void *stream) {
+  return chain_factor_entry<float>(B, L, b, diag, lower, factor, logdet, info, stream);
+}
+
+int selinv_chain_solve_f32(int64_t B, int64_t L, int32_t b, const float *lower, const float *factor,
+                           int64_t k, const float *y, float *x, void *stream) {
+  return chain_apply_entry<float>(B, L, b, lower, factor, k, y, x, false, stream);
+}
+
+int selinv_chain_sample_f32(int64_t B, int64_t L, int32_t b, const float *lower, const float *factor,
+                            int64_t k, const float *z, float *x, void *stream) {
+  return chain_apply_entry<float>(B, L, b, lower, factor, k, z, x, true, stream);
+}
+
+int selinv_star_factor_f32(int64_t B, int64_t K, int32_t b, const float *center, const float *leaves,
+                           const float *coupling, float *factor, double *logdet, int32_t *info,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  return star_factor_entry<float>(B, K, b, center, leaves, coupling, factor, logdet, info,
+                                workspace, workspace_bytes, stream);
+}
+
+int selinv_star_solve_f32(int64_t B, int64_t K, int32_t b, const float *coupling, const float *factor,
+                          int64_t k, const float *y_center, const float *y_leaves, float *x_center,
+                          float *x_leaves, void *workspace, size_t workspace_bytes, void *stream) {
+  return star_apply_entry<float>(B, K, b, coupling, factor, k, y_center, y_leaves, x_center,
+                               x_leaves, workspace, workspace_bytes, false, stream);
+}
+
+int selinv_star_sample_f32(int64_t B, int64_t K, int32_t b, const float *coupling,
+                           const float *factor, int64_t k, const float *z_center, const float *z_leaves,
+                           float *x_center, float *x_leaves, void *stream) {
+  return star_apply_entry<float>(B, K, b, coupling, factor, k, z_center, z_leaves, x_center,
+                               x_leaves, nullptr, 0, true, stream);
+}
+
+int selinv_tree_factor_f32(const selinv_tree_plan *plan, const float *diag, const float *edge,
+                           float *factor, double *logdet, int32_t *info, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  return tree_factor_entry<float>(plan, diag, edge, factor, logdet, info, workspace,
+                                workspace_bytes, stream);
+}
+
+int selinv_tree_solve_f32(const selinv_tree_plan *plan, const float *edge, const float *factor,
+                          int64_t k, const float *y, float *x, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  return tree_apply_entry<float>(plan, edge, factor, k, y, x, workspace, workspace_bytes, false,
+                               stream);
+}
+
+int selinv_tree_sample_f32(const selinv_tree_plan *plan, const float *edge, const float *factor,
+                           int64_t k, const float *z, float *x, void *stream) {
+  return tree_apply_entry<float>(plan, edge, factor, k, z, x, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

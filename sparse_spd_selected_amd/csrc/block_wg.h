@@ -139,6 +139,73 @@ __device__ inline void gemm_symmetrized(T *Out, const T *Base, const T *A, const
   __syncthreads();
 }
 
+// Packed lower triangle of a symmetric block: entry (r, c), r >= c, at
+// r (r + 1) / 2 + c.  packed_entries(b) rounds the count up to a multiple of
+// four elements so that consecutive packed blocks stay 16-byte aligned.
+__host__ __device__ inline int packed_entries(int b) { return (b * (b + 1) / 2 + 3) / 4 * 4; }
+
+// dst = packed lower triangle of the symmetric block src (read from its
+// lower triangle)
+template <typename T>
+__device__ inline void pack_lower(T *dst, const T *src, int b) {
+  for (int e = tid(); e < b * b; e += nthreads()) {
+    const int r = e / b, c = e % b;
+    if (r >= c) dst[r * (r + 1) / 2 + c] = src[r * b + c];
+  }
+  __syncthreads();
+}
+
+// dst = the full symmetric block of a packed lower triangle
+template <typename T>
+__device__ inline void unpack_sym(T *dst, const T *src, int b) {
+  for (int e = tid(); e < b * b; e += nthreads()) {
+    const int r = e / b, c = e % b;
+    dst[e] = r >= c ? src[r * (r + 1) / 2 + c] : src[c * (c + 1) / 2 + r];
+  }
+  __syncthreads();
+}
+
+// Block times a block of vectors: Out (b x kc, row stride ldo) =
+// beta * Base + alpha * op(A) V, A b x b, V b x kc with row stride ldv, Base
+// with row stride ldo (may alias Out; null = 0).  Out must not alias A or V.
+template <typename T, bool TA>
+__device__ inline void bmv(T *Out, int ldo, T beta, const T *Base, T alpha, const T *A,
+                           const T *V, int ldv, int b, int kc) {
+  for (int e = tid(); e < b * kc; e += nthreads()) {
+    const int r = e / kc, c = e % kc;
+    T acc = T(0);
+    for (int t = 0; t < b; ++t) acc += (TA ? A[t * b + r] : A[r * b + t]) * V[t * ldv + c];
+    Out[r * ldo + c] = (Base ? beta * Base[r * ldo + c] : T(0)) + alpha * acc;
+  }
+  __syncthreads();
+}
+
+// U = the upper triangular factor of a symmetric positive definite block S
+// with U U^T = S and a positive diagonal (Cholesky in reversed index order:
+// columns j = b-1 .. 0, each from the columns to its right).  U is written in
+// full, zeros below the diagonal.  For S = A^{-1} with A = R R^T (R lower
+// triangular), U = R^{-T}.
+template <typename T>
+__device__ inline void rev_cholesky(T *U, const T *S, int b) {
+  for (int e = tid(); e < b * b; e += nthreads()) U[e] = T(0);
+  __syncthreads();
+  for (int j = b - 1; j >= 0; --j) {
+    if (tid() == 0) {
+      T d = S[j * b + j];
+      for (int t = j + 1; t < b; ++t) d -= U[j * b + t] * U[j * b + t];
+      U[j * b + j] = sqrt(d);
+    }
+    __syncthreads();
+    const T ujj = U[j * b + j];
+    for (int i = tid(); i < j; i += nthreads()) {
+      T s = S[i * b + j];
+      for (int t = j + 1; t < b; ++t) s -= U[i * b + t] * U[j * b + t];
+      U[i * b + j] = s / ujj;
+    }
+    __syncthreads();
+  }
+}
+
 // In-place inverse of a symmetric positive definite block by the symmetric
 // Gauss-Jordan sweep, without pivoting.  Sweeping pivot k maps
 //   a_ij -> a_ij - a_ik a_kj / d   (i, j != k),   a_ik -> a_ik / d,

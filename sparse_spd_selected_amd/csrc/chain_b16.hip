@@ -34,7 +34,10 @@ using f16::Frag;
 #define SELINV_CHAIN16_WAVES 4
 #endif
 
-template <typename T>
+// kFactor: the collect pass only (the shared factor of the solve and the
+// sampler): packed Sinv_i of every block, root included, goes to `state`
+// ([B][L][136]; null = log det and info only) and G_diag, G_lower are unused.
+template <typename T, bool kFactor>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SELINV_CHAIN16_WAVES, 8)))
 void chain16_kernel(int L, const T *__restrict__ diag, const T *__restrict__ lower,
                     T *__restrict__ G_diag, T *__restrict__ G_lower, double *__restrict__ logdet,
@@ -51,9 +54,8 @@ void chain16_kernel(int L, const T *__restrict__ diag, const T *__restrict__ low
   // with L == 1 there is no off-diagonal block (lower may be null); the
   // unconditional prefetch below then reads diagonal data it never uses
   const T *C = L > 1 ? lower + m * (L - 1) * BB : D;
-  T *Gd = G_diag + m * L * BB;
-  T *Gl = G_lower + m * (L - 1) * BB;
-  T *st = state + m * L * PB;
+  T *st = state ? state + m * L * PB : nullptr;
+  const bool keep = !kFactor || st;  // the packed Sinv_i are stored
   const io16::SymLanes<T> sl(g, j, lane);
 
   f16::PivotLog pl;  // product of all pivots of the chain (log taken once)
@@ -90,7 +92,7 @@ void chain16_kernel(int L, const T *__restrict__ diag, const T *__restrict__ low
     const Frag<T> Ct = io16::get_frag_t(tB, g, j);  // O(C_i^T)
     f16::wave_sync();
     io16::put(tA, lane, Du);
-    io16::store_packed(st + i * PB, lane, pk);
+    if (keep) io16::store_packed(st + i * PB, lane, pk);
     f16::wave_sync();
     const Frag<T> Dn1 = sl.get_sym(tA);
     const Frag<T> Y = f16::mm<T>(S, Ct, f16::zero<T>());  // Sinv_i C_i^T
@@ -103,6 +105,21 @@ void chain16_kernel(int L, const T *__restrict__ diag, const T *__restrict__ low
   }
   if (i < L - 1) collect(i, C0, D0, C1, D1);
   if (f16::gj_inverse(S, col, g, j, pl) && !fail) fail = L;  // the root block
+  if constexpr (kFactor) {
+    if (st) {
+      f16::wave_sync();
+      io16::put_frag(tA, g, j, S);
+      f16::wave_sync();
+      io16::store_packed(st + (L - 1) * PB, lane, sl.gather_packed(tA));
+    }
+    if (lane == 0) {
+      logdet[m] = fail ? __builtin_nan("") : pl.log();
+      if (info) info[m] = fail;
+    }
+    return;
+  }
+  T *Gd = G_diag + m * L * BB;
+  T *Gl = G_lower + m * (L - 1) * BB;
   if (fail) {
     const T nan = static_cast<T>(__builtin_nan(""));
     for (int64_t e = lane; e < static_cast<int64_t>(L) * BB; e += 64) Gd[e] = nan;
@@ -165,14 +182,27 @@ size_t chain16_workspace_bytes(int dtype_bytes, int64_t B, int64_t L) {
 template <typename T>
 hipError_t chain16_launch(int64_t B, int64_t L, const T *diag, const T *lower, T *G_diag,
                           T *G_lower, double *logdet, int32_t *info, void *ws, hipStream_t s) {
-  hipLaunchKernelGGL(chain16_kernel<T>, dim3(static_cast<unsigned>(B)), dim3(64), 0, s,
+  hipLaunchKernelGGL((chain16_kernel<T, false>), dim3(static_cast<unsigned>(B)), dim3(64), 0, s,
                      static_cast<int>(L), diag, lower, G_diag, G_lower, logdet, info,
                      static_cast<T *>(ws));
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t chain16_factor_launch(int64_t B, int64_t L, const T *diag, const T *lower, T *factor,
+                                 double *logdet, int32_t *info, hipStream_t s) {
+  hipLaunchKernelGGL((chain16_kernel<T, true>), dim3(static_cast<unsigned>(B)), dim3(64), 0, s,
+                     static_cast<int>(L), diag, lower, nullptr, nullptr, logdet, info, factor);
+  return hipGetLastError();
+}
+
 template hipError_t chain16_launch<float>(int64_t, int64_t, const float *, const float *, float *,
                                           float *, double *, int32_t *, void *, hipStream_t);
+template hipError_t chain16_factor_launch<float>(int64_t, int64_t, const float *, const float *,
+                                                 float *, double *, int32_t *, hipStream_t);
+template hipError_t chain16_factor_launch<double>(int64_t, int64_t, const double *,
+                                                  const double *, double *, double *, int32_t *,
+                                                  hipStream_t);
 template hipError_t chain16_launch<double>(int64_t, int64_t, const double *, const double *,
                                            double *, double *, double *, int32_t *, void *,
                                            hipStream_t);

@@ -152,4 +152,39 @@ hipError_t tree_vjp_launch(const selinv_tree_plan *plan, const T *diag, const T 
                            const T *gd, const T *ge, const double *ld_bar, T *d_bar, T *e_bar,
                            int32_t *info, void *ws, hipStream_t s);
 
+// ------------------------- shared-factor siblings (shared_factor.hip)
+// factor = packed lower triangles of S_v^{-1} (wg::packed_entries(b) per block)
+template <typename T>
+hipError_t chain16_factor_launch(int64_t B, int64_t L, const T *diag, const T *lower, T *factor,
+                                 double *logdet, int32_t *info, hipStream_t s);
+size_t chain_factor_bytes(int dtype_bytes, int64_t B, int64_t L, int32_t b);
+template <typename T>
+hipError_t chain_factor_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower,
+                               T *factor, double *logdet, int32_t *info, hipStream_t s);
+template <typename T>
+hipError_t chain_apply_launch(int64_t B, int64_t L, int32_t b, int64_t k, bool sample,
+                              const T *lower, const T *factor, const T *in, T *out,
+                              hipStream_t s);
+size_t star_factor_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b);
+size_t star_factor_workspace_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b);
+template <typename T>
+hipError_t star_factor_launch(int64_t B, int64_t K, int32_t b, const T *center, const T *leaves,
+                              const T *coupling, T *factor, double *logdet, int32_t *info,
+                              void *ws, hipStream_t s);
+size_t star_apply_workspace_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b, int64_t k);
+template <typename T>
+hipError_t star_apply_launch(int64_t B, int64_t K, int32_t b, int64_t k, bool sample,
+                             const T *coupling, const T *factor, const T *in_center,
+                             const T *in_leaves, T *x_center, T *x_leaves, void *ws,
+                             hipStream_t s);
+size_t tree_factor_bytes(const selinv_tree_plan *plan);
+size_t tree_factor_workspace_bytes(const selinv_tree_plan *plan);
+template <typename T>
+hipError_t tree_factor_launch(const selinv_tree_plan *plan, const T *diag, const T *edge,
+                              T *factor, double *logdet, int32_t *info, void *ws, hipStream_t s);
+size_t tree_apply_workspace_bytes(const selinv_tree_plan *plan, int64_t k);
+template <typename T>
+hipError_t tree_apply_launch(const selinv_tree_plan *plan, int64_t k, bool sample, const T *edge,
+                             const T *factor, const T *in, T *out, void *ws, hipStream_t s);
+
 }  // namespace selinv
