@@ -12,6 +12,12 @@ root, never the executed count) and block-rows/s; roofline fraction of the
 dominant kernel against MI355X HBM bandwidth (8 TB/s) on compulsory bytes
 (every input block read once, every output block written once).
 
+``--op logdet`` times the log-det-only call (the collect pass without a
+stored factor); ``--op solve`` / ``--op sample`` time x = A^{-1} y and
+x = L^{-T} D^{-1/2} z with ``--k`` right-hand sides from a factor computed
+once before the timed region (nominal 8 b^2 k and 5 b^2 k + b^3 / 3 flop per
+block; compulsory bytes = factor + edge blocks + vectors in and out).
+
 ``--op vjp`` times the reverse mode instead (one call = the vector-Jacobian
 product of every matrix of the batch, seeded normal cotangents on every
 output): nominal 22 b^3 per non-root block and 4 b^3 per root, compulsory
@@ -68,7 +74,13 @@ def nominal_flops(kind, cfg, op="selinv"):
     X 2, M 1, W 2, Z 2, N 2, P 3; distribute: Dbar X 2, G Z 2, X^T Q 2, G X 2,
     symmetric X^T V 1).  Per root: b^3 forward, 4 b^3 reverse."""
     b = cfg["b"]
-    per, root = (7, 1) if op == "selinv" else (22, 4)
+    nblk = block_rows(kind, cfg)
+    k = cfg.get("k", 1)
+    if op == "solve":
+        return 8 * b * b * k * nblk
+    if op == "sample":
+        return (5 * b * b * k + b ** 3 // 3) * nblk
+    per, root = {"selinv": (7, 1), "vjp": (22, 4), "logdet": (4, 1)}[op]
     if kind == "chain":
         return cfg["B"] * (per * b ** 3 * (cfg["L"] - 1) + root * b ** 3)
     if kind == "star":
@@ -82,6 +94,18 @@ def compulsory_bytes(kind, cfg, w, op="selinv"):
     output cotangents read once, input cotangents written once, logdet_bar
     (f64) and info."""
     b2 = cfg["b"] ** 2
+    if op == "logdet":  # inputs read once, log det and info written
+        if kind == "chain":
+            return cfg["B"] * ((2 * cfg["L"] - 1) * b2 * w + 12)
+        if kind == "star":
+            return cfg["B"] * ((2 * cfg["K"] + 1) * b2 * w + 12)
+        return (2 * cfg["n"] - 1) * b2 * w + 4 * cfg["n"] + 12
+    if op in ("solve", "sample"):  # factor + edge blocks + vectors in and out
+        b = cfg["b"]
+        pk = (b * (b + 1) // 2 + 3) // 4 * 4
+        nblk = block_rows(kind, cfg)
+        nedge = nblk - (cfg["B"] if kind in ("chain", "star") else 1)
+        return (nblk * pk + nedge * b2 + 2 * nblk * b * cfg.get("k", 1)) * w
     if op == "vjp":
         if kind == "chain":
             return cfg["B"] * ((6 * cfg["L"] - 3) * b2 * w + 8 + 4)
@@ -140,7 +164,38 @@ def run_gpu(kind, cfg, dtname, steps, warmup, op="selinv"):
     dev = torch.device("cuda:0")
     dt = torch.float64 if dtname == "f64" else torch.float32
     inputs, parent = make_inputs(kind, cfg, dt, dev)
-    if op == "vjp":
+    if op in ("solve", "sample"):
+        import spdgen
+        k = cfg.get("k", 1)
+        if kind == "chain":
+            f = ssa.chain_factor(*inputs)
+            v = spdgen.cotangent((cfg["B"], cfg["L"], cfg["b"], k), seed=cfg["seed"])
+            v = torch.from_numpy(v).to(dev).to(dt)
+            call = (lambda: f.solve(v)) if op == "solve" else (lambda: f.sample(z=v))
+        elif kind == "star":
+            f = ssa.star_factor(*inputs)
+            vc = torch.from_numpy(spdgen.cotangent((cfg["B"], cfg["b"], k), seed=cfg["seed"],
+                                                   k=0)).to(dev).to(dt)
+            vl = torch.from_numpy(spdgen.cotangent((cfg["B"], cfg["K"], cfg["b"], k),
+                                                   seed=cfg["seed"], k=1)).to(dev).to(dt)
+            call = ((lambda: f.solve(vc, vl)) if op == "solve"
+                    else (lambda: f.sample(z_center=vc, z_leaves=vl)))
+        else:
+            plan = ssa.tree_plan(parent, cfg["b"], dt, dev)
+            f = ssa.tree_factor(parent, *inputs, plan=plan)
+            v = torch.from_numpy(spdgen.cotangent((cfg["n"], cfg["b"], k),
+                                                  seed=cfg["seed"])).to(dev).to(dt)
+            call = (lambda: f.solve(v)) if op == "solve" else (lambda: f.sample(z=v))
+    elif op == "logdet":
+        if kind == "chain":
+            call = lambda: ssa.chain_logdet(*inputs)
+        elif kind == "star":
+            call = lambda: ssa.star_logdet(*inputs)
+        else:
+            plan = ssa.tree_plan(parent, cfg["b"], dt, dev)
+            f0 = ssa.tree_factor(parent, *inputs, keep_factor=False, plan=plan)
+            call = lambda: ssa.tree_factor(parent, *inputs, keep_factor=False, plan=plan).logdet
+    elif op == "vjp":
         bars, lb = make_cotangents(kind, inputs, cfg, dt, dev)
         if kind == "chain":
             call = lambda: ssa.chain_vjp(*inputs, *bars, lb)
@@ -175,7 +230,48 @@ def run_gpu(kind, cfg, dtname, steps, warmup, op="selinv"):
     return {"wall_s": wall, "ev_ms": ev_ms}
 
 
-def cpu_baseline_vjp(kind, cfg):
+def cpu_baseline_apply(kind, cfg, op):
+    """The oracle's solve / sample (its collect included: the oracle keeps no
+    factor) on a bounded sample; value = nominal flops of the sweeps only."""
+    import oracle
+    import spdgen
+    lib = oracle.load()
+    k = cfg.get("k", 1)
+    if kind == "chain":
+        Bs = min(cfg["B"], 1024)
+        d, l = spdgen.chain(Bs, cfg["L"], cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
+        v = spdgen.cotangent((Bs, cfg["L"], cfg["b"], k), seed=cfg["seed"])
+        t0 = time.perf_counter()
+        oracle.chain_apply(d, l, v, op, lib=lib)
+        t = time.perf_counter() - t0
+        sub = dict(cfg, B=Bs)
+        sample = "%d of %d chains, k = %d, float64, collect + %s" % (Bs, cfg["B"], k, op)
+    elif kind == "star":
+        Bs = min(cfg["B"], 4)
+        c, lv, cp = spdgen.star(Bs, cfg["K"], cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
+        vc = spdgen.cotangent((Bs, cfg["b"], k), seed=cfg["seed"], k=0)
+        vl = spdgen.cotangent((Bs, cfg["K"], cfg["b"], k), seed=cfg["seed"], k=1)
+        t0 = time.perf_counter()
+        oracle.star_apply(c, lv, cp, vc, vl, op, lib=lib)
+        t = time.perf_counter() - t0
+        sub = dict(cfg, B=Bs)
+        sample = "%d of %d stars, k = %d, float64, collect + %s" % (Bs, cfg["B"], k, op)
+    else:
+        parent = spdgen.random_recursive_tree(cfg["n"], cfg["seed"])
+        d, e = spdgen.tree(parent, cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
+        v = spdgen.cotangent((cfg["n"], cfg["b"], k), seed=cfg["seed"])
+        t0 = time.perf_counter()
+        oracle.tree_apply(parent, d, e, v, op, lib=lib)
+        t = time.perf_counter() - t0
+        sub = cfg
+        sample = "the whole tree, k = %d, float64, collect + %s, single thread" % (k, op)
+    cores = 1 if kind == "tree" else int(lib.oracle_num_threads())
+    return {"value": round(nominal_flops(kind, sub, op) / t / 1e9, 3), "unit": "GFLOP/s",
+            "cores": cores, "kind": "oracle", "sample": sample, "seconds": round(t, 3),
+            "block_rows_per_s": round(block_rows(kind, sub) / t, 1)}
+
+
+def cpu_baseline_vjp(kind, cfg, op="vjp"):
     """The float64 oracle's VJP, as it stands, on a bounded sample."""
     import oracle
     import spdgen
@@ -219,8 +315,10 @@ def cpu_baseline_vjp(kind, cfg):
             "block_rows_per_s": round(block_rows(kind, sub) / t, 1)}
 
 
-def cpu_baseline(kind, cfg):
-    """The float64 oracle, as it stands, on a bounded sample of the workload."""
+def cpu_baseline(kind, cfg, op="selinv"):
+    """The float64 oracle, as it stands, on a bounded sample of the workload
+    (for --op logdet too: the oracle has no cheaper log-det path; value is
+    then the collect's nominal flops over the full oracle time)."""
     import numpy as np
     import oracle
     import spdgen
@@ -249,7 +347,7 @@ def cpu_baseline(kind, cfg):
         t = time.perf_counter() - t0
         sub = cfg
         sample = "the whole tree (n=%d, b=%d), float64, single thread" % (cfg["n"], cfg["b"])
-    gflops = nominal_flops(kind, sub) / t / 1e9
+    gflops = nominal_flops(kind, sub, op) / t / 1e9
     cores = 1 if kind == "tree" else int(lib.oracle_num_threads())
     return {"value": round(gflops, 3), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
             "sample": sample, "seconds": round(t, 3),
@@ -275,8 +373,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="chain_b16_batched")
-    ap.add_argument("--op", default="selinv", choices=("selinv", "vjp"),
-                    help="selinv: the selected inverse; vjp: its reverse mode")
+    ap.add_argument("--op", default="selinv",
+                    choices=("selinv", "vjp", "logdet", "solve", "sample"),
+                    help="selinv: the selected inverse; vjp: its reverse mode; logdet, solve, "
+                         "sample: the shared-factor siblings")
+    ap.add_argument("--k", type=int, default=1, help="right-hand sides for --op solve/sample")
     ap.add_argument("--dtype", default=None, help="f64 or f32 (default: the workload's first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-second-dtype", action="store_true")
@@ -300,6 +401,8 @@ def main():
     w = 8 if dtname == "f64" else 4
 
     op = args.op
+    if op in ("solve", "sample"):
+        cfg["k"] = args.k
     res = run_gpu(kind, cfg, dtname, args.steps, args.warmup, op)
     ev = sorted(res["ev_ms"])
     ms_mean = sum(res["ev_ms"]) / len(ev)
@@ -309,12 +412,12 @@ def main():
     gflops = F / (ms_step * 1e-3) / 1e9
     achieved_gbs = nbytes / (ms_mean * 1e-3) / 1e9
     peak_t = FP64_PEAK_TFLOPS if dtname == "f64" else FP32_PEAK_TFLOPS
-    tkey = args.workload if op == "selinv" else args.workload + "+vjp"
+    tkey = args.workload if op == "selinv" else args.workload + "+" + op
+    what = {"selinv": "selected-inverse", "vjp": "selected-inverse VJP",
+            "logdet": "log-det (collect only)", "solve": "shared-factor solve",
+            "sample": "shared-factor Gaussian sampling"}[op]
     out = {
-        "metric": ("selected-inverse GFLOP/s and block-rows/s (fp64/fp32), % of MI355X roofline"
-                   if op == "selinv" else
-                   "selected-inverse VJP GFLOP/s and block-rows/s (fp64/fp32), "
-                   "% of MI355X roofline"),
+        "metric": what + " GFLOP/s and block-rows/s (fp64/fp32), % of MI355X roofline",
         "value": round(gflops, 3),
         "unit": "GFLOP/s",
         "n_gpus": 1,
@@ -348,8 +451,9 @@ def main():
                       "hbm_frac": round(compulsory_bytes(kind, cfg, w2, op) / (ev2 * 1e-3) / 1e9
                                         / HBM_PEAK_GBS, 4)}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = (cpu_baseline(kind, cfg) if op == "selinv"
-                               else cpu_baseline_vjp(kind, cfg))
+        out["cpu_baseline"] = {"selinv": cpu_baseline, "vjp": cpu_baseline_vjp,
+                               "logdet": cpu_baseline, "solve": cpu_baseline_apply,
+                               "sample": cpu_baseline_apply}[op](kind, cfg, op)
     print(json.dumps(out), flush=True)
 
 

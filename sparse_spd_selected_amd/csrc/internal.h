@@ -157,6 +157,16 @@ hipError_t tree_vjp_launch(const selinv_tree_plan *plan, const T *diag, const T 
 template <typename T>
 hipError_t chain16_factor_launch(int64_t B, int64_t L, const T *diag, const T *lower, T *factor,
                                  double *logdet, int32_t *info, hipStream_t s);
+size_t star32_factor_workspace_bytes(int dtype_bytes, int64_t B, int64_t K);
+template <typename T>
+hipError_t star32_factor_launch(int64_t B, int64_t K, const T *center, const T *leaves,
+                                const T *coupling, T *factor, double *logdet, int32_t *info,
+                                void *ws, hipStream_t s);
+size_t tree8_factor_workspace_bytes(const selinv_tree_plan *plan);
+template <typename T>
+hipError_t tree8_factor_launch(const selinv_tree_plan *plan, const T *diag, const T *edge,
+                               T *factor, double *logdet, int32_t *info, void *ws,
+                               hipStream_t s);
 size_t chain_factor_bytes(int dtype_bytes, int64_t B, int64_t L, int32_t b);
 template <typename T>
 hipError_t chain_factor_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower,

@@ -479,6 +479,7 @@ size_t star_factor_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b) {
 }
 
 size_t star_factor_workspace_bytes(int dtype_bytes, int64_t B, int64_t K, int32_t b) {
+  if (b == 32) return star32_factor_workspace_bytes(dtype_bytes, B, K);
   const size_t nl = static_cast<size_t>(B) * K;
   return align_up(nl * b * b * dtype_bytes) + align_up(nl * sizeof(double)) +
          align_up(nl * sizeof(int32_t));
@@ -489,6 +490,8 @@ hipError_t star_factor_launch(int64_t B, int64_t K, int32_t b, const T *center, 
                               const T *coupling, T *factor, double *logdet, int32_t *info,
                               void *ws, hipStream_t s) {
   if (B == 0) return hipSuccess;
+  if (b == 32)
+    return star32_factor_launch<T>(B, K, center, leaves, coupling, factor, logdet, info, ws, s);
   const size_t nl = static_cast<size_t>(B) * K;
   Carve cv(ws);
   T *st_m = cv.take<T>(nl * b * b);
@@ -547,6 +550,7 @@ size_t tree_factor_bytes(const selinv_tree_plan *plan) {
 }
 
 size_t tree_factor_workspace_bytes(const selinv_tree_plan *plan) {
+  if (plan->b <= 8) return tree8_factor_workspace_bytes(plan);
   const size_t n = plan->n, bb = static_cast<size_t>(plan->b) * plan->b;
   return align_up(n * bb * plan->dtype_bytes) + align_up(n * sizeof(double)) +
          align_up(n * sizeof(int32_t)) + align_up(sizeof(int32_t));
@@ -555,6 +559,8 @@ size_t tree_factor_workspace_bytes(const selinv_tree_plan *plan) {
 template <typename T>
 hipError_t tree_factor_launch(const selinv_tree_plan *plan, const T *diag, const T *edge,
                               T *factor, double *logdet, int32_t *info, void *ws, hipStream_t s) {
+  if (plan->b <= 8)
+    return tree8_factor_launch<T>(plan, diag, edge, factor, logdet, info, ws, s);
   const size_t n = plan->n;
   const int b = plan->b;
   Carve cv(ws);

@@ -39,7 +39,9 @@ __device__ __forceinline__ void store_sym(T *P, const Blk<T> &b, int g, int j) {
   f16::store_t(P + 16 * 32 + 16, 32, b.t[1][1], g, j);
 }
 
-template <typename T>
+// kFactor: the collect pass of the shared factor; st_dinv is then the factor's
+// leaf part ([B][K][528]) and may be null (log det only).
+template <typename T, bool kFactor>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void star32_collect(
     int K, int nw, const T *__restrict__ leaves, const T *__restrict__ coupling,
     T *__restrict__ st_dinv, T *__restrict__ st_mpart, double *__restrict__ st_ld,
@@ -54,7 +56,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   const int j0 = w * kLPW, j1 = min(j0 + kLPW, K);
   const T *Dm = leaves + m * K * BB;
   const T *Fm = coupling + m * K * BB;
-  T *dinv = st_dinv + m * K * PB;
+  const bool keep = !kFactor || st_dinv;  // the packed Dinv_j are stored
+  T *dinv = keep ? st_dinv + m * K * PB : nullptr;
   const io32::SymLanes<T> sl(g, j, lane);
 
   Blk<T> Macc = f32t::zero<T>();
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     const Blk<T> Fo = io32::get_blk(tB, g, j);  // O32(F_j)
     f16::wave_sync();
     io32::put(tA, lane, Dn);
-    io32::store_packed(dinv + jj * PB, lane, pk);
+    if (keep) io32::store_packed(dinv + jj * PB, lane, pk);
     const Blk<T> Z = f32t::mm(S, Fo, f32t::zero<T>());  // Dinv_j F_j
     Macc = f32t::mm_lower(Fo, Z, Macc);                  // += F_j^T Z_j
     f16::wave_sync();
@@ -94,7 +97,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   }
 }
 
-template <typename T>
+// kFactor: G_center is the factor's centre part ([B][528], packed S_0^{-1})
+// and may be null; mat_fail is unused.
+template <typename T, bool kFactor>
 __global__ __launch_bounds__(64) void star32_center(int nw, const T *__restrict__ center,
                                                     const T *__restrict__ st_mpart,
                                                     const double *__restrict__ st_ld,
@@ -104,6 +109,7 @@ __global__ __launch_bounds__(64) void star32_center(int nw, const T *__restrict_
                                                     int32_t *__restrict__ info,
                                                     int32_t *__restrict__ mat_fail) {
   __shared__ __align__(32) T col[32];
+  __shared__ __align__(16) T tile[kFactor ? io32::Traits<T>::kTile : 1];
   const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
   const int64_t m = blockIdx.x;
   const f32t::SymOffsets<T> so(g, j);
@@ -118,6 +124,19 @@ __global__ __launch_bounds__(64) void star32_center(int nw, const T *__restrict_
   f16::PivotLog pl;
   const bool bad = f32t::gj_inverse(S, col, g, j, pl);
   if (!fail && bad) fail = 1;
+  if constexpr (kFactor) {
+    if (G_center) {
+      const io32::SymLanes<T> sl(g, j, lane);
+      io32::put_blk(tile, g, j, S);
+      f16::wave_sync();
+      io32::store_packed(G_center + m * PB, lane, sl.gather_packed(tile));
+    }
+    if (lane == 0) {
+      logdet[m] = fail ? __builtin_nan("") : ld + pl.log();
+      if (info) info[m] = fail;
+    }
+    return;
+  }
   if (fail) {
     S = f32t::zero<T>();
 #pragma unroll
@@ -217,10 +236,10 @@ hipError_t star32_launch(int64_t B, int64_t K, const T *center, const T *leaves,
   int32_t *failp = cv.take<int32_t>(static_cast<size_t>(B) * nw);
   int32_t *matfail = cv.take<int32_t>(B);
   if (nw > 0)
-    hipLaunchKernelGGL(star32_collect<T>, dim3(static_cast<unsigned>(B * nw)), dim3(64), 0, s,
-                       static_cast<int>(K), nw, leaves, coupling, dinv, mpart, ldp, failp);
-  hipLaunchKernelGGL(star32_center<T>, dim3(static_cast<unsigned>(B)), dim3(64), 0, s, nw, center,
-                     mpart, ldp, failp, G_center, logdet, info, matfail);
+    hipLaunchKernelGGL((star32_collect<T, false>), dim3(static_cast<unsigned>(B * nw)), dim3(64),
+                       0, s, static_cast<int>(K), nw, leaves, coupling, dinv, mpart, ldp, failp);
+  hipLaunchKernelGGL((star32_center<T, false>), dim3(static_cast<unsigned>(B)), dim3(64), 0, s,
+                     nw, center, mpart, ldp, failp, G_center, logdet, info, matfail);
   if (nw > 0)
     hipLaunchKernelGGL(star32_distribute<T>, dim3(static_cast<unsigned>(B * nw)), dim3(64), 0, s,
                        static_cast<int>(K), nw, coupling, G_center, dinv, matfail, G_leaf,
@@ -228,6 +247,38 @@ hipError_t star32_launch(int64_t B, int64_t K, const T *center, const T *leaves,
   return hipGetLastError();
 }
 
+size_t star32_factor_workspace_bytes(int dtype_bytes, int64_t B, int64_t K) {
+  const size_t nw = (K + kLPW - 1) / kLPW;
+  return align_up(static_cast<size_t>(B) * nw * BB * dtype_bytes) +
+         align_up(static_cast<size_t>(B) * nw * sizeof(double)) +
+         align_up(static_cast<size_t>(B) * nw * sizeof(int32_t));
+}
+
+template <typename T>
+hipError_t star32_factor_launch(int64_t B, int64_t K, const T *center, const T *leaves,
+                                const T *coupling, T *factor, double *logdet, int32_t *info,
+                                void *ws, hipStream_t s) {
+  const int nw = static_cast<int>((K + kLPW - 1) / kLPW);
+  Carve cv(ws);
+  T *mpart = cv.take<T>(static_cast<size_t>(B) * nw * BB);
+  double *ldp = cv.take<double>(static_cast<size_t>(B) * nw);
+  int32_t *failp = cv.take<int32_t>(static_cast<size_t>(B) * nw);
+  T *fc = factor ? factor + static_cast<size_t>(B) * K * PB : nullptr;
+  if (nw > 0)
+    hipLaunchKernelGGL((star32_collect<T, true>), dim3(static_cast<unsigned>(B * nw)), dim3(64),
+                       0, s, static_cast<int>(K), nw, leaves, coupling, factor, mpart, ldp,
+                       failp);
+  hipLaunchKernelGGL((star32_center<T, true>), dim3(static_cast<unsigned>(B)), dim3(64), 0, s, nw,
+                     center, mpart, ldp, failp, fc, logdet, info, nullptr);
+  return hipGetLastError();
+}
+
+template hipError_t star32_factor_launch<float>(int64_t, int64_t, const float *, const float *,
+                                                const float *, float *, double *, int32_t *,
+                                                void *, hipStream_t);
+template hipError_t star32_factor_launch<double>(int64_t, int64_t, const double *,
+                                                 const double *, const double *, double *,
+                                                 double *, int32_t *, void *, hipStream_t);
 template hipError_t star32_launch<float>(int64_t, int64_t, const float *, const float *,
                                          const float *, float *, float *, float *, double *,
                                          int32_t *, void *, hipStream_t);

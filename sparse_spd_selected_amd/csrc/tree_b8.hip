@@ -25,7 +25,10 @@ namespace {
 constexpr int kWaves = 4;  // wavefronts per workgroup
 constexpr int kSlots = 8;  // nodes per wavefront
 
-template <typename T>
+// kFactor: the collect pass of the shared factor: the packed lower triangle
+// of Sinv_v (wg-style layout, packed_entries(b) per position) goes to
+// st_sinv, which may be null (log det only); G_diag, G_edge are unused.
+template <typename T, bool kFactor>
 __global__ __launch_bounds__(256) void tree8_collect(
     int64_t p0, int64_t p1, int b, const int32_t *__restrict__ node_at,
     const int32_t *__restrict__ child_beg, const int32_t *__restrict__ child_end,
@@ -76,10 +79,19 @@ __global__ __launch_bounds__(256) void tree8_collect(
     st_ld[p] = failed ? static_cast<double>(__builtin_nan("")) : pl.log();
     if (bad && !child_failed) atomicMin(first_fail, fail_rank[p]);
   }
-  if (valid) r8::store8(st_sinv + p * 64, i, S);
-  if (p == 0) {  // root closure: G_rr = Sinv_r, and the root's edge slot is zero
-    r8::store(G_diag + v * bb, b, i, S);
-    r8::store(G_edge + v * bb, b, i, r8::zero<T>());
+  if constexpr (kFactor) {
+    if (valid && st_sinv && i < b) {  // row i of the packed lower triangle
+      T *row = st_sinv + p * ((b * (b + 1) / 2 + 3) / 4 * 4) + i * (i + 1) / 2;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (c <= i) row[c] = S.v[c];
+    }
+  } else {
+    if (valid) r8::store8(st_sinv + p * 64, i, S);
+    if (p == 0) {  // root closure: G_rr = Sinv_r, and the root's edge slot is zero
+      r8::store(G_diag + v * bb, b, i, S);
+      r8::store(G_edge + v * bb, b, i, r8::zero<T>());
+    }
   }
   // message to the parent (all slots take part in the staging; only valid
   // non-root slots store)
@@ -203,7 +215,7 @@ hipError_t tree8_launch(const selinv_tree_plan *plan, const T *diag, const T *ed
   for (int32_t lev = plan->levels - 1; lev >= 0; --lev) {
     const int64_t p0 = plan->level_off[lev], p1 = plan->level_off[lev + 1];
     const unsigned grid = static_cast<unsigned>((p1 - p0 + per_block - 1) / per_block);
-    hipLaunchKernelGGL(tree8_collect<T>, dim3(grid), dim3(256), 0, s, p0, p1, b, d.node_at,
+    hipLaunchKernelGGL((tree8_collect<T, false>), dim3(grid), dim3(256), 0, s, p0, p1, b, d.node_at,
                        d.child_beg, d.child_end, d.fail_rank, diag, edge, st_sinv, st_m, st_ld,
                        st_fail, first_fail, G_diag, G_edge);
   }
@@ -221,6 +233,49 @@ hipError_t tree8_launch(const selinv_tree_plan *plan, const T *diag, const T *ed
   return hipGetLastError();
 }
 
+size_t tree8_factor_workspace_bytes(const selinv_tree_plan *plan) {
+  const size_t n = plan->n;
+  return align_up(n * 64 * plan->dtype_bytes) + align_up(n * sizeof(double)) +
+         align_up(n * sizeof(int32_t)) + align_up(sizeof(int32_t)) +
+         align_up(kFinishGroups * sizeof(double));
+}
+
+template <typename T>
+hipError_t tree8_factor_launch(const selinv_tree_plan *plan, const T *diag, const T *edge,
+                               T *factor, double *logdet, int32_t *info, void *ws,
+                               hipStream_t s) {
+  const int64_t n = plan->n;
+  const int b = plan->b;
+  Carve cv(ws);
+  T *st_m = cv.take<T>(n * 64);
+  double *st_ld = cv.take<double>(n);
+  int32_t *st_fail = cv.take<int32_t>(n);
+  int32_t *first_fail = cv.take<int32_t>(1);
+  double *partial = cv.take<double>(kFinishGroups);
+  const TreePlanDev &d = plan->dev;
+  const int64_t per_block = kWaves * kSlots;
+  hipLaunchKernelGGL(tree8_init, dim3(1), dim3(1), 0, s, first_fail);
+  for (int32_t lev = plan->levels - 1; lev >= 0; --lev) {
+    const int64_t p0 = plan->level_off[lev], p1 = plan->level_off[lev + 1];
+    const unsigned grid = static_cast<unsigned>((p1 - p0 + per_block - 1) / per_block);
+    hipLaunchKernelGGL((tree8_collect<T, true>), dim3(grid), dim3(256), 0, s, p0, p1, b,
+                       d.node_at, d.child_beg, d.child_end, d.fail_rank, diag, edge, factor, st_m,
+                       st_ld, st_fail, first_fail, nullptr, nullptr);
+  }
+  const int64_t chunk = (n + kFinishGroups - 1) / kFinishGroups;
+  hipLaunchKernelGGL(tree8_ld_partial, dim3(kFinishGroups), dim3(1024), 0, s, n, chunk, st_ld,
+                     partial);
+  hipLaunchKernelGGL(tree8_finish, dim3(1), dim3(64), 0, s, partial, d.rank_node, first_fail,
+                     logdet, info);
+  return hipGetLastError();
+}
+
+template hipError_t tree8_factor_launch<float>(const selinv_tree_plan *, const float *,
+                                               const float *, float *, double *, int32_t *,
+                                               void *, hipStream_t);
+template hipError_t tree8_factor_launch<double>(const selinv_tree_plan *, const double *,
+                                                const double *, double *, double *, int32_t *,
+                                                void *, hipStream_t);
 template hipError_t tree8_launch<float>(const selinv_tree_plan *, const float *, const float *,
                                         float *, float *, double *, int32_t *, void *,
                                         hipStream_t);
