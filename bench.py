@@ -211,6 +211,7 @@ def run_gpu(kind, cfg, dtname, steps, warmup, op="selinv"):
     else:
         plan = ssa.tree_plan(parent, cfg["b"], dt, dev)
         call = lambda: ssa.tree(parent, *inputs, plan=plan)
+    out = None
     for _ in range(warmup):
         out = call()
     torch.cuda.synchronize()

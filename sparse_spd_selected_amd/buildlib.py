@@ -28,7 +28,7 @@ SOURCES = [
     "tree_b8.hip",
     "chain_small.hip",
     "vjp_generic.hip", "vjp_chain_b16.hip", "vjp_star_b32.hip",
-    "vjp_tree_b8.hip",
+    "vjp_tree_b8.hip", "vjp_chain_seg.hip",
     "shared_factor.hip",
 ]
 

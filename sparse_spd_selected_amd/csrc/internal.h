@@ -123,6 +123,14 @@ template <typename T>
 hipError_t chain16_vjp_launch(int64_t B, int64_t L, const T *diag, const T *lower, const T *gd,
                               const T *gl, const double *ld_bar, T *d_bar, T *l_bar,
                               int32_t *info, void *ws, hipStream_t s);
+// few long chains: parallel over segments of each chain (vjp_chain_seg.hip);
+// chain_vjp_segments returns the number of segments, 0 = not used
+int chain_vjp_segments(int64_t B, int64_t L, int32_t b);
+size_t chain_vjp_seg_workspace_bytes(int dtype_bytes, int64_t B, int64_t L, int32_t b, int P);
+template <typename T>
+hipError_t chain_vjp_seg_launch(int64_t B, int64_t L, int32_t b, int P, const T *diag,
+                                const T *lower, const T *gd, const T *gl, const double *ld_bar,
+                                T *d_bar, T *l_bar, int32_t *info, void *ws, hipStream_t s);
 template <typename T>
 hipError_t chain_vjp_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower,
                             const T *gd, const T *gl, const double *ld_bar, T *d_bar, T *l_bar,

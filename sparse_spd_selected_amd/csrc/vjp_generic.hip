@@ -376,6 +376,8 @@ __global__ void vjp_init_int(int32_t *p, int32_t v) { *p = v; }
 // ------------------------------------------------------------ launchers
 
 size_t chain_vjp_workspace_bytes(int dtype_bytes, int64_t B, int64_t L, int32_t b) {
+  const int Pv = chain_vjp_segments(B, L, b);
+  if (Pv > 0) return chain_vjp_seg_workspace_bytes(dtype_bytes, B, L, b, Pv);
   if (b == 16) return chain16_vjp_workspace_bytes(dtype_bytes, B, L);
   return align_up(static_cast<size_t>(B) * L * 4 * b * b * dtype_bytes);
 }
@@ -385,6 +387,10 @@ hipError_t chain_vjp_launch(int64_t B, int64_t L, int32_t b, const T *diag, cons
                             const T *gd, const T *gl, const double *ld_bar, T *d_bar, T *l_bar,
                             int32_t *info, void *ws, hipStream_t s) {
   if (B == 0) return hipSuccess;
+  const int Pv = chain_vjp_segments(B, L, b);
+  if (Pv > 0)
+    return chain_vjp_seg_launch<T>(B, L, b, Pv, diag, lower, gd, gl, ld_bar, d_bar, l_bar, info,
+                                   ws, s);
   if (b == 16)
     return chain16_vjp_launch<T>(B, L, diag, lower, gd, gl, ld_bar, d_bar, l_bar, info, ws, s);
   const size_t shm = (6 * b * b + b) * sizeof(T);

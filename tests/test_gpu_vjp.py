@@ -101,6 +101,50 @@ def test_chain_vjp_workload_b16_batched(ssa, dt):
                   sample=sorted(set([0, 1, 4095] + list(range(7, 4096, 91)))))
 
 
+@pytest.mark.parametrize("dt", ["f64", "f32"])
+@pytest.mark.parametrize("B,L", [(2, 600), (3, 1030)])
+def test_chain_vjp_segments(ssa, B, L, dt):
+    """b = 32 with few long chains runs the segment-parallel reverse mode
+    (4 and 8 segments of uneven length)."""
+    run_chain_vjp(ssa, B, L, 32, DT[dt], seed=B + L)
+
+
+def test_chain_vjp_workload_b32_long(ssa):
+    """64 chains of 16384 blocks of 32 (diagonal load 1.0), float64, 128
+    segments per chain; the oracle checks chains 0 and 63, each regenerated
+    with its cotangents on its own."""
+    B, L, b = 64, 16384, 32
+    say("chain_vjp long: generating")
+    d, l, gd, gl, lb = chain_case(B, L, b, seed=0, load=1.0)
+    args = [_to(x, torch.float64) for x in (d, l, gd, gl)]
+    del d, l, gd, gl
+    say("chain_vjp long: running")
+    db, lbar, info = ssa.chain_vjp(*args, torch.from_numpy(lb).to(DEV), return_info=True)
+    torch.cuda.synchronize()
+    del args
+    assert int(info.abs().sum()) == 0
+    for m in (0, 63):
+        dm, lm, gdm, glm, lbm = chain_case(1, L, b, seed=0, m0=m, load=1.0)
+        Od, Ol, st = oracle.chain_vjp(dm, lm, gdm, glm, lbm)
+        assert (st == 0).all()
+        say("chain_vjp long: chain %d  diag %.2e  lower %.2e" % (
+            m, _cmp("diag_bar[%d]" % m, db[m:m + 1], Od, torch.float64),
+            _cmp("lower_bar[%d]" % m, lbar[m:m + 1], Ol, torch.float64)))
+
+
+def test_chain_vjp_segments_not_pd(ssa):
+    d, l, gd, gl, lb = chain_case(2, 600, 32, seed=4)
+    d[1, 300] = -np.eye(32)
+    db, lbar, info = ssa.chain_vjp(_to(d, torch.float64), _to(l, torch.float64),
+                                   _to(gd, torch.float64), _to(gl, torch.float64),
+                                   torch.from_numpy(lb).to(DEV), return_info=True)
+    torch.cuda.synchronize()
+    assert list(info.cpu().numpy()) == [0, 301]
+    assert torch.isnan(db[1]).all() and torch.isnan(lbar[1]).all()
+    Od, Ol, _ = oracle.chain_vjp(d[:1], l[:1], gd[:1], gl[:1], lb[:1])
+    _cmp("diag_bar", db[:1], Od, torch.float64)
+
+
 def test_chain_vjp_logdet_only_is_selected_inverse(ssa):
     """With zero output cotangents and logdet_bar = 1: diag_bar = G_diag and
     lower_bar = 2 G_lower (d log det A = <A^-1, dA>), against the forward
