@@ -59,10 +59,13 @@ def load(path: str | None = None):
     lib.oracle_tree_vjp.argtypes = [i64, i32, vp, vp, vp, vp, vp, ctypes.c_double, vp, vp]
     lib.oracle_chain_vjp.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_tree_apply.argtypes = [i64, i32, vp, vp, vp, i64, vp, vp, i32]
+    lib.oracle_bidiag.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp]
+    lib.oracle_nonsym_tree.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_chain_apply.argtypes = [i64, i64, i32, vp, vp, i64, vp, vp, i32, vp]
     for f in (lib.oracle_chain, lib.oracle_star, lib.oracle_tree, lib.oracle_tree_depths,
               lib.oracle_num_threads, lib.oracle_tree_vjp, lib.oracle_chain_vjp,
-              lib.oracle_tree_apply, lib.oracle_chain_apply):
+              lib.oracle_tree_apply, lib.oracle_chain_apply, lib.oracle_bidiag,
+              lib.oracle_nonsym_tree):
         f.restype = ctypes.c_int
     if path == _LIB:
         _lib = lib
@@ -278,3 +281,35 @@ def star_apply(center, leaves, coupling, vec_center, vec_leaves, mode, lib=None)
         out = tree_apply(parent, diag, edge, vec, mode, lib=lib)
         oc[m], ol[m] = out[0], out[1:]
     return oc, ol
+
+
+# ------------------------------------------------- non-symmetric ladder
+
+def bidiag(diag, lower, lib=None):
+    """Block lower-bidiagonal M (diag [B,L,b,b], lower [B,L-1,b,b] = M_{i+1,i}).
+    -> (G_diag, G_lower, info)."""
+    lib = lib or load()
+    diag, lower = _f64(diag), _f64(lower)
+    B, L, b = diag.shape[0], diag.shape[1], diag.shape[2]
+    Gd = np.empty_like(diag)
+    Gl = np.empty_like(lower)
+    info = np.empty(B, np.int32)
+    rc = lib.oracle_bidiag(B, L, b, _p(diag), _p(lower), _p(Gd), _p(Gl), _p(info))
+    if rc:
+        raise OracleError("oracle_bidiag status %d" % rc)
+    return Gd, Gl, info
+
+
+def nonsym_tree(parent, diag, up, down, lib=None):
+    """-> (G_diag, G_up [v] = G_{parent,v}, G_down [v] = G_{v,parent}, info)."""
+    lib = lib or load()
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    diag, up, down = _f64(diag), _f64(up), _f64(down)
+    n, b = diag.shape[0], diag.shape[1]
+    Gd, Gu, Gw = np.empty_like(diag), np.empty_like(up), np.empty_like(down)
+    info = np.zeros(1, np.int32)
+    rc = lib.oracle_nonsym_tree(n, b, _p(parent), _p(diag), _p(up), _p(down), _p(Gd), _p(Gu),
+                                _p(Gw), _p(info))
+    if rc:
+        raise OracleError("oracle_nonsym_tree status %d" % rc)
+    return Gd, Gu, Gw, int(info[0])

@@ -758,6 +758,151 @@ ORACLE_API int oracle_chain_apply(int64_t B, int64_t L, int b, const double *dia
   return 0;
 }
 
+/* ------------------------------------------------- non-symmetric ladder */
+
+/* Inverse of a general b x b block by Gaussian elimination on [A | I]
+ * without pivoting (the page's non-symmetric kernels eliminate "with no
+ * pivoting", safe while block-diagonally dominant).  Returns 0, or 1 if a
+ * pivot is zero or not finite. */
+static int gen_inverse(int b, const double *A, double *Ainv) {
+  const int w = 2 * b;
+  double *M = (double *)malloc(sizeof(double) * (size_t)b * w);
+  int rc = 0;
+  for (int r = 0; r < b; ++r)
+    for (int c = 0; c < w; ++c) M[r * w + c] = c < b ? A[r * b + c] : (c - b == r ? 1.0 : 0.0);
+  for (int k = 0; k < b && !rc; ++k) {
+    const double d = M[k * w + k];
+    if (d == 0.0 || !isfinite(d)) {
+      rc = 1;
+      break;
+    }
+    for (int c = 0; c < w; ++c) M[k * w + c] /= d;
+    for (int r = 0; r < b; ++r) {
+      if (r == k) continue;
+      const double f = M[r * w + k];
+      for (int c = 0; c < w; ++c) M[r * w + c] -= f * M[k * w + c];
+    }
+  }
+  for (int r = 0; r < b; ++r)
+    for (int c = 0; c < b; ++c) Ainv[r * b + c] = M[r * w + b + c];
+  free(M);
+  return rc;
+}
+
+/* Block lower-bidiagonal M (item "Non-symmetric chain" of "Implemented and
+ * tested kernels"): fully local, G_ii = M_ii^{-1},
+ * G_{i+1,i} = -M_{i+1,i+1}^{-1} M_{i+1,i} M_ii^{-1}.  info[m] = 0, or 1 + the
+ * smallest block index whose inverse breaks down (the matrix's outputs are
+ * then NaN). */
+ORACLE_API int oracle_bidiag(int64_t B, int64_t L, int b, const double *diag,
+                             const double *lower, double *G_diag, double *G_lower,
+                             int32_t *info) {
+  if (B < 0 || L < 1 || b < 1 || !diag || !G_diag || !info) return 1;
+  if (L > 1 && (!lower || !G_lower)) return 1;
+  const int64_t bb = (int64_t)b * b;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t m = 0; m < B; ++m) {
+    double *Gd = G_diag + m * L * bb, *Gl = G_lower + m * (L - 1) * bb;
+    double *T = (double *)malloc(sizeof(double) * bb);
+    int32_t fail = 0;
+    for (int64_t i = 0; i < L && !fail; ++i)
+      if (gen_inverse(b, diag + (m * L + i) * bb, Gd + i * bb)) fail = (int32_t)(i + 1);
+    if (fail) {
+      fill_nan(Gd, L * bb);
+      if (L > 1) fill_nan(Gl, (L - 1) * bb);
+    } else {
+      for (int64_t i = 0; i + 1 < L; ++i) {
+        matmul(b, lower + (m * (L - 1) + i) * bb, Gd + i * bb, T); /* M_{i+1,i} M_ii^{-1} */
+        matmul(b, Gd + (i + 1) * bb, T, Gl + i * bb);
+        for (int64_t e = 0; e < bb; ++e) Gl[i * bb + e] = -Gl[i * bb + e];
+      }
+    }
+    info[m] = fail;
+    free(T);
+  }
+  return 0;
+}
+
+/* Non-symmetric tree (item "Non-symmetric tree"): a general block matrix
+ * whose off-diagonal graph is a tree, with independent directed edge blocks
+ * up[v] = M_{p,v} and down[v] = M_{v,p}.  Two-sided block elimination,
+ * children first, no pivoting:
+ *   collect:    S_v = M_vv - sum_children up_c S_c^{-1} down_c
+ *   root:       G_rr = S_r^{-1}
+ *   distribute: G_{p,v} = -G_pp up_v S_v^{-1},  G_{v,p} = -S_v^{-1} down_v G_pp,
+ *               G_vv = S_v^{-1} + S_v^{-1} down_v G_pp up_v S_v^{-1}
+ * (in the symmetric case up_v = E_v, down_v = E_v^T this is the tree kernel
+ * above).  Order as in oracle_tree; info = v + 1 for the first breakdown in
+ * that order. */
+ORACLE_API int oracle_nonsym_tree(int64_t n, int b, const int32_t *parent, const double *diag,
+                                  const double *up, const double *down, double *G_diag,
+                                  double *G_up, double *G_down, int32_t *info) {
+  if (n < 1 || b < 1 || !parent || !diag || !up || !down || !G_diag || !G_up || !G_down || !info)
+    return 1;
+  const int64_t bb = (int64_t)b * b;
+  int32_t *depth = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+  int64_t root = -1;
+  if (tree_depths(n, parent, depth, &root)) {
+    free(depth);
+    return 2;
+  }
+  int32_t H = 0;
+  for (int64_t v = 0; v < n; ++v)
+    if (depth[v] > H) H = depth[v];
+  int64_t *cnt = (int64_t *)calloc((size_t)H + 2, sizeof(int64_t));
+  for (int64_t v = 0; v < n; ++v) cnt[depth[v] + 1]++;
+  for (int32_t d = 0; d <= H; ++d) cnt[d + 1] += cnt[d];
+  int64_t *order = (int64_t *)malloc(sizeof(int64_t) * (size_t)n);
+  int64_t *fillp = (int64_t *)malloc(sizeof(int64_t) * ((size_t)H + 1));
+  for (int32_t d = 0; d <= H; ++d) fillp[d] = cnt[d];
+  for (int64_t v = 0; v < n; ++v) order[fillp[depth[v]]++] = v;
+  double *S = (double *)malloc(sizeof(double) * n * bb);
+  double *Si = (double *)malloc(sizeof(double) * n * bb);
+  double *T = (double *)malloc(sizeof(double) * 3 * bb);
+  double *T2 = T + bb, *T3 = T + 2 * bb;
+  memcpy(S, diag, sizeof(double) * n * bb);
+  int32_t fail = 0;
+  for (int32_t d = H; d >= 0 && !fail; --d)
+    for (int64_t q = cnt[d]; q < cnt[d + 1]; ++q) {
+      const int64_t v = order[q], p = parent[v];
+      if (gen_inverse(b, S + v * bb, Si + v * bb)) {
+        fail = (int32_t)(v + 1);
+        break;
+      }
+      if (p >= 0) {
+        matmul(b, Si + v * bb, down + v * bb, T);  /* S_v^{-1} down_v */
+        matmul(b, up + v * bb, T, T2);              /* up_v S_v^{-1} down_v */
+        for (int64_t e = 0; e < bb; ++e) S[p * bb + e] -= T2[e];
+      }
+    }
+  if (fail) {
+    fill_nan(G_diag, n * bb);
+    fill_nan(G_up, n * bb);
+    fill_nan(G_down, n * bb);
+  } else {
+    memcpy(G_diag + root * bb, Si + root * bb, sizeof(double) * bb);
+    memset(G_up + root * bb, 0, sizeof(double) * bb);
+    memset(G_down + root * bb, 0, sizeof(double) * bb);
+    for (int32_t d = 1; d <= H; ++d)
+      for (int64_t q = cnt[d]; q < cnt[d + 1]; ++q) {
+        const int64_t v = order[q], p = parent[v];
+        const double *Gp = G_diag + p * bb, *Sv = Si + v * bb;
+        matmul(b, up + v * bb, Sv, T);   /* up_v S_v^{-1} */
+        matmul(b, Gp, T, T2);            /* G_pp up_v S_v^{-1} = -G_{p,v} */
+        for (int64_t e = 0; e < bb; ++e) G_up[v * bb + e] = -T2[e];
+        matmul(b, Sv, down + v * bb, T); /* S_v^{-1} down_v */
+        matmul(b, T, Gp, T3);            /* S_v^{-1} down_v G_pp = -G_{v,p} */
+        for (int64_t e = 0; e < bb; ++e) G_down[v * bb + e] = -T3[e];
+        matmul(b, T, T2, T3);            /* S_v^{-1} down_v G_pp up_v S_v^{-1} */
+        for (int64_t e = 0; e < bb; ++e) G_diag[v * bb + e] = Sv[e] + T3[e];
+      }
+  }
+  *info = fail;
+  free(depth); free(cnt); free(order); free(fillp);
+  free(S); free(Si); free(T);
+  return 0;
+}
+
 /* Depth of every node of a valid tree (host helper for the tests); returns 0,
  * or 2 for an invalid parent array. */
 ORACLE_API int oracle_tree_depths(int64_t n, const int32_t *parent, int32_t *depth) {

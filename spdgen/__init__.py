@@ -49,6 +49,8 @@ def _load():
         lib.spdgen_normal.restype = dbl
         lib.spdgen_philox4x32_10.argtypes = [vp, vp, vp]
         lib.spdgen_cotangent.argtypes = [u64, ctypes.c_uint32, i64, i64, i64, vp]
+        lib.spdgen_nonsym_bidiag.argtypes = [u64, i64, i64, i64, i32, dbl, vp, vp]
+        lib.spdgen_nonsym_tree.argtypes = [u64, i64, i32, dbl, vp, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -114,6 +116,51 @@ def cotangent(shape, seed: int = 0, k: int = 0, m0: int = 0) -> np.ndarray:
     return out
 
 
+def nonsym_bidiag(B: int, L: int, b: int, seed: int = 0, diag_load: float = 2.0, m0: int = 0):
+    """Block lower-bidiagonal non-symmetric matrices [m0, m0+B): general
+    diagonal blocks and lower[i] = M_{i+1,i}, every scalar row strictly
+    diagonally dominant by diag_load."""
+    diag = np.empty((B, L, b, b), np.float64)
+    lower = np.empty((B, max(L - 1, 0), b, b), np.float64)
+    _load().spdgen_nonsym_bidiag(seed, m0, B, L, b, diag_load, _ptr(diag), _ptr(lower))
+    return diag, lower
+
+
+def nonsym_tree(parent, b: int, seed: int = 1, diag_load: float = 2.0):
+    """Tree-structured non-symmetric matrix: diag [n,b,b], up[v] = M_{parent,v},
+    down[v] = M_{v,parent} (zero root slots), rows diagonally dominant."""
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    n = parent.shape[0]
+    diag = np.empty((n, b, b), np.float64)
+    up = np.empty((n, b, b), np.float64)
+    down = np.empty((n, b, b), np.float64)
+    _load().spdgen_nonsym_tree(seed, n, b, diag_load, _ptr(parent), _ptr(diag), _ptr(up),
+                               _ptr(down))
+    return diag, up, down
+
+
+def to_dense_bidiag(diag: np.ndarray, lower: np.ndarray) -> np.ndarray:
+    L, b = diag.shape[0], diag.shape[1]
+    A = np.zeros((L * b, L * b))
+    for i in range(L):
+        A[i * b:(i + 1) * b, i * b:(i + 1) * b] = diag[i]
+    for i in range(L - 1):
+        A[(i + 1) * b:(i + 2) * b, i * b:(i + 1) * b] = lower[i]
+    return A
+
+
+def to_dense_nonsym_tree(parent, diag, up, down) -> np.ndarray:
+    n, b = diag.shape[0], diag.shape[1]
+    A = np.zeros((n * b, n * b))
+    for v in range(n):
+        A[v * b:(v + 1) * b, v * b:(v + 1) * b] = diag[v]
+        p = int(parent[v])
+        if p >= 0:
+            A[p * b:(p + 1) * b, v * b:(v + 1) * b] = up[v]
+            A[v * b:(v + 1) * b, p * b:(p + 1) * b] = down[v]
+    return A
+
+
 def random_recursive_tree(n: int, seed: int = 1) -> np.ndarray:
     """parent[0] = -1, parent[v] uniform over [0, v)."""
     parent = np.empty(n, np.int32)
@@ -166,6 +213,11 @@ WORKLOADS = {
     "star_b32": dict(kind="star", B=256, K=1024, b=32, seed=0, diag_load=2.0,
                      dtypes=("f64",)),
     "tree_b8_random": dict(kind="tree", n=262144, b=8, seed=1, diag_load=2.0,
+                           dtypes=("f64", "f32")),
+    # the non-symmetric ladder at the sizes of the chain and tree workloads
+    "bidiag_b16_batched": dict(kind="bidiag", B=4096, L=64, b=16, seed=0, diag_load=2.0,
+                               dtypes=("f64", "f32")),
+    "nonsym_tree_b8": dict(kind="nonsym_tree", n=262144, b=8, seed=1, diag_load=2.0,
                            dtypes=("f64", "f32")),
 }
 

@@ -292,3 +292,95 @@ SPDGEN_API void spdgen_cotangent(uint64_t seed, uint32_t k, int64_t m0, int64_t 
   for (int64_t m = 0; m < count; ++m)
     normals(seed, 16u + k, (uint64_t)(m0 + m), 0, per, 1.0, out + m * per);
 }
+
+/* ------------------------------------------------------- non-symmetric */
+
+/* D = R + shift I with R iid N(0, 1/b) and shift = load + max_r (sum_s
+ * |R_rs| + extra[r]): every scalar row of the block row is strictly
+ * diagonally dominant by at least `load` (extra[r] = the absolute row sum of
+ * the row's other blocks; |R_rr| is counted so that a negative R_rr cannot
+ * eat into the margin), so elimination without pivoting is safe. */
+static void dominant_block(int b, const double *R, const double *extra, double load, double *D) {
+  double shift = 0.0;
+  for (int r = 0; r < b; ++r) {
+    double s = extra ? extra[r] : 0.0;
+    for (int c = 0; c < b; ++c) s += fabs(R[r * b + c]);
+    if (s > shift) shift = s;
+  }
+  shift += load;
+  for (int r = 0; r < b; ++r)
+    for (int c = 0; c < b; ++c) D[r * b + c] = R[r * b + c] + (r == c ? shift : 0.0);
+}
+
+/* Block lower-bidiagonal M (the non-symmetric chain of "Implemented and
+ * tested kernels"), matrices [m0, m0+count):
+ *   diag  [count][L][b][b]   M_ii (general)
+ *   lower [count][L-1][b][b] lower[i] = M_{i+1,i} */
+SPDGEN_API void spdgen_nonsym_bidiag(uint64_t seed, int64_t m0, int64_t count, int64_t L, int b,
+                                     double diag_load, double *diag, double *lower) {
+  const int64_t bb = (int64_t)b * b;
+  const double sd = 1.0 / sqrt((double)b);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t m = 0; m < count; ++m) {
+    const uint64_t mat = (uint64_t)(m0 + m);
+    double *Cm = lower + m * (L - 1) * bb;
+    if (L > 1) normals(seed, 4, mat, 0, (L - 1) * bb, sd, Cm);
+    double *R = (double *)malloc(sizeof(double) * bb);
+    double *ex = (double *)malloc(sizeof(double) * b);
+    for (int64_t i = 0; i < L; ++i) {
+      normals(seed, 5, mat, (uint64_t)(i * bb), bb, sd, R);
+      for (int r = 0; r < b; ++r) {
+        ex[r] = 0.0;
+        if (i >= 1)
+          for (int c = 0; c < b; ++c) ex[r] += fabs(Cm[(i - 1) * bb + r * b + c]);
+      }
+      dominant_block(b, R, ex, diag_load, diag + m * L * bb + i * bb);
+    }
+    free(R);
+    free(ex);
+  }
+}
+
+/* Tree-structured non-symmetric matrix for a given parent array: two
+ * independent directed edge blocks per non-root node.
+ *   diag [n][b][b]  M_vv (general)
+ *   up   [n][b][b]  up[v]   = M_{parent(v),v}
+ *   down [n][b][b]  down[v] = M_{v,parent(v)}     (root slots zero)
+ * Block row v holds down[v] and up[c] for every child c. */
+SPDGEN_API void spdgen_nonsym_tree(uint64_t seed, int64_t n, int b, double diag_load,
+                                   const int32_t *parent, double *diag, double *up,
+                                   double *down) {
+  const int64_t bb = (int64_t)b * b;
+  const double sd = 1.0 / sqrt((double)b);
+  double *ex = (double *)calloc((size_t)(n * b), sizeof(double));
+#pragma omp parallel for schedule(static)
+  for (int64_t v = 0; v < n; ++v) {
+    if (parent[v] < 0) {
+      memset(up + v * bb, 0, sizeof(double) * bb);
+      memset(down + v * bb, 0, sizeof(double) * bb);
+    } else {
+      normals(seed, 6, 0, (uint64_t)(v * bb), bb, sd, up + v * bb);
+      normals(seed, 7, 0, (uint64_t)(v * bb), bb, sd, down + v * bb);
+    }
+  }
+  for (int64_t v = 0; v < n; ++v) { /* row sums: serial, a parent collects from children */
+    const int64_t p = parent[v];
+    if (p < 0) continue;
+    for (int r = 0; r < b; ++r)
+      for (int c = 0; c < b; ++c) {
+        ex[v * b + r] += fabs(down[v * bb + r * b + c]);
+        ex[p * b + r] += fabs(up[v * bb + r * b + c]);
+      }
+  }
+#pragma omp parallel
+  {
+    double *R = (double *)malloc(sizeof(double) * bb);
+#pragma omp for schedule(static)
+    for (int64_t v = 0; v < n; ++v) {
+      normals(seed, 8, 0, (uint64_t)(v * bb), bb, sd, R);
+      dominant_block(b, R, ex + v * b, diag_load, diag + v * bb);
+    }
+    free(R);
+  }
+  free(ex);
+}
