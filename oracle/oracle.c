@@ -862,8 +862,8 @@ ORACLE_API int oracle_nonsym_tree(int64_t n, int b, const int32_t *parent, const
   double *T2 = T + bb, *T3 = T + 2 * bb;
   memcpy(S, diag, sizeof(double) * n * bb);
   int32_t fail = 0;
-  for (int32_t d = H; d >= 0 && !fail; --d)
-    for (int64_t q = cnt[d]; q < cnt[d + 1]; ++q) {
+  for (int32_t lev = H; lev >= 0 && !fail; --lev)  /* deepest level first */
+    for (int64_t q = cnt[lev]; q < cnt[lev + 1]; ++q) {
       const int64_t v = order[q], p = parent[v];
       if (gen_inverse(b, S + v * bb, Si + v * bb)) {
         fail = (int32_t)(v + 1);
