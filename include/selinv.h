@@ -326,6 +326,42 @@ SELINV_API int selinv_tree_sample_f32(const selinv_tree_plan *plan, const float 
                            const float *factor, int64_t k, const float *z, float *x,
                            void *stream);
 
+/* ------------------------------------------------ non-symmetric ladder
+ * (gabp-sparse-inv 0.3.2, "Implemented and tested kernels", items
+ * Non-symmetric chain and Non-symmetric tree.)  General blocks, no symmetry
+ * or definiteness assumed, eliminated without pivoting (safe while the matrix
+ * is block-diagonally dominant); info = 1 + the block whose elimination met a
+ * zero or non-finite pivot, and that matrix's outputs are NaN.
+ *
+ * Block lower-bidiagonal M (fully local: G_ii = M_ii^{-1} and
+ * G_{i+1,i} = -M_{i+1,i+1}^{-1} M_{i+1,i} M_ii^{-1}), per matrix of B:
+ *   diag [B][L][b][b] M_ii, lower [B][L-1][b][b] M_{i+1,i};
+ *   G_diag, G_lower likewise; info [B] (1 + smallest failing block index).
+ * Workspace: selinv_bidiag_workspace_bytes. */
+SELINV_API size_t selinv_bidiag_workspace_bytes(int64_t B);
+SELINV_API int selinv_bidiag_f64(int64_t B, int64_t L, int32_t b, const double *diag,
+                      const double *lower, double *G_diag, double *G_lower, int32_t *info,
+                      void *workspace, size_t workspace_bytes, void *stream);
+SELINV_API int selinv_bidiag_f32(int64_t B, int64_t L, int32_t b, const float *diag,
+                      const float *lower, float *G_diag, float *G_lower, int32_t *info,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Non-symmetric tree with independent directed edge blocks, for a plan of
+ * selinv_tree_plan_create (same n, b, dtype):
+ *   diag [n][b][b] M_vv, up [n][b][b] up[v] = M_{parent(v),v},
+ *   down [n][b][b] down[v] = M_{v,parent(v)} (root slots ignored);
+ *   G_diag, G_up [v] = (M^-1)_{parent(v),v}, G_down [v] = (M^-1)_{v,parent(v)}
+ *   (root slots written as 0); info [1] as for selinv_tree_*. */
+SELINV_API size_t selinv_nonsym_tree_workspace_bytes(const selinv_tree_plan *plan);
+SELINV_API int selinv_nonsym_tree_f64(const selinv_tree_plan *plan, const double *diag,
+                           const double *up, const double *down, double *G_diag, double *G_up,
+                           double *G_down, int32_t *info, void *workspace, size_t workspace_bytes,
+                           void *stream);
+SELINV_API int selinv_nonsym_tree_f32(const selinv_tree_plan *plan, const float *diag,
+                           const float *up, const float *down, float *G_diag, float *G_up,
+                           float *G_down, int32_t *info, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -127,6 +127,17 @@ def lib():
             f = getattr(L, "selinv_%s_%s" % (name, sfx))
             f.argtypes = args
             f.restype = ctypes.c_int
+    L.selinv_bidiag_workspace_bytes.argtypes = [i64]
+    L.selinv_bidiag_workspace_bytes.restype = sz
+    L.selinv_nonsym_tree_workspace_bytes.argtypes = [vp]
+    L.selinv_nonsym_tree_workspace_bytes.restype = sz
+    for sfx in ("f64", "f32"):
+        f = getattr(L, "selinv_bidiag_" + sfx)
+        f.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        f.restype = ctypes.c_int
+        f = getattr(L, "selinv_nonsym_tree_" + sfx)
+        f.argtypes = [vp] * 8 + [vp, sz, vp]
+        f.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -772,3 +783,70 @@ def tree_factor(parent, diag, edge, keep_factor=True, plan: TreePlan | None = No
 def tree_logdet(parent, diag, edge, return_info=False):
     f = tree_factor(parent, diag, edge, keep_factor=False)
     return (f.logdet, f.info) if return_info else f.logdet
+
+
+# ------------------------------------------------- non-symmetric ladder
+def bidiag(diag, lower, check=False, return_info=False):
+    """Selected inverse of block lower-bidiagonal (non-symmetric) matrices:
+    diag [..., L, b, b] = M_ii, lower [..., L-1, b, b] = M_{i+1,i}.  Returns
+    (G_diag, G_lower) on M's pattern (the page's selinv_bidiag forward); no
+    pivoting, info = 1 + the block whose inverse broke down."""
+    dt, dev = diag.dtype, diag.device
+    diag = _check_tensor(diag, "diag", dev, dt)
+    lower = _check_tensor(lower, "lower", dev, dt)
+    sfx = _sfx(diag)
+    if diag.dim() < 3 or diag.shape[-1] != diag.shape[-2]:
+        raise ValueError("diag must be [..., L, b, b]")
+    *batch, L, b, _ = diag.shape
+    if L < 1 or b < 1 or b > MAX_B:
+        raise ValueError("need L >= 1 and 1 <= b <= %d" % MAX_B)
+    if tuple(lower.shape) != tuple(batch) + (L - 1, b, b):
+        raise ValueError("lower must be [..., L-1, b, b] matching diag")
+    B = 1
+    for s_ in batch:
+        B *= s_
+    G_diag, G_lower = torch.empty_like(diag), torch.empty_like(lower)
+    info = torch.empty(tuple(batch), dtype=torch.int32, device=dev)
+    nb = lib().selinv_bidiag_workspace_bytes(B)
+    ws = _workspace(nb, dev)
+    with torch.cuda.device(dev):
+        rc = getattr(lib(), "selinv_bidiag_" + sfx)(B, L, b, _ptr(diag), _ptr(lower),
+                                                     _ptr(G_diag), _ptr(G_lower), _ptr(info),
+                                                     _ptr(ws), nb, _stream(dev))
+    _status(rc, "selinv_bidiag_" + sfx)
+    if check:
+        _raise_info(info, "bidiag")
+    return (G_diag, G_lower, info) if return_info else (G_diag, G_lower)
+
+
+def nonsym_tree(parent, diag, up, down, check=False, return_info=False,
+                plan: TreePlan | None = None):
+    """Selected inverse of a non-symmetric block matrix whose off-diagonal graph
+    is a tree: up[v] = M_{parent(v),v}, down[v] = M_{v,parent(v)}.  Returns
+    (G_diag, G_up, G_down) with G_up[v] = (M^-1)_{parent(v),v},
+    G_down[v] = (M^-1)_{v,parent(v)} and zero root slots."""
+    dt, dev = diag.dtype, diag.device
+    diag = _check_tensor(diag, "diag", dev, dt)
+    up = _check_tensor(up, "up", dev, dt)
+    down = _check_tensor(down, "down", dev, dt)
+    sfx = _sfx(diag)
+    if diag.dim() != 3 or diag.shape[1] != diag.shape[2] or up.shape != diag.shape or \
+            down.shape != diag.shape:
+        raise ValueError("diag, up and down must be [n, b, b]")
+    n, b = diag.shape[0], diag.shape[1]
+    if plan is None:
+        plan = tree_plan(parent, b, dt, dev)
+    if plan.n != n or plan.b != b or plan.dtype != dt:
+        raise ValueError("plan does not match (n, b, dtype)")
+    G_diag, G_up, G_down = torch.empty_like(diag), torch.empty_like(up), torch.empty_like(down)
+    info = torch.empty((), dtype=torch.int32, device=dev)
+    nb = int(lib().selinv_nonsym_tree_workspace_bytes(plan.handle))
+    ws = _workspace(nb, dev)
+    with torch.cuda.device(dev):
+        rc = getattr(lib(), "selinv_nonsym_tree_" + sfx)(
+            plan.handle, _ptr(diag), _ptr(up), _ptr(down), _ptr(G_diag), _ptr(G_up),
+            _ptr(G_down), info.data_ptr(), _ptr(ws), nb, _stream(dev))
+    _status(rc, "selinv_nonsym_tree_" + sfx)
+    if check:
+        _raise_info(info.reshape(1), "nonsym_tree")
+    return (G_diag, G_up, G_down, info) if return_info else (G_diag, G_up, G_down)

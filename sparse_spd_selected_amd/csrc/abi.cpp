@@ -220,6 +220,37 @@ int tree_apply_entry(const selinv_tree_plan *plan, const T *edge, const T *facto
   return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
 }
 
+template <typename T>
+int bidiag_entry(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower, T *G_diag,
+                 T *G_lower, int32_t *info, void *ws, size_t ws_bytes, void *stream) {
+  if (B < 0 || L < 1 || bad_b(b) || B * L > 0x7fffffff) return SELINV_ERR_INVALID_ARG;
+  if (B == 0) return SELINV_OK;
+  if (!diag || !G_diag || (L > 1 && (!lower || !G_lower))) return SELINV_ERR_INVALID_ARG;
+  if (misaligned(diag) || misaligned(G_diag) || (L > 1 && (misaligned(lower) || misaligned(G_lower))))
+    return SELINV_ERR_INVALID_ARG;
+  const size_t need = selinv::bidiag_workspace_bytes(B);
+  if (ws_bytes < need || !ws || misaligned_ws(ws)) return SELINV_ERR_INVALID_ARG;
+  const hipError_t e = selinv::bidiag_launch<T>(B, L, b, diag, lower, G_diag, G_lower, info, ws,
+                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
+}
+
+template <typename T>
+int nonsym_tree_entry(const selinv_tree_plan *plan, const T *diag, const T *up, const T *down,
+                      T *G_diag, T *G_up, T *G_down, int32_t *info, void *ws, size_t ws_bytes,
+                      void *stream) {
+  if (!plan || plan->dtype_bytes != static_cast<int>(sizeof(T))) return SELINV_ERR_INVALID_ARG;
+  if (!diag || !up || !down || !G_diag || !G_up || !G_down) return SELINV_ERR_INVALID_ARG;
+  if (misaligned(diag) || misaligned(up) || misaligned(down) || misaligned(G_diag) ||
+      misaligned(G_up) || misaligned(G_down))
+    return SELINV_ERR_INVALID_ARG;
+  const size_t need = selinv::nonsym_tree_workspace_bytes(plan);
+  if (ws_bytes < need || !ws || misaligned_ws(ws)) return SELINV_ERR_INVALID_ARG;
+  const hipError_t e = selinv::nonsym_tree_launch<T>(plan, diag, up, down, G_diag, G_up, G_down,
+                                                     info, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -505,6 +536,42 @@ int selinv_tree_solve_f32(const selinv_tree_plan *plan, const float *edge, const
 int selinv_tree_sample_f32(const selinv_tree_plan *plan, const float *edge, const float *factor,
                            int64_t k, const float *z, float *x, void *stream) {
   return tree_apply_entry<float>(plan, edge, factor, k, z, x, nullptr, 0, true, stream);
+}
+
+size_t selinv_bidiag_workspace_bytes(int64_t B) {
+  return B < 0 ? 0 : selinv::bidiag_workspace_bytes(B);
+}
+
+size_t selinv_nonsym_tree_workspace_bytes(const selinv_tree_plan *plan) {
+  return plan ? selinv::nonsym_tree_workspace_bytes(plan) : 0;
+}
+
+int selinv_bidiag_f64(int64_t B, int64_t L, int32_t b, const double *diag, const double *lower,
+                      double *G_diag, double *G_lower, int32_t *info, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  return bidiag_entry<double>(B, L, b, diag, lower, G_diag, G_lower, info, workspace,
+                           workspace_bytes, stream);
+}
+
+int selinv_nonsym_tree_f64(const selinv_tree_plan *plan, const double *diag, const double *up,
+                           const double *down, double *G_diag, double *G_up, double *G_down, int32_t *info,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  return nonsym_tree_entry<double>(plan, diag, up, down, G_diag, G_up, G_down, info, workspace,
+                                workspace_bytes, stream);
+}
+
+int selinv_bidiag_f32(int64_t B, int64_t L, int32_t b, const float *diag, const float *lower,
+                      float *G_diag, float *G_lower, int32_t *info, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  return bidiag_entry<float>(B, L, b, diag, lower, G_diag, G_lower, info, workspace,
+                           workspace_bytes, stream);
+}
+
+int selinv_nonsym_tree_f32(const selinv_tree_plan *plan, const float *diag, const float *up,
+                           const float *down, float *G_diag, float *G_up, float *G_down, int32_t *info,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  return nonsym_tree_entry<float>(plan, diag, up, down, G_diag, G_up, G_down, info, workspace,
+                                workspace_bytes, stream);
 }
 
 }  // extern "C"

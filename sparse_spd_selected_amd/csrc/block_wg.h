@@ -206,6 +206,40 @@ __device__ inline void rev_cholesky(T *U, const T *S, int b) {
   }
 }
 
+// In-place inverse of a general block by Gauss-Jordan elimination without
+// pivoting: pivot k maps a_kk -> 1/d, a_kj -> a_kj / d and a_ik -> -a_ik / d
+// (i, j != k), a_ij -> a_ij - a_ik a_kj / d, with d = a_kk.  `rowk`, `colk`
+// are LDS scratch of b entries.  Returns 1 (uniformly across the workgroup)
+// if a pivot is zero or not finite; then A holds garbage.
+template <typename T>
+__device__ inline int gen_inverse(T *A, int b, T *rowk, T *colk) {
+  for (int k = 0; k < b; ++k) {
+    const T d = A[k * b + k];
+    if (d == T(0) || !__builtin_isfinite(d)) return 1;
+    if (tid() < b) {
+      rowk[tid()] = A[k * b + tid()];
+      colk[tid()] = A[tid() * b + k];
+    }
+    __syncthreads();
+    const T inv = T(1) / d;
+    for (int e = tid(); e < b * b; e += nthreads()) {
+      const int i = e / b, j = e % b;
+      T a;
+      if (i == k && j == k)
+        a = inv;
+      else if (i == k)
+        a = rowk[j] * inv;
+      else if (j == k)
+        a = -colk[i] * inv;
+      else
+        a = A[e] - colk[i] * (rowk[j] * inv);
+      A[e] = a;
+    }
+    __syncthreads();
+  }
+  return 0;
+}
+
 // In-place inverse of a symmetric positive definite block by the symmetric
 // Gauss-Jordan sweep, without pivoting.  Sweeping pivot k maps
 //   a_ij -> a_ij - a_ik a_kj / d   (i, j != k),   a_ik -> a_ik / d,

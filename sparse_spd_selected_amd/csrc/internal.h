@@ -205,4 +205,15 @@ template <typename T>
 hipError_t tree_apply_launch(const selinv_tree_plan *plan, int64_t k, bool sample, const T *edge,
                              const T *factor, const T *in, T *out, void *ws, hipStream_t s);
 
+// ------------------------------------ non-symmetric ladder (nonsym.hip)
+size_t bidiag_workspace_bytes(int64_t B);
+template <typename T>
+hipError_t bidiag_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower,
+                         T *G_diag, T *G_lower, int32_t *info, void *ws, hipStream_t s);
+size_t nonsym_tree_workspace_bytes(const selinv_tree_plan *plan);
+template <typename T>
+hipError_t nonsym_tree_launch(const selinv_tree_plan *plan, const T *diag, const T *up,
+                              const T *down, T *G_diag, T *G_up, T *G_down, int32_t *info,
+                              void *ws, hipStream_t s);
+
 }  // namespace selinv
