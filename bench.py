@@ -80,6 +80,10 @@ def nominal_flops(kind, cfg, op="selinv"):
         return 8 * b * b * k * nblk
     if op == "sample":
         return (5 * b * b * k + b ** 3 // 3) * nblk
+    if kind == "bidiag":  # general inverse 2 b^3 per block, two products per lower block
+        return cfg["B"] * (2 * b ** 3 * cfg["L"] + 4 * b ** 3 * (cfg["L"] - 1))
+    if kind == "nonsym_tree":  # collect 6 b^3, distribute 10 b^3 per non-root; root 2 b^3
+        return 16 * b ** 3 * (cfg["n"] - 1) + 2 * b ** 3
     per, root = {"selinv": (7, 1), "vjp": (22, 4), "logdet": (4, 1)}[op]
     if kind == "chain":
         return cfg["B"] * (per * b ** 3 * (cfg["L"] - 1) + root * b ** 3)
@@ -94,6 +98,10 @@ def compulsory_bytes(kind, cfg, w, op="selinv"):
     output cotangents read once, input cotangents written once, logdet_bar
     (f64) and info."""
     b2 = cfg["b"] ** 2
+    if kind == "bidiag":  # diag, lower in; G_diag, G_lower out; info
+        return cfg["B"] * (2 * (2 * cfg["L"] - 1) * b2 * w + 4)
+    if kind == "nonsym_tree":  # diag, up, down in (root edges skipped); three outputs
+        return (3 * cfg["n"] - 2 + 3 * cfg["n"]) * b2 * w + 4 * cfg["n"] + 4
     if op == "logdet":  # inputs read once, log det and info written
         if kind == "chain":
             return cfg["B"] * ((2 * cfg["L"] - 1) * b2 * w + 12)
@@ -120,7 +128,7 @@ def compulsory_bytes(kind, cfg, w, op="selinv"):
 
 
 def block_rows(kind, cfg):
-    if kind == "chain":
+    if kind in ("chain", "bidiag"):
         return cfg["B"] * cfg["L"]
     if kind == "star":
         return cfg["B"] * (cfg["K"] + 1)
@@ -139,7 +147,14 @@ def make_inputs(kind, cfg, dt, dev):
         arrs = spdgen.star(cfg["B"], cfg["K"], cfg["b"], seed=cfg["seed"],
                            diag_load=cfg["diag_load"])
         return [torch.from_numpy(x).to(dev).to(dt) for x in arrs], None
+    if kind == "bidiag":
+        d, l = spdgen.nonsym_bidiag(cfg["B"], cfg["L"], cfg["b"], seed=cfg["seed"],
+                                    diag_load=cfg["diag_load"])
+        return [torch.from_numpy(x).to(dev).to(dt) for x in (d, l)], None
     parent = spdgen.random_recursive_tree(cfg["n"], cfg["seed"])
+    if kind == "nonsym_tree":
+        arrs = spdgen.nonsym_tree(parent, cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
+        return [torch.from_numpy(x).to(dev).to(dt) for x in arrs], np.asarray(parent)
     d, e = spdgen.tree(parent, cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
     return [torch.from_numpy(x).to(dev).to(dt) for x in (d, e)], np.asarray(parent)
 
@@ -208,6 +223,11 @@ def run_gpu(kind, cfg, dtname, steps, warmup, op="selinv"):
         call = lambda: ssa.chain(*inputs)
     elif kind == "star":
         call = lambda: ssa.star(*inputs)
+    elif kind == "bidiag":
+        call = lambda: ssa.bidiag(*inputs)
+    elif kind == "nonsym_tree":
+        plan = ssa.tree_plan(parent, cfg["b"], dt, dev)
+        call = lambda: ssa.nonsym_tree(parent, *inputs, plan=plan)
     else:
         plan = ssa.tree_plan(parent, cfg["b"], dt, dev)
         call = lambda: ssa.tree(parent, *inputs, plan=plan)
@@ -324,6 +344,29 @@ def cpu_baseline(kind, cfg, op="selinv"):
     import oracle
     import spdgen
     lib = oracle.load()
+    if kind in ("bidiag", "nonsym_tree"):
+        if kind == "bidiag":
+            Bs = min(cfg["B"], 1024)
+            d, l = spdgen.nonsym_bidiag(Bs, cfg["L"], cfg["b"], seed=cfg["seed"],
+                                        diag_load=cfg["diag_load"])
+            t0 = time.perf_counter()
+            oracle.bidiag(d, l, lib=lib)
+            t = time.perf_counter() - t0
+            sub = dict(cfg, B=Bs)
+            sample = "%d of %d matrices (L=%d, b=%d), float64" % (Bs, cfg["B"], cfg["L"], cfg["b"])
+            cores = int(lib.oracle_num_threads())
+        else:
+            parent = spdgen.random_recursive_tree(cfg["n"], cfg["seed"])
+            arrs = spdgen.nonsym_tree(parent, cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
+            t0 = time.perf_counter()
+            oracle.nonsym_tree(parent, *arrs, lib=lib)
+            t = time.perf_counter() - t0
+            sub = cfg
+            sample = "the whole tree (n=%d, b=%d), float64, single thread" % (cfg["n"], cfg["b"])
+            cores = 1
+        return {"value": round(nominal_flops(kind, sub, op) / t / 1e9, 3), "unit": "GFLOP/s",
+                "cores": cores, "kind": "oracle", "sample": sample, "seconds": round(t, 3),
+                "block_rows_per_s": round(block_rows(kind, sub) / t, 1)}
     if kind == "chain":
         Bs = cfg["B"] if cfg["B"] * cfg["L"] * cfg["b"] ** 3 <= 4e9 else max(1, int(4e9 // (cfg["L"] * cfg["b"] ** 3)))
         d, l = spdgen.chain(Bs, cfg["L"], cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
