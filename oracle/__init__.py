@@ -62,10 +62,12 @@ def load(path: str | None = None):
     lib.oracle_bidiag.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp]
     lib.oracle_nonsym_tree.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_chain_apply.argtypes = [i64, i64, i32, vp, vp, i64, vp, vp, i32, vp]
+    lib.oracle_eliminate.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp, i64]
+    lib.oracle_junction.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     for f in (lib.oracle_chain, lib.oracle_star, lib.oracle_tree, lib.oracle_tree_depths,
               lib.oracle_num_threads, lib.oracle_tree_vjp, lib.oracle_chain_vjp,
               lib.oracle_tree_apply, lib.oracle_chain_apply, lib.oracle_bidiag,
-              lib.oracle_nonsym_tree):
+              lib.oracle_nonsym_tree, lib.oracle_eliminate, lib.oracle_junction):
         f.restype = ctypes.c_int
     if path == _LIB:
         _lib = lib
@@ -313,3 +315,96 @@ def nonsym_tree(parent, diag, up, down, lib=None):
     if rc:
         raise OracleError("oracle_nonsym_tree status %d" % rc)
     return Gd, Gu, Gw, int(info[0])
+
+
+# -------------------------------------------------------- junction tree
+
+def eliminate(n, edge_index, order=None, lib=None):
+    """Symbolic elimination of the block pattern (oracle_eliminate).
+
+    edge_index int32 [2, m], pairs (i, j) with i > j; order: None (greedy
+    minimum degree, smallest label on ties) or a permutation of range(n)
+    listing the nodes in elimination order.
+    -> (order [n], nbr_ptr [n+1], nbr [nnz]): step s eliminates order[s], whose
+    later neighbours (labels, ascending) are nbr[nbr_ptr[s]:nbr_ptr[s+1]]."""
+    lib = lib or load()
+    ei = np.ascontiguousarray(edge_index[0], dtype=np.int32)
+    ej = np.ascontiguousarray(edge_index[1], dtype=np.int32)
+    oin = None if order is None else np.ascontiguousarray(order, dtype=np.int32)
+    if oin is not None and oin.shape != (n,):
+        raise OracleError("order must have n entries")
+    out = np.empty(n, np.int32)
+    ptr = np.empty(n + 1, np.int64)
+    cap = 4 * ei.shape[0] + n
+    while True:
+        nbr = np.empty(max(cap, 1), np.int32)
+        rc = lib.oracle_eliminate(n, ei.shape[0], _p(ei), _p(ej), _p(oin) if oin is not None else None,
+                                  _p(out), _p(ptr), _p(nbr), cap)
+        if rc == 3:
+            cap = int(ptr[n])
+            continue
+        if rc:
+            raise OracleError("oracle_eliminate status %d" % rc)
+        return out, ptr, nbr[:ptr[n]].copy()
+
+
+def filled_pattern(n, edge_index, order=None, lib=None):
+    """The filled (chordal) pattern S of an elimination.
+
+    Returns a dict with the elimination (order, pos, nbr_ptr, nbr), the owner
+    node of every slot (col: the label eliminated at the slot's step), and
+    the lower pattern S_index int32 [2, nnz]: every pair (i, j), i > j, of S,
+    sorted by i then j.  slot[k] is the slot of S entry k and flip[k] says
+    that the slot's block (w, v) is the transpose of G_{i,j} (w < v)."""
+    order, ptr, nbr = eliminate(n, edge_index, order, lib)
+    pos = np.empty(n, np.int64)
+    pos[order] = np.arange(n)
+    col = np.repeat(order, np.diff(ptr)).astype(np.int64)
+    w = nbr.astype(np.int64)
+    i, j = np.maximum(w, col), np.minimum(w, col)
+    slot = np.lexsort((j, i))
+    S_index = np.stack([i[slot], j[slot]]).astype(np.int32)
+    return dict(order=order, pos=pos, nbr_ptr=ptr, nbr=nbr, col=col, S_index=S_index,
+                slot=slot, flip=(w < col)[slot])
+
+
+def junction(diag, edge_index, edge_val, order=None, lib=None, pattern=None):
+    """Selected inverse of general sparse SPD matrices sharing one pattern.
+
+    diag [B,n,b,b] (or [n,b,b]), edge_index int32 [2,m] with i > j,
+    edge_val [B,m,b,b] with edge_val[e] = A_{i_e, j_e}; order as for
+    `eliminate`.  -> (G_diag [B,n,b,b], S_index [2,nnz], G_lower [B,nnz,b,b]
+    with G_lower[k] = (A^-1)_{S_index[0,k], S_index[1,k]}, logdet [B], info [B]).
+    """
+    lib = lib or load()
+    diag, edge_val = _f64(diag), _f64(edge_val)
+    single = diag.ndim == 3
+    if single:
+        diag, edge_val = diag[None], edge_val[None]
+    B, n, b = diag.shape[0], diag.shape[1], diag.shape[2]
+    ei = np.asarray(edge_index[0], dtype=np.int64)
+    ej = np.asarray(edge_index[1], dtype=np.int64)
+    P = pattern or filled_pattern(n, edge_index, order, lib)
+    nnz = P["nbr"].shape[0]
+    # A on the slots: A_{w,v} = edge_val[e] when (w, v) = (i_e, j_e), its
+    # transpose when (w, v) = (j_e, i_e), zero on fill
+    key = {(int(a), int(c)): e for e, (a, c) in enumerate(zip(ei, ej))}
+    w, v = P["nbr"].astype(np.int64), P["col"]
+    Aoff = np.zeros((B, nnz, b, b))
+    for t in range(nnz):
+        e = key.get((max(w[t], v[t]), min(w[t], v[t])))
+        if e is not None:
+            Aoff[:, t] = edge_val[:, e] if w[t] > v[t] else np.swapaxes(edge_val[:, e], -1, -2)
+    Gd = np.empty_like(diag)
+    Go = np.empty((B, nnz, b, b))
+    logdet = np.empty(B)
+    info = np.empty(B, np.int32)
+    rc = lib.oracle_junction(B, n, b, _p(P["order"]), _p(P["nbr_ptr"]), _p(P["nbr"]), _p(diag),
+                             _p(Aoff), _p(Gd), _p(Go), _p(logdet), _p(info))
+    if rc:
+        raise OracleError("oracle_junction status %d" % rc)
+    Gl = Go[:, P["slot"]]
+    Gl[:, P["flip"]] = np.swapaxes(Gl[:, P["flip"]], -1, -2)
+    if single:
+        return Gd[0], P["S_index"], Gl[0], logdet[0], int(info[0])
+    return Gd, P["S_index"], Gl, logdet, info

@@ -903,6 +903,205 @@ ORACLE_API int oracle_nonsym_tree(int64_t n, int b, const int32_t *parent, const
   return 0;
 }
 
+/* ------------------------------------------------------- junction tree
+ * General sparse SPD (gabp-sparse-inv page, junction-tree section): an
+ * arbitrary block pattern is eliminated node by node in an elimination order
+ * (default: greedy minimum degree); eliminating v joins all of v's remaining
+ * neighbours into a clique, so the pattern grows to its chordal completion S
+ * = pattern(L + L^T).  The selected inverse on S then follows from the block
+ * LDL^T factor by the multi-neighbour Takahashi recurrence.
+ *
+ * Symbolic part.  The elimination graph is a dense n x n byte matrix; the
+ * degree of a node is its number of remaining neighbours.  Minimum degree
+ * picks, at every step, the remaining node of smallest degree, the smallest
+ * label among ties.  For step s (node v = order[s]) the labels of v's
+ * remaining neighbours at that moment, ascending, are nbr[nbr_ptr[s] ..
+ * nbr_ptr[s+1]): the later nodes w with (w, v) in S.  Returns 0, 2 for bad
+ * input (an edge out of range, i <= j, a repeated edge, an order that is not
+ * a permutation), 3 if `cap` is too small (nbr_ptr[n] then holds the size
+ * needed; nothing else is meaningful). */
+ORACLE_API int oracle_eliminate(int64_t n, int64_t m, const int32_t *ei, const int32_t *ej,
+                                const int32_t *order_in, int32_t *order_out, int64_t *nbr_ptr,
+                                int32_t *nbr, int64_t cap) {
+  if (n < 1 || n > 16384 || m < 0) return 2;
+  unsigned char *adj = (unsigned char *)calloc((size_t)(n * n), 1);
+  unsigned char *gone = (unsigned char *)calloc((size_t)n, 1);
+  int64_t *deg = (int64_t *)calloc((size_t)n, sizeof(int64_t));
+  int32_t *nb = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+  int rc = 0;
+  for (int64_t e = 0; e < m && !rc; ++e) {
+    const int64_t i = ei[e], j = ej[e];
+    if (j < 0 || i <= j || i >= n || adj[i * n + j]) {
+      rc = 2;
+      break;
+    }
+    adj[i * n + j] = adj[j * n + i] = 1;
+    deg[i]++;
+    deg[j]++;
+  }
+  int64_t fill = 0;
+  nbr_ptr[0] = 0;
+  for (int64_t s = 0; s < n && !rc; ++s) {
+    int64_t v = -1;
+    if (order_in) {
+      v = order_in[s];
+      if (v < 0 || v >= n || gone[v]) {
+        rc = 2;
+        break;
+      }
+    } else {
+      for (int64_t u = 0; u < n; ++u)
+        if (!gone[u] && (v < 0 || deg[u] < deg[v])) v = u;
+    }
+    gone[v] = 1;
+    order_out[s] = (int32_t)v;
+    int64_t k = 0;
+    for (int64_t u = 0; u < n; ++u)
+      if (adj[v * n + u]) nb[k++] = (int32_t)u;
+    for (int64_t a = 0; a < k; ++a) {
+      if (fill + a < cap) nbr[fill + a] = nb[a];
+      for (int64_t c = a + 1; c < k; ++c) {
+        const int64_t x = nb[a], y = nb[c];
+        if (!adj[x * n + y]) {
+          adj[x * n + y] = adj[y * n + x] = 1;
+          deg[x]++;
+          deg[y]++;
+        }
+      }
+    }
+    for (int64_t a = 0; a < k; ++a) {
+      adj[v * n + nb[a]] = adj[nb[a] * n + v] = 0;
+      deg[nb[a]]--;
+    }
+    fill += k;
+    nbr_ptr[s + 1] = fill;
+  }
+  if (!rc && fill > cap) rc = 3;
+  free(adj);
+  free(gone);
+  free(deg);
+  free(nb);
+  return rc;
+}
+
+/* Slot of the block (w, x) of S, x eliminated before w: its index in the
+ * neighbour list of x's elimination step; -1 if absent. */
+static int64_t junction_slot(const int64_t *nbr_ptr, const int32_t *nbr, const int32_t *pos,
+                             int32_t w, int32_t x) {
+  const int64_t s = pos[x];
+  for (int64_t t = nbr_ptr[s]; t < nbr_ptr[s + 1]; ++t)
+    if (nbr[t] == w) return t;
+  return -1;
+}
+
+/* Numeric part, for a batch of B matrices on the pattern of one elimination
+ * (order, nbr_ptr, nbr from oracle_eliminate).  Slot t of the neighbour list
+ * of step s holds the block (w, v) of S with w = nbr[t] and v = order[s].
+ *   diag   [B][n]   A_vv by label;  Aoff [B][nnz]  A_{w,v} per slot (zero
+ *                   where (w, v) is fill)
+ *   G_diag [B][n]   (A^-1)_vv by label;  G_off [B][nnz]  (A^-1)_{w,v} per slot
+ *   logdet [B], info [B] (0, or 1 + the label of the first node in the
+ *                   elimination order whose Schur pivot is not positive
+ *                   definite; logdet is then NaN).
+ * Block LDL^T, right-looking, in the elimination order: the pivot of v is
+ * D_v = C_vv (the fully updated diagonal block), L_{w,v} = C_{w,v} D_v^-1 for
+ * every later neighbour w, and every pair (w1, w2) of later neighbours
+ * receives C_{w1,w2} -= L_{w1,v} D_v L_{w2,v}^T (= L_{w1,v} C_{w2,v}^T).
+ * Takahashi, in reverse elimination order, with N = the later neighbours of v:
+ *   G_{w,v} = - sum_{x in N} G_{w,x} L_{x,v}        (w in N)
+ *   G_vv    = D_v^-1 - sum_{w in N} L_{w,v}^T G_{w,v}
+ * where G_{w,x} for w before x is G_{x,w}^T.  Every block read lies in S
+ * because N is a clique of S; returns 4 if the given pattern is not closed
+ * that way (not the output of an elimination), else 0. */
+ORACLE_API int oracle_junction(int64_t B, int64_t n, int b, const int32_t *order,
+                               const int64_t *nbr_ptr, const int32_t *nbr, const double *diag,
+                               const double *Aoff, double *G_diag, double *G_off, double *logdet,
+                               int32_t *info) {
+  const int64_t bb = (int64_t)b * b, nnz = nbr_ptr[n];
+  int32_t *pos = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+  for (int64_t s = 0; s < n; ++s) pos[order[s]] = (int32_t)s;
+  int bad_pattern = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t mat = 0; mat < B; ++mat) {
+    double *Cd = (double *)malloc(sizeof(double) * (size_t)(n * bb));
+    double *Co = (double *)malloc(sizeof(double) * (size_t)((nnz ? nnz : 1) * bb));
+    double *Lo = (double *)malloc(sizeof(double) * (size_t)((nnz ? nnz : 1) * bb));
+    double *Di = (double *)malloc(sizeof(double) * (size_t)(n * bb));
+    double *R = (double *)malloc(sizeof(double) * bb);
+    double *T = (double *)malloc(sizeof(double) * bb);
+    double *T2 = (double *)malloc(sizeof(double) * bb);
+    double *Gd = G_diag + mat * n * bb, *Go = G_off + mat * nnz * bb;
+    memcpy(Cd, diag + mat * n * bb, sizeof(double) * (size_t)(n * bb));
+    memcpy(Co, Aoff + mat * nnz * bb, sizeof(double) * (size_t)(nnz * bb));
+    int32_t fail = 0;
+    double ld = 0.0;
+    for (int64_t s = 0; s < n; ++s) {
+      const int32_t v = order[s];
+      /* the pivot: D_v = R R^T, its inverse and its log det */
+      if (chol(b, Cd + v * bb, R)) {
+        if (!fail) fail = v + 1;
+        fill_nan(Di + v * bb, bb);
+      } else {
+        inv_from_chol(b, R, Di + v * bb);
+        ld += logdet_chol(b, R);
+      }
+      for (int64_t t = nbr_ptr[s]; t < nbr_ptr[s + 1]; ++t)
+        matmul(b, Co + t * bb, Di + v * bb, Lo + t * bb);            /* L_{w,v} */
+      /* Schur update of every pair of later neighbours */
+      for (int64_t t1 = nbr_ptr[s]; t1 < nbr_ptr[s + 1]; ++t1)
+        for (int64_t t2 = nbr_ptr[s]; t2 < nbr_ptr[s + 1]; ++t2) {
+          const int32_t w1 = nbr[t1], w2 = nbr[t2];
+          if (pos[w1] < pos[w2]) continue;
+          mm_nt(b, Lo + t1 * bb, Co + t2 * bb, T);                   /* L_{w1,v} C_{w2,v}^T */
+          const int64_t t12 = w1 == w2 ? 0 : junction_slot(nbr_ptr, nbr, pos, w1, w2);
+          if (t12 < 0) {                          /* not a chordal pattern */
+            bad_pattern = 1;
+            continue;
+          }
+          add_to(bb, w1 == w2 ? Cd + w1 * bb : Co + t12 * bb, T, -1.0);
+        }
+    }
+    /* Takahashi, reverse elimination order */
+    for (int64_t s = n - 1; s >= 0; --s) {
+      const int32_t v = order[s];
+      for (int64_t t = nbr_ptr[s]; t < nbr_ptr[s + 1]; ++t) {
+        const int32_t w = nbr[t];
+        memset(Go + t * bb, 0, sizeof(double) * bb);
+        for (int64_t u = nbr_ptr[s]; u < nbr_ptr[s + 1]; ++u) {
+          const int32_t x = nbr[u];
+          const double *Gwx;
+          const int64_t twx = w == x ? 0 : pos[w] > pos[x] ? junction_slot(nbr_ptr, nbr, pos, w, x)
+                                                           : junction_slot(nbr_ptr, nbr, pos, x, w);
+          if (twx < 0) {
+            bad_pattern = 1;
+            continue;
+          }
+          if (w == x) {
+            Gwx = Gd + w * bb;
+          } else if (pos[w] > pos[x]) {
+            Gwx = Go + twx * bb;
+          } else {
+            transpose(b, Go + twx * bb, T2);
+            Gwx = T2;
+          }
+          matmul(b, Gwx, Lo + u * bb, T);                             /* G_{w,x} L_{x,v} */
+          add_to(bb, Go + t * bb, T, -1.0);
+        }
+      }
+      memcpy(Gd + v * bb, Di + v * bb, sizeof(double) * bb);
+      for (int64_t t = nbr_ptr[s]; t < nbr_ptr[s + 1]; ++t) {
+        mm_tn(b, Lo + t * bb, Go + t * bb, T);                        /* L_{w,v}^T G_{w,v} */
+        add_to(bb, Gd + v * bb, T, -1.0);
+      }
+    }
+    logdet[mat] = fail ? NAN : ld;
+    info[mat] = fail;
+    free(Cd); free(Co); free(Lo); free(Di); free(R); free(T); free(T2);
+  }
+  free(pos);
+  return bad_pattern ? 4 : 0;
+}
+
 /* Depth of every node of a valid tree (host helper for the tests); returns 0,
  * or 2 for an invalid parent array. */
 ORACLE_API int oracle_tree_depths(int64_t n, const int32_t *parent, int32_t *depth) {

@@ -51,6 +51,7 @@ def _load():
         lib.spdgen_cotangent.argtypes = [u64, ctypes.c_uint32, i64, i64, i64, vp]
         lib.spdgen_nonsym_bidiag.argtypes = [u64, i64, i64, i64, i32, dbl, vp, vp]
         lib.spdgen_nonsym_tree.argtypes = [u64, i64, i32, dbl, vp, vp, vp, vp]
+        lib.spdgen_graph.argtypes = [u64, i64, i64, i64, i64, i32, dbl, vp, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -201,6 +202,66 @@ def tree(parent: np.ndarray, b: int, seed: int = 1, diag_load: float = 2.0):
     return diag, edge
 
 
+def grid_edges(rows: int, cols: int) -> np.ndarray:
+    """Edges of the rows x cols grid graph (node r * cols + c), as an int32
+    array [2, m] of pairs (i, j) with i > j: for each node its right
+    neighbour, then its lower neighbour (the grid_edges helper of the
+    gabp-sparse-inv page's junction-tree section)."""
+    e = []
+    for r in range(rows):
+        for c in range(cols):
+            v = r * cols + c
+            if c + 1 < cols:
+                e.append((v + 1, v))
+            if r + 1 < rows:
+                e.append((v + cols, v))
+    return np.array(e, dtype=np.int32).reshape(-1, 2).T.copy()
+
+
+def random_graph_edges(n: int, extra: int, seed: int = 0) -> np.ndarray:
+    """A connected random graph: a random recursive tree on n nodes plus
+    `extra` further distinct random pairs; int32 [2, m] with i > j."""
+    p = random_recursive_tree(n, seed)
+    pairs = {(v, int(p[v])) for v in range(1, n)}
+    rng = np.random.default_rng(seed)
+    while len(pairs) < n - 1 + extra and len(pairs) < n * (n - 1) // 2:
+        i, j = rng.integers(0, n, size=2)
+        if i != j:
+            pairs.add((int(max(i, j)), int(min(i, j))))
+    e = sorted(pairs)
+    return np.array(e, dtype=np.int32).reshape(-1, 2).T.copy()
+
+
+def graph(edge_index: np.ndarray, n: int, b: int, B: int = 1, seed: int = 0,
+          diag_load: float = 2.0, m0: int = 0):
+    """SPD values on an arbitrary block pattern for a batch of B matrices that
+    share it.  ``edge_index`` is int32 [2, m] with rows (i, j), i > j.
+    Returns ``diag [B,n,b,b]`` and ``edge_val [B,m,b,b]`` with
+    ``edge_val[:, e] = A_{i_e, j_e}``."""
+    ei = np.ascontiguousarray(edge_index[0], dtype=np.int32)
+    ej = np.ascontiguousarray(edge_index[1], dtype=np.int32)
+    assert np.all(ei > ej) and np.all(ej >= 0) and np.all(ei < n)
+    m = ei.shape[0]
+    diag = np.empty((B, n, b, b), np.float64)
+    ev = np.empty((B, m, b, b), np.float64)
+    _load().spdgen_graph(seed, m0, B, n, m, b, diag_load, _ptr(ei), _ptr(ej), _ptr(diag),
+                         _ptr(ev))
+    return diag, ev
+
+
+def to_dense_graph(edge_index, diag: np.ndarray, edge_val: np.ndarray) -> np.ndarray:
+    """Assemble one general block matrix (diag [n,b,b], edge_val [m,b,b])."""
+    n, b = diag.shape[0], diag.shape[1]
+    A = np.zeros((n * b, n * b))
+    for v in range(n):
+        A[v * b:(v + 1) * b, v * b:(v + 1) * b] = diag[v]
+    for e in range(edge_index.shape[1]):
+        i, j = int(edge_index[0, e]), int(edge_index[1, e])
+        A[i * b:(i + 1) * b, j * b:(j + 1) * b] = edge_val[e]
+        A[j * b:(j + 1) * b, i * b:(i + 1) * b] = edge_val[e].T
+    return A
+
+
 # --------------------------------------------------------------- workloads
 # The five synthetic workloads the hot path is measured and checked on.
 WORKLOADS = {
@@ -219,6 +280,9 @@ WORKLOADS = {
                                dtypes=("f64", "f32")),
     "nonsym_tree_b8": dict(kind="nonsym_tree", n=262144, b=8, seed=1, diag_load=2.0,
                            dtypes=("f64", "f32")),
+    # general sparse SPD: a batch sharing the 64 x 64 grid pattern, b = 8
+    "junction_grid64_b8": dict(kind="junction", B=16, rows=64, cols=64, b=8, seed=0,
+                               diag_load=2.0, dtypes=("f64", "f32")),
 }
 
 

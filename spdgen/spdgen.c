@@ -384,3 +384,39 @@ SPDGEN_API void spdgen_nonsym_tree(uint64_t seed, int64_t n, int b, double diag_
   }
   free(ex);
 }
+
+/* --------------------------------------------------------- general graph */
+
+/* SPD values on an arbitrary block pattern shared by a batch (matrices
+ * [m0, m0+count)): the random_spd_graph(num_nodes, edges, block_size, seed)
+ * helper of the gabp-sparse-inv page's junction-tree section, restated with
+ * the same recipe as the tree.
+ *   edge_i, edge_j [m]      the pattern edges, edge_i[e] > edge_j[e]
+ *   diag     [count][n][b][b]   D_v
+ *   edge_val [count][m][b][b]   edge_val[e] = A_{edge_i[e], edge_j[e]}
+ * radius(v) = sum over edges at v of the row-abs maximum of the block as it
+ * sits in row v (rowabs_max for the row edge_i, colabs_max for edge_j).
+ * Streams 9 (edge blocks) and 10 (W of the diagonal blocks). */
+SPDGEN_API void spdgen_graph(uint64_t seed, int64_t m0, int64_t count, int64_t n, int64_t m,
+                             int b, double diag_load, const int32_t *edge_i,
+                             const int32_t *edge_j, double *diag, double *edge_val) {
+  const int64_t bb = (int64_t)b * b;
+  const double sd = 1.0 / sqrt((double)b);
+#pragma omp parallel for schedule(static)
+  for (int64_t mat = 0; mat < count; ++mat) {
+    double *E = edge_val + mat * m * bb, *D = diag + mat * n * bb;
+    double *rad = (double *)calloc((size_t)n, sizeof(double));
+    double *W = (double *)malloc(sizeof(double) * bb);
+    for (int64_t e = 0; e < m; ++e) {
+      normals(seed, 9, (uint64_t)(m0 + mat), (uint64_t)(e * bb), bb, sd, E + e * bb);
+      rad[edge_i[e]] += rowabs_max(b, E + e * bb);
+      rad[edge_j[e]] += colabs_max(b, E + e * bb);
+    }
+    for (int64_t v = 0; v < n; ++v) {
+      normals(seed, 10, (uint64_t)(m0 + mat), (uint64_t)(v * bb), bb, 1.0, W);
+      gram_block(b, W, diag_load + rad[v], D + v * bb);
+    }
+    free(W);
+    free(rad);
+  }
+}

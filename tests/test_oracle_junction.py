@@ -1,0 +1,241 @@
+"""Pins for the oracle's general sparse SPD selected inverse (the junction-tree
+section of the gabp-sparse-inv page: elimination to the chordal pattern, then
+the multi-neighbour Takahashi recurrence).
+
+Independent references:
+  * the hand-derived minimum-degree elimination of the 3 x 3 grid under
+    tests/golden/ (order, cliques and fill);
+  * numpy's dense inverse and slogdet of the assembled matrix, read on the
+    filled pattern, for grids, random graphs, trees and complete graphs, with
+    the default order and with explicit orders;
+  * the structural nonzeros of numpy's Cholesky factor of the permuted matrix
+    (scalar blocks, random values) must be exactly the filled pattern;
+  * minimum degree on a tree creates no fill, and then the result must be the
+    tree oracle's (pinned on its own); a path is the chain;
+  * planted mistakes must break one of the above.
+"""
+import os
+import re
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+import spdgen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "junction_grid3x3_mindegree.txt")
+
+
+def blk(M, r, c, b):
+    return M[r * b:(r + 1) * b, c * b:(c + 1) * b]
+
+
+def read_golden():
+    order, steps, fill = None, {}, set()
+    for line in open(GOLDEN):
+        t = line.split()
+        if not t or t[0].startswith("#"):
+            continue
+        if t[0] == "order":
+            order = [int(x) for x in t[1:]]
+        elif t[0] == "step":
+            steps[int(t[1])] = [int(x) for x in t[2:]]
+        elif t[0] == "fill":
+            fill.add((int(t[1]), int(t[2])))
+    return order, steps, fill
+
+
+def test_golden_grid3x3_min_degree():
+    order, steps, fill = read_golden()
+    e = spdgen.grid_edges(3, 3)
+    o, ptr, nbr = oracle.eliminate(9, e)
+    assert list(o) == order
+    for s, v in enumerate(o):
+        assert list(nbr[ptr[s]:ptr[s + 1]]) == steps[int(v)]
+    S = oracle.filled_pattern(9, e)["S_index"]
+    got = {(int(i), int(j)) for i, j in S.T}
+    grid = {(int(i), int(j)) for i, j in e.T}
+    assert got == grid | fill and len(got) == 17
+
+
+def check_dense(edge_index, n, b, B=2, seed=0, order=None, tol=1e-12):
+    d, v = spdgen.graph(edge_index, n, b, B=B, seed=seed)
+    Gd, S, Gl, ld, info = oracle.junction(d, edge_index, v, order=order)
+    assert (info == 0).all()
+    for m in range(B):
+        A = spdgen.to_dense_graph(edge_index, d[m], v[m])
+        Ai = np.linalg.inv(A)
+        sc = np.abs(Ai).max()
+        for x in range(n):
+            assert np.abs(Gd[m, x] - blk(Ai, x, x, b)).max() <= tol * sc
+        for k in range(S.shape[1]):
+            assert np.abs(Gl[m, k] - blk(Ai, S[0, k], S[1, k], b)).max() <= tol * sc
+        assert abs(ld[m] - np.linalg.slogdet(A)[1]) <= 1e-10 * max(1.0, abs(ld[m]))
+    return S
+
+
+@pytest.mark.parametrize("r,c,b", [(1, 1, 2), (1, 6, 3), (3, 3, 2), (4, 5, 1), (5, 4, 3),
+                                   (6, 6, 2)])
+def test_grid_dense(r, c, b):
+    S = check_dense(spdgen.grid_edges(r, c), r * c, b)
+    assert np.all(S[0] > S[1])
+
+
+@pytest.mark.parametrize("n,extra,b", [(12, 10, 2), (25, 30, 1), (30, 15, 3), (8, 28, 2)])
+def test_random_graph_dense(n, extra, b):
+    check_dense(spdgen.random_graph_edges(n, extra, seed=n), n, b, seed=n)
+
+
+def test_complete_graph_fills_nothing_new():
+    n = 7
+    e = np.array([(i, j) for i in range(n) for j in range(i)], np.int32).T.copy()
+    S = check_dense(e, n, 2)
+    assert S.shape[1] == n * (n - 1) // 2
+
+
+@pytest.mark.parametrize("kind", ["natural", "reversed", "random"])
+def test_explicit_orders(kind):
+    n = 16
+    e = spdgen.grid_edges(4, 4)
+    order = {"natural": np.arange(n), "reversed": np.arange(n)[::-1],
+             "random": np.random.default_rng(1).permutation(n)}[kind]
+    check_dense(e, n, 2, order=order)
+    o, _, _ = oracle.eliminate(n, e, order)
+    assert list(o) == list(order)
+
+
+@pytest.mark.parametrize("order_kind", ["mindeg", "random"])
+def test_pattern_is_the_cholesky_structure(order_kind):
+    """b = 1, random values: the structural nonzeros of chol(P A P^T) are S."""
+    n = 30
+    e = spdgen.random_graph_edges(n, 25, seed=4)
+    order = None if order_kind == "mindeg" else np.random.default_rng(2).permutation(n)
+    P = oracle.filled_pattern(n, e, order)
+    d, v = spdgen.graph(e, n, 1, B=1, seed=3)
+    A = spdgen.to_dense_graph(e, d[0], v[0])
+    o = P["order"]
+    Lc = np.linalg.cholesky(A[np.ix_(o, o)])
+    nz = {(max(int(o[r]), int(o[c])), min(int(o[r]), int(o[c])))
+          for r in range(n) for c in range(r) if abs(Lc[r, c]) > 1e-13}
+    assert nz == {(int(i), int(j)) for i, j in P["S_index"].T}
+
+
+def test_min_degree_is_greedy():
+    """Every step eliminates a node of minimum remaining degree, the smallest
+    label among those (checked on the recorded cliques)."""
+    n = 40
+    e = spdgen.random_graph_edges(n, 40, seed=6)
+    o, ptr, nbr = oracle.eliminate(n, e)
+    adj = {v: set() for v in range(n)}
+    for i, j in e.T:
+        adj[int(i)].add(int(j))
+        adj[int(j)].add(int(i))
+    for s, v in enumerate(o):
+        v = int(v)
+        best = min(adj, key=lambda u: (len(adj[u]), u))
+        assert v == best
+        assert sorted(adj[v]) == list(nbr[ptr[s]:ptr[s + 1]])
+        for a in adj[v]:
+            adj[a] |= adj[v] - {a}
+            adj[a].discard(v)
+        del adj[v]
+
+
+@pytest.mark.parametrize("kind", ["random", "star", "balanced"])
+def test_tree_has_no_fill_and_is_the_tree_oracle(kind):
+    n, b = 40, 3
+    parent = {"random": spdgen.random_recursive_tree(n, 2), "star": spdgen.star_tree(n),
+              "balanced": spdgen.balanced_tree(n, 2)}[kind]
+    d, ed = spdgen.tree(parent, b, seed=5)
+    e = np.array([(max(v, int(parent[v])), min(v, int(parent[v])))
+                  for v in range(n) if parent[v] >= 0], np.int32).T.copy()
+    # edge_val[k] = A_{i,j} with i > j; the tree's edge[v] = A_{parent(v),v}
+    ev = np.stack([ed[v] if parent[v] > v else ed[v].T
+                   for v in range(n) if parent[v] >= 0])
+    for k, v in enumerate(v for v in range(n) if parent[v] >= 0):
+        assert (e[0, k], e[1, k]) == (max(v, parent[v]), min(v, parent[v]))
+    Gd, S, Gl, ld, info = oracle.junction(d, e, ev)
+    assert S.shape[1] == n - 1                                  # no fill
+    Td, Te, Tld, Tinfo = oracle.tree(parent, d, ed)
+    assert info == 0 and abs(ld - Tld) <= 1e-11 * abs(Tld)
+    assert np.abs(Gd - Td).max() <= 1e-12 * np.abs(Td).max()
+    look = {(int(i), int(j)): k for k, (i, j) in enumerate(S.T)}
+    for v in range(n):
+        p = int(parent[v])
+        if p < 0:
+            continue
+        g = Gl[look[(max(v, p), min(v, p))]]
+        g = g if p > v else g.T                                 # -> G_{p,v}
+        assert np.abs(g - Te[v]).max() <= 1e-12 * np.abs(Te).max()
+
+
+def test_path_is_the_chain():
+    L, b = 9, 2
+    d, lo = spdgen.chain(1, L, b, seed=3)
+    e = np.array([(i + 1, i) for i in range(L - 1)], np.int32).T.copy()
+    Gd, S, Gl, ld, info = oracle.junction(d[0], e, lo[0])
+    Cd, Cl, Cld, Cinfo = oracle.chain(d, lo)
+    assert S.shape[1] == L - 1 and list(S[0]) == list(range(1, L))
+    assert np.abs(Gd - Cd[0]).max() <= 1e-12 * np.abs(Cd).max()
+    assert np.abs(Gl - Cl[0]).max() <= 1e-12 * np.abs(Cd).max()
+    assert abs(ld - Cld[0]) <= 1e-11 * abs(Cld[0])
+
+
+def test_not_positive_definite_reports_the_first_node():
+    e = spdgen.grid_edges(3, 4)
+    d, v = spdgen.graph(e, 12, 2, B=2, seed=1)
+    d[1, 6] = -np.eye(2)
+    Gd, S, Gl, ld, info = oracle.junction(d, e, v)
+    o, _, _ = oracle.eliminate(12, e)
+    assert info[0] == 0 and np.isfinite(ld[0])
+    assert info[1] == 7 and np.isnan(ld[1])
+    assert list(o).index(6) >= 0
+
+
+def test_bad_input_is_rejected():
+    with pytest.raises(oracle.OracleError):
+        oracle.eliminate(3, np.array([[0], [1]], np.int32))            # i < j
+    with pytest.raises(oracle.OracleError):
+        oracle.eliminate(3, np.array([[1, 1], [0, 0]], np.int32))      # repeated
+    with pytest.raises(oracle.OracleError):
+        oracle.eliminate(3, np.array([[1], [0]], np.int32), order=[0, 0, 1])
+
+
+MUTANTS = [
+    ("skips diagonal update", r"if \(pos\[w1\] < pos\[w2\]\) continue;",
+     "if (pos[w1] <= pos[w2]) continue;"),
+    ("missing transpose", r"Gwx = T2;", "Gwx = Go + twx * bb;"),
+    ("G_vv sign", r"add_to\(bb, Gd \+ v \* bb, T, -1\.0\);", "add_to(bb, Gd + v * bb, T, 1.0);"),
+    ("L from unupdated A", r"matmul\(b, Co \+ t \* bb, Di \+ v \* bb, Lo \+ t \* bb\);",
+     "matmul(b, Aoff + mat * nnz * bb + t * bb, Di + v * bb, Lo + t * bb);"),
+    ("ties to largest label", r"\(v < 0 \|\| deg\[u\] < deg\[v\]\)", "(v < 0 || deg[u] <= deg[v])"),
+    ("no fill", r"adj\[x \* n \+ y\] = adj\[y \* n \+ x\] = 1;", "(void)0;"),
+]
+
+
+@pytest.mark.parametrize("name,pat,rep", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutants_are_caught(name, pat, rep):
+    src = open(oracle.SOURCE).read()
+    mutated, cnt = re.subn(pat, rep, src)
+    assert cnt == 1, "mutation site not found: " + name
+    with tempfile.TemporaryDirectory() as td:
+        c, so = os.path.join(td, "m.c"), os.path.join(td, "m.so")
+        open(c, "w").write(mutated)
+        lib = oracle.load(oracle.compile_oracle(c, so))
+        order, _, _ = read_golden()
+        e = spdgen.grid_edges(3, 3)
+        bad = list(oracle.eliminate(9, e, lib=lib)[0]) != order
+        e = spdgen.grid_edges(4, 4)
+        d, v = spdgen.graph(e, 16, 2, B=1, seed=2)
+        try:
+            Gd, S, Gl, ld, info = oracle.junction(d[0], e, v[0], lib=lib)
+        except oracle.OracleError:
+            bad = True
+        else:
+            Ai = np.linalg.inv(spdgen.to_dense_graph(e, d[0], v[0]))
+            for x in range(16):
+                bad |= np.abs(Gd[x] - blk(Ai, x, x, 2)).max() > 1e-8
+            for k in range(S.shape[1]):
+                bad |= np.abs(Gl[k] - blk(Ai, S[0, k], S[1, k], 2)).max() > 1e-8
+        assert bad, name
