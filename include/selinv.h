@@ -66,6 +66,7 @@ extern "C" {
 #define SELINV_ERR_INVALID_ARG 1 /* null pointer, bad size, b unsupported, workspace too small */
 #define SELINV_ERR_BAD_TREE 2    /* parent array is not one rooted tree                        */
 #define SELINV_ERR_HIP 3         /* HIP runtime or launch error                                 */
+#define SELINV_ERR_BAD_PATTERN 4 /* junction pattern or elimination order is invalid            */
 
 #define SELINV_MAX_B 32
 
@@ -361,6 +362,70 @@ SELINV_API int selinv_nonsym_tree_f32(const selinv_tree_plan *plan, const float 
                            const float *up, const float *down, float *G_diag, float *G_up,
                            float *G_down, int32_t *info, void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/* ---------------------------------------------------- general sparse SPD
+ * Junction tree (gabp-sparse-inv page, junction-tree section): an arbitrary
+ * block sparsity pattern, eliminated in an elimination order (default:
+ * greedy minimum degree) and thereby completed to its chordal filled
+ * pattern S = pattern(L + L^T); the selected inverse is returned on S (a
+ * superset of the input pattern wherever elimination creates fill), from a
+ * sparse block Cholesky factorisation and the multi-neighbour Takahashi
+ * recurrence, run level by level over the elimination tree.  A batch of B
+ * matrices shares one pattern (one plan).
+ *
+ * selinv_junction_plan_create (all arguments HOST memory):
+ *   edge_index_host [2][m] int32: row 0 = i, row 1 = j, one entry per pattern
+ *       edge {i, j} with 0 <= j < i < n, no repeats (m may be 0 and the
+ *       pointer then NULL); else SELINV_ERR_BAD_PATTERN
+ *   order_host [n] int32 or NULL: the elimination order (order[s] = the node
+ *       eliminated at step s; a permutation, else SELINV_ERR_BAD_PATTERN).
+ *       NULL = greedy minimum degree: at every step the remaining node with
+ *       the fewest remaining neighbours, the smallest index among ties.
+ * It runs the symbolic analysis once per pattern (elimination, S, the
+ * elimination-tree level sets and every index table of the kernels) and
+ * copies the tables to the device on `stream` (the plan owns them; the call
+ * synchronises `stream`).  A plan is immutable and may be shared by
+ * concurrent calls; it is specific to (pattern, order, b, dtype_bytes).
+ *
+ * selinv_junction_plan_nnz: number of lower blocks of S (-1 for NULL);
+ * selinv_junction_plan_levels: number of elimination-tree levels;
+ * selinv_junction_plan_pattern copies to HOST memory S_index [2][nnz]
+ *   (pairs (i, j), i > j, sorted by i then j; may be NULL) and the
+ *   elimination order [n] (may be NULL).
+ *
+ * selinv_junction_f64 / _f32, for B matrices on the plan's pattern:
+ *   diag     [B][n][b][b]    A_{v,v}
+ *   edge_val [B][m][b][b]    edge_val[e] = A_{i_e, j_e}
+ *   G_diag   [B][n][b][b]    (A^-1)_{v,v}
+ *   G_lower  [B][nnz][b][b]  G_lower[k] = (A^-1)_{i_k, j_k} for S_index pair k
+ *   logdet [B], info [B]     info: 1 + the node index whose Schur pivot is
+ *                            not positive definite, the earliest such node
+ *                            in the elimination order
+ * Workspace: selinv_junction_workspace_bytes(plan, B). */
+typedef struct selinv_junction_plan selinv_junction_plan;
+
+SELINV_API int selinv_junction_plan_create(int64_t n, int64_t m, const int32_t *edge_index_host,
+                                const int32_t *order_host, int32_t b, int dtype_bytes,
+                                void *stream, selinv_junction_plan **out);
+SELINV_API void selinv_junction_plan_destroy(selinv_junction_plan *plan);
+SELINV_API int64_t selinv_junction_plan_nnz(const selinv_junction_plan *plan);
+SELINV_API int32_t selinv_junction_plan_levels(const selinv_junction_plan *plan);
+SELINV_API int selinv_junction_plan_pattern(const selinv_junction_plan *plan, int32_t *S_index_host,
+                                 int32_t *order_host);
+/* The symbolic analysis alone, on the host (no device work): nnz and the
+ * number of levels, S_index [2][nnz] when `cap` >= nnz (else not written),
+ * and the elimination order [n]; each output may be NULL.  Same validation
+ * and statuses as selinv_junction_plan_create. */
+SELINV_API int selinv_junction_symbolic(int64_t n, int64_t m, const int32_t *edge_index_host,
+                             const int32_t *order_host, int64_t *nnz_out, int32_t *levels_out,
+                             int32_t *S_index_host, int64_t cap, int32_t *order_out);
+SELINV_API size_t selinv_junction_workspace_bytes(const selinv_junction_plan *plan, int64_t B);
+SELINV_API int selinv_junction_f64(const selinv_junction_plan *plan, int64_t B, const double *diag,
+                        const double *edge_val, double *G_diag, double *G_lower, double *logdet,
+                        int32_t *info, void *workspace, size_t workspace_bytes, void *stream);
+SELINV_API int selinv_junction_f32(const selinv_junction_plan *plan, int64_t B, const float *diag,
+                        const float *edge_val, float *G_diag, float *G_lower, double *logdet,
+                        int32_t *info, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -138,6 +138,25 @@ def lib():
         f = getattr(L, "selinv_nonsym_tree_" + sfx)
         f.argtypes = [vp] * 8 + [vp, sz, vp]
         f.restype = ctypes.c_int
+    L.selinv_junction_plan_create.argtypes = [i64, i64, vp, vp, i32, ctypes.c_int, vp,
+                                              ctypes.POINTER(vp)]
+    L.selinv_junction_plan_create.restype = ctypes.c_int
+    L.selinv_junction_plan_destroy.argtypes = [vp]
+    L.selinv_junction_plan_destroy.restype = None
+    L.selinv_junction_plan_nnz.argtypes = [vp]
+    L.selinv_junction_plan_nnz.restype = i64
+    L.selinv_junction_plan_levels.argtypes = [vp]
+    L.selinv_junction_plan_levels.restype = i32
+    L.selinv_junction_plan_pattern.argtypes = [vp, vp, vp]
+    L.selinv_junction_plan_pattern.restype = ctypes.c_int
+    L.selinv_junction_symbolic.argtypes = [i64, i64, vp, vp, vp, vp, vp, i64, vp]
+    L.selinv_junction_symbolic.restype = ctypes.c_int
+    L.selinv_junction_workspace_bytes.argtypes = [vp, i64]
+    L.selinv_junction_workspace_bytes.restype = sz
+    for sfx in ("f64", "f32"):
+        f = getattr(L, "selinv_junction_" + sfx)
+        f.argtypes = [vp, i64] + [vp] * 6 + [vp, sz, vp]
+        f.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -850,3 +869,173 @@ def nonsym_tree(parent, diag, up, down, check=False, return_info=False,
     if check:
         _raise_info(info.reshape(1), "nonsym_tree")
     return (G_diag, G_up, G_down, info) if return_info else (G_diag, G_up, G_down)
+
+
+# ------------------------------------------------------ general sparse SPD
+def _edge_index_host(edge_index, n):
+    import numpy as np
+    if isinstance(edge_index, torch.Tensor):
+        edge_index = edge_index.detach().cpu().numpy()
+    e = np.ascontiguousarray(np.asarray(edge_index, dtype=np.int32))
+    if e.ndim != 2 or e.shape[0] != 2:
+        raise ValueError("edge_index must be [2, m]")
+    return e
+
+
+def _order_host(order, n):
+    import numpy as np
+    if order is None:
+        return None
+    if isinstance(order, torch.Tensor):
+        order = order.detach().cpu().numpy()
+    o = np.ascontiguousarray(np.asarray(order, dtype=np.int32))
+    if o.shape != (n,):
+        raise ValueError("order must have n entries")
+    return o
+
+
+def junction_symbolic(n: int, edge_index, order=None):
+    """Host-only symbolic analysis: (order [n], S_index [2, nnz], levels) as
+    numpy int32 arrays, the pattern selected_inverse_junction returns."""
+    import numpy as np
+    e = _edge_index_host(edge_index, n)
+    o = _order_host(order, n)
+    nnz, lev = ctypes.c_int64(), ctypes.c_int32()
+    rc = lib().selinv_junction_symbolic(n, e.shape[1], e.ctypes.data if e.size else None,
+                                        o.ctypes.data if o is not None else None,
+                                        ctypes.byref(nnz), ctypes.byref(lev), None, 0, None)
+    _status(rc, "selinv_junction_symbolic")
+    S = np.zeros((2, nnz.value), np.int32)
+    out = np.zeros(n, np.int32)
+    rc = lib().selinv_junction_symbolic(n, e.shape[1], e.ctypes.data if e.size else None,
+                                        o.ctypes.data if o is not None else None, None, None,
+                                        S.ctypes.data if S.size else None, nnz.value,
+                                        out.ctypes.data)
+    _status(rc, "selinv_junction_symbolic")
+    return out, S, int(lev.value)
+
+
+class JunctionPlan:
+    """Symbolic analysis of one block pattern (and elimination order) with
+    its device tables; owns device memory through the C library."""
+
+    def __init__(self, n: int, edge_index, b: int, dtype: torch.dtype, device, order=None):
+        import numpy as np
+        e = _edge_index_host(edge_index, n)
+        o = _order_host(order, n)
+        self.n, self.m, self.b = int(n), int(e.shape[1]), int(b)
+        self.dtype = dtype
+        self.device = torch.device(device)
+        h = ctypes.c_void_p()
+        esz = 8 if dtype == torch.float64 else 4
+        with torch.cuda.device(self.device):
+            rc = lib().selinv_junction_plan_create(
+                self.n, self.m, e.ctypes.data if e.size else None,
+                o.ctypes.data if o is not None else None, self.b, esz, _stream(self.device),
+                ctypes.byref(h))
+        _status(rc, "selinv_junction_plan_create")
+        self._h = h
+        self.nnz = int(lib().selinv_junction_plan_nnz(h))
+        self.levels = int(lib().selinv_junction_plan_levels(h))
+        S = np.zeros((2, self.nnz), np.int32)
+        od = np.zeros(self.n, np.int32)
+        _status(lib().selinv_junction_plan_pattern(h, S.ctypes.data if S.size else None,
+                                                   od.ctypes.data),
+                "selinv_junction_plan_pattern")
+        self.S_index = torch.from_numpy(S)
+        self.order = torch.from_numpy(od)
+
+    def workspace_bytes(self, B: int) -> int:
+        return int(lib().selinv_junction_workspace_bytes(self._h, B))
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.selinv_junction_plan_destroy(h)
+            self._h = None
+
+
+_JPLAN_CACHE: "OrderedDict[tuple, JunctionPlan]" = OrderedDict()
+
+
+def junction_plan(n: int, edge_index, b: int, dtype: torch.dtype, device,
+                  order=None) -> JunctionPlan:
+    """Cached plan keyed by the pattern's content, the order and (n, b,
+    dtype, device): repeated calls on one pattern pay only for the numeric
+    work (the symbolic analysis is done once per pattern)."""
+    e = _edge_index_host(edge_index, n)
+    o = _order_host(order, n)
+    key = (hashlib.sha1(e.tobytes()).hexdigest(), e.shape[1],
+           None if o is None else hashlib.sha1(o.tobytes()).hexdigest(), int(n), int(b), dtype,
+           str(device))
+    plan = _JPLAN_CACHE.get(key)
+    if plan is None:
+        plan = JunctionPlan(n, e, b, dtype, device, o)
+        _JPLAN_CACHE[key] = plan
+        while len(_JPLAN_CACHE) > _PLAN_CACHE_MAX:
+            _JPLAN_CACHE.popitem(last=False)
+    else:
+        _JPLAN_CACHE.move_to_end(key)
+    return plan
+
+
+def junction(diag: torch.Tensor, edge_index, edge_val: torch.Tensor, order=None,
+             check: bool = False, return_info=False, plan: JunctionPlan | None = None):
+    """Selected inverse of general sparse SPD matrices sharing one pattern.
+
+    diag [B, n, b, b] (or [n, b, b]); edge_index [2, m] (host array or
+    tensor) with pairs (i, j), i > j; edge_val [B, m, b, b] with
+    edge_val[e] = A_{i_e, j_e}; order: optional elimination order (default
+    greedy minimum degree).  Returns (G_diag, S_index, G_lower, logdet): the
+    selected inverse on the filled pattern S, S_index an int32 CPU tensor
+    [2, nnz] (pairs i > j, sorted), G_lower[k] = (A^-1)_{S_index[:, k]}.
+    """
+    dt, dev = diag.dtype, diag.device
+    diag = _check_tensor(diag, "diag", dev, dt)
+    single = diag.dim() == 3
+    if single:
+        diag = diag.unsqueeze(0)
+        edge_val = edge_val.unsqueeze(0)
+    edge_val = _check_tensor(edge_val, "edge_val", dev, dt)
+    sfx = _sfx(diag)
+    if diag.dim() != 4 or diag.shape[2] != diag.shape[3]:
+        raise ValueError("diag must be [B, n, b, b]")
+    B, n, b = diag.shape[0], diag.shape[1], diag.shape[2]
+    if plan is None:
+        plan = junction_plan(n, edge_index, b, dt, dev, order)
+    if plan.n != n or plan.b != b or plan.dtype != dt:
+        raise ValueError("plan does not match (n, b, dtype)")
+    if edge_val.shape != (B, plan.m, b, b):
+        raise ValueError("edge_val must be [B, m, b, b]")
+    if check:
+        _validate_values("diag", diag)
+        _validate_symmetric("diag", diag)
+    G_diag = torch.empty_like(diag)
+    G_lower = torch.empty((B, plan.nnz, b, b), dtype=dt, device=dev)
+    logdet = torch.empty(B, dtype=torch.float64, device=dev)
+    info = torch.empty(B, dtype=torch.int32, device=dev)
+    nbytes = plan.workspace_bytes(B)
+    ws = _workspace(nbytes, dev)
+    with torch.cuda.device(dev):
+        rc = getattr(lib(), "selinv_junction_" + sfx)(
+            plan.handle, B, _ptr(diag), _ptr(edge_val) if plan.m else None, _ptr(G_diag),
+            _ptr(G_lower) if plan.nnz else None, logdet.data_ptr(), info.data_ptr(), _ptr(ws),
+            nbytes, _stream(dev))
+    _status(rc, "selinv_junction_" + sfx)
+    if check:
+        _raise_info(info, "junction")
+    if single:
+        G_diag, G_lower, logdet, info = G_diag[0], G_lower[0], logdet[0], info[0]
+    if return_info:
+        return G_diag, plan.S_index, G_lower, logdet, info
+    return G_diag, plan.S_index, G_lower, logdet
+
+
+def junction_logdet(diag, edge_index, edge_val, order=None, return_info=False):
+    """log det A of general sparse SPD matrices from the same factorisation."""
+    r = junction(diag, edge_index, edge_val, order=order, return_info=True)
+    return (r[3], r[4]) if return_info else r[3]

@@ -251,9 +251,46 @@ int nonsym_tree_entry(const selinv_tree_plan *plan, const T *diag, const T *up, 
   return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
 }
 
+template <typename T>
+int junction_entry(const selinv_junction_plan *plan, int64_t B, const T *diag, const T *edge_val,
+                   T *G_diag, T *G_lower, double *logdet, int32_t *info, void *ws,
+                   size_t ws_bytes, void *stream) {
+  if (!plan || plan->dtype_bytes != static_cast<int>(sizeof(T))) return SELINV_ERR_INVALID_ARG;
+  if (B < 0 || B > 65535) return SELINV_ERR_INVALID_ARG;
+  if (B == 0) return SELINV_OK;
+  if (!diag || !G_diag || !logdet || (plan->m > 0 && !edge_val) || (plan->nnz > 0 && !G_lower))
+    return SELINV_ERR_INVALID_ARG;
+  if (misaligned(diag) || misaligned(edge_val) || misaligned(G_diag) || misaligned(G_lower))
+    return SELINV_ERR_INVALID_ARG;
+  const size_t need = selinv::junction_workspace_bytes(plan, B);
+  if (ws_bytes < need || !ws || misaligned_ws(ws)) return SELINV_ERR_INVALID_ARG;
+  const hipError_t e = selinv::junction_launch<T>(plan, B, diag, edge_val, G_diag, G_lower, logdet,
+                                                  info, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t selinv_junction_workspace_bytes(const selinv_junction_plan *plan, int64_t B) {
+  if (!plan || B < 0) return 0;
+  return selinv::junction_workspace_bytes(plan, B);
+}
+
+int selinv_junction_f64(const selinv_junction_plan *plan, int64_t B, const double *diag,
+                        const double *edge_val, double *G_diag, double *G_lower, double *logdet,
+                        int32_t *info, void *workspace, size_t workspace_bytes, void *stream) {
+  return junction_entry<double>(plan, B, diag, edge_val, G_diag, G_lower, logdet, info, workspace,
+                                workspace_bytes, stream);
+}
+
+int selinv_junction_f32(const selinv_junction_plan *plan, int64_t B, const float *diag,
+                        const float *edge_val, float *G_diag, float *G_lower, double *logdet,
+                        int32_t *info, void *workspace, size_t workspace_bytes, void *stream) {
+  return junction_entry<float>(plan, B, diag, edge_val, G_diag, G_lower, logdet, info, workspace,
+                               workspace_bytes, stream);
+}
 
 const char *selinv_strerror(int status) {
   switch (status) {
@@ -261,6 +298,7 @@ const char *selinv_strerror(int status) {
     case SELINV_ERR_INVALID_ARG: return "invalid argument (pointer, size, block size or workspace)";
     case SELINV_ERR_BAD_TREE: return "parent array is not a single rooted tree";
     case SELINV_ERR_HIP: return "HIP runtime or kernel launch error";
+    case SELINV_ERR_BAD_PATTERN: return "invalid junction pattern or elimination order";
     default: return "unknown status";
   }
 }

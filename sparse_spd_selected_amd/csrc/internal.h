@@ -6,6 +6,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <vector>
 
 #include "selinv.h"
 
@@ -46,7 +47,48 @@ struct TreePlanDev {
   int32_t *parent_node = nullptr;  // node index of the parent of position p (-1 at the root)
 };
 
+// Device tables of a junction plan (junction_plan.cpp builds them).  Node
+// ids run level by level; slot t is the block (w, v) of the filled pattern
+// with v = slot_node[t] and w a later node, column v's slots contiguous.
+//   colptr[p]      first slot of node p (n + 1 entries)
+//   node_label[p]  caller's label of node p;  node_pos[p] its elimination position
+//   order[s]       label eliminated at step s
+//   targets: node p owns colptr[p] + p .. colptr[p+1] + p (its diagonal, then
+//   one per slot); tgt_node, ain (input block: the label for a diagonal,
+//   else edge * 2 + transposed, or -1 for fill), fptr/fpair (the Schur
+//   update pairs (W_{t,u} slot, W_{v,u} slot) of every target)
+//   slot_node[t], outenc[t] (output position * 2 + stored transposed)
+//   gptr[p], gtab: k x k reads of G_{w,x} for node p (-(label + 1) for a
+//   diagonal block, else output position * 2 + transpose)
+struct JunctionPlanDev {
+  int32_t *colptr = nullptr;
+  int32_t *node_label = nullptr;
+  int32_t *node_pos = nullptr;
+  int32_t *order = nullptr;
+  int32_t *tgt_node = nullptr;
+  int32_t *ain = nullptr;
+  int32_t *fptr = nullptr;
+  int32_t *fpair = nullptr;
+  int32_t *slot_node = nullptr;
+  int32_t *outenc = nullptr;
+  int64_t *gptr = nullptr;
+  int32_t *gtab = nullptr;
+};
+
 }  // namespace selinv
+
+struct selinv_junction_plan {
+  int64_t n = 0, m = 0, nnz = 0, npairs = 0, max_k = 0;
+  int32_t b = 0;
+  int dtype_bytes = 0;
+  int32_t levels = 0;
+  std::vector<int64_t> level_off;    // node-id range of every level (levels + 1)
+  std::vector<int64_t> colptr_host;  // n + 1
+  std::vector<int32_t> S_index;      // [2][nnz], host copy for the caller
+  std::vector<int32_t> order;        // elimination order (labels)
+  selinv::JunctionPlanDev dev;
+  void *dev_block = nullptr;
+};
 
 struct selinv_tree_plan {
   int64_t n = 0;
@@ -204,6 +246,13 @@ size_t tree_apply_workspace_bytes(const selinv_tree_plan *plan, int64_t k);
 template <typename T>
 hipError_t tree_apply_launch(const selinv_tree_plan *plan, int64_t k, bool sample, const T *edge,
                              const T *factor, const T *in, T *out, void *ws, hipStream_t s);
+
+// --------------------------------- general sparse SPD (junction.hip)
+size_t junction_workspace_bytes(const selinv_junction_plan *plan, int64_t B);
+template <typename T>
+hipError_t junction_launch(const selinv_junction_plan *plan, int64_t B, const T *diag,
+                           const T *edge_val, T *G_diag, T *G_lower, double *logdet,
+                           int32_t *info, void *ws, hipStream_t s);
 
 // ------------------------------------ non-symmetric ladder (nonsym.hip)
 size_t bidiag_workspace_bytes(int64_t B);
