@@ -68,6 +68,29 @@ def measured_traffic(workload, dtname):
     return rec.get("bytes_per_call")
 
 
+_JCOUNTS = {}
+
+
+def junction_counts(cfg):
+    """(n, m, nnz, sum_v k_v, sum_v k_v^2) of a junction workload's filled
+    pattern, k_v = the number of later neighbours of v, from the library's
+    host-side symbolic analysis."""
+    key = (cfg["rows"], cfg["cols"])
+    if key not in _JCOUNTS:
+        import numpy as np
+        import spdgen
+        import sparse_spd_selected_amd as ssa
+        n = cfg["rows"] * cfg["cols"]
+        e = spdgen.grid_edges(cfg["rows"], cfg["cols"])
+        order, S, _ = ssa.junction_symbolic(n, e)
+        pos = np.empty(n, np.int64)
+        pos[order] = np.arange(n)
+        first = np.where(pos[S[0]] < pos[S[1]], S[0], S[1])      # the earlier node of each pair
+        k = np.bincount(first, minlength=n).astype(np.int64)
+        _JCOUNTS[key] = (n, e.shape[1], S.shape[1], int(k.sum()), int((k * k).sum()))
+    return _JCOUNTS[key]
+
+
 def nominal_flops(kind, cfg, op="selinv"):
     """Per non-root block: forward 7 b^3 (inverse b^3, X 2 b^3, symmetric M
     b^3, V 2 b^3, symmetric G b^3); reverse mode 22 b^3 (collect: inverse b^3,
@@ -84,6 +107,13 @@ def nominal_flops(kind, cfg, op="selinv"):
         return cfg["B"] * (2 * b ** 3 * cfg["L"] + 4 * b ** 3 * (cfg["L"] - 1))
     if kind == "nonsym_tree":  # collect 6 b^3, distribute 10 b^3 per non-root; root 2 b^3
         return 16 * b ** 3 * (cfg["n"] - 1) + 2 * b ** 3
+    if kind == "junction":
+        # per node with k later neighbours: factor k^2 b^3 (k(k-1)/2 Schur
+        # products of 2 b^3 and k symmetric ones of b^3) + k b^3 (triangular
+        # scaling) + b^3 / 3 (Cholesky); Takahashi 2 k^2 b^3 (G_NN W) + k b^3
+        # (times R^-1) + k b^3 (symmetric W^T G) + b^3 (R^-T X) + b^3 / 3 (R^-1)
+        n, m, nnz, sk, sk2 = junction_counts(cfg)
+        return cfg["B"] * b ** 3 * (3 * sk2 + 3 * sk + n * 5 // 3)
     per, root = {"selinv": (7, 1), "vjp": (22, 4), "logdet": (4, 1)}[op]
     if kind == "chain":
         return cfg["B"] * (per * b ** 3 * (cfg["L"] - 1) + root * b ** 3)
@@ -102,6 +132,9 @@ def compulsory_bytes(kind, cfg, w, op="selinv"):
         return cfg["B"] * (2 * (2 * cfg["L"] - 1) * b2 * w + 4)
     if kind == "nonsym_tree":  # diag, up, down in (root edges skipped); three outputs
         return (3 * cfg["n"] - 2 + 3 * cfg["n"]) * b2 * w + 4 * cfg["n"] + 4
+    if kind == "junction":  # diag, edge_val in; G_diag, G_lower (on S) out; logdet, info
+        n, m, nnz, sk, sk2 = junction_counts(cfg)
+        return cfg["B"] * ((2 * n + m + nnz) * b2 * w + 8 + 4)
     if op == "logdet":  # inputs read once, log det and info written
         if kind == "chain":
             return cfg["B"] * ((2 * cfg["L"] - 1) * b2 * w + 12)
@@ -130,6 +163,8 @@ def compulsory_bytes(kind, cfg, w, op="selinv"):
 def block_rows(kind, cfg):
     if kind in ("chain", "bidiag"):
         return cfg["B"] * cfg["L"]
+    if kind == "junction":
+        return cfg["B"] * cfg["rows"] * cfg["cols"]
     if kind == "star":
         return cfg["B"] * (cfg["K"] + 1)
     return cfg["n"]
@@ -151,6 +186,11 @@ def make_inputs(kind, cfg, dt, dev):
         d, l = spdgen.nonsym_bidiag(cfg["B"], cfg["L"], cfg["b"], seed=cfg["seed"],
                                     diag_load=cfg["diag_load"])
         return [torch.from_numpy(x).to(dev).to(dt) for x in (d, l)], None
+    if kind == "junction":
+        e = spdgen.grid_edges(cfg["rows"], cfg["cols"])
+        d, v = spdgen.graph(e, cfg["rows"] * cfg["cols"], cfg["b"], B=cfg["B"], seed=cfg["seed"],
+                            diag_load=cfg["diag_load"])
+        return [torch.from_numpy(x).to(dev).to(dt) for x in (d, v)], e
     parent = spdgen.random_recursive_tree(cfg["n"], cfg["seed"])
     if kind == "nonsym_tree":
         arrs = spdgen.nonsym_tree(parent, cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
@@ -228,6 +268,10 @@ def run_gpu(kind, cfg, dtname, steps, warmup, op="selinv"):
     elif kind == "nonsym_tree":
         plan = ssa.tree_plan(parent, cfg["b"], dt, dev)
         call = lambda: ssa.nonsym_tree(parent, *inputs, plan=plan)
+    elif kind == "junction":  # the symbolic plan is built once per pattern, untimed
+        e = parent
+        plan = ssa.junction_plan(cfg["rows"] * cfg["cols"], e, cfg["b"], dt, dev)
+        call = lambda: ssa.junction(inputs[0], e, inputs[1], plan=plan)
     else:
         plan = ssa.tree_plan(parent, cfg["b"], dt, dev)
         call = lambda: ssa.tree(parent, *inputs, plan=plan)
@@ -344,6 +388,22 @@ def cpu_baseline(kind, cfg, op="selinv"):
     import oracle
     import spdgen
     lib = oracle.load()
+    if kind == "junction":
+        Bs = min(cfg["B"], 8)
+        n = cfg["rows"] * cfg["cols"]
+        e = spdgen.grid_edges(cfg["rows"], cfg["cols"])
+        d, v = spdgen.graph(e, n, cfg["b"], B=Bs, seed=cfg["seed"], diag_load=cfg["diag_load"])
+        P = oracle.filled_pattern(n, e, lib=lib)
+        t0 = time.perf_counter()
+        oracle.junction(d, e, v, lib=lib, pattern=P)
+        t = time.perf_counter() - t0
+        sub = dict(cfg, B=Bs)
+        cores = min(Bs, int(lib.oracle_num_threads()))
+        return {"value": round(nominal_flops(kind, sub, op) / t / 1e9, 3), "unit": "GFLOP/s",
+                "cores": cores, "kind": "oracle", "seconds": round(t, 3),
+                "sample": "%d of %d matrices on the %d x %d grid (b=%d), float64, symbolic "
+                          "analysis untimed" % (Bs, cfg["B"], cfg["rows"], cfg["cols"], cfg["b"]),
+                "block_rows_per_s": round(block_rows(kind, sub) / t, 1)}
     if kind in ("bidiag", "nonsym_tree"):
         if kind == "bidiag":
             Bs = min(cfg["B"], 1024)
@@ -483,6 +543,15 @@ def main():
                      "traffic": measured_traffic(tkey, dtname),
                      "algorithmic_bytes": nbytes, "kernel_source_hash": kernel_source_hash()},
     }
+    if kind == "junction":
+        # about 100 nominal flops per compulsory byte: bound by vector ALU
+        # arithmetic (the level kernels run on the vector units)
+        tf = F / (ms_mean * 1e-3) / 1e12
+        out["roofline"] = {"bound": "alu", "achieved": round(tf, 4), "peak": peak_t,
+                           "unit": "TFLOP/s", "frac": round(tf / peak_t, 4),
+                           "traffic": measured_traffic(tkey, dtname),
+                           "algorithmic_flops": F, "algorithmic_bytes": nbytes,
+                           "kernel_source_hash": kernel_source_hash()}
     if not args.no_second_dtype and len(dtypes) > 1 and args.dtype is None:
         other = dtypes[1]
         r2 = run_gpu(kind, cfg, other, args.steps, args.warmup, op)

@@ -47,45 +47,47 @@ struct TreePlanDev {
   int32_t *parent_node = nullptr;  // node index of the parent of position p (-1 at the root)
 };
 
-// Device tables of a junction plan (junction_plan.cpp builds them).  Node
-// ids run level by level; slot t is the block (w, v) of the filled pattern
-// with v = slot_node[t] and w a later node, column v's slots contiguous.
-//   colptr[p]      first slot of node p (n + 1 entries)
-//   node_label[p]  caller's label of node p;  node_pos[p] its elimination position
-//   order[s]       label eliminated at step s
-//   targets: node p owns colptr[p] + p .. colptr[p+1] + p (its diagonal, then
-//   one per slot); tgt_node, ain (input block: the label for a diagonal,
-//   else edge * 2 + transposed, or -1 for fill), fptr/fpair (the Schur
-//   update pairs (W_{t,u} slot, W_{v,u} slot) of every target)
-//   slot_node[t], outenc[t] (output position * 2 + stored transposed)
-//   gptr[p], gtab: k x k reads of G_{w,x} for node p (-(label + 1) for a
-//   diagonal block, else output position * 2 + transpose)
+// Device tables of a junction plan (junction_plan.cpp builds them).  Chunks
+// (pieces of supernodes, treated as fat nodes) are numbered level by level.
+//   order[s]          label eliminated at step s
+//   ch_first/s/n[J]   first position, columns and later rows of chunk J
+//   ch_pbase[J]       first block of J's panel ((s + n) x s blocks)
+//   ch_rbase[J]       first block of J's pivot inverse (s x s blocks, dense)
+//   ch_gptr[J]        first entry of J's n x n G_{w,x} read codes in gtab
+//   rows_ptr[J]       first flat row of J; row_chunk[row] its chunk
+//   ch_cptr[J]        first flat column of J; col_chunk[column] its chunk
+//   tiles_ptr[J]      first row tile of J (tiles of 64 / b rows); tile_chunk[tile]
+//   tg_chunk/tg_rc/ain  per forward target: chunk, r * 64 + col, input block
+//                     (label for a diagonal, edge * 2 + transposed, -1 fill)
+//   fptr/fpair        Schur update pairs (panel block of W_{t,u}, of W_{v,u})
+//   gtab              -(label + 1) for a diagonal G block, else output
+//                     position * 2 + transpose
+//   poutenc           output code of every panel block (as gtab, -1 unused)
 struct JunctionPlanDev {
-  int32_t *colptr = nullptr;
-  int32_t *node_label = nullptr;
-  int32_t *node_pos = nullptr;
   int32_t *order = nullptr;
-  int32_t *tgt_node = nullptr;
-  int32_t *ain = nullptr;
-  int32_t *fptr = nullptr;
-  int32_t *fpair = nullptr;
-  int32_t *slot_node = nullptr;
-  int32_t *outenc = nullptr;
-  int64_t *gptr = nullptr;
-  int32_t *gtab = nullptr;
+  int32_t *ch_first = nullptr, *ch_s = nullptr, *ch_n = nullptr;
+  int64_t *ch_pbase = nullptr, *ch_rbase = nullptr, *ch_gptr = nullptr, *rows_ptr = nullptr;
+  int64_t *ch_cptr = nullptr, *tiles_ptr = nullptr;
+  int32_t *row_chunk = nullptr, *col_chunk = nullptr, *tile_chunk = nullptr;
+  int32_t *tg_chunk = nullptr, *tg_rc = nullptr, *ain = nullptr;
+  int32_t *fptr = nullptr, *fpair = nullptr;
+  int32_t *gtab = nullptr, *poutenc = nullptr;
 };
 
 }  // namespace selinv
 
 struct selinv_junction_plan {
-  int64_t n = 0, m = 0, nnz = 0, npairs = 0, max_k = 0;
-  int32_t b = 0;
+  int64_t n = 0, m = 0, nnz = 0, nch = 0, npanel = 0, nrinv = 0;
+  int32_t b = 0, smax = 0;
   int dtype_bytes = 0;
-  int32_t levels = 0;
-  std::vector<int64_t> level_off;    // node-id range of every level (levels + 1)
-  std::vector<int64_t> colptr_host;  // n + 1
-  std::vector<int32_t> S_index;      // [2][nnz], host copy for the caller
-  std::vector<int32_t> order;        // elimination order (labels)
+  int32_t levels = 0, node_levels = 0;
+  std::vector<int64_t> level_off;  // chunk-id range of every level (levels + 1)
+  std::vector<int64_t> ch_tptr;    // first forward target of every chunk (nch + 1)
+  std::vector<int64_t> rows_ptr;   // first flat row of every chunk (nch + 1)
+  std::vector<int64_t> ch_cptr;    // first flat column of every chunk (nch + 1)
+  std::vector<int64_t> tiles_ptr;  // first row tile of every chunk (nch + 1)
+  std::vector<int32_t> S_index;    // [2][nnz], host copy for the caller
+  std::vector<int32_t> order;      // elimination order (labels)
   selinv::JunctionPlanDev dev;
   void *dev_block = nullptr;
 };

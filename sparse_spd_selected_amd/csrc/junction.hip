@@ -1,32 +1,34 @@
 // junction.hip -- selected inverse of general sparse SPD matrices on their
 // filled (chordal) pattern, batched over matrices that share the pattern
 // (gabp-sparse-inv page, junction-tree section: sparse block Cholesky, then
-// the multi-neighbour Takahashi recurrence, level by level over the
-// elimination tree).
+// the multi-neighbour Takahashi recurrence, level by level).
 //
-// Cholesky form.  With A = L~ L~^T, L~_vv = R_v (lower) and the off-diagonal
-// factor blocks W_{w,v} = C_{w,v} R_v^-T for the later neighbours w of v:
-//   factor (levels upward, children first), for every target t of node v
-//   (t = v or t in N(v)):
-//       C_{t,v} = A_{t,v} - sum_u W_{t,u} W_{v,u}^T
-//   over the earlier nodes u whose clique holds both v and t; then
-//       R_v = chol(C_vv),  W_{t,v} = C_{t,v} R_v^-T,  log det += 2 sum ln R_kk
-//   Takahashi (levels downward, root first), N = N(v):
-//       G_{w,v} = -(sum_{x in N} G_{w,x} W_{x,v}) R_v^-1          (w in N)
-//       G_vv    = R_v^-T (R_v^-1 - sum_{w in N} W_{w,v}^T G_{w,v})
-// (the LDL^T recurrences of the page with L_{w,v} = W_{w,v} R_v^-1 and
-// D_v = R_v R_v^T).  Every block read lies in S because N(v) is a clique.
+// Fat nodes.  The plan groups the elimination into chunks J of consecutive
+// supernode columns (their pivot is one dense (s b) x (s b) block) and the
+// recurrences run on chunks.  In Cholesky form, with A = L~ L~^T, the
+// chunk's diagonal factor R_J (lower triangular) and its later rows
+// W_{N,J} = C_{N,J} R_J^-T:
+//   factor (chunk levels upward): for every block (t, j) of J's panel
+//       C_{t,j} = A_{t,j} - sum_u W_{t,u} W_{j,u}^T
+//   over the earlier columns u outside J with j and t in N(u); then
+//       R_J = chol(C_JJ) (dense),  W_{N,J} = C_{N,J} R_J^-T,
+//       log det += 2 sum ln diag(R_J)
+//   Takahashi (chunk levels downward, root first), N = N_J:
+//       G_{N,J} = -(G_{N,N} W_{N,J}) R_J^-1
+//       G_JJ    = R_J^-T (R_J^-1 - W_{N,J}^T G_{N,J})
+// (the page's LDL^T recurrences for the fat node, L_{N,J} = W_{N,J} R_J^-1,
+// D_J = R_J R_J^T).  Every block read lies in S because N_J is a clique;
+// the blocks inside a chunk are in S because a supernode's columns are dense.
+// One G_{N,N} block now serves s columns at once.
 //
-// Work decomposition.  One workgroup per (target or slot, matrix), four
-// launches per level: the Schur sums of all targets of the level, their
-// scaling by R_v^-T (each workgroup refactors its node's b x b pivot; the
-// diagonal target also stores R_v^-1 and the log det term), the rows
-// G_{w,v} of the level, and its diagonal blocks.  Every workgroup owns what
-// it writes, sums run in a fixed order (pairs in elimination order, then a
-// fixed reduction tree), so results are deterministic and need no atomics
-// except the first-failure index.  Sums of b x b products are staged
-// through LDS in rounds of several pairs; each group of b*b threads takes
-// every G-th pair of a round (G = 256 / b^2 groups for b <= 16).
+// Work decomposition, each workgroup owning what it writes for one matrix:
+// per level the Schur sums (one workgroup per panel block), the dense pivots
+// (one per chunk: R_J^-1, the log det term), the scaling of the later rows
+// (one per row), and in the Takahashi pass the rows G_{w,J} (one per tile of
+// rows) and the chunk's own blocks (one per block column).  Sums run in a fixed order, so
+// results are deterministic; the only atomic is the first-failure index.
+// Operands are staged through LDS in rounds; every thread issues a batch of
+// loads before storing them, so a round costs about one memory latency.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -46,11 +48,39 @@ __host__ __device__ inline int stage_pairs(int bb) {
   return c < 1 ? 1 : (c > 64 ? 64 : c);
 }
 
-// LDS: two staging buffers, a reduction buffer of kJT, and four blocks
+// LDS: the pair table of a staging round (two block pointers and a flag
+// byte per pair), two staging buffers, a reduction buffer of kJT and four
+// blocks.
+constexpr int kMaxPairs = 64;
+constexpr size_t kTableBytes = kMaxPairs * (2 * sizeof(void *) + 1);
+constexpr int kMaxLoads = 8;  // staged elements per thread and buffer (2048 / kJT)
+
 template <typename T>
 size_t lds_bytes(int b) {
   const int bb = b * b;
-  return sizeof(T) * (2 * size_t(stage_pairs(bb)) * bb + kJT + 4 * size_t(bb));
+  return kTableBytes + sizeof(T) * (2 * size_t(stage_pairs(bb)) * bb + kJT + 4 * size_t(bb));
+}
+
+template <typename T>
+struct Lds {
+  const T **pa, **pb;
+  unsigned char *tr;
+  T *sa, *sb, *red, *blk;
+};
+
+template <typename T>
+__device__ inline Lds<T> lds_carve(int b) {
+  extern __shared__ char smem_raw[];
+  Lds<T> l;
+  l.pa = reinterpret_cast<const T **>(smem_raw);
+  l.pb = l.pa + kMaxPairs;
+  l.tr = reinterpret_cast<unsigned char *>(l.pb + kMaxPairs);
+  const int bb = b * b, CH = stage_pairs(bb);
+  l.sa = reinterpret_cast<T *>(smem_raw + kTableBytes);
+  l.sb = l.sa + CH * bb;
+  l.red = l.sb + CH * bb;
+  l.blk = l.red + kJT;
+  return l;
 }
 
 enum Mode { kABt = 0, kAB = 1, kAtB = 2 };
@@ -67,11 +97,14 @@ __device__ inline T dot_block(const T *A, const T *Bm, int b, int r, int c) {
 }
 
 // Sum over q < count of op(A_q) op(B_q) into `out` (LDS, bb entries).
-// stage(q, el, a_val, b_val) returns entry el of A_q and of B_q (already in
-// the orientation MODE expects).  Deterministic: fixed pair-to-group map and
+// src(q, A, ta, B, tb) names the two blocks of pair q (global memory) and
+// whether each is to be read transposed.  Each round first puts the pair
+// table in LDS, then every thread issues all its element loads before it
+// stores any (one memory latency per round, not one per element), then the
+// groups of bb threads multiply.  Deterministic: fixed pair-to-group map and
 // fixed reduction order.
-template <int MODE, typename T, typename Stage>
-__device__ inline void staged_sum(T *out, int count, int b, T *sa, T *sb, T *red, Stage stage) {
+template <int MODE, typename T, typename Src>
+__device__ inline void staged_sum(T *out, int count, int b, const Lds<T> &l, Src src) {
   const int bb = b * b, t = threadIdx.x;
   const int CH = stage_pairs(bb);
   const bool small = bb <= kJT;
@@ -80,35 +113,58 @@ __device__ inline void staged_sum(T *out, int count, int b, T *sa, T *sb, T *red
   T acc[4] = {T(0), T(0), T(0), T(0)};
   for (int q0 = 0; q0 < count; q0 += CH) {
     const int cnt = count - q0 < CH ? count - q0 : CH;
-    for (int idx = t; idx < cnt * bb; idx += kJT) {
-      const int q = idx / bb, el = idx - q * bb;
-      T av, bv;
-      stage(q0 + q, el, av, bv);
-      sa[idx] = av;
-      sb[idx] = bv;
+    if (t < cnt) {
+      const T *A, *Bp;
+      int ta, tb;
+      src(q0 + t, A, ta, Bp, tb);
+      l.pa[t] = A;
+      l.pb[t] = Bp;
+      l.tr[t] = static_cast<unsigned char>(ta | (tb << 1));
+    }
+    __syncthreads();
+    const int tot = cnt * bb;
+    T va[kMaxLoads], vb[kMaxLoads];
+#pragma unroll
+    for (int j = 0; j < kMaxLoads; ++j) {
+      const int idx = t + j * kJT;
+      if (idx < tot) {
+        const int q = idx / bb, el = idx - q * bb, r = el / b, c = el - r * b;
+        const int f = l.tr[q];
+        va[j] = l.pa[q][(f & 1) ? c * b + r : el];
+        vb[j] = l.pb[q][(f & 2) ? c * b + r : el];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxLoads; ++j) {
+      const int idx = t + j * kJT;
+      if (idx < tot) {
+        l.sa[idx] = va[j];
+        l.sb[idx] = vb[j];
+      }
     }
     __syncthreads();
     if (small) {
       if (g < G) {
         const int e = t - g * bb, r = e / b, c = e - r * b;
-        for (int q = g; q < cnt; q += G) acc[0] += dot_block<MODE>(sa + q * bb, sb + q * bb, b, r, c);
+        for (int q = g; q < cnt; q += G)
+          acc[0] += dot_block<MODE>(l.sa + q * bb, l.sb + q * bb, b, r, c);
       }
     } else {
       for (int i = 0; i < 4; ++i) {
         const int e = t + i * kJT;
         if (e >= bb) break;
         const int r = e / b, c = e - r * b;
-        for (int q = 0; q < cnt; ++q) acc[i] += dot_block<MODE>(sa + q * bb, sb + q * bb, b, r, c);
+        for (int q = 0; q < cnt; ++q) acc[i] += dot_block<MODE>(l.sa + q * bb, l.sb + q * bb, b, r, c);
       }
     }
     __syncthreads();
   }
   if (small) {
-    red[t] = acc[0];
+    l.red[t] = acc[0];
     __syncthreads();
     if (t < bb) {
       T s = T(0);
-      for (int gg = 0; gg < G; ++gg) s += red[gg * bb + t];
+      for (int gg = 0; gg < G; ++gg) s += l.red[gg * bb + t];
       out[t] = s;
     }
   } else {
@@ -120,35 +176,119 @@ __device__ inline void staged_sum(T *out, int count, int b, T *sa, T *sb, T *red
   __syncthreads();
 }
 
-// S (LDS; lower triangle read) = R R^T: R overwrites the lower triangle of S
-// and Rinv (LDS) receives R^-1 (lower, zero above).  Returns 1, uniformly,
-// if a pivot is not > 0 (NaN included); *logdet = ln det S.
+
+// Pairs per round of the chunk kernel (a b x sb row and a block each), the
+// row tiles of the row kernel, and the LDS of every kernel.
+constexpr size_t kLdsMax = 64 * 1024;
+constexpr int kTileTable = 256;  // G block pointers per staging round of a row tile
+constexpr size_t kTileTableBytes = kTileTable * (sizeof(void *) + 1);
+
+// rows per tile: H = R b <= 64 scalar rows (16 threads x 4 rows)
+__host__ __device__ inline int tile_rows(int b) { return b >= 64 ? 1 : 64 / b; }
+// staging steps (x values) per round: about 4096 elements, table-limited
+__host__ __device__ inline int tile_steps(int b, int s) {
+  const int R = tile_rows(b), per = R * b * b + b * s * b;
+  int c = 4096 / per;
+  c = c < 1 ? 1 : c;
+  c = c > kTileTable / R ? kTileTable / R : c;
+  return c < 1 ? 1 : c;
+}
+
+__host__ __device__ inline int rows_pairs(int b, int s) {
+  const int per = b * b + b * s * b;
+  const int c = 4096 / per;
+  return c < 1 ? 1 : (c > kMaxPairs ? kMaxPairs : c);
+}
+__host__ __device__ inline int diag_pairs(int b, int s) {
+  const int per = b * s * b + b * b;
+  const int c = 4096 / per;
+  return c < 1 ? 1 : (c > kMaxPairs ? kMaxPairs : c);
+}
 template <typename T>
-__device__ inline int chol_inverse(T *S, T *Rinv, int b, double *logdet) {
+size_t fac_lds(int b, int sm) {
+  const size_t sb = size_t(sm) * b;
+  return sizeof(T) * 2 * sb * sb;
+}
+template <typename T>
+size_t scale_lds(int b, int sm) {
+  const size_t sb = size_t(sm) * b;
+  return sizeof(T) * (sb * sb + b * sb);
+}
+// the chunk size varies (s <= sm); the largest need over s bounds the launch
+template <typename T>
+size_t rows_lds(int b, int sm) {
+  size_t best = 0;
+  const size_t H = size_t(tile_rows(b)) * b;
+  for (int s = 1; s <= sm; ++s) {
+    const size_t sb = size_t(s) * b;
+    const size_t stage = size_t(tile_steps(b, s)) * (H * b + b * sb);
+    const size_t epi = H * sb + sb * sb;
+    const size_t e = stage > epi ? stage : epi;
+    best = e > best ? e : best;
+  }
+  return kTileTableBytes + sizeof(T) * best;
+}
+template <typename T>
+size_t diag_lds(int b, int sm) {
+  size_t best = 0;
+  for (int s = 1; s <= sm; ++s) {
+    const size_t sb = size_t(s) * b, wr = b * sb;
+    size_t stage = size_t(diag_pairs(b, s)) * (wr + b * b);
+    stage = stage < 2 * sb * b ? 2 * sb * b : stage;  // later X and Y (sb x b each)
+    const size_t e = sb * sb + stage;
+    best = e > best ? e : best;
+  }
+  return sizeof(T) * best;
+}
+
+// Copies tot elements into LDS dst, element e = src(e) (a global load),
+// each thread issuing up to eight loads before it stores them.
+template <typename T, typename F>
+__device__ inline void gather_lds(T *dst, int tot, F src) {
+  for (int base = 0; base < tot; base += 8 * kJT) {
+    T v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = base + threadIdx.x + j * kJT;
+      if (e < tot) v[j] = src(e);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = base + threadIdx.x + j * kJT;
+      if (e < tot) dst[e] = v[j];
+    }
+  }
+}
+
+// S (LDS, n x n; lower triangle read) = R R^T: R overwrites the lower
+// triangle of S and Rinv (LDS) receives R^-1 (lower, zero above).  Returns
+// 0, or 1 + the first column whose pivot is not > 0 (NaN included),
+// uniformly; *logdet = ln det S.
+template <typename T>
+__device__ inline int chol_inverse(T *S, T *Rinv, int n, double *logdet) {
   const int t = threadIdx.x;
   double ld = 0.0;
-  for (int j = 0; j < b; ++j) {
-    const T d = S[j * b + j];
-    if (!(d > T(0))) return 1;
+  for (int j = 0; j < n; ++j) {
+    const T d = S[j * n + j];
+    if (!(d > T(0))) return j + 1;
     ld += log(static_cast<double>(d));
     const T r = sqrt(d);
-    for (int i = j + 1 + t; i < b; i += kJT) S[i * b + j] /= r;
+    for (int i = j + 1 + t; i < n; i += kJT) S[i * n + j] /= r;
     __syncthreads();
-    const int rem = b - j - 1;
+    const int rem = n - j - 1;
     for (int e = t; e < rem * rem; e += kJT) {
       const int i = j + 1 + e / rem, l = j + 1 + e % rem;
-      if (l <= i) S[i * b + l] -= S[i * b + j] * S[l * b + j];
+      if (l <= i) S[i * n + l] -= S[i * n + j] * S[l * n + j];
     }
     __syncthreads();
   }
-  for (int j = t; j < b; j += kJT) S[j * b + j] = sqrt(S[j * b + j]);
+  for (int j = t; j < n; j += kJT) S[j * n + j] = sqrt(S[j * n + j]);
   __syncthreads();
-  // R X = I, one column of X per thread
-  for (int c = t; c < b; c += kJT) {
-    for (int i = 0; i < b; ++i) {
+  for (int c = t; c < n; c += kJT) {  // R X = I, one column of X per thread
+    for (int i = 0; i < n; ++i) {
       T s = i == c ? T(1) : T(0);
-      for (int k = c; k < i; ++k) s -= S[i * b + k] * Rinv[k * b + c];
-      Rinv[i * b + c] = i < c ? T(0) : s / S[i * b + i];
+      for (int k = c; k < i; ++k) s -= S[i * n + k] * Rinv[k * n + c];
+      Rinv[i * n + c] = i < c ? T(0) : s / S[i * n + i];
     }
   }
   __syncthreads();
@@ -156,160 +296,306 @@ __device__ inline int chol_inverse(T *S, T *Rinv, int b, double *logdet) {
   return 0;
 }
 
+struct Dims {
+  int64_t n, m, nnz, nch, npanel, nrinv;
+  int b;
+};
+
 template <typename T>
 __global__ void __launch_bounds__(kJT) jt_init(int32_t *info_ws, int64_t B) {
   const int64_t m = blockIdx.x * int64_t(kJT) + threadIdx.x;
   if (m < B) info_ws[m] = INT_MAX;
 }
 
-// Schur sums of the targets [tbase, tbase + gridDim.x) for matrix blockIdx.y
+// Schur sums of the panel blocks [tbase, tbase + gridDim.x), matrix blockIdx.y
 template <typename T>
-__global__ void __launch_bounds__(kJT) jt_fwd_update(JunctionPlanDev P, int64_t tbase, int64_t n,
-                                                     int64_t m_edges, int64_t nnz, int b,
+__global__ void __launch_bounds__(kJT) jt_fwd_update(JunctionPlanDev P, Dims d, int64_t tbase,
                                                      const T *__restrict__ diag,
-                                                     const T *__restrict__ edge_val, T *W, T *Cd) {
-  extern __shared__ char smem_raw[];
-  T *smem = reinterpret_cast<T *>(smem_raw);
-  const int bb = b * b, CH = stage_pairs(bb);
-  T *sa = smem, *sb = sa + CH * bb, *red = sb + CH * bb, *acc = red + kJT;
+                                                     const T *__restrict__ edge_val, T *W) {
+  const int b = d.b, bb = b * b;
+  const Lds<T> l = lds_carve<T>(b);
+  T *acc = l.blk;
   const int64_t tg = tbase + blockIdx.x, mat = blockIdx.y;
-  const int v = P.tgt_node[tg];
-  const int64_t a = tg - (int64_t(P.colptr[v]) + v);  // 0 = the diagonal
+  const int id = P.tg_chunk[tg], rc = P.tg_rc[tg], r = rc >> 6, col = rc & 63;
   const int32_t f0 = P.fptr[tg], f1 = P.fptr[tg + 1];
-  const T *Wm = W + mat * nnz * bb;
+  const T *Wm = W + mat * d.npanel * bb;
   const int32_t *fp = P.fpair;
-  staged_sum<kABt>(acc, f1 - f0, b, sa, sb, red, [&](int q, int el, T &av, T &bv) {
-    av = Wm[int64_t(fp[2 * (f0 + q)]) * bb + el];
-    bv = Wm[int64_t(fp[2 * (f0 + q) + 1]) * bb + el];
+  staged_sum<kABt>(acc, f1 - f0, b, l, [&](int q, const T *&A, int &ta, const T *&Bp, int &tb) {
+    A = Wm + int64_t(fp[2 * (f0 + q)]) * bb;
+    Bp = Wm + int64_t(fp[2 * (f0 + q) + 1]) * bb;
+    ta = tb = 0;
   });
   const int32_t enc = P.ain[tg];
-  if (a == 0) {
-    const T *D = diag + (mat * n + enc) * bb;
-    T *dst = Cd + (mat * n + v) * bb;
+  T *dst = W + (mat * d.npanel + P.ch_pbase[id] + int64_t(r) * P.ch_s[id] + col) * bb;
+  if (r == col) {
+    const T *D = diag + (mat * d.n + enc) * bb;
     for (int e = threadIdx.x; e < bb; e += kJT) {
-      const int r = e / b, c = e - r * b;
-      dst[e] = (r >= c ? D[r * b + c] : D[c * b + r]) - acc[e];
+      const int i = e / b, j = e - i * b;
+      dst[e] = (i >= j ? D[i * b + j] : D[j * b + i]) - acc[e];
     }
   } else {
-    T *dst = W + (mat * nnz + P.colptr[v] + (a - 1)) * bb;
-    const T *E = enc < 0 ? nullptr : edge_val + (mat * m_edges + (enc >> 1)) * bb;
+    const T *E = enc < 0 ? nullptr : edge_val + (mat * d.m + (enc >> 1)) * bb;
     const bool tr = enc >= 0 && (enc & 1);
     for (int e = threadIdx.x; e < bb; e += kJT) {
-      const int r = e / b, c = e - r * b;
-      const T base = E ? (tr ? E[c * b + r] : E[e]) : T(0);
-      dst[e] = base - acc[e];
+      const int i = e / b, j = e - i * b;
+      dst[e] = (E ? (tr ? E[j * b + i] : E[e]) : T(0)) - acc[e];
     }
   }
 }
 
-// R_v from C_vv; diagonal targets store R_v^-1, the log det term and a
-// failure; slot targets scale W_{t,v} = C_{t,v} R_v^-T in place
+// Dense pivot of every chunk of the level: R_J^-1 (into RJ), the log det
+// term, the first failing column
 template <typename T>
-__global__ void __launch_bounds__(kJT) jt_fwd_scale(JunctionPlanDev P, int64_t tbase, int64_t n,
-                                                    int64_t nnz, int b, T *W, const T *Cd, T *Rinv,
-                                                    double *ld_ws, int32_t *info_ws) {
+__global__ void __launch_bounds__(kJT) jt_fwd_factor(JunctionPlanDev P, Dims d, int64_t cbase,
+                                                     const T *W, T *RJ, double *ld_ws,
+                                                     int32_t *info_ws) {
   extern __shared__ char smem_raw[];
-  T *smem = reinterpret_cast<T *>(smem_raw);
-  const int bb = b * b;
-  T *S = smem, *Ri = S + bb, *X = Ri + bb;
-  const int64_t tg = tbase + blockIdx.x, mat = blockIdx.y;
-  const int v = P.tgt_node[tg];
-  const int64_t a = tg - (int64_t(P.colptr[v]) + v);
-  wg::copy(S, Cd + (mat * n + v) * bb, bb);
+  T *M = reinterpret_cast<T *>(smem_raw);
+  const int b = d.b, bb = b * b;
+  const int64_t id = cbase + blockIdx.x, mat = blockIdx.y;
+  const int s = P.ch_s[id], sb = s * b;
+  T *X = M + sb * sb;
+  const T *Wp = W + (mat * d.npanel + P.ch_pbase[id]) * bb;
+  gather_lds(M, sb * sb, [&](int e) {
+    const int I = e / sb, J = e - I * sb;
+    return I >= J ? Wp[(int64_t(I / b) * s + J / b) * bb + (I % b) * b + (J % b)] : T(0);
+  });
+  __syncthreads();
   double ld = 0.0;
-  const int fail = chol_inverse(S, Ri, b, &ld);
-  if (fail) wg::fill(Ri, bb, wg::qnan<T>());
-  if (a == 0) {
-    wg::copy(Rinv + (mat * n + v) * bb, Ri, bb);
-    if (threadIdx.x == 0) {
-      ld_ws[mat * n + v] = fail ? static_cast<double>(wg::qnan<T>()) : ld;
-      if (fail) atomicMin(info_ws + mat, P.node_pos[v]);
-    }
-  } else {
-    T *Wt = W + (mat * nnz + P.colptr[v] + (a - 1)) * bb;
-    wg::copy(X, Wt, bb);
-    wg::gemm<T, false, true>(S, X, Ri, b);  // C R^-T (S is free now)
-    wg::copy(Wt, S, bb);
+  const int fail = chol_inverse(M, X, sb, &ld);
+  if (fail) wg::fill(X, sb * sb, wg::qnan<T>());
+  T *Rout = RJ + (mat * d.nrinv + P.ch_rbase[id]) * bb;
+  for (int e = threadIdx.x; e < sb * sb; e += kJT) Rout[e] = X[e];
+  if (threadIdx.x == 0) {
+    ld_ws[mat * d.nch + id] = fail ? static_cast<double>(wg::qnan<T>()) : ld;
+    if (fail) atomicMin(info_ws + mat, P.ch_first[id] + (fail - 1) / b);
   }
 }
 
-// G_{w,v} for the slots [sbase, sbase + gridDim.x) of matrix blockIdx.y
+// Later rows of the level: W_{w,J} = C_{w,J} R_J^-T in place
 template <typename T>
-__global__ void __launch_bounds__(kJT) jt_bwd_rows(JunctionPlanDev P, int64_t sbase, int64_t n,
-                                                   int64_t nnz, int b, const T *__restrict__ W,
-                                                   const T *__restrict__ Rinv, const T *G_diag,
+__global__ void __launch_bounds__(kJT) jt_fwd_scale(JunctionPlanDev P, Dims d, int64_t rbase0,
+                                                    T *W, const T *RJ) {
+  extern __shared__ char smem_raw[];
+  T *Ri = reinterpret_cast<T *>(smem_raw);
+  const int b = d.b, bb = b * b;
+  const int64_t ri = rbase0 + blockIdx.x, mat = blockIdx.y;
+  const int id = P.row_chunk[ri], a = static_cast<int>(ri - P.rows_ptr[id]);
+  const int s = P.ch_s[id], sb = s * b, wr = b * sb;
+  T *C = Ri + sb * sb;
+  const T *Rj = RJ + (mat * d.nrinv + P.ch_rbase[id]) * bb;
+  T *Wrow = W + (mat * d.npanel + P.ch_pbase[id] + int64_t(s + a) * s) * bb;
+  gather_lds(Ri, sb * sb, [&](int e) { return Rj[e]; });
+  // C as a dense b x sb row: element (i, cc) is block cc / b, entry (i, cc % b)
+  gather_lds(C, wr, [&](int e) {
+    const int i = e / sb, cc = e - i * sb;
+    return Wrow[(cc / b) * bb + i * b + cc % b];
+  });
+  __syncthreads();
+  for (int e = threadIdx.x; e < wr; e += kJT) {
+    const int i = e / sb, cc = e - i * sb;
+    T v = T(0);
+    for (int kk = 0; kk <= cc; ++kk) v += C[i * sb + kk] * Ri[cc * sb + kk];
+    Wrow[(cc / b) * bb + i * b + cc % b] = v;
+  }
+}
+
+// Row tiles of the level: for R consecutive later rows w of a chunk (H = R b
+// scalar rows), G_{w,J} = -(sum_x G_{w,x} W_{x,J}) R_J^-1.  The sum is a
+// gathered product (H x n b) (n b x s b): each step stages, for one x, the
+// R blocks G_{w,x} and the row W_{x,J} once for all R rows; every thread
+// keeps a 4 x 3 register tile of the H x s b result.
+template <typename T>
+__global__ void __launch_bounds__(kJT) jt_bwd_rows(JunctionPlanDev P, Dims d, int64_t tbase,
+                                                   const T *__restrict__ W,
+                                                   const T *__restrict__ RJ, const T *G_diag,
                                                    T *G_lower) {
   extern __shared__ char smem_raw[];
-  T *smem = reinterpret_cast<T *>(smem_raw);
-  const int bb = b * b, CH = stage_pairs(bb);
-  T *sa = smem, *sb = sa + CH * bb, *red = sb + CH * bb, *acc = red + kJT, *Ri = acc + bb,
-    *X = Ri + bb;
-  const int64_t s = sbase + blockIdx.x, mat = blockIdx.y;
-  const int v = P.slot_node[s];
-  const int32_t c0 = P.colptr[v];
-  const int k = P.colptr[v + 1] - c0, a = static_cast<int>(s - c0);
-  const int32_t *gt = P.gtab + P.gptr[v] + int64_t(a) * k;
-  const T *Wm = W + mat * nnz * bb;
-  const T *Gd = G_diag + mat * n * bb, *Gl = G_lower + mat * nnz * bb;
-  staged_sum<kAB>(acc, k, b, sa, sb, red, [&](int q, int el, T &av, T &bv) {
-    const int32_t enc = gt[q];
-    if (enc < 0) {
-      av = Gd[int64_t(-enc - 1) * bb + el];
-    } else {
-      const int r = el / b, c = el - r * b;
-      av = Gl[int64_t(enc >> 1) * bb + ((enc & 1) ? c * b + r : el)];
+  const T **tab = reinterpret_cast<const T **>(smem_raw);
+  unsigned char *fl = reinterpret_cast<unsigned char *>(tab + kTileTable);
+  T *stage = reinterpret_cast<T *>(smem_raw + kTileTableBytes);
+  const int b = d.b, bb = b * b, t = threadIdx.x;
+  const int R = tile_rows(b), H = R * b;
+  const int64_t tile = tbase + blockIdx.x, mat = blockIdx.y;
+  const int id = P.tile_chunk[tile];
+  const int a0 = static_cast<int>(tile - P.tiles_ptr[id]) * R;
+  const int s = P.ch_s[id], nr = P.ch_n[id], sb = s * b;
+  const int rows = nr - a0 < R ? nr - a0 : R;  // valid rows of this tile
+  const int CQ = tile_steps(b, s);
+  T *sA = stage, *sB = sA + CQ * H * b;
+  const int64_t pb = P.ch_pbase[id];
+  const T *Wp = W + (mat * d.npanel + pb) * bb;
+  const T *Gd = G_diag + mat * d.n * bb, *Gl = G_lower + mat * d.nnz * bb;
+  const int32_t *gt = P.gtab + P.ch_gptr[id];
+  const int ty = t / 16, tx = t % 16;  // rows 4 ty .. 4 ty + 3, columns tx + 16 j
+  T acc[4][3];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) acc[r][j] = T(0);
+  for (int q0 = 0; q0 < nr; q0 += CQ) {
+    const int cnt = nr - q0 < CQ ? nr - q0 : CQ;
+    // table: block G_{w_{a0+ra}, x_{q0+q}} for ra < rows, q < cnt
+    for (int e = t; e < cnt * R; e += kJT) {
+      const int q = e / R, ra = e - q * R;
+      if (ra < rows) {
+        const int32_t enc = gt[int64_t(a0 + ra) * nr + q0 + q];
+        tab[e] = enc < 0 ? Gd + int64_t(-enc - 1) * bb : Gl + int64_t(enc >> 1) * bb;
+        fl[e] = enc >= 0 && (enc & 1);
+      } else {
+        tab[e] = nullptr;
+        fl[e] = 0;
+      }
     }
-    bv = Wm[int64_t(c0 + q) * bb + el];
-  });
-  wg::copy(Ri, Rinv + (mat * n + v) * bb, bb);
-  wg::gemm<T, false, false>(X, acc, Ri, b);   // T_w R_v^-1
-  const int32_t o = P.outenc[s];
-  T *dst = G_lower + (mat * nnz + (o >> 1)) * bb;
-  for (int e = threadIdx.x; e < bb; e += kJT) {
-    const int r = e / b, c = e - r * b;
-    dst[e] = -((o & 1) ? X[c * b + r] : X[e]);
+    __syncthreads();
+    // sA[q][h][k] = G_{w(h), x_q}[h % b][k]  (H x b per step)
+    gather_lds(sA, cnt * H * b, [&](int e) {
+      const int q = e / (H * b), rem = e - q * H * b, h = rem / b, k = rem - h * b;
+      const int ra = h / b, i = h - ra * b;
+      const T *src = tab[q * R + ra];
+      return src ? src[fl[q * R + ra] ? k * b + i : i * b + k] : T(0);
+    });
+    // sB[q][k][cc] = W_{x_q,J}[k][cc]  (b x sb per step, panel row s + q0 + q)
+    gather_lds(sB, cnt * b * sb, [&](int e) {
+      const int q = e / (b * sb), rem = e - q * b * sb, k = rem / sb, cc = rem - k * sb;
+      return Wp[(int64_t(s + q0 + q) * s + cc / b) * bb + k * b + cc % b];
+    });
+    __syncthreads();
+    for (int q = 0; q < cnt; ++q) {
+      const T *A = sA + q * H * b, *Bq = sB + q * b * sb;
+      for (int k = 0; k < b; ++k) {
+        T av[4], bv[3];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = 4 * ty + r;
+          av[r] = h < H ? A[h * b + k] : T(0);
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          const int cc = tx + 16 * j;
+          bv[j] = cc < sb ? Bq[k * sb + cc] : T(0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int j = 0; j < 3; ++j) acc[r][j] += av[r] * bv[j];
+      }
+    }
+    __syncthreads();
+  }
+  // epilogue: T (H x sb) and R_J^-1 in LDS, then -T R_J^-1 to the output
+  T *Tt = stage, *Ri = Tt + H * sb;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int h = 4 * ty + r, cc = tx + 16 * j;
+      if (h < H && cc < sb) Tt[h * sb + cc] = acc[r][j];
+    }
+  gather_lds(Ri, sb * sb, [&](int e) { return RJ[(mat * d.nrinv + P.ch_rbase[id]) * bb + e]; });
+  __syncthreads();
+  for (int e = t; e < rows * b * sb; e += kJT) {
+    const int h = e / sb, cc = e - h * sb;
+    T v = T(0);
+    for (int kk = cc; kk < sb; ++kk) v += Tt[h * sb + kk] * Ri[kk * sb + cc];
+    const int ra = h / b, i = h - ra * b, j = cc % b;
+    const int32_t o = P.poutenc[pb + int64_t(s + a0 + ra) * s + cc / b];
+    T *dst = G_lower + (mat * d.nnz + (o >> 1)) * bb;
+    dst[(o & 1) ? j * b + i : i * b + j] = -v;
   }
 }
 
-// G_vv for the nodes [nbase, nbase + gridDim.x) of matrix blockIdx.y
+// The chunk's own blocks, one workgroup per block column col of the chunk:
+// G_{J,col} = R_J^-T (R_J^-1 - W_{N,J}^T G_{N,J})_{:,col}; the blocks on and
+// below the diagonal are written (the diagonal block symmetrised).
 template <typename T>
-__global__ void __launch_bounds__(kJT) jt_bwd_diag(JunctionPlanDev P, int64_t nbase, int64_t n,
-                                                   int64_t nnz, int b, const T *__restrict__ W,
-                                                   const T *__restrict__ Rinv, T *G_diag,
-                                                   const T *G_lower) {
+__global__ void __launch_bounds__(kJT) jt_bwd_diag(JunctionPlanDev P, Dims d, int64_t fcbase,
+                                                   const T *__restrict__ W,
+                                                   const T *__restrict__ RJ, T *G_diag,
+                                                   T *G_lower) {
   extern __shared__ char smem_raw[];
-  T *smem = reinterpret_cast<T *>(smem_raw);
-  const int bb = b * b, CH = stage_pairs(bb);
-  T *sa = smem, *sb = sa + CH * bb, *red = sb + CH * bb, *acc = red + kJT, *Ri = acc + bb,
-    *X = Ri + bb, *Y = X + bb;
-  const int64_t v = nbase + blockIdx.x, mat = blockIdx.y;
-  const int32_t c0 = P.colptr[v];
-  const int k = P.colptr[v + 1] - c0;
-  const T *Wm = W + mat * nnz * bb, *Gl = G_lower + mat * nnz * bb;
-  staged_sum<kAtB>(acc, k, b, sa, sb, red, [&](int q, int el, T &av, T &bv) {
-    av = Wm[int64_t(c0 + q) * bb + el];
-    const int32_t o = P.outenc[c0 + q];
-    const int r = el / b, c = el - r * b;
-    bv = Gl[int64_t(o >> 1) * bb + ((o & 1) ? c * b + r : el)];
-  });
-  wg::copy(Ri, Rinv + (mat * n + v) * bb, bb);
-  for (int e = threadIdx.x; e < bb; e += kJT) X[e] = Ri[e] - acc[e];
+  T *Ri = reinterpret_cast<T *>(smem_raw);
+  const int b = d.b, bb = b * b, t = threadIdx.x;
+  const int64_t fc = fcbase + blockIdx.x, mat = blockIdx.y;
+  const int id = P.col_chunk[fc], col = static_cast<int>(fc - P.ch_cptr[id]);
+  const int s = P.ch_s[id], nr = P.ch_n[id], sb = s * b, wr = b * sb, f = P.ch_first[id];
+  const int CH = diag_pairs(b, s), ob = sb * b;  // output: sb x b
+  T *sA = Ri + sb * sb, *sB = sA + CH * wr;
+  const int64_t pb = P.ch_pbase[id];
+  const T *Wp = W + (mat * d.npanel + pb) * bb;
+  const T *Gl = G_lower + mat * d.nnz * bb;
+  gather_lds(Ri, sb * sb, [&](int e) { return RJ[(mat * d.nrinv + P.ch_rbase[id]) * bb + e]; });
+  __syncthreads();  // Ri is read below even when the chunk has no later rows
+  T acc[6] = {T(0), T(0), T(0), T(0), T(0), T(0)};
+  for (int q0 = 0; q0 < nr; q0 += CH) {
+    const int cnt = nr - q0 < CH ? nr - q0 : CH;
+    // W_{x_q,J} as dense b x sb rows; G_{x_q, f+col} blocks
+    gather_lds(sA, cnt * wr, [&](int e) {
+      const int q = e / wr, rem = e - q * wr, k = rem / sb, cc = rem - k * sb;
+      return Wp[(int64_t(s + q0 + q) * s + cc / b) * bb + k * b + cc % b];
+    });
+    gather_lds(sB, cnt * bb, [&](int e) {
+      const int q = e / bb, el = e - q * bb, k = el / b, j = el - k * b;
+      const int32_t o = P.poutenc[pb + int64_t(s + q0 + q) * s + col];
+      return Gl[int64_t(o >> 1) * bb + ((o & 1) ? j * b + k : el)];
+    });
+    __syncthreads();
+    for (int u = 0; u < 6; ++u) {
+      const int e = t + u * kJT;
+      if (e >= ob) break;
+      const int I = e / b, j = e - I * b;
+      for (int q = 0; q < cnt; ++q) {
+        const T *A = sA + q * wr + I, *Bq = sB + q * bb + j;
+        T v = T(0);
+        for (int k = 0; k < b; ++k) v += A[k * sb] * Bq[k * b];
+        acc[u] += v;
+      }
+    }
+    __syncthreads();
+  }
+  T *X = sA;  // sb x b column block of R^-1 - W^T G
+  for (int u = 0; u < 6; ++u) {
+    const int e = t + u * kJT;
+    if (e >= ob) break;
+    const int I = e / b, j = e - I * b;
+    X[e] = Ri[I * sb + col * b + j] - acc[u];
+  }
   __syncthreads();
-  wg::gemm<T, true, false>(Y, Ri, X, b);      // R^-T (R^-1 - W^T G)
-  wg::sym_part(X, Y, b);
-  wg::copy(G_diag + (mat * n + P.node_label[v]) * bb, X, bb);
+  // rows I >= col b of G_{:,col} = R^-T X: sum over K >= I of Ri[K][I] X[K][j]
+  T *Y = sA + ob;
+  for (int e = t; e < ob; e += kJT) {
+    const int I = e / b, j = e - I * b;
+    if (I < col * b) continue;
+    T y = T(0);
+    for (int K = I; K < sb; ++K) y += Ri[K * sb + I] * X[K * b + j];
+    Y[e] = y;
+  }
+  __syncthreads();
+  for (int e = t; e < ob; e += kJT) {
+    const int I = e / b, j = e - I * b, r = I / b, i = I - r * b;
+    if (r < col) continue;
+    if (r == col) {
+      if (i < j) continue;
+      const T v = T(0.5) * (Y[I * b + j] + Y[(col * b + j) * b + i]);
+      T *dst = G_diag + (mat * d.n + P.order[f + r]) * bb;
+      dst[i * b + j] = v;
+      dst[j * b + i] = v;
+    } else {
+      const int32_t o = P.poutenc[pb + int64_t(r) * s + col];
+      T *dst = G_lower + (mat * d.nnz + (o >> 1)) * bb;
+      dst[(o & 1) ? j * b + i : i * b + j] = Y[e];
+    }
+  }
 }
 
-// log det = sum of the per-node terms in a fixed order; info from the
-// earliest failing elimination position
 template <typename T>
-__global__ void __launch_bounds__(kJT) jt_finish(JunctionPlanDev P, int64_t n,
+__global__ void __launch_bounds__(kJT) jt_finish(JunctionPlanDev P, int64_t nch,
                                                  const double *ld_ws, const int32_t *info_ws,
                                                  double *logdet, int32_t *info) {
   __shared__ double red[kJT];
   const int64_t mat = blockIdx.x;
   double s = 0.0;
-  for (int64_t v = threadIdx.x; v < n; v += kJT) s += ld_ws[mat * n + v];
+  for (int64_t c = threadIdx.x; c < nch; c += kJT) s += ld_ws[mat * nch + c];
   red[threadIdx.x] = s;
   __syncthreads();
   for (int w = kJT / 2; w > 0; w >>= 1) {
@@ -324,7 +610,7 @@ __global__ void __launch_bounds__(kJT) jt_finish(JunctionPlanDev P, int64_t n,
 }
 
 struct JtWs {
-  void *W, *Cd, *Rinv;
+  void *W, *RJ;
   double *ld;
   int32_t *info;
 };
@@ -333,10 +619,9 @@ JtWs carve(const selinv_junction_plan *plan, int64_t B, void *ws) {
   const size_t bb = size_t(plan->b) * plan->b, es = plan->dtype_bytes;
   Carve cv(ws);
   JtWs w;
-  w.W = cv.take<char>(B * plan->nnz * bb * es);
-  w.Cd = cv.take<char>(B * plan->n * bb * es);
-  w.Rinv = cv.take<char>(B * plan->n * bb * es);
-  w.ld = cv.take<double>(B * plan->n);
+  w.W = cv.take<char>(B * plan->npanel * bb * es);
+  w.RJ = cv.take<char>(B * plan->nrinv * bb * es);
+  w.ld = cv.take<double>(B * plan->nch);
   w.info = cv.take<int32_t>(B);
   return w;
 }
@@ -344,12 +629,11 @@ JtWs carve(const selinv_junction_plan *plan, int64_t B, void *ws) {
 }  // namespace
 
 size_t junction_workspace_bytes(const selinv_junction_plan *plan, int64_t B) {
-  const size_t bb = size_t(plan->b) * plan->b, es = plan->dtype_bytes;
   Carve cv(nullptr);
-  cv.take<char>(B * plan->nnz * bb * es);
-  cv.take<char>(B * plan->n * bb * es);
-  cv.take<char>(B * plan->n * bb * es);
-  cv.take<double>(B * plan->n);
+  const size_t bb = size_t(plan->b) * plan->b, es = plan->dtype_bytes;
+  cv.take<char>(B * plan->npanel * bb * es);
+  cv.take<char>(B * plan->nrinv * bb * es);
+  cv.take<double>(B * plan->nch);
   cv.take<int32_t>(B);
   return cv.off;
 }
@@ -358,31 +642,43 @@ template <typename T>
 hipError_t junction_launch(const selinv_junction_plan *plan, int64_t B, const T *diag,
                            const T *edge_val, T *G_diag, T *G_lower, double *logdet,
                            int32_t *info, void *ws, hipStream_t s) {
-  const int b = plan->b;
-  const int64_t n = plan->n, nnz = plan->nnz, m = plan->m;
+  const int b = plan->b, sm = plan->smax;
+  const Dims d{plan->n, plan->m, plan->nnz, plan->nch, plan->npanel, plan->nrinv, b};
   const JunctionPlanDev &P = plan->dev;
   const JtWs w = carve(plan, B, ws);
-  T *W = static_cast<T *>(w.W), *Cd = static_cast<T *>(w.Cd), *Rinv = static_cast<T *>(w.Rinv);
-  const size_t lds = lds_bytes<T>(b);
+  T *W = static_cast<T *>(w.W), *RJ = static_cast<T *>(w.RJ);
+  const size_t l_upd = lds_bytes<T>(b), l_fac = fac_lds<T>(b, sm), l_scl = scale_lds<T>(b, sm),
+               l_row = rows_lds<T>(b, sm), l_dia = diag_lds<T>(b, sm);
+  if (l_upd > kLdsMax || l_fac > kLdsMax || l_scl > kLdsMax || l_row > kLdsMax ||
+      l_dia > kLdsMax)
+    return hipErrorInvalidValue;
   const auto &lo = plan->level_off;
-  const auto &cp = plan->colptr_host;
+  const auto &tp = plan->ch_tptr;
+  const auto &rp = plan->rows_ptr;
   const unsigned By = static_cast<unsigned>(B);
-  jt_init<T><<<dim3(static_cast<unsigned>((B + kJT - 1) / kJT)), dim3(kJT), 0, s>>>(w.info, B);
+  const dim3 blk(kJT);
+  jt_init<T><<<dim3(static_cast<unsigned>((B + kJT - 1) / kJT)), blk, 0, s>>>(w.info, B);
   for (int32_t l = 0; l < plan->levels; ++l) {
-    const int64_t t0 = cp[lo[l]] + lo[l], t1 = cp[lo[l + 1]] + lo[l + 1];
-    const dim3 grid(static_cast<unsigned>(t1 - t0), By);
-    jt_fwd_update<T><<<grid, dim3(kJT), lds, s>>>(P, t0, n, m, nnz, b, diag, edge_val, W, Cd);
-    jt_fwd_scale<T><<<grid, dim3(kJT), lds, s>>>(P, t0, n, nnz, b, W, Cd, Rinv, w.ld, w.info);
+    const int64_t c0 = lo[l], c1 = lo[l + 1];
+    jt_fwd_update<T><<<dim3(static_cast<unsigned>(tp[c1] - tp[c0]), By), blk, l_upd, s>>>(
+        P, d, tp[c0], diag, edge_val, W);
+    jt_fwd_factor<T><<<dim3(static_cast<unsigned>(c1 - c0), By), blk, l_fac, s>>>(
+        P, d, c0, W, RJ, w.ld, w.info);
+    if (rp[c1] > rp[c0])
+      jt_fwd_scale<T><<<dim3(static_cast<unsigned>(rp[c1] - rp[c0]), By), blk, l_scl, s>>>(
+          P, d, rp[c0], W, RJ);
   }
   for (int32_t l = plan->levels - 1; l >= 0; --l) {
-    const int64_t s0 = cp[lo[l]], s1 = cp[lo[l + 1]];
-    if (s1 > s0)
-      jt_bwd_rows<T><<<dim3(static_cast<unsigned>(s1 - s0), By), dim3(kJT), lds, s>>>(
-          P, s0, n, nnz, b, W, Rinv, G_diag, G_lower);
-    jt_bwd_diag<T><<<dim3(static_cast<unsigned>(lo[l + 1] - lo[l]), By), dim3(kJT), lds, s>>>(
-        P, lo[l], n, nnz, b, W, Rinv, G_diag, G_lower);
+    const int64_t c0 = lo[l], c1 = lo[l + 1];
+    const auto &tl = plan->tiles_ptr;
+    if (tl[c1] > tl[c0])
+      jt_bwd_rows<T><<<dim3(static_cast<unsigned>(tl[c1] - tl[c0]), By), blk, l_row, s>>>(
+          P, d, tl[c0], W, RJ, G_diag, G_lower);
+    const int64_t f0 = plan->ch_cptr[c0], f1 = plan->ch_cptr[c1];
+    jt_bwd_diag<T><<<dim3(static_cast<unsigned>(f1 - f0), By), blk, l_dia, s>>>(
+        P, d, f0, W, RJ, G_diag, G_lower);
   }
-  jt_finish<T><<<dim3(By), dim3(kJT), 0, s>>>(P, n, w.ld, w.info, logdet, info);
+  jt_finish<T><<<dim3(By), blk, 0, s>>>(P, plan->nch, w.ld, w.info, logdet, info);
   return hipGetLastError();
 }
 

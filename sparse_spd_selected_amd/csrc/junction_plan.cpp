@@ -13,17 +13,27 @@
 // level-set schedule the page describes for the batched path (its height is
 // about sqrt(n) on a 2-D grid).
 //
-// The plan renumbers the nodes level by level (elimination position within
-// a level) and precomputes every index the kernels need, so that a kernel
-// only follows flat integer tables:
-//   * W slots: column v's blocks (w, v), w in N(v), contiguous, rows in
-//     elimination order (the canonical orientation: later node first);
-//   * forward targets: per node, the diagonal then one per slot; per target
-//     the list of (W_{t,u}, W_{v,u}) pairs of its Schur update, u in
-//     elimination order, and the input block it starts from;
-//   * backward tables: per node, the k x k reads of G_{w,x} (w, x in N(v))
-//     as positions in the caller's output arrays with a transpose bit;
-//   * the output position of every slot in S_index order.
+// Supernodes.  Consecutive columns j, j+1 of the elimination form a
+// supernode when j+1 is j's parent and j's other later neighbours are
+// exactly j+1's; the factor's columns there share one dense structure.  The
+// plan cuts supernodes into chunks of at most s_max columns (s_max b <= 48,
+// so that a chunk's dense pivot fits in LDS) and the numeric work treats a
+// chunk as one fat node: its pivot is the dense (s b) x (s b) block, its
+// later rows N_J are the later neighbours of its last column.  The schedule
+// is the level sets of the chunk tree, much shorter than the node-level one
+// where supernodes are long.
+//
+// Tables (chunk ids level by level, then by position):
+//   * panels: chunk J's factor columns as (s + n_J) x s blocks, row-major
+//     by block, rows = the chunk's own columns then N_J in elimination
+//     order; only blocks on or below the block diagonal are used;
+//   * forward targets: every used panel block; per target the list of
+//     (W_{t,u}, W_{v,u}) panel blocks of its Schur update over the earlier
+//     columns u outside the chunk, u in elimination order, and the input
+//     block it starts from;
+//   * backward: per chunk the n_J x n_J reads of G_{w,x} (w, x in N_J) as
+//     positions in the caller's output arrays with a transpose bit, and the
+//     output code of every panel block.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -96,15 +106,22 @@ bool eliminate(int64_t n, std::vector<Vec> adj, const int32_t *order_in, Vec &or
 
 // Everything the symbolic analysis produces (host memory).
 struct HostTables {
-  int64_t n = 0, nnz = 0, npairs = 0, ntg = 0, ng = 0;
-  int32_t L = 0;
-  Vec order, S_index, node_label, node_pos, slot_node, outenc, tgt_node, ain, fpair, gtab;
-  std::vector<int64_t> level_off, colptr, fptr, gptr;
+  int64_t n = 0, nnz = 0, nch = 0, ntg = 0, npairs = 0, nrows = 0, npanel = 0, nrinv = 0, ng = 0;
+  int32_t node_levels = 0, levels = 0, smax = 0;
+  Vec order, S_index;
+  std::vector<int64_t> level_off;     // chunk-id range of every level
+  // chunk tables (by chunk id)
+  Vec ch_first, ch_s, ch_n;
+  std::vector<int64_t> ch_pbase, ch_rbase, ch_gptr, ch_tptr, rows_ptr, ch_cptr, tiles_ptr;
+  Vec row_chunk, col_chunk, tile_chunk, tg_chunk, tg_rc, ain, fpair, gtab, poutenc;
+  std::vector<int64_t> fptr;
 };
 
-// Symbolic analysis; with tables == false only the order, S and the levels.
+// Symbolic analysis.  With tables == false: the order, S and the height of
+// the elimination tree only; else also the supernode chunks (at most
+// `smax` columns each) and every table of the numeric kernels.
 int analyze(int64_t n, int64_t m, const int32_t *edge_index_host, const int32_t *order_host,
-            bool tables, HostTables &h) {
+            int32_t smax, int32_t tile_rows, bool tables, HostTables &h) {
   // ---- pattern: adjacency lists, validated
   std::vector<Vec> adj(n);
   std::unordered_map<int64_t, int32_t> edge_of;
@@ -125,189 +142,272 @@ int analyze(int64_t n, int64_t m, const int32_t *edge_index_host, const int32_t 
 
   Vec epos(n);  // label -> elimination position
   for (int64_t s = 0; s < n; ++s) epos[order[s]] = static_cast<int32_t>(s);
-
-  // ---- elimination tree levels (children come earlier in the order)
-  Vec level(n, 0);  // by position
-  int32_t H = 0;
+  // later neighbours as positions, ascending
+  std::vector<Vec> np(n);
+  int64_t nnz = 0;
   for (int64_t s = 0; s < n; ++s) {
-    int32_t par = -1;
-    for (int32_t w : nbr[s]) par = par < 0 ? epos[w] : std::min(par, epos[w]);
-    if (par >= 0) level[par] = std::max(level[par], level[s] + 1);
-    H = std::max(H, level[s]);
+    for (int32_t w : nbr[s]) np[s].push_back(epos[w]);
+    std::sort(np[s].begin(), np[s].end());
+    nnz += np[s].size();
   }
-  const int32_t L = H + 1;
+  std::vector<Vec>().swap(nbr);
+  if (nnz >= (int64_t(1) << 29)) return SELINV_ERR_INVALID_ARG;
 
-  // ---- node ids: by level, then elimination position
-  Vec id_of_pos(n), pos_of_id(n);
+  // ---- height of the elimination tree (children come earlier)
+  {
+    Vec level(n, 0);
+    int32_t H = 0;
+    for (int64_t s = 0; s < n; ++s) {
+      if (!np[s].empty()) level[np[s][0]] = std::max(level[np[s][0]], level[s] + 1);
+      H = std::max(H, level[s]);
+    }
+    h.node_levels = H + 1;
+  }
+
+  // ---- S_index (pairs i > j by label, sorted) and the output code of every
+  // block (w, v) of S, w later: position * 2 + (stored transposed)
+  std::vector<std::pair<std::pair<int32_t, int32_t>, int64_t>> pairs;
+  pairs.reserve(nnz);
+  for (int64_t s = 0; s < n; ++s)
+    for (int32_t wp : np[s]) {
+      const int32_t w = order[wp], v = order[s];
+      pairs.push_back({{std::max(w, v), std::min(w, v)}, int64_t(wp) * n + s});
+    }
+  std::sort(pairs.begin(), pairs.end());
+  std::unordered_map<int64_t, int32_t> out_of;  // (wpos * n + vpos) -> code
+  out_of.reserve(nnz * 2 + 1);
+  Vec S_index(2 * nnz);
+  for (int64_t k = 0; k < nnz; ++k) {
+    const int64_t key = pairs[k].second;
+    const int32_t w = order[key / n], v = order[key % n];
+    out_of[key] = static_cast<int32_t>(k * 2 + (w < v ? 1 : 0));
+    S_index[k] = pairs[k].first.first;
+    S_index[nnz + k] = pairs[k].first.second;
+  }
+  decltype(pairs)().swap(pairs);
+  h.order = order;
+  h.S_index.swap(S_index);
+  h.nnz = nnz;
+  if (!tables) return SELINV_OK;
+
+  // ---- supernodes (column j+1 is j's parent and j's other later
+  // neighbours are exactly j+1's), cut into chunks of at most smax columns
+  std::vector<std::pair<int32_t, int32_t>> chunks;  // (first position, size)
+  for (int64_t j = 0; j < n;) {
+    int64_t e = j;
+    while (e + 1 < n && e - j + 1 < smax && !np[e].empty() && np[e][0] == e + 1 &&
+           np[e].size() == np[e + 1].size() + 1 &&
+           std::equal(np[e].begin() + 1, np[e].end(), np[e + 1].begin()))
+      ++e;
+    chunks.push_back({static_cast<int32_t>(j), static_cast<int32_t>(e - j + 1)});
+    j = e + 1;
+  }
+  const int64_t nch = static_cast<int64_t>(chunks.size());
+  Vec chunk_of(n);  // position -> chunk (in position order)
+  for (int64_t c = 0; c < nch; ++c)
+    for (int32_t j = 0; j < chunks[c].second; ++j) chunk_of[chunks[c].first + j] = int32_t(c);
+  // the later rows of a chunk: the later neighbours of its last column
+  auto below = [&](int64_t c) -> const Vec & { return np[chunks[c].first + chunks[c].second - 1]; };
+  // chunk levels (children come earlier)
+  Vec clevel(nch, 0);
+  int32_t CH = 0;
+  for (int64_t c = 0; c < nch; ++c) {
+    const Vec &N = below(c);
+    if (!N.empty()) {
+      const int32_t p = chunk_of[N[0]];
+      clevel[p] = std::max(clevel[p], clevel[c] + 1);
+    }
+    CH = std::max(CH, clevel[c]);
+  }
+  const int32_t L = CH + 1;
+  // chunk ids: by level, then position
+  Vec id_of(nch), chunk_at(nch);
   std::vector<int64_t> level_off(L + 1, 0);
-  for (int64_t s = 0; s < n; ++s) level_off[level[s] + 1]++;
+  for (int64_t c = 0; c < nch; ++c) level_off[clevel[c] + 1]++;
   for (int32_t l = 0; l < L; ++l) level_off[l + 1] += level_off[l];
   {
     std::vector<int64_t> next(level_off.begin(), level_off.end() - 1);
-    for (int64_t s = 0; s < n; ++s) {
-      const int64_t p = next[level[s]]++;
-      id_of_pos[s] = static_cast<int32_t>(p);
-      pos_of_id[p] = static_cast<int32_t>(s);
+    for (int64_t c = 0; c < nch; ++c) {
+      const int64_t id = next[clevel[c]]++;
+      id_of[c] = static_cast<int32_t>(id);
+      chunk_at[id] = static_cast<int32_t>(c);
     }
   }
-
-  // ---- W slots by node id; rows (as positions) ascending
-  std::vector<int64_t> colptr(n + 1, 0);
-  for (int64_t p = 0; p < n; ++p) colptr[p + 1] = colptr[p] + nbr[pos_of_id[p]].size();
-  const int64_t nnz = colptr[n];
-  if (nnz >= (int64_t(1) << 30)) return SELINV_ERR_INVALID_ARG;
-  Vec rowpos(nnz), slot_node(nnz);
-  for (int64_t p = 0; p < n; ++p) {
-    const Vec &nb = nbr[pos_of_id[p]];
-    int64_t k = colptr[p];
-    for (int32_t w : nb) rowpos[k++] = epos[w];
-    std::sort(rowpos.begin() + colptr[p], rowpos.begin() + colptr[p + 1]);
-    for (int64_t t = colptr[p]; t < colptr[p + 1]; ++t) slot_node[t] = static_cast<int32_t>(p);
+  // per-id sizes and offsets
+  h.ch_first.resize(nch);
+  h.ch_s.resize(nch);
+  h.ch_n.resize(nch);
+  h.ch_pbase.assign(nch + 1, 0);
+  h.ch_rbase.assign(nch + 1, 0);
+  h.ch_gptr.assign(nch + 1, 0);
+  h.ch_tptr.assign(nch + 1, 0);
+  h.rows_ptr.assign(nch + 1, 0);
+  h.ch_cptr.assign(nch + 1, 0);
+  h.tiles_ptr.assign(nch + 1, 0);
+  for (int64_t id = 0; id < nch; ++id) {
+    const int64_t c = chunk_at[id];
+    const int64_t sz = chunks[c].second, nr = static_cast<int64_t>(below(c).size());
+    h.ch_first[id] = chunks[c].first;
+    h.ch_s[id] = static_cast<int32_t>(sz);
+    h.ch_n[id] = static_cast<int32_t>(nr);
+    h.ch_pbase[id + 1] = h.ch_pbase[id] + (sz + nr) * sz;
+    h.ch_rbase[id + 1] = h.ch_rbase[id] + sz * sz;
+    h.ch_gptr[id + 1] = h.ch_gptr[id] + nr * nr;
+    h.ch_tptr[id + 1] = h.ch_tptr[id] + sz * (sz + 1) / 2 + nr * sz;
+    h.rows_ptr[id + 1] = h.rows_ptr[id] + nr;
+    h.ch_cptr[id + 1] = h.ch_cptr[id] + sz;
+    h.tiles_ptr[id + 1] = h.tiles_ptr[id] + (nr + tile_rows - 1) / tile_rows;
   }
-  // slot of block (w, v) given positions, w later than v
-  auto slot_of = [&](int32_t wpos, int32_t vpos) -> int64_t {
-    const int64_t p = id_of_pos[vpos];
-    const auto b0 = rowpos.begin() + colptr[p], b1 = rowpos.begin() + colptr[p + 1];
-    const auto it = std::lower_bound(b0, b1, wpos);
-    return (it == b1 || *it != wpos) ? -1 : colptr[p] + (it - rowpos.begin() - colptr[p]);
+  const int64_t npanel = h.ch_pbase[nch];
+  if (npanel >= (int64_t(1) << 30)) return SELINV_ERR_INVALID_ARG;
+  // panel block of (w, v), w at or after v, both positions, (w, v) in S or w == v
+  auto panel_row = [&](int64_t id, int32_t wpos) -> int64_t {
+    const int64_t c = chunk_at[id];
+    const int32_t f = chunks[c].first, sz = chunks[c].second;
+    if (wpos >= f && wpos < f + sz) return wpos - f;
+    const Vec &N = below(c);
+    const auto it = std::lower_bound(N.begin(), N.end(), wpos);
+    if (it == N.end() || *it != wpos) return -1;
+    return sz + (it - N.begin());
   };
-
-  // ---- output positions: S_index sorted by (i, j), i > j labels
-  std::vector<int64_t> by_out(nnz);
-  for (int64_t t = 0; t < nnz; ++t) by_out[t] = t;
-  auto lab_pair = [&](int64_t t) {
-    const int32_t w = order[rowpos[t]], v = order[pos_of_id[slot_node[t]]];
-    return std::make_pair(std::max(w, v), std::min(w, v));
+  auto panel_index = [&](int32_t wpos, int32_t vpos) -> int64_t {
+    const int64_t id = id_of[chunk_of[vpos]];
+    const int64_t r = panel_row(id, wpos);
+    if (r < 0) return -1;
+    return h.ch_pbase[id] + r * h.ch_s[id] + (vpos - h.ch_first[id]);
   };
-  std::sort(by_out.begin(), by_out.end(),
-            [&](int64_t a, int64_t c) { return lab_pair(a) < lab_pair(c); });
-  Vec outenc(nnz);        // output position * 2 + (stored transposed)
-  Vec S_index(2 * nnz);
-  for (int64_t k = 0; k < nnz; ++k) {
-    const int64_t t = by_out[k];
-    const int32_t w = order[rowpos[t]], v = order[pos_of_id[slot_node[t]]];
-    outenc[t] = static_cast<int32_t>(k * 2 + (w < v ? 1 : 0));
-    S_index[k] = std::max(w, v);
-    S_index[nnz + k] = std::min(w, v);
-  }
-
-  h.order = order;
-  h.S_index.swap(S_index);
-  h.level_off = level_off;
-  h.colptr = colptr;
-  h.nnz = nnz;
-  h.L = L;
-  if (!tables) return SELINV_OK;
-
-  // ---- forward targets: per node id the diagonal, then one per slot
-  const int64_t ntg = nnz + n;
-  Vec tgt_node(ntg), ain(ntg);
-  for (int64_t p = 0; p < n; ++p) {
-    const int64_t t0 = colptr[p] + p;
-    const int32_t v = order[pos_of_id[p]];
-    tgt_node[t0] = static_cast<int32_t>(p);
-    ain[t0] = v;
-    for (int64_t t = colptr[p]; t < colptr[p + 1]; ++t) {
-      const int64_t tg = t0 + 1 + (t - colptr[p]);
-      tgt_node[tg] = static_cast<int32_t>(p);
-      const int32_t w = order[rowpos[t]];
-      const auto it = edge_of.find(int64_t(std::max(w, v)) * n + std::min(w, v));
-      ain[tg] = it == edge_of.end() ? -1 : it->second * 2 + (w < v ? 1 : 0);
-    }
-  }
-  auto target_of = [&](int32_t tpos, int32_t vpos) -> int64_t {  // t later than or equal to v
-    const int64_t p = id_of_pos[vpos];
-    if (tpos == vpos) return colptr[p] + p;
-    const int64_t s = slot_of(tpos, vpos);
-    return s < 0 ? -1 : colptr[p] + p + 1 + (s - colptr[p]);
-  };
-  // pairs: two passes over u in elimination order (count, then fill)
-  std::vector<int64_t> fptr(ntg + 1, 0);
-  for (int pass = 0; pass < 2; ++pass) {
-    std::vector<int64_t> fillp;
-    if (pass == 1) fillp.assign(fptr.begin(), fptr.end() - 1);
-    for (int64_t s = 0; s < n; ++s) {
-      const int64_t pu = id_of_pos[s];
-      for (int64_t i2 = colptr[pu]; i2 < colptr[pu + 1]; ++i2)    // v = rowpos[i2]
-        for (int64_t i1 = i2; i1 < colptr[pu + 1]; ++i1) {        // t = rowpos[i1] >= v
-          const int64_t tg = target_of(rowpos[i1], rowpos[i2]);
-          if (tg < 0) return SELINV_ERR_BAD_PATTERN;               // not chordal: cannot happen
-          if (pass == 0)
-            fptr[tg + 1]++;
-          else
-            fillp[tg]++;
-        }
-    }
-    if (pass == 0) {
-      for (int64_t tg = 0; tg < ntg; ++tg) fptr[tg + 1] += fptr[tg];
-    }
-  }
-  const int64_t npairs = fptr[ntg];
-  if (npairs >= (int64_t(1) << 31)) return SELINV_ERR_INVALID_ARG;
-  std::vector<int32_t> fpair(2 * npairs);
-  {
-    std::vector<int64_t> fillp(fptr.begin(), fptr.end() - 1);
-    for (int64_t s = 0; s < n; ++s) {
-      const int64_t pu = id_of_pos[s];
-      for (int64_t i2 = colptr[pu]; i2 < colptr[pu + 1]; ++i2)
-        for (int64_t i1 = i2; i1 < colptr[pu + 1]; ++i1) {
-          const int64_t tg = target_of(rowpos[i1], rowpos[i2]);
-          const int64_t q = fillp[tg]++;
-          fpair[2 * q] = static_cast<int32_t>(i1);      // W_{t,u}
-          fpair[2 * q + 1] = static_cast<int32_t>(i2);  // W_{v,u}
-        }
-    }
-  }
-
-  // ---- backward tables: per node id, k x k encoded reads of G_{w,x}
-  std::vector<int64_t> gptr(n + 1, 0);
-  for (int64_t p = 0; p < n; ++p) {
-    const int64_t k = colptr[p + 1] - colptr[p];
-    gptr[p + 1] = gptr[p] + k * k;
-  }
-  const int64_t ng = gptr[n];
-  Vec gtab(ng);
-  for (int64_t p = 0; p < n; ++p) {
-    const int64_t c0 = colptr[p], k = colptr[p + 1] - c0;
-    for (int64_t a = 0; a < k; ++a)
-      for (int64_t c = 0; c < k; ++c) {
-        const int32_t wp = rowpos[c0 + a], xp = rowpos[c0 + c];
-        int32_t enc;
-        if (a == c) {
-          enc = -(order[wp] + 1);                       // G_diag of w
+  // flat rows (chunk, a): a-th later row of the chunk
+  h.row_chunk.resize(h.rows_ptr[nch]);
+  for (int64_t id = 0; id < nch; ++id)
+    for (int64_t r = h.rows_ptr[id]; r < h.rows_ptr[id + 1]; ++r)
+      h.row_chunk[r] = static_cast<int32_t>(id);
+  h.tile_chunk.resize(h.tiles_ptr[nch]);
+  for (int64_t id = 0; id < nch; ++id)
+    for (int64_t c = h.tiles_ptr[id]; c < h.tiles_ptr[id + 1]; ++c) h.tile_chunk[c] = int32_t(id);
+  h.col_chunk.resize(n);
+  for (int64_t id = 0; id < nch; ++id)
+    for (int64_t c = h.ch_cptr[id]; c < h.ch_cptr[id + 1]; ++c) h.col_chunk[c] = int32_t(id);
+  // output codes of every panel block: -(label + 1) on the diagonal, the S
+  // code below it, -1 above
+  h.poutenc.assign(npanel, -1);
+  for (int64_t id = 0; id < nch; ++id) {
+    const int64_t c = chunk_at[id];
+    const int32_t f = chunks[c].first, sz = chunks[c].second;
+    const Vec &N = below(c);
+    for (int64_t r = 0; r < sz + static_cast<int64_t>(N.size()); ++r)
+      for (int32_t col = 0; col < sz && col <= r; ++col) {
+        const int32_t wpos = r < sz ? f + int32_t(r) : N[r - sz], vpos = f + col;
+        int32_t code;
+        if (wpos == vpos) {
+          code = -(order[vpos] + 1);
         } else {
-          const bool w_later = a > c;
-          const int64_t s = w_later ? slot_of(wp, xp) : slot_of(xp, wp);
-          if (s < 0) return SELINV_ERR_BAD_PATTERN;
-          const int32_t o = outenc[s];
-          // the slot's canonical block is G_{w,x} (w later) or G_{x,w};
-          // the output holds the canonical block transposed when o & 1
-          const int flip = (o & 1) ^ (w_later ? 0 : 1);
-          enc = (o & ~1) | flip;
+          const auto it = out_of.find(int64_t(wpos) * n + vpos);
+          if (it == out_of.end()) return SELINV_ERR_BAD_PATTERN;  // cannot happen: S is closed
+          code = it->second;
         }
-        gtab[gptr[p] + a * k + c] = enc;
+        h.poutenc[h.ch_pbase[id] + r * sz + col] = code;
       }
   }
-
-  h.ntg = ntg;
-  h.npairs = npairs;
-  h.ng = ng;
-  h.node_label.resize(n);
-  h.node_pos.resize(n);
-  for (int64_t p = 0; p < n; ++p) {
-    h.node_pos[p] = pos_of_id[p];
-    h.node_label[p] = order[pos_of_id[p]];
+  // ---- forward targets: every panel block (r >= col), chunk by chunk
+  const int64_t ntg = h.ch_tptr[nch];
+  h.tg_chunk.resize(ntg);
+  h.tg_rc.resize(ntg);
+  h.ain.resize(ntg);
+  for (int64_t id = 0; id < nch; ++id) {
+    const int64_t c = chunk_at[id];
+    const int32_t f = chunks[c].first, sz = chunks[c].second;
+    const Vec &N = below(c);
+    int64_t tg = h.ch_tptr[id];
+    for (int32_t col = 0; col < sz; ++col)
+      for (int64_t r = col; r < sz + static_cast<int64_t>(N.size()); ++r, ++tg) {
+        h.tg_chunk[tg] = static_cast<int32_t>(id);
+        h.tg_rc[tg] = static_cast<int32_t>(r * 64 + col);
+        const int32_t wpos = r < sz ? f + int32_t(r) : N[r - sz], vpos = f + col;
+        const int32_t w = order[wpos], v = order[vpos];
+        if (wpos == vpos) {
+          h.ain[tg] = v;
+        } else {
+          const auto it = edge_of.find(int64_t(std::max(w, v)) * n + std::min(w, v));
+          h.ain[tg] = it == edge_of.end() ? -1 : it->second * 2 + (w < v ? 1 : 0);
+        }
+      }
   }
-  h.slot_node.swap(slot_node);
-  h.outenc.swap(outenc);
-  h.tgt_node.swap(tgt_node);
-  h.ain.swap(ain);
-  h.fpair.swap(fpair);
-  h.gtab.swap(gtab);
-  h.fptr.swap(fptr);
-  h.gptr.swap(gptr);
+  auto target_of = [&](int32_t tpos, int32_t vpos) -> int64_t {
+    const int64_t id = id_of[chunk_of[vpos]];
+    const int64_t r = panel_row(id, tpos);
+    if (r < 0) return -1;
+    const int64_t sz = h.ch_s[id], nr = h.ch_n[id], col = vpos - h.ch_first[id];
+    // targets of column col start after columns 0..col-1 (each sz + nr - col' entries)
+    const int64_t before = col * (sz + nr) - col * (col - 1) / 2;
+    return h.ch_tptr[id] + before + (r - col);
+  };
+  // Schur pairs from every column u into the targets of later chunks, u in
+  // elimination order (two passes: count, then fill)
+  h.fptr.assign(ntg + 1, 0);
+  for (int pass = 0; pass < 2; ++pass) {
+    std::vector<int64_t> fillp;
+    if (pass == 1) fillp.assign(h.fptr.begin(), h.fptr.end() - 1);
+    for (int64_t u = 0; u < n; ++u) {
+      const Vec &N = np[u];
+      for (size_t i2 = 0; i2 < N.size(); ++i2) {
+        if (chunk_of[N[i2]] == chunk_of[u]) continue;  // inside the fat pivot
+        for (size_t i1 = i2; i1 < N.size(); ++i1) {
+          const int64_t tg = target_of(N[i1], N[i2]);
+          if (tg < 0) return SELINV_ERR_BAD_PATTERN;
+          if (pass == 0) {
+            h.fptr[tg + 1]++;
+          } else {
+            const int64_t q = fillp[tg]++;
+            const int64_t p1 = panel_index(N[i1], int32_t(u)), p2 = panel_index(N[i2], int32_t(u));
+            if (p1 < 0 || p2 < 0) return SELINV_ERR_BAD_PATTERN;  // cannot happen: S is closed
+            h.fpair[2 * q] = static_cast<int32_t>(p1);
+            h.fpair[2 * q + 1] = static_cast<int32_t>(p2);
+          }
+        }
+      }
+    }
+    if (pass == 0) {
+      for (int64_t tg = 0; tg < ntg; ++tg) h.fptr[tg + 1] += h.fptr[tg];
+      if (h.fptr[ntg] >= (int64_t(1) << 31)) return SELINV_ERR_INVALID_ARG;
+      h.fpair.resize(2 * h.fptr[ntg]);
+    }
+  }
+  // ---- backward: per chunk the n x n reads of G_{w,x}, w, x later rows
+  h.gtab.resize(h.ch_gptr[nch]);
+  for (int64_t id = 0; id < nch; ++id) {
+    const Vec &N = below(chunk_at[id]);
+    const int64_t nr = static_cast<int64_t>(N.size());
+    for (int64_t a = 0; a < nr; ++a)
+      for (int64_t q = 0; q < nr; ++q) {
+        int32_t enc;
+        if (a == q) {
+          enc = -(order[N[a]] + 1);
+        } else {
+          const bool w_later = a > q;
+          const int32_t hi = w_later ? N[a] : N[q], lo = w_later ? N[q] : N[a];
+          const auto it = out_of.find(int64_t(hi) * n + lo);
+          if (it == out_of.end()) return SELINV_ERR_BAD_PATTERN;
+          const int32_t o = it->second;
+          enc = (o & ~1) | ((o & 1) ^ (w_later ? 0 : 1));
+        }
+        h.gtab[h.ch_gptr[id] + a * nr + q] = enc;
+      }
+  }
+  h.nch = nch;
+  h.ntg = ntg;
+  h.npairs = h.fptr[ntg];
+  h.nrows = h.rows_ptr[nch];
+  h.npanel = npanel;
+  h.nrinv = h.ch_rbase[nch];
+  h.ng = h.ch_gptr[nch];
+  h.levels = L;
+  h.level_off = level_off;
+  h.smax = smax;
   return SELINV_OK;
 }
+
+// columns per chunk: the chunk's pivot (s b x s b) and its inverse fit LDS
+int32_t chunk_columns(int32_t b) { return std::max<int32_t>(1, 48 / b); }
 
 }  // namespace
 
@@ -320,74 +420,92 @@ extern "C" int selinv_junction_plan_create(int64_t n, int64_t m, const int32_t *
       b > SELINV_MAX_B || (dtype_bytes != 4 && dtype_bytes != 8))
     return SELINV_ERR_INVALID_ARG;
   HostTables h;
-  const int rc = analyze(n, m, edge_index_host, order_host, true, h);
+  const int rc = analyze(n, m, edge_index_host, order_host, chunk_columns(b),
+                         b >= 64 ? 1 : 64 / b, true, h);
   if (rc != SELINV_OK) return rc;
-  const int64_t nnz = h.nnz, ntg = h.ntg, npairs = h.npairs, ng = h.ng;
-  const int32_t L = h.L;
 
-  // ---- plan object and device tables
   selinv_junction_plan *plan = new (std::nothrow) selinv_junction_plan();
   if (!plan) return SELINV_ERR_HIP;
   plan->n = n;
   plan->m = m;
   plan->b = b;
   plan->dtype_bytes = dtype_bytes;
-  plan->nnz = nnz;
-  plan->levels = L;
-  plan->npairs = npairs;
+  plan->nnz = h.nnz;
+  plan->nch = h.nch;
+  plan->npanel = h.npanel;
+  plan->nrinv = h.nrinv;
+  plan->smax = h.smax;
+  plan->levels = h.levels;
+  plan->node_levels = h.node_levels;
   plan->level_off = h.level_off;
-  plan->colptr_host = h.colptr;
+  plan->ch_tptr = h.ch_tptr;
+  plan->rows_ptr = h.rows_ptr;
+  plan->ch_cptr = h.ch_cptr;
+  plan->tiles_ptr = h.tiles_ptr;
   plan->S_index.swap(h.S_index);
   plan->order.swap(h.order);
-  int64_t maxk = 0;
-  for (int64_t p = 0; p < n; ++p) maxk = std::max(maxk, h.colptr[p + 1] - h.colptr[p]);
-  plan->max_k = maxk;
 
-  Vec colptr32(n + 1), fptr32(ntg + 1);
-  for (int64_t p = 0; p <= n; ++p) colptr32[p] = static_cast<int32_t>(h.colptr[p]);
-  for (int64_t t = 0; t <= ntg; ++t) fptr32[t] = static_cast<int32_t>(h.fptr[t]);
-
-  const size_t i4 = sizeof(int32_t);
-  const size_t bytes = selinv::align_up((n + 1) * i4) + 2 * selinv::align_up(n * i4) +
-                       selinv::align_up(n * i4) + 2 * selinv::align_up(ntg * i4) +
-                       selinv::align_up((ntg + 1) * i4) + selinv::align_up(2 * npairs * i4) +
-                       2 * selinv::align_up(nnz * i4) + selinv::align_up((n + 1) * 8) +
-                       selinv::align_up(ng * i4) + 4096;
+  std::vector<int32_t> fptr32(h.ntg + 1);
+  for (int64_t t = 0; t <= h.ntg; ++t) fptr32[t] = static_cast<int32_t>(h.fptr[t]);
+  const size_t i4 = sizeof(int32_t), i8 = sizeof(int64_t);
+  using selinv::align_up;
+  const size_t bytes = align_up(n * i4) + 3 * align_up(h.nch * i4) +
+                       6 * align_up((h.nch + 1) * i8) + align_up(h.nrows * i4) +
+                       align_up(n * i4) + align_up(h.tiles_ptr[h.nch] * i4) +
+                       3 * align_up(h.ntg * i4) + align_up((h.ntg + 1) * i4) +
+                       align_up(2 * h.npairs * i4) + align_up(h.ng * i4) +
+                       align_up(h.npanel * i4) + 4096;
   if (hipMalloc(&plan->dev_block, bytes) != hipSuccess) {
     delete plan;
     return SELINV_ERR_HIP;
   }
   selinv::Carve cv(plan->dev_block);
   selinv::JunctionPlanDev &dv = plan->dev;
-  dv.colptr = cv.take<int32_t>(n + 1);
-  dv.node_label = cv.take<int32_t>(n);
-  dv.node_pos = cv.take<int32_t>(n);
   dv.order = cv.take<int32_t>(n);
-  dv.tgt_node = cv.take<int32_t>(ntg);
-  dv.ain = cv.take<int32_t>(ntg);
-  dv.fptr = cv.take<int32_t>(ntg + 1);
-  dv.fpair = cv.take<int32_t>(2 * npairs);
-  dv.slot_node = cv.take<int32_t>(nnz);
-  dv.outenc = cv.take<int32_t>(nnz);
-  dv.gptr = cv.take<int64_t>(n + 1);
-  dv.gtab = cv.take<int32_t>(ng);
+  dv.ch_first = cv.take<int32_t>(h.nch);
+  dv.ch_s = cv.take<int32_t>(h.nch);
+  dv.ch_n = cv.take<int32_t>(h.nch);
+  dv.ch_pbase = cv.take<int64_t>(h.nch + 1);
+  dv.ch_rbase = cv.take<int64_t>(h.nch + 1);
+  dv.ch_gptr = cv.take<int64_t>(h.nch + 1);
+  dv.rows_ptr = cv.take<int64_t>(h.nch + 1);
+  dv.ch_cptr = cv.take<int64_t>(h.nch + 1);
+  dv.row_chunk = cv.take<int32_t>(h.nrows);
+  dv.col_chunk = cv.take<int32_t>(n);
+  dv.tiles_ptr = cv.take<int64_t>(h.nch + 1);
+  dv.tile_chunk = cv.take<int32_t>(h.tiles_ptr[h.nch]);
+  dv.tg_chunk = cv.take<int32_t>(h.ntg);
+  dv.tg_rc = cv.take<int32_t>(h.ntg);
+  dv.ain = cv.take<int32_t>(h.ntg);
+  dv.fptr = cv.take<int32_t>(h.ntg + 1);
+  dv.fpair = cv.take<int32_t>(2 * h.npairs);
+  dv.gtab = cv.take<int32_t>(h.ng);
+  dv.poutenc = cv.take<int32_t>(h.npanel);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   auto up = [&](void *dst, const void *src, size_t nbytes) {
     if (e == hipSuccess && nbytes) e = hipMemcpyAsync(dst, src, nbytes, hipMemcpyHostToDevice, st);
   };
-  up(dv.colptr, colptr32.data(), (n + 1) * i4);
-  up(dv.node_label, h.node_label.data(), n * i4);
-  up(dv.node_pos, h.node_pos.data(), n * i4);
   up(dv.order, plan->order.data(), n * i4);
-  up(dv.tgt_node, h.tgt_node.data(), ntg * i4);
-  up(dv.ain, h.ain.data(), ntg * i4);
-  up(dv.fptr, fptr32.data(), (ntg + 1) * i4);
-  up(dv.fpair, h.fpair.data(), 2 * npairs * i4);
-  up(dv.slot_node, h.slot_node.data(), nnz * i4);
-  up(dv.outenc, h.outenc.data(), nnz * i4);
-  up(dv.gptr, h.gptr.data(), (n + 1) * 8);
-  up(dv.gtab, h.gtab.data(), ng * i4);
+  up(dv.ch_first, h.ch_first.data(), h.nch * i4);
+  up(dv.ch_s, h.ch_s.data(), h.nch * i4);
+  up(dv.ch_n, h.ch_n.data(), h.nch * i4);
+  up(dv.ch_pbase, h.ch_pbase.data(), (h.nch + 1) * i8);
+  up(dv.ch_rbase, h.ch_rbase.data(), (h.nch + 1) * i8);
+  up(dv.ch_gptr, h.ch_gptr.data(), (h.nch + 1) * i8);
+  up(dv.rows_ptr, h.rows_ptr.data(), (h.nch + 1) * i8);
+  up(dv.ch_cptr, h.ch_cptr.data(), (h.nch + 1) * i8);
+  up(dv.row_chunk, h.row_chunk.data(), h.nrows * i4);
+  up(dv.col_chunk, h.col_chunk.data(), n * i4);
+  up(dv.tiles_ptr, h.tiles_ptr.data(), (h.nch + 1) * i8);
+  up(dv.tile_chunk, h.tile_chunk.data(), h.tiles_ptr[h.nch] * i4);
+  up(dv.tg_chunk, h.tg_chunk.data(), h.ntg * i4);
+  up(dv.tg_rc, h.tg_rc.data(), h.ntg * i4);
+  up(dv.ain, h.ain.data(), h.ntg * i4);
+  up(dv.fptr, fptr32.data(), (h.ntg + 1) * i4);
+  up(dv.fpair, h.fpair.data(), 2 * h.npairs * i4);
+  up(dv.gtab, h.gtab.data(), h.ng * i4);
+  up(dv.poutenc, h.poutenc.data(), h.npanel * i4);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) {
     selinv_junction_plan_destroy(plan);
@@ -427,10 +545,10 @@ extern "C" int selinv_junction_symbolic(int64_t n, int64_t m, const int32_t *edg
   if (n < 1 || n > (int64_t(1) << 24) || m < 0 || (m > 0 && !edge_index_host))
     return SELINV_ERR_INVALID_ARG;
   HostTables h;
-  const int rc = analyze(n, m, edge_index_host, order_host, false, h);
+  const int rc = analyze(n, m, edge_index_host, order_host, 1, 1, false, h);
   if (rc != SELINV_OK) return rc;
   if (nnz_out) *nnz_out = h.nnz;
-  if (levels_out) *levels_out = h.L;
+  if (levels_out) *levels_out = h.node_levels;
   if (S_index_host && cap >= h.nnz && h.nnz)
     std::memcpy(S_index_host, h.S_index.data(), 2 * h.nnz * sizeof(int32_t));
   if (order_out) std::memcpy(order_out, h.order.data(), n * sizeof(int32_t));

@@ -162,3 +162,17 @@ def test_empty_batch_and_no_edges(ssa):
     v0 = torch.zeros((0, 4, 2, 2), dtype=torch.float64, device=DEV)
     Gd, S, Gl, ld = ssa.junction(d0, g, v0)
     assert Gd.shape == (0, 4, 2, 2) and ld.shape == (0,)
+
+
+def test_repeated_calls_are_bitwise_identical(ssa):
+    """Fixed summation orders and no atomics in the arithmetic: two calls on
+    the same input agree bit for bit."""
+    e = spdgen.grid_edges(12, 12)
+    d, v = spdgen.graph(e, 144, 4, B=3, seed=6)
+    D, V = _to(d, torch.float64), _to(v, torch.float64)
+    a = ssa.junction(D, e, V)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        c = ssa.junction(D, e, V)
+        torch.cuda.synchronize()
+        assert all(torch.equal(x, y) for x, y in zip(a, c))
