@@ -222,7 +222,7 @@ size_t rows_lds(int b, int sm) {
   for (int s = 1; s <= sm; ++s) {
     const size_t sb = size_t(s) * b;
     const size_t stage = size_t(tile_steps(b, s)) * (H * b + b * sb);
-    const size_t epi = H * sb + sb * sb;
+    const size_t epi = H * sb + sb * sb + (size_t(tile_rows(b)) * s * 4 + sizeof(T) - 1) / sizeof(T);
     const size_t e = stage > epi ? stage : epi;
     best = e > best ? e : best;
   }
@@ -234,7 +234,9 @@ size_t diag_lds(int b, int sm) {
   for (int s = 1; s <= sm; ++s) {
     const size_t sb = size_t(s) * b, wr = b * sb;
     size_t stage = size_t(diag_pairs(b, s)) * (wr + b * b);
-    stage = stage < 2 * sb * b ? 2 * sb * b : stage;  // later X and Y (sb x b each)
+    // later X and Y (sb x b each) and the s output codes of the block column
+    const size_t xy = 2 * sb * b + (size_t(s) * 4 + sizeof(T) - 1) / sizeof(T);
+    stage = stage < xy ? xy : stage;
     const size_t e = sb * sb + stage;
     best = e > best ? e : best;
   }
@@ -308,11 +310,11 @@ __global__ void __launch_bounds__(kJT) jt_init(int32_t *info_ws, int64_t B) {
 }
 
 // Schur sums of the panel blocks [tbase, tbase + gridDim.x), matrix blockIdx.y
-template <typename T>
+template <typename T, int BC>
 __global__ void __launch_bounds__(kJT) jt_fwd_update(JunctionPlanDev P, Dims d, int64_t tbase,
                                                      const T *__restrict__ diag,
                                                      const T *__restrict__ edge_val, T *W) {
-  const int b = d.b, bb = b * b;
+  const int b = BC ? BC : d.b, bb = b * b;
   const Lds<T> l = lds_carve<T>(b);
   T *acc = l.blk;
   const int64_t tg = tbase + blockIdx.x, mat = blockIdx.y;
@@ -345,13 +347,13 @@ __global__ void __launch_bounds__(kJT) jt_fwd_update(JunctionPlanDev P, Dims d, 
 
 // Dense pivot of every chunk of the level: R_J^-1 (into RJ), the log det
 // term, the first failing column
-template <typename T>
+template <typename T, int BC>
 __global__ void __launch_bounds__(kJT) jt_fwd_factor(JunctionPlanDev P, Dims d, int64_t cbase,
                                                      const T *W, T *RJ, double *ld_ws,
                                                      int32_t *info_ws) {
   extern __shared__ char smem_raw[];
   T *M = reinterpret_cast<T *>(smem_raw);
-  const int b = d.b, bb = b * b;
+  const int b = BC ? BC : d.b, bb = b * b;
   const int64_t id = cbase + blockIdx.x, mat = blockIdx.y;
   const int s = P.ch_s[id], sb = s * b;
   T *X = M + sb * sb;
@@ -373,12 +375,12 @@ __global__ void __launch_bounds__(kJT) jt_fwd_factor(JunctionPlanDev P, Dims d, 
 }
 
 // Later rows of the level: W_{w,J} = C_{w,J} R_J^-T in place
-template <typename T>
+template <typename T, int BC>
 __global__ void __launch_bounds__(kJT) jt_fwd_scale(JunctionPlanDev P, Dims d, int64_t rbase0,
                                                     T *W, const T *RJ) {
   extern __shared__ char smem_raw[];
   T *Ri = reinterpret_cast<T *>(smem_raw);
-  const int b = d.b, bb = b * b;
+  const int b = BC ? BC : d.b, bb = b * b;
   const int64_t ri = rbase0 + blockIdx.x, mat = blockIdx.y;
   const int id = P.row_chunk[ri], a = static_cast<int>(ri - P.rows_ptr[id]);
   const int s = P.ch_s[id], sb = s * b, wr = b * sb;
@@ -405,8 +407,40 @@ __global__ void __launch_bounds__(kJT) jt_fwd_scale(JunctionPlanDev P, Dims d, i
 // gathered product (H x n b) (n b x s b): each step stages, for one x, the
 // R blocks G_{w,x} and the row W_{x,J} once for all R rows; every thread
 // keeps a 4 x 3 register tile of the H x s b result.
-template <typename T>
+// Tt (LDS, H x sb, the tile's sum) -> -Tt R_J^-1 into the output rows;
+// Ri is LDS scratch of sb * sb entries.
+// The output codes of the tile's blocks are staged in LDS with R_J^-1, so
+// that no store waits on a dependent load.  Ri is LDS scratch of sb * sb
+// entries followed by room for rows * s codes.
+template <int BC, typename T>
+__device__ inline void rows_epilogue(const JunctionPlanDev &P, const Dims &d, int64_t mat, int id,
+                                     int a0, int rows, const T *Tt, T *Ri, const T *RJ,
+                                     T *G_lower) {
+  const int b = BC ? BC : d.b, bb = b * b, s = P.ch_s[id], sb = s * b;
+  const int64_t pb = P.ch_pbase[id];
+  int32_t *codes = reinterpret_cast<int32_t *>(Ri + sb * sb);
+  for (int e = threadIdx.x; e < rows * s; e += kJT)
+    codes[e] = P.poutenc[pb + int64_t(s + a0) * s + e];
+  gather_lds(Ri, sb * sb, [&](int e) { return RJ[(mat * d.nrinv + P.ch_rbase[id]) * bb + e]; });
+  __syncthreads();
+  for (int e = threadIdx.x; e < rows * b * sb; e += kJT) {
+    const int h = e / sb, cc = e - h * sb;
+    T v = T(0);
+#pragma unroll 4
+    for (int kk = cc; kk < sb; ++kk) v += Tt[h * sb + kk] * Ri[kk * sb + cc];
+    const int ra = h / b, i = h - ra * b, j = cc % b;
+    const int32_t o = codes[ra * s + cc / b];
+    T *dst = G_lower + (mat * d.nnz + (o >> 1)) * bb;
+    dst[(o & 1) ? j * b + i : i * b + j] = -v;
+  }
+}
+
+// Partial sums of a split row tile: kTilePart entries per (tile, part)
+constexpr int kTilePart = 64 * 48;
+
+template <typename T, int BC>
 __global__ void __launch_bounds__(kJT) jt_bwd_rows(JunctionPlanDev P, Dims d, int64_t tbase,
+                                                   int nsplit, T *Tpart,
                                                    const T *__restrict__ W,
                                                    const T *__restrict__ RJ, const T *G_diag,
                                                    T *G_lower) {
@@ -414,13 +448,18 @@ __global__ void __launch_bounds__(kJT) jt_bwd_rows(JunctionPlanDev P, Dims d, in
   const T **tab = reinterpret_cast<const T **>(smem_raw);
   unsigned char *fl = reinterpret_cast<unsigned char *>(tab + kTileTable);
   T *stage = reinterpret_cast<T *>(smem_raw + kTileTableBytes);
-  const int b = d.b, bb = b * b, t = threadIdx.x;
+  const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
   const int R = tile_rows(b), H = R * b;
-  const int64_t tile = tbase + blockIdx.x, mat = blockIdx.y;
+  const int64_t tl = blockIdx.x / nsplit, mat = blockIdx.y;
+  const int part = blockIdx.x - static_cast<int>(tl) * nsplit;
+  const int64_t tile = tbase + tl;
   const int id = P.tile_chunk[tile];
   const int a0 = static_cast<int>(tile - P.tiles_ptr[id]) * R;
   const int s = P.ch_s[id], nr = P.ch_n[id], sb = s * b;
   const int rows = nr - a0 < R ? nr - a0 : R;  // valid rows of this tile
+  // this part's range of the sum over x (all of it without a split)
+  const int qlo = static_cast<int>(int64_t(nr) * part / nsplit);
+  const int qhi = static_cast<int>(int64_t(nr) * (part + 1) / nsplit);
   const int CQ = tile_steps(b, s);
   T *sA = stage, *sB = sA + CQ * H * b;
   const int64_t pb = P.ch_pbase[id];
@@ -433,8 +472,8 @@ __global__ void __launch_bounds__(kJT) jt_bwd_rows(JunctionPlanDev P, Dims d, in
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int j = 0; j < 3; ++j) acc[r][j] = T(0);
-  for (int q0 = 0; q0 < nr; q0 += CQ) {
-    const int cnt = nr - q0 < CQ ? nr - q0 : CQ;
+  for (int q0 = qlo; q0 < qhi; q0 += CQ) {
+    const int cnt = qhi - q0 < CQ ? qhi - q0 : CQ;
     // table: block G_{w_{a0+ra}, x_{q0+q}} for ra < rows, q < cnt
     for (int e = t; e < cnt * R; e += kJT) {
       const int q = e / R, ra = e - q * R;
@@ -483,6 +522,17 @@ __global__ void __launch_bounds__(kJT) jt_bwd_rows(JunctionPlanDev P, Dims d, in
     }
     __syncthreads();
   }
+  if (nsplit > 1) {  // partial sum to the workspace; jt_bwd_rows_sum finishes the tile
+    T *dst = Tpart + ((mat * gridDim.x + blockIdx.x)) * int64_t(kTilePart);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int h = 4 * ty + r, cc = tx + 16 * j;
+        if (h < H && cc < sb) dst[h * sb + cc] = acc[r][j];
+      }
+    return;
+  }
   // epilogue: T (H x sb) and R_J^-1 in LDS, then -T R_J^-1 to the output
   T *Tt = stage, *Ri = Tt + H * sb;
 #pragma unroll
@@ -492,30 +542,44 @@ __global__ void __launch_bounds__(kJT) jt_bwd_rows(JunctionPlanDev P, Dims d, in
       const int h = 4 * ty + r, cc = tx + 16 * j;
       if (h < H && cc < sb) Tt[h * sb + cc] = acc[r][j];
     }
-  gather_lds(Ri, sb * sb, [&](int e) { return RJ[(mat * d.nrinv + P.ch_rbase[id]) * bb + e]; });
-  __syncthreads();
-  for (int e = t; e < rows * b * sb; e += kJT) {
-    const int h = e / sb, cc = e - h * sb;
+  rows_epilogue<BC>(P, d, mat, id, a0, rows, Tt, Ri, RJ, G_lower);
+}
+
+// Split row tiles: sum the parts in a fixed order, then the epilogue
+template <typename T, int BC>
+__global__ void __launch_bounds__(kJT) jt_bwd_rows_sum(JunctionPlanDev P, Dims d, int64_t tbase,
+                                                       int nsplit, const T *Tpart,
+                                                       const T *__restrict__ RJ, T *G_lower) {
+  extern __shared__ char smem_raw[];
+  T *Tt = reinterpret_cast<T *>(smem_raw);
+  const int b = BC ? BC : d.b, R = tile_rows(b), H = R * b;
+  const int64_t tl = blockIdx.x, mat = blockIdx.y;
+  const int64_t tile = tbase + tl;
+  const int id = P.tile_chunk[tile];
+  const int a0 = static_cast<int>(tile - P.tiles_ptr[id]) * R;
+  const int nr = P.ch_n[id], sb = P.ch_s[id] * b;
+  const int rows = nr - a0 < R ? nr - a0 : R;
+  const T *src = Tpart + (mat * int64_t(gridDim.x) * nsplit + tl * nsplit) * int64_t(kTilePart);
+  for (int e = threadIdx.x; e < H * sb; e += kJT) {
     T v = T(0);
-    for (int kk = cc; kk < sb; ++kk) v += Tt[h * sb + kk] * Ri[kk * sb + cc];
-    const int ra = h / b, i = h - ra * b, j = cc % b;
-    const int32_t o = P.poutenc[pb + int64_t(s + a0 + ra) * s + cc / b];
-    T *dst = G_lower + (mat * d.nnz + (o >> 1)) * bb;
-    dst[(o & 1) ? j * b + i : i * b + j] = -v;
+    for (int p = 0; p < nsplit; ++p) v += src[p * int64_t(kTilePart) + e];
+    Tt[e] = v;
   }
+  // (rows_epilogue's first gather is followed by a barrier before Tt is read)
+  rows_epilogue<BC>(P, d, mat, id, a0, rows, Tt, Tt + H * sb, RJ, G_lower);
 }
 
 // The chunk's own blocks, one workgroup per block column col of the chunk:
 // G_{J,col} = R_J^-T (R_J^-1 - W_{N,J}^T G_{N,J})_{:,col}; the blocks on and
 // below the diagonal are written (the diagonal block symmetrised).
-template <typename T>
+template <typename T, int BC>
 __global__ void __launch_bounds__(kJT) jt_bwd_diag(JunctionPlanDev P, Dims d, int64_t fcbase,
                                                    const T *__restrict__ W,
                                                    const T *__restrict__ RJ, T *G_diag,
                                                    T *G_lower) {
   extern __shared__ char smem_raw[];
   T *Ri = reinterpret_cast<T *>(smem_raw);
-  const int b = d.b, bb = b * b, t = threadIdx.x;
+  const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
   const int64_t fc = fcbase + blockIdx.x, mat = blockIdx.y;
   const int id = P.col_chunk[fc], col = static_cast<int>(fc - P.ch_cptr[id]);
   const int s = P.ch_s[id], nr = P.ch_n[id], sb = s * b, wr = b * sb, f = P.ch_first[id];
@@ -563,6 +627,8 @@ __global__ void __launch_bounds__(kJT) jt_bwd_diag(JunctionPlanDev P, Dims d, in
   __syncthreads();
   // rows I >= col b of G_{:,col} = R^-T X: sum over K >= I of Ri[K][I] X[K][j]
   T *Y = sA + ob;
+  int32_t *codes = reinterpret_cast<int32_t *>(Y + ob);  // block (r, col), r < s
+  for (int r = t; r < s; r += kJT) codes[r] = P.poutenc[pb + int64_t(r) * s + col];
   for (int e = t; e < ob; e += kJT) {
     const int I = e / b, j = e - I * b;
     if (I < col * b) continue;
@@ -581,7 +647,7 @@ __global__ void __launch_bounds__(kJT) jt_bwd_diag(JunctionPlanDev P, Dims d, in
       dst[i * b + j] = v;
       dst[j * b + i] = v;
     } else {
-      const int32_t o = P.poutenc[pb + int64_t(r) * s + col];
+      const int32_t o = codes[r];
       T *dst = G_lower + (mat * d.nnz + (o >> 1)) * bb;
       dst[(o & 1) ? j * b + i : i * b + j] = Y[e];
     }
@@ -609,10 +675,30 @@ __global__ void __launch_bounds__(kJT) jt_finish(JunctionPlanDev P, int64_t nch,
   }
 }
 
+// Parts of the sum over x for the row tiles of a level: enough workgroups
+// to occupy the chip (about 1024) when a level has few tiles.
+int rows_split(int64_t tiles, int64_t B) {
+  const int64_t wgs = tiles * B;
+  if (wgs <= 0 || wgs >= 1024) return 1;
+  const int64_t p = (1024 + wgs - 1) / wgs;
+  return static_cast<int>(p > 8 ? 8 : p);
+}
+
+int64_t max_split_tiles(const selinv_junction_plan *plan, int64_t B) {
+  int64_t best = 0;
+  for (int32_t l = 0; l < plan->levels; ++l) {
+    const int64_t t = plan->tiles_ptr[plan->level_off[l + 1]] - plan->tiles_ptr[plan->level_off[l]];
+    const int p = rows_split(t, B);
+    if (p > 1 && t * p > best) best = t * p;
+  }
+  return best;
+}
+
 struct JtWs {
-  void *W, *RJ;
+  void *W, *RJ, *Tpart;
   double *ld;
   int32_t *info;
+  size_t bytes;
 };
 
 JtWs carve(const selinv_junction_plan *plan, int64_t B, void *ws) {
@@ -621,25 +707,21 @@ JtWs carve(const selinv_junction_plan *plan, int64_t B, void *ws) {
   JtWs w;
   w.W = cv.take<char>(B * plan->npanel * bb * es);
   w.RJ = cv.take<char>(B * plan->nrinv * bb * es);
+  w.Tpart = cv.take<char>(B * max_split_tiles(plan, B) * kTilePart * es);
   w.ld = cv.take<double>(B * plan->nch);
   w.info = cv.take<int32_t>(B);
+  w.bytes = cv.off;
   return w;
 }
 
 }  // namespace
 
 size_t junction_workspace_bytes(const selinv_junction_plan *plan, int64_t B) {
-  Carve cv(nullptr);
-  const size_t bb = size_t(plan->b) * plan->b, es = plan->dtype_bytes;
-  cv.take<char>(B * plan->npanel * bb * es);
-  cv.take<char>(B * plan->nrinv * bb * es);
-  cv.take<double>(B * plan->nch);
-  cv.take<int32_t>(B);
-  return cv.off;
+  return carve(plan, B, nullptr).bytes;
 }
 
-template <typename T>
-hipError_t junction_launch(const selinv_junction_plan *plan, int64_t B, const T *diag,
+template <typename T, int BC>
+hipError_t junction_run(const selinv_junction_plan *plan, int64_t B, const T *diag,
                            const T *edge_val, T *G_diag, T *G_lower, double *logdet,
                            int32_t *info, void *ws, hipStream_t s) {
   const int b = plan->b, sm = plan->smax;
@@ -648,9 +730,11 @@ hipError_t junction_launch(const selinv_junction_plan *plan, int64_t B, const T 
   const JtWs w = carve(plan, B, ws);
   T *W = static_cast<T *>(w.W), *RJ = static_cast<T *>(w.RJ);
   const size_t l_upd = lds_bytes<T>(b), l_fac = fac_lds<T>(b, sm), l_scl = scale_lds<T>(b, sm),
-               l_row = rows_lds<T>(b, sm), l_dia = diag_lds<T>(b, sm);
+               l_row = rows_lds<T>(b, sm), l_dia = diag_lds<T>(b, sm),
+               l_sum = sizeof(T) * (size_t(kTilePart) + size_t(sm) * b * sm * b) +
+                       4 * size_t(tile_rows(b)) * sm;
   if (l_upd > kLdsMax || l_fac > kLdsMax || l_scl > kLdsMax || l_row > kLdsMax ||
-      l_dia > kLdsMax)
+      l_dia > kLdsMax || l_sum > kLdsMax)
     return hipErrorInvalidValue;
   const auto &lo = plan->level_off;
   const auto &tp = plan->ch_tptr;
@@ -660,26 +744,46 @@ hipError_t junction_launch(const selinv_junction_plan *plan, int64_t B, const T 
   jt_init<T><<<dim3(static_cast<unsigned>((B + kJT - 1) / kJT)), blk, 0, s>>>(w.info, B);
   for (int32_t l = 0; l < plan->levels; ++l) {
     const int64_t c0 = lo[l], c1 = lo[l + 1];
-    jt_fwd_update<T><<<dim3(static_cast<unsigned>(tp[c1] - tp[c0]), By), blk, l_upd, s>>>(
+    jt_fwd_update<T, BC><<<dim3(static_cast<unsigned>(tp[c1] - tp[c0]), By), blk, l_upd, s>>>(
         P, d, tp[c0], diag, edge_val, W);
-    jt_fwd_factor<T><<<dim3(static_cast<unsigned>(c1 - c0), By), blk, l_fac, s>>>(
+    jt_fwd_factor<T, BC><<<dim3(static_cast<unsigned>(c1 - c0), By), blk, l_fac, s>>>(
         P, d, c0, W, RJ, w.ld, w.info);
     if (rp[c1] > rp[c0])
-      jt_fwd_scale<T><<<dim3(static_cast<unsigned>(rp[c1] - rp[c0]), By), blk, l_scl, s>>>(
+      jt_fwd_scale<T, BC><<<dim3(static_cast<unsigned>(rp[c1] - rp[c0]), By), blk, l_scl, s>>>(
           P, d, rp[c0], W, RJ);
   }
   for (int32_t l = plan->levels - 1; l >= 0; --l) {
     const int64_t c0 = lo[l], c1 = lo[l + 1];
     const auto &tl = plan->tiles_ptr;
-    if (tl[c1] > tl[c0])
-      jt_bwd_rows<T><<<dim3(static_cast<unsigned>(tl[c1] - tl[c0]), By), blk, l_row, s>>>(
-          P, d, tl[c0], W, RJ, G_diag, G_lower);
+    const int64_t nt = tl[c1] - tl[c0];
+    if (nt > 0) {
+      const int sp = rows_split(nt, B);
+      jt_bwd_rows<T, BC><<<dim3(static_cast<unsigned>(nt * sp), By), blk, l_row, s>>>(
+          P, d, tl[c0], sp, static_cast<T *>(w.Tpart), W, RJ, G_diag, G_lower);
+      if (sp > 1)
+        jt_bwd_rows_sum<T, BC><<<dim3(static_cast<unsigned>(nt), By), blk, l_sum, s>>>(
+            P, d, tl[c0], sp, static_cast<const T *>(w.Tpart), RJ, G_lower);
+    }
     const int64_t f0 = plan->ch_cptr[c0], f1 = plan->ch_cptr[c1];
-    jt_bwd_diag<T><<<dim3(static_cast<unsigned>(f1 - f0), By), blk, l_dia, s>>>(
+    jt_bwd_diag<T, BC><<<dim3(static_cast<unsigned>(f1 - f0), By), blk, l_dia, s>>>(
         P, d, f0, W, RJ, G_diag, G_lower);
   }
   jt_finish<T><<<dim3(By), blk, 0, s>>>(P, plan->nch, w.ld, w.info, logdet, info);
   return hipGetLastError();
+}
+
+// Compile-time block sizes for the common b (fully unrolled inner loops),
+// the runtime b otherwise
+template <typename T>
+hipError_t junction_launch(const selinv_junction_plan *plan, int64_t B, const T *diag,
+                           const T *edge_val, T *G_diag, T *G_lower, double *logdet,
+                           int32_t *info, void *ws, hipStream_t s) {
+  switch (plan->b) {
+    case 4: return junction_run<T, 4>(plan, B, diag, edge_val, G_diag, G_lower, logdet, info, ws, s);
+    case 8: return junction_run<T, 8>(plan, B, diag, edge_val, G_diag, G_lower, logdet, info, ws, s);
+    case 16: return junction_run<T, 16>(plan, B, diag, edge_val, G_diag, G_lower, logdet, info, ws, s);
+    default: return junction_run<T, 0>(plan, B, diag, edge_val, G_diag, G_lower, logdet, info, ws, s);
+  }
 }
 
 template hipError_t junction_launch<double>(const selinv_junction_plan *, int64_t, const double *,
