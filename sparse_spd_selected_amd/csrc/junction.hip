@@ -207,7 +207,7 @@ __host__ __device__ inline int diag_pairs(int b, int s) {
 template <typename T>
 size_t fac_lds(int b, int sm) {
   const size_t sb = size_t(sm) * b;
-  return sizeof(T) * 2 * sb * sb;
+  return sizeof(T) * (2 * sb * sb + sb * b);
 }
 template <typename T>
 size_t scale_lds(int b, int sm) {
@@ -262,38 +262,65 @@ __device__ inline void gather_lds(T *dst, int tot, F src) {
   }
 }
 
-// S (LDS, n x n; lower triangle read) = R R^T: R overwrites the lower
-// triangle of S and Rinv (LDS) receives R^-1 (lower, zero above).  Returns
-// 0, or 1 + the first column whose pivot is not > 0 (NaN included),
-// uniformly; *logdet = ln det S.
+// S (LDS, n x n with n = s b; lower triangle read) = R R^T: R overwrites
+// the lower triangle of S, and X (LDS) receives R^-1 (lower, zero above);
+// tmp is LDS scratch of n b entries.  Returns 0, or 1 + the first column
+// whose pivot is not > 0 (NaN included), uniformly; *logdet = ln det S.
+// Cholesky: right-looking on unscaled columns, one barrier per column
+// (S_il -= S_ij S_lj / d_j for j < l <= i), scaled at the end.  Inverse:
+// block forward substitution with b x b blocks -- the diagonal blocks'
+// inverses, then one block diagonal of R^-1 at a time,
+// X_ik = -X_ii sum_{k <= q < i} R_iq X_qk.
 template <typename T>
-__device__ inline int chol_inverse(T *S, T *Rinv, int n, double *logdet) {
-  const int t = threadIdx.x;
-  double ld = 0.0;
+__device__ inline int chol_inverse(T *S, T *X, T *tmp, int n, int b, double *logdet) {
+  const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
   for (int j = 0; j < n; ++j) {
-    const T d = S[j * n + j];
-    if (!(d > T(0))) return j + 1;
-    ld += log(static_cast<double>(d));
-    const T r = sqrt(d);
-    for (int i = j + 1 + t; i < n; i += kJT) S[i * n + j] /= r;
-    __syncthreads();
-    const int rem = n - j - 1;
-    for (int e = t; e < rem * rem; e += kJT) {
-      const int i = j + 1 + e / rem, l = j + 1 + e % rem;
-      if (l <= i) S[i * n + l] -= S[i * n + j] * S[l * n + j];
+    const T dj = S[j * n + j];
+    if (!(dj > T(0))) return j + 1;
+    const T inv = T(1) / dj;
+    for (int i = j + 1 + ty; i < n; i += 16) {
+      const T sij = S[i * n + j] * inv;
+      for (int l = j + 1 + tx; l <= i; l += 16) S[i * n + l] -= sij * S[l * n + j];
     }
     __syncthreads();
   }
+  double ld = 0.0;
+  for (int j = 0; j < n; ++j) ld += log(static_cast<double>(S[j * n + j]));
+  for (int e = t; e < n * n; e += kJT) {
+    const int i = e / n, j = e - i * n;
+    if (i > j) S[e] /= sqrt(S[j * n + j]);
+    X[e] = T(0);
+  }
+  __syncthreads();
   for (int j = t; j < n; j += kJT) S[j * n + j] = sqrt(S[j * n + j]);
   __syncthreads();
-  for (int c = t; c < n; c += kJT) {  // R X = I, one column of X per thread
-    for (int i = 0; i < n; ++i) {
-      T s = i == c ? T(1) : T(0);
-      for (int k = c; k < i; ++k) s -= S[i * n + k] * Rinv[k * n + c];
-      Rinv[i * n + c] = i < c ? T(0) : s / S[i * n + i];
+  const int bb = b * b, s = n / b;
+  for (int kc = t; kc < n; kc += kJT) {  // diagonal blocks, one column each
+    const int o = (kc / b) * b, c = kc - o;
+    for (int r = c; r < b; ++r) {
+      T v = r == c ? T(1) : T(0);
+      for (int u = c; u < r; ++u) v -= S[(o + r) * n + o + u] * X[(o + u) * n + o + c];
+      X[(o + r) * n + o + c] = v / S[(o + r) * n + o + r];
     }
   }
   __syncthreads();
+  for (int m = 1; m < s; ++m) {
+    const int cnt = (s - m) * bb;
+    for (int e = t; e < cnt; e += kJT) {
+      const int k = e / bb, rem = e - k * bb, r = rem / b, c = rem - r * b, i0 = (k + m) * b;
+      T v = T(0);
+      for (int K = k * b; K < i0; ++K) v += S[(i0 + r) * n + K] * X[K * n + k * b + c];
+      tmp[e] = v;
+    }
+    __syncthreads();
+    for (int e = t; e < cnt; e += kJT) {
+      const int k = e / bb, rem = e - k * bb, r = rem / b, c = rem - r * b, i0 = (k + m) * b;
+      T v = T(0);
+      for (int u = 0; u <= r; ++u) v += X[(i0 + r) * n + i0 + u] * tmp[k * bb + u * b + c];
+      X[(i0 + r) * n + k * b + c] = -v;
+    }
+    __syncthreads();
+  }
   *logdet = ld;
   return 0;
 }
@@ -356,7 +383,7 @@ __global__ void __launch_bounds__(kJT) jt_fwd_factor(JunctionPlanDev P, Dims d, 
   const int b = BC ? BC : d.b, bb = b * b;
   const int64_t id = cbase + blockIdx.x, mat = blockIdx.y;
   const int s = P.ch_s[id], sb = s * b;
-  T *X = M + sb * sb;
+  T *X = M + sb * sb;  // then n b entries of scratch
   const T *Wp = W + (mat * d.npanel + P.ch_pbase[id]) * bb;
   gather_lds(M, sb * sb, [&](int e) {
     const int I = e / sb, J = e - I * sb;
@@ -364,7 +391,7 @@ __global__ void __launch_bounds__(kJT) jt_fwd_factor(JunctionPlanDev P, Dims d, 
   });
   __syncthreads();
   double ld = 0.0;
-  const int fail = chol_inverse(M, X, sb, &ld);
+  const int fail = chol_inverse(M, X, X + sb * sb, sb, b, &ld);
   if (fail) wg::fill(X, sb * sb, wg::qnan<T>());
   T *Rout = RJ + (mat * d.nrinv + P.ch_rbase[id]) * bb;
   for (int e = threadIdx.x; e < sb * sb; e += kJT) Rout[e] = X[e];
