@@ -587,10 +587,25 @@ __global__ void __launch_bounds__(kJT) jt_bwd_rows_sum(JunctionPlanDev P, Dims d
   const int nr = P.ch_n[id], sb = P.ch_s[id] * b;
   const int rows = nr - a0 < R ? nr - a0 : R;
   const T *src = Tpart + (mat * int64_t(gridDim.x) * nsplit + tl * nsplit) * int64_t(kTilePart);
-  for (int e = threadIdx.x; e < H * sb; e += kJT) {
-    T v = T(0);
-    for (int p = 0; p < nsplit; ++p) v += src[p * int64_t(kTilePart) + e];
-    Tt[e] = v;
+  // each thread owns at most 12 entries (H sb <= 3072): one batch of loads
+  // per part, added in part order
+  T v[12];
+#pragma unroll
+  for (int u = 0; u < 12; ++u) v[u] = T(0);
+  for (int p = 0; p < nsplit; ++p) {
+    T x[12];
+#pragma unroll
+    for (int u = 0; u < 12; ++u) {
+      const int e = threadIdx.x + u * kJT;
+      x[u] = e < H * sb ? src[p * int64_t(kTilePart) + e] : T(0);
+    }
+#pragma unroll
+    for (int u = 0; u < 12; ++u) v[u] += x[u];
+  }
+#pragma unroll
+  for (int u = 0; u < 12; ++u) {
+    const int e = threadIdx.x + u * kJT;
+    if (e < H * sb) Tt[e] = v[u];
   }
   // (rows_epilogue's first gather is followed by a barrier before Tt is read)
   rows_epilogue<BC>(P, d, mat, id, a0, rows, Tt, Tt + H * sb, RJ, G_lower);
