@@ -258,6 +258,10 @@ hipError_t junction_launch(const selinv_junction_plan *plan, int64_t B, const T 
 
 // ------------------------------------ non-symmetric ladder (nonsym.hip)
 size_t bidiag_workspace_bytes(int64_t B);
+// b = 16: one wavefront per matrix on the matrix cores (bidiag_b16.hip)
+template <typename T>
+hipError_t bidiag16_launch(int64_t B, int64_t L, const T *diag, const T *lower, T *G_diag,
+                           T *G_lower, int32_t *info, hipStream_t s);
 template <typename T>
 hipError_t bidiag_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower,
                          T *G_diag, T *G_lower, int32_t *info, void *ws, hipStream_t s);

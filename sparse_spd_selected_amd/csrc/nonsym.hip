@@ -181,6 +181,7 @@ template <typename T>
 hipError_t bidiag_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower,
                          T *G_diag, T *G_lower, int32_t *info, void *ws, hipStream_t s) {
   if (B == 0) return hipSuccess;
+  if (b == 16) return bidiag16_launch<T>(B, L, diag, lower, G_diag, G_lower, info, s);
   int32_t *first_fail = static_cast<int32_t *>(ws);
   const int nt = ns_threads(b);
   const size_t bb = static_cast<size_t>(b) * b;

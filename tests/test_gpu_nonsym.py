@@ -67,7 +67,7 @@ def run_bidiag(ssa, B, L, b, dt, seed):
 
 @pytest.mark.parametrize("dt", ["f64", "f32"])
 @pytest.mark.parametrize("B,L,b", [(1, 1, 3), (2, 2, 1), (3, 9, 4), (2, 12, 16), (2, 5, 32),
-                                   (4, 7, 5)])
+                                   (4, 7, 5), (3, 1, 16), (2, 2, 16), (5, 13, 16)])
 def test_bidiag_small(ssa, B, L, b, dt):
     run_bidiag(ssa, B, L, b, DT[dt], seed=B + L + b)
 
@@ -85,6 +85,20 @@ def test_bidiag_breakdown(ssa):
     torch.cuda.synchronize()
     assert list(info.cpu().numpy()) == [0, 5, 0]
     assert torch.isnan(Gd[1]).all() and torch.isnan(Gl[1]).all() and torch.isfinite(Gd[0]).all()
+
+
+@pytest.mark.parametrize("dt", ["f64", "f32"])
+def test_bidiag_breakdown_b16(ssa, dt):
+    """The b = 16 matrix-core kernel reports the first failing block and
+    poisons only that matrix."""
+    d, l = spdgen.nonsym_bidiag(3, 7, 16, seed=4)
+    d[1, 5] = 0.0
+    d[1, 6] = 0.0
+    Gd, Gl, info = ssa.bidiag(_to(d, DT[dt]), _to(l, DT[dt]), return_info=True)
+    torch.cuda.synchronize()
+    assert list(info.cpu().numpy()) == [0, 6, 0]
+    assert torch.isnan(Gd[1]).all() and torch.isnan(Gl[1]).all()
+    assert torch.isfinite(Gd[0]).all() and torch.isfinite(Gl[2]).all()
 
 
 def _perm_tree(n, seed):
