@@ -30,7 +30,7 @@ SOURCES = [
     "vjp_generic.hip", "vjp_chain_b16.hip", "vjp_star_b32.hip",
     "vjp_tree_b8.hip", "vjp_chain_seg.hip",
     "shared_factor.hip",
-    "nonsym.hip", "bidiag_b16.hip", "junction_plan.cpp", "junction.hip",
+    "nonsym.hip", "bidiag_b16.hip", "nonsym_b8.hip", "junction_plan.cpp", "junction.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

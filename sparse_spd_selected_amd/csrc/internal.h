@@ -266,6 +266,11 @@ template <typename T>
 hipError_t bidiag_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower,
                          T *G_diag, T *G_lower, int32_t *info, void *ws, hipStream_t s);
 size_t nonsym_tree_workspace_bytes(const selinv_tree_plan *plan);
+// b <= 8: one block row per lane, eight nodes per wavefront (nonsym_b8.hip)
+size_t nstree8_workspace_bytes(const selinv_tree_plan *plan);
+template <typename T>
+hipError_t nstree8_launch(const selinv_tree_plan *plan, const T *diag, const T *up, const T *down,
+                          T *G_diag, T *G_up, T *G_down, int32_t *info, void *ws, hipStream_t s);
 template <typename T>
 hipError_t nonsym_tree_launch(const selinv_tree_plan *plan, const T *diag, const T *up,
                               const T *down, T *G_diag, T *G_up, T *G_down, int32_t *info,

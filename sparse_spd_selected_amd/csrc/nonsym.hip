@@ -196,6 +196,7 @@ hipError_t bidiag_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T
 }
 
 size_t nonsym_tree_workspace_bytes(const selinv_tree_plan *plan) {
+  if (plan->b <= 8) return nstree8_workspace_bytes(plan);
   const size_t n = plan->n, bb = static_cast<size_t>(plan->b) * plan->b;
   return 2 * align_up(n * bb * plan->dtype_bytes) + align_up(n * sizeof(int32_t)) +
          align_up(sizeof(int32_t));
@@ -205,6 +206,8 @@ template <typename T>
 hipError_t nonsym_tree_launch(const selinv_tree_plan *plan, const T *diag, const T *up,
                               const T *down, T *G_diag, T *G_up, T *G_down, int32_t *info,
                               void *ws, hipStream_t s) {
+  if (plan->b <= 8)
+    return nstree8_launch<T>(plan, diag, up, down, G_diag, G_up, G_down, info, ws, s);
   const size_t n = plan->n;
   const int b = plan->b;
   const size_t bb = static_cast<size_t>(b) * b;
