@@ -4,15 +4,45 @@
 //
 // Every function starts from synchronised LDS and ends with __syncthreads(),
 // so calls can be chained without extra barriers.
+//
+// With b = 32 and 256 threads the products run on the matrix cores: each of
+// the four wavefronts forms one 16 x 16 quadrant of the result with eight
+// 16x16x4 MFMA steps, reading its operands straight from the row-major
+// blocks (frag16.h gives the operand and result layouts), and the SPD inverse
+// is the register-resident blocked Gauss-Jordan of frag32.h on one wavefront.
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include "frag32.h"
 
 namespace selinv {
 namespace wg {
 
 __device__ inline int tid() { return threadIdx.x; }
 __device__ inline int nthreads() { return blockDim.x; }
+
+// the b = 32 matrix-core path applies
+__device__ inline bool mfma32(int b) { return b == 32 && blockDim.x == 256; }
+
+// Quadrant (I, J) of op(A) op(B) for 32 x 32 row-major A, B (op = transpose
+// when TA / TB), in the MFMA result layout: lane (g, j) register r holds
+// entry (16 I + row(g, r), 16 J + j).  Step s of the 16x16x4 product takes
+// lane l's A operand op(A)[16 I + l % 16][4 s + l / 16] and its B operand
+// op(B)[4 s + l / 16][16 J + l % 16].
+template <typename T, bool TA, bool TB>
+__device__ __forceinline__ f16::Frag<T> quad32(const T *A, const T *B, int I, int J, int lane) {
+  const int i = lane & 15, kk = lane >> 4, r = 16 * I + i, c = 16 * J + i;
+  f16::Frag<T> acc = f16::zero<T>();
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int k = 4 * s + kk;
+    const T a = TA ? A[k * 32 + r] : A[r * 32 + k];
+    const T x = TB ? B[c * 32 + k] : B[k * 32 + c];
+    acc = f16::Mfma<T>::op(a, x, acc);
+  }
+  return acc;
+}
 
 template <typename T>
 __device__ inline T qnan() {
@@ -56,6 +86,15 @@ __device__ inline void fill(T *dst, int bb, T v) {
 // Out = op(A) op(B), op = transpose when TA/TB.  Out must not alias A or B.
 template <typename T, bool TA, bool TB>
 __device__ inline void gemm(T *Out, const T *A, const T *B, int b) {
+  if (mfma32(b)) {
+    const int w = tid() >> 6, lane = tid() & 63, I = w >> 1, J = w & 1;
+    const f16::Frag<T> p = quad32<T, TA, TB>(A, B, I, J, lane);
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Out[(16 * I + f16::row<T>(g, r)) * 32 + 16 * J + j] = p[r];
+    __syncthreads();
+    return;
+  }
   for (int e = tid(); e < b * b; e += nthreads()) {
     const int r = e / b, c = e % b;
     T acc = T(0);
@@ -74,6 +113,23 @@ __device__ inline void gemm(T *Out, const T *A, const T *B, int b) {
 // exact arithmetic).  Base may be null (taken as 0) and may alias Out.
 template <typename T, bool TA, bool TB>
 __device__ inline void gemm_sym(T *Out, const T *Base, const T *A, const T *B, int b, T sign) {
+  if (mfma32(b)) {  // quadrants on and below the diagonal
+    const int w = tid() >> 6, lane = tid() & 63, I = w >> 1, J = w & 1;
+    if (I >= J) {
+      const f16::Frag<T> p = quad32<T, TA, TB>(A, B, I, J, lane);
+      const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 16 * I + f16::row<T>(g, q), c = 16 * J + j;
+        if (r < c) continue;
+        const T v = (Base ? Base[r * 32 + c] : T(0)) + sign * p[q];
+        Out[r * 32 + c] = v;
+        Out[c * 32 + r] = v;
+      }
+    }
+    __syncthreads();
+    return;
+  }
   for (int e = tid(); e < b * b; e += nthreads()) {
     const int r = e / b, c = e % b;
     if (r < c) continue;
@@ -105,6 +161,18 @@ __device__ inline void sym_part(T *dst, const T *src, int b) {
 template <typename T, bool TA, bool TB>
 __device__ inline void gemm_axpby(T *Out, T beta, const T *Base, T alpha, const T *A, const T *B,
                                   int b) {
+  if (mfma32(b)) {
+    const int w = tid() >> 6, lane = tid() & 63, I = w >> 1, J = w & 1;
+    const f16::Frag<T> p = quad32<T, TA, TB>(A, B, I, J, lane);
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = (16 * I + f16::row<T>(g, q)) * 32 + 16 * J + j;
+      Out[e] = beta * Base[e] + alpha * p[q];
+    }
+    __syncthreads();
+    return;
+  }
   for (int e = tid(); e < b * b; e += nthreads()) {
     const int r = e / b, c = e % b;
     T acc = T(0);
@@ -124,6 +192,25 @@ __device__ inline void gemm_axpby(T *Out, T beta, const T *Base, T alpha, const 
 template <typename T, bool TA, bool TB>
 __device__ inline void gemm_symmetrized(T *Out, const T *Base, const T *A, const T *B, int b,
                                         T sign) {
+  if (mfma32(b)) {
+    // quadrant (I, J) of P and of P^T = op(B)^T op(A)^T, on and below the diagonal
+    const int w = tid() >> 6, lane = tid() & 63, I = w >> 1, J = w & 1;
+    if (I >= J) {
+      const f16::Frag<T> p = quad32<T, TA, TB>(A, B, I, J, lane);
+      const f16::Frag<T> pt = quad32<T, !TB, !TA>(B, A, I, J, lane);
+      const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 16 * I + f16::row<T>(g, q), c = 16 * J + j;
+        if (r < c) continue;
+        const T v = (Base ? Base[r * 32 + c] : T(0)) + sign * (T(0.5) * (p[q] + pt[q]));
+        Out[r * 32 + c] = v;
+        Out[c * 32 + r] = v;
+      }
+    }
+    __syncthreads();
+    return;
+  }
   for (int e = tid(); e < b * b; e += nthreads()) {
     const int r = e / b, c = e % b;
     if (r < c) continue;
@@ -252,6 +339,26 @@ __device__ inline int gen_inverse(T *A, int b, T *rowk, T *colk) {
 // is NaN; then A holds garbage.  *logdet receives sum ln d (float64).
 template <typename T>
 __device__ inline int spd_inverse(T *A, int b, T *col, double *logdet) {
+  if (mfma32(b)) {  // one wavefront, blocked Gauss-Jordan in registers (frag32.h)
+    __shared__ int s_bad;
+    __shared__ double s_ld;
+    if (tid() < 64) {
+      const int lane = tid(), g = lane >> 4, j = lane & 15;
+      f32t::Blk<T> a = f32t::load(A, g, j);
+      f16::PivotLog pl;
+      const bool bad = f32t::gj_inverse(a, col, g, j, pl);
+      f32t::store(A, a, g, j);
+      if (lane == 0) {
+        s_bad = bad ? 1 : 0;
+        s_ld = pl.log();
+      }
+    }
+    __syncthreads();
+    *logdet = s_ld;
+    const int bad = s_bad;
+    __syncthreads();
+    return bad;
+  }
   double ld = 0.0;
   for (int k = 0; k < b; ++k) {
     const T d = A[k * b + k];
