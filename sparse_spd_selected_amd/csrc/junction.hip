@@ -372,6 +372,83 @@ __global__ void __launch_bounds__(kJT) jt_fwd_update(JunctionPlanDev P, Dims d, 
   }
 }
 
+// Schur sums for b <= 8 (bb <= 64): one wavefront per panel block, four per
+// workgroup, no workgroup barrier.  Lane e owns entry e of the b x b sum
+// (b = 8) or, for smaller b, the 64 / bb lane groups take every
+// (64 / bb)-th pair and are added at the end.  Each round stages up to
+// 512 / bb pairs of blocks through the wavefront's LDS.
+template <typename T, int BC>
+__global__ void __launch_bounds__(kJT) jt_fwd_update_wave(JunctionPlanDev P, Dims d,
+                                                          int64_t tbase, int64_t tend,
+                                                          const T *__restrict__ diag,
+                                                          const T *__restrict__ edge_val, T *W) {
+  constexpr int b = BC, bb = b * b, CH = (512 / bb) > 32 ? 32 : 512 / bb, G = 64 / bb;
+  constexpr int NL = CH * bb / 64;  // staged elements per lane and operand
+  __shared__ __align__(16) T sa[4][CH * bb];
+  __shared__ __align__(16) T sb[4][CH * bb];
+  __shared__ int32_t tab[4][2 * CH];
+  __shared__ T red[4][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t tg = tbase + int64_t(blockIdx.x) * 4 + wave, mat = blockIdx.y;
+  if (tg >= tend) return;
+  const int id = P.tg_chunk[tg], rc = P.tg_rc[tg], r = rc >> 6, col = rc & 63;
+  const int32_t f0 = P.fptr[tg], f1 = P.fptr[tg + 1];
+  const T *Wm = W + mat * d.npanel * bb;
+  const int grp = lane / bb, e = lane - grp * bb, er = e / b, ec = e - er * b;
+  T acc = T(0);
+  for (int32_t q0 = f0; q0 < f1; q0 += CH) {
+    const int cnt = f1 - q0 < CH ? f1 - q0 : CH;
+    if (lane < 2 * cnt) tab[wave][lane] = P.fpair[2 * int64_t(q0) + lane];
+    f16::wave_sync();
+    T va[NL], vb[NL];
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int idx = lane + 64 * u, q = idx / bb, el = idx - q * bb;
+      if (q < cnt) {
+        va[u] = Wm[int64_t(tab[wave][2 * q]) * bb + el];
+        vb[u] = Wm[int64_t(tab[wave][2 * q + 1]) * bb + el];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int idx = lane + 64 * u;
+      if (idx / bb < cnt) {
+        sa[wave][idx] = va[u];
+        sb[wave][idx] = vb[u];
+      }
+    }
+    f16::wave_sync();
+    if (grp < G)
+      for (int q = grp; q < cnt; q += G) {
+        const T *A = sa[wave] + q * bb + er * b, *Bq = sb[wave] + q * bb + ec * b;
+#pragma unroll
+        for (int k = 0; k < b; ++k) acc += A[k] * Bq[k];
+      }
+    f16::wave_sync();
+  }
+  if (G > 1) {
+    red[wave][lane] = acc;
+    f16::wave_sync();
+    if (lane < bb) {
+      T v = T(0);
+      for (int gg = 0; gg < G; ++gg) v += red[wave][gg * bb + lane];
+      acc = v;
+    }
+  }
+  if (lane >= bb) return;
+  const int32_t enc = P.ain[tg];
+  T *dst = W + (mat * d.npanel + P.ch_pbase[id] + int64_t(r) * P.ch_s[id] + col) * bb;
+  T base;
+  if (r == col) {
+    const T *D = diag + (mat * d.n + enc) * bb;
+    base = er >= ec ? D[er * b + ec] : D[ec * b + er];
+  } else {
+    const T *E = enc < 0 ? nullptr : edge_val + (mat * d.m + (enc >> 1)) * bb;
+    base = E ? ((enc & 1) ? E[ec * b + er] : E[e]) : T(0);
+  }
+  dst[e] = base - acc;
+}
+
 // Dense pivot of every chunk of the level: R_J^-1 (into RJ), the log det
 // term, the first failing column
 template <typename T, int BC>
@@ -786,8 +863,14 @@ hipError_t junction_run(const selinv_junction_plan *plan, int64_t B, const T *di
   jt_init<T><<<dim3(static_cast<unsigned>((B + kJT - 1) / kJT)), blk, 0, s>>>(w.info, B);
   for (int32_t l = 0; l < plan->levels; ++l) {
     const int64_t c0 = lo[l], c1 = lo[l + 1];
-    jt_fwd_update<T, BC><<<dim3(static_cast<unsigned>(tp[c1] - tp[c0]), By), blk, l_upd, s>>>(
-        P, d, tp[c0], diag, edge_val, W);
+    if constexpr (BC == 4 || BC == 8) {
+      const int64_t nt = tp[c1] - tp[c0];
+      jt_fwd_update_wave<T, BC><<<dim3(static_cast<unsigned>((nt + 3) / 4), By), blk, 0, s>>>(
+          P, d, tp[c0], tp[c1], diag, edge_val, W);
+    } else {
+      jt_fwd_update<T, BC><<<dim3(static_cast<unsigned>(tp[c1] - tp[c0]), By), blk, l_upd, s>>>(
+          P, d, tp[c0], diag, edge_val, W);
+    }
     jt_fwd_factor<T, BC><<<dim3(static_cast<unsigned>(c1 - c0), By), blk, l_fac, s>>>(
         P, d, c0, W, RJ, w.ld, w.info);
     if (rp[c1] > rp[c0])
