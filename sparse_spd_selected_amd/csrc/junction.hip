@@ -688,30 +688,76 @@ __global__ void __launch_bounds__(kJT) jt_bwd_rows_sum(JunctionPlanDev P, Dims d
   rows_epilogue<BC>(P, d, mat, id, a0, rows, Tt, Tt + H * sb, RJ, G_lower);
 }
 
+// Epilogue of a chunk block column: X (LDS, sb x b) = (R_J^-1 - W^T G)_{:,col}
+// is mapped to G_{J,col} = R_J^-T X; the blocks on and below the diagonal are
+// written (the diagonal block symmetrised).  Y is LDS scratch of sb b entries
+// followed by room for s codes.
+template <int BC, typename T>
+__device__ inline void diag_epilogue(const JunctionPlanDev &P, const Dims &d, int64_t mat, int id,
+                                     int col, const T *Ri, const T *X, T *Y, T *G_diag,
+                                     T *G_lower) {
+  const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
+  const int s = P.ch_s[id], sb = s * b, ob = sb * b, f = P.ch_first[id];
+  const int64_t pb = P.ch_pbase[id];
+  int32_t *codes = reinterpret_cast<int32_t *>(Y + ob);  // block (r, col), r < s
+  for (int r = t; r < s; r += kJT) codes[r] = P.poutenc[pb + int64_t(r) * s + col];
+  // rows I >= col b: sum over K >= I of Ri[K][I] X[K][j]
+  for (int e = t; e < ob; e += kJT) {
+    const int I = e / b, j = e - I * b;
+    if (I < col * b) continue;
+    T y = T(0);
+    for (int K = I; K < sb; ++K) y += Ri[K * sb + I] * X[K * b + j];
+    Y[e] = y;
+  }
+  __syncthreads();
+  for (int e = t; e < ob; e += kJT) {
+    const int I = e / b, j = e - I * b, r = I / b, i = I - r * b;
+    if (r < col) continue;
+    if (r == col) {
+      if (i < j) continue;
+      const T v = T(0.5) * (Y[I * b + j] + Y[(col * b + j) * b + i]);
+      T *dst = G_diag + (mat * d.n + P.order[f + r]) * bb;
+      dst[i * b + j] = v;
+      dst[j * b + i] = v;
+    } else {
+      const int32_t o = codes[r];
+      T *dst = G_lower + (mat * d.nnz + (o >> 1)) * bb;
+      dst[(o & 1) ? j * b + i : i * b + j] = Y[e];
+    }
+  }
+}
+
+// Partial sums of a split block column: kDiagPart entries per (column, part)
+constexpr int kDiagPart = 48 * 32;
+
 // The chunk's own blocks, one workgroup per block column col of the chunk:
-// G_{J,col} = R_J^-T (R_J^-1 - W_{N,J}^T G_{N,J})_{:,col}; the blocks on and
-// below the diagonal are written (the diagonal block symmetrised).
+// G_{J,col} = R_J^-T (R_J^-1 - W_{N,J}^T G_{N,J})_{:,col}.  On levels with
+// few columns the sum over the later rows is split into nsplit parts whose
+// partial sums go to Dpart; jt_bwd_diag_sum finishes those columns.
 template <typename T, int BC>
 __global__ void __launch_bounds__(kJT) jt_bwd_diag(JunctionPlanDev P, Dims d, int64_t fcbase,
+                                                   int nsplit, T *Dpart,
                                                    const T *__restrict__ W,
                                                    const T *__restrict__ RJ, T *G_diag,
                                                    T *G_lower) {
   extern __shared__ char smem_raw[];
   T *Ri = reinterpret_cast<T *>(smem_raw);
   const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
-  const int64_t fc = fcbase + blockIdx.x, mat = blockIdx.y;
+  const int64_t fcl = blockIdx.x / nsplit, mat = blockIdx.y;
+  const int part = blockIdx.x - static_cast<int>(fcl) * nsplit;
+  const int64_t fc = fcbase + fcl;
   const int id = P.col_chunk[fc], col = static_cast<int>(fc - P.ch_cptr[id]);
-  const int s = P.ch_s[id], nr = P.ch_n[id], sb = s * b, wr = b * sb, f = P.ch_first[id];
+  const int s = P.ch_s[id], nr = P.ch_n[id], sb = s * b, wr = b * sb;
   const int CH = diag_pairs(b, s), ob = sb * b;  // output: sb x b
   T *sA = Ri + sb * sb, *sB = sA + CH * wr;
   const int64_t pb = P.ch_pbase[id];
   const T *Wp = W + (mat * d.npanel + pb) * bb;
   const T *Gl = G_lower + mat * d.nnz * bb;
-  gather_lds(Ri, sb * sb, [&](int e) { return RJ[(mat * d.nrinv + P.ch_rbase[id]) * bb + e]; });
-  __syncthreads();  // Ri is read below even when the chunk has no later rows
+  const int qlo = static_cast<int>(int64_t(nr) * part / nsplit);
+  const int qhi = static_cast<int>(int64_t(nr) * (part + 1) / nsplit);
   T acc[6] = {T(0), T(0), T(0), T(0), T(0), T(0)};
-  for (int q0 = 0; q0 < nr; q0 += CH) {
-    const int cnt = nr - q0 < CH ? nr - q0 : CH;
+  for (int q0 = qlo; q0 < qhi; q0 += CH) {
+    const int cnt = qhi - q0 < CH ? qhi - q0 : CH;
     // W_{x_q,J} as dense b x sb rows; G_{x_q, f+col} blocks
     gather_lds(sA, cnt * wr, [&](int e) {
       const int q = e / wr, rem = e - q * wr, k = rem / sb, cc = rem - k * sb;
@@ -736,6 +782,16 @@ __global__ void __launch_bounds__(kJT) jt_bwd_diag(JunctionPlanDev P, Dims d, in
     }
     __syncthreads();
   }
+  if (nsplit > 1) {
+    T *dst = Dpart + (mat * gridDim.x + blockIdx.x) * int64_t(kDiagPart);
+    for (int u = 0; u < 6; ++u) {
+      const int e = t + u * kJT;
+      if (e < ob) dst[e] = acc[u];
+    }
+    return;
+  }
+  gather_lds(Ri, sb * sb, [&](int e) { return RJ[(mat * d.nrinv + P.ch_rbase[id]) * bb + e]; });
+  __syncthreads();
   T *X = sA;  // sb x b column block of R^-1 - W^T G
   for (int u = 0; u < 6; ++u) {
     const int e = t + u * kJT;
@@ -744,33 +800,46 @@ __global__ void __launch_bounds__(kJT) jt_bwd_diag(JunctionPlanDev P, Dims d, in
     X[e] = Ri[I * sb + col * b + j] - acc[u];
   }
   __syncthreads();
-  // rows I >= col b of G_{:,col} = R^-T X: sum over K >= I of Ri[K][I] X[K][j]
-  T *Y = sA + ob;
-  int32_t *codes = reinterpret_cast<int32_t *>(Y + ob);  // block (r, col), r < s
-  for (int r = t; r < s; r += kJT) codes[r] = P.poutenc[pb + int64_t(r) * s + col];
-  for (int e = t; e < ob; e += kJT) {
-    const int I = e / b, j = e - I * b;
-    if (I < col * b) continue;
-    T y = T(0);
-    for (int K = I; K < sb; ++K) y += Ri[K * sb + I] * X[K * b + j];
-    Y[e] = y;
+  diag_epilogue<BC>(P, d, mat, id, col, Ri, X, sA + ob, G_diag, G_lower);
+}
+
+// Split block columns: the parts added in a fixed order, then the epilogue
+template <typename T, int BC>
+__global__ void __launch_bounds__(kJT) jt_bwd_diag_sum(JunctionPlanDev P, Dims d, int64_t fcbase,
+                                                       int nsplit, const T *Dpart,
+                                                       const T *__restrict__ RJ, T *G_diag,
+                                                       T *G_lower) {
+  extern __shared__ char smem_raw[];
+  T *Ri = reinterpret_cast<T *>(smem_raw);
+  const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
+  const int64_t fcl = blockIdx.x, mat = blockIdx.y, fc = fcbase + fcl;
+  const int id = P.col_chunk[fc], col = static_cast<int>(fc - P.ch_cptr[id]);
+  const int sb = P.ch_s[id] * b, ob = sb * b;
+  T *X = Ri + sb * sb;
+  const T *src = Dpart + (mat * int64_t(gridDim.x) * nsplit + fcl * nsplit) * int64_t(kDiagPart);
+  T v[6] = {T(0), T(0), T(0), T(0), T(0), T(0)};
+  for (int p = 0; p < nsplit; ++p) {
+    T x[6];
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+      const int e = t + u * kJT;
+      x[u] = e < ob ? src[p * int64_t(kDiagPart) + e] : T(0);
+    }
+#pragma unroll
+    for (int u = 0; u < 6; ++u) v[u] += x[u];
   }
+  gather_lds(Ri, sb * sb, [&](int e) { return RJ[(mat * d.nrinv + P.ch_rbase[id]) * bb + e]; });
   __syncthreads();
-  for (int e = t; e < ob; e += kJT) {
-    const int I = e / b, j = e - I * b, r = I / b, i = I - r * b;
-    if (r < col) continue;
-    if (r == col) {
-      if (i < j) continue;
-      const T v = T(0.5) * (Y[I * b + j] + Y[(col * b + j) * b + i]);
-      T *dst = G_diag + (mat * d.n + P.order[f + r]) * bb;
-      dst[i * b + j] = v;
-      dst[j * b + i] = v;
-    } else {
-      const int32_t o = codes[r];
-      T *dst = G_lower + (mat * d.nnz + (o >> 1)) * bb;
-      dst[(o & 1) ? j * b + i : i * b + j] = Y[e];
+#pragma unroll
+  for (int u = 0; u < 6; ++u) {
+    const int e = t + u * kJT;
+    if (e < ob) {
+      const int I = e / b, j = e - I * b;
+      X[e] = Ri[I * sb + col * b + j] - v[u];
     }
   }
+  __syncthreads();
+  diag_epilogue<BC>(P, d, mat, id, col, Ri, X, X + ob, G_diag, G_lower);
 }
 
 template <typename T>
@@ -803,6 +872,16 @@ int rows_split(int64_t tiles, int64_t B) {
   return static_cast<int>(p > 8 ? 8 : p);
 }
 
+int64_t max_split_cols(const selinv_junction_plan *plan, int64_t B) {
+  int64_t best = 0;
+  for (int32_t l = 0; l < plan->levels; ++l) {
+    const int64_t c = plan->ch_cptr[plan->level_off[l + 1]] - plan->ch_cptr[plan->level_off[l]];
+    const int p = rows_split(c, B);
+    if (p > 1 && c * p > best) best = c * p;
+  }
+  return best;
+}
+
 int64_t max_split_tiles(const selinv_junction_plan *plan, int64_t B) {
   int64_t best = 0;
   for (int32_t l = 0; l < plan->levels; ++l) {
@@ -814,7 +893,7 @@ int64_t max_split_tiles(const selinv_junction_plan *plan, int64_t B) {
 }
 
 struct JtWs {
-  void *W, *RJ, *Tpart;
+  void *W, *RJ, *Tpart, *Dpart;
   double *ld;
   int32_t *info;
   size_t bytes;
@@ -827,6 +906,7 @@ JtWs carve(const selinv_junction_plan *plan, int64_t B, void *ws) {
   w.W = cv.take<char>(B * plan->npanel * bb * es);
   w.RJ = cv.take<char>(B * plan->nrinv * bb * es);
   w.Tpart = cv.take<char>(B * max_split_tiles(plan, B) * kTilePart * es);
+  w.Dpart = cv.take<char>(B * max_split_cols(plan, B) * kDiagPart * es);
   w.ld = cv.take<double>(B * plan->nch);
   w.info = cv.take<int32_t>(B);
   w.bytes = cv.off;
@@ -851,9 +931,10 @@ hipError_t junction_run(const selinv_junction_plan *plan, int64_t B, const T *di
   const size_t l_upd = lds_bytes<T>(b), l_fac = fac_lds<T>(b, sm), l_scl = scale_lds<T>(b, sm),
                l_row = rows_lds<T>(b, sm), l_dia = diag_lds<T>(b, sm),
                l_sum = sizeof(T) * (size_t(kTilePart) + size_t(sm) * b * sm * b) +
-                       4 * size_t(tile_rows(b)) * sm;
+                       4 * size_t(tile_rows(b)) * sm,
+               l_dsum = sizeof(T) * (size_t(sm) * b * sm * b + 3 * size_t(sm) * b * b) + 4 * sm;
   if (l_upd > kLdsMax || l_fac > kLdsMax || l_scl > kLdsMax || l_row > kLdsMax ||
-      l_dia > kLdsMax || l_sum > kLdsMax)
+      l_dia > kLdsMax || l_sum > kLdsMax || l_dsum > kLdsMax)
     return hipErrorInvalidValue;
   const auto &lo = plan->level_off;
   const auto &tp = plan->ch_tptr;
@@ -890,8 +971,12 @@ hipError_t junction_run(const selinv_junction_plan *plan, int64_t B, const T *di
             P, d, tl[c0], sp, static_cast<const T *>(w.Tpart), RJ, G_lower);
     }
     const int64_t f0 = plan->ch_cptr[c0], f1 = plan->ch_cptr[c1];
-    jt_bwd_diag<T, BC><<<dim3(static_cast<unsigned>(f1 - f0), By), blk, l_dia, s>>>(
-        P, d, f0, W, RJ, G_diag, G_lower);
+    const int dsp = rows_split(f1 - f0, B);
+    jt_bwd_diag<T, BC><<<dim3(static_cast<unsigned>((f1 - f0) * dsp), By), blk, l_dia, s>>>(
+        P, d, f0, dsp, static_cast<T *>(w.Dpart), W, RJ, G_diag, G_lower);
+    if (dsp > 1)
+      jt_bwd_diag_sum<T, BC><<<dim3(static_cast<unsigned>(f1 - f0), By), blk, l_dsum, s>>>(
+          P, d, f0, dsp, static_cast<const T *>(w.Dpart), RJ, G_diag, G_lower);
   }
   jt_finish<T><<<dim3(By), blk, 0, s>>>(P, plan->nch, w.ld, w.info, logdet, info);
   return hipGetLastError();
