@@ -107,6 +107,9 @@ def nominal_flops(kind, cfg, op="selinv"):
         return cfg["B"] * (2 * b ** 3 * cfg["L"] + 4 * b ** 3 * (cfg["L"] - 1))
     if kind == "nonsym_tree":  # collect 6 b^3, distribute 10 b^3 per non-root; root 2 b^3
         return 16 * b ** 3 * (cfg["n"] - 1) + 2 * b ** 3
+    if kind == "junction" and op == "logdet":  # the factorisation part below
+        n, m, nnz, sk, sk2 = junction_counts(cfg)
+        return cfg["B"] * b ** 3 * (sk2 + sk + n // 3)
     if kind == "junction":
         # per node with k later neighbours: factor k^2 b^3 (k(k-1)/2 Schur
         # products of 2 b^3 and k symmetric ones of b^3) + k b^3 (triangular
@@ -134,6 +137,8 @@ def compulsory_bytes(kind, cfg, w, op="selinv"):
         return (3 * cfg["n"] - 2 + 3 * cfg["n"]) * b2 * w + 4 * cfg["n"] + 4
     if kind == "junction":  # diag, edge_val in; G_diag, G_lower (on S) out; logdet, info
         n, m, nnz, sk, sk2 = junction_counts(cfg)
+        if op == "logdet":
+            return cfg["B"] * ((n + m) * b2 * w + 8 + 4)
         return cfg["B"] * ((2 * n + m + nnz) * b2 * w + 8 + 4)
     if op == "logdet":  # inputs read once, log det and info written
         if kind == "chain":
@@ -241,6 +246,10 @@ def run_gpu(kind, cfg, dtname, steps, warmup, op="selinv"):
             v = torch.from_numpy(spdgen.cotangent((cfg["n"], cfg["b"], k),
                                                   seed=cfg["seed"])).to(dev).to(dt)
             call = (lambda: f.solve(v)) if op == "solve" else (lambda: f.sample(z=v))
+    elif op == "logdet" and kind == "junction":
+        e = parent
+        plan = ssa.junction_plan(cfg["rows"] * cfg["cols"], e, cfg["b"], dt, dev)
+        call = lambda: ssa.junction_logdet(inputs[0], e, inputs[1], plan=plan)
     elif op == "logdet":
         if kind == "chain":
             call = lambda: ssa.chain_logdet(*inputs)

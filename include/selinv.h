@@ -426,6 +426,18 @@ SELINV_API int selinv_junction_f64(const selinv_junction_plan *plan, int64_t B, 
 SELINV_API int selinv_junction_f32(const selinv_junction_plan *plan, int64_t B, const float *diag,
                         const float *edge_val, float *G_diag, float *G_lower, double *logdet,
                         int32_t *info, void *workspace, size_t workspace_bytes, void *stream);
+/* log det A alone from the same factorisation (the junction_logdet sibling
+ * of the same section): the sparse block Cholesky pass of selinv_junction_*
+ * without the Takahashi pass; logdet [B], info [B] and the workspace as
+ * above (same size query). */
+SELINV_API int selinv_junction_logdet_f64(const selinv_junction_plan *plan, int64_t B,
+                               const double *diag, const double *edge_val, double *logdet,
+                               int32_t *info, void *workspace, size_t workspace_bytes,
+                               void *stream);
+SELINV_API int selinv_junction_logdet_f32(const selinv_junction_plan *plan, int64_t B,
+                               const float *diag, const float *edge_val, double *logdet,
+                               int32_t *info, void *workspace, size_t workspace_bytes,
+                               void *stream);
 
 #ifdef __cplusplus
 }

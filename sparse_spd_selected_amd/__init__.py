@@ -157,6 +157,9 @@ def lib():
         f = getattr(L, "selinv_junction_" + sfx)
         f.argtypes = [vp, i64] + [vp] * 6 + [vp, sz, vp]
         f.restype = ctypes.c_int
+        f = getattr(L, "selinv_junction_logdet_" + sfx)
+        f.argtypes = [vp, i64] + [vp] * 4 + [vp, sz, vp]
+        f.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -1035,7 +1038,42 @@ def junction(diag: torch.Tensor, edge_index, edge_val: torch.Tensor, order=None,
     return G_diag, plan.S_index, G_lower, logdet
 
 
-def junction_logdet(diag, edge_index, edge_val, order=None, return_info=False):
-    """log det A of general sparse SPD matrices from the same factorisation."""
-    r = junction(diag, edge_index, edge_val, order=order, return_info=True)
-    return (r[3], r[4]) if return_info else r[3]
+def junction_logdet(diag, edge_index, edge_val, order=None, check=False, return_info=False,
+                    plan: JunctionPlan | None = None):
+    """log det A of general sparse SPD matrices sharing one pattern, from the
+    sparse block Cholesky factorisation alone (no selected inverse).
+    diag [B, n, b, b] (or [n, b, b]) and edge_val as for `junction`."""
+    dt, dev = diag.dtype, diag.device
+    diag = _check_tensor(diag, "diag", dev, dt)
+    single = diag.dim() == 3
+    if single:
+        diag = diag.unsqueeze(0)
+        edge_val = edge_val.unsqueeze(0)
+    edge_val = _check_tensor(edge_val, "edge_val", dev, dt)
+    sfx = _sfx(diag)
+    if diag.dim() != 4 or diag.shape[2] != diag.shape[3]:
+        raise ValueError("diag must be [B, n, b, b]")
+    B, n, b = diag.shape[0], diag.shape[1], diag.shape[2]
+    if plan is None:
+        plan = junction_plan(n, edge_index, b, dt, dev, order)
+    if plan.n != n or plan.b != b or plan.dtype != dt:
+        raise ValueError("plan does not match (n, b, dtype)")
+    if edge_val.shape != (B, plan.m, b, b):
+        raise ValueError("edge_val must be [B, m, b, b]")
+    if check:
+        _validate_values("diag", diag)
+        _validate_symmetric("diag", diag)
+    logdet = torch.empty(B, dtype=torch.float64, device=dev)
+    info = torch.empty(B, dtype=torch.int32, device=dev)
+    nbytes = plan.workspace_bytes(B)
+    ws = _workspace(nbytes, dev)
+    with torch.cuda.device(dev):
+        rc = getattr(lib(), "selinv_junction_logdet_" + sfx)(
+            plan.handle, B, _ptr(diag), _ptr(edge_val) if plan.m else None, logdet.data_ptr(),
+            info.data_ptr(), _ptr(ws), nbytes, _stream(dev))
+    _status(rc, "selinv_junction_logdet_" + sfx)
+    if check:
+        _raise_info(info, "junction")
+    if single:
+        logdet, info = logdet[0], info[0]
+    return (logdet, info) if return_info else logdet

@@ -269,9 +269,40 @@ int junction_entry(const selinv_junction_plan *plan, int64_t B, const T *diag, c
   return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
 }
 
+template <typename T>
+int junction_logdet_entry(const selinv_junction_plan *plan, int64_t B, const T *diag,
+                          const T *edge_val, double *logdet, int32_t *info, void *ws,
+                          size_t ws_bytes, void *stream) {
+  if (!plan || plan->dtype_bytes != static_cast<int>(sizeof(T))) return SELINV_ERR_INVALID_ARG;
+  if (B < 0 || B > 65535) return SELINV_ERR_INVALID_ARG;
+  if (B == 0) return SELINV_OK;
+  if (!diag || !logdet || (plan->m > 0 && !edge_val)) return SELINV_ERR_INVALID_ARG;
+  if (misaligned(diag) || misaligned(edge_val)) return SELINV_ERR_INVALID_ARG;
+  const size_t need = selinv::junction_workspace_bytes(plan, B);
+  if (ws_bytes < need || !ws || misaligned_ws(ws)) return SELINV_ERR_INVALID_ARG;
+  const hipError_t e = selinv::junction_launch<T>(plan, B, diag, edge_val, nullptr, nullptr,
+                                                  logdet, info, ws,
+                                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+int selinv_junction_logdet_f64(const selinv_junction_plan *plan, int64_t B, const double *diag,
+                               const double *edge_val, double *logdet, int32_t *info,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  return junction_logdet_entry<double>(plan, B, diag, edge_val, logdet, info, workspace,
+                                       workspace_bytes, stream);
+}
+
+int selinv_junction_logdet_f32(const selinv_junction_plan *plan, int64_t B, const float *diag,
+                               const float *edge_val, double *logdet, int32_t *info,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  return junction_logdet_entry<float>(plan, B, diag, edge_val, logdet, info, workspace,
+                                      workspace_bytes, stream);
+}
 
 size_t selinv_junction_workspace_bytes(const selinv_junction_plan *plan, int64_t B) {
   if (!plan || B < 0) return 0;

@@ -919,6 +919,7 @@ size_t junction_workspace_bytes(const selinv_junction_plan *plan, int64_t B) {
   return carve(plan, B, nullptr).bytes;
 }
 
+// G_diag == nullptr: the factorisation alone (log det and info)
 template <typename T, int BC>
 hipError_t junction_run(const selinv_junction_plan *plan, int64_t B, const T *diag,
                            const T *edge_val, T *G_diag, T *G_lower, double *logdet,
@@ -958,7 +959,7 @@ hipError_t junction_run(const selinv_junction_plan *plan, int64_t B, const T *di
       jt_fwd_scale<T, BC><<<dim3(static_cast<unsigned>(rp[c1] - rp[c0]), By), blk, l_scl, s>>>(
           P, d, rp[c0], W, RJ);
   }
-  for (int32_t l = plan->levels - 1; l >= 0; --l) {
+  for (int32_t l = G_diag ? plan->levels - 1 : -1; l >= 0; --l) {
     const int64_t c0 = lo[l], c1 = lo[l + 1];
     const auto &tl = plan->tiles_ptr;
     const int64_t nt = tl[c1] - tl[c0];

@@ -167,3 +167,44 @@ def test_star_and_tree_vjp_argument_validation(lib):
     assert star(wsb=8) == ssa.INVALID_ARG
     assert lib.selinv_tree_vjp_f64(None, p, p, p, p, None, p, p, None, p, 1 << 30, None) == \
         ssa.INVALID_ARG
+
+
+def test_junction_argument_validation(lib):
+    """The junction entry points reject bad arguments before touching a device:
+    a null plan, sizes and dtypes out of range, bad patterns (checked by the
+    host-only symbolic analysis, which shares the plan's validation)."""
+    vp = ctypes.c_void_p
+    h = vp()
+    e = np.array([[1], [0]], np.int32)
+    # plan creation: bad sizes and dtypes are rejected before any device work
+    assert lib.selinv_junction_plan_create(0, 1, e.ctypes.data, None, 4, 8, None,
+                                           ctypes.byref(h)) == 1
+    assert lib.selinv_junction_plan_create(2, 1, e.ctypes.data, None, 33, 8, None,
+                                           ctypes.byref(h)) == 1
+    assert lib.selinv_junction_plan_create(2, 1, e.ctypes.data, None, 4, 2, None,
+                                           ctypes.byref(h)) == 1
+    assert lib.selinv_junction_plan_create(2, 1, None, None, 4, 8, None, ctypes.byref(h)) == 1
+    assert lib.selinv_junction_plan_create(2, 1, e.ctypes.data, None, 4, 8, None, None) == 1
+    # queries on a null plan
+    assert lib.selinv_junction_plan_nnz(None) == -1
+    assert lib.selinv_junction_plan_levels(None) == -1
+    assert lib.selinv_junction_workspace_bytes(None, 4) == 0
+    assert lib.selinv_junction_plan_pattern(None, None, None) == 1
+    lib.selinv_junction_plan_destroy(None)
+    # calls without a plan
+    for f in (lib.selinv_junction_f64, lib.selinv_junction_f32):
+        assert f(None, 1, None, None, None, None, None, None, None, 0, None) == 1
+    # the symbolic analysis: status 4 for bad patterns and orders
+    nnz, lev = ctypes.c_int64(), ctypes.c_int32()
+    bad = [np.array([[0], [1]], np.int32), np.array([[1, 1], [0, 0]], np.int32),
+           np.array([[5], [0]], np.int32)]
+    for b in bad:
+        assert lib.selinv_junction_symbolic(3, b.shape[1], b.ctypes.data, None, ctypes.byref(nnz),
+                                            ctypes.byref(lev), None, 0, None) == 4
+    o = np.array([0, 0, 1], np.int32)
+    assert lib.selinv_junction_symbolic(3, 1, e.ctypes.data, o.ctypes.data, ctypes.byref(nnz),
+                                        ctypes.byref(lev), None, 0, None) == 4
+    assert lib.selinv_junction_symbolic(3, 1, e.ctypes.data, None, ctypes.byref(nnz),
+                                        ctypes.byref(lev), None, 0, None) == 0
+    assert nnz.value == 1 and lev.value == 2
+    assert lib.selinv_strerror(4) != b"unknown status"

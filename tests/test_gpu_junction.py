@@ -176,3 +176,22 @@ def test_repeated_calls_are_bitwise_identical(ssa):
         c = ssa.junction(D, e, V)
         torch.cuda.synchronize()
         assert all(torch.equal(x, y) for x, y in zip(a, c))
+
+
+@pytest.mark.parametrize("dt", ["f64", "f32"])
+def test_logdet_only(ssa, dt):
+    """The factorisation alone gives the same log det (bit for bit: the same
+    forward kernels) and the same failure index as the full call."""
+    e = spdgen.grid_edges(9, 11)
+    d, v = spdgen.graph(e, 99, 8, B=3, seed=8)
+    d[2, 40] = -np.eye(8)
+    D, V = _to(d, DT[dt]), _to(v, DT[dt])
+    ld, info = ssa.junction_logdet(D, e, V, return_info=True)
+    _, _, _, ld_full, info_full = ssa.junction(D, e, V, return_info=True)
+    torch.cuda.synchronize()
+    assert torch.equal(info, info_full) and list(info.cpu().numpy())[:2] == [0, 0]
+    assert int(info[2]) == 41
+    assert torch.equal(ld[:2], ld_full[:2]) and torch.isnan(ld[2])
+    _, _, _, Old, Oinfo = oracle.junction(_as_used(d, DT[dt]), e, _as_used(v, DT[dt]))
+    assert list(Oinfo) == list(info.cpu().numpy())
+    assert np.all(np.abs(ld[:2].cpu().numpy() - Old[:2]) <= LDTOL[DT[dt]] * np.abs(Old[:2]))
