@@ -22,11 +22,15 @@
 // One G_{N,N} block now serves s columns at once.
 //
 // Work decomposition, each workgroup owning what it writes for one matrix:
-// per level the Schur sums (one workgroup per panel block), the dense pivots
-// (one per chunk: R_J^-1, the log det term), the scaling of the later rows
-// (one per row), and in the Takahashi pass the rows G_{w,J} (one per tile of
-// rows) and the chunk's own blocks (one per block column).  Sums run in a fixed order, so
-// results are deterministic; the only atomic is the first-failure index.
+// per level the Schur sums (one workgroup per panel block, or one wavefront
+// per panel block for b <= 8), the dense pivots (one per chunk: R_J^-1, the
+// log det term), the scaling of the later rows (one per row), and in the
+// Takahashi pass the rows G_{w,J} (one per tile of rows) and the chunk's own
+// blocks (one per block column); on levels with few tiles or columns the
+// last two split their sums over several workgroups and add the parts in a
+// fixed order.  Sums run in a fixed order, so results are deterministic; the
+// only atomic is the first-failure index.  Without G outputs only the
+// factorisation runs (the log det call).
 // Operands are staged through LDS in rounds; every thread issues a batch of
 // loads before storing them, so a round costs about one memory latency.
 #include <hip/hip_runtime.h>
@@ -177,8 +181,8 @@ __device__ inline void staged_sum(T *out, int count, int b, const Lds<T> &l, Src
 }
 
 
-// Pairs per round of the chunk kernel (a b x sb row and a block each), the
-// row tiles of the row kernel, and the LDS of every kernel.
+// Row tiles of the row kernel, pairs per round of the chunk kernel (a b x sb
+// row and a block each), and the LDS of every kernel.
 constexpr size_t kLdsMax = 64 * 1024;
 constexpr int kTileTable = 256;  // G block pointers per staging round of a row tile
 constexpr size_t kTileTableBytes = kTileTable * (sizeof(void *) + 1);
@@ -194,11 +198,6 @@ __host__ __device__ inline int tile_steps(int b, int s) {
   return c < 1 ? 1 : c;
 }
 
-__host__ __device__ inline int rows_pairs(int b, int s) {
-  const int per = b * b + b * s * b;
-  const int c = 4096 / per;
-  return c < 1 ? 1 : (c > kMaxPairs ? kMaxPairs : c);
-}
 __host__ __device__ inline int diag_pairs(int b, int s) {
   const int per = b * s * b + b * b;
   const int c = 4096 / per;
