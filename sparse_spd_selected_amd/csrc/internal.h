@@ -72,6 +72,10 @@ struct JunctionPlanDev {
   int32_t *tg_chunk = nullptr, *tg_rc = nullptr, *ain = nullptr;
   int32_t *fptr = nullptr, *fpair = nullptr;
   int32_t *gtab = nullptr, *poutenc = nullptr;
+  // Schur-sum work items: target, pair range, partial-sum slot (-1: the
+  // target's only item); targets with several items per level; it_ptr[tg]
+  int32_t *it_tg = nullptr, *it_lo = nullptr, *it_hi = nullptr, *it_slot = nullptr;
+  int32_t *multi_tg = nullptr, *it_ptr = nullptr;
 };
 
 }  // namespace selinv
@@ -86,6 +90,9 @@ struct selinv_junction_plan {
   std::vector<int64_t> rows_ptr;   // first flat row of every chunk (nch + 1)
   std::vector<int64_t> ch_cptr;    // first flat column of every chunk (nch + 1)
   std::vector<int64_t> tiles_ptr;  // first row tile of every chunk (nch + 1)
+  std::vector<int64_t> it_ptr;     // first Schur work item of every target (ntg + 1)
+  std::vector<int64_t> multi_off;  // range of multi-item targets of every level (levels + 1)
+  int64_t max_slots = 0;           // partial-sum slots of the busiest level
   std::vector<int32_t> S_index;    // [2][nnz], host copy for the caller
   std::vector<int32_t> order;      // elimination order (labels)
   selinv::JunctionPlanDev dev;

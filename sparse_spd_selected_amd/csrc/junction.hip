@@ -371,14 +371,40 @@ __global__ void __launch_bounds__(kJT) jt_fwd_update(JunctionPlanDev P, Dims d, 
   }
 }
 
-// Schur sums for b <= 8 (bb <= 64): one wavefront per panel block, four per
-// workgroup, no workgroup barrier.  Lane e owns entry e of the b x b sum
-// (b = 8) or, for smaller b, the 64 / bb lane groups take every
-// (64 / bb)-th pair and are added at the end.  Each round stages up to
-// 512 / bb pairs of blocks through the wavefront's LDS.
+// C_{t,j} = A_{t,j} - acc for lane e < bb of the wavefront (entry e of the
+// panel block of target tg)
+template <typename T, int BC>
+__device__ __forceinline__ void write_target(const JunctionPlanDev &P, const Dims &d, int64_t tg,
+                                             int64_t mat, int e, T acc, const T *diag,
+                                             const T *edge_val, T *W) {
+  constexpr int b = BC, bb = b * b;
+  const int er = e / b, ec = e - er * b;
+  const int id = P.tg_chunk[tg], rc = P.tg_rc[tg], r = rc >> 6, col = rc & 63;
+  const int32_t enc = P.ain[tg];
+  T *dst = W + (mat * d.npanel + P.ch_pbase[id] + int64_t(r) * P.ch_s[id] + col) * bb;
+  T base;
+  if (r == col) {
+    const T *D = diag + (mat * d.n + enc) * bb;
+    base = er >= ec ? D[er * b + ec] : D[ec * b + er];
+  } else {
+    const T *E = enc < 0 ? nullptr : edge_val + (mat * d.m + (enc >> 1)) * bb;
+    base = E ? ((enc & 1) ? E[ec * b + er] : E[e]) : T(0);
+  }
+  dst[e] = base - acc;
+}
+
+// Schur sums for b <= 8 (bb <= 64): one wavefront per work item (a run of at
+// most 64 pairs of one panel block's list), four per workgroup, no
+// workgroup barrier.  Lane e owns entry e of the b x b sum (b = 8) or, for
+// smaller b, the 64 / bb lane groups take every (64 / bb)-th pair and are
+// added at the end.  Each round stages up to 512 / bb pairs of blocks through
+// the wavefront's LDS.  A target with one item is finished here; the items
+// of a longer list leave partial sums in their slots of Spart for
+// jt_fwd_update_sum.
 template <typename T, int BC>
 __global__ void __launch_bounds__(kJT) jt_fwd_update_wave(JunctionPlanDev P, Dims d,
-                                                          int64_t tbase, int64_t tend,
+                                                          int64_t ibase, int64_t iend,
+                                                          int64_t nslots, T *Spart,
                                                           const T *__restrict__ diag,
                                                           const T *__restrict__ edge_val, T *W) {
   constexpr int b = BC, bb = b * b, CH = (512 / bb) > 32 ? 32 : 512 / bb, G = 64 / bb;
@@ -388,10 +414,10 @@ __global__ void __launch_bounds__(kJT) jt_fwd_update_wave(JunctionPlanDev P, Dim
   __shared__ int32_t tab[4][2 * CH];
   __shared__ T red[4][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t tg = tbase + int64_t(blockIdx.x) * 4 + wave, mat = blockIdx.y;
-  if (tg >= tend) return;
-  const int id = P.tg_chunk[tg], rc = P.tg_rc[tg], r = rc >> 6, col = rc & 63;
-  const int32_t f0 = P.fptr[tg], f1 = P.fptr[tg + 1];
+  const int64_t it = ibase + int64_t(blockIdx.x) * 4 + wave, mat = blockIdx.y;
+  if (it >= iend) return;
+  const int64_t tg = P.it_tg[it];
+  const int32_t f0 = P.it_lo[it], f1 = P.it_hi[it], slot = P.it_slot[it];
   const T *Wm = W + mat * d.npanel * bb;
   const int grp = lane / bb, e = lane - grp * bb, er = e / b, ec = e - er * b;
   T acc = T(0);
@@ -435,17 +461,28 @@ __global__ void __launch_bounds__(kJT) jt_fwd_update_wave(JunctionPlanDev P, Dim
     }
   }
   if (lane >= bb) return;
-  const int32_t enc = P.ain[tg];
-  T *dst = W + (mat * d.npanel + P.ch_pbase[id] + int64_t(r) * P.ch_s[id] + col) * bb;
-  T base;
-  if (r == col) {
-    const T *D = diag + (mat * d.n + enc) * bb;
-    base = er >= ec ? D[er * b + ec] : D[ec * b + er];
-  } else {
-    const T *E = enc < 0 ? nullptr : edge_val + (mat * d.m + (enc >> 1)) * bb;
-    base = E ? ((enc & 1) ? E[ec * b + er] : E[e]) : T(0);
-  }
-  dst[e] = base - acc;
+  if (slot < 0)
+    write_target<T, BC>(P, d, tg, mat, e, acc, diag, edge_val, W);
+  else
+    Spart[(mat * nslots + slot) * bb + e] = acc;
+}
+
+// Targets with several work items: their partial sums added in item order
+template <typename T, int BC>
+__global__ void __launch_bounds__(kJT) jt_fwd_update_sum(JunctionPlanDev P, Dims d,
+                                                         int64_t mbase, int64_t mend,
+                                                         int64_t nslots, const T *Spart,
+                                                         const T *__restrict__ diag,
+                                                         const T *__restrict__ edge_val, T *W) {
+  constexpr int bb = BC * BC;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t k = mbase + int64_t(blockIdx.x) * 4 + wave, mat = blockIdx.y;
+  if (k >= mend || lane >= bb) return;
+  const int64_t tg = P.multi_tg[k];
+  const int32_t i0 = P.it_ptr[tg], i1 = P.it_ptr[tg + 1], s0 = P.it_slot[i0];
+  T acc = T(0);
+  for (int32_t i = 0; i < i1 - i0; ++i) acc += Spart[(mat * nslots + s0 + i) * bb + lane];
+  write_target<T, BC>(P, d, tg, mat, lane, acc, diag, edge_val, W);
 }
 
 // Dense pivot of every chunk of the level: R_J^-1 (into RJ), the log det
@@ -892,7 +929,7 @@ int64_t max_split_tiles(const selinv_junction_plan *plan, int64_t B) {
 }
 
 struct JtWs {
-  void *W, *RJ, *Tpart, *Dpart;
+  void *W, *RJ, *Tpart, *Dpart, *Spart;
   double *ld;
   int32_t *info;
   size_t bytes;
@@ -906,6 +943,7 @@ JtWs carve(const selinv_junction_plan *plan, int64_t B, void *ws) {
   w.RJ = cv.take<char>(B * plan->nrinv * bb * es);
   w.Tpart = cv.take<char>(B * max_split_tiles(plan, B) * kTilePart * es);
   w.Dpart = cv.take<char>(B * max_split_cols(plan, B) * kDiagPart * es);
+  w.Spart = cv.take<char>(B * plan->max_slots * bb * es);
   w.ld = cv.take<double>(B * plan->nch);
   w.info = cv.take<int32_t>(B);
   w.bytes = cv.off;
@@ -945,9 +983,15 @@ hipError_t junction_run(const selinv_junction_plan *plan, int64_t B, const T *di
   for (int32_t l = 0; l < plan->levels; ++l) {
     const int64_t c0 = lo[l], c1 = lo[l + 1];
     if constexpr (BC == 4 || BC == 8) {
-      const int64_t nt = tp[c1] - tp[c0];
-      jt_fwd_update_wave<T, BC><<<dim3(static_cast<unsigned>((nt + 3) / 4), By), blk, 0, s>>>(
-          P, d, tp[c0], tp[c1], diag, edge_val, W);
+      const auto &ip = plan->it_ptr;
+      const int64_t i0 = ip[tp[c0]], i1 = ip[tp[c1]];
+      T *Sp = static_cast<T *>(w.Spart);
+      jt_fwd_update_wave<T, BC><<<dim3(static_cast<unsigned>((i1 - i0 + 3) / 4), By), blk, 0, s>>>(
+          P, d, i0, i1, plan->max_slots, Sp, diag, edge_val, W);
+      const int64_t m0 = plan->multi_off[l], m1 = plan->multi_off[l + 1];
+      if (m1 > m0)
+        jt_fwd_update_sum<T, BC><<<dim3(static_cast<unsigned>((m1 - m0 + 3) / 4), By), blk, 0, s>>>(
+            P, d, m0, m1, plan->max_slots, Sp, diag, edge_val, W);
     } else {
       jt_fwd_update<T, BC><<<dim3(static_cast<unsigned>(tp[c1] - tp[c0]), By), blk, l_upd, s>>>(
           P, d, tp[c0], diag, edge_val, W);

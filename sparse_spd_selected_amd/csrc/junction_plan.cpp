@@ -30,7 +30,8 @@
 //   * forward targets: every used panel block; per target the list of
 //     (W_{t,u}, W_{v,u}) panel blocks of its Schur update over the earlier
 //     columns u outside the chunk, u in elimination order, and the input
-//     block it starts from;
+//     block it starts from; long lists are cut into work items of at most
+//     64 pairs whose partial sums are added in order;
 //   * backward: per chunk the n_J x n_J reads of G_{w,x} (w, x in N_J) as
 //     positions in the caller's output arrays with a transpose bit, and the
 //     output code of every panel block.
@@ -115,7 +116,14 @@ struct HostTables {
   std::vector<int64_t> ch_pbase, ch_rbase, ch_gptr, ch_tptr, rows_ptr, ch_cptr, tiles_ptr;
   Vec row_chunk, col_chunk, tile_chunk, tg_chunk, tg_rc, ain, fpair, gtab, poutenc;
   std::vector<int64_t> fptr;
+  // Schur-sum work items: each target's pair list cut into runs of at most
+  // kItemPairs; targets with several items add partial sums (slots)
+  std::vector<int64_t> it_ptr, multi_off;
+  Vec it_tg, it_lo, it_hi, it_slot, multi_tg;
+  int64_t nitems = 0, max_slots = 0;
 };
+
+constexpr int64_t kItemPairs = 64;
 
 // Symbolic analysis.  With tables == false: the order, S and the height of
 // the elimination tree only; else also the supernode chunks (at most
@@ -393,6 +401,34 @@ int analyze(int64_t n, int64_t m, const int32_t *edge_index_host, const int32_t 
         h.gtab[h.ch_gptr[id] + a * nr + q] = enc;
       }
   }
+  // ---- Schur-sum work items, level by level (targets are level-ordered)
+  h.it_ptr.assign(ntg + 1, 0);
+  for (int64_t tg = 0; tg < ntg; ++tg) {
+    const int64_t np = h.fptr[tg + 1] - h.fptr[tg];
+    h.it_ptr[tg + 1] = h.it_ptr[tg] + std::max<int64_t>(1, (np + kItemPairs - 1) / kItemPairs);
+  }
+  h.nitems = h.it_ptr[ntg];
+  if (h.nitems >= (int64_t(1) << 31)) return SELINV_ERR_INVALID_ARG;
+  h.it_tg.resize(h.nitems);
+  h.it_lo.resize(h.nitems);
+  h.it_hi.resize(h.nitems);
+  h.it_slot.assign(h.nitems, -1);
+  h.multi_off.assign(L + 1, 0);
+  for (int32_t l = 0; l < L; ++l) {
+    int64_t slots = 0;
+    for (int64_t tg = h.ch_tptr[level_off[l]]; tg < h.ch_tptr[level_off[l + 1]]; ++tg) {
+      const int64_t i0 = h.it_ptr[tg], ni = h.it_ptr[tg + 1] - i0;
+      for (int64_t k = 0; k < ni; ++k) {
+        h.it_tg[i0 + k] = static_cast<int32_t>(tg);
+        h.it_lo[i0 + k] = static_cast<int32_t>(h.fptr[tg] + k * kItemPairs);
+        h.it_hi[i0 + k] = static_cast<int32_t>(std::min(h.fptr[tg + 1], h.fptr[tg] + (k + 1) * kItemPairs));
+        if (ni > 1) h.it_slot[i0 + k] = static_cast<int32_t>(slots++);
+      }
+      if (ni > 1) h.multi_tg.push_back(static_cast<int32_t>(tg));
+    }
+    h.multi_off[l + 1] = static_cast<int64_t>(h.multi_tg.size());
+    h.max_slots = std::max(h.max_slots, slots);
+  }
   h.nch = nch;
   h.ntg = ntg;
   h.npairs = h.fptr[ntg];
@@ -442,6 +478,9 @@ extern "C" int selinv_junction_plan_create(int64_t n, int64_t m, const int32_t *
   plan->rows_ptr = h.rows_ptr;
   plan->ch_cptr = h.ch_cptr;
   plan->tiles_ptr = h.tiles_ptr;
+  plan->it_ptr = h.it_ptr;
+  plan->multi_off = h.multi_off;
+  plan->max_slots = h.max_slots;
   plan->S_index.swap(h.S_index);
   plan->order.swap(h.order);
 
@@ -454,7 +493,8 @@ extern "C" int selinv_junction_plan_create(int64_t n, int64_t m, const int32_t *
                        align_up(n * i4) + align_up(h.tiles_ptr[h.nch] * i4) +
                        3 * align_up(h.ntg * i4) + align_up((h.ntg + 1) * i4) +
                        align_up(2 * h.npairs * i4) + align_up(h.ng * i4) +
-                       align_up(h.npanel * i4) + 4096;
+                       align_up(h.npanel * i4) + 4 * align_up(h.nitems * i4) +
+                       align_up(h.multi_tg.size() * i4) + align_up((h.ntg + 1) * i4) + 4096;
   if (hipMalloc(&plan->dev_block, bytes) != hipSuccess) {
     delete plan;
     return SELINV_ERR_HIP;
@@ -481,6 +521,14 @@ extern "C" int selinv_junction_plan_create(int64_t n, int64_t m, const int32_t *
   dv.fpair = cv.take<int32_t>(2 * h.npairs);
   dv.gtab = cv.take<int32_t>(h.ng);
   dv.poutenc = cv.take<int32_t>(h.npanel);
+  dv.it_tg = cv.take<int32_t>(h.nitems);
+  dv.it_lo = cv.take<int32_t>(h.nitems);
+  dv.it_hi = cv.take<int32_t>(h.nitems);
+  dv.it_slot = cv.take<int32_t>(h.nitems);
+  dv.multi_tg = cv.take<int32_t>(h.multi_tg.size());
+  dv.it_ptr = cv.take<int32_t>(h.ntg + 1);
+  std::vector<int32_t> itptr32(h.ntg + 1);
+  for (int64_t t = 0; t <= h.ntg; ++t) itptr32[t] = static_cast<int32_t>(h.it_ptr[t]);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   auto up = [&](void *dst, const void *src, size_t nbytes) {
@@ -506,6 +554,12 @@ extern "C" int selinv_junction_plan_create(int64_t n, int64_t m, const int32_t *
   up(dv.fpair, h.fpair.data(), 2 * h.npairs * i4);
   up(dv.gtab, h.gtab.data(), h.ng * i4);
   up(dv.poutenc, h.poutenc.data(), h.npanel * i4);
+  up(dv.it_tg, h.it_tg.data(), h.nitems * i4);
+  up(dv.it_lo, h.it_lo.data(), h.nitems * i4);
+  up(dv.it_hi, h.it_hi.data(), h.nitems * i4);
+  up(dv.it_slot, h.it_slot.data(), h.nitems * i4);
+  up(dv.multi_tg, h.multi_tg.data(), h.multi_tg.size() * i4);
+  up(dv.it_ptr, itptr32.data(), (h.ntg + 1) * i4);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) {
     selinv_junction_plan_destroy(plan);
