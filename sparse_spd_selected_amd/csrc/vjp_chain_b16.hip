@@ -17,14 +17,17 @@
 //     W^T    = GG_i Y,  Y1^T = W^T - Gl_i^T,  Y2^T = W^T + Y1^T
 //     Z_i    = Y2 Sinv_i
 //     GG_{i+1} = sym(Gd_{i+1}) + sym(Y1 X_i^T)
-//   distribute i = L-2 .. 0 (G = Sinv_{L-1}, Dbar_{L-1} = P_{L-1}):
+//   distribute i = L-2 .. 0 (G = Sinv_{L-1}, Dbar_{L-1} = P_{L-1}), with
+//   X_i, Z_i and P_i rebuilt from Sinv_i, GG_i, C_i and Gl_i:
 //     Q          = G Z_i - Dbar_{i+1} X_i
 //     lower_bar[i] = Q - Dbar_{i+1} X_i
 //     Dbar_i     = P_i - sym(X_i^T Q)
 //     G          = Sinv_i + X_i^T G X_i
 // Workspace per block (temporal accesses, written by the collect pass and
-// read back by the distribute pass of the same wavefront): packed Sinv_i,
-// packed P_i, X_i^T and Z_i.
+// read back by the distribute pass of the same wavefront): the packed
+// symmetric Sinv_i and GG_i only.  The distribute pass re-reads C_i and
+// Gl_i and rebuilds X_i = C_i Sinv_i, Z_i and P_i on the matrix cores, which
+// moves less data than storing X_i, Z_i and P_i.
 #include "frag16.h"
 #include "internal.h"
 #include "io16.h"
@@ -36,7 +39,7 @@ namespace {
 using f16::Frag;
 
 constexpr int kBB = 256, kPB = f16::kPacked16;
-constexpr int kStateBlock = 2 * kPB + 2 * kBB;  // elements of workspace per block
+constexpr int kStateBlock = 2 * kPB;  // elements of workspace per block
 
 // Occupancy per element type: the f64 kernel needs about 200 VGPRs (two
 // waves per SIMD), the f32 one about 130 (three) to run without spills.
@@ -83,18 +86,15 @@ void chain16_vjp_kernel(int L, const T *__restrict__ diag, const T *__restrict__
     GG = T(0.5) * (io16::get_frag(tB, g, j) + io16::get_frag_t(tB, g, j));
     f16::wave_sync();
   }
-  // Sinv_i = S^{-1}, P_i, both packed to the workspace.  Leaves Sinv in S.
-  auto invert_and_p = [&](int i) -> Frag<T> {
+  // Sinv_i = S^{-1} and GG_i, both packed to the workspace.  Leaves Sinv in S.
+  auto invert = [&](int i) {
     if (f16::gj_inverse(S, col, g, j, pl) && !fail) fail = i + 1;
-    const Frag<T> U = f16::mm<T>(GG, S, zero);  // GG Sinv
-    const Frag<T> P = f16::mm<T>(-U, S, lb * S);  // lb Sinv - Sinv GG Sinv
     f16::wave_sync();
     io16::put_frag(tA, g, j, S);
-    io16::put_frag(tB, g, j, P);
+    io16::put_frag(tB, g, j, GG);
     f16::wave_sync();
     io16::store_packed(st + i * kStateBlock, lane, sl.gather_packed(tA));
     io16::store_packed(st + i * kStateBlock + kPB, lane, sl.gather_packed(tB));
-    return P;
   };
   // Collect with the next step's four input blocks in flight (two register
   // sets alternate, indices clamped; single-exit loop, see chain_b16.hip).
@@ -110,7 +110,7 @@ void chain16_vjp_kernel(int L, const T *__restrict__ diag, const T *__restrict__
     En = io16::load(Gl + min(i + 1, lc) * kBB, lane);
     Dn = io16::load(D + min(i + 2, L - 1) * kBB, lane);
     Hn = io16::load(Gd + min(i + 2, L - 1) * kBB, lane);
-    invert_and_p(i);
+    invert(i);
     f16::wave_sync();
     io16::put(tA, lane, Cu);
     io16::put(tB, lane, Eu);
@@ -125,20 +125,12 @@ void chain16_vjp_kernel(int L, const T *__restrict__ diag, const T *__restrict__
     const Frag<T> Dn1 = sl.get_sym(tA);
     const Frag<T> Y = f16::mm<T>(S, Ct, zero);      // O(X_i^T)
     const Frag<T> Wt = f16::mm<T>(GG, Y, zero);     // O(W^T)
-    const Frag<T> Y1t = Wt - Glt;
-    const Frag<T> Z = f16::mm<T>(Wt + Y1t, S, zero);  // O(Y2 Sinv_i)
-    const Frag<T> N = f16::mm<T>(Y1t, Y, zero);       // O(Y1 X_i^T)
+    const Frag<T> N = f16::mm<T>(Wt - Glt, Y, zero);  // O(Y1 X_i^T)
     S = Dn1 - f16::mm<T>(Ct, Y, zero);                // S_{i+1}
     f16::wave_sync();
     io16::put_frag(tA, g, j, N);
-    io16::put_frag(tB, g, j, Y);
-    io16::put_frag(tC, g, j, Z);
     f16::wave_sync();
-    const Frag<T> Nt = io16::get_frag_t(tA, g, j);
-    T *sb = st + i * kStateBlock + 2 * kPB;
-    io16::store_ws(sb, lane, io16::get(tB, lane));        // X_i^T
-    io16::store_ws(sb + kBB, lane, io16::get(tC, lane));  // Z_i
-    GG = Gdn + T(0.5) * (N + Nt);
+    GG = Gdn + T(0.5) * (N + io16::get_frag_t(tA, g, j));
   };
   int i = 0;
   for (; i + 1 < L - 1; i += 2) {
@@ -146,7 +138,7 @@ void chain16_vjp_kernel(int L, const T *__restrict__ diag, const T *__restrict__
     collect(i + 1, C1, E1, D1, H1, C0, E0, D0, H0);
   }
   if (i < L - 1) collect(i, C0, E0, D0, H0, C1, E1, D1, H1);
-  const Frag<T> Pr = invert_and_p(L - 1);  // the root block
+  invert(L - 1);  // the root block
   if (fail) {
     const T nan = static_cast<T>(__builtin_nan(""));
     for (int64_t e = lane; e < static_cast<int64_t>(L) * kBB; e += 64) Db[e] = nan;
@@ -157,50 +149,58 @@ void chain16_vjp_kernel(int L, const T *__restrict__ diag, const T *__restrict__
   Frag<T> G = S;  // Sinv_{L-1}
   Frag<T> Dbar;
   {
+    // Dbar_{L-1} = P_{L-1} = lb Sinv - Sinv GG Sinv, symmetrised
+    const Frag<T> U = f16::mm<T>(GG, S, zero);
+    const Frag<T> Pr = f16::mm<T>(-U, S, lb * S);
     f16::wave_sync();
     io16::put_frag(tA, g, j, Pr);
     f16::wave_sync();
-    Dbar = sl.get_sym(tA);  // the same symmetric P the packed copy holds
+    Dbar = T(0.5) * (Pr + io16::get_frag_t(tA, g, j));
     f16::wave_sync();
     io16::put_frag(tA, g, j, Dbar);
     f16::wave_sync();
     io16::store(Db + (L - 1) * kBB, lane, io16::get(tA, lane));
   }
-  // Distribute, with the next block's four workspace entries in flight.
-  auto ld_x = [&](int k) { return io16::load_ws(st + k * kStateBlock + 2 * kPB, lane); };
-  auto ld_z = [&](int k) { return io16::load_ws(st + k * kStateBlock + 2 * kPB + kBB, lane); };
+  // Distribute, with the next block's packed Sinv, GG and its C, Gl in flight.
   auto ld_s = [&](int k) { return io16::load_packed(st + k * kStateBlock, lane); };
-  auto ld_p = [&](int k) { return io16::load_packed(st + k * kStateBlock + kPB, lane); };
-  io16::Nat<T> X0 = ld_x(lc), Z0 = ld_z(lc), S0 = ld_s(lc), P0 = ld_p(lc);
-  io16::Nat<T> X1, Z1, S1, P1;
-  auto distribute = [&](int i, const io16::Nat<T> &Xu, const io16::Nat<T> &Zu,
-                        const io16::Nat<T> &Su, const io16::Nat<T> &Pu, io16::Nat<T> &Xn,
-                        io16::Nat<T> &Zn, io16::Nat<T> &Sn, io16::Nat<T> &Pn) {
+  auto ld_g = [&](int k) { return io16::load_packed(st + k * kStateBlock + kPB, lane); };
+  io16::Nat<T> S0 = ld_s(lc), Q0 = ld_g(lc), C2 = io16::load(C + lc * kBB, lane),
+               E2 = io16::load(Gl + lc * kBB, lane);
+  io16::Nat<T> S1, Q1, C3, E3;
+  auto distribute = [&](int i, const io16::Nat<T> &Su, const io16::Nat<T> &Qu,
+                        const io16::Nat<T> &Cu, const io16::Nat<T> &Eu, io16::Nat<T> &Sn,
+                        io16::Nat<T> &Qn, io16::Nat<T> &Cn, io16::Nat<T> &En) {
     const int in = max(i - 1, 0);
-    Xn = ld_x(in);
-    Zn = ld_z(in);
     Sn = ld_s(in);
-    Pn = ld_p(in);
+    Qn = ld_g(in);
+    Cn = io16::load(C + in * kBB, lane);
+    En = io16::load(Gl + in * kBB, lane);
     f16::wave_sync();
-    io16::put(tA, lane, Xu);
-    io16::put(tB, lane, Zu);
     io16::put_packed(tP, lane, Su);
-    io16::put_packed(tQ, lane, Pu);
+    io16::put_packed(tQ, lane, Qu);
+    io16::put(tA, lane, Cu);
+    io16::put(tB, lane, Eu);
     f16::wave_sync();
-    const Frag<T> Xf = io16::get_frag_t(tA, g, j);  // the tile holds X^T
-    const Frag<T> Zf = io16::get_frag(tB, g, j);
     const Frag<T> Si = sl.get_packed(tP);
-    const Frag<T> Pf = sl.get_packed(tQ);
+    const Frag<T> GGf = sl.get_packed(tQ);
+    const Frag<T> Ct = io16::get_frag_t(tA, g, j);   // O(C_i^T)
+    const Frag<T> Glt = io16::get_frag_t(tB, g, j);  // O(Gl_i^T)
+    const Frag<T> Xf = f16::mm<T>(Ct, Si, zero);     // O(X_i), X_i = C_i Sinv_i
+    const Frag<T> Yt = f16::mm<T>(Si, Ct, zero);     // O(X_i^T)
+    const Frag<T> Wt = f16::mm<T>(GGf, Yt, zero);    // O(W^T)
+    const Frag<T> Zf = f16::mm<T>(Wt + Wt - Glt, Si, zero);  // O(Z_i), Y2^T = 2 W^T - Gl^T
+    const Frag<T> U = f16::mm<T>(GGf, Si, zero);             // O(GG Sinv)
+    const Frag<T> Pf = f16::mm<T>(-U, Si, lb * Si);          // O(P_i)
     const Frag<T> T2 = f16::mm<T>(Dbar, Xf, zero);  // Dbar_{i+1} X_i
     const Frag<T> Q = f16::mm<T>(G, Zf, -T2);       // G Z_i - Dbar X_i
     const Frag<T> R = f16::mm<T>(Xf, Q, zero);      // X_i^T Q
     const Frag<T> V = f16::mm<T>(G, Xf, zero);      // G X_i
     G = f16::mm<T>(Xf, V, Si);                      // Sinv_i + X_i^T V
     f16::wave_sync();
-    io16::put_frag(tA, g, j, R);
+    io16::put_frag(tA, g, j, Pf - R);
     io16::put_frag(tB, g, j, Q - T2);
     f16::wave_sync();
-    Dbar = Pf - T(0.5) * (R + io16::get_frag_t(tA, g, j));
+    Dbar = T(0.5) * ((Pf - R) + io16::get_frag_t(tA, g, j));  // P_i - sym(X_i^T Q)
     io16::store(Cb + i * kBB, lane, io16::get(tB, lane));
     f16::wave_sync();
     io16::put_frag(tC, g, j, Dbar);
@@ -209,10 +209,10 @@ void chain16_vjp_kernel(int L, const T *__restrict__ diag, const T *__restrict__
   };
   i = L - 2;
   for (; i >= 1; i -= 2) {
-    distribute(i, X0, Z0, S0, P0, X1, Z1, S1, P1);
-    distribute(i - 1, X1, Z1, S1, P1, X0, Z0, S0, P0);
+    distribute(i, S0, Q0, C2, E2, S1, Q1, C3, E3);
+    distribute(i - 1, S1, Q1, C3, E3, S0, Q0, C2, E2);
   }
-  if (i == 0) distribute(0, X0, Z0, S0, P0, X1, Z1, S1, P1);
+  if (i == 0) distribute(0, S0, Q0, C2, E2, S1, Q1, C3, E3);
   if (lane == 0 && info) info[m] = 0;
 }
 
