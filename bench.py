@@ -217,7 +217,7 @@ def make_cotangents(kind, inputs, cfg, dt, dev):
     return bars, lb
 
 
-def run_gpu(kind, cfg, dtname, steps, warmup, op="selinv"):
+def run_gpu(kind, cfg, dtname, steps, warmup, op="selinv", graph=False):
     import torch
     import sparse_spd_selected_amd as ssa
     ssa.lib()  # fail loudly if the HIP library is missing
@@ -281,6 +281,10 @@ def run_gpu(kind, cfg, dtname, steps, warmup, op="selinv"):
         e = parent
         plan = ssa.junction_plan(cfg["rows"] * cfg["cols"], e, cfg["b"], dt, dev)
         call = lambda: ssa.junction(inputs[0], e, inputs[1], plan=plan)
+    elif graph:  # the level-set schedule recorded once as a HIP graph, untimed
+        plan = ssa.tree_plan(parent, cfg["b"], dt, dev)
+        g = ssa.tree_graph(parent, *inputs, plan=plan)
+        call = g.launch
     else:
         plan = ssa.tree_plan(parent, cfg["b"], dt, dev)
         call = lambda: ssa.tree(parent, *inputs, plan=plan)
@@ -492,6 +496,8 @@ def main():
                          "sample: the shared-factor siblings")
     ap.add_argument("--k", type=int, default=1, help="right-hand sides for --op solve/sample")
     ap.add_argument("--dtype", default=None, help="f64 or f32 (default: the workload's first)")
+    ap.add_argument("--graph", action="store_true",
+                    help="tree workloads: replay the schedule as one recorded HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-second-dtype", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -516,7 +522,10 @@ def main():
     op = args.op
     if op in ("solve", "sample"):
         cfg["k"] = args.k
-    res = run_gpu(kind, cfg, dtname, args.steps, args.warmup, op)
+    if args.graph and (kind != "tree" or op != "selinv"):
+        print("bench.py: --graph applies to the tree selected inverse only", file=sys.stderr)
+        sys.exit(2)
+    res = run_gpu(kind, cfg, dtname, args.steps, args.warmup, op, graph=args.graph)
     ev = sorted(res["ev_ms"])
     ms_mean = sum(res["ev_ms"]) / len(ev)
     ms_step = res["wall_s"] * 1e3 / args.steps
@@ -542,7 +551,8 @@ def main():
         "vs_baseline": None,
         "dtype": dtname,
         "data": "synthetic (seeded Philox SPD blocks)",
-        "config": dict({"workload": args.workload, "pattern": kind, "op": op}, **cfg),
+        "config": dict({"workload": args.workload, "pattern": kind, "op": op}, **cfg,
+                       **({"graph": True} if args.graph else {})),
         "block_rows_per_s": round(block_rows(kind, cfg) / (ms_step * 1e-3), 1),
         "kernel_ms": {"mean": round(ms_mean, 4), "median": round(ev[len(ev) // 2], 4),
                       "min": round(ev[0], 4)},
@@ -563,7 +573,7 @@ def main():
                            "kernel_source_hash": kernel_source_hash()}
     if not args.no_second_dtype and len(dtypes) > 1 and args.dtype is None:
         other = dtypes[1]
-        r2 = run_gpu(kind, cfg, other, args.steps, args.warmup, op)
+        r2 = run_gpu(kind, cfg, other, args.steps, args.warmup, op, graph=args.graph)
         ms2 = r2["wall_s"] * 1e3 / args.steps
         ev2 = sum(r2["ev_ms"]) / len(r2["ev_ms"])
         w2 = 8 if other == "f64" else 4

@@ -153,6 +153,40 @@ SELINV_API int selinv_tree_f32(const selinv_tree_plan *plan, const float *diag, 
                     float *G_diag, float *G_edge, double *logdet, int32_t *info,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* Tree schedule recorded as one HIP graph.  The batched form on the page
+ * (item Tree: collect over depth levels leaves -> root, then distribute root
+ * -> leaves) issues one batched step per level; here the whole launch
+ * sequence of selinv_tree_f64 / _f32 for fixed buffers -- collect kernels
+ * from the deepest level to the root, distribute kernels from depth 1 down,
+ * then the log-det reduction -- is captured once and replayed with a single
+ * launch.
+ *   selinv_tree_graph_create_*: same arguments, layouts and checks as
+ *     selinv_tree_* (SELINV_ERR_INVALID_ARG on the same conditions), minus
+ *     the stream: capture runs on a private stream.  Nothing is computed at
+ *     creation.  Returns SELINV_ERR_HIP if capture or instantiation fails;
+ *     *out is set only on success.  The plan and every buffer must outlive
+ *     the graph; the graph owns no device memory of its own.
+ *   selinv_tree_graph_launch: replays the graph on `stream`: the outputs are
+ *     recomputed from the current contents of diag and edge, exactly as a
+ *     selinv_tree_* call on that stream would (bitwise the same results).
+ *     Replays of one graph on one stream run in order; replays that overlap
+ *     on different streams race on the shared workspace.
+ *   selinv_tree_graph_nodes: number of kernel launches in the graph, -1 for
+ *     NULL.  selinv_tree_graph_destroy: frees the graph (NULL is ignored);
+ *     no replay may be pending. */
+typedef struct selinv_tree_graph selinv_tree_graph;
+SELINV_API int selinv_tree_graph_create_f64(const selinv_tree_plan *plan, const double *diag,
+                                 const double *edge, double *G_diag, double *G_edge,
+                                 double *logdet, int32_t *info, void *workspace,
+                                 size_t workspace_bytes, selinv_tree_graph **out);
+SELINV_API int selinv_tree_graph_create_f32(const selinv_tree_plan *plan, const float *diag,
+                                 const float *edge, float *G_diag, float *G_edge,
+                                 double *logdet, int32_t *info, void *workspace,
+                                 size_t workspace_bytes, selinv_tree_graph **out);
+SELINV_API int selinv_tree_graph_launch(const selinv_tree_graph *graph, void *stream);
+SELINV_API int64_t selinv_tree_graph_nodes(const selinv_tree_graph *graph);
+SELINV_API void selinv_tree_graph_destroy(selinv_tree_graph *graph);
+
 /* ---------------------------------------------------- reverse mode (VJP)
  * Vector-Jacobian products of the three computations above: given the
  * cotangents of every output, the cotangents of the inputs (the analytic

@@ -86,6 +86,16 @@ def lib():
         f = getattr(L, name)
         f.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         f.restype = ctypes.c_int
+    for name in ("selinv_tree_graph_create_f64", "selinv_tree_graph_create_f32"):
+        f = getattr(L, name)
+        f.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.POINTER(vp)]
+        f.restype = ctypes.c_int
+    L.selinv_tree_graph_launch.argtypes = [vp, vp]
+    L.selinv_tree_graph_launch.restype = ctypes.c_int
+    L.selinv_tree_graph_nodes.argtypes = [vp]
+    L.selinv_tree_graph_nodes.restype = i64
+    L.selinv_tree_graph_destroy.argtypes = [vp]
+    L.selinv_tree_graph_destroy.restype = None
     L.selinv_chain_vjp_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32]
     L.selinv_chain_vjp_workspace_bytes.restype = sz
     L.selinv_star_vjp_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32]
@@ -412,6 +422,76 @@ def tree(parent, diag: torch.Tensor, edge: torch.Tensor, check: bool = False,
     if return_info:
         return G_diag, G_edge, logdet, info
     return G_diag, G_edge, logdet
+
+
+class TreeGraph:
+    """The tree computation for fixed buffers, recorded once as one HIP graph
+    (collect levels deepest first, then distribute levels, then the log-det
+    reduction) and replayed with a single launch.
+
+    ``diag`` and ``edge`` are the graph's input buffers: change their contents
+    in place (``copy_``) between launches.  ``G_diag``, ``G_edge``,
+    ``logdet`` and ``info`` are its output buffers, rewritten by every
+    ``launch()`` on the current stream.
+    """
+
+    def __init__(self, parent, diag: torch.Tensor, edge: torch.Tensor,
+                 plan: TreePlan | None = None):
+        dt, dev = diag.dtype, diag.device
+        sfx = _sfx(diag)
+        if diag.dim() != 3 or diag.shape[1] != diag.shape[2] or edge.shape != diag.shape:
+            raise ValueError("diag and edge must be [n, b, b]")
+        for name, t in (("diag", diag), ("edge", edge)):
+            if (not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.device != dev
+                    or t.dtype != dt or not t.is_contiguous() or t.data_ptr() % 16):
+                raise ValueError("%s must be a contiguous, 16-byte aligned tensor on the "
+                                 "device and dtype of diag (it is the graph's own buffer)"
+                                 % name)
+        n, b = diag.shape[0], diag.shape[1]
+        if plan is None:
+            plan = tree_plan(parent, b, dt, dev)
+        if plan.n != n or plan.b != b or plan.dtype != dt:
+            raise ValueError("plan does not match (n, b, dtype)")
+        self.plan, self.device = plan, dev
+        self.diag, self.edge = diag, edge
+        self.G_diag = torch.empty_like(diag)
+        self.G_edge = torch.empty_like(edge)
+        self.logdet = torch.empty((), dtype=torch.float64, device=dev)
+        self.info = torch.empty((), dtype=torch.int32, device=dev)
+        self._ws = _workspace(plan.workspace_bytes, dev)
+        h = ctypes.c_void_p()
+        with torch.cuda.device(dev):
+            rc = getattr(lib(), "selinv_tree_graph_create_" + sfx)(
+                plan.handle, _ptr(diag), _ptr(edge), _ptr(self.G_diag), _ptr(self.G_edge),
+                self.logdet.data_ptr(), self.info.data_ptr(), _ptr(self._ws),
+                plan.workspace_bytes, ctypes.byref(h))
+        _status(rc, "selinv_tree_graph_create_" + sfx)
+        self._h = h
+        self.nodes = int(lib().selinv_tree_graph_nodes(h))
+
+    def launch(self):
+        """Replay the graph on the current stream; returns (G_diag, G_edge,
+        logdet), the graph's output buffers."""
+        with torch.cuda.device(self.device):
+            rc = lib().selinv_tree_graph_launch(self._h, _stream(self.device))
+        _status(rc, "selinv_tree_graph_launch")
+        return self.G_diag, self.G_edge, self.logdet
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            # no replay may still be pending when the graph is freed
+            with torch.cuda.device(self.device):
+                torch.cuda.synchronize(self.device)
+            _lib.selinv_tree_graph_destroy(h)
+            self._h = None
+
+
+def tree_graph(parent, diag: torch.Tensor, edge: torch.Tensor,
+               plan: TreePlan | None = None) -> TreeGraph:
+    """Record the tree computation on (diag, edge) as a HIP graph; see
+    TreeGraph."""
+    return TreeGraph(parent, diag, edge, plan)
 
 
 # ------------------------------------------------------- reverse mode (VJP)

@@ -1,7 +1,10 @@
 // abi.cpp -- the extern "C" entry points declared in include/selinv.h:
 // argument validation, workspace checks and dispatch to the kernels.  No
-// allocation happens here; all device memory is the caller's.
+// device memory is allocated here; all of it is the caller's (a tree graph
+// holds only its HIP graph objects).
 #include <hip/hip_runtime.h>
+
+#include <new>
 
 #include "internal.h"
 
@@ -53,17 +56,67 @@ int star_entry(int64_t B, int64_t K, int32_t b, const T *center, const T *leaves
 }
 
 template <typename T>
-int tree_entry(const selinv_tree_plan *plan, const T *diag, const T *edge, T *G_diag, T *G_edge,
-               double *logdet, int32_t *info, void *ws, size_t ws_bytes, void *stream) {
+int tree_check(const selinv_tree_plan *plan, const T *diag, const T *edge, T *G_diag, T *G_edge,
+               double *logdet, void *ws, size_t ws_bytes) {
   if (!plan || plan->dtype_bytes != static_cast<int>(sizeof(T))) return SELINV_ERR_INVALID_ARG;
   if (!diag || !edge || !G_diag || !G_edge || !logdet) return SELINV_ERR_INVALID_ARG;
   if (misaligned(diag) || misaligned(edge) || misaligned(G_diag) || misaligned(G_edge))
     return SELINV_ERR_INVALID_ARG;
   const size_t need = selinv::tree_workspace_bytes(plan);
   if (ws_bytes < need || (need && !ws) || misaligned_ws(ws)) return SELINV_ERR_INVALID_ARG;
+  return SELINV_OK;
+}
+
+template <typename T>
+int tree_entry(const selinv_tree_plan *plan, const T *diag, const T *edge, T *G_diag, T *G_edge,
+               double *logdet, int32_t *info, void *ws, size_t ws_bytes, void *stream) {
+  const int rc = tree_check(plan, diag, edge, G_diag, G_edge, logdet, ws, ws_bytes);
+  if (rc != SELINV_OK) return rc;
   const hipError_t e = selinv::tree_launch<T>(plan, diag, edge, G_diag, G_edge, logdet, info, ws,
                                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
+}
+
+// The tree launch sequence captured on a private stream.  The capture is
+// always ended (and the stream destroyed) before returning, also when a
+// launch inside it fails.
+template <typename T>
+int tree_graph_create(const selinv_tree_plan *plan, const T *diag, const T *edge, T *G_diag,
+                      T *G_edge, double *logdet, int32_t *info, void *ws, size_t ws_bytes,
+                      selinv_tree_graph **out) {
+  if (!out) return SELINV_ERR_INVALID_ARG;
+  const int rc = tree_check(plan, diag, edge, G_diag, G_edge, logdet, ws, ws_bytes);
+  if (rc != SELINV_OK) return rc;
+  hipStream_t cap = nullptr;
+  if (hipStreamCreateWithFlags(&cap, hipStreamNonBlocking) != hipSuccess) return SELINV_ERR_HIP;
+  hipGraph_t graph = nullptr;
+  hipError_t e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    const hipError_t el =
+        selinv::tree_launch<T>(plan, diag, edge, G_diag, G_edge, logdet, info, ws, cap);
+    e = hipStreamEndCapture(cap, &graph);
+    if (el != hipSuccess) e = el;
+  }
+  (void)hipStreamDestroy(cap);
+  size_t nodes = 0;
+  hipGraphExec_t exec = nullptr;
+  if (e == hipSuccess) e = hipGraphGetNodes(graph, nullptr, &nodes);
+  if (e == hipSuccess) e = hipGraphInstantiateWithFlags(&exec, graph, 0);
+  selinv_tree_graph *g = nullptr;
+  if (e == hipSuccess) {
+    g = new (std::nothrow) selinv_tree_graph();
+    if (!g) e = hipErrorOutOfMemory;
+  }
+  if (e != hipSuccess) {
+    if (exec) (void)hipGraphExecDestroy(exec);
+    if (graph) (void)hipGraphDestroy(graph);
+    return SELINV_ERR_HIP;
+  }
+  g->graph = graph;
+  g->exec = exec;
+  g->nodes = static_cast<int64_t>(nodes);
+  *out = g;
+  return SELINV_OK;
 }
 
 template <typename T>
@@ -392,6 +445,40 @@ int selinv_tree_f32(const selinv_tree_plan *plan, const float *diag, const float
                     void *workspace, size_t workspace_bytes, void *stream) {
   return tree_entry<float>(plan, diag, edge, G_diag, G_edge, logdet, info, workspace,
                            workspace_bytes, stream);
+}
+
+int selinv_tree_graph_create_f64(const selinv_tree_plan *plan, const double *diag,
+                                 const double *edge, double *G_diag, double *G_edge,
+                                 double *logdet, int32_t *info, void *workspace,
+                                 size_t workspace_bytes, selinv_tree_graph **out) {
+  return tree_graph_create<double>(plan, diag, edge, G_diag, G_edge, logdet, info, workspace,
+                                   workspace_bytes, out);
+}
+
+int selinv_tree_graph_create_f32(const selinv_tree_plan *plan, const float *diag,
+                                 const float *edge, float *G_diag, float *G_edge,
+                                 double *logdet, int32_t *info, void *workspace,
+                                 size_t workspace_bytes, selinv_tree_graph **out) {
+  return tree_graph_create<float>(plan, diag, edge, G_diag, G_edge, logdet, info, workspace,
+                                  workspace_bytes, out);
+}
+
+int selinv_tree_graph_launch(const selinv_tree_graph *graph, void *stream) {
+  if (!graph) return SELINV_ERR_INVALID_ARG;
+  return hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SELINV_OK
+             : SELINV_ERR_HIP;
+}
+
+int64_t selinv_tree_graph_nodes(const selinv_tree_graph *graph) {
+  return graph ? graph->nodes : -1;
+}
+
+void selinv_tree_graph_destroy(selinv_tree_graph *graph) {
+  if (!graph) return;
+  (void)hipGraphExecDestroy(graph->exec);
+  (void)hipGraphDestroy(graph->graph);
+  delete graph;
 }
 
 size_t selinv_chain_vjp_workspace_bytes(int dtype_bytes, int64_t B, int64_t L, int32_t b) {

@@ -110,6 +110,13 @@ struct selinv_tree_plan {
   void *dev_block = nullptr;      // one device allocation backing `dev`
 };
 
+// A tree plan's launch sequence captured for fixed buffers (abi.cpp).
+struct selinv_tree_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int64_t nodes = 0;
+};
+
 namespace selinv {
 
 // ---------------------------------------------------------------- chain

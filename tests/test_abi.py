@@ -126,8 +126,8 @@ def test_python_binding_rejects_cpu_tensors():
 
 
 def test_vjp_workspace_sizes(lib):
-    # b = 16: packed Sinv and P plus X^T and Z per block
-    assert lib.selinv_chain_vjp_workspace_bytes(8, 4096, 64, 16) >= 4096 * 64 * 784 * 8
+    # b = 16: packed Sinv and packed GG per block
+    assert lib.selinv_chain_vjp_workspace_bytes(8, 4096, 64, 16) >= 4096 * 64 * 272 * 8
     assert lib.selinv_chain_vjp_workspace_bytes(4, 3, 5, 7) >= 3 * 5 * 4 * 49 * 4
     assert lib.selinv_chain_vjp_workspace_bytes(8, 1, 0, 4) == 0  # L < 1
     assert lib.selinv_star_vjp_workspace_bytes(8, 2, 3, 33) == 0
@@ -167,6 +167,20 @@ def test_star_and_tree_vjp_argument_validation(lib):
     assert star(wsb=8) == ssa.INVALID_ARG
     assert lib.selinv_tree_vjp_f64(None, p, p, p, p, None, p, p, None, p, 1 << 30, None) == \
         ssa.INVALID_ARG
+
+
+def test_tree_graph_argument_validation(lib):
+    """The tree graph calls reject a missing plan, handle or output pointer
+    before any device work; queries and destroy accept NULL."""
+    p = ctypes.c_void_p(0x1000)
+    h = ctypes.c_void_p()
+    for f in (lib.selinv_tree_graph_create_f64, lib.selinv_tree_graph_create_f32):
+        assert f(None, p, p, p, p, p, None, p, 1 << 30, ctypes.byref(h)) == ssa.INVALID_ARG
+        assert f(None, p, p, p, p, p, None, p, 1 << 30, None) == ssa.INVALID_ARG
+    assert not h.value
+    assert lib.selinv_tree_graph_launch(None, None) == ssa.INVALID_ARG
+    assert lib.selinv_tree_graph_nodes(None) == -1
+    lib.selinv_tree_graph_destroy(None)
 
 
 def test_junction_argument_validation(lib):
