@@ -137,7 +137,11 @@ SELINV_API int selinv_star_f32(int64_t B, int64_t K, int32_t b, const float *cen
  *   G_edge [n][b][b]   (A^-1)_{parent(v),v}; the root slot is written as 0
  *   logdet [1], info [1]   info: v+1 for node v
  * With several bad pivots, info names the first failure in the order
- * (deepest depth first, increasing node index within a depth). */
+ * (deepest depth first, increasing node index within a depth).
+ * For b <= 8 each pass is one launch in which tiles of a level wait for
+ * flags set by the tiles of the level they depend on; every such wait is
+ * bounded (selinv_set_wait_limit), and a call in which one gives up ends
+ * with info = -1, a NaN log det and unusable blocks (it cannot hang). */
 typedef struct selinv_tree_plan selinv_tree_plan;
 
 SELINV_API int selinv_tree_plan_create(const int32_t *parent_host, int64_t n, int32_t b, int dtype_bytes,
@@ -175,6 +179,14 @@ SELINV_API int selinv_tree_f32(const selinv_tree_plan *plan, const float *diag, 
  *     NULL.  selinv_tree_graph_destroy: frees the graph (NULL is ignored);
  *     no replay may be pending. */
 typedef struct selinv_tree_graph selinv_tree_graph;
+/* Bound of each wait inside a single-launch level schedule, in ticks of the
+ * GPU's 100 MHz constant clock (default 2^24, about 0.17 s).  Process-wide;
+ * read when a call is issued (a tree graph keeps the value it was created
+ * with).  A wait that expires makes its call report info = -1.  Meant for
+ * diagnostics and tests of that path: 0 gives up on the first unready flag.
+ * selinv_wait_limit returns the current value. */
+SELINV_API void selinv_set_wait_limit(uint64_t ticks);
+SELINV_API uint64_t selinv_wait_limit(void);
 SELINV_API int selinv_tree_graph_create_f64(const selinv_tree_plan *plan, const double *diag,
                                  const double *edge, double *G_diag, double *G_edge,
                                  double *logdet, int32_t *info, void *workspace,

@@ -90,6 +90,10 @@ def lib():
         f = getattr(L, name)
         f.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.POINTER(vp)]
         f.restype = ctypes.c_int
+    L.selinv_set_wait_limit.argtypes = [ctypes.c_uint64]
+    L.selinv_set_wait_limit.restype = None
+    L.selinv_wait_limit.argtypes = []
+    L.selinv_wait_limit.restype = ctypes.c_uint64
     L.selinv_tree_graph_launch.argtypes = [vp, vp]
     L.selinv_tree_graph_launch.restype = ctypes.c_int
     L.selinv_tree_graph_nodes.argtypes = [vp]
@@ -422,6 +426,18 @@ def tree(parent, diag: torch.Tensor, edge: torch.Tensor, check: bool = False,
     if return_info:
         return G_diag, G_edge, logdet, info
     return G_diag, G_edge, logdet
+
+
+def set_wait_limit(ticks: int):
+    """Bound of each wait inside the single-launch tree schedules, in ticks of
+    the GPU's 100 MHz constant clock (default 2**24).  A call whose wait
+    expires reports info = -1 and a NaN log det.  Process-wide; for
+    diagnostics and tests of that path."""
+    lib().selinv_set_wait_limit(int(ticks))
+
+
+def wait_limit() -> int:
+    return int(lib().selinv_wait_limit())
 
 
 class TreeGraph:

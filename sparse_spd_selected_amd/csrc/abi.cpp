@@ -4,9 +4,20 @@
 // holds only its HIP graph objects).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <new>
 
 #include "internal.h"
+
+namespace selinv {
+
+namespace {
+std::atomic<uint64_t> g_wait_ticks{uint64_t(1) << 24};
+}  // namespace
+
+uint64_t wait_limit_ticks() { return g_wait_ticks.load(std::memory_order_relaxed); }
+
+}  // namespace selinv
 
 namespace {
 
@@ -469,6 +480,12 @@ int selinv_tree_graph_launch(const selinv_tree_graph *graph, void *stream) {
              ? SELINV_OK
              : SELINV_ERR_HIP;
 }
+
+void selinv_set_wait_limit(uint64_t ticks) {
+  selinv::g_wait_ticks.store(ticks, std::memory_order_relaxed);
+}
+
+uint64_t selinv_wait_limit(void) { return selinv::wait_limit_ticks(); }
 
 int64_t selinv_tree_graph_nodes(const selinv_tree_graph *graph) {
   return graph ? graph->nodes : -1;

@@ -45,7 +45,13 @@ struct TreePlanDev {
   int32_t *fail_rank = nullptr;
   int32_t *rank_node = nullptr;
   int32_t *parent_node = nullptr;  // node index of the parent of position p (-1 at the root)
+  // tiles of kTreeTile consecutive positions within one level, levels from
+  // the root down: tile t covers positions [tile_lo[t], tile_hi[t])
+  int32_t *tile_lo = nullptr;
+  int32_t *tile_hi = nullptr;
 };
+
+constexpr int kTreeTile = 8;  // positions per tile (one wavefront of the b <= 8 kernels)
 
 // Device tables of a junction plan (junction_plan.cpp builds them).  Chunks
 // (pieces of supernodes, treated as fat nodes) are numbered level by level.
@@ -106,6 +112,7 @@ struct selinv_tree_plan {
   int32_t levels = 0;
   int64_t *level_off = nullptr;   // host, levels+1 entries
   int32_t max_children = 0;
+  int64_t tiles = 0;              // number of tiles (see TreePlanDev)
   selinv::TreePlanDev dev;
   void *dev_block = nullptr;      // one device allocation backing `dev`
 };

@@ -135,7 +135,19 @@ extern "C" int selinv_tree_plan_create(const int32_t *parent_host, int64_t n, in
   plan->level_off[0] = 0;
   for (int32_t d = 0; d <= H; ++d) plan->level_off[d + 1] = plan->level_off[d] + level_count[d];
 
-  const size_t bytes = 7 * selinv::align_up(n * sizeof(int32_t));
+  // tiles of kTreeTile positions, level by level from the root
+  std::vector<int32_t> tile_lo, tile_hi;
+  for (int32_t d = 0; d <= H; ++d)
+    for (int64_t q = plan->level_off[d]; q < plan->level_off[d + 1]; q += selinv::kTreeTile) {
+      tile_lo.push_back(static_cast<int32_t>(q));
+      tile_hi.push_back(static_cast<int32_t>(std::min<int64_t>(q + selinv::kTreeTile,
+                                                               plan->level_off[d + 1])));
+    }
+  const int64_t T = static_cast<int64_t>(tile_lo.size());
+  plan->tiles = T;
+
+  const size_t bytes =
+      7 * selinv::align_up(n * sizeof(int32_t)) + 2 * selinv::align_up(T * sizeof(int32_t));
   if (hipMalloc(&plan->dev_block, bytes) != hipSuccess) {
     delete[] plan->level_off;
     delete plan;
@@ -150,6 +162,8 @@ extern "C" int selinv_tree_plan_create(const int32_t *parent_host, int64_t n, in
   dv.fail_rank = cv.take<int32_t>(n);
   dv.rank_node = cv.take<int32_t>(n);
   dv.parent_node = cv.take<int32_t>(n);
+  dv.tile_lo = cv.take<int32_t>(T);
+  dv.tile_hi = cv.take<int32_t>(T);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t nb = n * sizeof(int32_t);
   hipError_t e = hipSuccess;
@@ -160,6 +174,9 @@ extern "C" int selinv_tree_plan_create(const int32_t *parent_host, int64_t n, in
       {dv.parent_node, parent_node.data()}};
   for (const auto &c : copies)
     if (e == hipSuccess) e = hipMemcpyAsync(c.first, c.second, nb, hipMemcpyHostToDevice, s);
+  const size_t tb = T * sizeof(int32_t);
+  if (e == hipSuccess) e = hipMemcpyAsync(dv.tile_lo, tile_lo.data(), tb, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(dv.tile_hi, tile_hi.data(), tb, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     selinv_tree_plan_destroy(plan);

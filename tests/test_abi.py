@@ -183,6 +183,18 @@ def test_tree_graph_argument_validation(lib):
     lib.selinv_tree_graph_destroy(None)
 
 
+def test_wait_limit_setting(lib):
+    """The dataflow wait bound is a host-side setting (no device work)."""
+    old = lib.selinv_wait_limit()
+    assert old == 1 << 24
+    try:
+        lib.selinv_set_wait_limit(12345)
+        assert lib.selinv_wait_limit() == 12345
+    finally:
+        lib.selinv_set_wait_limit(old)
+    assert lib.selinv_wait_limit() == old
+
+
 def test_junction_argument_validation(lib):
     """The junction entry points reject bad arguments before touching a device:
     a null plan, sizes and dtypes out of range, bad patterns (checked by the

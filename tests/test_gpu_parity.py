@@ -276,6 +276,25 @@ def test_tree_workload_b8_random(ssa, dt):
     run_tree(ssa, spdgen.random_recursive_tree(262144, 1), 8, DT[dt], seed=1)
 
 
+def test_tree_wait_limit_reports_timeout(ssa):
+    """With a zero wait bound the single-launch schedule gives up at the first
+    unready flag: the call still ends, with info = -1 and a NaN log det.  A
+    path tree makes every tile wait for the one just before it.  With the
+    default bound restored, the same call is exact again."""
+    p = spdgen.path_tree(3000)
+    d, e = spdgen.tree(p, 4, seed=3)
+    D, E = _to(d, torch.float64), _to(e, torch.float64)
+    old = ssa.wait_limit()
+    try:
+        ssa.set_wait_limit(0)
+        _, _, ld, info = ssa.tree(p, D, E, return_info=True)
+        torch.cuda.synchronize()
+    finally:
+        ssa.set_wait_limit(old)
+    assert int(info) == -1 and np.isnan(float(ld))
+    run_tree(ssa, p, 4, torch.float64, seed=3)
+
+
 def test_tree_not_pd_info(ssa):
     p = spdgen.random_recursive_tree(64, 1)
     d, e = spdgen.tree(p, 3)

@@ -57,9 +57,10 @@ def test_tree_graph_replays(ssa, n, b, dt):
     edge = _to(inputs[0][1], dt)
     g = ssa.tree_graph(parent, diag, edge)
     plan = ssa.tree_plan(parent, b, dt, DEV)
-    assert g.nodes >= 2 * plan.levels - 1
-    if b <= 8:  # init, one collect per level, one distribute per level below the root, 2 reductions
-        assert g.nodes == 2 * plan.levels + 2
+    if b <= 8:  # init, one dataflow collect, one dataflow distribute (none for n = 1), 2 reductions
+        assert g.nodes == (5 if n > 1 else 4)
+    else:  # one collect launch per level, one distribute launch per level below the root
+        assert g.nodes >= 2 * plan.levels - 1
     # the eager results of the first input set against the oracle
     Ed, Ee, Eld = ssa.tree(parent, diag, edge)
     torch.cuda.synchronize()
