@@ -14,9 +14,15 @@
 //               G_vv = Sinv_v + B G_pp A
 // Diagonal blocks smaller than 8 are padded with the identity, the others
 // with zeros, so every operation is an 8 x 8 one.  Sinv_v and the messages
-// live in the workspace as padded 8 x 8 blocks indexed by position.
+// live in the workspace as padded 8 x 8 blocks indexed by position; once the
+// parent has consumed a message, the slot holds G_vv for the node's children.
+// Each pass is one launch over the plan's tiles with per-position flags
+// between producer and consumer tiles (dataflow.h); messages, failure flags
+// and the G_vv copies are exchanged through device-coherent accesses in the
+// interleaved layout.
 #include <climits>
 
+#include "dataflow.h"
 #include "internal.h"
 #include "rows8.h"
 
@@ -24,8 +30,7 @@ namespace selinv {
 
 namespace {
 
-constexpr int kWaves = 4;  // wavefronts per workgroup
-constexpr int kSlots = 8;  // nodes per wavefront
+constexpr int kSlots = kTreeTile;  // nodes per wavefront
 
 // row i of a general b x b diagonal block, identity-padded beyond b
 template <typename T>
@@ -65,19 +70,25 @@ __device__ __forceinline__ bool gen_inverse8(r8::Row<T> &a, const r8::Stage<T> &
   return bad;
 }
 
+// Collect of one tile; workgroup w takes tile tiles - 1 - w (deepest level
+// first); flags[p] becomes 1.
 template <typename T>
-__global__ __launch_bounds__(256) void nstree8_collect(
-    int64_t p0, int64_t p1, int b, const int32_t *__restrict__ node_at,
+__global__ __launch_bounds__(64) void nstree8_collect(
+    int32_t tiles, const int32_t *__restrict__ tile_lo, const int32_t *__restrict__ tile_hi,
+    int b, const int32_t *__restrict__ node_at,
     const int32_t *__restrict__ child_beg, const int32_t *__restrict__ child_end,
     const int32_t *__restrict__ fail_rank, const T *__restrict__ diag, const T *__restrict__ up,
     const T *__restrict__ down, T *__restrict__ st_sinv, T *__restrict__ st_m,
-    int32_t *__restrict__ st_fail, int32_t *__restrict__ first_fail) {
-  __shared__ __align__(32) T lds[kWaves][2][kSlots * 64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int32_t *__restrict__ st_fail, int32_t *__restrict__ first_fail,
+    int32_t *__restrict__ flags, int32_t *__restrict__ timeout, uint64_t wait_ticks) {
+  __shared__ __align__(32) T lds[2][kSlots * 64];
+  const uint64_t deadline = wall_clock64() + wait_ticks;
+  const int lane = threadIdx.x;
   const int s = lane >> 3, i = lane & 7;
-  const r8::Stage<T> sa{lds[wave][0]}, sb{lds[wave][1]};
-  const int64_t p = p0 + (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * kSlots + s;
-  const bool valid = p < p1;
+  const r8::Stage<T> sa{lds[0]}, sb{lds[1]};
+  const int32_t t = tiles - 1 - static_cast<int32_t>(blockIdx.x);
+  const int64_t p = tile_lo[t] + s;
+  const bool valid = p < tile_hi[t];
   const int bb = b * b;
   int64_t v = 0;
   int32_t cb = 0, ce = 0;
@@ -86,7 +97,12 @@ __global__ __launch_bounds__(256) void nstree8_collect(
     cb = child_beg[p];
     ce = child_end[p];
   }
-  r8::Row<T> S = load_diag(diag + v * bb, b, i);  // slots past the level re-read node 0
+  r8::Row<T> S = load_diag(diag + v * bb, b, i);  // slots past the tile re-read node 0
+  const bool edge = valid && p != 0;
+  const r8::Row<T> Dn = edge ? r8::load(down + v * bb, b, i) : r8::zero<T>();
+  const r8::Row<T> U = edge ? r8::load(up + v * bb, b, i) : r8::zero<T>();
+  df::wait_flags(flags, cb, ce, 1, i, 8, timeout, deadline);
+  df::acquire();
   bool child_failed = false;
   // children's messages, four loads in flight at a time, subtracted in child order
   for (int32_t c0 = cb; c0 < ce; c0 += 4) {
@@ -95,8 +111,8 @@ __global__ __launch_bounds__(256) void nstree8_collect(
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int32_t c = min(c0 + q, ce - 1);
-      mc[q] = r8::load8(st_m + static_cast<int64_t>(c) * 64, i);
-      fc[q] = st_fail[c];
+      mc[q] = df::load_interleaved(st_m + static_cast<int64_t>(c) * 64, i);
+      fc[q] = df::load_coherent(st_fail + c);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -109,14 +125,11 @@ __global__ __launch_bounds__(256) void nstree8_collect(
   }
   const bool bad = gen_inverse8(S, sa, s, i);
   if (valid && i == 0) {
-    st_fail[p] = (bad || child_failed) ? 1 : 0;
+    df::store_coherent(st_fail + p, (bad || child_failed) ? int32_t(1) : int32_t(0));
     if (bad && !child_failed) atomicMin(first_fail, fail_rank[p]);
   }
   if (valid) r8::store8(st_sinv + p * 64, i, S);
   // message up_v Sinv_v down_v (all slots stage; valid non-root slots store)
-  const bool edge = valid && p != 0;
-  const r8::Row<T> Dn = edge ? r8::load(down + v * bb, b, i) : r8::zero<T>();
-  const r8::Row<T> U = edge ? r8::load(up + v * bb, b, i) : r8::zero<T>();
   f16::wave_sync();
   sb.put(s, i, Dn);
   f16::wave_sync();
@@ -125,33 +138,42 @@ __global__ __launch_bounds__(256) void nstree8_collect(
   sa.put(s, i, X);
   f16::wave_sync();
   const r8::Row<T> M = r8::mul(U, sa, s, r8::zero<T>());  // up_v X
-  if (edge) r8::store8(st_m + p * 64, i, M);
+  if (edge) df::store_interleaved(st_m + p * 64, i, M);
+  df::publish(flags, p, valid && i == 0, 1);
 }
 
+// Distribute of one tile; workgroup w takes tile w + 1 (root level first).
+// Waits for flags[parent] == 2, reads the parent's G (its message slot),
+// stores its own G there and sets flags[p] = 2.
 template <typename T>
-__global__ __launch_bounds__(256) void nstree8_distribute(
-    int64_t p0, int64_t p1, int b, const int32_t *__restrict__ node_at,
-    const int32_t *__restrict__ parent_node, const T *__restrict__ up,
-    const T *__restrict__ down, const T *__restrict__ st_sinv,
-    const int32_t *__restrict__ first_fail, T *__restrict__ G_diag, T *__restrict__ G_up,
-    T *__restrict__ G_down) {
-  __shared__ __align__(32) T lds[kWaves][2][kSlots * 64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__global__ __launch_bounds__(64) void nstree8_distribute(
+    const int32_t *__restrict__ tile_lo, const int32_t *__restrict__ tile_hi, int b,
+    const int32_t *__restrict__ node_at, const int32_t *__restrict__ parent_pos,
+    const T *__restrict__ up, const T *__restrict__ down, const T *__restrict__ st_sinv,
+    T *__restrict__ st_m, const int32_t *__restrict__ first_fail, T *__restrict__ G_diag,
+    T *__restrict__ G_up, T *__restrict__ G_down, int32_t *__restrict__ flags,
+    int32_t *__restrict__ timeout, uint64_t wait_ticks) {
+  __shared__ __align__(32) T lds[2][kSlots * 64];
+  const uint64_t deadline = wall_clock64() + wait_ticks;
+  const int lane = threadIdx.x;
   const int s = lane >> 3, i = lane & 7;
-  const r8::Stage<T> sa{lds[wave][0]}, sb{lds[wave][1]};
-  const int64_t p = p0 + (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * kSlots + s;
-  const bool valid = p < p1;
+  const r8::Stage<T> sa{lds[0]}, sb{lds[1]};
+  const int32_t t = static_cast<int32_t>(blockIdx.x) + 1;
+  const int64_t p = tile_lo[t] + s;
+  const bool valid = p < tile_hi[t];
   const int bb = b * b;
-  const bool failed = *first_fail != INT_MAX;
-  int64_t v = 0, u = 0;
+  int64_t v = 0, q = 0;
   if (valid) {
     v = node_at[p];
-    u = parent_node[p];
+    q = parent_pos[p];
   }
   const r8::Row<T> Si = valid ? r8::load8(st_sinv + p * 64, i) : r8::zero<T>();
   const r8::Row<T> U = valid ? r8::load(up + v * bb, b, i) : r8::zero<T>();
   const r8::Row<T> Dn = valid ? r8::load(down + v * bb, b, i) : r8::zero<T>();
-  const r8::Row<T> G = valid ? r8::load(G_diag + u * bb, b, i) : r8::zero<T>();
+  if (valid && i == 0) df::wait_flags(flags, q, q + 1, 2, 0, 1, timeout, deadline);
+  df::acquire();
+  const bool failed = *first_fail != INT_MAX || df::timed_out(timeout);
+  const r8::Row<T> G = valid ? df::load_interleaved(st_m + q * 64, i) : r8::zero<T>();
   sa.put(s, i, Si);
   sb.put(s, i, Dn);
   f16::wave_sync();
@@ -167,30 +189,36 @@ __global__ __launch_bounds__(256) void nstree8_distribute(
   sa.put(s, i, V);
   f16::wave_sync();
   const r8::Row<T> Gv = r8::mul(Bm, sa, s, Si);              // Sinv_v + B G_pp A
-  if (!valid) return;
-  if (failed) {
-    r8::Row<T> nan;
+  if (valid) {
+    if (failed) {
+      r8::Row<T> nan;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) nan.v[k] = static_cast<T>(__builtin_nan(""));
-    r8::store(G_up + v * bb, b, i, nan);
-    r8::store(G_down + v * bb, b, i, nan);
-    r8::store(G_diag + v * bb, b, i, nan);
-    return;
+      for (int k = 0; k < 8; ++k) nan.v[k] = static_cast<T>(__builtin_nan(""));
+      r8::store(G_up + v * bb, b, i, nan);
+      r8::store(G_down + v * bb, b, i, nan);
+      r8::store(G_diag + v * bb, b, i, nan);
+    } else {
+      r8::store(G_up + v * bb, b, i, r8::neg(V));
+      r8::store(G_down + v * bb, b, i, r8::neg(W));
+      r8::store(G_diag + v * bb, b, i, Gv);
+      df::store_interleaved(st_m + p * 64, i, Gv);  // for the children
+    }
   }
-  r8::store(G_up + v * bb, b, i, r8::neg(V));
-  r8::store(G_down + v * bb, b, i, r8::neg(W));
-  r8::store(G_diag + v * bb, b, i, Gv);
+  df::publish(flags, p, valid && i == 0, 2);
 }
 
-// the root: G_rr = Sinv_r (NaN after a failure), zero edge slots, info
+// the root (a launch between the passes): G_rr = Sinv_r (NaN after a
+// failure), zero edge slots; G_rr also goes to the root's message slot
+// (interleaved, element (i, c) at c * 8 + i) for its children, and
+// flags[0] = 2
 template <typename T>
 __global__ __launch_bounds__(64) void nstree8_root(int b, const int32_t *__restrict__ node_at,
-                                                   const int32_t *__restrict__ rank_node,
                                                    const T *__restrict__ st_sinv,
+                                                   T *__restrict__ st_m,
                                                    const int32_t *__restrict__ first_fail,
                                                    T *__restrict__ G_diag, T *__restrict__ G_up,
                                                    T *__restrict__ G_down,
-                                                   int32_t *__restrict__ info) {
+                                                   int32_t *__restrict__ flags) {
   const int bb = b * b;
   const int64_t r = node_at[0];
   const bool failed = *first_fail != INT_MAX;
@@ -200,17 +228,25 @@ __global__ __launch_bounds__(64) void nstree8_root(int b, const int32_t *__restr
     G_up[r * bb + e] = T(0);
     G_down[r * bb + e] = T(0);
   }
-  if (threadIdx.x == 0 && info) *info = failed ? rank_node[*first_fail] + 1 : 0;
+  const int row = threadIdx.x >> 3, c = threadIdx.x & 7;  // the padded 8 x 8 block
+  st_m[c * 8 + row] = st_sinv[row * 8 + c];
+  if (threadIdx.x == 0) flags[0] = 2;
 }
 
-__global__ void nstree8_init(int32_t *first_fail) { *first_fail = INT_MAX; }
+// info = -1 if a dataflow wait gave up
+__global__ void nstree8_finish(const int32_t *__restrict__ rank_node,
+                               const int32_t *__restrict__ first_fail,
+                               const int32_t *__restrict__ timeout, int32_t *__restrict__ info) {
+  if (info)
+    *info = *timeout != 0 ? -1 : *first_fail != INT_MAX ? rank_node[*first_fail] + 1 : 0;
+}
 
 }  // namespace
 
 size_t nstree8_workspace_bytes(const selinv_tree_plan *plan) {
   const size_t n = plan->n;
-  return 2 * align_up(n * 64 * plan->dtype_bytes) + align_up(n * sizeof(int32_t)) +
-         align_up(sizeof(int32_t));
+  return 2 * align_up(n * 64 * plan->dtype_bytes) + 2 * align_up(n * sizeof(int32_t)) +
+         2 * align_up(sizeof(int32_t));
 }
 
 template <typename T>
@@ -223,24 +259,24 @@ hipError_t nstree8_launch(const selinv_tree_plan *plan, const T *diag, const T *
   T *st_m = cv.take<T>(n * 64);
   int32_t *st_fail = cv.take<int32_t>(n);
   int32_t *first_fail = cv.take<int32_t>(1);
+  int32_t *flags = cv.take<int32_t>(n);
+  int32_t *timeout = cv.take<int32_t>(1);
   const TreePlanDev &d = plan->dev;
-  const int64_t per_block = kWaves * kSlots;
-  hipLaunchKernelGGL(nstree8_init, dim3(1), dim3(1), 0, s, first_fail);
-  for (int32_t lev = plan->levels - 1; lev >= 0; --lev) {
-    const int64_t p0 = plan->level_off[lev], p1 = plan->level_off[lev + 1];
-    const unsigned grid = static_cast<unsigned>((p1 - p0 + per_block - 1) / per_block);
-    hipLaunchKernelGGL(nstree8_collect<T>, dim3(grid), dim3(256), 0, s, p0, p1, b, d.node_at,
-                       d.child_beg, d.child_end, d.fail_rank, diag, up, down, st_sinv, st_m,
-                       st_fail, first_fail);
-  }
-  hipLaunchKernelGGL(nstree8_root<T>, dim3(1), dim3(64), 0, s, b, d.node_at, d.rank_node, st_sinv,
-                     first_fail, G_diag, G_up, G_down, info);
-  for (int32_t lev = 1; lev < plan->levels; ++lev) {
-    const int64_t p0 = plan->level_off[lev], p1 = plan->level_off[lev + 1];
-    const unsigned grid = static_cast<unsigned>((p1 - p0 + per_block - 1) / per_block);
-    hipLaunchKernelGGL(nstree8_distribute<T>, dim3(grid), dim3(256), 0, s, p0, p1, b, d.node_at,
-                       d.parent_node, up, down, st_sinv, first_fail, G_diag, G_up, G_down);
-  }
+  const int32_t tiles = static_cast<int32_t>(plan->tiles);
+  const uint64_t wt = wait_limit_ticks();
+  hipError_t e = df::launch_init(n, flags, first_fail, timeout, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(nstree8_collect<T>, dim3(tiles), dim3(64), 0, s, tiles, d.tile_lo,
+                     d.tile_hi, b, d.node_at, d.child_beg, d.child_end, d.fail_rank, diag, up,
+                     down, st_sinv, st_m, st_fail, first_fail, flags, timeout, wt);
+  hipLaunchKernelGGL(nstree8_root<T>, dim3(1), dim3(64), 0, s, b, d.node_at, st_sinv, st_m,
+                     first_fail, G_diag, G_up, G_down, flags);
+  if (tiles > 1)
+    hipLaunchKernelGGL(nstree8_distribute<T>, dim3(tiles - 1), dim3(64), 0, s, d.tile_lo,
+                       d.tile_hi, b, d.node_at, d.parent_pos, up, down, st_sinv, st_m,
+                       first_fail, G_diag, G_up, G_down, flags, timeout, wt);
+  hipLaunchKernelGGL(nstree8_finish, dim3(1), dim3(1), 0, s, d.rank_node, first_fail, timeout,
+                     info);
   return hipGetLastError();
 }
 

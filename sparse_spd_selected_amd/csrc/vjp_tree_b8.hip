@@ -21,8 +21,14 @@
 //     G_vv = Sinv_v + X_v^T G_uu X_v
 // Workspace per position (8 x 8 each): Sinv, P, X, Z, M, N; the M slot holds
 // G_vv in the distribute pass (the parent has consumed M by then).
+// Each pass is one launch over the plan's tiles with per-position flags
+// between producer and consumer tiles (dataflow.h): M, N and the failure
+// flags (collect) and the M slot and diag_bar (distribute) are exchanged
+// through device-coherent accesses, M / N / G in the interleaved layout,
+// diag_bar (exactly symmetric) transposed.
 #include <climits>
 
+#include "dataflow.h"
 #include "internal.h"
 #include "rows8.h"
 
@@ -30,8 +36,7 @@ namespace selinv {
 
 namespace {
 
-constexpr int kWaves = 4;  // wavefronts per workgroup
-constexpr int kSlots = 8;  // nodes per wavefront
+constexpr int kSlots = kTreeTile;  // nodes per wavefront
 enum { kSinv = 0, kP, kX, kZ, kM, kN, kArrays };
 constexpr int kChildBatch = 2;  // children's (M, N) pairs loaded together
 
@@ -70,20 +75,26 @@ __device__ __forceinline__ r8::Row<T> sym_rows(const r8::Row<T> &r, const r8::St
   return axpby(T(0.5), r, T(0.5), column(st, s, i));
 }
 
+// Collect of one tile; workgroup w takes tile tiles - 1 - w (deepest level
+// first); flags[p] becomes 1 (2 for the root).
 template <typename T>
-__global__ __launch_bounds__(256) void tree8_vjp_collect(
-    int64_t p0, int64_t p1, int b, const int32_t *__restrict__ node_at,
+__global__ __launch_bounds__(64) void tree8_vjp_collect(
+    int32_t tiles, const int32_t *__restrict__ tile_lo, const int32_t *__restrict__ tile_hi,
+    int b, const int32_t *__restrict__ node_at,
     const int32_t *__restrict__ child_beg, const int32_t *__restrict__ child_end,
     const int32_t *__restrict__ fail_rank, const T *__restrict__ diag, const T *__restrict__ edge,
     const T *__restrict__ gd, const T *__restrict__ ge, const double *__restrict__ ld_bar,
     T *__restrict__ st, int64_t n, int32_t *__restrict__ st_fail,
-    int32_t *__restrict__ first_fail, T *__restrict__ d_bar, T *__restrict__ e_bar) {
-  __shared__ __align__(32) T lds[kWaves][2][kSlots * 64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int32_t *__restrict__ first_fail, T *__restrict__ d_bar, T *__restrict__ e_bar,
+    int32_t *__restrict__ flags, int32_t *__restrict__ timeout, uint64_t wait_ticks) {
+  __shared__ __align__(32) T lds[2][kSlots * 64];
+  const uint64_t deadline = wall_clock64() + wait_ticks;
+  const int lane = threadIdx.x;
   const int s = lane >> 3, i = lane & 7;
-  const r8::Stage<T> sa{lds[wave][0]}, sb{lds[wave][1]};
-  const int64_t p = p0 + (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * kSlots + s;
-  const bool valid = p < p1;
+  const r8::Stage<T> sa{lds[0]}, sb{lds[1]};
+  const int32_t t = tiles - 1 - static_cast<int32_t>(blockIdx.x);
+  const int64_t p = tile_lo[t] + s;
+  const bool valid = p < tile_hi[t];
   const int bb = b * b;
   const T lb = ld_bar ? static_cast<T>(*ld_bar) : T(0);
   auto arr = [&](int k) { return st + k * n * 64; };
@@ -99,6 +110,8 @@ __global__ __launch_bounds__(256) void tree8_vjp_collect(
   const r8::Row<T> E = r8::load(edge + v * bb, b, i);
   const r8::Row<T> Ge = r8::load(ge + v * bb, b, i);
   r8::Row<T> GG = sym_rows(r8::load(gd + v * bb, b, i), sb, s, i);
+  df::wait_flags(flags, cb, ce, 1, i, 8, timeout, deadline);
+  df::acquire();
   bool child_failed = false;
   for (int32_t c0 = cb; c0 < ce; c0 += kChildBatch) {  // children in flight, summed in order
     r8::Row<T> mc[kChildBatch], nc[kChildBatch];
@@ -106,9 +119,9 @@ __global__ __launch_bounds__(256) void tree8_vjp_collect(
 #pragma unroll
     for (int q = 0; q < kChildBatch; ++q) {
       const int64_t c = min(c0 + q, ce - 1);
-      mc[q] = r8::load8(arr(kM) + c * 64, i);
-      nc[q] = r8::load8(arr(kN) + c * 64, i);
-      fc[q] = st_fail[c];
+      mc[q] = df::load_interleaved(arr(kM) + c * 64, i);
+      nc[q] = df::load_interleaved(arr(kN) + c * 64, i);
+      fc[q] = df::load_coherent(st_fail + c);
     }
 #pragma unroll
     for (int q = 0; q < kChildBatch; ++q) {
@@ -125,7 +138,7 @@ __global__ __launch_bounds__(256) void tree8_vjp_collect(
   f16::PivotLog pl;
   const bool bad = r8::gj_inverse(S, sa, s, i, pl);  // S <- Sinv
   if (valid && i == 0) {
-    st_fail[p] = (bad || child_failed) ? 1 : 0;
+    df::store_coherent(st_fail + p, (bad || child_failed) ? int32_t(1) : int32_t(0));
     if (bad && !child_failed) atomicMin(first_fail, fail_rank[p]);
   }
   // P = sym(lb Sinv - Sinv (GG Sinv))
@@ -143,10 +156,12 @@ __global__ __launch_bounds__(256) void tree8_vjp_collect(
     r8::store8(arr(kP) + p * 64, i, P);
   }
   if (valid && p == 0) {  // the root: diag_bar = P, G_rr = Sinv (in its M slot)
-    const bool failed = bad || child_failed || *first_fail != INT_MAX;
+    // every other collect has published before the root runs; first_fail is
+    // read coherently (another XCD may have lowered it)
+    const bool failed = bad || child_failed || df::load_coherent(first_fail) != INT_MAX;
     r8::store(d_bar + v * bb, b, i, failed ? nan_row<T>() : P);
     r8::store(e_bar + v * bb, b, i, r8::zero<T>());
-    r8::store8(arr(kM) + p * 64, i, S);
+    df::store_interleaved(arr(kM) + p * 64, i, S);
   }
   // messages to the parent; sa still holds Sinv
   const r8::Row<T> X = r8::mul(E, sa, s, r8::zero<T>());  // E Sinv
@@ -167,23 +182,31 @@ __global__ __launch_bounds__(256) void tree8_vjp_collect(
   if (valid && p != 0) {
     r8::store8(arr(kX) + p * 64, i, X);
     r8::store8(arr(kZ) + p * 64, i, Z);
-    r8::store8(arr(kM) + p * 64, i, M);
-    r8::store8(arr(kN) + p * 64, i, N);
+    df::store_interleaved(arr(kM) + p * 64, i, M);
+    df::store_interleaved(arr(kN) + p * 64, i, N);
   }
+  df::publish(flags, p, valid && i == 0, p == 0 ? 2 : 1);
 }
 
+// Distribute of one tile; workgroup w takes tile w + 1 (root level first).
+// Waits for flags[parent] == 2, then reads the parent's G (M slot) and
+// diag_bar; sets flags[p] = 2.
 template <typename T>
-__global__ __launch_bounds__(256) void tree8_vjp_distribute(
-    int64_t p0, int64_t p1, int b, const int32_t *__restrict__ node_at,
+__global__ __launch_bounds__(64) void tree8_vjp_distribute(
+    const int32_t *__restrict__ tile_lo, const int32_t *__restrict__ tile_hi, int b,
+    const int32_t *__restrict__ node_at,
     const int32_t *__restrict__ parent_pos, const int32_t *__restrict__ parent_node,
     T *__restrict__ st, int64_t n, const int32_t *__restrict__ first_fail,
-    T *__restrict__ d_bar, T *__restrict__ e_bar) {
-  __shared__ __align__(32) T lds[kWaves][2][kSlots * 64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    T *__restrict__ d_bar, T *__restrict__ e_bar, int32_t *__restrict__ flags,
+    int32_t *__restrict__ timeout, uint64_t wait_ticks) {
+  __shared__ __align__(32) T lds[2][kSlots * 64];
+  const uint64_t deadline = wall_clock64() + wait_ticks;
+  const int lane = threadIdx.x;
   const int s = lane >> 3, i = lane & 7;
-  const r8::Stage<T> sa{lds[wave][0]}, sb{lds[wave][1]};
-  const int64_t p = p0 + (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * kSlots + s;
-  const bool valid = p < p1;
+  const r8::Stage<T> sa{lds[0]}, sb{lds[1]};
+  const int32_t t = static_cast<int32_t>(blockIdx.x) + 1;
+  const int64_t p = tile_lo[t] + s;
+  const bool valid = p < tile_hi[t];
   const int bb = b * b;
   auto arr = [&](int k) { return st + k * n * 64; };
   int64_t v = 0, u = 0, q = 0, pp = 0;
@@ -193,12 +216,14 @@ __global__ __launch_bounds__(256) void tree8_vjp_distribute(
     q = parent_pos[p];
     pp = p;
   }
-  const r8::Row<T> G = r8::load8(arr(kM) + q * 64, i);  // G of the parent
-  const r8::Row<T> Db = r8::load(d_bar + u * bb, b, i);
   const r8::Row<T> X = r8::load8(arr(kX) + pp * 64, i);
   const r8::Row<T> Z = r8::load8(arr(kZ) + pp * 64, i);
   const r8::Row<T> P = r8::load8(arr(kP) + pp * 64, i);
   const r8::Row<T> Si = r8::load8(arr(kSinv) + pp * 64, i);
+  if (valid && i == 0) df::wait_flags(flags, q, q + 1, 2, 0, 1, timeout, deadline);
+  df::acquire();
+  const r8::Row<T> G = df::load_interleaved(arr(kM) + q * 64, i);  // G of the parent
+  const r8::Row<T> Db = df::load_transposed(d_bar + u * bb, b, i);
   sa.put(s, i, X);
   sb.put(s, i, Z);
   f16::wave_sync();
@@ -215,31 +240,34 @@ __global__ __launch_bounds__(256) void tree8_vjp_distribute(
   f16::wave_sync();
   const r8::Row<T> Gv = r8::mul_tn(sa, sb, s, i, Si);  // Sinv + X^T V
   const r8::Row<T> Dn = axpby(T(1), P, T(-1), sym_rows(R, sb, s, i));
-  if (!valid) return;
-  if (*first_fail != INT_MAX) {
-    r8::store(e_bar + v * bb, b, i, nan_row<T>());
-    r8::store(d_bar + v * bb, b, i, nan_row<T>());
-    return;
+  if (valid) {
+    if (*first_fail != INT_MAX || df::timed_out(timeout)) {
+      r8::store(e_bar + v * bb, b, i, nan_row<T>());
+      df::store_transposed(d_bar + v * bb, b, i, nan_row<T>());
+    } else {
+      r8::store(e_bar + v * bb, b, i, Eb);
+      df::store_transposed(d_bar + v * bb, b, i, Dn);
+      df::store_interleaved(arr(kM) + p * 64, i, Gv);
+    }
   }
-  r8::store(e_bar + v * bb, b, i, Eb);
-  r8::store(d_bar + v * bb, b, i, Dn);
-  r8::store8(arr(kM) + p * 64, i, Gv);
+  df::publish(flags, p, valid && i == 0, 2);
 }
 
-__global__ void tree8_vjp_init(int32_t *first_fail) { *first_fail = INT_MAX; }
-
+// info = -1 if a dataflow wait gave up
 __global__ void tree8_vjp_finish(const int32_t *__restrict__ rank_node,
                                  const int32_t *__restrict__ first_fail,
+                                 const int32_t *__restrict__ timeout,
                                  int32_t *__restrict__ info) {
-  if (info) *info = *first_fail != INT_MAX ? rank_node[*first_fail] + 1 : 0;
+  if (info)
+    *info = *timeout != 0 ? -1 : *first_fail != INT_MAX ? rank_node[*first_fail] + 1 : 0;
 }
 
 }  // namespace
 
 size_t tree8_vjp_workspace_bytes(const selinv_tree_plan *plan) {
   const size_t n = plan->n;
-  return align_up(kArrays * n * 64 * plan->dtype_bytes) + align_up(n * sizeof(int32_t)) +
-         align_up(sizeof(int32_t));
+  return align_up(kArrays * n * 64 * plan->dtype_bytes) + 2 * align_up(n * sizeof(int32_t)) +
+         2 * align_up(sizeof(int32_t));
 }
 
 template <typename T>
@@ -252,23 +280,22 @@ hipError_t tree8_vjp_launch(const selinv_tree_plan *plan, const T *diag, const T
   T *st = cv.take<T>(kArrays * n * 64);
   int32_t *st_fail = cv.take<int32_t>(n);
   int32_t *first_fail = cv.take<int32_t>(1);
+  int32_t *flags = cv.take<int32_t>(n);
+  int32_t *timeout = cv.take<int32_t>(1);
   const TreePlanDev &d = plan->dev;
-  const int64_t per_block = kWaves * kSlots;
-  hipLaunchKernelGGL(tree8_vjp_init, dim3(1), dim3(1), 0, s, first_fail);
-  for (int32_t lev = plan->levels - 1; lev >= 0; --lev) {
-    const int64_t p0 = plan->level_off[lev], p1 = plan->level_off[lev + 1];
-    const unsigned grid = static_cast<unsigned>((p1 - p0 + per_block - 1) / per_block);
-    hipLaunchKernelGGL(tree8_vjp_collect<T>, dim3(grid), dim3(256), 0, s, p0, p1, b, d.node_at,
-                       d.child_beg, d.child_end, d.fail_rank, diag, edge, gd, ge, ld_bar, st, n,
-                       st_fail, first_fail, d_bar, e_bar);
-  }
-  for (int32_t lev = 1; lev < plan->levels; ++lev) {
-    const int64_t p0 = plan->level_off[lev], p1 = plan->level_off[lev + 1];
-    const unsigned grid = static_cast<unsigned>((p1 - p0 + per_block - 1) / per_block);
-    hipLaunchKernelGGL(tree8_vjp_distribute<T>, dim3(grid), dim3(256), 0, s, p0, p1, b,
-                       d.node_at, d.parent_pos, d.parent_node, st, n, first_fail, d_bar, e_bar);
-  }
-  hipLaunchKernelGGL(tree8_vjp_finish, dim3(1), dim3(1), 0, s, d.rank_node, first_fail, info);
+  const int32_t tiles = static_cast<int32_t>(plan->tiles);
+  const uint64_t wt = wait_limit_ticks();
+  hipError_t e = df::launch_init(n, flags, first_fail, timeout, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(tree8_vjp_collect<T>, dim3(tiles), dim3(64), 0, s, tiles, d.tile_lo,
+                     d.tile_hi, b, d.node_at, d.child_beg, d.child_end, d.fail_rank, diag, edge,
+                     gd, ge, ld_bar, st, n, st_fail, first_fail, d_bar, e_bar, flags, timeout, wt);
+  if (tiles > 1)
+    hipLaunchKernelGGL(tree8_vjp_distribute<T>, dim3(tiles - 1), dim3(64), 0, s, d.tile_lo,
+                       d.tile_hi, b, d.node_at, d.parent_pos, d.parent_node, st, n, first_fail,
+                       d_bar, e_bar, flags, timeout, wt);
+  hipLaunchKernelGGL(tree8_vjp_finish, dim3(1), dim3(1), 0, s, d.rank_node, first_fail, timeout,
+                     info);
   return hipGetLastError();
 }
 
