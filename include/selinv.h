@@ -350,7 +350,9 @@ SELINV_API int selinv_star_sample_f32(int64_t B, int64_t K, int32_t b, const flo
                            const float *z_leaves, float *x_center, float *x_leaves,
                            void *stream);
 
-/* tree: vectors [n][b][k] by node index */
+/* tree: vectors [n][b][k] by node index.  For b <= 8 the solve runs both
+ * sweeps as single launches with bounded waits (see selinv_tree_f64); a solve
+ * whose wait gives up returns NaN in x. */
 SELINV_API size_t selinv_tree_factor_bytes(const selinv_tree_plan *plan);
 SELINV_API size_t selinv_tree_factor_workspace_bytes(const selinv_tree_plan *plan);
 SELINV_API size_t selinv_tree_solve_workspace_bytes(const selinv_tree_plan *plan, int64_t k);

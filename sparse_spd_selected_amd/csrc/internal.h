@@ -266,6 +266,11 @@ template <typename T>
 hipError_t tree_factor_launch(const selinv_tree_plan *plan, const T *diag, const T *edge,
                               T *factor, double *logdet, int32_t *info, void *ws, hipStream_t s);
 size_t tree_apply_workspace_bytes(const selinv_tree_plan *plan, int64_t k);
+// b <= 8 solve on the single-launch schedule (tree_b8.hip)
+size_t tree8_solve_workspace_bytes(const selinv_tree_plan *plan, int64_t k);
+template <typename T>
+hipError_t tree8_solve_launch(const selinv_tree_plan *plan, int64_t k, const T *edge,
+                              const T *factor, const T *y, T *x, void *ws, hipStream_t s);
 template <typename T>
 hipError_t tree_apply_launch(const selinv_tree_plan *plan, int64_t k, bool sample, const T *edge,
                              const T *factor, const T *in, T *out, void *ws, hipStream_t s);

@@ -583,6 +583,7 @@ hipError_t tree_factor_launch(const selinv_tree_plan *plan, const T *diag, const
 }
 
 size_t tree_apply_workspace_bytes(const selinv_tree_plan *plan, int64_t k) {
+  if (plan->b <= 8) return tree8_solve_workspace_bytes(plan, k);
   return align_up(static_cast<size_t>(plan->n) * plan->b * k * plan->dtype_bytes);
 }
 
@@ -590,6 +591,7 @@ template <typename T>
 hipError_t tree_apply_launch(const selinv_tree_plan *plan, int64_t k, bool sample, const T *edge,
                              const T *factor, const T *in, T *out, void *ws, hipStream_t s) {
   if (k == 0) return hipSuccess;
+  if (!sample && plan->b <= 8) return tree8_solve_launch<T>(plan, k, edge, factor, in, out, ws, s);
   const int b = plan->b;
   const int nch = nchunks(k);
   const int nt = sf_threads(b);

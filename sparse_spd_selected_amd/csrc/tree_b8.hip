@@ -19,6 +19,7 @@
 // consecutive levels overlap.  Sinv_v lives in the workspace as a padded
 // 8 x 8 block indexed by position, M_v as an interleaved 8 x 8 block; X_v is
 // recomputed from the re-read edge block.
+#include <algorithm>
 #include <climits>
 
 #include "dataflow.h"
@@ -179,6 +180,163 @@ __global__ __launch_bounds__(64) void tree8_distribute(
   df::publish(flags, p, valid && i == 0, 2);
 }
 
+// ------------------------------------------------------------------ solve
+// x = A^-1 y from the shared factor (packed lower triangle of Sinv_v per
+// position, r (r + 1) / 2 + c, padded to a multiple of 4 entries):
+//   forward, children first:  u_v = y_v - sum_children E_c w_c,  w_v = Sinv_v u_v
+//   backward, parents first:  x_v = w_v - Sinv_v E_v^T x_parent  (x_root = w_root)
+// Right-hand sides go in chunks of kw = min(k, 8) columns; lane (s, i) holds
+// row i of its node's b x kw chunk, zero-padded to 8 x 8, so every step is an
+// 8 x 8 product.  Both passes are single launches over (tile, chunk) pairs on
+// the dataflow schedule; flags and messages are chunk-major, the message
+// E_v w_v at [chunk][position][c * 8 + i].  x is written by the forward pass
+// (w_v) and overwritten by the backward pass (coherently: children read it).
+// A call whose dataflow wait gives up leaves NaN in x (at least in the
+// blocks of the workgroups that saw it, all of them if it was the forward).
+constexpr int kSolveCols = 8;
+
+template <typename T>
+__device__ __forceinline__ r8::Row<T> packed_row(const T *P, int b, int i) {
+  r8::Row<T> r;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    r.v[c] = (i < b && c < b) ? P[c <= i ? i * (i + 1) / 2 + c : c * (c + 1) / 2 + i] : T(0);
+  return r;
+}
+
+// row i of the b x kc chunk of node v's k columns, starting at column c0
+template <typename T, bool kCoherent>
+__device__ __forceinline__ r8::Row<T> load_cols(const T *X, int64_t v, int b, int64_t k,
+                                                int64_t c0, int kc, int i) {
+  r8::Row<T> r;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const T *a = X + (v * b + i) * k + c0 + c;
+    r.v[c] = (i < b && c < kc) ? (kCoherent ? df::load_coherent(a) : *a) : T(0);
+  }
+  return r;
+}
+
+template <typename T, bool kCoherent>
+__device__ __forceinline__ void store_cols(T *X, int64_t v, int b, int64_t k, int64_t c0, int kc,
+                                           int i, const r8::Row<T> &r) {
+  if (i >= b) return;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    T *a = X + (v * b + i) * k + c0 + c;
+    if (c < kc) {
+      if (kCoherent)
+        df::store_coherent(a, r.v[c]);
+      else
+        *a = r.v[c];
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void tree8_solve_fwd(
+    int32_t tiles, int nch, int64_t n, int64_t k, int kw, const int32_t *__restrict__ tile_lo,
+    const int32_t *__restrict__ tile_hi, int b, const int32_t *__restrict__ node_at,
+    const int32_t *__restrict__ child_beg, const int32_t *__restrict__ child_end,
+    const T *__restrict__ edge, const T *__restrict__ factor, const T *__restrict__ y,
+    T *__restrict__ x, T *__restrict__ msg, int32_t *__restrict__ flags,
+    int32_t *__restrict__ timeout, uint64_t wait_ticks) {
+  __shared__ __align__(32) T lds[2][kSlots * 64];
+  const uint64_t deadline = wall_clock64() + wait_ticks;
+  const int lane = threadIdx.x;
+  const int s = lane >> 3, i = lane & 7;
+  const r8::Stage<T> sa{lds[0]}, sb{lds[1]};
+  const int chunk = static_cast<int>(blockIdx.x % nch);
+  const int32_t t = tiles - 1 - static_cast<int32_t>(blockIdx.x / nch);
+  const int64_t c0 = int64_t(chunk) * kSolveCols;
+  const int kc = static_cast<int>(min<int64_t>(kw, k - c0));
+  const int64_t p = tile_lo[t] + s;
+  const bool valid = p < tile_hi[t];
+  const int bb = b * b, pk = (b * (b + 1) / 2 + 3) / 4 * 4;
+  int64_t v = 0;
+  int32_t cb = 0, ce = 0;
+  if (valid) {
+    v = node_at[p];
+    cb = child_beg[p];
+    ce = child_end[p];
+  }
+  const r8::Row<T> Si = valid ? packed_row(factor + p * pk, b, i) : r8::zero<T>();
+  r8::Row<T> U = valid ? load_cols<T, false>(y, v, b, k, c0, kc, i) : r8::zero<T>();
+  const r8::Row<T> E = (valid && p != 0) ? r8::load(edge + v * bb, b, i) : r8::zero<T>();
+  int32_t *fl = flags + chunk * n;
+  T *mg = msg + chunk * n * (8 * kw);
+  df::wait_flags(fl, cb, ce, 1, i, 8, timeout, deadline);
+  df::acquire();
+  for (int32_t c = cb; c < ce; ++c) {  // children in order
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      if (cc < kc) U.v[cc] -= df::load_coherent(mg + int64_t(c) * (8 * kw) + cc * 8 + i);
+  }
+  sa.put(s, i, U);
+  f16::wave_sync();
+  const r8::Row<T> W = r8::mul(Si, sa, s, r8::zero<T>());  // Sinv_v u_v
+  if (valid) store_cols<T, false>(x, v, b, k, c0, kc, i, W);
+  sb.put(s, i, W);
+  f16::wave_sync();
+  const r8::Row<T> M = r8::mul(E, sb, s, r8::zero<T>());  // E_v w_v
+  if (valid && p != 0) {
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      if (cc < kc) df::store_coherent(mg + p * (8 * kw) + cc * 8 + i, M.v[cc]);
+  }
+  df::publish(fl, p, valid && i == 0, 1);
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void tree8_solve_bwd(
+    int nch, int64_t n, int64_t k, int kw, const int32_t *__restrict__ tile_lo,
+    const int32_t *__restrict__ tile_hi, int b, const int32_t *__restrict__ node_at,
+    const int32_t *__restrict__ parent_pos, const int32_t *__restrict__ parent_node,
+    const T *__restrict__ edge, const T *__restrict__ factor, T *__restrict__ x,
+    int32_t *__restrict__ flags, int32_t *__restrict__ timeout, uint64_t wait_ticks) {
+  __shared__ __align__(32) T lds[2][kSlots * 64];
+  const uint64_t deadline = wall_clock64() + wait_ticks;
+  const int lane = threadIdx.x;
+  const int s = lane >> 3, i = lane & 7;
+  const r8::Stage<T> sa{lds[0]}, sb{lds[1]};
+  const int chunk = static_cast<int>(blockIdx.x % nch);
+  const int32_t t = static_cast<int32_t>(blockIdx.x / nch);
+  const int64_t c0 = int64_t(chunk) * kSolveCols;
+  const int kc = static_cast<int>(min<int64_t>(kw, k - c0));
+  const int64_t p = tile_lo[t] + s;
+  const bool valid = p < tile_hi[t];
+  const bool has_parent = valid && p != 0;
+  const int bb = b * b, pk = (b * (b + 1) / 2 + 3) / 4 * 4;
+  int64_t v = 0, u = 0, q = 0;
+  if (valid) v = node_at[p];
+  if (has_parent) {
+    u = parent_node[p];
+    q = parent_pos[p];
+  }
+  const r8::Row<T> Si = valid ? packed_row(factor + p * pk, b, i) : r8::zero<T>();
+  const r8::Row<T> W = valid ? load_cols<T, false>(x, v, b, k, c0, kc, i) : r8::zero<T>();
+  const r8::Row<T> E = has_parent ? r8::load(edge + v * bb, b, i) : r8::zero<T>();
+  int32_t *fl = flags + chunk * n;
+  if (has_parent && i == 0) df::wait_flags(fl, q, q + 1, 2, 0, 1, timeout, deadline);
+  df::acquire();
+  const r8::Row<T> Xp = has_parent ? load_cols<T, true>(x, u, b, k, c0, kc, i) : r8::zero<T>();
+  sa.put(s, i, E);
+  sb.put(s, i, Xp);
+  f16::wave_sync();
+  const r8::Row<T> Tt = r8::mul_tn(sa, sb, s, i, r8::zero<T>());  // E_v^T x_parent
+  f16::wave_sync();
+  sa.put(s, i, Tt);
+  f16::wave_sync();
+  const r8::Row<T> V = r8::mul(Si, sa, s, r8::zero<T>());  // Sinv_v E_v^T x_parent
+  const bool gave_up = df::timed_out(timeout);  // then x is NaN, not silently wrong
+  r8::Row<T> X;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    X.v[c] = gave_up ? static_cast<T>(__builtin_nan("")) : W.v[c] - V.v[c];
+  if (valid) store_cols<T, true>(x, v, b, k, c0, kc, i, X);
+  df::publish(fl, p, valid && i == 0, 2);
+}
+
 // log det A = sum of the per-node terms in a fixed order, in two stages:
 // workgroup w reduces the contiguous chunk [w * chunk, (w + 1) * chunk)
 // (thread t takes entries t, t + 1024, ... of the chunk, then a fixed tree),
@@ -297,6 +455,48 @@ hipError_t tree8_factor_launch(const selinv_tree_plan *plan, const T *diag, cons
                      timeout, logdet, info);
   return hipGetLastError();
 }
+
+size_t tree8_solve_workspace_bytes(const selinv_tree_plan *plan, int64_t k) {
+  if (k <= 0) return 0;
+  const size_t n = plan->n, nch = (k + kSolveCols - 1) / kSolveCols;
+  const size_t kw = std::min<int64_t>(k, kSolveCols);
+  return align_up(nch * n * 8 * kw * plan->dtype_bytes) + align_up(nch * n * sizeof(int32_t)) +
+         align_up(sizeof(int32_t));
+}
+
+template <typename T>
+hipError_t tree8_solve_launch(const selinv_tree_plan *plan, int64_t k, const T *edge,
+                              const T *factor, const T *y, T *x, void *ws, hipStream_t s) {
+  if (k <= 0) return hipSuccess;
+  const int64_t n = plan->n;
+  const int b = plan->b;
+  const int nch = static_cast<int>((k + kSolveCols - 1) / kSolveCols);
+  const int kw = static_cast<int>(std::min<int64_t>(k, kSolveCols));
+  Carve cv(ws);
+  T *msg = cv.take<T>(int64_t(nch) * n * 8 * kw);
+  int32_t *flags = cv.take<int32_t>(int64_t(nch) * n);
+  int32_t *timeout = cv.take<int32_t>(1);
+  const TreePlanDev &d = plan->dev;
+  const int32_t tiles = static_cast<int32_t>(plan->tiles);
+  const uint64_t wt = wait_limit_ticks();
+  hipError_t e = df::launch_init(int64_t(nch) * n, flags, nullptr, timeout, s);
+  if (e != hipSuccess) return e;
+  const unsigned grid = static_cast<unsigned>(int64_t(tiles) * nch);
+  hipLaunchKernelGGL(tree8_solve_fwd<T>, dim3(grid), dim3(64), 0, s, tiles, nch, n, k, kw,
+                     d.tile_lo, d.tile_hi, b, d.node_at, d.child_beg, d.child_end, edge, factor,
+                     y, x, msg, flags, timeout, wt);
+  hipLaunchKernelGGL(tree8_solve_bwd<T>, dim3(grid), dim3(64), 0, s, nch, n, k, kw, d.tile_lo,
+                     d.tile_hi, b, d.node_at, d.parent_pos, d.parent_node, edge, factor, x, flags,
+                     timeout, wt);
+  return hipGetLastError();
+}
+
+template hipError_t tree8_solve_launch<float>(const selinv_tree_plan *, int64_t, const float *,
+                                              const float *, const float *, float *, void *,
+                                              hipStream_t);
+template hipError_t tree8_solve_launch<double>(const selinv_tree_plan *, int64_t,
+                                               const double *, const double *, const double *,
+                                               double *, void *, hipStream_t);
 
 template hipError_t tree8_factor_launch<float>(const selinv_tree_plan *, const float *,
                                                const float *, float *, double *, int32_t *,
