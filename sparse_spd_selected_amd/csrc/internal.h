@@ -266,6 +266,11 @@ template <typename T>
 hipError_t tree_factor_launch(const selinv_tree_plan *plan, const T *diag, const T *edge,
                               T *factor, double *logdet, int32_t *info, void *ws, hipStream_t s);
 size_t tree_apply_workspace_bytes(const selinv_tree_plan *plan, int64_t k);
+// b = 16 chain solve, one wavefront per chain and 16 right-hand sides
+// (chain_solve_b16.hip)
+template <typename T>
+hipError_t chain16_solve_launch(int64_t B, int64_t L, int64_t k, const T *lower, const T *factor,
+                                const T *y, T *x, hipStream_t s);
 // b <= 8 solve on the single-launch schedule (tree_b8.hip)
 size_t tree8_solve_workspace_bytes(const selinv_tree_plan *plan, int64_t k);
 template <typename T>

@@ -66,7 +66,8 @@ def _cmp_ld(got, ref, n, dt):
 # ---------------------------------------------------------------- chain
 @pytest.mark.parametrize("dt", ["f64", "f32"])
 @pytest.mark.parametrize("B,L,b,k", [(2, 1, 3, 1), (3, 5, 1, 2), (2, 9, 4, 17), (3, 6, 16, 1),
-                                     (2, 13, 16, 20), (2, 4, 17, 3), (2, 7, 32, 2)])
+                                     (2, 13, 16, 20), (2, 1, 16, 3), (5, 2, 16, 33),
+                                     (2, 4, 17, 3), (2, 7, 32, 2)])
 def test_chain_siblings(ssa, B, L, b, k, dt):
     dt = DT[dt]
     say("chain siblings B=%d L=%d b=%d k=%d %s" % (B, L, b, k, dt))
