@@ -335,7 +335,138 @@ __global__ __launch_bounds__(64) void chain16_solve_narrow(int L, int64_t k,
   }
 }
 
+// Sampling, x = L^-T D^-1/2 z with D^-1/2 = blockdiag(U_i), U_i U_i^T =
+// Sinv_i, U_i upper triangular (up to four right-hand sides): parents
+// first, w_i = U_i z_i, x_{L-1} = w_{L-1}, x_i = w_i - Sinv_i C_i^T x_{i+1}.
+// U_i is formed in registers, one block per step: lane (r, q) holds entries
+// (r, q + 4t) of Sinv_i and turns them into those of U_i by the reversed
+// (upper-lower) Cholesky, columns 15 down to 0: u_jj = sqrt(a_jj),
+// u_rj = a_rj / u_jj (r < j), then a_rl -= u_rj u_lj for r, l < j.  Column j
+// is broadcast through LDS.  Dot products use the same strided column sets.
+template <typename T>
+__global__ __launch_bounds__(64) void chain16_sample_narrow(int L, int64_t k,
+                                                           const T *__restrict__ lower,
+                                                           const T *__restrict__ factor,
+                                                           const T *__restrict__ z,
+                                                           T *__restrict__ x) {
+  __shared__ __align__(16) T bufA[16 * kNarrow];
+  __shared__ __align__(16) T bufB[16 * kNarrow];
+  __shared__ __align__(16) T bufC[16 * kNarrow];
+  __shared__ __align__(16) T colj[16];
+  __shared__ __align__(16) T sP[kPB];
+  __shared__ __align__(16) T sC[256];
+  const int lane = threadIdx.x, r = lane & 15, q = lane >> 4;
+  const int64_t m = blockIdx.x;
+  const int kc = static_cast<int>(k);
+  const T *F = factor + m * L * kPB;
+  const T *C = L > 1 ? lower + m * (L - 1) * 256 : nullptr;  // none for one block
+  const int lc = L > 1 ? L - 2 : 0;
+  auto vrow = [&](const T *base, int i) { return base + ((m * L + i) * 16 + r) * k; };
+  auto vrow_w = [&](T *base, int i) { return base + ((m * L + i) * 16 + r) * k; };
+  auto coupling = [&](int i) -> const T * {
+    return C ? C + int64_t(min(max(i, 0), lc)) * 256 : nullptr;
+  };
+  // sum over this lane's columns q + 4t of a_t V[q + 4t][c], then over the row's lanes
+  auto dot = [&](T (&o)[kNarrow], const T (&a)[4], const T *V) {
+#pragma unroll
+    for (int c = 0; c < kNarrow; ++c) {
+      T acc = T(0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc += a[t] * V[(q + 4 * t) * kNarrow + c];
+      o[c] = c < kc ? row_sum(acc) : T(0);
+    }
+  };
+  auto put_row = [&](T *V, const T (&v)[kNarrow]) {
+    if (q == 0)
+#pragma unroll
+      for (int c = 0; c < kNarrow; ++c) V[r * kNarrow + c] = v[c];
+  };
+  auto load_row = [&](T (&o)[kNarrow], const T *row) {
+#pragma unroll
+    for (int c = 0; c < kNarrow; ++c) o[c] = c < kc ? row[c] : T(0);
+  };
+  auto store_row = [&](T *row, const T (&v)[kNarrow]) {
+    if (q == 0)
+#pragma unroll
+      for (int c = 0; c < kNarrow; ++c)
+        if (c < kc) row[c] = v[c];
+  };
+
+  Raw<T> nx;
+  load_raw(nx, F + int64_t(L - 1) * kPB, coupling(L - 1), lane);
+  T zn[kNarrow];
+  load_row(zn, vrow(z, L - 1));
+  for (int i = L - 1; i >= 0; --i) {
+    put_raw(sP, sC, nx, lane);
+    T zi[kNarrow];
+#pragma unroll
+    for (int c = 0; c < kNarrow; ++c) zi[c] = zn[c];
+    if (i > 0) {
+      load_raw(nx, F + int64_t(i - 1) * kPB, coupling(i - 1), lane);
+      load_row(zn, vrow(z, i - 1));
+    }
+    put_row(bufA, zi);
+    f16::wave_sync();
+    T si[4], u[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = q + 4 * t;
+      si[t] = sP[c <= r ? r * (r + 1) / 2 + c : c * (c + 1) / 2 + r];
+      u[t] = si[t];
+    }
+    // reversed Cholesky of Sinv_i into u (entries (r, q + 4t) of U_i)
+#pragma unroll
+    for (int j = 15; j >= 0; --j) {
+      const int tj = j >> 2;
+      if ((j & 3) == q) colj[r] = u[tj];  // column j, current values
+      f16::wave_sync();
+      const T ujj = sqrt(colj[j]);
+      const T urj = colj[r] / ujj;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int c = q + 4 * t;
+        if (c < j && r < j) u[t] -= urj * (colj[c] / ujj);
+      }
+      if ((j & 3) == q) u[tj] = r < j ? urj : (r == j ? ujj : T(0));
+      f16::wave_sync();
+    }
+    T w[kNarrow];
+    dot(w, u, bufA);  // U_i z_i
+    if (i < L - 1) {  // x_i = w_i - Sinv_i C_i^T x_{i+1}, x_{i+1} in bufB
+      T cc[4], t2[kNarrow];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) cc[t] = sC[(q + 4 * t) * 16 + r];
+      dot(t2, cc, bufB);
+      put_row(bufC, t2);
+      f16::wave_sync();
+      T v[kNarrow];
+      dot(v, si, bufC);
+#pragma unroll
+      for (int c = 0; c < kNarrow; ++c) w[c] -= v[c];
+    }
+    store_row(vrow_w(x, i), w);
+    put_row(bufB, w);
+    f16::wave_sync();
+  }
+}
+
 }  // namespace
+
+template <typename T>
+hipError_t chain16_sample_launch(int64_t B, int64_t L, int64_t k, const T *lower,
+                                 const T *factor, const T *z, T *x, hipStream_t s) {
+  if (B == 0 || k == 0) return hipSuccess;
+  hipLaunchKernelGGL(chain16_sample_narrow<T>, dim3(static_cast<unsigned>(B)), dim3(64), 0, s,
+                     static_cast<int>(L), k, lower, factor, z, x);
+  return hipGetLastError();
+}
+
+template hipError_t chain16_sample_launch<float>(int64_t, int64_t, int64_t, const float *,
+                                                 const float *, const float *, float *,
+                                                 hipStream_t);
+template hipError_t chain16_sample_launch<double>(int64_t, int64_t, int64_t, const double *,
+                                                  const double *, const double *, double *,
+                                                  hipStream_t);
 
 template <typename T>
 hipError_t chain16_solve_launch(int64_t B, int64_t L, int64_t k, const T *lower, const T *factor,

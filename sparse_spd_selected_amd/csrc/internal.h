@@ -271,6 +271,10 @@ size_t tree_apply_workspace_bytes(const selinv_tree_plan *plan, int64_t k);
 template <typename T>
 hipError_t chain16_solve_launch(int64_t B, int64_t L, int64_t k, const T *lower, const T *factor,
                                 const T *y, T *x, hipStream_t s);
+// b = 16 chain sampling for k <= 4, one wavefront per chain
+template <typename T>
+hipError_t chain16_sample_launch(int64_t B, int64_t L, int64_t k, const T *lower,
+                                 const T *factor, const T *z, T *x, hipStream_t s);
 // b <= 8 solve on the single-launch schedule (tree_b8.hip)
 size_t tree8_solve_workspace_bytes(const selinv_tree_plan *plan, int64_t k);
 template <typename T>
