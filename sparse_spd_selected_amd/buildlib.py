@@ -29,7 +29,7 @@ SOURCES = [
     "chain_small.hip",
     "vjp_generic.hip", "vjp_chain_b16.hip", "vjp_star_b32.hip",
     "vjp_tree_b8.hip", "vjp_chain_seg.hip",
-    "shared_factor.hip", "chain_solve_b16.hip",
+    "shared_factor.hip", "chain_solve_b16.hip", "star_solve_b32.hip",
     "nonsym.hip", "bidiag_b16.hip", "nonsym_b8.hip", "junction_plan.cpp", "junction.hip",
 ]
 

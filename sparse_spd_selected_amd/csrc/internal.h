@@ -275,6 +275,11 @@ hipError_t chain16_solve_launch(int64_t B, int64_t L, int64_t k, const T *lower,
 template <typename T>
 hipError_t chain16_sample_launch(int64_t B, int64_t L, int64_t k, const T *lower,
                                  const T *factor, const T *z, T *x, hipStream_t s);
+// b = 32 star solve / sampling for k <= 4 (star_solve_b32.hip)
+template <typename T>
+hipError_t star32_apply_launch(int64_t B, int64_t K, int64_t k, bool sample, const T *coupling,
+                               const T *factor, const T *in_center, const T *in_leaves,
+                               T *x_center, T *x_leaves, void *ws, hipStream_t s);
 // b <= 8 solve on the single-launch schedule (tree_b8.hip)
 size_t tree8_solve_workspace_bytes(const selinv_tree_plan *plan, int64_t k);
 template <typename T>

@@ -521,6 +521,9 @@ hipError_t star_apply_launch(int64_t B, int64_t K, int32_t b, int64_t k, bool sa
                              const T *in_leaves, T *x_center, T *x_leaves, void *ws,
                              hipStream_t s) {
   if (B == 0 || k == 0) return hipSuccess;
+  if (b == 32 && k <= 4)
+    return star32_apply_launch<T>(B, K, k, sample, coupling, factor, in_center, in_leaves,
+                                  x_center, x_leaves, ws, s);
   const int nch = nchunks(k);
   const size_t nl = static_cast<size_t>(B) * K;
   const int nt = sf_threads(b);

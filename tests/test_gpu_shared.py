@@ -138,7 +138,9 @@ def test_chain_sample_deterministic_and_draws(ssa):
 
 # ------------------------------------------------------------------ star
 @pytest.mark.parametrize("dt", ["f64", "f32"])
-@pytest.mark.parametrize("B,K,b,k", [(1, 0, 3, 2), (2, 5, 4, 1), (2, 33, 8, 18), (2, 9, 32, 3)])
+@pytest.mark.parametrize("B,K,b,k", [(1, 0, 3, 2), (2, 5, 4, 1), (2, 33, 8, 18), (2, 9, 32, 3),
+                                     (3, 40, 32, 1), (1, 0, 32, 4), (2, 17, 32, 4),
+                                     (2, 5, 32, 7)])
 def test_star_siblings(ssa, B, K, b, k, dt):
     dt = DT[dt]
     say("star siblings B=%d K=%d b=%d k=%d %s" % (B, K, b, k, dt))
@@ -163,6 +165,30 @@ def test_star_siblings(ssa, B, K, b, k, dt):
     rs = np.concatenate([Osc.reshape(B, -1), Osl.reshape(B, -1)], 1)
     say("  solve %.2e sample %.2e" % (_cmp_vec("solve", gx, rx, dt),
                                        _cmp_vec("sample", gs, rs, dt)))
+
+
+@pytest.mark.parametrize("dt", ["f64", "f32"])
+def test_star_siblings_workload_b32(ssa, dt):
+    """256 stars of 1024 leaves of 32, k = 1: solve and sample checked on three
+    matrices spread over the batch."""
+    dt = DT[dt]
+    B, K, b, k = 256, 1024, 32, 1
+    c, lv, cp = spdgen.star(B, K, b, seed=0)
+    yc = spdgen.cotangent((B, b, k), seed=0, k=0)
+    yl = spdgen.cotangent((B, K, b, k), seed=0, k=1)
+    f = ssa.star_factor(_to(c, dt), _to(lv, dt), _to(cp, dt))
+    xc, xl = f.solve(_to(yc, dt), _to(yl, dt))
+    sc, sl = f.sample(z_center=_to(yc, dt), z_leaves=_to(yl, dt))
+    torch.cuda.synchronize()
+    sel = [0, 101, 255]
+    cu, lu, pu = _as_used(c[sel], dt), _as_used(lv[sel], dt), _as_used(cp[sel], dt)
+    ycu, ylu = _as_used(yc[sel], dt), _as_used(yl[sel], dt)
+    n = len(sel)
+    for mode, (gc, gl) in (("solve", (xc, xl)), ("sample", (sc, sl))):
+        Oc, Ol = oracle.star_apply(cu, lu, pu, ycu, ylu, mode)
+        g = torch.cat([gc[sel].reshape(n, -1), gl[sel].reshape(n, -1)], 1)
+        r = np.concatenate([Oc.reshape(n, -1), Ol.reshape(n, -1)], 1)
+        say("  %s %.2e" % (mode, _cmp_vec(mode, g, r, dt)))
 
 
 # ------------------------------------------------------------------ tree
