@@ -443,11 +443,18 @@ def cpu_baseline(kind, cfg, op="selinv"):
     if kind == "chain":
         Bs = cfg["B"] if cfg["B"] * cfg["L"] * cfg["b"] ** 3 <= 4e9 else max(1, int(4e9 // (cfg["L"] * cfg["b"] ** 3)))
         d, l = spdgen.chain(Bs, cfg["L"], cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
-        t0 = time.perf_counter()
-        oracle.chain(d, l, lib=lib)
-        t = time.perf_counter() - t0
+        # the whole batch takes well under a second here: repeat it (up to ~3 s)
+        # and report the mean time of one pass
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.chain(d, l, lib=lib)
+            reps += 1
+            if time.perf_counter() - t0 >= 3.0 or reps >= 30:
+                break
+        t = (time.perf_counter() - t0) / reps
         sub = dict(cfg, B=Bs)
-        sample = "%d of %d chains (L=%d, b=%d), float64" % (Bs, cfg["B"], cfg["L"], cfg["b"])
+        sample = "%d of %d chains (L=%d, b=%d), float64, mean of %d passes" % (
+            Bs, cfg["B"], cfg["L"], cfg["b"], reps)
     elif kind == "star":
         Bs = min(cfg["B"], 16)
         arrs = spdgen.star(Bs, cfg["K"], cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
