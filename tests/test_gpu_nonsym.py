@@ -168,3 +168,20 @@ def test_nonsym_tree_breakdown(ssa):
                                        _to(w, torch.float64), return_info=True)
     torch.cuda.synchronize()
     assert int(info) == 12 and torch.isnan(Gd).any()
+
+
+def test_nonsym_tree_wait_limit_reports_timeout(ssa):
+    """Zero wait bound on a path tree: info = -1 instead of a hang; with the
+    bound restored the same call matches the oracle."""
+    p = spdgen.path_tree(2000)
+    d, u, w = spdgen.nonsym_tree(p, 4, seed=6)
+    old = ssa.wait_limit()
+    try:
+        ssa.set_wait_limit(0)
+        _, _, _, info = ssa.nonsym_tree(p, _to(d, torch.float64), _to(u, torch.float64),
+                                        _to(w, torch.float64), return_info=True)
+        torch.cuda.synchronize()
+    finally:
+        ssa.set_wait_limit(old)
+    assert int(info) == -1
+    run_nonsym_tree(ssa, p, 4, torch.float64, seed=6)

@@ -241,6 +241,27 @@ def test_tree_siblings_workload_b8(ssa, dt):
                                                DT[dt], seed=1))
 
 
+def test_tree_solve_wait_limit_gives_nan(ssa):
+    """Zero wait bound on a path tree: the single-launch solve gives up and
+    leaves NaN in x rather than a silently wrong result; with the bound
+    restored the same solve matches the oracle."""
+    p = spdgen.path_tree(2000)
+    d, e = spdgen.tree(p, 4, seed=7)
+    y = spdgen.cotangent((2000, 4, 1), seed=7, k=0)
+    f = ssa.tree_factor(p, _to(d, torch.float64), _to(e, torch.float64))
+    old = ssa.wait_limit()
+    try:
+        ssa.set_wait_limit(0)
+        x = f.solve(_to(y, torch.float64))
+        torch.cuda.synchronize()
+    finally:
+        ssa.set_wait_limit(old)
+    assert torch.isnan(x).any()
+    x = f.solve(_to(y, torch.float64))
+    Ox = oracle.tree_apply(p, d, e, y, "solve")
+    _cmp_vec("solve", x[None], Ox[None], torch.float64)
+
+
 def test_tree_factor_not_pd(ssa):
     p = spdgen.random_recursive_tree(40, 1)
     d, e = spdgen.tree(p, 3)

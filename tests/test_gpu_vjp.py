@@ -293,3 +293,24 @@ def test_tree_vjp_not_pd(ssa):
     _, _, _, Oinfo = oracle.tree(p, d, e)
     assert int(info) == Oinfo != 0
     assert torch.isnan(db).any()
+
+
+def test_tree_vjp_wait_limit_reports_timeout(ssa):
+    """Zero wait bound on a path tree: the single-launch reverse passes give up
+    at the first unready flag and report info = -1; with the bound restored
+    the same call matches the oracle."""
+    p = spdgen.path_tree(2000)
+    d, e = spdgen.tree(p, 4, seed=5)
+    gd = spdgen.cotangent(d.shape, seed=5, k=0)
+    ge = spdgen.cotangent(e.shape, seed=5, k=1)
+    args = (_to(d, torch.float64), _to(e, torch.float64), _to(gd, torch.float64),
+            _to(ge, torch.float64), 0.5)
+    old = ssa.wait_limit()
+    try:
+        ssa.set_wait_limit(0)
+        _, _, info = ssa.tree_vjp(p, *args, return_info=True)
+        torch.cuda.synchronize()
+    finally:
+        ssa.set_wait_limit(old)
+    assert int(info) == -1
+    run_tree_vjp(ssa, p, 4, torch.float64, seed=5)
