@@ -515,8 +515,8 @@ def main():
         copy_probe(args.copy_probe_mib, args.steps)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
-              "(batches shard across GPUs with no communication; see DESIGN.md)" % args.gpus,
+        print("bench.py: runs on exactly one GPU; --gpus %d is not supported (independent "
+              "matrices shard across GPUs with no communication)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     import spdgen
