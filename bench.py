@@ -491,6 +491,46 @@ def copy_probe(mib, steps):
     print(json.dumps({"copy_probe_bytes_each_way": n * 4, "launches": max(steps, 1)}), flush=True)
 
 
+def peak_probe():
+    """Achievable peaks on this device, for reading the roofline fractions
+    against measured rather than datasheet limits: a device-to-device copy
+    (bytes read + written per second) and large float64 / float32 matrix
+    products through torch (vendor GEMM)."""
+    import torch
+    dev = torch.device("cuda:0")
+    out = {}
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    n = (1 << 30) // 4  # 1 GiB of float32 each way
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src), 20)
+    out["copy_GBps"] = round(2 * n * 4 / t / 1e9, 1)
+    del src, dst
+    for name, dt, m in (("gemm_f64_TFLOPs", torch.float64, 8192),
+                        ("gemm_f32_TFLOPs", torch.float32, 8192)):
+        a = torch.randn(m, m, dtype=dt, device=dev)
+        b = torch.randn(m, m, dtype=dt, device=dev)
+        c = torch.empty_like(a)
+        t = timed(lambda: torch.matmul(a, b, out=c), 10)
+        out[name] = round(2 * m ** 3 / t / 1e12, 2)
+        del a, b, c
+    out["datasheet"] = {"hbm_GBps": HBM_PEAK_GBS, "f64_TFLOPs": FP64_PEAK_TFLOPS,
+                        "f32_TFLOPs": FP32_PEAK_TFLOPS}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -510,7 +550,13 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--peak-probe", action="store_true",
+                    help="only measure achievable peaks (device copy, float64/float32 GEMM) "
+                         "and exit")
     args = ap.parse_args()
+    if args.peak_probe:
+        peak_probe()
+        return
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib, args.steps)
         return
