@@ -17,7 +17,9 @@
 //     r_i = P_i - sym(X_i^T G_{i+1,i+1} Z_i), the same congruence run
 //     backwards: Dbar_a = Phi^T Dbar_e Phi + R, R = sum_i Pi_i^T r_i Pi_i,
 //     Pi_i = X_{i-1} ... X_a.
-// Passes (one workgroup per segment unless noted, blocks in LDS):
+// Passes (b = 32; prep, mid and out are one wavefront per segment with the
+// blocks in the MFMA 32 x 32 register layout of frag32.h, the two scans one
+// workgroup per chain with the blocks in LDS):
 //   forward selected inverse (any forward path) -> G, info
 //   prep:  Sinv_i, X_i per block; the GG map (Phi, Cm) per segment
 //   scan:  one workgroup per chain, GG at every segment start
@@ -29,7 +31,9 @@
 #include <climits>
 
 #include "block_wg.h"
+#include "frag32.h"
 #include "internal.h"
+#include "io32.h"
 
 namespace selinv {
 
@@ -37,70 +41,11 @@ namespace {
 
 inline int cvs_threads(int b) { return b <= 8 ? 64 : 256; }
 
-template <typename T>
-__device__ inline void set_identity(T *A, int b) {
-  for (int e = threadIdx.x; e < b * b; e += blockDim.x) A[e] = (e / b == e % b) ? T(1) : T(0);
-  __syncthreads();
-}
-
 struct SegRange {
   int64_t a0, a1;
 };
 __device__ inline SegRange seg_range(int64_t L, int P, int s) {
   return {static_cast<int64_t>(s) * L / P, static_cast<int64_t>(s + 1) * L / P};
-}
-
-template <typename T>
-__global__ void cvs_prep(int64_t L, int b, int P, const T *__restrict__ diag,
-                         const T *__restrict__ lower, const T *__restrict__ gd,
-                         const T *__restrict__ gl, const T *__restrict__ Gd,
-                         const T *__restrict__ Gl, T *__restrict__ sinv_ws, T *__restrict__ x_ws,
-                         T *__restrict__ phi, T *__restrict__ cmap) {
-  extern __shared__ unsigned char smem_raw[];
-  T *smem = reinterpret_cast<T *>(smem_raw);
-  const int bb = b * b;
-  T *S = smem, *X = S + bb, *Ph = X + bb, *Cm = Ph + bb, *T1 = Cm + bb, *T2 = T1 + bb,
-    *Cs = T2 + bb, *col = Cs + bb;
-  const int64_t m = blockIdx.x / P;
-  const int s = blockIdx.x % P;
-  const SegRange r = seg_range(L, P, s);
-  const T *D = diag + m * L * bb, *C = lower + m * (L - 1) * bb;
-  const T *GDm = Gd + m * L * bb, *GLm = Gl + m * (L - 1) * bb;
-  const T *gdm = gd + m * L * bb, *glm = gl + m * (L - 1) * bb;
-  double ld;
-  if (s == 0) {
-    wg::load_sym_lower(S, D, b);
-    wg::spd_inverse(S, b, col, &ld);
-  } else {  // Sinv_a = G_aa - G_{a+1,a}^T G_{a+1,a+1}^{-1} G_{a+1,a}
-    wg::load_sym_lower(T1, GDm + (r.a0 + 1) * bb, b);
-    wg::spd_inverse(T1, b, col, &ld);
-    wg::copy(Cs, GLm + r.a0 * bb, bb);
-    wg::gemm<T, false, false>(T2, T1, Cs, b);
-    wg::gemm_sym<T, true, false>(S, GDm + r.a0 * bb, Cs, T2, b, T(-1));
-  }
-  set_identity(Ph, b);
-  wg::fill(Cm, bb, T(0));
-  for (int64_t i = r.a0; i < r.a1; ++i) {
-    if (i > r.a0) {  // S_i = D_i - X_{i-1} C_{i-1}^T (X, Cs of the previous step)
-      wg::load_sym_lower(S, D + i * bb, b);
-      wg::gemm_sym<T, false, true>(S, S, X, Cs, b, T(-1));
-      wg::spd_inverse(S, b, col, &ld);
-    }
-    wg::copy(sinv_ws + (m * L + i) * bb, S, bb);
-    if (i == L - 1) break;
-    wg::copy(Cs, C + i * bb, bb);
-    wg::gemm<T, false, false>(X, Cs, S, b);  // X_i = C_i Sinv_i
-    wg::copy(x_ws + (m * L + i) * bb, X, bb);
-    wg::sym_part(T1, gdm + (i + 1) * bb, b);  // c_i = sym(Gd_{i+1}) - sym(Gl_i X_i^T)
-    wg::copy(T2, glm + i * bb, bb);
-    wg::gemm_symmetrized<T, false, true>(T1, T1, T2, X, b, T(-1));
-    wg::gemm<T, false, false>(T2, X, Ph, b);  // Phi <- X_i Phi
-    wg::copy(Ph, T2, bb);
-    wg::gemm<T, false, false>(T2, X, Cm, b);  // Cm <- X_i Cm X_i^T + c_i
-    wg::gemm_sym<T, false, true>(Cm, T1, T2, X, b, T(1));
-  }
-  wg::copy(phi + (m * P + s) * bb, Ph, bb);
-  wg::copy(cmap + (m * P + s) * bb, Cm, bb);
 }
 
 // GG at every segment start, one workgroup per chain
@@ -121,57 +66,6 @@ __global__ void cvs_gg_scan(int b, int P, int64_t L, const T *__restrict__ gd,
     wg::gemm<T, false, false>(T2, Ph, GG, b);
     wg::gemm_sym<T, false, true>(GG, cmap + q * bb, T2, Ph, b, T(1));  // base read once
   }
-}
-
-template <typename T>
-__global__ void cvs_mid(int64_t L, int b, int P, const T *__restrict__ gd,
-                        const T *__restrict__ gl, const double *__restrict__ ld_bar,
-                        const T *__restrict__ Gd, const T *__restrict__ sinv_ws,
-                        const T *__restrict__ x_ws, const T *__restrict__ gg_start,
-                        T *__restrict__ p_ws, T *__restrict__ z_ws, T *__restrict__ rmap) {
-  extern __shared__ unsigned char smem_raw[];
-  T *smem = reinterpret_cast<T *>(smem_raw);
-  const int bb = b * b;
-  // every operand of a product is staged in LDS first (one coalesced copy)
-  T *GG = smem, *Pi = GG + bb, *R = Pi + bb, *Si = R + bb, *Xi = Si + bb, *A = Xi + bb,
-    *Bq = A + bb, *Cq = Bq + bb;
-  const int64_t m = blockIdx.x / P;
-  const int s = blockIdx.x % P;
-  const SegRange rg = seg_range(L, P, s);
-  const T lb = ld_bar ? static_cast<T>(ld_bar[m]) : T(0);
-  const T *gdm = gd + m * L * bb, *glm = gl + m * (L - 1) * bb, *GDm = Gd + m * L * bb;
-  wg::copy(GG, gg_start + (m * P + s) * bb, bb);
-  set_identity(Pi, b);
-  wg::fill(R, bb, T(0));
-  for (int64_t i = rg.a0; i < rg.a1; ++i) {
-    T *Pw = p_ws + (m * L + i) * bb, *Zw = z_ws + (m * L + i) * bb;
-    wg::copy(Si, sinv_ws + (m * L + i) * bb, bb);
-    wg::gemm<T, false, false>(A, GG, Si, b);  // P_i = lb Sinv - Sinv (GG Sinv), in Cq
-    wg::copy_scaled(Cq, Si, bb, lb);
-    wg::gemm_sym<T, false, false>(Cq, Cq, Si, A, b, T(-1));
-    wg::copy(Pw, Cq, bb);
-    if (i == L - 1) break;
-    wg::copy(Xi, x_ws + (m * L + i) * bb, bb);
-    wg::gemm<T, false, false>(A, Xi, GG, b);  // W = X GG
-    for (int e = threadIdx.x; e < bb; e += blockDim.x) {
-      const T w = A[e], g = glm[i * bb + e];
-      A[e] = w - g;          // Y1 = W - Gl
-      Bq[e] = (w + w) - g;   // Y2 = 2 W - Gl
-    }
-    __syncthreads();
-    wg::sym_part(GG, gdm + (i + 1) * bb, b);  // GG <- sym(Gd_{i+1}) + sym(Y1 X^T)
-    wg::gemm_symmetrized<T, false, true>(GG, GG, A, Xi, b, T(1));
-    wg::gemm<T, false, false>(A, Bq, Si, b);  // Z_i = Y2 Sinv
-    wg::copy(Zw, A, bb);
-    wg::copy(Bq, GDm + (i + 1) * bb, bb);
-    wg::gemm<T, false, false>(Si, Bq, A, b);                          // G_{i+1} Z_i
-    wg::gemm_symmetrized<T, true, false>(Bq, Cq, Xi, Si, b, T(-1));  // r_i = P - sym(X^T G Z)
-    wg::gemm<T, false, false>(A, Bq, Pi, b);                          // R += Pi^T r Pi
-    wg::gemm_sym<T, true, false>(R, R, Pi, A, b, T(1));
-    wg::gemm<T, false, false>(A, Xi, Pi, b);  // Pi <- X_i Pi
-    wg::copy(Pi, A, bb);
-  }
-  wg::copy(rmap + (m * P + s) * bb, R, bb);
 }
 
 // Dbar at every segment end (the first block after the segment; the root for
@@ -195,43 +89,259 @@ __global__ void cvs_db_scan(int b, int P, int64_t L, const T *__restrict__ p_ws,
   }
 }
 
+// ------------------------------------------------------ wave kernels, b = 32
+// O32(M) is the register layout of frag32.h; f32t::mm(O(A^T), O(B)) = O(A B).
+// Workspace blocks: Sinv_i as its packed lower triangle, X_i stored as X_i^T
+// (row-major), P_i and Z_i row-major.
+using f32t::Blk;
+constexpr int kBB32 = 1024;
+
 template <typename T>
-__global__ void cvs_out(int64_t L, int b, int P, const T *__restrict__ Gd,
-                        const T *__restrict__ x_ws, const T *__restrict__ z_ws,
-                        const T *__restrict__ p_ws, const T *__restrict__ db_end,
-                        const int32_t *__restrict__ info_ws, T *__restrict__ d_bar,
-                        T *__restrict__ l_bar, int32_t *__restrict__ info) {
-  extern __shared__ unsigned char smem_raw[];
-  T *smem = reinterpret_cast<T *>(smem_raw);
-  const int bb = b * b;
-  T *Db = smem, *T2 = Db + bb, *Q = T2 + bb, *Dn = Q + bb, *Xs = Dn + bb, *Zs = Xs + bb,
-    *Gs = Zs + bb;
+__device__ __forceinline__ Blk<T> lin32(T a, const Blk<T> &x, T c, const Blk<T> &y) {
+  Blk<T> r;
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J) r.t[I][J] = a * x.t[I][J] + c * y.t[I][J];
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ Blk<T> scale32(T a, const Blk<T> &x) {
+  Blk<T> r;
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J) r.t[I][J] = a * x.t[I][J];
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ Blk<T> identity32(int g, int j) {
+  Blk<T> r = f32t::zero<T>();
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r.t[I][I][q] = f16::row<T>(g, q) == j ? T(1) : T(0);
+  return r;
+}
+
+// row-major block -> its O32 (and, optionally, the O32 of its transpose)
+// through the wavefront's tile; `ws` selects cacheable workspace loads
+template <typename T>
+struct Io32 {
+  T *tile;
+  int lane, g, j;
+  __device__ __forceinline__ void stage(const T *P, bool ws) const {
+    f16::wave_sync();
+    io32::put(tile, lane, ws ? io32::load_ws(P, lane) : io32::load(P, lane));
+    f16::wave_sync();
+  }
+  __device__ __forceinline__ Blk<T> blk() const { return io32::get_blk(tile, g, j); }
+  __device__ __forceinline__ Blk<T> blk_t() const { return io32::get_blk_t(tile, g, j); }
+  // row-major store of the block b (all four tiles formed)
+  __device__ __forceinline__ void store(T *P, const Blk<T> &b, bool ws) const {
+    f16::wave_sync();
+    io32::put_blk(tile, g, j, b);
+    f16::wave_sync();
+    if (ws)
+      io32::store_ws(P, lane, io32::get(tile, lane));
+    else
+      io32::store(P, lane, io32::get(tile, lane));
+  }
+  // (M + M^T) / 2 of a block with all four tiles formed: exactly symmetric
+  // (entries (a, c) and (c, a) are the same two terms added)
+  __device__ __forceinline__ Blk<T> symmetrize(const Blk<T> &b) const {
+    f16::wave_sync();
+    io32::put_blk(tile, g, j, b);
+    f16::wave_sync();
+    return lin32(T(0.5), io32::get_blk(tile, g, j), T(0.5), io32::get_blk_t(tile, g, j));
+  }
+  // row-major store of a symmetric result of which tiles (0,0), (1,0), (1,1)
+  // are formed, made exactly symmetric; returns the full block in registers
+  __device__ __forceinline__ Blk<T> store_sym(T *P, const Blk<T> &b, bool ws) const {
+    f16::wave_sync();
+    io32::put_sym(tile, g, j, b);
+    f16::wave_sync();
+    const Blk<T> f = lin32(T(0.5), io32::get_blk(tile, g, j), T(0.5), io32::get_blk_t(tile, g, j));
+    store(P, f, ws);
+    return f;
+  }
+};
+
+// prep: Sinv_i (packed) and X_i^T per block, the segment's GG map (Phi, Cm)
+template <typename T>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void cvs32_prep(
+    int64_t L, int P, const T *__restrict__ diag, const T *__restrict__ lower,
+    const T *__restrict__ gd, const T *__restrict__ gl, const T *__restrict__ Gd,
+    const T *__restrict__ Gl, T *__restrict__ sinv_ws, T *__restrict__ x_ws,
+    T *__restrict__ phi, T *__restrict__ cmap) {
+  using Tr = io32::Traits<T>;
+  __shared__ __align__(16) T col[32];
+  __shared__ __align__(16) T tA[Tr::kTile];
+  const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
+  const Io32<T> io{tA, lane, g, j};
+  const io32::SymLanes<T> sl(g, j, lane);
+  const int64_t m = blockIdx.x / P;
+  const int s = blockIdx.x % P;
+  const SegRange r = seg_range(L, P, s);
+  const T *D = diag + m * L * kBB32, *C = lower + m * (L - 1) * kBB32;
+  const T *GDm = Gd + m * L * kBB32, *GLm = Gl + m * (L - 1) * kBB32;
+  const T *gdm = gd + m * L * kBB32, *glm = gl + m * (L - 1) * kBB32;
+  f16::PivotLog pl;  // pivots unused here
+  Blk<T> S;
+  if (s == 0) {
+    f16::wave_sync();
+    io32::put(tA, lane, io32::load(D, lane));
+    f16::wave_sync();
+    S = sl.get_sym(tA);
+  } else {  // Sinv_a = G_aa - G_{a+1,a}^T G_{a+1,a+1}^{-1} G_{a+1,a}
+    f16::wave_sync();
+    io32::put(tA, lane, io32::load_ws(GDm + (r.a0 + 1) * kBB32, lane));
+    f16::wave_sync();
+    Blk<T> Gn = sl.get_sym(tA);
+    f32t::gj_inverse(Gn, col, g, j, pl);
+    io.stage(GLm + r.a0 * kBB32, true);
+    const Blk<T> GLa = io.blk();                                 // O(G_{a+1,a})
+    const Blk<T> T2 = f32t::mm(Gn, GLa, f32t::zero<T>());        // G_{a+1,a+1}^-1 G_{a+1,a}
+    f16::wave_sync();
+    io32::put(tA, lane, io32::load_ws(GDm + r.a0 * kBB32, lane));
+    f16::wave_sync();
+    S = f32t::sub(sl.get_sym(tA), f32t::mm(GLa, T2, f32t::zero<T>()));
+  }
+  Blk<T> Ph = identity32<T>(g, j), Cm = f32t::zero<T>();
+  for (int64_t i = r.a0; i < r.a1; ++i) {
+    if (i > r.a0 || s == 0) f32t::gj_inverse(S, col, g, j, pl);  // S <- Sinv_i
+    f16::wave_sync();
+    io32::put_blk(tA, g, j, S);
+    f16::wave_sync();
+    io32::store_packed(sinv_ws + (m * L + i) * kBB32, lane, sl.gather_packed(tA));
+    if (i == L - 1) break;
+    io.stage(C + i * kBB32, false);
+    const Blk<T> Ct = io.blk_t();                                // O(C_i^T)
+    const Blk<T> XT = f32t::mm(S, Ct, f32t::zero<T>());          // O(X_i^T) = O(Sinv C_i^T)
+    io.store(x_ws + (m * L + i) * kBB32, XT, true);              // X_i^T, row-major
+    {  // S_{i+1} = D_{i+1} - C_i Sinv_i C_i^T (tile (1,0) not formed)
+      f16::wave_sync();
+      io32::put(tA, lane, io32::load(D + (i + 1) * kBB32, lane));
+      f16::wave_sync();
+      S = f32t::sub(sl.get_sym(tA), f32t::mm_upper(Ct, XT, f32t::zero<T>()));
+    }
+    // c_i = sym(gd_{i+1}) - sym(gl_i X_i^T)
+    io.stage(gdm + (i + 1) * kBB32, false);
+    Blk<T> c = lin32(T(0.5), io.blk(), T(0.5), io.blk_t());
+    io.stage(glm + i * kBB32, false);
+    const Blk<T> GLth = scale32(T(-0.5), io.blk_t());           // -O(gl_i^T) / 2
+    c = f32t::mm(GLth, XT, c);                                   // - gl X^T / 2
+    c = f32t::mm(XT, GLth, c);                                   // - X gl^T / 2
+    Ph = f32t::mm(XT, Ph, f32t::zero<T>());                      // Phi <- X_i Phi
+    const Blk<T> W = f32t::mm(Cm, XT, f32t::zero<T>());          // Cm X^T
+    Cm = f32t::mm(XT, W, c);                                     // X Cm X^T + c
+  }
+  io.store(phi + (m * P + s) * kBB32, Ph, true);
+  io.store(cmap + (m * P + s) * kBB32, Cm, true);
+}
+
+// mid: P_i, Z_i per block and the segment's Dbar map R, from GG at the start
+template <typename T>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void cvs32_mid(
+    int64_t L, int P, const T *__restrict__ gd, const T *__restrict__ gl,
+    const double *__restrict__ ld_bar, const T *__restrict__ Gd, const T *__restrict__ sinv_ws,
+    const T *__restrict__ x_ws, const T *__restrict__ gg_start, T *__restrict__ p_ws,
+    T *__restrict__ z_ws, T *__restrict__ rmap) {
+  using Tr = io32::Traits<T>;
+  __shared__ __align__(16) T tA[Tr::kTile];
+  __shared__ __align__(16) T tP[Tr::kPacked];
+  const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
+  const Io32<T> io{tA, lane, g, j};
+  const io32::SymLanes<T> sl(g, j, lane);
+  const int64_t m = blockIdx.x / P;
+  const int s = blockIdx.x % P;
+  const SegRange rg = seg_range(L, P, s);
+  const T lb = ld_bar ? static_cast<T>(ld_bar[m]) : T(0);
+  const T *gdm = gd + m * L * kBB32, *glm = gl + m * (L - 1) * kBB32, *GDm = Gd + m * L * kBB32;
+  io.stage(gg_start + (m * P + s) * kBB32, true);
+  Blk<T> GG = io.blk(), Pi = identity32<T>(g, j), R = f32t::zero<T>();
+  for (int64_t i = rg.a0; i < rg.a1; ++i) {
+    f16::wave_sync();
+    io32::put_packed(tP, lane, io32::load_packed(sinv_ws + (m * L + i) * kBB32, lane));
+    f16::wave_sync();
+    const Blk<T> Si = sl.get_packed(tP);
+    // P_i = lb Sinv - Sinv GG Sinv (lower tiles), stored and read back in full
+    const Blk<T> A = f32t::mm(GG, Si, f32t::zero<T>());          // GG Sinv
+    const Blk<T> Pf = io.store_sym(p_ws + (m * L + i) * kBB32,
+                                   f32t::mm_lower(f32t::neg(A), Si, scale32(lb, Si)), true);
+    if (i == L - 1) break;
+    io.stage(x_ws + (m * L + i) * kBB32, true);                  // X_i^T
+    const Blk<T> XT = io.blk(), Xo = io.blk_t();                 // O(X^T), O(X)
+    io.stage(glm + i * kBB32, false);
+    const Blk<T> GLt = io.blk_t();                               // O(gl_i^T)
+    const Blk<T> Wt = f32t::mm(GG, XT, f32t::zero<T>());         // O(W^T), W = X GG
+    const Blk<T> Y1t = f32t::sub(Wt, GLt);                       // O((W - gl)^T)
+    const Blk<T> Y2t = lin32(T(2), Wt, T(-1), GLt);              // O((2W - gl)^T)
+    // GG <- sym(gd_{i+1}) + sym(Y1 X^T)
+    io.stage(gdm + (i + 1) * kBB32, false);
+    GG = lin32(T(0.5), io.blk(), T(0.5), io.blk_t());
+    const Blk<T> Y1h = scale32(T(0.5), Y1t);
+    GG = f32t::mm(Y1h, XT, GG);                                  // + Y1 X^T / 2
+    GG = f32t::mm(XT, Y1h, GG);                                  // + X Y1^T / 2
+    const Blk<T> Z = f32t::mm(Y2t, Si, f32t::zero<T>());         // Z_i = Y2 Sinv
+    io.store(z_ws + (m * L + i) * kBB32, Z, true);
+    // r_i = P_i - sym(X^T G_{i+1,i+1} Z_i)
+    io.stage(GDm + (i + 1) * kBB32, true);
+    const Blk<T> Vh = scale32(T(-0.5), f32t::mm(io.blk_t(), Z, f32t::zero<T>()));  // -G Z / 2
+    Blk<T> rr = f32t::mm(Xo, Vh, Pf);                            // - X^T V / 2
+    rr = f32t::mm(Vh, Xo, rr);                                   // - V^T X / 2
+    // R += Pi^T r Pi, Pi <- X_i Pi
+    const Blk<T> A2 = f32t::mm(rr, Pi, f32t::zero<T>());         // r Pi
+    R = f32t::mm(Pi, A2, R);
+    Pi = f32t::mm(XT, Pi, f32t::zero<T>());
+  }
+  io.store(rmap + (m * P + s) * kBB32, R, true);
+}
+
+// out: Dbar_i and lower_bar_i = G_{i+1,i+1} Z_i - 2 Dbar_{i+1} X_i, descending
+template <typename T>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void cvs32_out(
+    int64_t L, int P, const T *__restrict__ Gd, const T *__restrict__ x_ws,
+    const T *__restrict__ z_ws, const T *__restrict__ p_ws, const T *__restrict__ db_end,
+    const int32_t *__restrict__ info_ws, T *__restrict__ d_bar, T *__restrict__ l_bar,
+    int32_t *__restrict__ info) {
+  using Tr = io32::Traits<T>;
+  __shared__ __align__(16) T tA[Tr::kTile];
+  const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
+  const Io32<T> io{tA, lane, g, j};
   const int64_t m = blockIdx.x / P;
   const int s = blockIdx.x % P;
   const SegRange rg = seg_range(L, P, s);
   const int64_t e = s == P - 1 ? L - 1 : rg.a1;
-  T *Dbm = d_bar + m * L * bb, *Lbm = l_bar + m * (L - 1) * bb;
-  if (s == 0 && threadIdx.x == 0 && info) info[m] = info_ws[m];
+  T *Dbm = d_bar + m * L * kBB32, *Lbm = l_bar + m * (L - 1) * kBB32;
+  if (s == 0 && lane == 0 && info) info[m] = info_ws[m];
   if (info_ws[m]) {
-    for (int64_t q = rg.a0 * bb + threadIdx.x; q < rg.a1 * bb; q += blockDim.x)
-      Dbm[q] = wg::qnan<T>();
-    for (int64_t q = rg.a0 * bb + threadIdx.x; q < min(rg.a1, L - 1) * bb; q += blockDim.x)
-      Lbm[q] = wg::qnan<T>();
+    const T nan = static_cast<T>(__builtin_nan(""));
+    for (int64_t q = rg.a0 * kBB32 + lane; q < rg.a1 * kBB32; q += 64) Dbm[q] = nan;
+    for (int64_t q = rg.a0 * kBB32 + lane; q < min(rg.a1, L - 1) * kBB32; q += 64) Lbm[q] = nan;
     return;
   }
-  wg::copy(Db, db_end + (m * P + s) * bb, bb);
-  if (s == P - 1) wg::copy(Dbm + (L - 1) * bb, Db, bb);  // Dbar_{L-1} = P_{L-1}
+  io.stage(db_end + (m * P + s) * kBB32, true);
+  Blk<T> Db = io.blk();
+  if (s == P - 1) io.store(Dbm + (L - 1) * kBB32, Db, false);  // Dbar_{L-1} = P_{L-1}
   for (int64_t i = e - 1; i >= rg.a0; --i) {
-    wg::copy(Xs, x_ws + (m * L + i) * bb, bb);
-    wg::copy(Zs, z_ws + (m * L + i) * bb, bb);
-    wg::copy(Gs, Gd + (m * L + i + 1) * bb, bb);
-    const T *Pi = p_ws + (m * L + i) * bb;
-    wg::gemm<T, false, false>(T2, Db, Xs, b);                       // Dbar_{i+1} X_i
-    wg::gemm_axpby<T, false, false>(Q, T(-1), T2, T(1), Gs, Zs, b);  // G Z - Dbar X
-    for (int q = threadIdx.x; q < bb; q += blockDim.x) Lbm[i * bb + q] = Q[q] - T2[q];
-    wg::gemm_symmetrized<T, true, false>(Dn, Pi, Xs, Q, b, T(-1));  // P - sym(X^T Q)
-    wg::copy(Db, Dn, bb);
-    wg::copy(Dbm + i * bb, Dn, bb);
+    io.stage(x_ws + (m * L + i) * kBB32, true);
+    const Blk<T> Xo = io.blk_t();                                // O(X_i)
+    io.stage(z_ws + (m * L + i) * kBB32, true);
+    const Blk<T> Z = io.blk();
+    io.stage(Gd + (m * L + i + 1) * kBB32, true);
+    const Blk<T> Gt = io.blk_t();                                // O(G^T)
+    const Blk<T> T2 = f32t::mm(Db, Xo, f32t::zero<T>());         // Dbar_{i+1} X_i (Dbar sym)
+    const Blk<T> Q = f32t::mm(Gt, Z, f32t::neg(T2));             // G Z - Dbar X
+    io.store(Lbm + i * kBB32, f32t::sub(Q, T2), false);          // lower_bar_i = Q - T2
+    io.stage(p_ws + (m * L + i) * kBB32, true);
+    const Blk<T> Qh = scale32(T(-0.5), Q);
+    Blk<T> Dn = f32t::mm(Xo, Qh, io.blk());                      // P - X^T Q / 2
+    Dn = io.symmetrize(f32t::mm(Qh, Xo, Dn));                    // - Q^T X / 2
+    io.store(Dbm + i * kBB32, Dn, false);
+    Db = Dn;
   }
 }
 
@@ -293,19 +403,20 @@ hipError_t chain_vjp_seg_launch(int64_t B, int64_t L, int32_t b, int P, const T 
   T *dbe = reinterpret_cast<T *>(base + o.dbe);
   hipError_t e = chain_launch<T>(B, L, b, diag, lower, Gd, Gl, ld, info_ws, base + o.fwd, s);
   if (e != hipSuccess) return e;
+  if (b != 32) return hipErrorInvalidValue;  // segments are planned for b = 32 only
   const int nt = cvs_threads(b);
   const size_t bb = static_cast<size_t>(b) * b;
   const dim3 segs(static_cast<unsigned>(B * P)), chains(static_cast<unsigned>(B));
-  hipLaunchKernelGGL(cvs_prep<T>, segs, dim3(nt), (7 * bb + b) * sizeof(T), s, L, b, P, diag,
-                     lower, gd, gl, Gd, Gl, sinv, x, phi, cmap);
+  hipLaunchKernelGGL(cvs32_prep<T>, segs, dim3(64), 0, s, L, P, diag, lower, gd, gl, Gd, Gl,
+                     sinv, x, phi, cmap);
   hipLaunchKernelGGL(cvs_gg_scan<T>, chains, dim3(nt), 3 * bb * sizeof(T), s, b, P, L, gd, phi,
                      cmap, ggs);
-  hipLaunchKernelGGL(cvs_mid<T>, segs, dim3(nt), 8 * bb * sizeof(T), s, L, b, P, gd, gl, ld_bar,
-                     Gd, sinv, x, ggs, p, z, rmap);
+  hipLaunchKernelGGL(cvs32_mid<T>, segs, dim3(64), 0, s, L, P, gd, gl, ld_bar, Gd, sinv, x, ggs,
+                     p, z, rmap);
   hipLaunchKernelGGL(cvs_db_scan<T>, chains, dim3(nt), 3 * bb * sizeof(T), s, b, P, L, p, phi,
                      rmap, dbe);
-  hipLaunchKernelGGL(cvs_out<T>, segs, dim3(nt), 7 * bb * sizeof(T), s, L, b, P, Gd, x, z, p, dbe,
-                     info_ws, d_bar, l_bar, info);
+  hipLaunchKernelGGL(cvs32_out<T>, segs, dim3(64), 0, s, L, P, Gd, x, z, p, dbe, info_ws, d_bar,
+                     l_bar, info);
   return hipGetLastError();
 }
 
