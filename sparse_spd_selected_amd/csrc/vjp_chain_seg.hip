@@ -137,6 +137,12 @@ struct Io32 {
     io32::put(tile, lane, ws ? io32::load_ws(P, lane) : io32::load(P, lane));
     f16::wave_sync();
   }
+  // a block already loaded into registers
+  __device__ __forceinline__ void stage(const io32::Nat<T> &n) const {
+    f16::wave_sync();
+    io32::put(tile, lane, n);
+    f16::wave_sync();
+  }
   __device__ __forceinline__ Blk<T> blk() const { return io32::get_blk(tile, g, j); }
   __device__ __forceinline__ Blk<T> blk_t() const { return io32::get_blk_t(tile, g, j); }
   // row-major store of the block b (all four tiles formed)
@@ -217,23 +223,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     f16::wave_sync();
     io32::store_packed(sinv_ws + (m * L + i) * kBB32, lane, sl.gather_packed(tA));
     if (i == L - 1) break;
-    io.stage(C + i * kBB32, false);
+    // the step's four input blocks, loaded together
+    const io32::Nat<T> nC = io32::load(C + i * kBB32, lane);
+    const io32::Nat<T> nD = io32::load(D + (i + 1) * kBB32, lane);
+    const io32::Nat<T> nGl = io32::load(glm + i * kBB32, lane);
+    const io32::Nat<T> nGd = io32::load(gdm + (i + 1) * kBB32, lane);
+    io.stage(nC);
     const Blk<T> Ct = io.blk_t();                                // O(C_i^T)
     const Blk<T> XT = f32t::mm(S, Ct, f32t::zero<T>());          // O(X_i^T) = O(Sinv C_i^T)
     io.store(x_ws + (m * L + i) * kBB32, XT, true);              // X_i^T, row-major
-    {  // S_{i+1} = D_{i+1} - C_i Sinv_i C_i^T (tile (1,0) not formed)
-      f16::wave_sync();
-      io32::put(tA, lane, io32::load(D + (i + 1) * kBB32, lane));
-      f16::wave_sync();
-      S = f32t::sub(sl.get_sym(tA), f32t::mm_upper(Ct, XT, f32t::zero<T>()));
-    }
-    // c_i = sym(gd_{i+1}) - sym(gl_i X_i^T)
-    io.stage(gdm + (i + 1) * kBB32, false);
-    Blk<T> c = lin32(T(0.5), io.blk(), T(0.5), io.blk_t());
-    io.stage(glm + i * kBB32, false);
-    const Blk<T> GLth = scale32(T(-0.5), io.blk_t());           // -O(gl_i^T) / 2
-    c = f32t::mm(GLth, XT, c);                                   // - gl X^T / 2
-    c = f32t::mm(XT, GLth, c);                                   // - X gl^T / 2
+    // S_{i+1} = D_{i+1} - C_i Sinv_i C_i^T (tile (1,0) not formed)
+    io.stage(nD);
+    S = f32t::sub(sl.get_sym(tA), f32t::mm_upper(Ct, XT, f32t::zero<T>()));
+    // c_i = sym(gd_{i+1}) - sym(gl_i X_i^T) = sym(gd_{i+1} - gl_i X_i^T)
+    io.stage(nGl);
+    const Blk<T> GLtn = f32t::neg(io.blk_t());                   // -O(gl_i^T)
+    io.stage(nGd);
+    const Blk<T> c = io.symmetrize(f32t::mm(GLtn, XT, io.blk()));
     Ph = f32t::mm(XT, Ph, f32t::zero<T>());                      // Phi <- X_i Phi
     const Blk<T> W = f32t::mm(Cm, XT, f32t::zero<T>());          // Cm X^T
     Cm = f32t::mm(XT, W, c);                                     // X Cm X^T + c
@@ -263,35 +269,39 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   io.stage(gg_start + (m * P + s) * kBB32, true);
   Blk<T> GG = io.blk(), Pi = identity32<T>(g, j), R = f32t::zero<T>();
   for (int64_t i = rg.a0; i < rg.a1; ++i) {
+    // the step's input blocks, loaded together (the last block has only Sinv)
+    const bool more = i < L - 1;
+    const int64_t inx = more ? i + 1 : i;
+    const io32::NatP<T> nS = io32::load_packed(sinv_ws + (m * L + i) * kBB32, lane);
+    const io32::Nat<T> nX = io32::load_ws(x_ws + (m * L + (more ? i : 0)) * kBB32, lane);
+    const io32::Nat<T> nGl = io32::load(glm + (more ? i : 0) * kBB32, lane);
+    const io32::Nat<T> nGd = io32::load(gdm + inx * kBB32, lane);
+    const io32::Nat<T> nG = io32::load_ws(GDm + inx * kBB32, lane);
     f16::wave_sync();
-    io32::put_packed(tP, lane, io32::load_packed(sinv_ws + (m * L + i) * kBB32, lane));
+    io32::put_packed(tP, lane, nS);
     f16::wave_sync();
     const Blk<T> Si = sl.get_packed(tP);
     // P_i = lb Sinv - Sinv GG Sinv (lower tiles), stored and read back in full
     const Blk<T> A = f32t::mm(GG, Si, f32t::zero<T>());          // GG Sinv
     const Blk<T> Pf = io.store_sym(p_ws + (m * L + i) * kBB32,
                                    f32t::mm_lower(f32t::neg(A), Si, scale32(lb, Si)), true);
-    if (i == L - 1) break;
-    io.stage(x_ws + (m * L + i) * kBB32, true);                  // X_i^T
+    if (!more) break;
+    io.stage(nX);                                                // X_i^T
     const Blk<T> XT = io.blk(), Xo = io.blk_t();                 // O(X^T), O(X)
-    io.stage(glm + i * kBB32, false);
+    io.stage(nGl);
     const Blk<T> GLt = io.blk_t();                               // O(gl_i^T)
     const Blk<T> Wt = f32t::mm(GG, XT, f32t::zero<T>());         // O(W^T), W = X GG
     const Blk<T> Y1t = f32t::sub(Wt, GLt);                       // O((W - gl)^T)
     const Blk<T> Y2t = lin32(T(2), Wt, T(-1), GLt);              // O((2W - gl)^T)
-    // GG <- sym(gd_{i+1}) + sym(Y1 X^T)
-    io.stage(gdm + (i + 1) * kBB32, false);
-    GG = lin32(T(0.5), io.blk(), T(0.5), io.blk_t());
-    const Blk<T> Y1h = scale32(T(0.5), Y1t);
-    GG = f32t::mm(Y1h, XT, GG);                                  // + Y1 X^T / 2
-    GG = f32t::mm(XT, Y1h, GG);                                  // + X Y1^T / 2
+    // GG <- sym(gd_{i+1}) + sym(Y1 X^T) = sym(gd_{i+1} + Y1 X^T)
+    io.stage(nGd);
+    GG = io.symmetrize(f32t::mm(Y1t, XT, io.blk()));
     const Blk<T> Z = f32t::mm(Y2t, Si, f32t::zero<T>());         // Z_i = Y2 Sinv
     io.store(z_ws + (m * L + i) * kBB32, Z, true);
-    // r_i = P_i - sym(X^T G_{i+1,i+1} Z_i)
-    io.stage(GDm + (i + 1) * kBB32, true);
-    const Blk<T> Vh = scale32(T(-0.5), f32t::mm(io.blk_t(), Z, f32t::zero<T>()));  // -G Z / 2
-    Blk<T> rr = f32t::mm(Xo, Vh, Pf);                            // - X^T V / 2
-    rr = f32t::mm(Vh, Xo, rr);                                   // - V^T X / 2
+    // r_i = P_i - sym(X^T G_{i+1,i+1} Z_i) = sym(P_i - X^T G Z)  (P_i symmetric)
+    io.stage(nG);
+    const Blk<T> Vn = f32t::neg(f32t::mm(io.blk_t(), Z, f32t::zero<T>()));  // -G Z
+    const Blk<T> rr = io.symmetrize(f32t::mm(Xo, Vn, Pf));
     // R += Pi^T r Pi, Pi <- X_i Pi
     const Blk<T> A2 = f32t::mm(rr, Pi, f32t::zero<T>());         // r Pi
     R = f32t::mm(Pi, A2, R);
@@ -327,19 +337,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   Blk<T> Db = io.blk();
   if (s == P - 1) io.store(Dbm + (L - 1) * kBB32, Db, false);  // Dbar_{L-1} = P_{L-1}
   for (int64_t i = e - 1; i >= rg.a0; --i) {
-    io.stage(x_ws + (m * L + i) * kBB32, true);
+    // the step's input blocks, loaded together
+    const io32::Nat<T> nX = io32::load_ws(x_ws + (m * L + i) * kBB32, lane);
+    const io32::Nat<T> nZ = io32::load_ws(z_ws + (m * L + i) * kBB32, lane);
+    const io32::Nat<T> nG = io32::load_ws(Gd + (m * L + i + 1) * kBB32, lane);
+    const io32::Nat<T> nP = io32::load_ws(p_ws + (m * L + i) * kBB32, lane);
+    io.stage(nX);
     const Blk<T> Xo = io.blk_t();                                // O(X_i)
-    io.stage(z_ws + (m * L + i) * kBB32, true);
+    io.stage(nZ);
     const Blk<T> Z = io.blk();
-    io.stage(Gd + (m * L + i + 1) * kBB32, true);
+    io.stage(nG);
     const Blk<T> Gt = io.blk_t();                                // O(G^T)
     const Blk<T> T2 = f32t::mm(Db, Xo, f32t::zero<T>());         // Dbar_{i+1} X_i (Dbar sym)
     const Blk<T> Q = f32t::mm(Gt, Z, f32t::neg(T2));             // G Z - Dbar X
     io.store(Lbm + i * kBB32, f32t::sub(Q, T2), false);          // lower_bar_i = Q - T2
-    io.stage(p_ws + (m * L + i) * kBB32, true);
-    const Blk<T> Qh = scale32(T(-0.5), Q);
-    Blk<T> Dn = f32t::mm(Xo, Qh, io.blk());                      // P - X^T Q / 2
-    Dn = io.symmetrize(f32t::mm(Qh, Xo, Dn));                    // - Q^T X / 2
+    io.stage(nP);
+    // Dbar_i = P_i - sym(X^T Q) = sym(P_i - X^T Q)  (P_i symmetric)
+    const Blk<T> Dn = io.symmetrize(f32t::mm(Xo, f32t::neg(Q), io.blk()));
     io.store(Dbm + i * kBB32, Dn, false);
     Db = Dn;
   }
