@@ -91,6 +91,13 @@ __device__ __forceinline__ void store_transposed(T *P, int b, int i, const r8::R
     if (c < b) store_coherent(P + c * b + i, r.v[c]);
 }
 
+// The end of a wait that starts now and lasts `ticks` (clamped, so that a
+// huge limit cannot wrap around).
+__device__ __forceinline__ uint64_t deadline_after(uint64_t ticks) {
+  const uint64_t cap = uint64_t(1) << 62;
+  return static_cast<uint64_t>(wall_clock64()) + (ticks < cap ? ticks : cap);
+}
+
 // Lanes sub, sub + stride, ... of [beg, end) wait until flags[c] >= want.
 __device__ __forceinline__ void wait_flags(const int32_t *flags, int64_t beg, int64_t end,
                                            int32_t want, int sub, int stride, int32_t *timeout,
@@ -98,7 +105,7 @@ __device__ __forceinline__ void wait_flags(const int32_t *flags, int64_t beg, in
   for (int64_t c = beg + sub; c < end; c += stride) {
     while (__hip_atomic_load(flags + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
       if (__hip_atomic_load(timeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
-      if (wall_clock64() >= deadline) {
+      if (static_cast<uint64_t>(wall_clock64()) >= deadline) {
         __hip_atomic_store(timeout, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
       }

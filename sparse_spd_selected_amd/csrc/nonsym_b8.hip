@@ -82,7 +82,7 @@ __global__ __launch_bounds__(64) void nstree8_collect(
     int32_t *__restrict__ st_fail, int32_t *__restrict__ first_fail,
     int32_t *__restrict__ flags, int32_t *__restrict__ timeout, uint64_t wait_ticks) {
   __shared__ __align__(32) T lds[2][kSlots * 64];
-  const uint64_t deadline = wall_clock64() + wait_ticks;
+  const uint64_t deadline = df::deadline_after(wait_ticks);
   const int lane = threadIdx.x;
   const int s = lane >> 3, i = lane & 7;
   const r8::Stage<T> sa{lds[0]}, sb{lds[1]};
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(64) void nstree8_distribute(
     T *__restrict__ G_up, T *__restrict__ G_down, int32_t *__restrict__ flags,
     int32_t *__restrict__ timeout, uint64_t wait_ticks) {
   __shared__ __align__(32) T lds[2][kSlots * 64];
-  const uint64_t deadline = wall_clock64() + wait_ticks;
+  const uint64_t deadline = df::deadline_after(wait_ticks);
   const int lane = threadIdx.x;
   const int s = lane >> 3, i = lane & 7;
   const r8::Stage<T> sa{lds[0]}, sb{lds[1]};

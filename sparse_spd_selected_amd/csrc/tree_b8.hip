@@ -52,7 +52,7 @@ __global__ __launch_bounds__(64) void tree8_collect(
     int32_t *__restrict__ first_fail, T *__restrict__ G_diag, T *__restrict__ G_edge,
     int32_t *__restrict__ flags, int32_t *__restrict__ timeout, uint64_t wait_ticks) {
   __shared__ __align__(32) T lds[2][kSlots * 64];
-  const uint64_t deadline = wall_clock64() + wait_ticks;
+  const uint64_t deadline = df::deadline_after(wait_ticks);
   const int lane = threadIdx.x;
   const int s = lane >> 3, i = lane & 7;
   const r8::Stage<T> sa{lds[0]}, sb{lds[1]};
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(64) void tree8_distribute(
     T *__restrict__ G_diag, T *__restrict__ G_edge, int32_t *__restrict__ flags,
     int32_t *__restrict__ timeout, uint64_t wait_ticks) {
   __shared__ __align__(32) T lds[2][kSlots * 64];
-  const uint64_t deadline = wall_clock64() + wait_ticks;
+  const uint64_t deadline = df::deadline_after(wait_ticks);
   const int lane = threadIdx.x;
   const int s = lane >> 3, i = lane & 7;
   const r8::Stage<T> sa{lds[0]}, sb{lds[1]};
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64) void tree8_solve_fwd(
     T *__restrict__ x, T *__restrict__ msg, int32_t *__restrict__ flags,
     int32_t *__restrict__ timeout, uint64_t wait_ticks) {
   __shared__ __align__(32) T lds[2][kSlots * 64];
-  const uint64_t deadline = wall_clock64() + wait_ticks;
+  const uint64_t deadline = df::deadline_after(wait_ticks);
   const int lane = threadIdx.x;
   const int s = lane >> 3, i = lane & 7;
   const r8::Stage<T> sa{lds[0]}, sb{lds[1]};
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(64) void tree8_solve_bwd(
     const T *__restrict__ edge, const T *__restrict__ factor, T *__restrict__ x,
     int32_t *__restrict__ flags, int32_t *__restrict__ timeout, uint64_t wait_ticks) {
   __shared__ __align__(32) T lds[2][kSlots * 64];
-  const uint64_t deadline = wall_clock64() + wait_ticks;
+  const uint64_t deadline = df::deadline_after(wait_ticks);
   const int lane = threadIdx.x;
   const int s = lane >> 3, i = lane & 7;
   const r8::Stage<T> sa{lds[0]}, sb{lds[1]};

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(64) void tree8_vjp_collect(
     int32_t *__restrict__ first_fail, T *__restrict__ d_bar, T *__restrict__ e_bar,
     int32_t *__restrict__ flags, int32_t *__restrict__ timeout, uint64_t wait_ticks) {
   __shared__ __align__(32) T lds[2][kSlots * 64];
-  const uint64_t deadline = wall_clock64() + wait_ticks;
+  const uint64_t deadline = df::deadline_after(wait_ticks);
   const int lane = threadIdx.x;
   const int s = lane >> 3, i = lane & 7;
   const r8::Stage<T> sa{lds[0]}, sb{lds[1]};
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(64) void tree8_vjp_distribute(
     T *__restrict__ d_bar, T *__restrict__ e_bar, int32_t *__restrict__ flags,
     int32_t *__restrict__ timeout, uint64_t wait_ticks) {
   __shared__ __align__(32) T lds[2][kSlots * 64];
-  const uint64_t deadline = wall_clock64() + wait_ticks;
+  const uint64_t deadline = df::deadline_after(wait_ticks);
   const int lane = threadIdx.x;
   const int s = lane >> 3, i = lane & 7;
   const r8::Stage<T> sa{lds[0]}, sb{lds[1]};
