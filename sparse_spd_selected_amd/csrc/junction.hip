@@ -38,6 +38,7 @@
 #include <climits>
 
 #include "block_wg.h"
+#include "frag16.h"
 #include "internal.h"
 
 namespace selinv {
@@ -607,6 +608,13 @@ __global__ void __launch_bounds__(kJT) jt_bwd_rows(JunctionPlanDev P, Dims d, in
   const T *Gd = G_diag + mat * d.n * bb, *Gl = G_lower + mat * d.nnz * bb;
   const int32_t *gt = P.gtab + P.ch_gptr[id];
   const int ty = t / 16, tx = t % 16;  // rows 4 ty .. 4 ty + 3, columns tx + 16 j
+  // b a multiple of 4 (compile time): the products run on the matrix cores,
+  // wavefront w owning rows 16 w .. 16 w + 15 of the tile and the column
+  // blocks 16 cb .. 16 cb + 15 (cb < 3); otherwise a 4 x 3 register tile per
+  // thread on the vector units
+  constexpr bool kMfma = BC != 0 && BC % 4 == 0;
+  const int wv = t >> 6, ln = t & 63, lr = ln & 15, lk = ln >> 4;
+  f16::Frag<T> accm[3] = {f16::zero<T>(), f16::zero<T>(), f16::zero<T>()};
   T acc[4][3];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -640,6 +648,26 @@ __global__ void __launch_bounds__(kJT) jt_bwd_rows(JunctionPlanDev P, Dims d, in
       return Wp[(int64_t(s + q0 + q) * s + cc / b) * bb + k * b + cc % b];
     });
     __syncthreads();
+    if constexpr (kMfma) {
+      // one MFMA step per 4 of the b inner indices: lane (lk, lr) supplies
+      // A[16 w + lr][4 kk + lk] and B[4 kk + lk][16 cb + lr]
+      for (int q = 0; q < cnt; ++q) {
+        const T *A = sA + q * H * b, *Bq = sB + q * b * sb;
+#pragma unroll
+        for (int kk = 0; kk < BC / 4; ++kk) {
+          const int k = 4 * kk + lk;
+          const T a = A[(16 * wv + lr) * b + k];
+#pragma unroll
+          for (int cb = 0; cb < 3; ++cb) {
+            const int cc = 16 * cb + lr;
+            const T bv = cc < sb ? Bq[k * sb + cc] : T(0);
+            accm[cb] = f16::Mfma<T>::op(a, bv, accm[cb]);
+          }
+        }
+      }
+      __syncthreads();
+      continue;
+    }
     for (int q = 0; q < cnt; ++q) {
       const T *A = sA + q * H * b, *Bq = sB + q * b * sb;
       for (int k = 0; k < b; ++k) {
@@ -662,26 +690,33 @@ __global__ void __launch_bounds__(kJT) jt_bwd_rows(JunctionPlanDev P, Dims d, in
     }
     __syncthreads();
   }
+  // the tile's H x sb result, row-major, to dst
+  auto put_tile = [&](T *dst) {
+    if constexpr (kMfma) {
+#pragma unroll
+      for (int cb = 0; cb < 3; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = 16 * wv + f16::Mfma<T>::row(lk, r), cc = 16 * cb + lr;
+          if (cc < sb) dst[h * sb + cc] = accm[cb][r];
+        }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          const int h = 4 * ty + r, cc = tx + 16 * j;
+          if (h < H && cc < sb) dst[h * sb + cc] = acc[r][j];
+        }
+    }
+  };
   if (nsplit > 1) {  // partial sum to the workspace; jt_bwd_rows_sum finishes the tile
-    T *dst = Tpart + ((mat * gridDim.x + blockIdx.x)) * int64_t(kTilePart);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const int h = 4 * ty + r, cc = tx + 16 * j;
-        if (h < H && cc < sb) dst[h * sb + cc] = acc[r][j];
-      }
+    put_tile(Tpart + ((mat * gridDim.x + blockIdx.x)) * int64_t(kTilePart));
     return;
   }
   // epilogue: T (H x sb) and R_J^-1 in LDS, then -T R_J^-1 to the output
   T *Tt = stage, *Ri = Tt + H * sb;
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const int h = 4 * ty + r, cc = tx + 16 * j;
-      if (h < H && cc < sb) Tt[h * sb + cc] = acc[r][j];
-    }
+  put_tile(Tt);
   rows_epilogue<BC>(P, d, mat, id, a0, rows, Tt, Ri, RJ, G_lower);
 }
 
