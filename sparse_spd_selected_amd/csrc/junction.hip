@@ -543,6 +543,56 @@ __global__ void __launch_bounds__(kJT) jt_fwd_scale(JunctionPlanDev P, Dims d, i
   }
 }
 
+// The same scaling for b = 4, 8, 16, a tile of up to 64 / b later rows of one
+// chunk per workgroup (the tiles of the backward row products): R_J^-1 is
+// staged once per tile, and W_tile = C_tile R_J^-T runs on the matrix cores,
+// wavefront w owning rows 16 w .. 16 w + 15 and three 16-column blocks; lane
+// (lk, lr) supplies C[16 w + lr][k] and R_J^-1[16 cb + lr][k], k = 4 kk + lk.
+template <typename T, int BC>
+__global__ void __launch_bounds__(kJT) jt_fwd_scale_tiles(JunctionPlanDev P, Dims d,
+                                                          int64_t tbase, T *W, const T *RJ) {
+  static_assert(BC % 4 == 0, "matrix-core scaling needs b a multiple of 4");
+  extern __shared__ char smem_raw[];
+  T *Ri = reinterpret_cast<T *>(smem_raw);
+  constexpr int b = BC, bb = b * b, R = 64 / b, H = 64;
+  const int t = threadIdx.x;
+  const int64_t tile = tbase + blockIdx.x, mat = blockIdx.y;
+  const int id = P.tile_chunk[tile];
+  const int a0 = static_cast<int>(tile - P.tiles_ptr[id]) * R;
+  const int s = P.ch_s[id], nr = P.ch_n[id], sb = s * b;
+  const int rows = nr - a0 < R ? nr - a0 : R;
+  T *Cs = Ri + sb * sb;  // H x sb
+  const T *Rj = RJ + (mat * d.nrinv + P.ch_rbase[id]) * bb;
+  T *Wp = W + (mat * d.npanel + P.ch_pbase[id]) * bb;
+  gather_lds(Ri, sb * sb, [&](int e) { return Rj[e]; });
+  gather_lds(Cs, H * sb, [&](int e) {
+    const int h = e / sb, cc = e - h * sb, ra = h / b, i = h - ra * b;
+    return ra < rows ? Wp[(int64_t(s + a0 + ra) * s + cc / b) * bb + i * b + cc % b] : T(0);
+  });
+  __syncthreads();
+  const int wv = t >> 6, ln = t & 63, lr = ln & 15, lk = ln >> 4;
+  f16::Frag<T> acc[3] = {f16::zero<T>(), f16::zero<T>(), f16::zero<T>()};
+  for (int kk = 0; kk < sb / 4; ++kk) {
+    const int k = 4 * kk + lk;
+    const T a = Cs[(16 * wv + lr) * sb + k];
+#pragma unroll
+    for (int cb = 0; cb < 3; ++cb) {
+      const int cc = 16 * cb + lr;
+      const T bv = cc < sb ? Ri[cc * sb + k] : T(0);
+      acc[cb] = f16::Mfma<T>::op(a, bv, acc[cb]);
+    }
+  }
+#pragma unroll
+  for (int cb = 0; cb < 3; ++cb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 16 * wv + f16::Mfma<T>::row(lk, r), cc = 16 * cb + lr;
+      const int ra = h / b, i = h - ra * b;
+      if (cc < sb && ra < rows)
+        Wp[(int64_t(s + a0 + ra) * s + cc / b) * bb + i * b + cc % b] = acc[cb][r];
+    }
+}
+
 // Row tiles of the level: for R consecutive later rows w of a chunk (H = R b
 // scalar rows), G_{w,J} = -(sum_x G_{w,x} W_{x,J}) R_J^-1.  The sum is a
 // gathered product (H x n b) (n b x s b): each step stages, for one x, the
@@ -1006,7 +1056,8 @@ hipError_t junction_run(const selinv_junction_plan *plan, int64_t B, const T *di
                l_sum = sizeof(T) * (size_t(kTilePart) + size_t(sm) * b * sm * b) +
                        4 * size_t(tile_rows(b)) * sm,
                l_dsum = sizeof(T) * (size_t(sm) * b * sm * b + 3 * size_t(sm) * b * b) + 4 * sm;
-  if (l_upd > kLdsMax || l_fac > kLdsMax || l_scl > kLdsMax || l_row > kLdsMax ||
+  const size_t l_sct = sizeof(T) * (size_t(sm) * b * sm * b + 64 * size_t(sm) * b);
+  if (l_upd > kLdsMax || l_fac > kLdsMax || l_scl > kLdsMax || l_sct > kLdsMax || l_row > kLdsMax ||
       l_dia > kLdsMax || l_sum > kLdsMax || l_dsum > kLdsMax)
     return hipErrorInvalidValue;
   const auto &lo = plan->level_off;
@@ -1033,9 +1084,16 @@ hipError_t junction_run(const selinv_junction_plan *plan, int64_t B, const T *di
     }
     jt_fwd_factor<T, BC><<<dim3(static_cast<unsigned>(c1 - c0), By), blk, l_fac, s>>>(
         P, d, c0, W, RJ, w.ld, w.info);
-    if (rp[c1] > rp[c0])
+    if constexpr (BC == 4 || BC == 8 || BC == 16) {
+      const auto &tl = plan->tiles_ptr;
+      const int64_t nt = tl[c1] - tl[c0];
+      if (nt > 0)
+        jt_fwd_scale_tiles<T, BC><<<dim3(static_cast<unsigned>(nt), By), blk, l_sct, s>>>(
+            P, d, tl[c0], W, RJ);
+    } else if (rp[c1] > rp[c0]) {
       jt_fwd_scale<T, BC><<<dim3(static_cast<unsigned>(rp[c1] - rp[c0]), By), blk, l_scl, s>>>(
           P, d, rp[c0], W, RJ);
+    }
   }
   for (int32_t l = G_diag ? plan->levels - 1 : -1; l >= 0; --l) {
     const int64_t c0 = lo[l], c1 = lo[l + 1];
