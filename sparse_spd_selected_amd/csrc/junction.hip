@@ -614,6 +614,36 @@ __device__ inline void rows_epilogue(const JunctionPlanDev &P, const Dims &d, in
     codes[e] = P.poutenc[pb + int64_t(s + a0) * s + e];
   gather_lds(Ri, sb * sb, [&](int e) { return RJ[(mat * d.nrinv + P.ch_rbase[id]) * bb + e]; });
   __syncthreads();
+  if constexpr (BC != 0 && BC % 4 == 0) {
+    // on the matrix cores (the tile is 64 rows): wavefront w owns rows
+    // 16 w .. 16 w + 15 and three 16-column blocks; lane (lk, lr) supplies
+    // T[16 w + lr][k] and R_J^-1[k][16 cb + lr], k = 4 kk + lk
+    const int t = threadIdx.x, wv = t >> 6, ln = t & 63, lr = ln & 15, lk = ln >> 4;
+    f16::Frag<T> acc[3] = {f16::zero<T>(), f16::zero<T>(), f16::zero<T>()};
+    for (int kk = 0; kk < sb / 4; ++kk) {
+      const int k = 4 * kk + lk;
+      const T a = Tt[(16 * wv + lr) * sb + k];
+#pragma unroll
+      for (int cb = 0; cb < 3; ++cb) {
+        const int cc = 16 * cb + lr;
+        const T bv = cc < sb ? Ri[k * sb + cc] : T(0);
+        acc[cb] = f16::Mfma<T>::op(a, bv, acc[cb]);
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < 3; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 16 * wv + f16::Mfma<T>::row(lk, r), cc = 16 * cb + lr;
+        const int ra = h / b, i = h - ra * b, j = cc % b;
+        if (cc < sb && ra < rows) {
+          const int32_t o = codes[ra * s + cc / b];
+          T *dst = G_lower + (mat * d.nnz + (o >> 1)) * bb;
+          dst[(o & 1) ? j * b + i : i * b + j] = -acc[cb][r];
+        }
+      }
+    return;
+  }
   for (int e = threadIdx.x; e < rows * b * sb; e += kJT) {
     const int h = e / sb, cc = e - h * sb;
     T v = T(0);
