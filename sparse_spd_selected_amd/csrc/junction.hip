@@ -907,6 +907,10 @@ __global__ void __launch_bounds__(kJT) jt_bwd_diag(JunctionPlanDev P, Dims d, in
   const int qlo = static_cast<int>(int64_t(nr) * part / nsplit);
   const int qhi = static_cast<int>(int64_t(nr) * (part + 1) / nsplit);
   T acc[6] = {T(0), T(0), T(0), T(0), T(0), T(0)};
+  // b a multiple of 4 (compile time): the sum runs on the matrix cores
+  constexpr bool kMfma = BC != 0 && BC % 4 == 0;
+  const int wv = t >> 6, ln = t & 63, lr = ln & 15, lk = ln >> 4;
+  f16::Frag<T> accm = f16::zero<T>();
   for (int q0 = qlo; q0 < qhi; q0 += CH) {
     const int cnt = qhi - q0 < CH ? qhi - q0 : CH;
     // W_{x_q,J} as dense b x sb rows; G_{x_q, f+col} blocks
@@ -920,16 +924,47 @@ __global__ void __launch_bounds__(kJT) jt_bwd_diag(JunctionPlanDev P, Dims d, in
       return Gl[int64_t(o >> 1) * bb + ((o & 1) ? j * b + k : el)];
     });
     __syncthreads();
+    if constexpr (kMfma) {
+      // wavefront w < 3 owns rows 16 w .. 16 w + 15 of the sb x b result;
+      // lane (lk, lr) supplies W_q[k][16 w + lr] and G_q[k][lr], k = 4 kk + lk
+      if (wv < 3 && 16 * wv < sb) {
+        for (int q = 0; q < cnt; ++q) {
+          const T *A = sA + q * wr, *Bq = sB + q * bb;
+#pragma unroll
+          for (int kk = 0; kk < BC / 4; ++kk) {
+            const int k = 4 * kk + lk, I = 16 * wv + lr;
+            const T a = I < sb ? A[k * sb + I] : T(0);
+            const T bv = lr < b ? Bq[k * b + lr] : T(0);
+            accm = f16::Mfma<T>::op(a, bv, accm);
+          }
+        }
+      }
+    } else {
+      for (int u = 0; u < 6; ++u) {
+        const int e = t + u * kJT;
+        if (e >= ob) break;
+        const int I = e / b, j = e - I * b;
+        for (int q = 0; q < cnt; ++q) {
+          const T *A = sA + q * wr + I, *Bq = sB + q * bb + j;
+          T v = T(0);
+          for (int k = 0; k < b; ++k) v += A[k * sb] * Bq[k * b];
+          acc[u] += v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if constexpr (kMfma) {  // the matrix-core result to acc[] in the vector layout, through sA
+    if (wv < 3)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int I = 16 * wv + f16::Mfma<T>::row(lk, r);
+        if (I < sb && lr < b) sA[I * b + lr] = accm[r];
+      }
+    __syncthreads();
     for (int u = 0; u < 6; ++u) {
       const int e = t + u * kJT;
-      if (e >= ob) break;
-      const int I = e / b, j = e - I * b;
-      for (int q = 0; q < cnt; ++q) {
-        const T *A = sA + q * wr + I, *Bq = sB + q * bb + j;
-        T v = T(0);
-        for (int k = 0; k < b; ++k) v += A[k * sb] * Bq[k * b];
-        acc[u] += v;
-      }
+      if (e < ob) acc[u] = sA[e];
     }
     __syncthreads();
   }
