@@ -402,6 +402,21 @@ __device__ __forceinline__ void write_target(const JunctionPlanDev &P, const Dim
 // the wavefront's LDS.  A target with one item is finished here; the items
 // of a longer list leave partial sums in their slots of Spart for
 // jt_fwd_update_sum.
+// Workgroup (x, matrix) of a 2-D launch, remapped so that each of the eight
+// XCDs (the dispatcher deals workgroups to them round-robin by linear index)
+// runs one contiguous range of linear indices: neighbouring work items, which
+// read many of the same panel blocks, then share that XCD's L2.  A bijection
+// of the grid, so the result does not depend on the real dispatch.
+struct WgXM {
+  int64_t x, mat;
+};
+__device__ inline WgXM xcd_wg() {
+  const int64_t nx = gridDim.x, n = nx * gridDim.y, w = int64_t(blockIdx.y) * nx + blockIdx.x;
+  const int64_t xcd = w % 8, k = w / 8, q = n / 8, r = n % 8;
+  const int64_t l = xcd * q + (xcd < r ? xcd : r) + k;
+  return {l % nx, l / nx};
+}
+
 template <typename T, int BC>
 __global__ void __launch_bounds__(kJT) jt_fwd_update_wave(JunctionPlanDev P, Dims d,
                                                           int64_t ibase, int64_t iend,
@@ -415,7 +430,8 @@ __global__ void __launch_bounds__(kJT) jt_fwd_update_wave(JunctionPlanDev P, Dim
   __shared__ int32_t tab[4][2 * CH];
   __shared__ T red[4][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t it = ibase + int64_t(blockIdx.x) * 4 + wave, mat = blockIdx.y;
+  const WgXM wg = xcd_wg();
+  const int64_t it = ibase + wg.x * 4 + wave, mat = wg.mat;
   if (it >= iend) return;
   const int64_t tg = P.it_tg[it];
   const int32_t f0 = P.it_lo[it], f1 = P.it_hi[it], slot = P.it_slot[it];
@@ -556,7 +572,8 @@ __global__ void __launch_bounds__(kJT) jt_fwd_scale_tiles(JunctionPlanDev P, Dim
   T *Ri = reinterpret_cast<T *>(smem_raw);
   constexpr int b = BC, bb = b * b, R = 64 / b, H = 64;
   const int t = threadIdx.x;
-  const int64_t tile = tbase + blockIdx.x, mat = blockIdx.y;
+  const WgXM wg = xcd_wg();
+  const int64_t tile = tbase + wg.x, mat = wg.mat;
   const int id = P.tile_chunk[tile];
   const int a0 = static_cast<int>(tile - P.tiles_ptr[id]) * R;
   const int s = P.ch_s[id], nr = P.ch_n[id], sb = s * b;
@@ -671,8 +688,9 @@ __global__ void __launch_bounds__(kJT) jt_bwd_rows(JunctionPlanDev P, Dims d, in
   T *stage = reinterpret_cast<T *>(smem_raw + kTileTableBytes);
   const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
   const int R = tile_rows(b), H = R * b;
-  const int64_t tl = blockIdx.x / nsplit, mat = blockIdx.y;
-  const int part = blockIdx.x - static_cast<int>(tl) * nsplit;
+  const WgXM wg = xcd_wg();
+  const int64_t bx = wg.x, tl = bx / nsplit, mat = wg.mat;
+  const int part = static_cast<int>(bx - tl * nsplit);
   const int64_t tile = tbase + tl;
   const int id = P.tile_chunk[tile];
   const int a0 = static_cast<int>(tile - P.tiles_ptr[id]) * R;
@@ -791,7 +809,7 @@ __global__ void __launch_bounds__(kJT) jt_bwd_rows(JunctionPlanDev P, Dims d, in
     }
   };
   if (nsplit > 1) {  // partial sum to the workspace; jt_bwd_rows_sum finishes the tile
-    put_tile(Tpart + ((mat * gridDim.x + blockIdx.x)) * int64_t(kTilePart));
+    put_tile(Tpart + ((mat * gridDim.x + bx)) * int64_t(kTilePart));
     return;
   }
   // epilogue: T (H x sb) and R_J^-1 in LDS, then -T R_J^-1 to the output
@@ -894,8 +912,9 @@ __global__ void __launch_bounds__(kJT) jt_bwd_diag(JunctionPlanDev P, Dims d, in
   extern __shared__ char smem_raw[];
   T *Ri = reinterpret_cast<T *>(smem_raw);
   const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
-  const int64_t fcl = blockIdx.x / nsplit, mat = blockIdx.y;
-  const int part = blockIdx.x - static_cast<int>(fcl) * nsplit;
+  const WgXM wg = xcd_wg();
+  const int64_t bx = wg.x, fcl = bx / nsplit, mat = wg.mat;
+  const int part = static_cast<int>(bx - fcl * nsplit);
   const int64_t fc = fcbase + fcl;
   const int id = P.col_chunk[fc], col = static_cast<int>(fc - P.ch_cptr[id]);
   const int s = P.ch_s[id], nr = P.ch_n[id], sb = s * b, wr = b * sb;
@@ -969,7 +988,7 @@ __global__ void __launch_bounds__(kJT) jt_bwd_diag(JunctionPlanDev P, Dims d, in
     __syncthreads();
   }
   if (nsplit > 1) {
-    T *dst = Dpart + (mat * gridDim.x + blockIdx.x) * int64_t(kDiagPart);
+    T *dst = Dpart + (mat * gridDim.x + bx) * int64_t(kDiagPart);
     for (int u = 0; u < 6; ++u) {
       const int e = t + u * kJT;
       if (e < ob) dst[e] = acc[u];
