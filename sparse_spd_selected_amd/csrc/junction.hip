@@ -274,18 +274,56 @@ __device__ inline void gather_lds(T *dst, int tot, F src) {
 template <typename T>
 __device__ inline int chol_inverse(T *S, T *X, T *tmp, int n, int b, double *logdet) {
   const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
-  for (int j = 0; j < n; ++j) {
-    const T dj = S[j * n + j];
-    if (!(dj > T(0))) return j + 1;
-    const T inv = T(1) / dj;
-    for (int i = j + 1 + ty; i < n; i += 16) {
-      const T sij = S[i * n + j] * inv;
-      for (int l = j + 1 + tx; l <= i; l += 16) S[i * n + l] -= sij * S[l * n + j];
+  if (n <= 48) {
+    // the trailing matrix in registers (n^2 <= 9 kJT entries, entry t + kJT u
+    // per thread); step j reads column j from LDS and writes back column
+    // j + 1, so LDS ends with every column as it was at its pivot step
+    constexpr int kU = 48 * 48 / kJT;
+    T r[kU];
+    int ri[kU], rl[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int e = t + kJT * u;
+      ri[u] = e < n * n ? e / n : -1;
+      rl[u] = e < n * n ? e - ri[u] * n : 0;
+      r[u] = e < n * n ? S[e] : T(0);
+    }
+    for (int j = 0; j < n; ++j) {
+      __syncthreads();
+      const T dj = S[j * n + j];
+      if (!(dj > T(0))) return j + 1;
+      const T inv = T(1) / dj;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = ri[u], l = rl[u];
+        if (l > j && i >= l) {
+          r[u] -= S[i * n + j] * inv * S[l * n + j];
+          if (l == j + 1) S[i * n + l] = r[u];
+        }
+      }
     }
     __syncthreads();
+  } else {
+    for (int j = 0; j < n; ++j) {
+      const T dj = S[j * n + j];
+      if (!(dj > T(0))) return j + 1;
+      const T inv = T(1) / dj;
+      for (int i = j + 1 + ty; i < n; i += 16) {
+        const T sij = S[i * n + j] * inv;
+        for (int l = j + 1 + tx; l <= i; l += 16) S[i * n + l] -= sij * S[l * n + j];
+      }
+      __syncthreads();
+    }
   }
   double ld = 0.0;
-  for (int j = 0; j < n; ++j) ld += log(static_cast<double>(S[j * n + j]));
+  if (n <= 48) {  // the pivots' logs in parallel, summed in column order
+    __shared__ double lg[48];
+    if (t < n) lg[t] = log(static_cast<double>(S[t * n + t]));
+    __syncthreads();
+    for (int j = 0; j < n; ++j) ld += lg[j];
+  } else {
+    for (int j = 0; j < n; ++j) ld += log(static_cast<double>(S[j * n + j]));
+  }
   for (int e = t; e < n * n; e += kJT) {
     const int i = e / n, j = e - i * n;
     if (i > j) S[e] /= sqrt(S[j * n + j]);
