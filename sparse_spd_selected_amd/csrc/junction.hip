@@ -465,7 +465,6 @@ __global__ void __launch_bounds__(kJT) jt_fwd_update_wave(JunctionPlanDev P, Dim
   constexpr int NL = CH * bb / 64;  // staged elements per lane and operand
   __shared__ __align__(16) T sa[4][CH * bb];
   __shared__ __align__(16) T sb[4][CH * bb];
-  __shared__ int32_t tab[4][2 * CH];
   __shared__ T red[4][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const WgXM wg = xcd_wg();
@@ -476,19 +475,33 @@ __global__ void __launch_bounds__(kJT) jt_fwd_update_wave(JunctionPlanDev P, Dim
   const T *Wm = W + mat * d.npanel * bb;
   const int grp = lane / bb, e = lane - grp * bb, er = e / b, ec = e - er * b;
   T acc = T(0);
-  for (int32_t q0 = f0; q0 < f1; q0 += CH) {
-    const int cnt = f1 - q0 < CH ? f1 - q0 : CH;
-    if (lane < 2 * cnt) tab[wave][lane] = P.fpair[2 * int64_t(q0) + lane];
-    f16::wave_sync();
-    T va[NL], vb[NL];
+  // Rounds of CH pairs, pipelined one round ahead: round r + 1's blocks are
+  // loaded (their pair codes read a round earlier still, lane l < 2 CH
+  // holding code l) while round r's products run.  Wavefront-scope
+  // synchronisation only, so nothing waits on the loads in flight.
+  const int nround = (f1 - f0 + CH - 1) / CH;
+  auto cnt_of = [&](int r) { const int32_t q0 = f0 + r * CH; return f1 - q0 < CH ? f1 - q0 : CH; };
+  auto codes = [&](int r) -> int32_t {
+    return r < nround && lane < 2 * cnt_of(r) ? P.fpair[2 * int64_t(f0 + r * CH) + lane] : 0;
+  };
+  T va[NL], vb[NL];
+  auto load = [&](int r, int32_t code) {
+    const int cnt = cnt_of(r);
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
       const int idx = lane + 64 * u, q = idx / bb, el = idx - q * bb;
+      const int32_t ca = __shfl(code, 2 * q < 64 ? 2 * q : 0), cb = __shfl(code, 2 * q + 1 < 64 ? 2 * q + 1 : 0);
       if (q < cnt) {
-        va[u] = Wm[int64_t(tab[wave][2 * q]) * bb + el];
-        vb[u] = Wm[int64_t(tab[wave][2 * q + 1]) * bb + el];
+        va[u] = Wm[int64_t(ca) * bb + el];
+        vb[u] = Wm[int64_t(cb) * bb + el];
       }
     }
+  };
+  int32_t code = codes(0);
+  if (nround > 0) load(0, code);
+  code = codes(1);
+  for (int r = 0; r < nround; ++r) {
+    const int cnt = cnt_of(r);
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
       const int idx = lane + 64 * u;
@@ -498,6 +511,10 @@ __global__ void __launch_bounds__(kJT) jt_fwd_update_wave(JunctionPlanDev P, Dim
       }
     }
     f16::wave_sync();
+    if (r + 1 < nround) {
+      load(r + 1, code);
+      code = codes(r + 2);
+    }
     if (grp < G)
       for (int q = grp; q < cnt; q += G) {
         const T *A = sa[wave] + q * bb + er * b, *Bq = sb[wave] + q * bb + ec * b;
