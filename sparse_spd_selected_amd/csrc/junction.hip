@@ -24,15 +24,19 @@
 // Work decomposition, each workgroup owning what it writes for one matrix:
 // per level the Schur sums (one workgroup per panel block, or one wavefront
 // per panel block for b <= 8), the dense pivots (one per chunk: R_J^-1, the
-// log det term), the scaling of the later rows (one per row), and in the
-// Takahashi pass the rows G_{w,J} (one per tile of rows) and the chunk's own
-// blocks (one per block column); on levels with few tiles or columns the
-// last two split their sums over several workgroups and add the parts in a
-// fixed order.  Sums run in a fixed order, so results are deterministic; the
+// log det term), the scaling of the later rows (one per row, or one per tile
+// of 64 / b rows for b = 4, 8, 16), and in the Takahashi pass the rows
+// G_{w,J} (one per tile of rows) and the chunk's own blocks (one per block
+// column); on levels with few tiles or columns the last two split their sums
+// over several workgroups and add the parts in a fixed order.  For b = 4, 8,
+// 16 the scaling, row and diagonal products run on the matrix cores
+// (16x16x4, one 16-row block per wavefront; s b <= 48 gives three 16-column
+// blocks).  Sums run in a fixed order, so results are deterministic; the
 // only atomic is the first-failure index.  Without G outputs only the
 // factorisation runs (the log det call).
 // Operands are staged through LDS in rounds; every thread issues a batch of
-// loads before storing them, so a round costs about one memory latency.
+// loads before storing them, so a round costs about one memory latency.  The
+// level kernels take their workgroups in XCD-contiguous ranges (xcd_wg).
 #include <hip/hip_runtime.h>
 
 #include <climits>
