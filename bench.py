@@ -4,13 +4,20 @@
 
 One step = one call of the C ABI over one batch of synthetic input already
 resident in HBM (all collect, root and distribute work of every matrix).
-Default workload: 4096 block-tridiagonal chains of 64 blocks of 16 (float64;
-the float32 run is reported alongside).  Prints ONE JSON line.
+Default workload: the largest single-GPU configuration, 64 block-tridiagonal
+chains of 16384 blocks of 32 in float64 (diagonal load 1.0).  The other
+workloads (one chain of 8 blocks of 4; 4096 chains of 64 blocks of 16 in
+float64 and float32; 256 stars of 1024 leaves of 32; the random recursive
+tree of 262144 nodes, b = 8, float64 and float32) are timed in the same run
+and reported compactly under "configs".  Prints ONE JSON line.
 
 Metric: nominal selected-inverse GFLOP/s (7 b^3 per non-root block, b^3 per
 root, never the executed count) and block-rows/s; roofline fraction of the
-dominant kernel against MI355X HBM bandwidth (8 TB/s) on compulsory bytes
-(every input block read once, every output block written once).
+call against MI355X HBM bandwidth (8 TB/s) on compulsory bytes (every input
+block read once, every output block written once).  Every workload here has
+a compulsory arithmetic intensity below the fp64 / fp32 ridge points, so the
+HBM roofline is the binding one; the fraction of the matrix-core peak is
+reported beside it.
 
 ``--op logdet`` times the log-det-only call (the collect pass without a
 stored factor); ``--op solve`` / ``--op sample`` time x = A^{-1} y and
@@ -33,6 +40,12 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+DEFAULT_WORKLOAD = "chain_b32_long"
+# the other forward workloads, timed compactly in the default run
+OTHER_CONFIGS = (("chain_b4_single", "f64"), ("chain_b16_batched", "f64"),
+                 ("chain_b16_batched", "f32"), ("star_b32", "f64"),
+                 ("tree_b8_random", "f64"), ("tree_b8_random", "f32"))
 
 HBM_PEAK_GBS = 8000.0
 FP64_PEAK_TFLOPS = 78.6
@@ -440,42 +453,83 @@ def cpu_baseline(kind, cfg, op="selinv"):
         return {"value": round(nominal_flops(kind, sub, op) / t / 1e9, 3), "unit": "GFLOP/s",
                 "cores": cores, "kind": "oracle", "sample": sample, "seconds": round(t, 3),
                 "block_rows_per_s": round(block_rows(kind, sub) / t, 1)}
-    if kind == "chain":
-        Bs = cfg["B"] if cfg["B"] * cfg["L"] * cfg["b"] ** 3 <= 4e9 else max(1, int(4e9 // (cfg["L"] * cfg["b"] ** 3)))
-        d, l = spdgen.chain(Bs, cfg["L"], cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
-        # the whole batch takes well under a second here: repeat it (up to ~3 s)
-        # and report the mean time of one pass
+    def timed(fn, min_s=0.0, max_reps=30):
         reps, t0 = 0, time.perf_counter()
         while True:
-            oracle.chain(d, l, lib=lib)
+            fn()
             reps += 1
-            if time.perf_counter() - t0 >= 3.0 or reps >= 30:
+            if time.perf_counter() - t0 >= min_s or reps >= max_reps:
                 break
-        t = (time.perf_counter() - t0) / reps
-        sub = dict(cfg, B=Bs)
-        sample = "%d of %d chains (L=%d, b=%d), float64, mean of %d passes" % (
-            Bs, cfg["B"], cfg["L"], cfg["b"], reps)
+        return (time.perf_counter() - t0) / reps, reps
+
+    nthr = int(lib.oracle_num_threads())
+    if kind == "chain":
+        per = cfg["L"] * cfg["b"] ** 3
+        # all threads: the whole batch when it is small (repeated for ~3 s),
+        # else one chain per thread
+        Bs = cfg["B"] if cfg["B"] * per <= 4e9 else max(1, min(cfg["B"], nthr))
+        B1 = max(1, min(cfg["B"], int(5e8 // per)))  # one thread: ~1-4 s of work
+        d, l = spdgen.chain(max(Bs, B1), cfg["L"], cfg["b"], seed=cfg["seed"],
+                            diag_load=cfg["diag_load"])
+        t, reps = timed(lambda: oracle.chain(d[:Bs], l[:Bs], lib=lib), 3.0)
+        old = lib.oracle_set_num_threads(1)
+        try:
+            t1, _ = timed(lambda: oracle.chain(d[:B1], l[:B1], lib=lib))
+        finally:
+            lib.oracle_set_num_threads(old)
+        sub, sub1 = dict(cfg, B=Bs), dict(cfg, B=B1)
+        what = "chains (L=%d, b=%d), float64" % (cfg["L"], cfg["b"])
+        sample = "%d of %d %s, mean of %d passes" % (Bs, cfg["B"], what, reps)
+        sample1 = "%d of %d %s" % (B1, cfg["B"], what)
+        cores = min(nthr, Bs)
     elif kind == "star":
-        Bs = min(cfg["B"], 16)
+        Bs = min(cfg["B"], nthr)
         arrs = spdgen.star(Bs, cfg["K"], cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
-        t0 = time.perf_counter()
-        oracle.star(*arrs, lib=lib)
-        t = time.perf_counter() - t0
-        sub = dict(cfg, B=Bs)
-        sample = "%d of %d stars (K=%d, b=%d), float64" % (Bs, cfg["B"], cfg["K"], cfg["b"])
+        t, _ = timed(lambda: oracle.star(*arrs, lib=lib))
+        old = lib.oracle_set_num_threads(1)
+        try:
+            t1, _ = timed(lambda: oracle.star(*(a[:1] for a in arrs), lib=lib))
+        finally:
+            lib.oracle_set_num_threads(old)
+        sub, sub1 = dict(cfg, B=Bs), dict(cfg, B=1)
+        what = "stars (K=%d, b=%d), float64" % (cfg["K"], cfg["b"])
+        sample = "%d of %d %s" % (Bs, cfg["B"], what)
+        sample1 = "1 of %d %s" % (cfg["B"], what)
+        cores = Bs
     else:
         parent = spdgen.random_recursive_tree(cfg["n"], cfg["seed"])
         d, e = spdgen.tree(parent, cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
-        t0 = time.perf_counter()
-        oracle.tree(parent, d, e, lib=lib)
-        t = time.perf_counter() - t0
-        sub = cfg
-        sample = "the whole tree (n=%d, b=%d), float64, single thread" % (cfg["n"], cfg["b"])
-    gflops = nominal_flops(kind, sub, op) / t / 1e9
-    cores = 1 if kind == "tree" else int(lib.oracle_num_threads())
-    return {"value": round(gflops, 3), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": sample, "seconds": round(t, 3),
-            "block_rows_per_s": round(block_rows(kind, sub) / t, 1)}
+        t, _ = timed(lambda: oracle.tree(parent, d, e, lib=lib))
+        t1, sub, sub1 = t, cfg, cfg
+        sample = sample1 = "the whole tree (n=%d, b=%d), float64" % (cfg["n"], cfg["b"])
+        cores = 1  # one tree: the oracle's tree recurrence is sequential
+    out = {"value": round(nominal_flops(kind, sub, op) / t / 1e9, 3), "unit": "GFLOP/s",
+           "cores": cores, "kind": "oracle", "sample": sample, "seconds": round(t, 3),
+           "block_rows_per_s": round(block_rows(kind, sub) / t, 1),
+           "one_thread": {"value": round(nominal_flops(kind, sub1, op) / t1 / 1e9, 3),
+                          "unit": "GFLOP/s", "cores": 1, "sample": sample1,
+                          "seconds": round(t1, 3),
+                          "block_rows_per_s": round(block_rows(kind, sub1) / t1, 1)}}
+    out.update(host_info())
+    return out
+
+
+def host_info():
+    """CPU model, logical CPU count and the CPUs this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": usable, "logical_cpus": os.cpu_count()}
 
 
 def copy_probe(mib, steps):
@@ -531,12 +585,37 @@ def peak_probe():
     print(json.dumps(out), flush=True)
 
 
+def compact(workload, dtname, steps, warmup):
+    """Event-timed forward calls of another workload: median and min call
+    time, nominal GFLOP/s, block-rows/s and the HBM roofline fraction on
+    compulsory bytes (median call)."""
+    import spdgen
+    import torch
+    cfg = dict(spdgen.WORKLOADS[workload])
+    kind = cfg.pop("kind")
+    cfg.pop("dtypes")
+    w = 8 if dtname == "f64" else 4
+    res = run_gpu(kind, cfg, dtname, max(steps, 20), max(warmup, 3))
+    torch.cuda.empty_cache()
+    ev = sorted(res["ev_ms"])
+    med = ev[len(ev) // 2]
+    F = nominal_flops(kind, cfg)
+    nbytes = compulsory_bytes(kind, cfg, w)
+    peak_t = FP64_PEAK_TFLOPS if dtname == "f64" else FP32_PEAK_TFLOPS
+    return {"ms_median": round(med, 4), "ms_min": round(ev[0], 4),
+            "gflops": round(F / (med * 1e-3) / 1e9, 3),
+            "block_rows_per_s": round(block_rows(kind, cfg) / (med * 1e-3), 1),
+            "hbm_frac": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "flop_frac": round(F / (med * 1e-3) / 1e12 / peak_t, 4),
+            "algorithmic_bytes": nbytes, "nominal_flops": F}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="chain_b16_batched")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--op", default="selinv",
                     choices=("selinv", "vjp", "logdet", "solve", "sample"),
                     help="selinv: the selected inverse; vjp: its reverse mode; logdet, solve, "
@@ -547,6 +626,8 @@ def main():
                     help="tree workloads: replay the schedule as one recorded HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-second-dtype", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the compact timings of the other workloads")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -612,6 +693,7 @@ def main():
         "flop_frac_of_peak": round(gflops / (peak_t * 1e3), 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "scope": "one call (every launch of the step), HIP events on its stream",
                      "traffic": measured_traffic(tkey, dtname),
                      "algorithmic_bytes": nbytes, "kernel_source_hash": kernel_source_hash()},
     }
@@ -635,6 +717,11 @@ def main():
                       "block_rows_per_s": round(block_rows(kind, cfg) / (ms2 * 1e-3), 1),
                       "hbm_frac": round(compulsory_bytes(kind, cfg, w2, op) / (ev2 * 1e-3) / 1e9
                                         / HBM_PEAK_GBS, 4)}
+    if (op == "selinv" and args.workload == DEFAULT_WORKLOAD and args.dtype is None
+            and not args.no_configs):
+        out["configs"] = {}
+        for wl, dn in OTHER_CONFIGS:
+            out["configs"]["%s/%s" % (wl, dn)] = compact(wl, dn, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = {"selinv": cpu_baseline, "vjp": cpu_baseline_vjp,
                                "logdet": cpu_baseline, "solve": cpu_baseline_apply,

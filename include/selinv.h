@@ -41,6 +41,14 @@
  *   entry point below.  This follows the "not positive definite -> error"
  *   convention of the sparsax page (Features list); the Python binding's
  *   check=True turns a nonzero info into an exception.
+ * - info = SELINV_INFO_WAIT_TIMEOUT (-1) is not a numerical failure: the
+ *   single-launch tree schedules (selinv_tree_*, selinv_nonsym_tree_*, the
+ *   tree reverse mode and solve) bound every wait of one workgroup on
+ *   another; a wait that expires reports -1, NaN outputs and a NaN log det.
+ *   It can happen when other work keeps the GPU's workgroup slots busy for
+ *   longer than the bound (selinv_set_wait_limit); calling again on an idle
+ *   stream, or with a larger bound, is the remedy.  selinv_strerror(
+ *   SELINV_ERR_WAIT_TIMEOUT) gives its text.
  * - Return value: a synchronous status (SELINV_OK or an error below) about
  *   the arguments and the launch, not about the numerics.
  * - Supported block sizes: 1 <= b <= 32.  Distinct calls on distinct streams
@@ -67,6 +75,10 @@ extern "C" {
 #define SELINV_ERR_BAD_TREE 2    /* parent array is not one rooted tree                        */
 #define SELINV_ERR_HIP 3         /* HIP runtime or launch error                                 */
 #define SELINV_ERR_BAD_PATTERN 4 /* junction pattern or elimination order is invalid            */
+#define SELINV_ERR_WAIT_TIMEOUT 5 /* a bounded dataflow wait expired (reported as info = -1)    */
+
+/* info value of a call whose bounded dataflow wait expired */
+#define SELINV_INFO_WAIT_TIMEOUT (-1)
 
 #define SELINV_MAX_B 32
 

@@ -56,6 +56,7 @@ def load(path: str | None = None):
     lib.oracle_tree.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_tree_depths.argtypes = [i64, vp, vp]
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_set_num_threads.argtypes = [i32]
     lib.oracle_tree_vjp.argtypes = [i64, i32, vp, vp, vp, vp, vp, ctypes.c_double, vp, vp]
     lib.oracle_chain_vjp.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_tree_apply.argtypes = [i64, i32, vp, vp, vp, i64, vp, vp, i32]
@@ -65,7 +66,7 @@ def load(path: str | None = None):
     lib.oracle_eliminate.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp, i64]
     lib.oracle_junction.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     for f in (lib.oracle_chain, lib.oracle_star, lib.oracle_tree, lib.oracle_tree_depths,
-              lib.oracle_num_threads, lib.oracle_tree_vjp, lib.oracle_chain_vjp,
+              lib.oracle_num_threads, lib.oracle_set_num_threads, lib.oracle_tree_vjp, lib.oracle_chain_vjp,
               lib.oracle_tree_apply, lib.oracle_chain_apply, lib.oracle_bidiag,
               lib.oracle_nonsym_tree, lib.oracle_eliminate, lib.oracle_junction):
         f.restype = ctypes.c_int

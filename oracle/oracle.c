@@ -1121,3 +1121,16 @@ ORACLE_API int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Sets the number of OpenMP threads of the batch loops started from the
+ * calling thread (n >= 1); returns the previous number. */
+ORACLE_API int oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  const int old = omp_get_max_threads();
+  if (n >= 1) omp_set_num_threads(n);
+  return old;
+#else
+  (void)n;
+  return 1;
+#endif
+}

@@ -13,7 +13,8 @@ gabp-sparse-inv 0.3.2 page: ``lower[i] = A_{i+1,i}``, ``coupling[j] =
 A_{j,0}``, ``edge[v] = A_{parent(v),v}``; leading batch dimensions are allowed
 for the chain and star.  ``check=True`` synchronises and raises
 ``NotPositiveDefinite`` if any Schur pivot failed (the "not positive definite
--> error" convention of the sparsax page), and validates the inputs.
+-> error" convention of the sparsax page), ``WaitTimeout`` if a bounded wait of
+the single-launch tree schedule expired (info = -1), and validates the inputs.
 """
 from __future__ import annotations
 
@@ -27,7 +28,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libselinv.so")
 
-OK, INVALID_ARG, BAD_TREE, HIP_ERROR = 0, 1, 2, 3
+OK, INVALID_ARG, BAD_TREE, HIP_ERROR, BAD_PATTERN, WAIT_TIMEOUT = 0, 1, 2, 3, 4, 5
+INFO_WAIT_TIMEOUT = -1
 MAX_B = 32
 
 _lib = None
@@ -38,7 +40,14 @@ class SelinvError(RuntimeError):
 
 
 class NotPositiveDefinite(SelinvError):
-    """A Schur pivot was not positive definite (info != 0)."""
+    """A Schur pivot was not positive definite (info > 0)."""
+
+
+class WaitTimeout(SelinvError):
+    """A bounded wait between workgroups of the single-launch tree schedule
+    expired (info = -1): the outputs are NaN.  Not a property of the matrix;
+    it can happen when other work holds the GPU for longer than the bound
+    (set_wait_limit).  Calling again is the remedy."""
 
 
 def build():
@@ -229,6 +238,11 @@ def _validate_symmetric(name, t):
 
 
 def _raise_info(info: torch.Tensor, what: str):
+    timed_out = (info == INFO_WAIT_TIMEOUT).nonzero()
+    if timed_out.numel():
+        idx = tuple(int(i) for i in timed_out[0])
+        raise WaitTimeout("%s: %s (matrix %s)" % (
+            what, lib().selinv_strerror(WAIT_TIMEOUT).decode(), idx))
     bad = info.nonzero()
     if bad.numel():
         idx = tuple(int(i) for i in bad[0])

@@ -46,7 +46,26 @@ def test_library_exports_every_declared_symbol(lib):
 def test_strerror_and_version(lib):
     assert lib.selinv_strerror(0) == b"ok"
     assert b"tree" in lib.selinv_strerror(2)
+    assert b"wait" in lib.selinv_strerror(ssa.WAIT_TIMEOUT)
+    assert lib.selinv_strerror(99) == b"unknown status"
     assert lib.selinv_version() >= 100
+
+
+def test_header_status_codes_match_binding():
+    src = open(os.path.join(ROOT, "include", "selinv.h")).read()
+    codes = dict((k, int(v)) for k, v in re.findall(r"#define (SELINV_[A-Z_]+) \(?(-?\d+)\)?", src))
+    assert codes["SELINV_ERR_WAIT_TIMEOUT"] == ssa.WAIT_TIMEOUT
+    assert codes["SELINV_INFO_WAIT_TIMEOUT"] == ssa.INFO_WAIT_TIMEOUT
+    assert codes["SELINV_ERR_BAD_PATTERN"] == ssa.BAD_PATTERN
+
+
+def test_raise_info_distinguishes_timeout_from_not_pd(lib):
+    import torch
+    with pytest.raises(ssa.WaitTimeout):
+        ssa._raise_info(torch.tensor([0, -1, 3], dtype=torch.int32), "tree")
+    with pytest.raises(ssa.NotPositiveDefinite):
+        ssa._raise_info(torch.tensor([0, 0, 3], dtype=torch.int32), "chain")
+    ssa._raise_info(torch.zeros(4, dtype=torch.int32), "chain")
 
 
 def test_workspace_sizes(lib):

@@ -181,6 +181,9 @@ def test_nonsym_tree_wait_limit_reports_timeout(ssa):
         _, _, _, info = ssa.nonsym_tree(p, _to(d, torch.float64), _to(u, torch.float64),
                                         _to(w, torch.float64), return_info=True)
         torch.cuda.synchronize()
+        with pytest.raises(ssa.WaitTimeout):
+            ssa.nonsym_tree(p, _to(d, torch.float64), _to(u, torch.float64),
+                            _to(w, torch.float64), check=True)
     finally:
         ssa.set_wait_limit(old)
     assert int(info) == -1

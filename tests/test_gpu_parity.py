@@ -95,26 +95,29 @@ def test_chain_workload_b16_batched(ssa, dt):
     run_chain(ssa, 4096, 64, 16, DT[dt], seed=0)
 
 
+@pytest.mark.timeout(900)
 def test_chain_workload_b32_long(ssa):
-    """64 chains of 16384 blocks of 32 (diagonal load 1.0), float64.  The
-    oracle checks chains {0, 1, 31, 63} in full (each regenerated on its own);
-    every chain gets the residual check on the GPU."""
+    """64 chains of 16384 blocks of 32 (diagonal load 1.0), float64.  Every
+    chain is compared with the oracle (in batches of 16 chains), and every
+    chain gets the block-diagonal residual check on the GPU."""
     B, L, b = 64, 16384, 32
     say("chain long: generating")
     d, l = spdgen.chain(B, L, b, seed=0, diag_load=1.0)
     D, C = _to(d, torch.float64), _to(l, torch.float64)
-    del d, l
     say("chain long: running")
     Gd, Gl, ld, info = ssa.chain(D, C, return_info=True)
     torch.cuda.synchronize()
     assert int(info.abs().sum()) == 0
-    for m in (0, 1, 31, 63):
-        dm, lm = spdgen.chain(1, L, b, seed=0, diag_load=1.0, m0=m)
-        Od, Ol, Old, _ = oracle.chain(dm, lm)
-        _cmp("G_diag[%d]" % m, Gd[m:m + 1], Od, torch.float64)
-        _cmp("G_lower[%d]" % m, Gl[m:m + 1], Ol, torch.float64)
-        _cmp_ld(ld[m:m + 1], Old, L, torch.float64)
-        say("chain long: chain %d ok" % m)
+    for m0 in range(0, B, 16):
+        sl = slice(m0, m0 + 16)
+        Od, Ol, Old, Oinfo = oracle.chain(d[sl], l[sl])
+        assert not Oinfo.any()
+        e = max(_cmp("G_diag[%d:]" % m0, Gd[sl], Od, torch.float64),
+                _cmp("G_lower[%d:]" % m0, Gl[sl], Ol, torch.float64))
+        _cmp_ld(ld[sl], Old, L, torch.float64)
+        say("chain long: chains %d..%d ok, worst rel err %.2e" % (m0, m0 + 15, e))
+        del Od, Ol
+    del d, l
     # block-diagonal residual on all chains: D_i G_ii + C_{i-1} G_{i-1,i} + C_i^T G_{i+1,i} = I
     eye = torch.eye(b, dtype=torch.float64, device=DEV)
     worst = 0.0
@@ -216,9 +219,10 @@ def test_star_small(ssa, B, K, b, dt):
     run_star(ssa, B, K, b, DT[dt], seed=K + b)
 
 
+@pytest.mark.timeout(600)
 def test_star_workload_b32(ssa):
-    """256 stars of 1024 leaves of 32, float64; oracle on matrices 0, 100, 255."""
-    run_star(ssa, 256, 1024, 32, torch.float64, seed=0, mats=(0, 100, 255))
+    """256 stars of 1024 leaves of 32, float64; the oracle checks every star."""
+    run_star(ssa, 256, 1024, 32, torch.float64, seed=0)
 
 
 def test_star_not_pd_info(ssa):
@@ -289,9 +293,11 @@ def test_tree_wait_limit_reports_timeout(ssa):
         ssa.set_wait_limit(0)
         _, _, ld, info = ssa.tree(p, D, E, return_info=True)
         torch.cuda.synchronize()
+        with pytest.raises(ssa.WaitTimeout):
+            ssa.tree(p, D, E, check=True)
     finally:
         ssa.set_wait_limit(old)
-    assert int(info) == -1 and np.isnan(float(ld))
+    assert int(info) == ssa.INFO_WAIT_TIMEOUT and np.isnan(float(ld))
     run_tree(ssa, p, 4, torch.float64, seed=3)
 
 

@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import oracle
+import par
 import spdgen
 
 pytestmark = pytest.mark.gpu
@@ -95,8 +96,8 @@ def test_chain_siblings(ssa, B, L, b, k, dt):
 
 @pytest.mark.parametrize("dt", ["f64", "f32"])
 def test_chain_siblings_workload_b16(ssa, dt):
-    """4096 chains of 64 blocks of 16: log det of all chains, solve and sample
-    with k = 4 checked on 40 chains spread over the batch."""
+    """4096 chains of 64 blocks of 16: log det, solve and sample with k = 4,
+    every chain checked."""
     dt = DT[dt]
     B, L, b, k = 4096, 64, 16, 4
     d, l = spdgen.chain(B, L, b, seed=0)
@@ -106,14 +107,13 @@ def test_chain_siblings_workload_b16(ssa, dt):
     x = f.solve(_to(y, dt))
     s = f.sample(z=_to(z, dt))
     torch.cuda.synchronize()
-    sel = sorted(set([0, 4095] + list(range(3, 4096, 103))))
-    du, lu = _as_used(d[sel], dt), _as_used(l[sel], dt)
-    _, _, Old, _ = oracle.chain(_as_used(d, dt), _as_used(l, dt))
+    du, lu = _as_used(d, dt), _as_used(l, dt)
+    _, _, Old, _ = oracle.chain(du, lu)
     _cmp_ld(f.logdet, Old, L, dt)
-    Ox, _ = oracle.chain_apply(du, lu, _as_used(y[sel], dt), "solve")
-    Os, _ = oracle.chain_apply(du, lu, _as_used(z[sel], dt), "sample")
-    say("  solve %.2e sample %.2e" % (_cmp_vec("solve", x[sel], Ox, dt),
-                                       _cmp_vec("sample", s[sel], Os, dt)))
+    Ox, _ = oracle.chain_apply(du, lu, _as_used(y, dt), "solve")
+    Os, _ = oracle.chain_apply(du, lu, _as_used(z, dt), "sample")
+    say("  solve %.2e sample %.2e" % (_cmp_vec("solve", x, Ox, dt),
+                                       _cmp_vec("sample", s, Os, dt)))
 
 
 @pytest.mark.parametrize("b", [4, 16])
@@ -167,27 +167,31 @@ def test_star_siblings(ssa, B, K, b, k, dt):
                                        _cmp_vec("sample", gs, rs, dt)))
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("dt", ["f64", "f32"])
 def test_star_siblings_workload_b32(ssa, dt):
-    """256 stars of 1024 leaves of 32, k = 1: solve and sample checked on three
-    matrices spread over the batch."""
+    """256 stars of 1024 leaves of 32, k = 1: log det, solve and sample
+    checked on every star (host threads over chunks of the batch)."""
     dt = DT[dt]
     B, K, b, k = 256, 1024, 32, 1
     c, lv, cp = spdgen.star(B, K, b, seed=0)
     yc = spdgen.cotangent((B, b, k), seed=0, k=0)
     yl = spdgen.cotangent((B, K, b, k), seed=0, k=1)
     f = ssa.star_factor(_to(c, dt), _to(lv, dt), _to(cp, dt))
+    ld_only = ssa.star_logdet(_to(c, dt), _to(lv, dt), _to(cp, dt))
     xc, xl = f.solve(_to(yc, dt), _to(yl, dt))
     sc, sl = f.sample(z_center=_to(yc, dt), z_leaves=_to(yl, dt))
     torch.cuda.synchronize()
-    sel = [0, 101, 255]
-    cu, lu, pu = _as_used(c[sel], dt), _as_used(lv[sel], dt), _as_used(cp[sel], dt)
-    ycu, ylu = _as_used(yc[sel], dt), _as_used(yl[sel], dt)
-    n = len(sel)
+    cu, lu, pu = _as_used(c, dt), _as_used(lv, dt), _as_used(cp, dt)
+    ycu, ylu = _as_used(yc, dt), _as_used(yl, dt)
+    *_, Old, Oinfo = oracle.star(cu, lu, pu)
+    assert not Oinfo.any()
+    _cmp_ld(ld_only, Old, K + 1, dt)
+    _cmp_ld(f.logdet, Old, K + 1, dt)
     for mode, (gc, gl) in (("solve", (xc, xl)), ("sample", (sc, sl))):
-        Oc, Ol = oracle.star_apply(cu, lu, pu, ycu, ylu, mode)
-        g = torch.cat([gc[sel].reshape(n, -1), gl[sel].reshape(n, -1)], 1)
-        r = np.concatenate([Oc.reshape(n, -1), Ol.reshape(n, -1)], 1)
+        Oc, Ol = par.chunked(lambda *a: oracle.star_apply(*a, mode), B, [cu, lu, pu, ycu, ylu])
+        g = torch.cat([gc.reshape(B, -1), gl.reshape(B, -1)], 1)
+        r = np.concatenate([Oc.reshape(B, -1), Ol.reshape(B, -1)], 1)
         say("  %s %.2e" % (mode, _cmp_vec(mode, g, r, dt)))
 
 
