@@ -161,6 +161,22 @@ SELINV_API int selinv_tree_plan_create(const int32_t *parent_host, int64_t n, in
 SELINV_API void selinv_tree_plan_destroy(selinv_tree_plan *plan);
 /* number of depth levels (tree height + 1) of a plan, or -1 for NULL */
 SELINV_API int32_t selinv_tree_plan_levels(const selinv_tree_plan *plan);
+
+/* The level-set schedule selinv_tree_plan_create builds, computed on the host
+ * alone (no device work), for inspection and tests.  Nodes get breadth-first
+ * positions p: node_at[p] is the node at position p, so every depth level is
+ * the contiguous range [level_off[d], level_off[d + 1]) and the children of
+ * the node at p are the contiguous positions [child_beg[p], child_end[p]) in
+ * increasing node index; parent_pos[p] is the parent's position (-1 at the
+ * root); fail_rank[p] is the node's rank in the oracle's elimination order
+ * (depth descending, then node index ascending), used to name the first
+ * failing pivot.  Every output is caller-owned host memory and may be NULL:
+ * n int32 each, level_off at most n + 1 int64 (levels + 1 are written),
+ * *levels = tree height + 1.  Returns SELINV_OK, SELINV_ERR_INVALID_ARG
+ * (NULL parent, n < 1) or SELINV_ERR_BAD_TREE (as selinv_tree_plan_create). */
+SELINV_API int selinv_tree_schedule(const int32_t *parent_host, int64_t n, int32_t *node_at,
+                                    int32_t *parent_pos, int32_t *child_beg, int32_t *child_end,
+                                    int32_t *fail_rank, int64_t *level_off, int32_t *levels);
 SELINV_API size_t selinv_tree_workspace_bytes(const selinv_tree_plan *plan);
 SELINV_API int selinv_tree_f64(const selinv_tree_plan *plan, const double *diag, const double *edge,
                     double *G_diag, double *G_edge, double *logdet, int32_t *info,

@@ -1032,7 +1032,7 @@ ORACLE_API int oracle_junction(int64_t B, int64_t n, int b, const int32_t *order
     double *T2 = (double *)malloc(sizeof(double) * bb);
     double *Gd = G_diag + mat * n * bb, *Go = G_off + mat * nnz * bb;
     memcpy(Cd, diag + mat * n * bb, sizeof(double) * (size_t)(n * bb));
-    memcpy(Co, Aoff + mat * nnz * bb, sizeof(double) * (size_t)(nnz * bb));
+    if (nnz) memcpy(Co, Aoff + mat * nnz * bb, sizeof(double) * (size_t)(nnz * bb));
     int32_t fail = 0;
     double ld = 0.0;
     for (int64_t s = 0; s < n; ++s) {

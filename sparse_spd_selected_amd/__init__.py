@@ -68,6 +68,8 @@ def lib():
         raise ImportError("libselinv.so is not built (run sparse_spd_selected_amd.build())")
     L = ctypes.CDLL(LIB_PATH)
     i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    L.selinv_tree_schedule.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp]
+    L.selinv_tree_schedule.restype = ctypes.c_int
     L.selinv_strerror.argtypes = [ctypes.c_int]
     L.selinv_strerror.restype = ctypes.c_char_p
     L.selinv_version.restype = ctypes.c_int
@@ -248,6 +250,27 @@ def _raise_info(info: torch.Tensor, what: str):
         idx = tuple(int(i) for i in bad[0])
         raise NotPositiveDefinite("%s: Schur pivot not positive definite (matrix %s, info=%d)"
                                   % (what, idx, int(info[idx])))
+
+
+def tree_schedule(parent):
+    """The breadth-first level-set schedule of a parent array, computed on the
+    host by the library (selinv_tree_schedule): a dict of numpy arrays
+    node_at, parent_pos, child_beg, child_end, fail_rank (per position) and
+    level_off (levels + 1)."""
+    import numpy as np
+    parent = np.ascontiguousarray(np.asarray(parent), dtype=np.int32)
+    n = parent.shape[0]
+    out = {k: np.empty(n, np.int32) for k in ("node_at", "parent_pos", "child_beg", "child_end",
+                                               "fail_rank")}
+    level_off = np.empty(n + 1, np.int64)
+    levels = ctypes.c_int32(0)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    rc = lib().selinv_tree_schedule(p(parent), n, p(out["node_at"]), p(out["parent_pos"]),
+                                    p(out["child_beg"]), p(out["child_end"]),
+                                    p(out["fail_rank"]), p(level_off), ctypes.byref(levels))
+    _status(rc, "selinv_tree_schedule")
+    out["level_off"] = level_off[:levels.value + 1].copy()
+    return out
 
 
 # ------------------------------------------------------------------ chain

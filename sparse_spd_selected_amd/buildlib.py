@@ -45,10 +45,10 @@ HIP_FLAGS = ["-x", "hip", "--offload-arch=" + ARCH,
              "-munsafe-fp-atomics"]
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, build_dir: str = BUILD_DIR, host_flags=()) -> str:
     path = os.path.join(CSRC, src)
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON_FLAGS
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + COMMON_FLAGS + list(host_flags)
     if src.endswith(".hip"):
         cmd += HIP_FLAGS
     else:
@@ -60,19 +60,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD_DIR,
+          host_flags=()) -> str:
+    """Compile every source and link `out`.  `host_flags` go to the host side
+    of every compile and to the link (the tests use it for a host-sanitizer
+    build of the library in its own build_dir)."""
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+        objs = list(ex.map(lambda src: _compile(src, build_dir, host_flags), SOURCES))
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH] + list(host_flags) + \
+        ["-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s" % (r.stdout, r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -50,19 +50,21 @@ int validate(const int32_t *parent, int64_t n, std::vector<int32_t> &depth, int6
   return SELINV_OK;
 }
 
-}  // namespace
+// The host-side schedule of one parent array (no device work).
+struct Schedule {
+  int64_t root = -1;
+  int32_t levels = 0, max_children = 0;
+  std::vector<int64_t> level_off;  // levels + 1
+  std::vector<int32_t> node_at, parent_pos, child_beg, child_end, fail_rank, rank_node,
+      parent_node;
+};
 
-extern "C" int selinv_tree_plan_create(const int32_t *parent_host, int64_t n, int32_t b,
-                                       int dtype_bytes, void *stream, selinv_tree_plan **out) {
-  if (!out) return SELINV_ERR_INVALID_ARG;
-  *out = nullptr;
-  if (!parent_host || n < 1 || n > (int64_t(1) << 30) || b < 1 || b > SELINV_MAX_B ||
-      (dtype_bytes != 4 && dtype_bytes != 8))
-    return SELINV_ERR_INVALID_ARG;
+int build_schedule(const int32_t *parent_host, int64_t n, Schedule &sc) {
   std::vector<int32_t> depth;
   int64_t root;
   int rc = validate(parent_host, n, depth, root);
   if (rc != SELINV_OK) return rc;
+  sc.root = root;
 
   // children lists, increasing index (counting sort by parent)
   std::vector<int64_t> cstart(n + 1, 0);
@@ -76,22 +78,26 @@ extern "C" int selinv_tree_plan_create(const int32_t *parent_host, int64_t n, in
       if (parent_host[v] >= 0) clist[fillp[parent_host[v]]++] = static_cast<int32_t>(v);
   }
   // breadth-first order
-  std::vector<int32_t> node_at(n), pos(n), parent_pos(n), child_beg(n), child_end(n);
+  std::vector<int32_t> pos(n);
+  sc.node_at.assign(n, 0);
+  sc.parent_pos.assign(n, 0);
+  sc.child_beg.assign(n, 0);
+  sc.child_end.assign(n, 0);
   int64_t head = 0, tail = 0;
-  node_at[tail++] = static_cast<int32_t>(root);
-  int32_t max_children = 0;
+  sc.node_at[tail++] = static_cast<int32_t>(root);
+  sc.max_children = 0;
   while (head < tail) {
-    const int32_t v = node_at[head];
+    const int32_t v = sc.node_at[head];
     pos[v] = static_cast<int32_t>(head);
-    child_beg[head] = static_cast<int32_t>(tail);
-    for (int64_t k = cstart[v]; k < cstart[v + 1]; ++k) node_at[tail++] = clist[k];
-    child_end[head] = static_cast<int32_t>(tail);
-    max_children = std::max<int32_t>(max_children, child_end[head] - child_beg[head]);
+    sc.child_beg[head] = static_cast<int32_t>(tail);
+    for (int64_t k = cstart[v]; k < cstart[v + 1]; ++k) sc.node_at[tail++] = clist[k];
+    sc.child_end[head] = static_cast<int32_t>(tail);
+    sc.max_children = std::max<int32_t>(sc.max_children, sc.child_end[head] - sc.child_beg[head]);
     ++head;
   }
   for (int64_t p = 0; p < n; ++p) {
-    const int32_t par = parent_host[node_at[p]];
-    parent_pos[p] = par < 0 ? -1 : pos[par];
+    const int32_t par = parent_host[sc.node_at[p]];
+    sc.parent_pos[p] = par < 0 ? -1 : pos[par];
   }
   const int32_t H = *std::max_element(depth.begin(), depth.end());
   std::vector<int64_t> level_count(H + 1, 0);
@@ -105,20 +111,65 @@ extern "C" int selinv_tree_plan_create(const int32_t *parent_host, int64_t n, in
       acc += level_count[d];
     }
   }
-  std::vector<int32_t> rank_of(n), rank_node(n);
+  std::vector<int32_t> rank_of(n);
+  sc.rank_node.assign(n, 0);
   {
     std::vector<int64_t> next(rank_start.begin(), rank_start.end());
     for (int64_t v = 0; v < n; ++v) {  // increasing index within each depth
       const int64_t r = next[depth[v]]++;
       rank_of[v] = static_cast<int32_t>(r);
-      rank_node[r] = static_cast<int32_t>(v);
+      sc.rank_node[r] = static_cast<int32_t>(v);
     }
   }
-  std::vector<int32_t> fail_rank(n), parent_node(n);
+  sc.fail_rank.assign(n, 0);
+  sc.parent_node.assign(n, 0);
   for (int64_t p = 0; p < n; ++p) {
-    fail_rank[p] = rank_of[node_at[p]];
-    parent_node[p] = parent_host[node_at[p]];
+    sc.fail_rank[p] = rank_of[sc.node_at[p]];
+    sc.parent_node[p] = parent_host[sc.node_at[p]];
   }
+  sc.levels = H + 1;
+  sc.level_off.assign(H + 2, 0);
+  for (int32_t d = 0; d <= H; ++d) sc.level_off[d + 1] = sc.level_off[d] + level_count[d];
+  return SELINV_OK;
+}
+
+}  // namespace
+
+extern "C" int selinv_tree_schedule(const int32_t *parent_host, int64_t n, int32_t *node_at,
+                                    int32_t *parent_pos, int32_t *child_beg, int32_t *child_end,
+                                    int32_t *fail_rank, int64_t *level_off, int32_t *levels) {
+  if (!parent_host || n < 1 || n > (int64_t(1) << 30)) return SELINV_ERR_INVALID_ARG;
+  Schedule sc;
+  const int rc = build_schedule(parent_host, n, sc);
+  if (rc != SELINV_OK) return rc;
+  const size_t nb = static_cast<size_t>(n) * sizeof(int32_t);
+  if (node_at) std::memcpy(node_at, sc.node_at.data(), nb);
+  if (parent_pos) std::memcpy(parent_pos, sc.parent_pos.data(), nb);
+  if (child_beg) std::memcpy(child_beg, sc.child_beg.data(), nb);
+  if (child_end) std::memcpy(child_end, sc.child_end.data(), nb);
+  if (fail_rank) std::memcpy(fail_rank, sc.fail_rank.data(), nb);
+  if (level_off)
+    std::memcpy(level_off, sc.level_off.data(), sc.level_off.size() * sizeof(int64_t));
+  if (levels) *levels = sc.levels;
+  return SELINV_OK;
+}
+
+extern "C" int selinv_tree_plan_create(const int32_t *parent_host, int64_t n, int32_t b,
+                                       int dtype_bytes, void *stream, selinv_tree_plan **out) {
+  if (!out) return SELINV_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!parent_host || n < 1 || n > (int64_t(1) << 30) || b < 1 || b > SELINV_MAX_B ||
+      (dtype_bytes != 4 && dtype_bytes != 8))
+    return SELINV_ERR_INVALID_ARG;
+  Schedule sc;
+  int rc = build_schedule(parent_host, n, sc);
+  if (rc != SELINV_OK) return rc;
+  const int32_t H = sc.levels - 1;
+  std::vector<int32_t> &node_at = sc.node_at, &parent_pos = sc.parent_pos,
+                       &child_beg = sc.child_beg, &child_end = sc.child_end,
+                       &fail_rank = sc.fail_rank, &rank_node = sc.rank_node,
+                       &parent_node = sc.parent_node;
+  const int32_t max_children = sc.max_children;
 
   selinv_tree_plan *plan = new (std::nothrow) selinv_tree_plan();
   if (!plan) return SELINV_ERR_HIP;
@@ -132,8 +183,7 @@ extern "C" int selinv_tree_plan_create(const int32_t *parent_host, int64_t n, in
     delete plan;
     return SELINV_ERR_HIP;
   }
-  plan->level_off[0] = 0;
-  for (int32_t d = 0; d <= H; ++d) plan->level_off[d + 1] = plan->level_off[d] + level_count[d];
+  for (int32_t d = 0; d <= H + 1; ++d) plan->level_off[d] = sc.level_off[d];
 
   // tiles of kTreeTile positions, level by level from the root
   std::vector<int32_t> tile_lo, tile_hi;
