@@ -27,8 +27,22 @@
 // next (lower) block and G_{a_s,t} becomes G_lower[a_s - 1].
 //
 // Work per block: one 32x32 inverse, five block products forward and eight
-// backward (against one and three for the plain sweep), in exchange for B*P
+// backward (against two and three for the plain sweep), in exchange for B*P
 // independent sweeps instead of B.
+//
+// Fill decay.  F_{i+1} = -C_i Sinv F_i shrinks geometrically along a
+// diagonally dominant segment (by |C_i S_i^-1| per block: 2^-3.6 on the
+// b = 32 workload).  Once every entry of F_{i+1} is at most 2^-100 times the
+// largest entry of the segment's first coupling block A_{a,t}, the collect
+// stops carrying it: F_j = 0 for j > i, which is exactly the elimination of
+// A + E with E one block at (i+1, t) (and its transpose) equal to the F_{i+1}
+// just computed.  max|E| <= 2^-100 max|A|, 47 bits below the rounding of A's
+// own entries, so the result is the selected inverse of A to within the
+// rounding error the computation has anyway.  From there on every step of
+// the segment is the plain sweep (two products forward, three backward):
+// with F = 0 the update of t stops, the segment's final fill block is zero,
+// so G_{t_s,t} = 0 comes out of the separator chain exactly and G_{t,j} = 0
+// for every j past the drop.  A fill that does not decay is never dropped.
 #include <algorithm>
 #include <cmath>
 
@@ -51,7 +65,8 @@ template <typename T>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void seg32_collect(
     int L, int P, const T *__restrict__ diag, const T *__restrict__ lower,
     T *__restrict__ st_sinv, T *__restrict__ st_f, T *__restrict__ r_S, T *__restrict__ r_F,
-    T *__restrict__ r_U, double *__restrict__ seg_ld, int32_t *__restrict__ seg_fail) {
+    T *__restrict__ r_U, double *__restrict__ seg_ld, int32_t *__restrict__ seg_fail,
+    int32_t *__restrict__ seg_fill_end) {
   using Tr = io32::Traits<T>;
   __shared__ __align__(16) T col[32];
   __shared__ __align__(16) T tA[Tr::kTile];
@@ -76,6 +91,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     S = sl.get_sym(tA);
     if (left) F = io32::get_blk(tB, g, j);
   }
+  // fill is carried while `fill`; fe = the first block whose fill is dropped
+  bool fill = left;
+  int fe = left ? ts : a;
+  const T drop_below = left ? f32t::max_abs(F) * T(0x1p-100) : T(0);
+  if (left && f32t::all_below(F, drop_below)) {  // a zero coupling block: no fill
+    fill = false;
+    fe = a;
+    F = f32t::zero<T>();
+  }
   f16::PivotLog pl;
   int32_t fail = 0;
   for (int i = a; i < ts; ++i) {
@@ -85,23 +109,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     if (f32t::gj_inverse(S, col, g, j, pl) && !fail) fail = i + 1;
     f16::wave_sync();
     io32::put_blk(tA, g, j, S);
-    if (left) io32::put_blk(tB, g, j, F);
+    if (fill) io32::put_blk(tB, g, j, F);
     f16::wave_sync();
     const io32::NatP<T> pk = sl.gather_packed(tA);
     io32::Nat<T> fn;
-    if (left) fn = io32::get(tB, lane);
+    if (fill) fn = io32::get(tB, lane);
     f16::wave_sync();
     io32::store_packed(sinv + i * PB, lane, pk);
-    if (left) io32::store_ws(fst + i * BB, lane, fn);
+    if (fill) io32::store_ws(fst + i * BB, lane, fn);
     io32::put(tA, lane, Cn);
     io32::put(tB, lane, Dn);
     f16::wave_sync();
     const Blk<T> Ct = io32::get_blk_t(tA, g, j);  // O32(C_i^T)
     const Blk<T> Dd = sl.get_sym(tB);
-    if (left) {
+    if (fill) {
       const Blk<T> Y2 = f32t::mm(S, F, f32t::zero<T>());  // Sinv F_i
       U = f32t::mm_lower(F, Y2, U);                       // += F_i^T Sinv F_i
       F = f32t::neg(f32t::mm(Ct, Y2, f32t::zero<T>()));   // -C_i Sinv F_i
+      if (f32t::all_below(F, drop_below)) {               // dropped from i + 1 on
+        fill = false;
+        fe = i + 1;
+        F = f32t::zero<T>();
+      }
     }
     const Blk<T> Y1 = f32t::mm(S, Ct, f32t::zero<T>());  // Sinv C_i^T
     // D_{i+1} - C_i Sinv C_i^T; the (1,0) tile is not formed (the blocked
@@ -128,6 +157,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   if (lane == 0) {
     seg_ld[q] = pl.log();
     seg_fail[q] = fail;
+    seg_fill_end[q] = fe;
   }
 }
 
@@ -157,7 +187,7 @@ template <typename T>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void seg32_distribute(
     int L, int P, const T *__restrict__ lower, const T *__restrict__ st_sinv,
     const T *__restrict__ st_f, const T *__restrict__ Gr_d, const T *__restrict__ Gr_l,
-    T *__restrict__ G_diag, T *__restrict__ G_lower) {
+    const int32_t *__restrict__ seg_fill_end, T *__restrict__ G_diag, T *__restrict__ G_lower) {
   using Tr = io32::Traits<T>;
   __shared__ __align__(16) T tA[Tr::kTile];
   __shared__ __align__(16) T tB[Tr::kTile];
@@ -167,6 +197,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int s = blockIdx.x % P;
   const int a = seg_begin(s, L, P), ts = seg_begin(s + 1, L, P) - 1;
   const bool left = s > 0;
+  // blocks [a, fe) carry fill to t; past fe the steps are the plain sweep
+  const int fe = seg_fill_end[m * P + s];
   const T *C = lower + m * (L - 1) * BB;
   const T *sinv = st_sinv + m * L * PB;
   const T *fst = st_f + m * L * BB;
@@ -188,11 +220,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
     f16::wave_sync();
     Gnn = io32::get_blk(tA, g, j);
-    if (left) {
+    if (left && fe == ts) {  // fill carried to the end: G_{ts,t} couples the step
       Gnt = io32::get_blk(tB, g, j);    // O32(G_{i+1,t})
       Gtn = io32::get_blk_t(tB, g, j);  // O32(G_{t,i+1})
-      Gtt = io32::get_blk(tC, g, j);
-    }
+    }  // else the final fill block was dropped and G_{ts,t} = 0 exactly
+    if (left) Gtt = io32::get_blk(tC, g, j);
   }
   if (ts == a) return;
   // Block i's packed Sinv, C_i and F_i are staged in LDS, then the next
@@ -200,23 +232,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   io32::NatP<T> Pc = io32::load_packed(sinv + (ts - 1) * PB, lane);
   io32::Nat<T> Cc = io32::load(C + (ts - 1) * BB, lane);
   io32::Nat<T> Fc;
-  if (left) Fc = io32::load_ws(fst + (ts - 1) * BB, lane);
+  if (ts - 1 < fe) Fc = io32::load_ws(fst + (ts - 1) * BB, lane);
   for (int i = ts - 1; i >= a; --i) {
     const int in = max(i - 1, a);
+    const bool two = i < fe;  // block i carries fill (implies left)
     f16::wave_sync();
     io32::put_packed(tA, lane, Pc);
     io32::put(tB, lane, Cc);
-    if (left) io32::put(tC, lane, Fc);
+    if (two) io32::put(tC, lane, Fc);
     Pc = io32::load_packed(sinv + in * PB, lane);
     Cc = io32::load(C + in * BB, lane);
-    if (left) Fc = io32::load_ws(fst + in * BB, lane);
+    if (in < fe) Fc = io32::load_ws(fst + in * BB, lane);
     f16::wave_sync();
     const Blk<T> Si = sl.get_packed(tA);
     const Blk<T> Ct = io32::get_blk_t(tB, g, j);            // O32(C_i^T)
     const Blk<T> X1 = f32t::mm(Ct, Si, f32t::zero<T>());     // C_i Sinv
     Blk<T> V1 = f32t::mm(Gnn, X1, f32t::zero<T>());
     Blk<T> Gii;
-    if (left) {
+    if (two) {
       const Blk<T> Fb = io32::get_blk(tC, g, j);             // O32(F_i)
       const Blk<T> X2 = f32t::mm(Fb, Si, f32t::zero<T>());   // F_i^T Sinv
       V1 = f32t::mm(Gtn, X2, V1);                            // + G_{i+1,t} X2
@@ -230,14 +263,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     f16::wave_sync();
     io32::put_blk(tA, g, j, f32t::neg(V1));  // G_{i+1,i}
     io32::put_sym(tB, g, j, Gii);
-    if (left) io32::put_blk_t(tC, g, j, Gtn);  // G_{i,t} = G_{t,i}^T
+    if (two) io32::put_blk_t(tC, g, j, Gtn);  // G_{i,t} = G_{t,i}^T
     f16::wave_sync();
     io32::store(Gl + i * BB, lane, io32::get(tA, lane));
     io32::store(Gd + i * BB, lane, io32::get(tB, lane));
     Gnn = io32::get_blk(tB, g, j);
-    if (left) {
-      Gnt = io32::get_blk(tC, g, j);
-      if (i == a) io32::store(Gl + (a - 1) * BB, lane, io32::get(tC, lane));
+    if (two) Gnt = io32::get_blk(tC, g, j);
+    if (left && i == a) {  // G_{a,t}; zero when the segment carried no fill
+      if (two)
+        io32::store(Gl + (a - 1) * BB, lane, io32::get(tC, lane));
+      else
+        io32::store(Gl + (a - 1) * BB, lane, io32::Nat<T>{});
     }
   }
 }
@@ -267,8 +303,8 @@ __global__ void seg32_finish(int64_t B, int L, int P, const double *__restrict__
 }
 
 struct SegLayout {
-  size_t sinv, f, rS, rF, rU, diag_r, lower_r, gr_d, gr_l, seg_ld, seg_fail, ld_r, info_r, ws_r,
-      total;
+  size_t sinv, f, rS, rF, rU, diag_r, lower_r, gr_d, gr_l, seg_ld, seg_fail, seg_fe, ld_r, info_r,
+      ws_r, total;
 };
 
 SegLayout seg_layout(int dtype_bytes, int64_t B, int64_t L, int P) {
@@ -291,6 +327,7 @@ SegLayout seg_layout(int dtype_bytes, int64_t B, int64_t L, int P) {
   o.gr_l = take(B * P * BB * w);
   o.seg_ld = take(B * P * sizeof(double));
   o.seg_fail = take(B * P * sizeof(int32_t));
+  o.seg_fe = take(B * P * sizeof(int32_t));
   o.ld_r = take(B * sizeof(double));
   o.info_r = take(B * sizeof(int32_t));
   o.ws_r = take(chain32_workspace_bytes(dtype_bytes, B, P));
@@ -329,16 +366,17 @@ hipError_t chain32_seg_launch(int64_t B, int64_t L, int P, const T *diag, const 
   T *gr_l = reinterpret_cast<T *>(base + o.gr_l);
   double *seg_ld = reinterpret_cast<double *>(base + o.seg_ld);
   int32_t *seg_fail = reinterpret_cast<int32_t *>(base + o.seg_fail);
+  int32_t *seg_fe = reinterpret_cast<int32_t *>(base + o.seg_fe);
   double *ld_r = reinterpret_cast<double *>(base + o.ld_r);
   int32_t *info_r = reinterpret_cast<int32_t *>(base + o.info_r);
   const unsigned grid = static_cast<unsigned>(B * P);
   hipLaunchKernelGGL(seg32_collect<T>, dim3(grid), dim3(64), 0, s, static_cast<int>(L), P, diag,
-                     lower, sinv, f, rS, rF, rU, seg_ld, seg_fail);
+                     lower, sinv, f, rS, rF, rU, seg_ld, seg_fail, seg_fe);
   hipLaunchKernelGGL(seg32_reduce<T>, dim3(grid), dim3(64), 0, s, P, rS, rF, rU, diag_r, lower_r);
   hipError_t e = chain32_launch<T>(B, P, diag_r, lower_r, gr_d, gr_l, ld_r, info_r, base + o.ws_r, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(seg32_distribute<T>, dim3(grid), dim3(64), 0, s, static_cast<int>(L), P,
-                     lower, sinv, f, gr_d, gr_l, G_diag, G_lower);
+                     lower, sinv, f, gr_d, gr_l, seg_fe, G_diag, G_lower);
   hipLaunchKernelGGL(seg32_finish, dim3(static_cast<unsigned>((B + 255) / 256)), dim3(256), 0, s,
                      B, static_cast<int>(L), P, seg_ld, seg_fail, ld_r, info_r, logdet, info);
   return hipGetLastError();

@@ -117,6 +117,34 @@ __device__ __forceinline__ void store_t(T *P, const Blk<T> &b, int g, int j) {
     for (int J = 0; J < 2; ++J) f16::store_t(P + 16 * J * 32 + 16 * I, 32, b.t[I][J], g, j);
 }
 
+// Largest |entry| of a block, the same value in every lane of the wavefront.
+template <typename T>
+__device__ __forceinline__ T max_abs(const Blk<T> &b) {
+  T m = T(0);
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m = fmax(m, fabs(b.t[I][J][r]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off, 64));
+  return m;
+}
+
+// True in every lane when every entry of the block has |entry| <= bound.
+template <typename T>
+__device__ __forceinline__ bool all_below(const Blk<T> &b, T bound) {
+  bool ok = true;
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ok = ok && fabs(b.t[I][J][r]) <= bound;
+  return __all(ok);
+}
+
 template <typename T>
 __device__ __forceinline__ Blk<T> neg(Blk<T> b) {
 #pragma unroll

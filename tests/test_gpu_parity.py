@@ -137,6 +137,58 @@ def test_chain_b32_segments(ssa, B, L, dt):
     run_chain(ssa, B, L, 32, DT[dt], seed=B * 100 + L, load=1.0)
 
 
+@pytest.mark.parametrize("dt", ["f64", "f32"])
+def test_chain_b32_fill_drop(ssa, dt):
+    """8 chains of 8192 blocks of 32 (diagonal load 1.0): 128 segments of 64
+    blocks per chain.  The fill block to each segment's left separator decays
+    below 2^-100 of the segment's first coupling block after about 28 blocks
+    and is dropped from there on; every chain is compared with the oracle."""
+    e = run_chain(ssa, 8, 8192, 32, DT[dt], seed=11, load=1.0)
+    say("  worst rel err %.2e" % e)
+
+
+def test_chain_b32_fill_drop_zero_coupling(ssa):
+    """Zero coupling blocks at segment starts (256 segments of 32 blocks per
+    chain; the chain splits there, so those segments carry no fill at all and
+    (A^-1)_{a,a-1} = 0 exactly)."""
+    d, l = spdgen.chain(2, 8192, 32, seed=12, diag_load=1.0)
+    for a in (64, 4096, 8128):
+        l[:, a - 1] = 0.0
+    Gd, Gl, ld, info = ssa.chain(_to(d, torch.float64), _to(l, torch.float64), return_info=True)
+    torch.cuda.synchronize()
+    Od, Ol, Old, Oinfo = oracle.chain(d, l)
+    assert not info.any() and not Oinfo.any()
+    _cmp("G_diag", Gd, Od, torch.float64)
+    for a in (64, 4096, 8128):
+        assert not Gl[:, a - 1].any()
+    mask = np.ones(8191, bool)
+    mask[[63, 4095, 8127]] = False
+    _cmp("G_lower", Gl[:, torch.from_numpy(mask).to(DEV)], Ol[:, mask], torch.float64)
+    _cmp_ld(ld, Old, 8192, torch.float64)
+
+
+def test_chain_b32_slow_decay_fill_kept(ssa):
+    """D_i = (2 + 0.01) M, C_i = -M (M SPD, b = 32), 2 chains of 20000 blocks
+    (400 segments of 50 blocks): the fill shrinks only by about 0.905 per
+    block, so it is carried to every segment's end; every chain matches the
+    oracle.  (The condition number stays near 400.)"""
+    rng = np.random.default_rng(21)
+    B, L, b = 2, 20000, 32
+    d = np.empty((B, L, b, b))
+    l = np.empty((B, L - 1, b, b))
+    for m in range(B):
+        M = pins.random_spd(b, rng, load=1.0)
+        d[m] = 2.01 * M
+        l[m] = -M
+    Gd, Gl, ld, info = ssa.chain(_to(d, torch.float64), _to(l, torch.float64), return_info=True)
+    torch.cuda.synchronize()
+    Od, Ol, Old, Oinfo = oracle.chain(d, l)
+    assert not info.any() and not Oinfo.any()
+    e = max(_cmp("G_diag", Gd, Od, torch.float64), _cmp("G_lower", Gl, Ol, torch.float64))
+    _cmp_ld(ld, Old, L, torch.float64)
+    say("  worst rel err %.2e" % e)
+
+
 @pytest.mark.parametrize("k", [3, 7, 8, 12, 31, 63])
 def test_chain_b32_segments_not_pd_info(ssa, k):
     """One bad block in a segment interior (3, 12), at a separator (7, 31,
