@@ -122,6 +122,107 @@ __global__ __launch_bounds__(256) void chain_small_kernel(
   }
 }
 
+// Short chains (L <= kTinyL), few of them: one chain per workgroup of one
+// wavefront, the whole chain staged in LDS by one burst of coalesced loads
+// (its diagonal blocks mirrored from their lower triangles, padded to 8 x 8),
+// Sinv_k kept in LDS, so the sweep pays one global-memory latency instead of
+// one per block.  The eight slots of the wavefront run the same chain; slot 0
+// writes the outputs.
+constexpr int kTinyL = 32;
+
+template <typename T>
+__global__ __launch_bounds__(64) void chain_tiny_kernel(
+    int L, int b, const T *__restrict__ diag, const T *__restrict__ lower,
+    T *__restrict__ G_diag, T *__restrict__ G_lower, double *__restrict__ logdet,
+    int32_t *__restrict__ info) {
+  __shared__ __align__(32) T Dl[kTinyL * 64];
+  __shared__ __align__(32) T Cl[(kTinyL - 1) * 64];
+  __shared__ __align__(32) T Sl[kTinyL * 64];
+  __shared__ __align__(32) T stage[2][8 * 64];
+  const int lane = threadIdx.x;
+  const int s = lane >> 3, i = lane & 7;
+  const int64_t m = blockIdx.x;
+  const int bb = b * b;
+  const T *D = diag + m * L * bb;
+  const T *C = lower + m * (L - 1) * bb;
+  T *Gd = G_diag + m * L * bb;
+  T *Gl = G_lower + m * (L - 1) * bb;
+  const bool writer = s == 0;
+  const r8::Stage<T> sa{stage[0]}, sb{stage[1]};
+
+  // padding: identity diagonal blocks, zero off-diagonal blocks
+  for (int e = lane; e < L * 64; e += 64) Dl[e] = ((e & 63) >> 3) == (e & 7) ? T(1) : T(0);
+  for (int e = lane; e < (L - 1) * 64; e += 64) Cl[e] = T(0);
+  __syncthreads();
+  // every entry read once, consecutive lanes on consecutive addresses
+  for (int e = lane; e < L * bb; e += 64) {
+    const int k = e / bb, r = (e % bb) / b, c = e % b;
+    if (c <= r) {  // lower triangle, mirrored
+      const T x = D[e];
+      Dl[k * 64 + r * 8 + c] = x;
+      Dl[k * 64 + c * 8 + r] = x;
+    }
+  }
+  for (int e = lane; e < (L - 1) * bb; e += 64) {
+    const int k = e / bb, r = (e % bb) / b, c = e % b;
+    Cl[k * 64 + r * 8 + c] = C[e];
+  }
+  __syncthreads();
+
+  double ld = 0.0;
+  int32_t fail = 0;
+  r8::Row<T> S = r8::load8(Dl, i);
+  for (int k = 0; k < L; ++k) {
+    f16::PivotLog pl;
+    if (r8::gj_inverse(S, sa, s, i, pl) && !fail) fail = k + 1;
+    ld += pl.log();
+    if (k == L - 1) break;
+    if (writer) r8::store8(Sl + k * 64, i, S);
+    f16::wave_sync();
+    const r8::Stage<T> sk{Sl + k * 64}, ck{Cl + k * 64};
+    const r8::Row<T> X = r8::mul(r8::load8(Cl + k * 64, i), sk, 0, r8::zero<T>());  // C_k Sinv_k
+    const r8::Row<T> M = r8::mul_t(X, ck, 0, r8::zero<T>());                        // X C_k^T
+    const r8::Row<T> Dn = r8::load8(Dl + (k + 1) * 64, i);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) S.v[c] = Dn.v[c] - M.v[c];
+  }
+  if (fail) {
+    if (writer) {
+      r8::Row<T> nan;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) nan.v[c] = static_cast<T>(__builtin_nan(""));
+      for (int k = 0; k < L; ++k) r8::store(Gd + k * bb, b, i, nan);
+      for (int k = 0; k + 1 < L; ++k) r8::store(Gl + k * bb, b, i, nan);
+      if (i == 0) {
+        logdet[m] = __builtin_nan("");
+        if (info) info[m] = fail;
+      }
+    }
+    return;
+  }
+  r8::Row<T> G = S;  // G_{L-1} = Sinv_{L-1}
+  if (writer) r8::store(Gd + (L - 1) * bb, b, i, G);
+  for (int k = L - 2; k >= 0; --k) {
+    const r8::Stage<T> sk{Sl + k * 64};
+    const r8::Row<T> X = r8::mul(r8::load8(Cl + k * 64, i), sk, 0, r8::zero<T>());  // C_k Sinv_k
+    f16::wave_sync();
+    sb.put(s, i, X);
+    f16::wave_sync();
+    const r8::Row<T> V = r8::mul(G, sb, s, r8::zero<T>());  // G_{k+1} X
+    sa.put(s, i, V);
+    f16::wave_sync();
+    G = r8::mul_tn(sb, sa, s, i, r8::load8(Sl + k * 64, i));  // Sinv_k + X^T V
+    if (writer) {
+      r8::store(Gl + k * bb, b, i, r8::neg(V));
+      r8::store(Gd + k * bb, b, i, G);
+    }
+  }
+  if (writer && i == 0) {
+    logdet[m] = ld;
+    if (info) info[m] = 0;
+  }
+}
+
 }  // namespace
 
 size_t chain_small_workspace_bytes(int dtype_bytes, int64_t B, int64_t L) {
@@ -132,6 +233,11 @@ template <typename T>
 hipError_t chain_small_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower,
                               T *G_diag, T *G_lower, double *logdet, int32_t *info, void *ws,
                               hipStream_t s) {
+  if (L <= kTinyL && B <= 64) {  // the whole chain in LDS, one chain per workgroup
+    hipLaunchKernelGGL(chain_tiny_kernel<T>, dim3(static_cast<unsigned>(B)), dim3(64), 0, s,
+                       static_cast<int>(L), b, diag, lower, G_diag, G_lower, logdet, info);
+    return hipGetLastError();
+  }
   const int64_t per_block = kWaves * 8;
   const unsigned grid = static_cast<unsigned>((B + per_block - 1) / per_block);
   hipLaunchKernelGGL(chain_small_kernel<T>, dim3(grid), dim3(256), 0, s, B,
