@@ -77,6 +77,8 @@ extern "C" {
 #define SELINV_ERR_BAD_PATTERN 4 /* junction pattern or elimination order is invalid            */
 #define SELINV_ERR_WAIT_TIMEOUT 5 /* a bounded dataflow wait expired (reported as info = -1)    */
 
+#define SELINV_ERR_SCRATCH_LIMIT 6 /* the call needs more scratch than the static array holds */
+
 /* info value of a call whose bounded dataflow wait expired */
 #define SELINV_INFO_WAIT_TIMEOUT (-1)
 
@@ -105,6 +107,27 @@ SELINV_API int selinv_chain_f64(int64_t B, int64_t L, int32_t b, const double *d
 SELINV_API int selinv_chain_f32(int64_t B, int64_t L, int32_t b, const float *diag, const float *lower,
                      float *G_diag, float *G_lower, double *logdet, int32_t *info,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* The chain call without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, layouts, info, logdet
+ * and stream semantics as selinv_chain_f64 / _f32, minus workspace.  The
+ * kernels' scratch is a file-scope device array of
+ * selinv_chain_static_scratch_bytes() bytes (256 MiB) on each device the
+ * library runs on, held until the process ends; the call itself allocates
+ * nothing.  A call that needs more scratch than that
+ * (selinv_chain_workspace_bytes > the array) returns SELINV_ERR_SCRATCH_LIMIT
+ * and launches nothing.  The array is shared by every call on a device:
+ * calls that overlap in time on one device (different streams, or host
+ * threads) race and must be serialised by the caller.  The stream's device
+ * must be the current device. */
+SELINV_API size_t selinv_chain_static_scratch_bytes(void);
+SELINV_API int selinv_chain_noalloc_f64(int64_t B, int64_t L, int32_t b, const double *diag,
+                                        const double *lower, double *G_diag, double *G_lower,
+                                        double *logdet, int32_t *info, void *stream);
+SELINV_API int selinv_chain_noalloc_f32(int64_t B, int64_t L, int32_t b, const float *diag,
+                                        const float *lower, float *G_diag, float *G_lower,
+                                        double *logdet, int32_t *info, void *stream);
 
 /* ------------------------------------------------------------------- star
  * Block-arrowhead SPD matrices (item "Star": one centre block coupled to K

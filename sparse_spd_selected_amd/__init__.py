@@ -28,7 +28,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libselinv.so")
 
-OK, INVALID_ARG, BAD_TREE, HIP_ERROR, BAD_PATTERN, WAIT_TIMEOUT = 0, 1, 2, 3, 4, 5
+OK, INVALID_ARG, BAD_TREE, HIP_ERROR, BAD_PATTERN, WAIT_TIMEOUT, SCRATCH_LIMIT = range(7)
 INFO_WAIT_TIMEOUT = -1
 MAX_B = 32
 
@@ -68,6 +68,12 @@ def lib():
         raise ImportError("libselinv.so is not built (run sparse_spd_selected_amd.build())")
     L = ctypes.CDLL(LIB_PATH)
     i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    L.selinv_chain_static_scratch_bytes.argtypes = []
+    L.selinv_chain_static_scratch_bytes.restype = sz
+    for name in ("selinv_chain_noalloc_f64", "selinv_chain_noalloc_f32"):
+        f = getattr(L, name)
+        f.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, vp, vp]
+        f.restype = ctypes.c_int
     L.selinv_tree_schedule.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp]
     L.selinv_tree_schedule.restype = ctypes.c_int
     L.selinv_strerror.argtypes = [ctypes.c_int]
@@ -316,6 +322,33 @@ def chain(diag: torch.Tensor, lower: torch.Tensor, check: bool = False, return_i
     if return_info:
         return G_diag, G_lower, logdet, info
     return G_diag, G_lower, logdet
+
+
+def chain_noalloc(diag: torch.Tensor, lower: torch.Tensor, return_info=False):
+    """chain() through the entry point that allocates no scratch
+    (selinv_chain_noalloc_*): the kernels use the library's static per-device
+    scratch array instead of a workspace.  Only the outputs are allocated
+    here; calls that overlap in time on one device race."""
+    dt, dev = diag.dtype, diag.device
+    diag = _check_tensor(diag, "diag", dev, dt)
+    lower = _check_tensor(lower, "lower", dev, dt)
+    if diag.dim() < 3 or diag.shape[-1] != diag.shape[-2]:
+        raise ValueError("diag must be [..., L, b, b]")
+    *batch, L, b, _ = diag.shape
+    if tuple(lower.shape) != tuple(batch) + (L - 1, b, b):
+        raise ValueError("lower must be [..., L-1, b, b] matching diag")
+    B = 1
+    for s_ in batch:
+        B *= s_
+    G_diag, G_lower = torch.empty_like(diag), torch.empty_like(lower)
+    logdet = torch.empty(tuple(batch), dtype=torch.float64, device=dev)
+    info = torch.empty(tuple(batch), dtype=torch.int32, device=dev)
+    fn = "selinv_chain_noalloc_" + _sfx(diag)
+    with torch.cuda.device(dev):
+        rc = getattr(lib(), fn)(B, L, b, _ptr(diag), _ptr(lower), _ptr(G_diag), _ptr(G_lower),
+                                _ptr(logdet), _ptr(info), _stream(dev))
+    _status(rc, fn)
+    return (G_diag, G_lower, logdet, info) if return_info else (G_diag, G_lower, logdet)
 
 
 # ------------------------------------------------------------------- star

@@ -26,7 +26,7 @@ SOURCES = [
     "star_b32.hip",
     "chain_b32.hip", "chain_b32_seg.hip",
     "tree_b8.hip",
-    "chain_small.hip",
+    "chain_small.hip", "chain_noalloc.hip",
     "vjp_generic.hip", "vjp_chain_b16.hip", "vjp_star_b32.hip",
     "vjp_tree_b8.hip", "vjp_chain_seg.hip",
     "shared_factor.hip", "chain_solve_b16.hip", "star_solve_b32.hip",

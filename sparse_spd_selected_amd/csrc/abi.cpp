@@ -394,6 +394,8 @@ const char *selinv_strerror(int status) {
     case SELINV_ERR_BAD_TREE: return "parent array is not a single rooted tree";
     case SELINV_ERR_HIP: return "HIP runtime or kernel launch error";
     case SELINV_ERR_BAD_PATTERN: return "invalid junction pattern or elimination order";
+    case SELINV_ERR_SCRATCH_LIMIT:
+      return "the call needs more scratch than the static scratch array holds";
     case SELINV_ERR_WAIT_TIMEOUT:
       return "a bounded wait of the single-launch tree schedule expired (info = -1)";
     default: return "unknown status";

@@ -57,6 +57,7 @@ def test_header_status_codes_match_binding():
     assert codes["SELINV_ERR_WAIT_TIMEOUT"] == ssa.WAIT_TIMEOUT
     assert codes["SELINV_INFO_WAIT_TIMEOUT"] == ssa.INFO_WAIT_TIMEOUT
     assert codes["SELINV_ERR_BAD_PATTERN"] == ssa.BAD_PATTERN
+    assert codes["SELINV_ERR_SCRATCH_LIMIT"] == ssa.SCRATCH_LIMIT
 
 
 def test_raise_info_distinguishes_timeout_from_not_pd(lib):
