@@ -65,10 +65,13 @@ def load(path: str | None = None):
     lib.oracle_chain_apply.argtypes = [i64, i64, i32, vp, vp, i64, vp, vp, i32, vp]
     lib.oracle_eliminate.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp, i64]
     lib.oracle_junction.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_junction_apply.argtypes = [i64, i64, i32, vp, vp, vp, vp, vp, i64, vp, vp, i32,
+                                          vp]
     for f in (lib.oracle_chain, lib.oracle_star, lib.oracle_tree, lib.oracle_tree_depths,
               lib.oracle_num_threads, lib.oracle_set_num_threads, lib.oracle_tree_vjp, lib.oracle_chain_vjp,
               lib.oracle_tree_apply, lib.oracle_chain_apply, lib.oracle_bidiag,
-              lib.oracle_nonsym_tree, lib.oracle_eliminate, lib.oracle_junction):
+              lib.oracle_nonsym_tree, lib.oracle_eliminate, lib.oracle_junction,
+              lib.oracle_junction_apply):
         f.restype = ctypes.c_int
     if path == _LIB:
         _lib = lib
@@ -369,6 +372,24 @@ def filled_pattern(n, edge_index, order=None, lib=None):
                 slot=slot, flip=(w < col)[slot])
 
 
+def _slot_values(P, edge_index, edge_val):
+    """A on the slots of an elimination: A_{w,v} = edge_val[e] when
+    (w, v) = (i_e, j_e), its transpose when (w, v) = (j_e, i_e), zero on
+    fill.  edge_val [B, m, b, b] -> [B, nnz, b, b]."""
+    B, b = edge_val.shape[0], edge_val.shape[-1]
+    ei = np.asarray(edge_index[0], dtype=np.int64)
+    ej = np.asarray(edge_index[1], dtype=np.int64)
+    nnz = P["nbr"].shape[0]
+    key = {(int(a), int(c)): e for e, (a, c) in enumerate(zip(ei, ej))}
+    w, v = P["nbr"].astype(np.int64), P["col"]
+    Aoff = np.zeros((B, nnz, b, b))
+    for t in range(nnz):
+        e = key.get((max(w[t], v[t]), min(w[t], v[t])))
+        if e is not None:
+            Aoff[:, t] = edge_val[:, e] if w[t] > v[t] else np.swapaxes(edge_val[:, e], -1, -2)
+    return Aoff
+
+
 def junction(diag, edge_index, edge_val, order=None, lib=None, pattern=None):
     """Selected inverse of general sparse SPD matrices sharing one pattern.
 
@@ -383,19 +404,9 @@ def junction(diag, edge_index, edge_val, order=None, lib=None, pattern=None):
     if single:
         diag, edge_val = diag[None], edge_val[None]
     B, n, b = diag.shape[0], diag.shape[1], diag.shape[2]
-    ei = np.asarray(edge_index[0], dtype=np.int64)
-    ej = np.asarray(edge_index[1], dtype=np.int64)
     P = pattern or filled_pattern(n, edge_index, order, lib)
     nnz = P["nbr"].shape[0]
-    # A on the slots: A_{w,v} = edge_val[e] when (w, v) = (i_e, j_e), its
-    # transpose when (w, v) = (j_e, i_e), zero on fill
-    key = {(int(a), int(c)): e for e, (a, c) in enumerate(zip(ei, ej))}
-    w, v = P["nbr"].astype(np.int64), P["col"]
-    Aoff = np.zeros((B, nnz, b, b))
-    for t in range(nnz):
-        e = key.get((max(w[t], v[t]), min(w[t], v[t])))
-        if e is not None:
-            Aoff[:, t] = edge_val[:, e] if w[t] > v[t] else np.swapaxes(edge_val[:, e], -1, -2)
+    Aoff = _slot_values(P, edge_index, edge_val)
     Gd = np.empty_like(diag)
     Go = np.empty((B, nnz, b, b))
     logdet = np.empty(B)
@@ -409,3 +420,33 @@ def junction(diag, edge_index, edge_val, order=None, lib=None, pattern=None):
     if single:
         return Gd[0], P["S_index"], Gl[0], logdet[0], int(info[0])
     return Gd, P["S_index"], Gl, logdet, info
+
+
+def junction_apply(diag, edge_index, edge_val, vec, mode, order=None, lib=None, pattern=None):
+    """Solve (mode "solve": x = A^{-1} y) or the sampling transform (mode
+    "sample": x = L^{-T} D^{-1/2} z) on the filled pattern, from the block
+    LDL^T of the elimination (oracle_junction_apply).
+
+    diag [B,n,b,b] (or [n,b,b]), edge_index, edge_val and order as for
+    `junction`; vec [B,n,b,k] (or [n,b,k]) by label.  -> (x, info)."""
+    lib = lib or load()
+    diag, edge_val, vec = _f64(diag), _f64(edge_val), _f64(vec)
+    single = diag.ndim == 3
+    if single:
+        diag, edge_val, vec = diag[None], edge_val[None], vec[None]
+    B, n, b = diag.shape[0], diag.shape[1], diag.shape[2]
+    k = vec.shape[-1]
+    if vec.shape != (B, n, b, k):
+        raise OracleError("vec must be [B, n, b, k]")
+    P = pattern or filled_pattern(n, edge_index, order, lib)
+    Aoff = _slot_values(P, edge_index, edge_val)
+    out = np.empty_like(vec)
+    info = np.empty(B, np.int32)
+    md = {"solve": 0, "sample": 1}[mode]
+    rc = lib.oracle_junction_apply(B, n, b, _p(P["order"]), _p(P["nbr_ptr"]), _p(P["nbr"]),
+                                   _p(diag), _p(Aoff), k, _p(vec), _p(out), md, _p(info))
+    if rc:
+        raise OracleError("oracle_junction_apply status %d" % rc)
+    if single:
+        return out[0], int(info[0])
+    return out, info

@@ -1013,6 +1013,74 @@ static int64_t junction_slot(const int64_t *nbr_ptr, const int32_t *nbr, const i
  * where G_{w,x} for w before x is G_{x,w}^T.  Every block read lies in S
  * because N is a clique of S; returns 4 if the given pattern is not closed
  * that way (not the output of an elimination), else 0. */
+/* The block LDL^T of one matrix in the elimination order (right-looking):
+ * on return Cd holds the pivots D_v by label, Rv their Cholesky factors
+ * (D_v = R_v R_v^T), Di their inverses and Lo the multipliers
+ * L_{w,v} = C_{w,v} D_v^-1 by slot; Co is the working copy of the
+ * off-diagonal blocks.  *fail = 0 or 1 + the label of the first node whose
+ * pivot is not positive definite (its Di and Rv are NaN); *ld = log det A
+ * when *fail == 0.  Returns 1 if the pattern is not closed under elimination
+ * (a block the Schur update needs is missing), else 0. */
+static int junction_ldl(int64_t n, int b, const int32_t *order, const int64_t *nbr_ptr,
+                        const int32_t *nbr, const int32_t *pos, const double *A_diag,
+                        const double *A_off, double *Cd, double *Co, double *Lo, double *Di,
+                        double *Rv, double *T, int32_t *fail, double *ld) {
+  const int64_t bb = (int64_t)b * b, nnz = nbr_ptr[n];
+  int bad_pattern = 0;
+  memcpy(Cd, A_diag, sizeof(double) * (size_t)(n * bb));
+  if (nnz) memcpy(Co, A_off, sizeof(double) * (size_t)(nnz * bb));
+  *fail = 0;
+  *ld = 0.0;
+  for (int64_t s = 0; s < n; ++s) {
+    const int32_t v = order[s];
+    /* the pivot: D_v = R R^T, its inverse and its log det */
+    if (chol(b, Cd + v * bb, Rv + v * bb)) {
+      if (!*fail) *fail = v + 1;
+      fill_nan(Di + v * bb, bb);
+      fill_nan(Rv + v * bb, bb);
+    } else {
+      inv_from_chol(b, Rv + v * bb, Di + v * bb);
+      *ld += logdet_chol(b, Rv + v * bb);
+    }
+    for (int64_t t = nbr_ptr[s]; t < nbr_ptr[s + 1]; ++t)
+      matmul(b, Co + t * bb, Di + v * bb, Lo + t * bb);            /* L_{w,v} */
+    /* Schur update of every pair of later neighbours */
+    for (int64_t t1 = nbr_ptr[s]; t1 < nbr_ptr[s + 1]; ++t1)
+      for (int64_t t2 = nbr_ptr[s]; t2 < nbr_ptr[s + 1]; ++t2) {
+        const int32_t w1 = nbr[t1], w2 = nbr[t2];
+        if (pos[w1] < pos[w2]) continue;
+        mm_nt(b, Lo + t1 * bb, Co + t2 * bb, T);                     /* L_{w1,v} C_{w2,v}^T */
+        const int64_t t12 = w1 == w2 ? 0 : junction_slot(nbr_ptr, nbr, pos, w1, w2);
+        if (t12 < 0) {                          /* not a chordal pattern */
+          bad_pattern = 1;
+          continue;
+        }
+        add_to(bb, w1 == w2 ? Cd + w1 * bb : Co + t12 * bb, T, -1.0);
+      }
+  }
+  return bad_pattern;
+}
+
+/* Numeric part, for a batch of B matrices on the pattern of one elimination
+ * (order, nbr_ptr, nbr from oracle_eliminate).  Slot t of the neighbour list
+ * of step s holds the block (w, v) of S with w = nbr[t] and v = order[s].
+ *   diag   [B][n]   A_vv by label;  Aoff [B][nnz]  A_{w,v} per slot (zero
+ *                   where (w, v) is fill)
+ *   G_diag [B][n]   (A^-1)_vv by label;  G_off [B][nnz]  (A^-1)_{w,v} per slot
+ *   logdet [B], info [B] (0, or 1 + the label of the first node in the
+ *                   elimination order whose Schur pivot is not positive
+ *                   definite; logdet is then NaN).
+ * Block LDL^T, right-looking, in the elimination order (junction_ldl): the
+ * pivot of v is D_v = C_vv (the fully updated diagonal block),
+ * L_{w,v} = C_{w,v} D_v^-1 for every later neighbour w, and every pair
+ * (w1, w2) of later neighbours receives C_{w1,w2} -= L_{w1,v} D_v L_{w2,v}^T
+ * (= L_{w1,v} C_{w2,v}^T).
+ * Takahashi, in reverse elimination order, with N = the later neighbours of v:
+ *   G_{w,v} = - sum_{x in N} G_{w,x} L_{x,v}        (w in N)
+ *   G_vv    = D_v^-1 - sum_{w in N} L_{w,v}^T G_{w,v}
+ * where G_{w,x} for w before x is G_{x,w}^T.  Every block read lies in S
+ * because N is a clique of S; returns 4 if the given pattern is not closed
+ * that way (not the output of an elimination), else 0. */
 ORACLE_API int oracle_junction(int64_t B, int64_t n, int b, const int32_t *order,
                                const int64_t *nbr_ptr, const int32_t *nbr, const double *diag,
                                const double *Aoff, double *G_diag, double *G_off, double *logdet,
@@ -1027,40 +1095,15 @@ ORACLE_API int oracle_junction(int64_t B, int64_t n, int b, const int32_t *order
     double *Co = (double *)malloc(sizeof(double) * (size_t)((nnz ? nnz : 1) * bb));
     double *Lo = (double *)malloc(sizeof(double) * (size_t)((nnz ? nnz : 1) * bb));
     double *Di = (double *)malloc(sizeof(double) * (size_t)(n * bb));
-    double *R = (double *)malloc(sizeof(double) * bb);
+    double *Rv = (double *)malloc(sizeof(double) * (size_t)(n * bb));
     double *T = (double *)malloc(sizeof(double) * bb);
     double *T2 = (double *)malloc(sizeof(double) * bb);
     double *Gd = G_diag + mat * n * bb, *Go = G_off + mat * nnz * bb;
-    memcpy(Cd, diag + mat * n * bb, sizeof(double) * (size_t)(n * bb));
-    if (nnz) memcpy(Co, Aoff + mat * nnz * bb, sizeof(double) * (size_t)(nnz * bb));
     int32_t fail = 0;
     double ld = 0.0;
-    for (int64_t s = 0; s < n; ++s) {
-      const int32_t v = order[s];
-      /* the pivot: D_v = R R^T, its inverse and its log det */
-      if (chol(b, Cd + v * bb, R)) {
-        if (!fail) fail = v + 1;
-        fill_nan(Di + v * bb, bb);
-      } else {
-        inv_from_chol(b, R, Di + v * bb);
-        ld += logdet_chol(b, R);
-      }
-      for (int64_t t = nbr_ptr[s]; t < nbr_ptr[s + 1]; ++t)
-        matmul(b, Co + t * bb, Di + v * bb, Lo + t * bb);            /* L_{w,v} */
-      /* Schur update of every pair of later neighbours */
-      for (int64_t t1 = nbr_ptr[s]; t1 < nbr_ptr[s + 1]; ++t1)
-        for (int64_t t2 = nbr_ptr[s]; t2 < nbr_ptr[s + 1]; ++t2) {
-          const int32_t w1 = nbr[t1], w2 = nbr[t2];
-          if (pos[w1] < pos[w2]) continue;
-          mm_nt(b, Lo + t1 * bb, Co + t2 * bb, T);                   /* L_{w1,v} C_{w2,v}^T */
-          const int64_t t12 = w1 == w2 ? 0 : junction_slot(nbr_ptr, nbr, pos, w1, w2);
-          if (t12 < 0) {                          /* not a chordal pattern */
-            bad_pattern = 1;
-            continue;
-          }
-          add_to(bb, w1 == w2 ? Cd + w1 * bb : Co + t12 * bb, T, -1.0);
-        }
-    }
+    if (junction_ldl(n, b, order, nbr_ptr, nbr, pos, diag + mat * n * bb, Aoff + mat * nnz * bb,
+                     Cd, Co, Lo, Di, Rv, T, &fail, &ld))
+      bad_pattern = 1;
     /* Takahashi, reverse elimination order */
     for (int64_t s = n - 1; s >= 0; --s) {
       const int32_t v = order[s];
@@ -1096,7 +1139,93 @@ ORACLE_API int oracle_junction(int64_t B, int64_t n, int b, const int32_t *order
     }
     logdet[mat] = fail ? NAN : ld;
     info[mat] = fail;
-    free(Cd); free(Co); free(Lo); free(Di); free(R); free(T); free(T2);
+    free(Cd); free(Co); free(Lo); free(Di); free(Rv); free(T); free(T2);
+  }
+  free(pos);
+  return bad_pattern ? 4 : 0;
+}
+
+/* Solve and Gaussian sampling on the filled pattern, from the same block
+ * LDL^T (gabp-sparse-inv page, junction-tree section: junction_solve for one
+ * or several right-hand sides, and Gaussian sampling, both reusing the
+ * factorisation of the selected inverse):
+ *   solve A x = y:  u = y; in elimination order, for every later neighbour
+ *                   w of v: u_w -= L_{w,v} u_v; then w_v = D_v^-1 u_v (two
+ *                   triangular solves with R_v); in reverse order:
+ *                   x_v = w_v - sum_{w in N(v)} L_{w,v}^T x_w
+ *   sample:         w_v = R_v^-T z_v (D_v = R_v R_v^T), then the same reverse
+ *                   sweep, x = L^-T D^-1/2 z: Cov(x) = L^-T D^-1 L^-1 = A^-1
+ *                   for z ~ N(0, I).
+ * in, out [B][n][b][k] by label (k right-hand sides, k fastest); mode 0 =
+ * solve, 1 = sample; info [B] as for oracle_junction, and a matrix that
+ * fails gets NaN in out.  Returns 0, 1 for a bad argument, 4 for a pattern
+ * that is not closed under elimination. */
+ORACLE_API int oracle_junction_apply(int64_t B, int64_t n, int b, const int32_t *order,
+                                     const int64_t *nbr_ptr, const int32_t *nbr,
+                                     const double *diag, const double *Aoff, int64_t k,
+                                     const double *in, double *out, int mode, int32_t *info) {
+  if (B < 0 || n < 1 || b < 1 || k < 0 || (mode != 0 && mode != 1)) return 1;
+  const int64_t bb = (int64_t)b * b, bk = (int64_t)b * k, nnz = nbr_ptr[n];
+  int32_t *pos = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+  for (int64_t s = 0; s < n; ++s) pos[order[s]] = (int32_t)s;
+  int bad_pattern = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t mat = 0; mat < B; ++mat) {
+    double *Cd = (double *)malloc(sizeof(double) * (size_t)(n * bb));
+    double *Co = (double *)malloc(sizeof(double) * (size_t)((nnz ? nnz : 1) * bb));
+    double *Lo = (double *)malloc(sizeof(double) * (size_t)((nnz ? nnz : 1) * bb));
+    double *Di = (double *)malloc(sizeof(double) * (size_t)(n * bb));
+    double *Rv = (double *)malloc(sizeof(double) * (size_t)(n * bb));
+    double *T = (double *)malloc(sizeof(double) * bb);
+    double *u = (double *)malloc(sizeof(double) * (size_t)(n * bk + 1));
+    double *w = (double *)malloc(sizeof(double) * (size_t)(n * bk + 1));
+    double *t1 = (double *)malloc(sizeof(double) * (size_t)(bk + 1));
+    const double *y = in + mat * n * bk;
+    double *x = out + mat * n * bk;
+    int32_t fail = 0;
+    double ld = 0.0;
+    if (junction_ldl(n, b, order, nbr_ptr, nbr, pos, diag + mat * n * bb, Aoff + mat * nnz * bb,
+                     Cd, Co, Lo, Di, Rv, T, &fail, &ld))
+      bad_pattern = 1;
+    info[mat] = fail;
+    if (fail) {
+      fill_nan(x, n * bk);
+    } else {
+      if (mode == 0) {
+        memcpy(u, y, sizeof(double) * (size_t)(n * bk));
+        for (int64_t s = 0; s < n; ++s) {          /* L u' = y, elimination order */
+          const int32_t v = order[s];
+          for (int64_t t = nbr_ptr[s]; t < nbr_ptr[s + 1]; ++t) {
+            const int32_t wl = nbr[t];
+            for (int i = 0; i < b; ++i)
+              for (int64_t c = 0; c < k; ++c) {
+                double acc = 0.0;
+                for (int j = 0; j < b; ++j) acc += Lo[t * bb + i * b + j] * u[v * bk + j * k + c];
+                u[wl * bk + i * k + c] -= acc;
+              }
+          }
+        }
+        for (int64_t v = 0; v < n; ++v) {          /* D w = u' */
+          trsv_L(b, k, Rv + v * bb, u + v * bk, t1);
+          trsv_LT(b, k, Rv + v * bb, t1, w + v * bk);
+        }
+      } else {
+        for (int64_t v = 0; v < n; ++v) trsv_LT(b, k, Rv + v * bb, y + v * bk, w + v * bk);
+      }
+      for (int64_t s = n - 1; s >= 0; --s) {       /* L^T x = w, reverse order */
+        const int32_t v = order[s];
+        for (int i = 0; i < b; ++i)
+          for (int64_t c = 0; c < k; ++c) {
+            double acc = 0.0;
+            for (int64_t t = nbr_ptr[s]; t < nbr_ptr[s + 1]; ++t) {
+              const int32_t wl = nbr[t];
+              for (int j = 0; j < b; ++j) acc += Lo[t * bb + j * b + i] * x[wl * bk + j * k + c];
+            }
+            x[v * bk + i * k + c] = w[v * bk + i * k + c] - acc;
+          }
+      }
+    }
+    free(Cd); free(Co); free(Lo); free(Di); free(Rv); free(T); free(u); free(w); free(t1);
   }
   free(pos);
   return bad_pattern ? 4 : 0;

@@ -13,6 +13,13 @@ Independent references:
   * minimum degree on a tree creates no fill, and then the result must be the
     tree oracle's (pinned on its own); a path is the chain;
   * planted mistakes must break one of the above.
+
+The solve and sampling siblings (oracle_junction_apply) are pinned to
+numpy's dense solve of the assembled matrix (solve) and to numpy's Cholesky
+factor of the matrix permuted into the elimination order (sample: the
+factor's diagonal blocks are the Cholesky factors of the pivots, so
+x = L^-T D^-1/2 z is P^T Lc^-T P z for P A P^T = Lc Lc^T), plus
+x^T A x = z^T z, the tree reduction and planted mistakes.
 """
 import os
 import re
@@ -208,7 +215,7 @@ MUTANTS = [
     ("missing transpose", r"Gwx = T2;", "Gwx = Go + twx * bb;"),
     ("G_vv sign", r"add_to\(bb, Gd \+ v \* bb, T, -1\.0\);", "add_to(bb, Gd + v * bb, T, 1.0);"),
     ("L from unupdated A", r"matmul\(b, Co \+ t \* bb, Di \+ v \* bb, Lo \+ t \* bb\);",
-     "matmul(b, Aoff + mat * nnz * bb + t * bb, Di + v * bb, Lo + t * bb);"),
+     "matmul(b, A_off + t * bb, Di + v * bb, Lo + t * bb);"),
     ("ties to largest label", r"\(v < 0 \|\| deg\[u\] < deg\[v\]\)", "(v < 0 || deg[u] <= deg[v])"),
     ("no fill", r"adj\[x \* n \+ y\] = adj\[y \* n \+ x\] = 1;", "(void)0;"),
 ]
@@ -239,3 +246,134 @@ def test_mutants_are_caught(name, pat, rep):
             for k in range(S.shape[1]):
                 bad |= np.abs(Gl[k] - blk(Ai, S[0, k], S[1, k], 2)).max() > 1e-8
         assert bad, name
+
+
+# ------------------------------------------------ solve and sampling siblings
+def _perm_blocks(order, b):
+    return np.concatenate([np.arange(v * b, (v + 1) * b) for v in order])
+
+
+def check_apply(edge_index, n, b, k, B=2, seed=0, order=None, lib=None, tol=1e-11):
+    """Solve against numpy's dense solve; sample against numpy's Cholesky of
+    the matrix permuted into the elimination order.  Returns False on a
+    mismatch (for the planted-mistake battery)."""
+    d, v = spdgen.graph(edge_index, n, b, B=B, seed=seed)
+    rng = np.random.default_rng(seed + 100)
+    y = rng.standard_normal((B, n, b, k))
+    z = rng.standard_normal((B, n, b, k))
+    x, info = oracle.junction_apply(d, edge_index, v, y, "solve", order=order, lib=lib)
+    xs, info2 = oracle.junction_apply(d, edge_index, v, z, "sample", order=order, lib=lib)
+    if (info != 0).any() or (info2 != 0).any():
+        return False
+    o = oracle.eliminate(n, edge_index, order, lib=lib)[0]
+    p = _perm_blocks(o, b)
+    ok = True
+    for m in range(B):
+        A = spdgen.to_dense_graph(edge_index, d[m], v[m])
+        ref = np.linalg.solve(A, y[m].reshape(n * b, k))
+        ok &= np.abs(x[m].reshape(n * b, k) - ref).max() <= tol * np.abs(ref).max()
+        Lc = np.linalg.cholesky(A[np.ix_(p, p)])
+        xp = np.linalg.solve(Lc.T, z[m].reshape(n * b, k)[p])
+        ref_s = np.empty_like(xp)
+        ref_s[p] = xp
+        ok &= np.abs(xs[m].reshape(n * b, k) - ref_s).max() <= tol * np.abs(ref_s).max()
+        # x^T A x = z^T z column by column
+        X, Z = xs[m].reshape(n * b, k), z[m].reshape(n * b, k)
+        q = np.einsum("ic,ij,jc->c", X, A, X)
+        ok &= np.allclose(q, (Z * Z).sum(0), rtol=1e-10, atol=0)
+    return bool(ok)
+
+
+@pytest.mark.parametrize("r,c,b,k", [(1, 1, 2, 1), (1, 7, 3, 2), (3, 3, 2, 3), (4, 5, 1, 4),
+                                     (5, 4, 3, 1), (6, 6, 2, 5)])
+def test_apply_grid_dense(r, c, b, k):
+    assert check_apply(spdgen.grid_edges(r, c), r * c, b, k, seed=r * c + b)
+
+
+@pytest.mark.parametrize("n,extra,b,k", [(20, 30, 2, 3), (40, 80, 1, 2), (12, 40, 4, 1)])
+def test_apply_random_graph_dense(n, extra, b, k):
+    e = spdgen.random_graph_edges(n, extra, seed=n + extra)
+    assert check_apply(e, n, b, k, seed=n)
+
+
+@pytest.mark.parametrize("kind", ["natural", "reversed", "random"])
+def test_apply_explicit_orders(kind):
+    n = 16
+    order = {"natural": np.arange(n), "reversed": np.arange(n)[::-1].copy(),
+             "random": np.random.default_rng(3).permutation(n)}[kind]
+    assert check_apply(spdgen.grid_edges(4, 4), n, 2, 3, seed=5, order=order)
+
+
+def test_apply_no_edges_is_blockwise():
+    """No edges: A is block diagonal, x_v = A_vv^-1 y_v and x_v = R_v^-T z_v."""
+    n, b, k = 5, 3, 2
+    e = np.zeros((2, 0), np.int32)
+    d, v = spdgen.graph(e, n, b, B=1, seed=4)
+    y = np.random.default_rng(0).standard_normal((1, n, b, k))
+    x, info = oracle.junction_apply(d, e, v, y, "solve")
+    xs, _ = oracle.junction_apply(d, e, v, y, "sample")
+    for u in range(n):
+        assert np.allclose(x[0, u], np.linalg.solve(d[0, u], y[0, u]), rtol=1e-12, atol=1e-14)
+        R = np.linalg.cholesky(d[0, u])
+        assert np.allclose(xs[0, u], np.linalg.solve(R.T, y[0, u]), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("mode", ["solve", "sample"])
+def test_apply_tree_is_the_tree_oracle(mode):
+    """A tree eliminated children first (deepest level first, the tree
+    oracle's order) creates no fill, and its factor is the tree's collect:
+    both sweeps must be the tree oracle's (pinned on its own)."""
+    n, b, k = 40, 3, 2
+    parent = spdgen.random_recursive_tree(n, 2)
+    depth = oracle.tree_depths(parent)
+    order = np.array(sorted(range(n), key=lambda v: (-depth[v], v)), np.int32)
+    e = np.array([(max(v, int(parent[v])), min(v, int(parent[v])))
+                  for v in range(n) if parent[v] >= 0], np.int32).T.copy()
+    d, ed = spdgen.tree(parent, b, seed=7)
+    val = np.stack([ed[v] if parent[v] > v else ed[v].T for v in range(n) if parent[v] >= 0])
+    vec = np.random.default_rng(1).standard_normal((n, b, k))
+    got, info = oracle.junction_apply(d, e, val, vec, mode, order=order)
+    ref = oracle.tree_apply(parent, d, ed, vec, mode)
+    assert info == 0
+    assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+def test_apply_not_positive_definite():
+    e = spdgen.grid_edges(3, 4)
+    d, v = spdgen.graph(e, 12, 2, B=2, seed=1)
+    d[1, 6] = -np.eye(2)
+    y = np.ones((2, 12, 2, 3))
+    for mode in ("solve", "sample"):
+        x, info = oracle.junction_apply(d, e, v, y, mode)
+        assert info[0] == 0 and np.isfinite(x[0]).all()
+        assert info[1] == 7 and np.isnan(x[1]).all()
+
+
+APPLY_MUTANTS = [
+    ("forward update transposed",
+     r"acc \+= Lo\[t \* bb \+ i \* b \+ j\] \* u\[v \* bk \+ j \* k \+ c\];",
+     "acc += Lo[t * bb + j * b + i] * u[v * bk + j * k + c];"),
+    ("backward not transposed",
+     r"acc \+= Lo\[t \* bb \+ j \* b \+ i\] \* x\[wl \* bk \+ j \* k \+ c\];",
+     "acc += Lo[t * bb + i * b + j] * x[wl * bk + j * k + c];"),
+    ("forward update sign", r"u\[wl \* bk \+ i \* k \+ c\] -= acc;",
+     "u[wl * bk + i * k + c] += acc;"),
+    ("sample with R^-1", r"trsv_LT\(b, k, Rv \+ v \* bb, y \+ v \* bk, w \+ v \* bk\);",
+     "trsv_L(b, k, Rv + v * bb, y + v * bk, w + v * bk);"),
+    ("pivot solve one-sided", r"trsv_LT\(b, k, Rv \+ v \* bb, t1, w \+ v \* bk\);",
+     "memcpy(w + v * bk, t1, sizeof(double) * (size_t)bk);"),
+]
+
+
+@pytest.mark.parametrize("name,pat,rep", APPLY_MUTANTS, ids=[m[0] for m in APPLY_MUTANTS])
+def test_apply_mutants_are_caught(name, pat, rep):
+    src = open(oracle.SOURCE).read()
+    mutated, cnt = re.subn(pat, rep, src)
+    assert cnt == 1, "mutation site not found: " + name
+    with tempfile.TemporaryDirectory() as td:
+        c, so = os.path.join(td, "m.c"), os.path.join(td, "m.so")
+        open(c, "w").write(mutated)
+        lib = oracle.load(oracle.compile_oracle(c, so))
+        with np.errstate(all="ignore"):
+            ok = check_apply(spdgen.grid_edges(4, 4), 16, 2, 2, B=1, seed=2, lib=lib)
+        assert not ok, name
