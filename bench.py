@@ -23,7 +23,10 @@ reported beside it.
 stored factor); ``--op solve`` / ``--op sample`` time x = A^{-1} y and
 x = L^{-T} D^{-1/2} z with ``--k`` right-hand sides from a factor computed
 once before the timed region (nominal 8 b^2 k and 5 b^2 k + b^3 / 3 flop per
-block; compulsory bytes = factor + edge blocks + vectors in and out).
+block; compulsory bytes = factor + edge blocks + vectors in and out).  For the
+junction workload the solve / sample run on the filled pattern: 2 b^2 k per
+block of S in each sweep plus the pivot solves; compulsory bytes = the
+factor's S blocks and pivot triangles + vectors in and out.
 
 ``--op vjp`` times the reverse mode instead (one call = the vector-Jacobian
 product of every matrix of the batch, seeded normal cotangents on every
@@ -112,6 +115,13 @@ def nominal_flops(kind, cfg, op="selinv"):
     b = cfg["b"]
     nblk = block_rows(kind, cfg)
     k = cfg.get("k", 1)
+    if kind == "junction" and op in ("solve", "sample"):
+        # per S block (w, v): 2 b^2 k in each sweep it enters; per node the
+        # pivot solve (two triangular b x b solves, b^2 k each) for a solve,
+        # one (R_v^-T) for a sample
+        n, m, nnz, sk, sk2 = junction_counts(cfg)
+        sweeps, tri = (2, 2) if op == "solve" else (1, 1)
+        return cfg["B"] * b * b * k * (2 * sweeps * nnz + tri * n)
     if op == "solve":
         return 8 * b * b * k * nblk
     if op == "sample":
@@ -150,6 +160,10 @@ def compulsory_bytes(kind, cfg, w, op="selinv"):
         return (3 * cfg["n"] - 2 + 3 * cfg["n"]) * b2 * w + 4 * cfg["n"] + 4
     if kind == "junction":  # diag, edge_val in; G_diag, G_lower (on S) out; logdet, info
         n, m, nnz, sk, sk2 = junction_counts(cfg)
+        if op in ("solve", "sample"):  # the factor's S blocks and pivots once, vectors in, out
+            b = cfg["b"]
+            return cfg["B"] * ((nnz * b2 + n * b * (b + 1) // 2) * w
+                               + 2 * n * b * cfg.get("k", 1) * w)
         if op == "logdet":
             return cfg["B"] * ((n + m) * b2 * w + 8 + 4)
         return cfg["B"] * ((2 * n + m + nnz) * b2 * w + 8 + 4)
@@ -253,6 +267,13 @@ def run_gpu(kind, cfg, dtname, steps, warmup, op="selinv", graph=False):
                                                    seed=cfg["seed"], k=1)).to(dev).to(dt)
             call = ((lambda: f.solve(vc, vl)) if op == "solve"
                     else (lambda: f.sample(z_center=vc, z_leaves=vl)))
+        elif kind == "junction":  # plan and factor once, untimed
+            e = parent
+            plan = ssa.junction_plan(cfg["rows"] * cfg["cols"], e, cfg["b"], dt, dev)
+            f = ssa.junction_factor(inputs[0], e, inputs[1], plan=plan)
+            v = torch.from_numpy(spdgen.cotangent((cfg["B"], cfg["rows"] * cfg["cols"], cfg["b"],
+                                                   k), seed=cfg["seed"])).to(dev).to(dt)
+            call = (lambda: f.solve(v)) if op == "solve" else (lambda: f.sample(z=v))
         else:
             plan = ssa.tree_plan(parent, cfg["b"], dt, dev)
             f = ssa.tree_factor(parent, *inputs, plan=plan)
@@ -347,6 +368,20 @@ def cpu_baseline_apply(kind, cfg, op):
         t = time.perf_counter() - t0
         sub = dict(cfg, B=Bs)
         sample = "%d of %d stars, k = %d, float64, collect + %s" % (Bs, cfg["B"], k, op)
+    elif kind == "junction":
+        Bs = min(cfg["B"], 8)
+        n = cfg["rows"] * cfg["cols"]
+        e = spdgen.grid_edges(cfg["rows"], cfg["cols"])
+        d, val = spdgen.graph(e, n, cfg["b"], B=Bs, seed=cfg["seed"], diag_load=cfg["diag_load"])
+        v = spdgen.cotangent((Bs, n, cfg["b"], k), seed=cfg["seed"])
+        P = oracle.filled_pattern(n, e, lib=lib)
+        t0 = time.perf_counter()
+        oracle.junction_apply(d, e, val, v, op, lib=lib, pattern=P)
+        t = time.perf_counter() - t0
+        sub = dict(cfg, B=Bs)
+        sample = ("%d of %d matrices on the %d x %d grid (b=%d), k = %d, float64, "
+                  "factorisation + %s, symbolic analysis untimed"
+                  % (Bs, cfg["B"], cfg["rows"], cfg["cols"], cfg["b"], k, op))
     else:
         parent = spdgen.random_recursive_tree(cfg["n"], cfg["seed"])
         d, e = spdgen.tree(parent, cfg["b"], seed=cfg["seed"], diag_load=cfg["diag_load"])
@@ -357,6 +392,8 @@ def cpu_baseline_apply(kind, cfg, op):
         sub = cfg
         sample = "the whole tree, k = %d, float64, collect + %s, single thread" % (k, op)
     cores = 1 if kind == "tree" else int(lib.oracle_num_threads())
+    if kind == "junction":
+        cores = min(Bs, cores)
     return {"value": round(nominal_flops(kind, sub, op) / t / 1e9, 3), "unit": "GFLOP/s",
             "cores": cores, "kind": "oracle", "sample": sample, "seconds": round(t, 3),
             "block_rows_per_s": round(block_rows(kind, sub) / t, 1)}

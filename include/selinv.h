@@ -538,6 +538,49 @@ SELINV_API int selinv_junction_logdet_f32(const selinv_junction_plan *plan, int6
                                int32_t *info, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* Solve and Gaussian sampling on the filled pattern (the junction_solve
+ * sibling of the junction-tree section, one or several right-hand sides,
+ * and Gaussian sampling; both reuse the factorisation of the selected
+ * inverse, as in the shared-factor section above):
+ *   selinv_junction_factor_*: the factorisation of selinv_junction_logdet_*
+ *     (logdet [B], info [B] as there), keeping the factor in `factor`, a
+ *     caller-owned device buffer of selinv_junction_factor_bytes(plan, B)
+ *     bytes, 16-byte aligned, layout private to the library; factor must not
+ *     be NULL (selinv_junction_logdet_* computes log det alone).  Workspace:
+ *     selinv_junction_factor_workspace_bytes(plan, B).
+ *   selinv_junction_solve_*:  x = A^{-1} y,       y, x [B][n][b][k]
+ *   selinv_junction_sample_*: x = L^{-T} D^{-1/2} z, z, x [B][n][b][k]
+ *     with A = L D L^T the block LDL^T in the plan's elimination order and
+ *     D^{-1/2}_v = R_v^{-T} for D_v = R_v R_v^T, so x ~ N(0, A^{-1}) when
+ *     z ~ N(0, I) (the caller draws z; the map z -> x is deterministic).
+ *     Vectors by node label, k fastest, no alignment requirement; x must not
+ *     alias y / z (x == y is rejected).  The factor must come from a factor
+ *     call with the same plan and B; where that call reported info != 0 for
+ *     a matrix, that matrix's x is unspecified.  No workspace. */
+SELINV_API size_t selinv_junction_factor_bytes(const selinv_junction_plan *plan, int64_t B);
+SELINV_API size_t selinv_junction_factor_workspace_bytes(const selinv_junction_plan *plan,
+                                                        int64_t B);
+SELINV_API int selinv_junction_factor_f64(const selinv_junction_plan *plan, int64_t B,
+                               const double *diag, const double *edge_val, double *factor,
+                               double *logdet, int32_t *info, void *workspace,
+                               size_t workspace_bytes, void *stream);
+SELINV_API int selinv_junction_factor_f32(const selinv_junction_plan *plan, int64_t B,
+                               const float *diag, const float *edge_val, float *factor,
+                               double *logdet, int32_t *info, void *workspace,
+                               size_t workspace_bytes, void *stream);
+SELINV_API int selinv_junction_solve_f64(const selinv_junction_plan *plan, int64_t B,
+                              const double *factor, int64_t k, const double *y, double *x,
+                              void *stream);
+SELINV_API int selinv_junction_solve_f32(const selinv_junction_plan *plan, int64_t B,
+                              const float *factor, int64_t k, const float *y, float *x,
+                              void *stream);
+SELINV_API int selinv_junction_sample_f64(const selinv_junction_plan *plan, int64_t B,
+                               const double *factor, int64_t k, const double *z, double *x,
+                               void *stream);
+SELINV_API int selinv_junction_sample_f32(const selinv_junction_plan *plan, int64_t B,
+                               const float *factor, int64_t k, const float *z, float *x,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif

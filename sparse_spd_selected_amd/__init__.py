@@ -191,6 +191,16 @@ def lib():
         f = getattr(L, "selinv_junction_logdet_" + sfx)
         f.argtypes = [vp, i64] + [vp] * 4 + [vp, sz, vp]
         f.restype = ctypes.c_int
+        f = getattr(L, "selinv_junction_factor_" + sfx)
+        f.argtypes = [vp, i64] + [vp] * 5 + [vp, sz, vp]
+        f.restype = ctypes.c_int
+        for op in ("solve", "sample"):
+            f = getattr(L, "selinv_junction_%s_%s" % (op, sfx))
+            f.argtypes = [vp, i64, vp, i64, vp, vp, vp]
+            f.restype = ctypes.c_int
+    for name in ("selinv_junction_factor_bytes", "selinv_junction_factor_workspace_bytes"):
+        getattr(L, name).argtypes = [vp, i64]
+        getattr(L, name).restype = sz
     _lib = L
     return L
 
@@ -1243,3 +1253,86 @@ def junction_logdet(diag, edge_index, edge_val, order=None, check=False, return_
     if single:
         logdet, info = logdet[0], info[0]
     return (logdet, info) if return_info else logdet
+
+
+class JunctionFactor:
+    """Factor of general sparse SPD matrices on one pattern (see
+    junction_factor): log det, info, and the solve / sample sweeps."""
+
+    def __init__(self, plan, B, single, factor, logdet, info):
+        self.plan, self.B, self.single = plan, B, single
+        self.factor, self.logdet, self.info = factor, logdet, info
+
+    def _apply(self, v, name, sample):
+        dev, dt = self.factor.device, self.factor.dtype
+        if self.single:
+            v = _vec(v, name, dev, dt, (self.plan.n, self.plan.b)).unsqueeze(0)
+        else:
+            v = _vec(v, name, dev, dt, (self.B, self.plan.n, self.plan.b))
+        k = v.shape[-1]
+        x = torch.empty_like(v)
+        op = "sample" if sample else "solve"
+        sfx = _sfx(self.factor)
+        with torch.cuda.device(dev):
+            rc = getattr(lib(), "selinv_junction_%s_%s" % (op, sfx))(
+                self.plan.handle, self.B, _ptr(self.factor), k, _ptr(v), _ptr(x), _stream(dev))
+        _status(rc, "selinv_junction_%s_%s" % (op, sfx))
+        return x[0] if self.single else x
+
+    def solve(self, y):
+        """x = A^{-1} y, y [B, n, b, k] (or [n, b, k])."""
+        return self._apply(y, "y", False)
+
+    def sample(self, num_samples=None, z=None, generator=None):
+        """x = L^{-T} D^{-1/2} z ~ N(0, A^{-1}); z drawn here unless given."""
+        if z is None:
+            shape = (self.plan.n, self.plan.b, num_samples or 1)
+            if not self.single:
+                shape = (self.B,) + shape
+            z = _normal_like(shape, self.factor.dtype, self.factor.device, generator)
+        return self._apply(z, "z", True)
+
+
+def junction_factor(diag, edge_index, edge_val, order=None, plan: JunctionPlan | None = None):
+    """Sparse block Cholesky factorisation of general sparse SPD matrices
+    sharing one pattern (diag [B, n, b, b] or [n, b, b], edge_val as for
+    `junction`), kept for junction_solve / sampling; returns a
+    JunctionFactor with .logdet, .info, .solve(y) and .sample(...)."""
+    dt, dev = diag.dtype, diag.device
+    diag = _check_tensor(diag, "diag", dev, dt)
+    single = diag.dim() == 3
+    if single:
+        diag = diag.unsqueeze(0)
+        edge_val = edge_val.unsqueeze(0)
+    edge_val = _check_tensor(edge_val, "edge_val", dev, dt)
+    sfx = _sfx(diag)
+    if diag.dim() != 4 or diag.shape[2] != diag.shape[3]:
+        raise ValueError("diag must be [B, n, b, b]")
+    B, n, b = diag.shape[0], diag.shape[1], diag.shape[2]
+    if plan is None:
+        plan = junction_plan(n, edge_index, b, dt, dev, order)
+    if plan.n != n or plan.b != b or plan.dtype != dt:
+        raise ValueError("plan does not match (n, b, dtype)")
+    if edge_val.shape != (B, plan.m, b, b):
+        raise ValueError("edge_val must be [B, m, b, b]")
+    L_ = lib()
+    nbytes = int(L_.selinv_junction_factor_bytes(plan.handle, B))
+    factor = torch.empty(max(nbytes // diag.element_size(), 1), dtype=dt, device=dev)
+    logdet = torch.empty(B, dtype=torch.float64, device=dev)
+    info = torch.empty(B, dtype=torch.int32, device=dev)
+    nb = int(L_.selinv_junction_factor_workspace_bytes(plan.handle, B))
+    ws = _workspace(nb, dev)
+    with torch.cuda.device(dev):
+        rc = getattr(L_, "selinv_junction_factor_" + sfx)(
+            plan.handle, B, _ptr(diag), _ptr(edge_val) if plan.m else None, _ptr(factor),
+            logdet.data_ptr(), info.data_ptr(), _ptr(ws), nb, _stream(dev))
+    _status(rc, "selinv_junction_factor_" + sfx)
+    if single:
+        logdet, info = logdet[0], info[0]
+    return JunctionFactor(plan, B, single, factor, logdet, info)
+
+
+def junction_solve(diag, edge_index, edge_val, y, order=None, plan: JunctionPlan | None = None):
+    """x = A^{-1} y on a pattern (one or several right-hand sides, y
+    [B, n, b, k] or [n, b, k]); factorises, then solves."""
+    return junction_factor(diag, edge_index, edge_val, order, plan).solve(y)

@@ -31,6 +31,7 @@ SOURCES = [
     "vjp_tree_b8.hip", "vjp_chain_seg.hip",
     "shared_factor.hip", "chain_solve_b16.hip", "star_solve_b32.hip",
     "nonsym.hip", "bidiag_b16.hip", "nonsym_b8.hip", "junction_plan.cpp", "junction.hip",
+    "junction_solve.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

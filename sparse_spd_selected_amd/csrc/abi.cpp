@@ -350,6 +350,34 @@ int junction_logdet_entry(const selinv_junction_plan *plan, int64_t B, const T *
   return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
 }
 
+template <typename T>
+int junction_factor_entry(const selinv_junction_plan *plan, int64_t B, const T *diag,
+                          const T *edge_val, T *factor, double *logdet, int32_t *info, void *ws,
+                          size_t ws_bytes, void *stream) {
+  if (!plan || plan->dtype_bytes != static_cast<int>(sizeof(T))) return SELINV_ERR_INVALID_ARG;
+  if (B < 0 || B > 65535) return SELINV_ERR_INVALID_ARG;
+  if (B == 0) return SELINV_OK;
+  if (!diag || !factor || !logdet || (plan->m > 0 && !edge_val)) return SELINV_ERR_INVALID_ARG;
+  if (misaligned(diag) || misaligned(edge_val) || misaligned(factor)) return SELINV_ERR_INVALID_ARG;
+  const size_t need = selinv::junction_factor_workspace_bytes(plan, B);
+  if (ws_bytes < need || !ws || misaligned_ws(ws)) return SELINV_ERR_INVALID_ARG;
+  const hipError_t e = selinv::junction_factor_launch<T>(plan, B, diag, edge_val, factor, logdet,
+                                                         info, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
+}
+
+template <typename T>
+int junction_apply_entry(const selinv_junction_plan *plan, int64_t B, const T *factor, int64_t k,
+                         const T *in, T *out, bool sample, void *stream) {
+  if (!plan || plan->dtype_bytes != static_cast<int>(sizeof(T))) return SELINV_ERR_INVALID_ARG;
+  if (B < 0 || B > 65535 || k < 0) return SELINV_ERR_INVALID_ARG;
+  if (B == 0 || k == 0) return SELINV_OK;
+  if (!factor || !in || !out || in == out || misaligned(factor)) return SELINV_ERR_INVALID_ARG;
+  const hipError_t e = selinv::junction_apply_launch<T>(plan, B, factor, k, sample, in, out,
+                                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -366,6 +394,50 @@ int selinv_junction_logdet_f32(const selinv_junction_plan *plan, int64_t B, cons
                                void *workspace, size_t workspace_bytes, void *stream) {
   return junction_logdet_entry<float>(plan, B, diag, edge_val, logdet, info, workspace,
                                       workspace_bytes, stream);
+}
+
+size_t selinv_junction_factor_bytes(const selinv_junction_plan *plan, int64_t B) {
+  return (plan && B >= 0) ? selinv::junction_factor_bytes(plan, B) : 0;
+}
+
+size_t selinv_junction_factor_workspace_bytes(const selinv_junction_plan *plan, int64_t B) {
+  return (plan && B >= 0) ? selinv::junction_factor_workspace_bytes(plan, B) : 0;
+}
+
+int selinv_junction_factor_f64(const selinv_junction_plan *plan, int64_t B, const double *diag,
+                               const double *edge_val, double *factor, double *logdet,
+                               int32_t *info, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  return junction_factor_entry<double>(plan, B, diag, edge_val, factor, logdet, info, workspace,
+                                       workspace_bytes, stream);
+}
+
+int selinv_junction_factor_f32(const selinv_junction_plan *plan, int64_t B, const float *diag,
+                               const float *edge_val, float *factor, double *logdet,
+                               int32_t *info, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  return junction_factor_entry<float>(plan, B, diag, edge_val, factor, logdet, info, workspace,
+                                      workspace_bytes, stream);
+}
+
+int selinv_junction_solve_f64(const selinv_junction_plan *plan, int64_t B, const double *factor,
+                              int64_t k, const double *y, double *x, void *stream) {
+  return junction_apply_entry<double>(plan, B, factor, k, y, x, false, stream);
+}
+
+int selinv_junction_solve_f32(const selinv_junction_plan *plan, int64_t B, const float *factor,
+                              int64_t k, const float *y, float *x, void *stream) {
+  return junction_apply_entry<float>(plan, B, factor, k, y, x, false, stream);
+}
+
+int selinv_junction_sample_f64(const selinv_junction_plan *plan, int64_t B, const double *factor,
+                               int64_t k, const double *z, double *x, void *stream) {
+  return junction_apply_entry<double>(plan, B, factor, k, z, x, true, stream);
+}
+
+int selinv_junction_sample_f32(const selinv_junction_plan *plan, int64_t B, const float *factor,
+                               int64_t k, const float *z, float *x, void *stream) {
+  return junction_apply_entry<float>(plan, B, factor, k, z, x, true, stream);
 }
 
 size_t selinv_junction_workspace_bytes(const selinv_junction_plan *plan, int64_t B) {

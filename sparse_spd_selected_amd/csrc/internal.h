@@ -69,6 +69,8 @@ constexpr int kTreeTile = 8;  // positions per tile (one wavefront of the b <= 8
 //   gtab              -(label + 1) for a diagonal G block, else output
 //                     position * 2 + transpose
 //   poutenc           output code of every panel block (as gtab, -1 unused)
+//   row_node          label of every flat row (the solve sweeps)
+//   occ_ptr/occ_row   per flat column, the flat rows of the same node
 struct JunctionPlanDev {
   int32_t *order = nullptr;
   int32_t *ch_first = nullptr, *ch_s = nullptr, *ch_n = nullptr;
@@ -82,6 +84,7 @@ struct JunctionPlanDev {
   // target's only item); targets with several items per level; it_ptr[tg]
   int32_t *it_tg = nullptr, *it_lo = nullptr, *it_hi = nullptr, *it_slot = nullptr;
   int32_t *multi_tg = nullptr, *it_ptr = nullptr;
+  int32_t *row_node = nullptr, *occ_ptr = nullptr, *occ_row = nullptr;
 };
 
 }  // namespace selinv
@@ -295,6 +298,17 @@ template <typename T>
 hipError_t junction_launch(const selinv_junction_plan *plan, int64_t B, const T *diag,
                            const T *edge_val, T *G_diag, T *G_lower, double *logdet,
                            int32_t *info, void *ws, hipStream_t s);
+// the shared-factor siblings: the factorisation into a caller-owned factor
+// (junction.hip), then the solve / sample sweeps (junction_solve.hip)
+size_t junction_factor_workspace_bytes(const selinv_junction_plan *plan, int64_t B);
+size_t junction_factor_bytes(const selinv_junction_plan *plan, int64_t B);
+template <typename T>
+hipError_t junction_factor_launch(const selinv_junction_plan *plan, int64_t B, const T *diag,
+                                  const T *edge_val, T *factor, double *logdet, int32_t *info,
+                                  void *ws, hipStream_t s);
+template <typename T>
+hipError_t junction_apply_launch(const selinv_junction_plan *plan, int64_t B, const T *factor,
+                                 int64_t k, bool sample, const T *in, T *out, hipStream_t s);
 
 // ------------------------------------ non-symmetric ladder (nonsym.hip)
 size_t bidiag_workspace_bytes(int64_t B);

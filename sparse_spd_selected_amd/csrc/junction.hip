@@ -1163,12 +1163,13 @@ struct JtWs {
   size_t bytes;
 };
 
-JtWs carve(const selinv_junction_plan *plan, int64_t B, void *ws) {
+// ext_factor: W and RJ live in a caller-owned factor buffer (not carved)
+JtWs carve(const selinv_junction_plan *plan, int64_t B, void *ws, bool ext_factor = false) {
   const size_t bb = size_t(plan->b) * plan->b, es = plan->dtype_bytes;
   Carve cv(ws);
   JtWs w;
-  w.W = cv.take<char>(B * plan->npanel * bb * es);
-  w.RJ = cv.take<char>(B * plan->nrinv * bb * es);
+  w.W = ext_factor ? nullptr : cv.take<char>(B * plan->npanel * bb * es);
+  w.RJ = ext_factor ? nullptr : cv.take<char>(B * plan->nrinv * bb * es);
   w.Tpart = cv.take<char>(B * max_split_tiles(plan, B) * kTilePart * es);
   w.Dpart = cv.take<char>(B * max_split_cols(plan, B) * kDiagPart * es);
   w.Spart = cv.take<char>(B * plan->max_slots * bb * es);
@@ -1184,16 +1185,29 @@ size_t junction_workspace_bytes(const selinv_junction_plan *plan, int64_t B) {
   return carve(plan, B, nullptr).bytes;
 }
 
-// G_diag == nullptr: the factorisation alone (log det and info)
+size_t junction_factor_workspace_bytes(const selinv_junction_plan *plan, int64_t B) {
+  return carve(plan, B, nullptr, true).bytes;
+}
+
+// The factor a solve or a sample reads: every chunk's panel (the later rows
+// W_{N,J}; the pivot rows hold C_JJ) [B][npanel][b][b], then every chunk's
+// R_J^-1 (dense, row-major s b x s b) [B][nrinv][b][b].
+size_t junction_factor_bytes(const selinv_junction_plan *plan, int64_t B) {
+  return size_t(B) * (plan->npanel + plan->nrinv) * plan->b * plan->b * plan->dtype_bytes;
+}
+
+// G_diag == nullptr: the factorisation alone (log det and info); factor !=
+// nullptr: W and R_J^-1 are kept there (junction_factor_bytes layout)
 template <typename T, int BC>
 hipError_t junction_run(const selinv_junction_plan *plan, int64_t B, const T *diag,
                            const T *edge_val, T *G_diag, T *G_lower, double *logdet,
-                           int32_t *info, void *ws, hipStream_t s) {
+                           int32_t *info, void *ws, hipStream_t s, T *factor = nullptr) {
   const int b = plan->b, sm = plan->smax;
   const Dims d{plan->n, plan->m, plan->nnz, plan->nch, plan->npanel, plan->nrinv, b};
   const JunctionPlanDev &P = plan->dev;
-  const JtWs w = carve(plan, B, ws);
-  T *W = static_cast<T *>(w.W), *RJ = static_cast<T *>(w.RJ);
+  const JtWs w = carve(plan, B, ws, factor != nullptr);
+  T *W = factor ? factor : static_cast<T *>(w.W);
+  T *RJ = factor ? factor + B * plan->npanel * int64_t(b) * b : static_cast<T *>(w.RJ);
   const size_t l_upd = lds_bytes<T>(b), l_fac = fac_lds<T>(b, sm), l_scl = scale_lds<T>(b, sm),
                l_row = rows_lds<T>(b, sm), l_dia = diag_lds<T>(b, sm),
                l_sum = sizeof(T) * (size_t(kTilePart) + size_t(sm) * b * sm * b) +
@@ -1276,6 +1290,25 @@ hipError_t junction_launch(const selinv_junction_plan *plan, int64_t B, const T 
   }
 }
 
+// The factorisation alone, keeping W and R_J^-1 in `factor` for the sweeps
+template <typename T>
+hipError_t junction_factor_launch(const selinv_junction_plan *plan, int64_t B, const T *diag,
+                                  const T *edge_val, T *factor, double *logdet, int32_t *info,
+                                  void *ws, hipStream_t s) {
+  switch (plan->b) {
+    case 4: return junction_run<T, 4>(plan, B, diag, edge_val, nullptr, nullptr, logdet, info, ws, s, factor);
+    case 8: return junction_run<T, 8>(plan, B, diag, edge_val, nullptr, nullptr, logdet, info, ws, s, factor);
+    case 16: return junction_run<T, 16>(plan, B, diag, edge_val, nullptr, nullptr, logdet, info, ws, s, factor);
+    default: return junction_run<T, 0>(plan, B, diag, edge_val, nullptr, nullptr, logdet, info, ws, s, factor);
+  }
+}
+
+template hipError_t junction_factor_launch<double>(const selinv_junction_plan *, int64_t,
+                                                   const double *, const double *, double *,
+                                                   double *, int32_t *, void *, hipStream_t);
+template hipError_t junction_factor_launch<float>(const selinv_junction_plan *, int64_t,
+                                                  const float *, const float *, float *, double *,
+                                                  int32_t *, void *, hipStream_t);
 template hipError_t junction_launch<double>(const selinv_junction_plan *, int64_t, const double *,
                                             const double *, double *, double *, double *,
                                             int32_t *, void *, hipStream_t);

@@ -115,6 +115,9 @@ struct HostTables {
   Vec ch_first, ch_s, ch_n;
   std::vector<int64_t> ch_pbase, ch_rbase, ch_gptr, ch_tptr, rows_ptr, ch_cptr, tiles_ptr;
   Vec row_chunk, col_chunk, tile_chunk, tg_chunk, tg_rc, ain, fpair, gtab, poutenc;
+  // solve sweeps: the label of every flat row, and per flat column the flat
+  // rows whose node is that column's node (in flat-row order)
+  Vec row_node, occ_ptr, occ_row;
   std::vector<int64_t> fptr;
   // Schur-sum work items: each target's pair list cut into runs of at most
   // kItemPairs; targets with several items add partial sums (slots)
@@ -316,6 +319,31 @@ int analyze(int64_t n, int64_t m, const int32_t *edge_index_host, const int32_t 
         h.poutenc[h.ch_pbase[id] + r * sz + col] = code;
       }
   }
+  // ---- solve sweeps: node of every flat row; flat rows by their node's
+  // flat column (chunk id order, then column)
+  h.row_node.resize(h.rows_ptr[nch]);
+  h.occ_ptr.assign(n + 1, 0);
+  auto flat_col = [&](int32_t wpos) -> int64_t {
+    const int64_t c = chunk_of[wpos];
+    return h.ch_cptr[id_of[c]] + (wpos - chunks[c].first);
+  };
+  for (int64_t id = 0; id < nch; ++id) {
+    const Vec &N = below(chunk_at[id]);
+    for (size_t a = 0; a < N.size(); ++a) {
+      h.row_node[h.rows_ptr[id] + a] = order[N[a]];
+      h.occ_ptr[flat_col(N[a]) + 1]++;
+    }
+  }
+  for (int64_t c = 0; c < n; ++c) h.occ_ptr[c + 1] += h.occ_ptr[c];
+  h.occ_row.resize(h.rows_ptr[nch]);
+  {
+    Vec next(h.occ_ptr.begin(), h.occ_ptr.end() - 1);
+    for (int64_t id = 0; id < nch; ++id) {
+      const Vec &N = below(chunk_at[id]);
+      for (size_t a = 0; a < N.size(); ++a)
+        h.occ_row[next[flat_col(N[a])]++] = static_cast<int32_t>(h.rows_ptr[id] + a);
+    }
+  }
   // ---- forward targets: every panel block (r >= col), chunk by chunk
   const int64_t ntg = h.ch_tptr[nch];
   h.tg_chunk.resize(ntg);
@@ -494,7 +522,8 @@ extern "C" int selinv_junction_plan_create(int64_t n, int64_t m, const int32_t *
                        3 * align_up(h.ntg * i4) + align_up((h.ntg + 1) * i4) +
                        align_up(2 * h.npairs * i4) + align_up(h.ng * i4) +
                        align_up(h.npanel * i4) + 4 * align_up(h.nitems * i4) +
-                       align_up(h.multi_tg.size() * i4) + align_up((h.ntg + 1) * i4) + 4096;
+                       align_up(h.multi_tg.size() * i4) + align_up((h.ntg + 1) * i4) +
+                       2 * align_up(h.nrows * i4) + align_up((n + 1) * i4) + 4096;
   if (hipMalloc(&plan->dev_block, bytes) != hipSuccess) {
     delete plan;
     return SELINV_ERR_HIP;
@@ -527,6 +556,9 @@ extern "C" int selinv_junction_plan_create(int64_t n, int64_t m, const int32_t *
   dv.it_slot = cv.take<int32_t>(h.nitems);
   dv.multi_tg = cv.take<int32_t>(h.multi_tg.size());
   dv.it_ptr = cv.take<int32_t>(h.ntg + 1);
+  dv.row_node = cv.take<int32_t>(h.nrows);
+  dv.occ_ptr = cv.take<int32_t>(n + 1);
+  dv.occ_row = cv.take<int32_t>(h.nrows);
   std::vector<int32_t> itptr32(h.ntg + 1);
   for (int64_t t = 0; t <= h.ntg; ++t) itptr32[t] = static_cast<int32_t>(h.it_ptr[t]);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -560,6 +592,9 @@ extern "C" int selinv_junction_plan_create(int64_t n, int64_t m, const int32_t *
   up(dv.it_slot, h.it_slot.data(), h.nitems * i4);
   up(dv.multi_tg, h.multi_tg.data(), h.multi_tg.size() * i4);
   up(dv.it_ptr, itptr32.data(), (h.ntg + 1) * i4);
+  up(dv.row_node, h.row_node.data(), h.nrows * i4);
+  up(dv.occ_ptr, h.occ_ptr.data(), (n + 1) * i4);
+  up(dv.occ_row, h.occ_row.data(), h.nrows * i4);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) {
     selinv_junction_plan_destroy(plan);

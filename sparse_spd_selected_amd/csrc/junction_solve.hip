@@ -1,0 +1,217 @@
+// junction_solve.hip -- solve and Gaussian sampling on the filled pattern of
+// a junction plan, from the factor its factorisation leaves behind
+// (gabp-sparse-inv page, junction-tree section: junction_solve with one or
+// several right-hand sides, and Gaussian sampling, both reusing the
+// factorisation of the selected inverse).
+//
+// The factor is the Cholesky form the factorisation kernels compute,
+// A = L~ L~^T with, per chunk J (s consecutive supernode columns), the dense
+// pivot factor R_J (kept as R_J^-1) and the later rows W_{N,J} = C_{N,J} R_J^-T:
+//   forward, chunk levels upward (children first):
+//       z_J = R_J^-1 (y_J - sum_K W_{J,K} z_K)
+//   over the earlier chunks K whose later rows hold nodes of J;
+//   backward, chunk levels downward (root first):
+//       x_J = R_J^-T (v_J - W_{N,J}^T x_N)
+// with v = z for a solve (x = A^-1 y) and v = the caller's z for a sample
+// (x = L~^-T z, so Cov x = L~^-T L~^-1 = A^-1 for z ~ N(0, I)).  L~'s
+// diagonal blocks are the Cholesky factors R_v of the node pivots D_v (the
+// Cholesky factor of A in the elimination order is unique), so the sample is
+// x = L^-T D^-1/2 z with D^-1/2_v = R_v^-T, as for chains, stars and trees.
+//
+// One workgroup per (chunk, matrix, tile of right-hand sides) and level.
+// Thread e of the first s b kt threads owns entry (I, kc) of the chunk's
+// s b x kt tile; the workgroup's other threads form further groups that split
+// the sum over occurrences (forward) or later rows (backward), and the groups'
+// partial sums are added in a fixed order, so results are deterministic.
+// Vectors are [B][n][b][k] by label, k fastest: consecutive threads read
+// consecutive right-hand sides.  The solve keeps z in the output (the
+// backward pass of chunk J reads z_J before any thread writes x_J, and no
+// chunk of the same level reads J's nodes), so it needs no workspace.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace selinv {
+namespace {
+
+constexpr int kST = 256;  // threads per workgroup
+
+struct SDims {
+  int64_t n, npanel, nrinv, k;
+  int kt, b;
+};
+
+// The chunk's tile: R_J^-1 staged in LDS, the thread's entry and group.
+template <typename T>
+struct Tile {
+  int64_t id, mat, koff;
+  int s, sb, f, kt, ne, G, g, I, kc, c, i;
+};
+
+template <typename T, int BC>
+__device__ inline Tile<T> tile_setup(const JunctionPlanDev &P, const SDims &d, int64_t cbase,
+                                     const T *RJ, T *Ri) {
+  Tile<T> q;
+  const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
+  q.id = cbase + blockIdx.x;
+  q.mat = blockIdx.y;
+  const int64_t k0 = int64_t(blockIdx.z) * d.kt;
+  q.kt = d.k - k0 < d.kt ? static_cast<int>(d.k - k0) : d.kt;
+  q.s = P.ch_s[q.id];
+  q.sb = q.s * b;
+  q.f = P.ch_first[q.id];
+  const T *Rj = RJ + (q.mat * d.nrinv + P.ch_rbase[q.id]) * bb;
+  for (int e = t; e < q.sb * q.sb; e += kST) Ri[e] = Rj[e];
+  q.ne = q.sb * q.kt;
+  q.G = kST / q.ne;
+  q.g = t / q.ne;
+  const int e = t - q.g * q.ne;
+  q.I = e / q.kt;
+  q.kc = e - q.I * q.kt;
+  q.c = q.I / b;
+  q.i = q.I - q.c * b;
+  q.koff = k0 + q.kc;
+  return q;
+}
+
+// Forward level: z_J = R_J^-1 (y_J - sum_K W_{J,K} z_K)
+template <typename T, int BC>
+__global__ void __launch_bounds__(kST) js_forward(JunctionPlanDev P, SDims d, int64_t cbase,
+                                                  const T *__restrict__ W,
+                                                  const T *__restrict__ RJ,
+                                                  const T *__restrict__ y, T *z) {
+  extern __shared__ char smem_raw[];
+  T *Ri = reinterpret_cast<T *>(smem_raw);
+  const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
+  const Tile<T> q = tile_setup<T, BC>(P, d, cbase, RJ, Ri);
+  T *part = Ri + q.sb * q.sb, *rs = part + kST;
+  const int64_t k = d.k;
+  if (q.g < q.G) {
+    const T *Wm = W + q.mat * d.npanel * bb;
+    const T *zm = z + q.mat * d.n * b * k + q.koff;
+    const int64_t fc = P.ch_cptr[q.id] + q.c;
+    const int32_t o0 = P.occ_ptr[fc], o1 = P.occ_ptr[fc + 1];
+    T acc = T(0);
+    for (int32_t o = o0 + q.g; o < o1; o += q.G) {
+      const int32_t r = P.occ_row[o], K = P.row_chunk[r];
+      const int sK = P.ch_s[K], fK = P.ch_first[K];
+      const int a = static_cast<int>(r - P.rows_ptr[K]);
+      // row a of K's panel: sK blocks W_{j, u_cc}, this thread's row i
+      const T *Wr = Wm + (P.ch_pbase[K] + int64_t(sK + a) * sK) * bb + q.i * b;
+      for (int cc = 0; cc < sK; ++cc) {
+        const T *zu = zm + int64_t(P.order[fK + cc]) * b * k;
+        const T *Wb = Wr + cc * bb;
+#pragma unroll
+        for (int l = 0; l < b; ++l) acc += Wb[l] * zu[l * k];
+      }
+    }
+    part[q.g * q.ne + (t - q.g * q.ne)] = acc;
+  }
+  __syncthreads();
+  const int64_t node = P.order[q.f + q.c];
+  const int64_t at = ((q.mat * d.n + node) * b + q.i) * k + q.koff;
+  if (t < q.ne) {
+    T v = T(0);
+    for (int gg = 0; gg < q.G; ++gg) v += part[gg * q.ne + t];
+    rs[t] = y[at] - v;
+  }
+  __syncthreads();
+  if (t < q.ne) {
+    T v = T(0);
+    for (int K = 0; K <= q.I; ++K) v += Ri[q.I * q.sb + K] * rs[K * q.kt + q.kc];
+    z[at] = v;
+  }
+}
+
+// Backward level: x_J = R_J^-T (v_J - W_{N,J}^T x_N).  v may be x itself
+// (the solve): the tile reads v_J before the barrier that precedes its
+// writes, and no other workgroup of the level touches J's nodes.
+template <typename T, int BC>
+__global__ void __launch_bounds__(kST) js_backward(JunctionPlanDev P, SDims d, int64_t cbase,
+                                                   const T *__restrict__ W,
+                                                   const T *__restrict__ RJ, const T *v,
+                                                   T *x) {
+  extern __shared__ char smem_raw[];
+  T *Ri = reinterpret_cast<T *>(smem_raw);
+  const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
+  const Tile<T> q = tile_setup<T, BC>(P, d, cbase, RJ, Ri);
+  T *part = Ri + q.sb * q.sb, *rs = part + kST;
+  const int64_t k = d.k;
+  const int l = q.i;  // entry I = c b + l of the chunk's columns
+  if (q.g < q.G) {
+    const int nr = P.ch_n[q.id];
+    const int64_t rb = P.rows_ptr[q.id];
+    // column l of block (a, c) of the panel: stride b down its rows
+    const T *Wc = W + (q.mat * d.npanel + P.ch_pbase[q.id] + int64_t(q.s) * q.s + q.c) * bb + l;
+    const T *xm = x + q.mat * d.n * b * k + q.koff;
+    T acc = T(0);
+    for (int a = q.g; a < nr; a += q.G) {
+      const T *Wb = Wc + int64_t(a) * q.s * bb;
+      const T *xw = xm + int64_t(P.row_node[rb + a]) * b * k;
+#pragma unroll
+      for (int i = 0; i < b; ++i) acc += Wb[i * b] * xw[i * k];
+    }
+    part[q.g * q.ne + (t - q.g * q.ne)] = acc;
+  }
+  __syncthreads();
+  const int64_t node = P.order[q.f + q.c];
+  const int64_t at = ((q.mat * d.n + node) * b + l) * k + q.koff;
+  if (t < q.ne) {
+    T s = T(0);
+    for (int gg = 0; gg < q.G; ++gg) s += part[gg * q.ne + t];
+    rs[t] = v[at] - s;
+  }
+  __syncthreads();
+  if (t < q.ne) {
+    T s = T(0);
+    for (int K = q.I; K < q.sb; ++K) s += Ri[K * q.sb + q.I] * rs[K * q.kt + q.kc];
+    x[at] = s;
+  }
+}
+
+template <typename T, int BC>
+hipError_t apply_run(const selinv_junction_plan *plan, int64_t B, const T *factor, int64_t k,
+                     bool sample, const T *in, T *out, hipStream_t s) {
+  const int b = plan->b, sbm = plan->smax * b;
+  if (sbm > kST) return hipErrorInvalidValue;
+  const int64_t ktl = kST / sbm;
+  const int kt = static_cast<int>(k < ktl ? k : ktl);
+  const int64_t nkt = (k + kt - 1) / kt;
+  if (nkt > 65535) return hipErrorInvalidValue;
+  const SDims d{plan->n, plan->npanel, plan->nrinv, k, kt, b};
+  const T *W = factor, *RJ = factor + B * plan->npanel * int64_t(b) * b;
+  const size_t lds = sizeof(T) * (size_t(sbm) * sbm + 2 * kST);
+  const auto &lo = plan->level_off;
+  const unsigned By = static_cast<unsigned>(B), Z = static_cast<unsigned>(nkt);
+  if (!sample)
+    for (int32_t l = 0; l < plan->levels; ++l)
+      js_forward<T, BC><<<dim3(static_cast<unsigned>(lo[l + 1] - lo[l]), By, Z), dim3(kST), lds,
+                          s>>>(plan->dev, d, lo[l], W, RJ, in, out);
+  const T *v = sample ? in : out;
+  for (int32_t l = plan->levels - 1; l >= 0; --l)
+    js_backward<T, BC><<<dim3(static_cast<unsigned>(lo[l + 1] - lo[l]), By, Z), dim3(kST), lds,
+                         s>>>(plan->dev, d, lo[l], W, RJ, v, out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t junction_apply_launch(const selinv_junction_plan *plan, int64_t B, const T *factor,
+                                 int64_t k, bool sample, const T *in, T *out, hipStream_t s) {
+  switch (plan->b) {
+    case 4: return apply_run<T, 4>(plan, B, factor, k, sample, in, out, s);
+    case 8: return apply_run<T, 8>(plan, B, factor, k, sample, in, out, s);
+    case 16: return apply_run<T, 16>(plan, B, factor, k, sample, in, out, s);
+    default: return apply_run<T, 0>(plan, B, factor, k, sample, in, out, s);
+  }
+}
+
+template hipError_t junction_apply_launch<double>(const selinv_junction_plan *, int64_t,
+                                                  const double *, int64_t, bool, const double *,
+                                                  double *, hipStream_t);
+template hipError_t junction_apply_launch<float>(const selinv_junction_plan *, int64_t,
+                                                 const float *, int64_t, bool, const float *,
+                                                 float *, hipStream_t);
+
+}  // namespace selinv
