@@ -556,7 +556,9 @@ SELINV_API int selinv_junction_logdet_f32(const selinv_junction_plan *plan, int6
  *     Vectors by node label, k fastest, no alignment requirement; x must not
  *     alias y / z (x == y is rejected).  The factor must come from a factor
  *     call with the same plan and B; where that call reported info != 0 for
- *     a matrix, that matrix's x is unspecified.  No workspace. */
+ *     a matrix, that matrix's x is unspecified.  The solve's workspace:
+ *     selinv_junction_solve_workspace_bytes(plan, B, k) (per later row of
+ *     every chunk a b x k vector); the sample needs none. */
 SELINV_API size_t selinv_junction_factor_bytes(const selinv_junction_plan *plan, int64_t B);
 SELINV_API size_t selinv_junction_factor_workspace_bytes(const selinv_junction_plan *plan,
                                                         int64_t B);
@@ -568,12 +570,14 @@ SELINV_API int selinv_junction_factor_f32(const selinv_junction_plan *plan, int6
                                const float *diag, const float *edge_val, float *factor,
                                double *logdet, int32_t *info, void *workspace,
                                size_t workspace_bytes, void *stream);
+SELINV_API size_t selinv_junction_solve_workspace_bytes(const selinv_junction_plan *plan,
+                                                       int64_t B, int64_t k);
 SELINV_API int selinv_junction_solve_f64(const selinv_junction_plan *plan, int64_t B,
                               const double *factor, int64_t k, const double *y, double *x,
-                              void *stream);
+                              void *workspace, size_t workspace_bytes, void *stream);
 SELINV_API int selinv_junction_solve_f32(const selinv_junction_plan *plan, int64_t B,
                               const float *factor, int64_t k, const float *y, float *x,
-                              void *stream);
+                              void *workspace, size_t workspace_bytes, void *stream);
 SELINV_API int selinv_junction_sample_f64(const selinv_junction_plan *plan, int64_t B,
                                const double *factor, int64_t k, const double *z, double *x,
                                void *stream);

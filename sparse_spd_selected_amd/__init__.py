@@ -194,10 +194,14 @@ def lib():
         f = getattr(L, "selinv_junction_factor_" + sfx)
         f.argtypes = [vp, i64] + [vp] * 5 + [vp, sz, vp]
         f.restype = ctypes.c_int
-        for op in ("solve", "sample"):
-            f = getattr(L, "selinv_junction_%s_%s" % (op, sfx))
-            f.argtypes = [vp, i64, vp, i64, vp, vp, vp]
-            f.restype = ctypes.c_int
+        f = getattr(L, "selinv_junction_solve_" + sfx)
+        f.argtypes = [vp, i64, vp, i64, vp, vp, vp, sz, vp]
+        f.restype = ctypes.c_int
+        f = getattr(L, "selinv_junction_sample_" + sfx)
+        f.argtypes = [vp, i64, vp, i64, vp, vp, vp]
+        f.restype = ctypes.c_int
+    L.selinv_junction_solve_workspace_bytes.argtypes = [vp, i64, i64]
+    L.selinv_junction_solve_workspace_bytes.restype = sz
     for name in ("selinv_junction_factor_bytes", "selinv_junction_factor_workspace_bytes"):
         getattr(L, name).argtypes = [vp, i64]
         getattr(L, name).restype = sz
@@ -1274,8 +1278,16 @@ class JunctionFactor:
         op = "sample" if sample else "solve"
         sfx = _sfx(self.factor)
         with torch.cuda.device(dev):
-            rc = getattr(lib(), "selinv_junction_%s_%s" % (op, sfx))(
-                self.plan.handle, self.B, _ptr(self.factor), k, _ptr(v), _ptr(x), _stream(dev))
+            if sample:
+                rc = getattr(lib(), "selinv_junction_sample_" + sfx)(
+                    self.plan.handle, self.B, _ptr(self.factor), k, _ptr(v), _ptr(x),
+                    _stream(dev))
+            else:
+                nb = int(lib().selinv_junction_solve_workspace_bytes(self.plan.handle, self.B, k))
+                ws = _workspace(nb, dev)
+                rc = getattr(lib(), "selinv_junction_solve_" + sfx)(
+                    self.plan.handle, self.B, _ptr(self.factor), k, _ptr(v), _ptr(x), _ptr(ws),
+                    nb, _stream(dev))
         _status(rc, "selinv_junction_%s_%s" % (op, sfx))
         return x[0] if self.single else x
 

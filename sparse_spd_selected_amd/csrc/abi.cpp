@@ -368,12 +368,17 @@ int junction_factor_entry(const selinv_junction_plan *plan, int64_t B, const T *
 
 template <typename T>
 int junction_apply_entry(const selinv_junction_plan *plan, int64_t B, const T *factor, int64_t k,
-                         const T *in, T *out, bool sample, void *stream) {
+                         const T *in, T *out, void *ws, size_t ws_bytes, bool sample,
+                         void *stream) {
   if (!plan || plan->dtype_bytes != static_cast<int>(sizeof(T))) return SELINV_ERR_INVALID_ARG;
   if (B < 0 || B > 65535 || k < 0) return SELINV_ERR_INVALID_ARG;
   if (B == 0 || k == 0) return SELINV_OK;
   if (!factor || !in || !out || in == out || misaligned(factor)) return SELINV_ERR_INVALID_ARG;
-  const hipError_t e = selinv::junction_apply_launch<T>(plan, B, factor, k, sample, in, out,
+  if (!sample) {
+    const size_t need = selinv::junction_solve_workspace_bytes(plan, B, k);
+    if (ws_bytes < need || (need && (!ws || misaligned_ws(ws)))) return SELINV_ERR_INVALID_ARG;
+  }
+  const hipError_t e = selinv::junction_apply_launch<T>(plan, B, factor, k, sample, in, out, ws,
                                                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SELINV_OK : SELINV_ERR_HIP;
 }
@@ -420,24 +425,33 @@ int selinv_junction_factor_f32(const selinv_junction_plan *plan, int64_t B, cons
                                       workspace_bytes, stream);
 }
 
+size_t selinv_junction_solve_workspace_bytes(const selinv_junction_plan *plan, int64_t B,
+                                             int64_t k) {
+  return (plan && B >= 0 && k >= 0) ? selinv::junction_solve_workspace_bytes(plan, B, k) : 0;
+}
+
 int selinv_junction_solve_f64(const selinv_junction_plan *plan, int64_t B, const double *factor,
-                              int64_t k, const double *y, double *x, void *stream) {
-  return junction_apply_entry<double>(plan, B, factor, k, y, x, false, stream);
+                              int64_t k, const double *y, double *x, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  return junction_apply_entry<double>(plan, B, factor, k, y, x, workspace, workspace_bytes, false,
+                                      stream);
 }
 
 int selinv_junction_solve_f32(const selinv_junction_plan *plan, int64_t B, const float *factor,
-                              int64_t k, const float *y, float *x, void *stream) {
-  return junction_apply_entry<float>(plan, B, factor, k, y, x, false, stream);
+                              int64_t k, const float *y, float *x, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  return junction_apply_entry<float>(plan, B, factor, k, y, x, workspace, workspace_bytes, false,
+                                     stream);
 }
 
 int selinv_junction_sample_f64(const selinv_junction_plan *plan, int64_t B, const double *factor,
                                int64_t k, const double *z, double *x, void *stream) {
-  return junction_apply_entry<double>(plan, B, factor, k, z, x, true, stream);
+  return junction_apply_entry<double>(plan, B, factor, k, z, x, nullptr, 0, true, stream);
 }
 
 int selinv_junction_sample_f32(const selinv_junction_plan *plan, int64_t B, const float *factor,
                                int64_t k, const float *z, float *x, void *stream) {
-  return junction_apply_entry<float>(plan, B, factor, k, z, x, true, stream);
+  return junction_apply_entry<float>(plan, B, factor, k, z, x, nullptr, 0, true, stream);
 }
 
 size_t selinv_junction_workspace_bytes(const selinv_junction_plan *plan, int64_t B) {

@@ -306,9 +306,11 @@ template <typename T>
 hipError_t junction_factor_launch(const selinv_junction_plan *plan, int64_t B, const T *diag,
                                   const T *edge_val, T *factor, double *logdet, int32_t *info,
                                   void *ws, hipStream_t s);
+size_t junction_solve_workspace_bytes(const selinv_junction_plan *plan, int64_t B, int64_t k);
 template <typename T>
 hipError_t junction_apply_launch(const selinv_junction_plan *plan, int64_t B, const T *factor,
-                                 int64_t k, bool sample, const T *in, T *out, hipStream_t s);
+                                 int64_t k, bool sample, const T *in, T *out, void *ws,
+                                 hipStream_t s);
 
 // ------------------------------------ non-symmetric ladder (nonsym.hip)
 size_t bidiag_workspace_bytes(int64_t B);

@@ -18,6 +18,15 @@
 // Cholesky factor of A in the elimination order is unique), so the sample is
 // x = L^-T D^-1/2 z with D^-1/2_v = R_v^-T, as for chains, stars and trees.
 //
+// Forward as producer and consumer: once chunk K has z_K, the same
+// workgroup multiplies it into every later row a of K's panel and stores
+// u_a = W_{a,K} z_K (b x k) in a row buffer (one slot per later row, so no
+// two workgroups write one slot).  A later chunk J then only adds, for each
+// of its nodes, the b-vectors of the rows that hold that node (occ_ptr /
+// occ_row, in a fixed order); the matrix-vector work runs where the rows are
+// produced, spread over all rows of a level instead of serialised on the
+// few separator chunks whose nodes occur in many panels.
+//
 // One workgroup per (chunk, matrix, tile of right-hand sides) and level.
 // Thread e of the first s b kt threads owns entry (I, kc) of the chunk's
 // s b x kt tile; the workgroup's other threads form further groups that split
@@ -26,7 +35,8 @@
 // Vectors are [B][n][b][k] by label, k fastest: consecutive threads read
 // consecutive right-hand sides.  The solve keeps z in the output (the
 // backward pass of chunk J reads z_J before any thread writes x_J, and no
-// chunk of the same level reads J's nodes), so it needs no workspace.
+// chunk of the same level reads J's nodes); its workspace is the row buffer
+// [B][rows][b][k].  The sample runs the backward pass alone, without one.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -37,7 +47,7 @@ namespace {
 constexpr int kST = 256;  // threads per workgroup
 
 struct SDims {
-  int64_t n, npanel, nrinv, k;
+  int64_t n, npanel, nrinv, nrows, k;
   int kt, b;
 };
 
@@ -74,37 +84,26 @@ __device__ inline Tile<T> tile_setup(const JunctionPlanDev &P, const SDims &d, i
   return q;
 }
 
-// Forward level: z_J = R_J^-1 (y_J - sum_K W_{J,K} z_K)
+// Forward level: z_J = R_J^-1 (y_J - sum of the row vectors of J's nodes),
+// then u_a = W_{a,J} z_J for every later row a of J into the row buffer U
 template <typename T, int BC>
 __global__ void __launch_bounds__(kST) js_forward(JunctionPlanDev P, SDims d, int64_t cbase,
                                                   const T *__restrict__ W,
                                                   const T *__restrict__ RJ,
-                                                  const T *__restrict__ y, T *z) {
+                                                  const T *__restrict__ y, T *z, T *U) {
   extern __shared__ char smem_raw[];
   T *Ri = reinterpret_cast<T *>(smem_raw);
   const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
   const Tile<T> q = tile_setup<T, BC>(P, d, cbase, RJ, Ri);
   T *part = Ri + q.sb * q.sb, *rs = part + kST;
-  const int64_t k = d.k;
+  const int64_t k = d.k, k0 = q.koff - q.kc;
+  const T *Um = U + q.mat * d.nrows * b * k;
   if (q.g < q.G) {
-    const T *Wm = W + q.mat * d.npanel * bb;
-    const T *zm = z + q.mat * d.n * b * k + q.koff;
     const int64_t fc = P.ch_cptr[q.id] + q.c;
     const int32_t o0 = P.occ_ptr[fc], o1 = P.occ_ptr[fc + 1];
+    const T *Ui = Um + int64_t(q.i) * k + q.koff;
     T acc = T(0);
-    for (int32_t o = o0 + q.g; o < o1; o += q.G) {
-      const int32_t r = P.occ_row[o], K = P.row_chunk[r];
-      const int sK = P.ch_s[K], fK = P.ch_first[K];
-      const int a = static_cast<int>(r - P.rows_ptr[K]);
-      // row a of K's panel: sK blocks W_{j, u_cc}, this thread's row i
-      const T *Wr = Wm + (P.ch_pbase[K] + int64_t(sK + a) * sK) * bb + q.i * b;
-      for (int cc = 0; cc < sK; ++cc) {
-        const T *zu = zm + int64_t(P.order[fK + cc]) * b * k;
-        const T *Wb = Wr + cc * bb;
-#pragma unroll
-        for (int l = 0; l < b; ++l) acc += Wb[l] * zu[l * k];
-      }
-    }
+    for (int32_t o = o0 + q.g; o < o1; o += q.G) acc += Ui[int64_t(P.occ_row[o]) * b * k];
     part[q.g * q.ne + (t - q.g * q.ne)] = acc;
   }
   __syncthreads();
@@ -116,10 +115,28 @@ __global__ void __launch_bounds__(kST) js_forward(JunctionPlanDev P, SDims d, in
     rs[t] = y[at] - v;
   }
   __syncthreads();
+  T zv = T(0);
   if (t < q.ne) {
-    T v = T(0);
-    for (int K = 0; K <= q.I; ++K) v += Ri[q.I * q.sb + K] * rs[K * q.kt + q.kc];
-    z[at] = v;
+    for (int K = 0; K <= q.I; ++K) zv += Ri[q.I * q.sb + K] * rs[K * q.kt + q.kc];
+    z[at] = zv;
+  }
+  __syncthreads();
+  if (t < q.ne) rs[t] = zv;  // z_J, s b x kt
+  __syncthreads();
+  // the later rows' vectors: entry (a, i, kc) = sum_I W_{a,J}[i][I] z_J[I][kc]
+  const int nr = P.ch_n[q.id], per = b * q.kt;
+  const T *Wp = W + (q.mat * d.npanel + P.ch_pbase[q.id] + int64_t(q.s) * q.s) * bb;
+  T *Ur = U + (q.mat * d.nrows + P.rows_ptr[q.id]) * b * k + k0;
+  for (int e = t; e < nr * per; e += kST) {
+    const int a = e / per, rem = e - a * per, i = rem / q.kt, kc = rem - i * q.kt;
+    const T *Wa = Wp + int64_t(a) * q.s * bb + i * b;
+    T acc = T(0);
+    for (int c = 0; c < q.s; ++c) {
+      const T *Wb = Wa + c * bb, *zc = rs + c * b * q.kt + kc;
+#pragma unroll
+      for (int l = 0; l < b; ++l) acc += Wb[l] * zc[l * q.kt];
+    }
+    Ur[(int64_t(a) * b + i) * k + kc] = acc;
   }
 }
 
@@ -171,14 +188,14 @@ __global__ void __launch_bounds__(kST) js_backward(JunctionPlanDev P, SDims d, i
 
 template <typename T, int BC>
 hipError_t apply_run(const selinv_junction_plan *plan, int64_t B, const T *factor, int64_t k,
-                     bool sample, const T *in, T *out, hipStream_t s) {
+                     bool sample, const T *in, T *out, void *ws, hipStream_t s) {
   const int b = plan->b, sbm = plan->smax * b;
   if (sbm > kST) return hipErrorInvalidValue;
   const int64_t ktl = kST / sbm;
   const int kt = static_cast<int>(k < ktl ? k : ktl);
   const int64_t nkt = (k + kt - 1) / kt;
   if (nkt > 65535) return hipErrorInvalidValue;
-  const SDims d{plan->n, plan->npanel, plan->nrinv, k, kt, b};
+  const SDims d{plan->n, plan->npanel, plan->nrinv, plan->rows_ptr[plan->nch], k, kt, b};
   const T *W = factor, *RJ = factor + B * plan->npanel * int64_t(b) * b;
   const size_t lds = sizeof(T) * (size_t(sbm) * sbm + 2 * kST);
   const auto &lo = plan->level_off;
@@ -186,7 +203,7 @@ hipError_t apply_run(const selinv_junction_plan *plan, int64_t B, const T *facto
   if (!sample)
     for (int32_t l = 0; l < plan->levels; ++l)
       js_forward<T, BC><<<dim3(static_cast<unsigned>(lo[l + 1] - lo[l]), By, Z), dim3(kST), lds,
-                          s>>>(plan->dev, d, lo[l], W, RJ, in, out);
+                          s>>>(plan->dev, d, lo[l], W, RJ, in, out, static_cast<T *>(ws));
   const T *v = sample ? in : out;
   for (int32_t l = plan->levels - 1; l >= 0; --l)
     js_backward<T, BC><<<dim3(static_cast<unsigned>(lo[l + 1] - lo[l]), By, Z), dim3(kST), lds,
@@ -196,22 +213,27 @@ hipError_t apply_run(const selinv_junction_plan *plan, int64_t B, const T *facto
 
 }  // namespace
 
+size_t junction_solve_workspace_bytes(const selinv_junction_plan *plan, int64_t B, int64_t k) {
+  return size_t(B) * plan->rows_ptr[plan->nch] * plan->b * size_t(k) * plan->dtype_bytes;
+}
+
 template <typename T>
 hipError_t junction_apply_launch(const selinv_junction_plan *plan, int64_t B, const T *factor,
-                                 int64_t k, bool sample, const T *in, T *out, hipStream_t s) {
+                                 int64_t k, bool sample, const T *in, T *out, void *ws,
+                                 hipStream_t s) {
   switch (plan->b) {
-    case 4: return apply_run<T, 4>(plan, B, factor, k, sample, in, out, s);
-    case 8: return apply_run<T, 8>(plan, B, factor, k, sample, in, out, s);
-    case 16: return apply_run<T, 16>(plan, B, factor, k, sample, in, out, s);
-    default: return apply_run<T, 0>(plan, B, factor, k, sample, in, out, s);
+    case 4: return apply_run<T, 4>(plan, B, factor, k, sample, in, out, ws, s);
+    case 8: return apply_run<T, 8>(plan, B, factor, k, sample, in, out, ws, s);
+    case 16: return apply_run<T, 16>(plan, B, factor, k, sample, in, out, ws, s);
+    default: return apply_run<T, 0>(plan, B, factor, k, sample, in, out, ws, s);
   }
 }
 
 template hipError_t junction_apply_launch<double>(const selinv_junction_plan *, int64_t,
                                                   const double *, int64_t, bool, const double *,
-                                                  double *, hipStream_t);
+                                                  double *, void *, hipStream_t);
 template hipError_t junction_apply_launch<float>(const selinv_junction_plan *, int64_t,
                                                  const float *, int64_t, bool, const float *,
-                                                 float *, hipStream_t);
+                                                 float *, void *, hipStream_t);
 
 }  // namespace selinv

@@ -158,19 +158,26 @@ def test_repeated_calls_are_bitwise_identical(ssa):
 
 
 def test_abi_arguments(ssa):
-    """Status codes of the C entry points: k = 0 and B = 0 do nothing, an
-    output that aliases the input and a NULL factor are rejected."""
+    """Status codes of the C entry points: k = 0 and B = 0 do nothing; an
+    output that aliases the input, a short workspace, a wrong dtype and a
+    NULL factor are rejected."""
     e = spdgen.grid_edges(3, 3)
     d, v = spdgen.graph(e, 9, 2, B=1, seed=1)
     f = ssa.junction_factor(_to(d, torch.float64), e, _to(v, torch.float64))
     L = ssa.lib()
     y = torch.ones((1, 9, 2, 1), dtype=torch.float64, device=DEV)
     h, fp, yp = f.plan.handle, f.factor.data_ptr(), y.data_ptr()
-    assert L.selinv_junction_solve_f64(h, 1, fp, 0, yp, yp, None) == ssa.OK
-    assert L.selinv_junction_solve_f64(h, 0, fp, 1, yp, yp, None) == ssa.OK
-    assert L.selinv_junction_solve_f64(h, 1, fp, 1, yp, yp, None) == ssa.INVALID_ARG
+    nb = L.selinv_junction_solve_workspace_bytes(h, 1, 1)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    wp = ws.data_ptr()
+    assert L.selinv_junction_solve_f64(h, 1, fp, 0, yp, yp, None, 0, None) == ssa.OK
+    assert L.selinv_junction_solve_f64(h, 0, fp, 1, yp, yp, None, 0, None) == ssa.OK
+    assert L.selinv_junction_solve_f64(h, 1, fp, 1, yp, yp, wp, nb, None) == ssa.INVALID_ARG
+    assert L.selinv_junction_solve_f64(h, 1, fp, 1, yp, yp + 8, wp, nb - 1, None) == \
+        ssa.INVALID_ARG
     assert L.selinv_junction_sample_f64(h, 1, None, 1, yp, yp + 8, None) == ssa.INVALID_ARG
-    assert L.selinv_junction_solve_f32(h, 1, fp, 1, yp, yp + 8, None) == ssa.INVALID_ARG
+    assert L.selinv_junction_solve_f32(h, 1, fp, 1, yp, yp + 8, wp, nb, None) == ssa.INVALID_ARG
+    assert L.selinv_junction_solve_workspace_bytes(h, 1, 2) == 2 * nb > 0
     D, V = _to(d, torch.float64), _to(v, torch.float64)
     ld = torch.empty(1, dtype=torch.float64, device=DEV)
     assert L.selinv_junction_factor_f64(h, 1, D.data_ptr(), V.data_ptr(), None, ld.data_ptr(),
