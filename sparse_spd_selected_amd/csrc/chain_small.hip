@@ -9,6 +9,7 @@
 //   distribute i = L-2 .. 0: X = C_i Sinv_i,  V = G_{i+1} X,
 //                            G_lower[i] = -V,  G_i = Sinv_i + X^T V
 // Sinv_i (padded 8 x 8) is the only state kept between the passes.
+#include "frag32.h"
 #include "internal.h"
 #include "rows8.h"
 
@@ -131,14 +132,21 @@ __global__ __launch_bounds__(256) void chain_small_kernel(
 constexpr int kTinyL = 32;
 
 template <typename T>
-__global__ __launch_bounds__(64) void chain_tiny_kernel(
-    int L, int b, const T *__restrict__ diag, const T *__restrict__ lower,
-    T *__restrict__ G_diag, T *__restrict__ G_lower, double *__restrict__ logdet,
-    int32_t *__restrict__ info) {
-  __shared__ __align__(32) T Dl[kTinyL * 64];
-  __shared__ __align__(32) T Cl[(kTinyL - 1) * 64];
-  __shared__ __align__(32) T Sl[kTinyL * 64];
-  __shared__ __align__(32) T stage[2][8 * 64];
+struct TinyLds {
+  __align__(32) T Dl[kTinyL * 64];
+  __align__(32) T Cl[(kTinyL - 1) * 64];
+  __align__(32) T Sl[kTinyL * 64];
+  __align__(32) T stage[2][8 * 64];
+};
+
+template <typename T>
+__device__ __forceinline__ void tiny_chain(TinyLds<T> &sm, int L, int b,
+                                           const T *__restrict__ diag,
+                                           const T *__restrict__ lower, T *__restrict__ G_diag,
+                                           T *__restrict__ G_lower, double *__restrict__ logdet,
+                                           int32_t *__restrict__ info) {
+  T *Dl = sm.Dl, *Cl = sm.Cl, *Sl = sm.Sl;
+  auto &stage = sm.stage;
   const int lane = threadIdx.x;
   const int s = lane >> 3, i = lane & 7;
   const int64_t m = blockIdx.x;
@@ -223,6 +231,86 @@ __global__ __launch_bounds__(64) void chain_tiny_kernel(
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(64) void chain_tiny_kernel(
+    int L, int b, const T *__restrict__ diag, const T *__restrict__ lower,
+    T *__restrict__ G_diag, T *__restrict__ G_lower, double *__restrict__ logdet,
+    int32_t *__restrict__ info) {
+  __shared__ TinyLds<T> sm;
+  tiny_chain(sm, L, b, diag, lower, G_diag, G_lower, logdet, info);
+}
+
+// Chains of n = L b <= 32 (b <= 8, at most 64 chains), one per wavefront:
+// the whole matrix A, padded to 32 x 32 with the identity, is assembled in
+// LDS and inverted in registers by the blocked 32 x 32 Gauss-Jordan sweep of
+// frag32.h, whose pivots are the scalar LDL^T pivots in block order (so the
+// positive-definiteness test and log det = sum ln d are those of the chain
+// recurrence).  The selected inverse is a set of blocks of A^-1, read off as
+// G_k = (A^-1)_{k,k} and G_lower[k] = (A^-1)_{k+1,k}: 32 pivot steps and six
+// tile products replace L dependent block steps of both passes.  When a
+// pivot fails, the chain runs through the block recurrence instead, so that
+// info names the first failing block as every other path does.
+template <typename T>
+__global__ __launch_bounds__(64) void chain_dense32_kernel(
+    int L, int b, const T *__restrict__ diag, const T *__restrict__ lower,
+    T *__restrict__ G_diag, T *__restrict__ G_lower, double *__restrict__ logdet,
+    int32_t *__restrict__ info) {
+  __shared__ TinyLds<T> sm;
+  T *Al = sm.Dl, *col = sm.Dl + 32 * 32;  // 1024 + 16 entries of the 2048
+  const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
+  const int64_t m = blockIdx.x;
+  const int bb = b * b, n = L * b;
+  const T *D = diag + m * L * bb;
+  const T *C = lower + m * (L - 1) * bb;
+  // A(R, c): D_k (lower triangle mirrored) on the diagonal blocks, C_k below
+  // them, C_k^T above, the identity past n; 16 independent loads per lane
+  T v[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int e = lane + 64 * u, R = e >> 5, c = e & 31;
+    const int kr = R / b, kc = c / b, r = R - kr * b, cc = c - kc * b;
+    T x = R == c ? T(1) : T(0);
+    if (R < n && c < n) {
+      if (kr == kc)
+        x = r >= cc ? D[kr * bb + r * b + cc] : D[kr * bb + cc * b + r];
+      else if (kr == kc + 1)
+        x = C[kc * bb + r * b + cc];
+      else if (kc == kr + 1)
+        x = C[kr * bb + cc * b + r];
+      else
+        x = T(0);
+    }
+    v[u] = x;
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) Al[lane + 64 * u] = v[u];
+  __syncthreads();
+  f32t::Blk<T> a = f32t::load(Al, g, j);
+  f16::PivotLog pl;
+  const bool bad = f32t::gj_inverse(a, col, g, j, pl);
+  __syncthreads();
+  if (bad) {  // uniform: every lane sees the same pivots
+    tiny_chain(sm, L, b, diag, lower, G_diag, G_lower, logdet, info);
+    return;
+  }
+  f32t::store(Al, a, g, j);
+  __syncthreads();
+  T *Gd = G_diag + m * L * bb;
+  T *Gl = G_lower + m * (L - 1) * bb;
+  for (int e = lane; e < L * bb; e += 64) {
+    const int k = e / bb, r = (e - k * bb) / b, c = e - k * bb - r * b;
+    Gd[e] = Al[(k * b + r) * 32 + k * b + c];
+  }
+  for (int e = lane; e < (L - 1) * bb; e += 64) {
+    const int k = e / bb, r = (e - k * bb) / b, c = e - k * bb - r * b;
+    Gl[e] = Al[((k + 1) * b + r) * 32 + k * b + c];
+  }
+  if (lane == 0) {
+    logdet[m] = pl.log();
+    if (info) info[m] = 0;
+  }
+}
+
 }  // namespace
 
 size_t chain_small_workspace_bytes(int dtype_bytes, int64_t B, int64_t L) {
@@ -233,6 +321,11 @@ template <typename T>
 hipError_t chain_small_launch(int64_t B, int64_t L, int32_t b, const T *diag, const T *lower,
                               T *G_diag, T *G_lower, double *logdet, int32_t *info, void *ws,
                               hipStream_t s) {
+  if (L * b <= 32 && B <= 64) {  // the whole matrix in one wavefront's registers
+    hipLaunchKernelGGL(chain_dense32_kernel<T>, dim3(static_cast<unsigned>(B)), dim3(64), 0, s,
+                       static_cast<int>(L), b, diag, lower, G_diag, G_lower, logdet, info);
+    return hipGetLastError();
+  }
   if (L <= kTinyL && B <= 64) {  // the whole chain in LDS, one chain per workgroup
     hipLaunchKernelGGL(chain_tiny_kernel<T>, dim3(static_cast<unsigned>(B)), dim3(64), 0, s,
                        static_cast<int>(L), b, diag, lower, G_diag, G_lower, logdet, info);

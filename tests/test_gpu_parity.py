@@ -79,7 +79,8 @@ def run_chain(ssa, B, L, b, dt, seed=0, load=2.0):
 @pytest.mark.parametrize("B,L,b", [(1, 1, 1), (3, 1, 4), (2, 2, 1), (3, 3, 2), (2, 8, 3),
                                    (5, 37, 4), (3, 19, 5), (4, 9, 8), (2, 12, 16), (3, 7, 17),
                                    (2, 6, 31), (2, 11, 32), (1, 200, 1), (65, 5, 16),
-                                   (7, 70, 16)])
+                                   (7, 70, 16), (64, 4, 8), (5, 32, 1), (2, 5, 6), (1, 16, 2),
+                                   (65, 4, 8)])
 def test_chain_small(ssa, B, L, b, dt):
     run_chain(ssa, B, L, b, DT[dt], seed=B * 100 + L)
 
