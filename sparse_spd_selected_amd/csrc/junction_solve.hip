@@ -52,16 +52,15 @@ struct SDims {
 };
 
 // The chunk's tile: R_J^-1 staged in LDS, the thread's entry and group.
-template <typename T>
 struct Tile {
   int64_t id, mat, koff;
   int s, sb, f, kt, ne, G, g, I, kc, c, i;
 };
 
 template <typename T, int BC>
-__device__ inline Tile<T> tile_setup(const JunctionPlanDev &P, const SDims &d, int64_t cbase,
-                                     const T *RJ, T *Ri) {
-  Tile<T> q;
+__device__ inline Tile tile_setup(const JunctionPlanDev &P, const SDims &d, int64_t cbase,
+                                  const T *RJ, T *Ri) {
+  Tile q;
   const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
   q.id = cbase + blockIdx.x;
   q.mat = blockIdx.y;
@@ -94,7 +93,7 @@ __global__ void __launch_bounds__(kST) js_forward(JunctionPlanDev P, SDims d, in
   extern __shared__ char smem_raw[];
   T *Ri = reinterpret_cast<T *>(smem_raw);
   const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
-  const Tile<T> q = tile_setup<T, BC>(P, d, cbase, RJ, Ri);
+  const Tile q = tile_setup<T, BC>(P, d, cbase, RJ, Ri);
   T *part = Ri + q.sb * q.sb, *rs = part + kST;
   const int64_t k = d.k, k0 = q.koff - q.kc;
   const T *Um = U + q.mat * d.nrows * b * k;
@@ -151,7 +150,7 @@ __global__ void __launch_bounds__(kST) js_backward(JunctionPlanDev P, SDims d, i
   extern __shared__ char smem_raw[];
   T *Ri = reinterpret_cast<T *>(smem_raw);
   const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
-  const Tile<T> q = tile_setup<T, BC>(P, d, cbase, RJ, Ri);
+  const Tile q = tile_setup<T, BC>(P, d, cbase, RJ, Ri);
   T *part = Ri + q.sb * q.sb, *rs = part + kST;
   const int64_t k = d.k;
   const int l = q.i;  // entry I = c b + l of the chunk's columns
