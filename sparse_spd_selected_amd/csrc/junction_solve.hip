@@ -44,7 +44,8 @@
 namespace selinv {
 namespace {
 
-constexpr int kST = 256;  // threads per workgroup
+constexpr int kST = 256;   // threads per workgroup
+constexpr int kIdx = 1024;  // row indices per LDS staging batch
 
 struct SDims {
   int64_t n, npanel, nrinv, nrows, k;
@@ -95,15 +96,33 @@ __global__ void __launch_bounds__(kST) js_forward(JunctionPlanDev P, SDims d, in
   const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
   const Tile q = tile_setup<T, BC>(P, d, cbase, RJ, Ri);
   T *part = Ri + q.sb * q.sb, *rs = part + kST;
+  int32_t *idx = reinterpret_cast<int32_t *>(rs + kST);
   const int64_t k = d.k, k0 = q.koff - q.kc;
   const T *Um = U + q.mat * d.nrows * b * k;
-  if (q.g < q.G) {
-    const int64_t fc = P.ch_cptr[q.id] + q.c;
-    const int32_t o0 = P.occ_ptr[fc], o1 = P.occ_ptr[fc + 1];
+  {
+    // the occurrences of the chunk's nodes are one contiguous range of
+    // occ_row (flat columns of a chunk are consecutive); their row indices are
+    // staged in LDS in batches, so that the row-vector loads do not wait on
+    // index loads
+    const int64_t fc0 = P.ch_cptr[q.id];
+    const int32_t ob = P.occ_ptr[fc0], oe = P.occ_ptr[fc0 + q.s];
+    const int32_t o0 = P.occ_ptr[fc0 + q.c], o1 = P.occ_ptr[fc0 + q.c + 1];
     const T *Ui = Um + int64_t(q.i) * k + q.koff;
     T acc = T(0);
-    for (int32_t o = o0 + q.g; o < o1; o += q.G) acc += Ui[int64_t(P.occ_row[o]) * b * k];
-    part[q.g * q.ne + (t - q.g * q.ne)] = acc;
+    for (int32_t b0 = ob; b0 < oe; b0 += kIdx) {
+      const int32_t b1 = oe - b0 < kIdx ? oe : b0 + kIdx;
+      __syncthreads();  // the previous batch has been read
+      for (int32_t e = b0 + t; e < b1; e += kST) idx[e - b0] = P.occ_row[e];
+      __syncthreads();
+      if (q.g < q.G) {
+        const int32_t lo = o0 > b0 ? o0 : b0, hi = o1 < b1 ? o1 : b1;
+        int32_t o = o0 + q.g;
+        if (o < lo) o += (lo - o + q.G - 1) / q.G * q.G;
+#pragma unroll 4
+        for (; o < hi; o += q.G) acc += Ui[int64_t(idx[o - b0]) * b * k];
+      }
+    }
+    if (q.g < q.G) part[q.g * q.ne + (t - q.g * q.ne)] = acc;
   }
   __syncthreads();
   const int64_t node = P.order[q.f + q.c];
@@ -152,22 +171,34 @@ __global__ void __launch_bounds__(kST) js_backward(JunctionPlanDev P, SDims d, i
   const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
   const Tile q = tile_setup<T, BC>(P, d, cbase, RJ, Ri);
   T *part = Ri + q.sb * q.sb, *rs = part + kST;
+  int32_t *idx = reinterpret_cast<int32_t *>(rs + kST);
   const int64_t k = d.k;
   const int l = q.i;  // entry I = c b + l of the chunk's columns
-  if (q.g < q.G) {
+  {
     const int nr = P.ch_n[q.id];
     const int64_t rb = P.rows_ptr[q.id];
     // column l of block (a, c) of the panel: stride b down its rows
     const T *Wc = W + (q.mat * d.npanel + P.ch_pbase[q.id] + int64_t(q.s) * q.s + q.c) * bb + l;
     const T *xm = x + q.mat * d.n * b * k + q.koff;
     T acc = T(0);
-    for (int a = q.g; a < nr; a += q.G) {
-      const T *Wb = Wc + int64_t(a) * q.s * bb;
-      const T *xw = xm + int64_t(P.row_node[rb + a]) * b * k;
+    for (int a0 = 0; a0 < nr; a0 += kIdx) {  // the later rows' labels, staged in LDS
+      const int a1 = nr - a0 < kIdx ? nr : a0 + kIdx;
+      __syncthreads();  // the previous batch has been read
+      for (int e = a0 + t; e < a1; e += kST) idx[e - a0] = P.row_node[rb + e];
+      __syncthreads();
+      if (q.g < q.G) {
+        int a = q.g;
+        if (a < a0) a += (a0 - a + q.G - 1) / q.G * q.G;
+#pragma unroll 2
+        for (; a < a1; a += q.G) {
+          const T *Wb = Wc + int64_t(a) * q.s * bb;
+          const T *xw = xm + int64_t(idx[a - a0]) * b * k;
 #pragma unroll
-      for (int i = 0; i < b; ++i) acc += Wb[i * b] * xw[i * k];
+          for (int i = 0; i < b; ++i) acc += Wb[i * b] * xw[i * k];
+        }
+      }
     }
-    part[q.g * q.ne + (t - q.g * q.ne)] = acc;
+    if (q.g < q.G) part[q.g * q.ne + (t - q.g * q.ne)] = acc;
   }
   __syncthreads();
   const int64_t node = P.order[q.f + q.c];
@@ -196,7 +227,7 @@ hipError_t apply_run(const selinv_junction_plan *plan, int64_t B, const T *facto
   if (nkt > 65535) return hipErrorInvalidValue;
   const SDims d{plan->n, plan->npanel, plan->nrinv, plan->rows_ptr[plan->nch], k, kt, b};
   const T *W = factor, *RJ = factor + B * plan->npanel * int64_t(b) * b;
-  const size_t lds = sizeof(T) * (size_t(sbm) * sbm + 2 * kST);
+  const size_t lds = sizeof(T) * (size_t(sbm) * sbm + 2 * kST) + sizeof(int32_t) * kIdx;
   const auto &lo = plan->level_off;
   const unsigned By = static_cast<unsigned>(B), Z = static_cast<unsigned>(nkt);
   if (!sample)
