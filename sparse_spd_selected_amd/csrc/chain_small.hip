@@ -250,16 +250,18 @@ __global__ __launch_bounds__(64) void chain_tiny_kernel(
 // tile products replace L dependent block steps of both passes.  When a
 // pivot fails, the chain runs through the block recurrence instead, so that
 // info names the first failing block as every other path does.
-template <typename T>
+// (b is a template parameter, so the index arithmetic divides by constants)
+template <typename T, int b>
 __global__ __launch_bounds__(64) void chain_dense32_kernel(
-    int L, int b, const T *__restrict__ diag, const T *__restrict__ lower,
+    int L, const T *__restrict__ diag, const T *__restrict__ lower,
     T *__restrict__ G_diag, T *__restrict__ G_lower, double *__restrict__ logdet,
     int32_t *__restrict__ info) {
   __shared__ TinyLds<T> sm;
   T *Al = sm.Dl, *col = sm.Dl + 32 * 32;  // 1024 + 16 entries of the 2048
   const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
   const int64_t m = blockIdx.x;
-  const int bb = b * b, n = L * b;
+  constexpr int bb = b * b;
+  const int n = L * b;
   const T *D = diag + m * L * bb;
   const T *C = lower + m * (L - 1) * bb;
   // A(R, c): D_k (lower triangle mirrored) on the diagonal blocks, C_k below
@@ -322,8 +324,19 @@ hipError_t chain_small_launch(int64_t B, int64_t L, int32_t b, const T *diag, co
                               T *G_diag, T *G_lower, double *logdet, int32_t *info, void *ws,
                               hipStream_t s) {
   if (L * b <= 32 && B <= 64) {  // the whole matrix in one wavefront's registers
-    hipLaunchKernelGGL(chain_dense32_kernel<T>, dim3(static_cast<unsigned>(B)), dim3(64), 0, s,
-                       static_cast<int>(L), b, diag, lower, G_diag, G_lower, logdet, info);
+    const dim3 grid(static_cast<unsigned>(B));
+    const int Li = static_cast<int>(L);
+    switch (b) {
+#define SELINV_DENSE32(BV)                                                                    \
+  case BV:                                                                                     \
+    hipLaunchKernelGGL((chain_dense32_kernel<T, BV>), grid, dim3(64), 0, s, Li, diag, lower, \
+                       G_diag, G_lower, logdet, info);                                         \
+    break;
+      SELINV_DENSE32(1) SELINV_DENSE32(2) SELINV_DENSE32(3) SELINV_DENSE32(4)
+      SELINV_DENSE32(5) SELINV_DENSE32(6) SELINV_DENSE32(7) SELINV_DENSE32(8)
+#undef SELINV_DENSE32
+      default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
   }
   if (L <= kTinyL && B <= 64) {  // the whole chain in LDS, one chain per workgroup
