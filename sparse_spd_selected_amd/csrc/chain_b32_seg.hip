@@ -61,11 +61,43 @@ __device__ __forceinline__ int seg_begin(int s, int L, int P) {
   return static_cast<int>(static_cast<int64_t>(s) * L / P);
 }
 
+// A block's register image (16 entries per lane) in the workspace, entry r
+// of tile (I, J) of lane l at ((2 I + J) 4 + r) 64 + l: each access
+// instruction covers 64 consecutive entries.
 template <typename T>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void seg32_collect(
+__device__ __forceinline__ void store_image(T *P, int lane, const Blk<T> &b) {
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) P[((2 * I + J) * 4 + r) * 64 + lane] = b.t[I][J][r];
+}
+
+template <typename T>
+__device__ __forceinline__ Blk<T> load_image(const T *P, int lane) {
+  Blk<T> b;
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int J = 0; J < 2; ++J)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b.t[I][J][r] = P[((2 * I + J) * 4 + r) * 64 + lane];
+  return b;
+}
+
+// The collect runs in two kernels.  seg32_fill takes each segment from its
+// first block while the fill block is carried (until it is dropped, or to the
+// separator if it never decays) and hands the current Schur block over;
+// seg32_plain continues with the plain sweep to the separator.  The plain
+// sweep holds no fill state, so it fits in half the registers and runs two
+// wavefronts per SIMD, which hides much of its dependent latency; the fill
+// phase is short (about 28 blocks per segment on the b = 32 workload).
+template <typename T>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void seg32_fill(
     int L, int P, const T *__restrict__ diag, const T *__restrict__ lower,
-    T *__restrict__ st_sinv, T *__restrict__ st_f, T *__restrict__ r_S, T *__restrict__ r_F,
-    T *__restrict__ r_U, double *__restrict__ seg_ld, int32_t *__restrict__ seg_fail,
+    T *__restrict__ st_sinv, T *__restrict__ st_f, T *__restrict__ r_F, T *__restrict__ r_U,
+    T *__restrict__ st_hand, double *__restrict__ seg_ld, int32_t *__restrict__ seg_fail,
     int32_t *__restrict__ seg_fill_end) {
   using Tr = io32::Traits<T>;
   __shared__ __align__(16) T col[32];
@@ -102,50 +134,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   }
   f16::PivotLog pl;
   int32_t fail = 0;
-  for (int i = a; i < ts; ++i) {
+  for (int i = a; i < ts && fill; ++i) {
     // C_i and D_{i+1} are consumed after the sweep of block i
     const io32::Nat<T> Cn = io32::load(C + i * BB, lane);
     const io32::Nat<T> Dn = io32::load(D + (i + 1) * BB, lane);
     if (f32t::gj_inverse(S, col, g, j, pl) && !fail) fail = i + 1;
     f16::wave_sync();
     io32::put_blk(tA, g, j, S);
-    if (fill) io32::put_blk(tB, g, j, F);
+    io32::put_blk(tB, g, j, F);
     f16::wave_sync();
     const io32::NatP<T> pk = sl.gather_packed(tA);
-    io32::Nat<T> fn;
-    if (fill) fn = io32::get(tB, lane);
+    const io32::Nat<T> fn = io32::get(tB, lane);
     f16::wave_sync();
     io32::store_packed(sinv + i * PB, lane, pk);
-    if (fill) io32::store_ws(fst + i * BB, lane, fn);
+    io32::store_ws(fst + i * BB, lane, fn);
     io32::put(tA, lane, Cn);
     io32::put(tB, lane, Dn);
     f16::wave_sync();
     const Blk<T> Ct = io32::get_blk_t(tA, g, j);  // O32(C_i^T)
     const Blk<T> Dd = sl.get_sym(tB);
-    if (fill) {
-      const Blk<T> Y2 = f32t::mm(S, F, f32t::zero<T>());  // Sinv F_i
-      U = f32t::mm_lower(F, Y2, U);                       // += F_i^T Sinv F_i
-      F = f32t::neg(f32t::mm(Ct, Y2, f32t::zero<T>()));   // -C_i Sinv F_i
-      if (f32t::all_below(F, drop_below)) {               // dropped from i + 1 on
-        fill = false;
-        fe = i + 1;
-        F = f32t::zero<T>();
-      }
+    const Blk<T> Y2 = f32t::mm(S, F, f32t::zero<T>());  // Sinv F_i
+    U = f32t::mm_lower(F, Y2, U);                       // += F_i^T Sinv F_i
+    F = f32t::neg(f32t::mm(Ct, Y2, f32t::zero<T>()));   // -C_i Sinv F_i
+    if (f32t::all_below(F, drop_below)) {               // dropped from i + 1 on
+      fill = false;
+      fe = i + 1;
+      F = f32t::zero<T>();
     }
     const Blk<T> Y1 = f32t::mm(S, Ct, f32t::zero<T>());  // Sinv C_i^T
     // D_{i+1} - C_i Sinv C_i^T; the (1,0) tile is not formed (the blocked
     // inverse reads only the upper off-diagonal tile)
     S = f32t::sub(Dd, f32t::mm_upper(Ct, Y1, f32t::zero<T>()));
   }
-  // separator t_s: its partial Schur block, fill block and update of t
+  // hand-over (block fe's Schur block), the segment's fill block and update of t
   const int64_t q = m * P + s;
-  f16::wave_sync();
-  if (ts > a)
-    io32::put_sym_u(tA, g, j, S);
-  else
-    io32::put_blk(tA, g, j, S);
-  f16::wave_sync();
-  io32::store_ws(r_S + q * BB, lane, io32::get(tA, lane));
+  store_image(st_hand + q * BB, lane, S);
   if (left) {
     f16::wave_sync();
     io32::put_blk(tA, g, j, F);
@@ -158,6 +181,64 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     seg_ld[q] = pl.log();
     seg_fail[q] = fail;
     seg_fill_end[q] = fe;
+  }
+}
+
+// The plain sweep from block fe to the separator, then the separator's
+// partial Schur block.
+template <typename T>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void seg32_plain(
+    int L, int P, const T *__restrict__ diag, const T *__restrict__ lower,
+    T *__restrict__ st_sinv, const T *__restrict__ st_hand, T *__restrict__ r_S,
+    double *__restrict__ seg_ld, int32_t *__restrict__ seg_fail,
+    const int32_t *__restrict__ seg_fill_end) {
+  using Tr = io32::Traits<T>;
+  __shared__ __align__(16) T col[32];
+  __shared__ __align__(16) T tA[Tr::kTile];
+  __shared__ __align__(16) T tB[Tr::kTile];
+  const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
+  const int64_t m = blockIdx.x / P;
+  const int s = blockIdx.x % P;
+  const int64_t q = m * P + s;
+  const int a = seg_begin(s, L, P), ts = seg_begin(s + 1, L, P) - 1;
+  const int fe = seg_fill_end[q];
+  const T *D = diag + m * L * BB;
+  const T *C = lower + m * (L - 1) * BB;
+  T *sinv = st_sinv + m * L * PB;
+  const io32::SymLanes<T> sl(g, j, lane);
+  Blk<T> S = load_image(st_hand + q * BB, lane);
+  f16::PivotLog pl;
+  int32_t fail = 0;
+  for (int i = fe; i < ts; ++i) {
+    const io32::Nat<T> Cn = io32::load(C + i * BB, lane);
+    const io32::Nat<T> Dn = io32::load(D + (i + 1) * BB, lane);
+    if (f32t::gj_inverse(S, col, g, j, pl) && !fail) fail = i + 1;
+    f16::wave_sync();
+    io32::put_blk(tA, g, j, S);
+    f16::wave_sync();
+    const io32::NatP<T> pk = sl.gather_packed(tA);
+    f16::wave_sync();
+    io32::store_packed(sinv + i * PB, lane, pk);
+    io32::put(tA, lane, Cn);
+    io32::put(tB, lane, Dn);
+    f16::wave_sync();
+    const Blk<T> Ct = io32::get_blk_t(tA, g, j);  // O32(C_i^T)
+    const Blk<T> Dd = sl.get_sym(tB);
+    const Blk<T> Y1 = f32t::mm(S, Ct, f32t::zero<T>());  // Sinv C_i^T
+    S = f32t::sub(Dd, f32t::mm_upper(Ct, Y1, f32t::zero<T>()));
+  }
+  // separator t_s: its partial Schur block (its (1,0) tile was formed only if
+  // no block of the segment was eliminated)
+  f16::wave_sync();
+  if (ts > a)
+    io32::put_sym_u(tA, g, j, S);
+  else
+    io32::put_blk(tA, g, j, S);
+  f16::wave_sync();
+  io32::store_ws(r_S + q * BB, lane, io32::get(tA, lane));
+  if (lane == 0) {
+    seg_ld[q] += pl.log();
+    if (!seg_fail[q]) seg_fail[q] = fail;
   }
 }
 
@@ -303,8 +384,8 @@ __global__ void seg32_finish(int64_t B, int L, int P, const double *__restrict__
 }
 
 struct SegLayout {
-  size_t sinv, f, rS, rF, rU, diag_r, lower_r, gr_d, gr_l, seg_ld, seg_fail, seg_fe, ld_r, info_r,
-      ws_r, total;
+  size_t sinv, f, rS, rF, rU, hand, diag_r, lower_r, gr_d, gr_l, seg_ld, seg_fail, seg_fe, ld_r,
+      info_r, ws_r, total;
 };
 
 SegLayout seg_layout(int dtype_bytes, int64_t B, int64_t L, int P) {
@@ -321,6 +402,7 @@ SegLayout seg_layout(int dtype_bytes, int64_t B, int64_t L, int P) {
   o.rS = take(B * P * BB * w);
   o.rF = take(B * P * BB * w);
   o.rU = take(B * P * BB * w);
+  o.hand = take(B * P * BB * w);
   o.diag_r = take(B * P * BB * w);
   o.lower_r = take(B * P * BB * w);
   o.gr_d = take(B * P * BB * w);
@@ -339,7 +421,8 @@ SegLayout seg_layout(int dtype_bytes, int64_t B, int64_t L, int P) {
 
 int chain32_segments(int64_t B, int64_t L) {
   if (B <= 0 || B >= 512 || L < 64) return 0;
-  const int64_t by_occupancy = std::max<int64_t>(2, 1024 / B);
+  // two wavefronts per SIMD for the plain sweep (seg32_plain)
+  const int64_t by_occupancy = std::max<int64_t>(2, 2048 / B);
   const int64_t by_length = L / 8;
   const int64_t by_balance = static_cast<int64_t>(std::sqrt(8.0 * static_cast<double>(L)));
   return static_cast<int>(std::max<int64_t>(2, std::min({by_occupancy, by_length, by_balance})));
@@ -360,6 +443,7 @@ hipError_t chain32_seg_launch(int64_t B, int64_t L, int P, const T *diag, const 
   T *rS = reinterpret_cast<T *>(base + o.rS);
   T *rF = reinterpret_cast<T *>(base + o.rF);
   T *rU = reinterpret_cast<T *>(base + o.rU);
+  T *hand = reinterpret_cast<T *>(base + o.hand);
   T *diag_r = reinterpret_cast<T *>(base + o.diag_r);
   T *lower_r = reinterpret_cast<T *>(base + o.lower_r);
   T *gr_d = reinterpret_cast<T *>(base + o.gr_d);
@@ -370,8 +454,10 @@ hipError_t chain32_seg_launch(int64_t B, int64_t L, int P, const T *diag, const 
   double *ld_r = reinterpret_cast<double *>(base + o.ld_r);
   int32_t *info_r = reinterpret_cast<int32_t *>(base + o.info_r);
   const unsigned grid = static_cast<unsigned>(B * P);
-  hipLaunchKernelGGL(seg32_collect<T>, dim3(grid), dim3(64), 0, s, static_cast<int>(L), P, diag,
-                     lower, sinv, f, rS, rF, rU, seg_ld, seg_fail, seg_fe);
+  hipLaunchKernelGGL(seg32_fill<T>, dim3(grid), dim3(64), 0, s, static_cast<int>(L), P, diag,
+                     lower, sinv, f, rF, rU, hand, seg_ld, seg_fail, seg_fe);
+  hipLaunchKernelGGL(seg32_plain<T>, dim3(grid), dim3(64), 0, s, static_cast<int>(L), P, diag,
+                     lower, sinv, hand, rS, seg_ld, seg_fail, seg_fe);
   hipLaunchKernelGGL(seg32_reduce<T>, dim3(grid), dim3(64), 0, s, P, rS, rF, rU, diag_r, lower_r);
   hipError_t e = chain32_launch<T>(B, P, diag_r, lower_r, gr_d, gr_l, ld_r, info_r, base + o.ws_r, s);
   if (e != hipSuccess) return e;
