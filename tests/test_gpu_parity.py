@@ -140,10 +140,11 @@ def test_chain_b32_segments(ssa, B, L, dt):
 
 @pytest.mark.parametrize("dt", ["f64", "f32"])
 def test_chain_b32_fill_drop(ssa, dt):
-    """8 chains of 8192 blocks of 32 (diagonal load 1.0): 128 segments of 64
+    """8 chains of 8192 blocks of 32 (diagonal load 1.0): 256 segments of 32
     blocks per chain.  The fill block to each segment's left separator decays
     below 2^-100 of the segment's first coupling block after about 28 blocks
-    and is dropped from there on; every chain is compared with the oracle."""
+    and is dropped from there on (the rest of the segment runs in the plain
+    collect and distribute); every chain is compared with the oracle."""
     e = run_chain(ssa, 8, 8192, 32, DT[dt], seed=11, load=1.0)
     say("  worst rel err %.2e" % e)
 
