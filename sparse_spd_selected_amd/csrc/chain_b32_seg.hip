@@ -209,12 +209,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   Blk<T> S = load_image(st_hand + q * BB, lane);
   f16::PivotLog pl;
   int32_t fail = 0;
+  // C_i^T is staged one block ahead; C_{i+1} and D_{i+1} load during step i
+  if (fe < ts) io32::put(tA, lane, io32::load(C + fe * BB, lane));
+  f16::wave_sync();
+  Blk<T> Ct = io32::get_blk_t(tA, g, j);  // O32(C_fe^T)
   for (int i = fe; i < ts; ++i) {
-    const io32::Nat<T> Cn = io32::load(C + i * BB, lane);
+    const io32::Nat<T> Cn = io32::load(C + min(i + 1, ts - 1) * BB, lane);
     const io32::Nat<T> Dn = io32::load(D + (i + 1) * BB, lane);
-    if (f32t::gj_inverse(S, col, g, j, pl) && !fail) fail = i + 1;
+    Blk<T> M = f32t::zero<T>();  // C_i Sinv C_i^T
+    if (f32t::gj_congruence(S, Ct, M, col, g, j, pl) && !fail) fail = i + 1;
     f16::wave_sync();
-    io32::put_blk(tA, g, j, S);
+    io32::put_blk_low(tA, g, j, S);
     f16::wave_sync();
     const io32::NatP<T> pk = sl.gather_packed(tA);
     f16::wave_sync();
@@ -222,10 +227,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     io32::put(tA, lane, Cn);
     io32::put(tB, lane, Dn);
     f16::wave_sync();
-    const Blk<T> Ct = io32::get_blk_t(tA, g, j);  // O32(C_i^T)
-    const Blk<T> Dd = sl.get_sym(tB);
-    const Blk<T> Y1 = f32t::mm(S, Ct, f32t::zero<T>());  // Sinv C_i^T
-    S = f32t::sub(Dd, f32t::mm_upper(Ct, Y1, f32t::zero<T>()));
+    Ct = io32::get_blk_t(tA, g, j);  // O32(C_{i+1}^T)
+    S = f32t::sub(sl.get_sym(tB), M);
   }
   // separator t_s: its partial Schur block (its (1,0) tile was formed only if
   // no block of the segment was eliminated)

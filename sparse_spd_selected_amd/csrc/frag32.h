@@ -346,5 +346,45 @@ __device__ __forceinline__ bool gj_inverse(Blk<T> &a, T *col, int g, int j, f16:
   return bad;
 }
 
+// One elimination step with a 32x32 SPD pivot S and the block C that couples
+// it to the next pivot: S is replaced by S^-1 (tiles (0,0), (1,0) and (1,1);
+// tile (0,1) is left as it was) and the message C S^-1 C^T is added to tiles
+// (0,0), (0,1) and (1,1) of M (tile (1,0) is not touched).  `Ct` is O32(C^T).
+// With the block LDL^T of S,
+//     S = L diag(S00, Sc) L^T,  L = [[I, 0], [X, I]],  X = S10 S00^-1,
+//     Sc = S11 - X S01,
+// the message is M = W^T diag(S00^-1, Sc^-1) W with W = L^-1 C^T, whose tile
+// row 0 is that of C^T and tile row 1 is (C^T)_1 - X (C^T)_0.  That takes 12
+// tile products where forming C S^-1 and then M takes 14, and the explicit
+// inverse needs three more (X, P = Sc^-1 X, S00^-1 + X^T P) where gj_inverse
+// takes six; after the second sweep only three products stand between Sc^-1
+// and M.  The pivots are gj_inverse's, in the same order.
+template <typename T>
+__device__ __forceinline__ bool gj_congruence(Blk<T> &a, const Blk<T> &Ct, Blk<T> &M, T *col,
+                                              int g, int j, f16::PivotLog &pl) {
+  const Frag<T> z = f16::zero<T>();
+  Frag<T> i00 = a.t[0][0];
+  bool bad = f16::gj_inverse(i00, col, g, j, pl);
+  const Frag<T> a01 = a.t[0][1];                        // O(S01) = O(S10^T)
+  const Frag<T> nXt = -f16::mm<T>(i00, a01, z);         // O(-X^T)
+  Frag<T> s11 = f16::mm<T>(nXt, a01, a.t[1][1]);        // O(S11 - X S01)
+  const Frag<T> W10 = f16::mm<T>(nXt, Ct.t[0][0], Ct.t[1][0]);
+  const Frag<T> W11 = f16::mm<T>(nXt, Ct.t[0][1], Ct.t[1][1]);
+  const Frag<T> Z00 = f16::mm<T>(i00, Ct.t[0][0], z);   // S00^-1 W_00
+  const Frag<T> Z01 = f16::mm<T>(i00, Ct.t[0][1], z);
+  const Frag<T> X = f16::mm<T>(a01, i00, z);            // O(X)
+  bad |= f16::gj_inverse(s11, col, g, j, pl);           // Sc^-1
+  const Frag<T> Z10 = f16::mm<T>(s11, W10, z);          // Sc^-1 W_10
+  const Frag<T> Z11 = f16::mm<T>(s11, W11, z);
+  M.t[0][0] = f16::mm<T>(W10, Z10, f16::mm<T>(Ct.t[0][0], Z00, M.t[0][0]));
+  M.t[0][1] = f16::mm<T>(W10, Z11, f16::mm<T>(Ct.t[0][0], Z01, M.t[0][1]));
+  M.t[1][1] = f16::mm<T>(W11, Z11, f16::mm<T>(Ct.t[0][1], Z01, M.t[1][1]));
+  const Frag<T> P = f16::mm<T>(s11, X, z);              // O(Sc^-1 X)
+  a.t[0][0] = f16::mm<T>(X, P, i00);                    // S00^-1 + X^T Sc^-1 X
+  a.t[1][0] = -P;                                       // -Sc^-1 X
+  a.t[1][1] = s11;
+  return bad;
+}
+
 }  // namespace f32t
 }  // namespace selinv

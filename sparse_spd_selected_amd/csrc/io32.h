@@ -150,6 +150,19 @@ __device__ __forceinline__ void put_blk(T *tile, int g, int j, const Blk<T> &b) 
       for (int r = 0; r < 4; ++r) tile[(16 * I + row<T>(g, r)) * ld + 16 * J + j] = b.t[I][J][r];
 }
 
+// write tiles (0,0), (1,0) and (1,1) of O32(M) (enough for its lower triangle)
+template <typename T>
+__device__ __forceinline__ void put_blk_low(T *tile, int g, int j, const Blk<T> &b) {
+  constexpr int ld = Traits<T>::kLd;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int a = row<T>(g, r);
+    tile[a * ld + j] = b.t[0][0][r];
+    tile[(16 + a) * ld + j] = b.t[1][0][r];
+    tile[(16 + a) * ld + 16 + j] = b.t[1][1][r];
+  }
+}
+
 // write O32(M) as M^T
 template <typename T>
 __device__ __forceinline__ void put_blk_t(T *tile, int g, int j, const Blk<T> &b) {

@@ -30,12 +30,12 @@ constexpr int kLPW = 16;  // leaves per wavefront
 constexpr int BB = 1024, PB = f32t::kPacked32;
 
 template <typename T>
-__device__ __forceinline__ void store_sym(T *P, const Blk<T> &b, int g, int j) {
-  // symmetric result with tiles (0,0), (1,0), (1,1) formed: the (0,1) block is
-  // the transpose of the (1,0) block
+__device__ __forceinline__ void store_sym_u(T *P, const Blk<T> &b, int g, int j) {
+  // symmetric result with tiles (0,0), (0,1), (1,1) formed: the (1,0) block is
+  // the transpose of the (0,1) block
   f16::store_t(P, 32, b.t[0][0], g, j);
-  f16::store(P + 16 * 32, 32, b.t[1][0], g, j);
-  f16::store_t(P + 16, 32, b.t[1][0], g, j);
+  f16::store(P + 16, 32, b.t[0][1], g, j);
+  f16::store_t(P + 16 * 32, 32, b.t[0][1], g, j);
   f16::store_t(P + 16 * 32 + 16, 32, b.t[1][1], g, j);
 }
 
@@ -60,37 +60,40 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   T *dinv = keep ? st_dinv + m * K * PB : nullptr;
   const io32::SymLanes<T> sl(g, j, lane);
 
-  Blk<T> Macc = f32t::zero<T>();
+  Blk<T> Macc = f32t::zero<T>();  // sum of F_j^T Dinv_j F_j, tiles (0,0), (0,1), (1,1)
   f16::PivotLog pl;  // product of all pivots of this wavefront's leaves
   int32_t first_bad = 0;
-  Blk<T> S;
+  Blk<T> S, Fo;
   {
-    const io32::Nat<T> d0 = io32::load(Dm + j0 * BB, lane);
-    io32::put(tA, lane, d0);
+    io32::put(tA, lane, io32::load(Dm + j0 * BB, lane));
+    io32::put(tB, lane, io32::load(Fm + j0 * BB, lane));
     f16::wave_sync();
     S = sl.get_sym(tA);
+    Fo = io32::get_blk(tB, g, j);  // O32(F_j0)
   }
-  // Per leaf: this leaf's coupling and the next leaf's diagonal block are
-  // loaded first and consumed after the sweep (single-exit loop).
+  // Per leaf: the next leaf's blocks are loaded first and staged after the
+  // step (single-exit loop).  With C = F_j^T the step's message C Dinv_j C^T
+  // is F_j^T Dinv_j F_j, and O32(C^T) = O32(F_j).
   for (int jj = j0; jj < j1; ++jj) {
-    const io32::Nat<T> Fn = io32::load(Fm + jj * BB, lane);
-    const io32::Nat<T> Dn = io32::load(Dm + min(jj + 1, j1 - 1) * BB, lane);
-    if (f32t::gj_inverse(S, col, g, j, pl) && !first_bad) first_bad = jj + 1;
-    f16::wave_sync();
-    io32::put_blk(tA, g, j, S);  // Dinv_j -> packed workspace triangle
-    io32::put(tB, lane, Fn);
-    f16::wave_sync();
-    const io32::NatP<T> pk = sl.gather_packed(tA);
-    const Blk<T> Fo = io32::get_blk(tB, g, j);  // O32(F_j)
+    const int jn = min(jj + 1, j1 - 1);
+    const io32::Nat<T> Fn = io32::load(Fm + jn * BB, lane);
+    const io32::Nat<T> Dn = io32::load(Dm + jn * BB, lane);
+    if (f32t::gj_congruence(S, Fo, Macc, col, g, j, pl) && !first_bad) first_bad = jj + 1;
+    if (keep) {  // Dinv_j -> packed workspace triangle
+      f16::wave_sync();
+      io32::put_blk_low(tA, g, j, S);
+      f16::wave_sync();
+      const io32::NatP<T> pk = sl.gather_packed(tA);
+      io32::store_packed(dinv + jj * PB, lane, pk);
+    }
     f16::wave_sync();
     io32::put(tA, lane, Dn);
-    if (keep) io32::store_packed(dinv + jj * PB, lane, pk);
-    const Blk<T> Z = f32t::mm(S, Fo, f32t::zero<T>());  // Dinv_j F_j
-    Macc = f32t::mm_lower(Fo, Z, Macc);                  // += F_j^T Z_j
+    io32::put(tB, lane, Fn);
     f16::wave_sync();
     S = sl.get_sym(tA);
+    Fo = io32::get_blk(tB, g, j);
   }
-  store_sym(st_mpart + (m * nw + w) * BB, Macc, g, j);
+  store_sym_u(st_mpart + (m * nw + w) * BB, Macc, g, j);
   if (lane == 0) {
     st_ld[m * nw + w] = pl.log();
     st_fail[m * nw + w] = first_bad;
