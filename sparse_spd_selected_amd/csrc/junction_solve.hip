@@ -52,26 +52,46 @@ struct SDims {
   int kt, b;
 };
 
-// The chunk's tile: R_J^-1 staged in LDS, the thread's entry and group.
+// dst[0 .. n) = src[0 .. n) by the workgroup, n >= 1: each thread issues up to
+// kR loads (at clamped, in-range addresses) before it waits for any of them,
+// so a long copy costs a few memory round trips instead of one per element.
+template <typename T>
+__device__ inline void stage(T *dst, const T *src, int n) {
+  constexpr int kR = 8;
+  for (int base = threadIdx.x; base < n; base += kR * kST) {
+    T v[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) v[r] = src[min(base + r * kST, n - 1)];
+#pragma unroll
+    for (int r = 0; r < kR; ++r)
+      if (base + r * kST < n) dst[base + r * kST] = v[r];
+  }
+}
+
+// The chunk's tile: its plan entries, the thread's entry and group.
 struct Tile {
-  int64_t id, mat, koff;
-  int s, sb, f, kt, ne, G, g, I, kc, c, i;
+  int64_t id, mat, koff, rbase, pbase, rows, cptr;
+  int s, sb, f, nr, kt, ne, G, g, I, kc, c, i;
 };
 
-template <typename T, int BC>
-__device__ inline Tile tile_setup(const JunctionPlanDev &P, const SDims &d, int64_t cbase,
-                                  const T *RJ, T *Ri) {
+// All plan entries of the chunk are read here, together, before any of them
+// is waited for.
+template <int BC>
+__device__ inline Tile tile_setup(const JunctionPlanDev &P, const SDims &d, int64_t cbase) {
   Tile q;
-  const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
+  const int b = BC ? BC : d.b, t = threadIdx.x;
   q.id = cbase + blockIdx.x;
   q.mat = blockIdx.y;
   const int64_t k0 = int64_t(blockIdx.z) * d.kt;
   q.kt = d.k - k0 < d.kt ? static_cast<int>(d.k - k0) : d.kt;
   q.s = P.ch_s[q.id];
-  q.sb = q.s * b;
   q.f = P.ch_first[q.id];
-  const T *Rj = RJ + (q.mat * d.nrinv + P.ch_rbase[q.id]) * bb;
-  for (int e = t; e < q.sb * q.sb; e += kST) Ri[e] = Rj[e];
+  q.nr = P.ch_n[q.id];
+  q.rbase = P.ch_rbase[q.id];
+  q.pbase = P.ch_pbase[q.id];
+  q.rows = P.rows_ptr[q.id];
+  q.cptr = P.ch_cptr[q.id];
+  q.sb = q.s * b;
   q.ne = q.sb * q.kt;
   q.G = kST / q.ne;
   q.g = t / q.ne;
@@ -94,43 +114,44 @@ __global__ void __launch_bounds__(kST) js_forward(JunctionPlanDev P, SDims d, in
   extern __shared__ char smem_raw[];
   T *Ri = reinterpret_cast<T *>(smem_raw);
   const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
-  const Tile q = tile_setup<T, BC>(P, d, cbase, RJ, Ri);
+  const Tile q = tile_setup<BC>(P, d, cbase);
   T *part = Ri + q.sb * q.sb, *rs = part + kST;
   int32_t *idx = reinterpret_cast<int32_t *>(rs + kST);
   const int64_t k = d.k, k0 = q.koff - q.kc;
   const T *Um = U + q.mat * d.nrows * b * k;
+  // the occurrences of the chunk's nodes are one contiguous range of occ_row
+  // (flat columns of a chunk are consecutive)
+  const int32_t ob = P.occ_ptr[q.cptr], oe = P.occ_ptr[q.cptr + q.s];
+  const int32_t o0 = P.occ_ptr[q.cptr + q.c], o1 = P.occ_ptr[q.cptr + q.c + 1];
+  const int64_t node = P.order[q.f + q.c];
+  const int64_t at = ((q.mat * d.n + node) * b + q.i) * k + q.koff;
+  const T yv = t < q.ne ? y[at] : T(0);
+  stage(Ri, RJ + (q.mat * d.nrinv + q.rbase) * bb, q.sb * q.sb);
   {
-    // the occurrences of the chunk's nodes are one contiguous range of
-    // occ_row (flat columns of a chunk are consecutive); their row indices are
-    // staged in LDS in batches, so that the row-vector loads do not wait on
-    // index loads
-    const int64_t fc0 = P.ch_cptr[q.id];
-    const int32_t ob = P.occ_ptr[fc0], oe = P.occ_ptr[fc0 + q.s];
-    const int32_t o0 = P.occ_ptr[fc0 + q.c], o1 = P.occ_ptr[fc0 + q.c + 1];
+    // the occurrences' row indices are staged in LDS in batches, so that the
+    // row-vector loads do not wait on index loads
     const T *Ui = Um + int64_t(q.i) * k + q.koff;
     T acc = T(0);
     for (int32_t b0 = ob; b0 < oe; b0 += kIdx) {
       const int32_t b1 = oe - b0 < kIdx ? oe : b0 + kIdx;
       __syncthreads();  // the previous batch has been read
-      for (int32_t e = b0 + t; e < b1; e += kST) idx[e - b0] = P.occ_row[e];
+      stage(idx, P.occ_row + b0, b1 - b0);
       __syncthreads();
       if (q.g < q.G) {
         const int32_t lo = o0 > b0 ? o0 : b0, hi = o1 < b1 ? o1 : b1;
         int32_t o = o0 + q.g;
         if (o < lo) o += (lo - o + q.G - 1) / q.G * q.G;
-#pragma unroll 4
+#pragma unroll 8
         for (; o < hi; o += q.G) acc += Ui[int64_t(idx[o - b0]) * b * k];
       }
     }
     if (q.g < q.G) part[q.g * q.ne + (t - q.g * q.ne)] = acc;
   }
   __syncthreads();
-  const int64_t node = P.order[q.f + q.c];
-  const int64_t at = ((q.mat * d.n + node) * b + q.i) * k + q.koff;
   if (t < q.ne) {
     T v = T(0);
     for (int gg = 0; gg < q.G; ++gg) v += part[gg * q.ne + t];
-    rs[t] = y[at] - v;
+    rs[t] = yv - v;
   }
   __syncthreads();
   T zv = T(0);
@@ -142,9 +163,9 @@ __global__ void __launch_bounds__(kST) js_forward(JunctionPlanDev P, SDims d, in
   if (t < q.ne) rs[t] = zv;  // z_J, s b x kt
   __syncthreads();
   // the later rows' vectors: entry (a, i, kc) = sum_I W_{a,J}[i][I] z_J[I][kc]
-  const int nr = P.ch_n[q.id], per = b * q.kt;
-  const T *Wp = W + (q.mat * d.npanel + P.ch_pbase[q.id] + int64_t(q.s) * q.s) * bb;
-  T *Ur = U + (q.mat * d.nrows + P.rows_ptr[q.id]) * b * k + k0;
+  const int nr = q.nr, per = b * q.kt;
+  const T *Wp = W + (q.mat * d.npanel + q.pbase + int64_t(q.s) * q.s) * bb;
+  T *Ur = U + (q.mat * d.nrows + q.rows) * b * k + k0;
   for (int e = t; e < nr * per; e += kST) {
     const int a = e / per, rem = e - a * per, i = rem / q.kt, kc = rem - i * q.kt;
     const T *Wa = Wp + int64_t(a) * q.s * bb + i * b;
@@ -169,27 +190,31 @@ __global__ void __launch_bounds__(kST) js_backward(JunctionPlanDev P, SDims d, i
   extern __shared__ char smem_raw[];
   T *Ri = reinterpret_cast<T *>(smem_raw);
   const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
-  const Tile q = tile_setup<T, BC>(P, d, cbase, RJ, Ri);
+  const Tile q = tile_setup<BC>(P, d, cbase);
   T *part = Ri + q.sb * q.sb, *rs = part + kST;
   int32_t *idx = reinterpret_cast<int32_t *>(rs + kST);
   const int64_t k = d.k;
   const int l = q.i;  // entry I = c b + l of the chunk's columns
+  const int64_t node = P.order[q.f + q.c];
+  const int64_t at = ((q.mat * d.n + node) * b + l) * k + q.koff;
+  const T vv = t < q.ne ? v[at] : T(0);  // read before any write of x (v may be x)
+  stage(Ri, RJ + (q.mat * d.nrinv + q.rbase) * bb, q.sb * q.sb);
   {
-    const int nr = P.ch_n[q.id];
-    const int64_t rb = P.rows_ptr[q.id];
+    const int nr = q.nr;
+    const int64_t rb = q.rows;
     // column l of block (a, c) of the panel: stride b down its rows
-    const T *Wc = W + (q.mat * d.npanel + P.ch_pbase[q.id] + int64_t(q.s) * q.s + q.c) * bb + l;
+    const T *Wc = W + (q.mat * d.npanel + q.pbase + int64_t(q.s) * q.s + q.c) * bb + l;
     const T *xm = x + q.mat * d.n * b * k + q.koff;
     T acc = T(0);
     for (int a0 = 0; a0 < nr; a0 += kIdx) {  // the later rows' labels, staged in LDS
       const int a1 = nr - a0 < kIdx ? nr : a0 + kIdx;
       __syncthreads();  // the previous batch has been read
-      for (int e = a0 + t; e < a1; e += kST) idx[e - a0] = P.row_node[rb + e];
+      stage(idx, P.row_node + rb + a0, a1 - a0);
       __syncthreads();
       if (q.g < q.G) {
         int a = q.g;
         if (a < a0) a += (a0 - a + q.G - 1) / q.G * q.G;
-#pragma unroll 2
+#pragma unroll 4
         for (; a < a1; a += q.G) {
           const T *Wb = Wc + int64_t(a) * q.s * bb;
           const T *xw = xm + int64_t(idx[a - a0]) * b * k;
@@ -201,12 +226,10 @@ __global__ void __launch_bounds__(kST) js_backward(JunctionPlanDev P, SDims d, i
     if (q.g < q.G) part[q.g * q.ne + (t - q.g * q.ne)] = acc;
   }
   __syncthreads();
-  const int64_t node = P.order[q.f + q.c];
-  const int64_t at = ((q.mat * d.n + node) * b + l) * k + q.koff;
   if (t < q.ne) {
     T s = T(0);
     for (int gg = 0; gg < q.G; ++gg) s += part[gg * q.ne + t];
-    rs[t] = v[at] - s;
+    rs[t] = vv - s;
   }
   __syncthreads();
   if (t < q.ne) {
