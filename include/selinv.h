@@ -558,7 +558,11 @@ SELINV_API int selinv_junction_logdet_f32(const selinv_junction_plan *plan, int6
  *     call with the same plan and B; where that call reported info != 0 for
  *     a matrix, that matrix's x is unspecified.  The solve's workspace:
  *     selinv_junction_solve_workspace_bytes(plan, B, k) (per later row of
- *     every chunk a b x k vector); the sample needs none. */
+ *     every chunk a b x k vector, and the flags of its single-launch
+ *     sweeps); the sample needs none.  Each solve sweep is one launch whose
+ *     workgroups wait for one another (bounded by selinv_set_wait_limit); if
+ *     a wait gives up, every x entry computed after that is NaN (there is no
+ *     info output): calling again, or raising the limit, is the remedy. */
 SELINV_API size_t selinv_junction_factor_bytes(const selinv_junction_plan *plan, int64_t B);
 SELINV_API size_t selinv_junction_factor_workspace_bytes(const selinv_junction_plan *plan,
                                                         int64_t B);

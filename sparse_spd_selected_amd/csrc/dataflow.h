@@ -53,6 +53,30 @@ __device__ __forceinline__ void store_coherent(T *p, T v) {
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Reads of values that other workgroups of the same launch stored with
+// store_coherent, performed at the point of coherence as load_coherent's
+// are (the same cache policy, sc1) but as plain buffer loads: the compiler
+// waits for every atomic load before the next one is issued, while these can
+// be in flight together.  Reads must follow the handshake (acquire()), and
+// the region [base, base + n) must be smaller than 2^31 bytes.
+template <typename T>
+struct CoherentReader {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "4- or 8-byte values");
+  static constexpr int kWord3 = 0x00020000;  // untyped buffer access (gfx9 family)
+  static constexpr int kSc1 = 16;            // cache policy: device scope
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ CoherentReader(const T *base, int64_t n)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(base), static_cast<short>(0),
+                                            static_cast<int>(n * int64_t(sizeof(T))), kWord3)) {}
+  __device__ __forceinline__ T operator[](int64_t i) const {
+    const int off = static_cast<int>(i * int64_t(sizeof(T)));
+    if constexpr (sizeof(T) == 8)
+      return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kSc1));
+    else
+      return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSc1));
+  }
+};
+
 // Row i of an 8 x 8 state block stored interleaved, element (i, c) at
 // c * 8 + i, so that each coherent access instruction covers 64 contiguous
 // bytes of a slot.

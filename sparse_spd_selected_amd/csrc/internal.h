@@ -85,6 +85,7 @@ struct JunctionPlanDev {
   int32_t *it_tg = nullptr, *it_lo = nullptr, *it_hi = nullptr, *it_slot = nullptr;
   int32_t *multi_tg = nullptr, *it_ptr = nullptr;
   int32_t *row_node = nullptr, *occ_ptr = nullptr, *occ_row = nullptr;
+  int32_t *fdep_ptr = nullptr, *fdep = nullptr, *bdep_ptr = nullptr, *bdep = nullptr;
 };
 
 }  // namespace selinv

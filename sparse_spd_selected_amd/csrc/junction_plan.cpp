@@ -118,6 +118,10 @@ struct HostTables {
   // solve sweeps: the label of every flat row, and per flat column the flat
   // rows whose node is that column's node (in flat-row order)
   Vec row_node, occ_ptr, occ_row;
+  // single-launch solve: per chunk, the chunks it waits for in the forward
+  // sweep (fdep: those whose later rows hold its nodes) and in the backward
+  // sweep (bdep: those that hold the nodes of its later rows)
+  Vec fdep_ptr, fdep, bdep_ptr, bdep;
   std::vector<int64_t> fptr;
   // Schur-sum work items: each target's pair list cut into runs of at most
   // kItemPairs; targets with several items add partial sums (slots)
@@ -344,6 +348,31 @@ int analyze(int64_t n, int64_t m, const int32_t *edge_index_host, const int32_t 
         h.occ_row[next[flat_col(N[a])]++] = static_cast<int32_t>(h.rows_ptr[id] + a);
     }
   }
+  // ---- dependencies of the single-launch solve.  The nodes of a chunk's
+  // later rows belong to its ancestors in the elimination tree, which have
+  // higher chunk levels and so larger ids; fdep is the transposed relation.
+  h.bdep_ptr.assign(nch + 1, 0);
+  for (int64_t id = 0; id < nch; ++id) {
+    int32_t last = -1;
+    for (const int32_t w : below(chunk_at[id])) {  // positions ascending: chunks ascending
+      const int32_t x = id_of[chunk_of[w]];
+      if (x == last) continue;
+      if (x <= id) return SELINV_ERR_BAD_PATTERN;  // cannot happen: ancestors come later
+      h.bdep.push_back(x);
+      last = x;
+    }
+    h.bdep_ptr[id + 1] = static_cast<int32_t>(h.bdep.size());
+  }
+  h.fdep_ptr.assign(nch + 1, 0);
+  for (const int32_t x : h.bdep) h.fdep_ptr[x + 1]++;
+  for (int64_t id = 0; id < nch; ++id) h.fdep_ptr[id + 1] += h.fdep_ptr[id];
+  h.fdep.resize(h.bdep.size());
+  {
+    Vec next(h.fdep_ptr.begin(), h.fdep_ptr.end() - 1);
+    for (int64_t id = 0; id < nch; ++id)
+      for (int32_t e = h.bdep_ptr[id]; e < h.bdep_ptr[id + 1]; ++e)
+        h.fdep[next[h.bdep[e]]++] = static_cast<int32_t>(id);
+  }
   // ---- forward targets: every panel block (r >= col), chunk by chunk
   const int64_t ntg = h.ch_tptr[nch];
   h.tg_chunk.resize(ntg);
@@ -523,7 +552,8 @@ extern "C" int selinv_junction_plan_create(int64_t n, int64_t m, const int32_t *
                        align_up(2 * h.npairs * i4) + align_up(h.ng * i4) +
                        align_up(h.npanel * i4) + 4 * align_up(h.nitems * i4) +
                        align_up(h.multi_tg.size() * i4) + align_up((h.ntg + 1) * i4) +
-                       2 * align_up(h.nrows * i4) + align_up((n + 1) * i4) + 4096;
+                       2 * align_up(h.nrows * i4) + align_up((n + 1) * i4) +
+                       2 * align_up((h.nch + 1) * i4) + 2 * align_up(h.bdep.size() * i4) + 4096;
   if (hipMalloc(&plan->dev_block, bytes) != hipSuccess) {
     delete plan;
     return SELINV_ERR_HIP;
@@ -559,6 +589,10 @@ extern "C" int selinv_junction_plan_create(int64_t n, int64_t m, const int32_t *
   dv.row_node = cv.take<int32_t>(h.nrows);
   dv.occ_ptr = cv.take<int32_t>(n + 1);
   dv.occ_row = cv.take<int32_t>(h.nrows);
+  dv.fdep_ptr = cv.take<int32_t>(h.nch + 1);
+  dv.fdep = cv.take<int32_t>(h.fdep.size());
+  dv.bdep_ptr = cv.take<int32_t>(h.nch + 1);
+  dv.bdep = cv.take<int32_t>(h.bdep.size());
   std::vector<int32_t> itptr32(h.ntg + 1);
   for (int64_t t = 0; t <= h.ntg; ++t) itptr32[t] = static_cast<int32_t>(h.it_ptr[t]);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -595,6 +629,10 @@ extern "C" int selinv_junction_plan_create(int64_t n, int64_t m, const int32_t *
   up(dv.row_node, h.row_node.data(), h.nrows * i4);
   up(dv.occ_ptr, h.occ_ptr.data(), (n + 1) * i4);
   up(dv.occ_row, h.occ_row.data(), h.nrows * i4);
+  up(dv.fdep_ptr, h.fdep_ptr.data(), (h.nch + 1) * i4);
+  up(dv.fdep, h.fdep.data(), h.fdep.size() * i4);
+  up(dv.bdep_ptr, h.bdep_ptr.data(), (h.nch + 1) * i4);
+  up(dv.bdep, h.bdep.data(), h.bdep.size() * i4);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) {
     selinv_junction_plan_destroy(plan);

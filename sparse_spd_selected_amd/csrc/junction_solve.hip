@@ -27,18 +27,35 @@
 // produced, spread over all rows of a level instead of serialised on the
 // few separator chunks whose nodes occur in many panels.
 //
-// One workgroup per (chunk, matrix, tile of right-hand sides) and level.
-// Thread e of the first s b kt threads owns entry (I, kc) of the chunk's
-// s b x kt tile; the workgroup's other threads form further groups that split
-// the sum over occurrences (forward) or later rows (backward), and the groups'
-// partial sums are added in a fixed order, so results are deterministic.
-// Vectors are [B][n][b][k] by label, k fastest: consecutive threads read
-// consecutive right-hand sides.  The solve keeps z in the output (the
-// backward pass of chunk J reads z_J before any thread writes x_J, and no
-// chunk of the same level reads J's nodes); its workspace is the row buffer
-// [B][rows][b][k].  The sample runs the backward pass alone, without one.
+// One workgroup per (chunk, matrix, tile of right-hand sides).  Thread e of
+// the first s b kt threads owns entry (I, kc) of the chunk's s b x kt tile;
+// the workgroup's other threads form further groups that split the sum over
+// occurrences (forward) or later rows (backward), and the groups' partial sums
+// are added in a fixed order, so results are deterministic.  Vectors are
+// [B][n][b][k] by label, k fastest: consecutive threads read consecutive
+// right-hand sides.  The solve keeps z in the output (the backward pass of
+// chunk J reads z_J before any thread writes x_J, and no chunk that runs
+// before J has written x_J reads J's nodes).
+//
+// Schedules.  The solve runs each sweep as one launch over all chunks
+// (kDF): workgroups in chunk-id order for the forward sweep (children have
+// lower chunk levels, hence lower ids) and in reverse for the backward sweep.
+// A workgroup first issues every load that needs no other chunk (its plan
+// entries, y or z, R_J^-1), then waits for the flags of the chunks it reads
+// (fdep: those whose later rows hold its nodes; bdep: those holding the nodes
+// of its later rows), computes, stores and sets its own flag once its stores
+// have completed.  Rows and x that cross workgroups are written and read with
+// device-coherent accesses, and every wait is bounded, as in dataflow.h; a
+// call whose wait gives up writes NaN into every x entry computed after that.
+// Its workspace is the row buffer [B][rows][b][k], then the two sweeps' flags
+// and the give-up word.  The sample has no workspace: it runs the backward
+// sweep as one launch per chunk level (levels downward), which orders the
+// chunks by kernel boundaries instead.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
+#include "dataflow.h"
 #include "internal.h"
 
 namespace selinv {
@@ -50,7 +67,68 @@ constexpr int kIdx = 1024;  // row indices per LDS staging batch
 struct SDims {
   int64_t n, npanel, nrinv, nrows, k;
   int kt, b;
+  int64_t nch, B, nkt;  // chunks, matrices, tiles of right-hand sides
 };
+
+// Reads of a region that other workgroups of the same launch write (kDF:
+// at the point of coherence, several in flight), or plain loads.
+template <bool kDF, typename T>
+struct Reader {
+  const T *p;
+  __device__ __forceinline__ Reader(const T *base, int64_t) : p(base) {}
+  __device__ __forceinline__ T operator[](int64_t i) const { return p[i]; }
+};
+
+template <typename T>
+struct Reader<true, T> : df::CoherentReader<T> {
+  __device__ __forceinline__ Reader(const T *base, int64_t n) : df::CoherentReader<T>(base, n) {}
+};
+
+template <bool kDF, typename T>
+__device__ __forceinline__ void st(T *p, T v) {
+  if constexpr (kDF)
+    df::store_coherent(p, v);
+  else
+    *p = v;
+}
+
+// Waits (bounded) until flags[dep[e] * per + off] >= 1 for every e in
+// [d0, d1), the workgroup's threads sharing the list; then no load of the
+// workgroup moves above the waits.
+__device__ inline void wait_deps(const int32_t *flags, const int32_t *dep, int32_t d0, int32_t d1,
+                                 int64_t per, int64_t off, int32_t *timeout, uint64_t ticks) {
+  const uint64_t deadline = df::deadline_after(ticks);
+  for (int32_t e = d0 + static_cast<int32_t>(threadIdx.x); e < d1; e += kST) {
+    const int32_t *f = flags + int64_t(dep[e]) * per + off;
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < 1) {
+      if (df::timed_out(timeout)) break;
+      if (static_cast<uint64_t>(wall_clock64()) >= deadline) {
+        __hip_atomic_store(timeout, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  df::acquire();
+}
+
+// The workgroup's (chunk id, matrix, tile of right-hand sides): one launch
+// per level (blockIdx = (chunk in level, matrix, tile)), or one launch over
+// all chunks, chunk-major, ascending (forward) or descending (backward).
+template <bool kDF>
+__device__ inline void workgroup_item(const SDims &d, int64_t cbase, bool descending,
+                                      int64_t &id, int64_t &mat, int64_t &kz) {
+  if constexpr (kDF) {
+    const int64_t per = d.B * d.nkt, w = blockIdx.x, c = w / per, r = w - c * per;
+    id = descending ? d.nch - 1 - c : c;
+    mat = r / d.nkt;
+    kz = r - mat * d.nkt;
+  } else {
+    id = cbase + blockIdx.x;
+    mat = blockIdx.y;
+    kz = blockIdx.z;
+  }
+}
 
 // dst[0 .. n) = src[0 .. n) by the workgroup, n >= 1: each thread issues up to
 // kR loads (at clamped, in-range addresses) before it waits for any of them,
@@ -77,12 +155,13 @@ struct Tile {
 // All plan entries of the chunk are read here, together, before any of them
 // is waited for.
 template <int BC>
-__device__ inline Tile tile_setup(const JunctionPlanDev &P, const SDims &d, int64_t cbase) {
+__device__ inline Tile tile_setup(const JunctionPlanDev &P, const SDims &d, int64_t id,
+                                  int64_t mat, int64_t kz) {
   Tile q;
   const int b = BC ? BC : d.b, t = threadIdx.x;
-  q.id = cbase + blockIdx.x;
-  q.mat = blockIdx.y;
-  const int64_t k0 = int64_t(blockIdx.z) * d.kt;
+  q.id = id;
+  q.mat = mat;
+  const int64_t k0 = kz * d.kt;
   q.kt = d.k - k0 < d.kt ? static_cast<int>(d.k - k0) : d.kt;
   q.s = P.ch_s[q.id];
   q.f = P.ch_first[q.id];
@@ -104,17 +183,21 @@ __device__ inline Tile tile_setup(const JunctionPlanDev &P, const SDims &d, int6
   return q;
 }
 
-// Forward level: z_J = R_J^-1 (y_J - sum of the row vectors of J's nodes),
-// then u_a = W_{a,J} z_J for every later row a of J into the row buffer U
-template <typename T, int BC>
+// Forward: z_J = R_J^-1 (y_J - sum of the row vectors of J's nodes), then
+// u_a = W_{a,J} z_J for every later row a of J into the row buffer U
+template <typename T, int BC, bool kDF>
 __global__ void __launch_bounds__(kST) js_forward(JunctionPlanDev P, SDims d, int64_t cbase,
                                                   const T *__restrict__ W,
                                                   const T *__restrict__ RJ,
-                                                  const T *__restrict__ y, T *z, T *U) {
+                                                  const T *__restrict__ y, T *z, T *U,
+                                                  int32_t *flags, int32_t *timeout,
+                                                  uint64_t ticks) {
   extern __shared__ char smem_raw[];
   T *Ri = reinterpret_cast<T *>(smem_raw);
   const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
-  const Tile q = tile_setup<BC>(P, d, cbase);
+  int64_t id, mat, kz;
+  workgroup_item<kDF>(d, cbase, false, id, mat, kz);
+  const Tile q = tile_setup<BC>(P, d, id, mat, kz);
   T *part = Ri + q.sb * q.sb, *rs = part + kST;
   int32_t *idx = reinterpret_cast<int32_t *>(rs + kST);
   const int64_t k = d.k, k0 = q.koff - q.kc;
@@ -127,10 +210,15 @@ __global__ void __launch_bounds__(kST) js_forward(JunctionPlanDev P, SDims d, in
   const int64_t at = ((q.mat * d.n + node) * b + q.i) * k + q.koff;
   const T yv = t < q.ne ? y[at] : T(0);
   stage(Ri, RJ + (q.mat * d.nrinv + q.rbase) * bb, q.sb * q.sb);
+  const int64_t per_ch = d.B * d.nkt, self = q.mat * d.nkt + kz;
+  if constexpr (kDF)  // the chunks whose later rows hold J's nodes
+    wait_deps(flags, P.fdep, P.fdep_ptr[q.id], P.fdep_ptr[q.id + 1], per_ch, self, timeout,
+              ticks);
   {
     // the occurrences' row indices are staged in LDS in batches, so that the
     // row-vector loads do not wait on index loads
-    const T *Ui = Um + int64_t(q.i) * k + q.koff;
+    const Reader<kDF, T> Ur(Um, d.nrows * b * k);  // this matrix's row buffer
+    const int64_t ui = int64_t(q.i) * k + q.koff;
     T acc = T(0);
     for (int32_t b0 = ob; b0 < oe; b0 += kIdx) {
       const int32_t b1 = oe - b0 < kIdx ? oe : b0 + kIdx;
@@ -142,7 +230,7 @@ __global__ void __launch_bounds__(kST) js_forward(JunctionPlanDev P, SDims d, in
         int32_t o = o0 + q.g;
         if (o < lo) o += (lo - o + q.G - 1) / q.G * q.G;
 #pragma unroll 8
-        for (; o < hi; o += q.G) acc += Ui[int64_t(idx[o - b0]) * b * k];
+        for (; o < hi; o += q.G) acc += Ur[int64_t(idx[o - b0]) * b * k + ui];
       }
     }
     if (q.g < q.G) part[q.g * q.ne + (t - q.g * q.ne)] = acc;
@@ -175,22 +263,26 @@ __global__ void __launch_bounds__(kST) js_forward(JunctionPlanDev P, SDims d, in
 #pragma unroll
       for (int l = 0; l < b; ++l) acc += Wb[l] * zc[l * q.kt];
     }
-    Ur[(int64_t(a) * b + i) * k + kc] = acc;
+    st<kDF>(Ur + (int64_t(a) * b + i) * k + kc, acc);
   }
+  if constexpr (kDF) df::publish(flags, q.id * per_ch + self, t == 0, 1);
 }
 
-// Backward level: x_J = R_J^-T (v_J - W_{N,J}^T x_N).  v may be x itself
-// (the solve): the tile reads v_J before the barrier that precedes its
-// writes, and no other workgroup of the level touches J's nodes.
-template <typename T, int BC>
+// Backward: x_J = R_J^-T (v_J - W_{N,J}^T x_N).  v may be x itself (the
+// solve): the tile reads v_J before it writes x_J, and the chunks that read
+// J's nodes (its descendants) run after it.
+template <typename T, int BC, bool kDF>
 __global__ void __launch_bounds__(kST) js_backward(JunctionPlanDev P, SDims d, int64_t cbase,
                                                    const T *__restrict__ W,
                                                    const T *__restrict__ RJ, const T *v,
-                                                   T *x) {
+                                                   T *x, int32_t *flags, int32_t *timeout,
+                                                   uint64_t ticks) {
   extern __shared__ char smem_raw[];
   T *Ri = reinterpret_cast<T *>(smem_raw);
   const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
-  const Tile q = tile_setup<BC>(P, d, cbase);
+  int64_t id, mat, kz;
+  workgroup_item<kDF>(d, cbase, true, id, mat, kz);
+  const Tile q = tile_setup<BC>(P, d, id, mat, kz);
   T *part = Ri + q.sb * q.sb, *rs = part + kST;
   int32_t *idx = reinterpret_cast<int32_t *>(rs + kST);
   const int64_t k = d.k;
@@ -199,12 +291,16 @@ __global__ void __launch_bounds__(kST) js_backward(JunctionPlanDev P, SDims d, i
   const int64_t at = ((q.mat * d.n + node) * b + l) * k + q.koff;
   const T vv = t < q.ne ? v[at] : T(0);  // read before any write of x (v may be x)
   stage(Ri, RJ + (q.mat * d.nrinv + q.rbase) * bb, q.sb * q.sb);
+  const int64_t per_ch = d.B * d.nkt, self = q.mat * d.nkt + kz;
+  if constexpr (kDF)  // the chunks that hold the nodes of J's later rows
+    wait_deps(flags, P.bdep, P.bdep_ptr[q.id], P.bdep_ptr[q.id + 1], per_ch, self, timeout,
+              ticks);
   {
     const int nr = q.nr;
     const int64_t rb = q.rows;
     // column l of block (a, c) of the panel: stride b down its rows
     const T *Wc = W + (q.mat * d.npanel + q.pbase + int64_t(q.s) * q.s + q.c) * bb + l;
-    const T *xm = x + q.mat * d.n * b * k + q.koff;
+    const Reader<kDF, T> xr(x + q.mat * d.n * b * k, d.n * b * k);  // this matrix's x
     T acc = T(0);
     for (int a0 = 0; a0 < nr; a0 += kIdx) {  // the later rows' labels, staged in LDS
       const int a1 = nr - a0 < kIdx ? nr : a0 + kIdx;
@@ -217,9 +313,9 @@ __global__ void __launch_bounds__(kST) js_backward(JunctionPlanDev P, SDims d, i
 #pragma unroll 4
         for (; a < a1; a += q.G) {
           const T *Wb = Wc + int64_t(a) * q.s * bb;
-          const T *xw = xm + int64_t(idx[a - a0]) * b * k;
+          const int64_t xw = int64_t(idx[a - a0]) * b * k + q.koff;
 #pragma unroll
-          for (int i = 0; i < b; ++i) acc += Wb[i * b] * xw[i * k];
+          for (int i = 0; i < b; ++i) acc += Wb[i * b] * xr[xw + i * k];
         }
       }
     }
@@ -235,8 +331,38 @@ __global__ void __launch_bounds__(kST) js_backward(JunctionPlanDev P, SDims d, i
   if (t < q.ne) {
     T s = T(0);
     for (int K = q.I; K < q.sb; ++K) s += Ri[K * q.sb + q.I] * rs[K * q.kt + q.kc];
-    x[at] = s;
+    if constexpr (kDF) {
+      if (df::timed_out(timeout)) s = static_cast<T>(__builtin_nan(""));
+    }
+    st<kDF>(x + at, s);
   }
+  if constexpr (kDF) df::publish(flags, q.id * per_ch + self, t == 0, 1);
+}
+
+// Right-hand sides per tile and tiles (k >= 1)
+inline void rhs_tiles(const selinv_junction_plan *plan, int64_t k, int &kt, int64_t &nkt) {
+  const int64_t ktl = kST / (plan->smax * plan->b);
+  kt = static_cast<int>(k < ktl ? k : ktl);
+  nkt = (k + kt - 1) / kt;
+}
+
+// Workspace of a solve: the row buffer, then the flags of both sweeps
+// ([2][nch][B][nkt]) and the give-up word.
+struct SolveWs {
+  size_t rows, flags, total;
+};
+
+inline SolveWs solve_ws(const selinv_junction_plan *plan, int64_t B, int64_t k) {
+  if (B <= 0 || k <= 0) return SolveWs{0, 0, 0};
+  int kt;
+  int64_t nkt;
+  rhs_tiles(plan, k, kt, nkt);
+  SolveWs o;
+  o.rows = align_up(size_t(B) * plan->rows_ptr[plan->nch] * plan->b * size_t(k) *
+                    plan->dtype_bytes);
+  o.flags = 2 * size_t(plan->nch) * size_t(B) * size_t(nkt);
+  o.total = o.rows + align_up((o.flags + 1) * sizeof(int32_t));
+  return o;
 }
 
 template <typename T, int BC>
@@ -244,30 +370,47 @@ hipError_t apply_run(const selinv_junction_plan *plan, int64_t B, const T *facto
                      bool sample, const T *in, T *out, void *ws, hipStream_t s) {
   const int b = plan->b, sbm = plan->smax * b;
   if (sbm > kST) return hipErrorInvalidValue;
-  const int64_t ktl = kST / sbm;
-  const int kt = static_cast<int>(k < ktl ? k : ktl);
-  const int64_t nkt = (k + kt - 1) / kt;
+  int kt;
+  int64_t nkt;
+  rhs_tiles(plan, k, kt, nkt);
   if (nkt > 65535) return hipErrorInvalidValue;
-  const SDims d{plan->n, plan->npanel, plan->nrinv, plan->rows_ptr[plan->nch], k, kt, b};
+  const SDims d{plan->n,  plan->npanel, plan->nrinv, plan->rows_ptr[plan->nch], k, kt, b,
+                plan->nch, B,           nkt};
   const T *W = factor, *RJ = factor + B * plan->npanel * int64_t(b) * b;
   const size_t lds = sizeof(T) * (size_t(sbm) * sbm + 2 * kST) + sizeof(int32_t) * kIdx;
   const auto &lo = plan->level_off;
   const unsigned By = static_cast<unsigned>(B), Z = static_cast<unsigned>(nkt);
-  if (!sample)
-    for (int32_t l = 0; l < plan->levels; ++l)
-      js_forward<T, BC><<<dim3(static_cast<unsigned>(lo[l + 1] - lo[l]), By, Z), dim3(kST), lds,
-                          s>>>(plan->dev, d, lo[l], W, RJ, in, out, static_cast<T *>(ws));
-  const T *v = sample ? in : out;
-  for (int32_t l = plan->levels - 1; l >= 0; --l)
-    js_backward<T, BC><<<dim3(static_cast<unsigned>(lo[l + 1] - lo[l]), By, Z), dim3(kST), lds,
-                         s>>>(plan->dev, d, lo[l], W, RJ, v, out);
+  if (sample) {  // no workspace: one launch per level, levels downward
+    for (int32_t l = plan->levels - 1; l >= 0; --l)
+      js_backward<T, BC, false><<<dim3(static_cast<unsigned>(lo[l + 1] - lo[l]), By, Z),
+                                  dim3(kST), lds, s>>>(plan->dev, d, lo[l], W, RJ, in, out,
+                                                       nullptr, nullptr, 0);
+    return hipGetLastError();
+  }
+  const int64_t grid = plan->nch * B * nkt;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  // a matrix's row buffer and vector are read through 32-bit buffer offsets
+  const int64_t span = std::max(d.nrows, d.n) * b * k * int64_t(sizeof(T));
+  if (span >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const SolveWs o = solve_ws(plan, B, k);
+  T *U = static_cast<T *>(ws);
+  int32_t *flags = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + o.rows);
+  int32_t *fflags = flags, *bflags = flags + o.flags / 2, *timeout = flags + o.flags;
+  hipError_t e = df::launch_init(static_cast<int64_t>(o.flags), flags, nullptr, timeout, s);
+  if (e != hipSuccess) return e;
+  const uint64_t wt = wait_limit_ticks();
+  const unsigned G = static_cast<unsigned>(grid);
+  js_forward<T, BC, true><<<dim3(G), dim3(kST), lds, s>>>(plan->dev, d, 0, W, RJ, in, out, U,
+                                                          fflags, timeout, wt);
+  js_backward<T, BC, true><<<dim3(G), dim3(kST), lds, s>>>(plan->dev, d, 0, W, RJ, out, out,
+                                                           bflags, timeout, wt);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t junction_solve_workspace_bytes(const selinv_junction_plan *plan, int64_t B, int64_t k) {
-  return size_t(B) * plan->rows_ptr[plan->nch] * plan->b * size_t(k) * plan->dtype_bytes;
+  return solve_ws(plan, B, k).total;
 }
 
 template <typename T>

@@ -157,6 +157,30 @@ def test_repeated_calls_are_bitwise_identical(ssa):
     assert torch.equal(a, b_) and torch.equal(s1, s2)
 
 
+def test_solve_wait_limit_gives_nan(ssa):
+    """With a zero wait bound the single-launch solve gives up at the first
+    unready flag: the call still ends, and every entry of x is NaN (every
+    backward workgroup sees the give-up word).  A path pattern eliminated end
+    to end makes the chunks a chain, each waiting for the one before it.  With
+    the default bound restored, the same solve is exact again."""
+    n = 2000
+    e = spdgen.grid_edges(1, n)
+    d, v = spdgen.graph(e, n, 4, B=1, seed=5)
+    y = spdgen.cotangent((1, n, 4, 1), seed=5, k=0)
+    f = ssa.junction_factor(_to(d, torch.float64), e, _to(v, torch.float64))
+    Y = _to(y, torch.float64)
+    old = ssa.wait_limit()
+    try:
+        ssa.set_wait_limit(0)
+        x = f.solve(Y)
+        torch.cuda.synchronize()
+    finally:
+        ssa.set_wait_limit(old)
+    assert torch.isnan(x).all()
+    ref, _ = oracle.junction_apply(d, e, v, y, "solve")
+    _cmp_vec("solve", f.solve(Y), ref, torch.float64)
+
+
 def test_abi_arguments(ssa):
     """Status codes of the C entry points: k = 0 and B = 0 do nothing; an
     output that aliases the input, a short workspace, a wrong dtype and a
@@ -177,7 +201,8 @@ def test_abi_arguments(ssa):
         ssa.INVALID_ARG
     assert L.selinv_junction_sample_f64(h, 1, None, 1, yp, yp + 8, None) == ssa.INVALID_ARG
     assert L.selinv_junction_solve_f32(h, 1, fp, 1, yp, yp + 8, wp, nb, None) == ssa.INVALID_ARG
-    assert L.selinv_junction_solve_workspace_bytes(h, 1, 2) == 2 * nb > 0
+    assert L.selinv_junction_solve_workspace_bytes(h, 1, 2) > nb > 0
+    assert L.selinv_junction_solve_workspace_bytes(h, 1, 0) == 0
     D, V = _to(d, torch.float64), _to(v, torch.float64)
     ld = torch.empty(1, dtype=torch.float64, device=DEV)
     assert L.selinv_junction_factor_f64(h, 1, D.data_ptr(), V.data_ptr(), None, ld.data_ptr(),
