@@ -128,7 +128,6 @@ __global__ __launch_bounds__(64) void nstree8_collect(
     df::store_coherent(st_fail + p, (bad || child_failed) ? int32_t(1) : int32_t(0));
     if (bad && !child_failed) atomicMin(first_fail, fail_rank[p]);
   }
-  if (valid) r8::store8(st_sinv + p * 64, i, S);
   // message up_v Sinv_v down_v (all slots stage; valid non-root slots store)
   f16::wave_sync();
   sb.put(s, i, Dn);
@@ -139,7 +138,10 @@ __global__ __launch_bounds__(64) void nstree8_collect(
   f16::wave_sync();
   const r8::Row<T> M = r8::mul(U, sa, s, r8::zero<T>());  // up_v X
   if (edge) df::store_interleaved(st_m + p * 64, i, M);
+  // the flag waits for every store issued so far: Sinv_v, read only by later
+  // launches, goes after it
   df::publish(flags, p, valid && i == 0, 1);
+  if (valid) r8::store8(st_sinv + p * 64, i, S);
 }
 
 // Distribute of one tile; workgroup w takes tile w + 1 (root level first).
@@ -189,22 +191,16 @@ __global__ __launch_bounds__(64) void nstree8_distribute(
   sa.put(s, i, V);
   f16::wave_sync();
   const r8::Row<T> Gv = r8::mul(Bm, sa, s, Si);              // Sinv_v + B G_pp A
-  if (valid) {
-    if (failed) {
-      r8::Row<T> nan;
+  r8::Row<T> nan;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) nan.v[k] = static_cast<T>(__builtin_nan(""));
-      r8::store(G_up + v * bb, b, i, nan);
-      r8::store(G_down + v * bb, b, i, nan);
-      r8::store(G_diag + v * bb, b, i, nan);
-    } else {
-      r8::store(G_up + v * bb, b, i, r8::neg(V));
-      r8::store(G_down + v * bb, b, i, r8::neg(W));
-      r8::store(G_diag + v * bb, b, i, Gv);
-      df::store_interleaved(st_m + p * 64, i, Gv);  // for the children
-    }
-  }
+  for (int k = 0; k < 8; ++k) nan.v[k] = static_cast<T>(__builtin_nan(""));
+  if (valid && !failed) df::store_interleaved(st_m + p * 64, i, Gv);  // for the children
   df::publish(flags, p, valid && i == 0, 2);
+  if (valid) {  // the outputs, read only after this launch
+    r8::store(G_up + v * bb, b, i, failed ? nan : r8::neg(V));
+    r8::store(G_down + v * bb, b, i, failed ? nan : r8::neg(W));
+    r8::store(G_diag + v * bb, b, i, failed ? nan : Gv);
+  }
 }
 
 // the root (a launch between the passes): G_rr = Sinv_r (NaN after a

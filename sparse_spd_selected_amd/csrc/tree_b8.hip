@@ -92,9 +92,19 @@ __global__ __launch_bounds__(64) void tree8_collect(
   }
   f16::PivotLog pl;
   const bool bad = r8::gj_inverse(S, sa, s, i, pl);
+  // What the parent reads in this launch is stored before the flag (which
+  // waits for every store issued so far); the rest only after it.
+  const bool failed = bad || child_failed;
+  if (valid && i == 0) store_coherent(st_fail + p, failed ? int32_t(1) : int32_t(0));
+  f16::wave_sync();
+  sa.put(s, i, S);
+  sb.put(s, i, E);
+  f16::wave_sync();
+  const r8::Row<T> X = r8::mul(E, sa, s, r8::zero<T>());   // E_v Sinv_v
+  const r8::Row<T> M = r8::mul_t(X, sb, s, r8::zero<T>());  // X_v E_v^T
+  if (valid && p != 0) df::store_interleaved(st_m + p * 64, i, M);
+  df::publish(flags, p, valid && i == 0, (!kFactor && p == 0) ? 2 : 1);
   if (valid && i == 0) {
-    const bool failed = bad || child_failed;
-    store_coherent(st_fail + p, failed ? int32_t(1) : int32_t(0));
     st_ld[p] = failed ? static_cast<double>(__builtin_nan("")) : pl.log();
     if (bad && !child_failed) atomicMin(first_fail, fail_rank[p]);
   }
@@ -112,14 +122,6 @@ __global__ __launch_bounds__(64) void tree8_collect(
       r8::store(G_edge + v * bb, b, i, r8::zero<T>());
     }
   }
-  f16::wave_sync();
-  sa.put(s, i, S);
-  sb.put(s, i, E);
-  f16::wave_sync();
-  const r8::Row<T> X = r8::mul(E, sa, s, r8::zero<T>());   // E_v Sinv_v
-  const r8::Row<T> M = r8::mul_t(X, sb, s, r8::zero<T>());  // X_v E_v^T
-  if (valid && p != 0) df::store_interleaved(st_m + p * 64, i, M);
-  df::publish(flags, p, valid && i == 0, (!kFactor && p == 0) ? 2 : 1);
 }
 
 // Distribute of one tile; grid = tiles - 1, workgroup w takes tile w + 1
@@ -165,19 +167,14 @@ __global__ __launch_bounds__(64) void tree8_distribute(
   sa.put(s, i, V);
   f16::wave_sync();
   const r8::Row<T> Gv = r8::mul_tn(sb, sa, s, i, Si);     // Sinv_v + X_v^T V
-  if (valid) {
-    if (failed) {
-      r8::Row<T> nan;
+  r8::Row<T> nan;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) nan.v[k] = static_cast<T>(__builtin_nan(""));
-      r8::store(G_edge + v * bb, b, i, nan);
-      df::store_transposed(G_diag + v * bb, b, i, nan);
-    } else {
-      r8::store(G_edge + v * bb, b, i, r8::neg(V));
-      df::store_transposed(G_diag + v * bb, b, i, Gv);
-    }
-  }
+  for (int k = 0; k < 8; ++k) nan.v[k] = static_cast<T>(__builtin_nan(""));
+  // G_vv is read by the children in this launch: stored before the flag;
+  // G_edge only after it
+  if (valid) df::store_transposed(G_diag + v * bb, b, i, failed ? nan : Gv);
   df::publish(flags, p, valid && i == 0, 2);
+  if (valid) r8::store(G_edge + v * bb, b, i, failed ? nan : r8::neg(V));
 }
 
 // ------------------------------------------------------------------ solve

@@ -151,18 +151,6 @@ __global__ __launch_bounds__(64) void tree8_vjp_collect(
   f16::wave_sync();
   const r8::Row<T> P =
       sym_rows(axpby(lb, S, T(-1), r8::mul(S, sb, s, r8::zero<T>())), sb, s, i);
-  if (valid) {
-    r8::store8(arr(kSinv) + p * 64, i, S);
-    r8::store8(arr(kP) + p * 64, i, P);
-  }
-  if (valid && p == 0) {  // the root: diag_bar = P, G_rr = Sinv (in its M slot)
-    // every other collect has published before the root runs; first_fail is
-    // read coherently (another XCD may have lowered it)
-    const bool failed = bad || child_failed || df::load_coherent(first_fail) != INT_MAX;
-    r8::store(d_bar + v * bb, b, i, failed ? nan_row<T>() : P);
-    r8::store(e_bar + v * bb, b, i, r8::zero<T>());
-    df::store_interleaved(arr(kM) + p * 64, i, S);
-  }
   // messages to the parent; sa still holds Sinv
   const r8::Row<T> X = r8::mul(E, sa, s, r8::zero<T>());  // E Sinv
   f16::wave_sync();
@@ -179,13 +167,29 @@ __global__ __launch_bounds__(64) void tree8_vjp_collect(
   sb.put(s, i, X);
   f16::wave_sync();
   const r8::Row<T> N = sym_rows(r8::mul_t(Y1, sb, s, r8::zero<T>()), sa, s, i);  // sym(Y1 X^T)
+  // what the parent reads in this launch goes before the flag (which waits
+  // for every store issued so far), what only later launches read after it
   if (valid && p != 0) {
-    r8::store8(arr(kX) + p * 64, i, X);
-    r8::store8(arr(kZ) + p * 64, i, Z);
     df::store_interleaved(arr(kM) + p * 64, i, M);
     df::store_interleaved(arr(kN) + p * 64, i, N);
   }
   df::publish(flags, p, valid && i == 0, p == 0 ? 2 : 1);
+  if (valid) {
+    r8::store8(arr(kSinv) + p * 64, i, S);
+    r8::store8(arr(kP) + p * 64, i, P);
+  }
+  if (valid && p != 0) {
+    r8::store8(arr(kX) + p * 64, i, X);
+    r8::store8(arr(kZ) + p * 64, i, Z);
+  }
+  if (valid && p == 0) {  // the root: diag_bar = P, G_rr = Sinv (in its M slot)
+    // every other collect has published before the root runs; first_fail is
+    // read coherently (another XCD may have lowered it)
+    const bool failed = bad || child_failed || df::load_coherent(first_fail) != INT_MAX;
+    r8::store(d_bar + v * bb, b, i, failed ? nan_row<T>() : P);
+    r8::store(e_bar + v * bb, b, i, r8::zero<T>());
+    df::store_interleaved(arr(kM) + p * 64, i, S);
+  }
 }
 
 // Distribute of one tile; workgroup w takes tile w + 1 (root level first).
@@ -240,17 +244,17 @@ __global__ __launch_bounds__(64) void tree8_vjp_distribute(
   f16::wave_sync();
   const r8::Row<T> Gv = r8::mul_tn(sa, sb, s, i, Si);  // Sinv + X^T V
   const r8::Row<T> Dn = axpby(T(1), P, T(-1), sym_rows(R, sb, s, i));
-  if (valid) {
-    if (*first_fail != INT_MAX || df::timed_out(timeout)) {
-      r8::store(e_bar + v * bb, b, i, nan_row<T>());
+  const bool failed = *first_fail != INT_MAX || df::timed_out(timeout);
+  if (valid) {  // read by the children in this launch
+    if (failed) {
       df::store_transposed(d_bar + v * bb, b, i, nan_row<T>());
     } else {
-      r8::store(e_bar + v * bb, b, i, Eb);
       df::store_transposed(d_bar + v * bb, b, i, Dn);
       df::store_interleaved(arr(kM) + p * 64, i, Gv);
     }
   }
   df::publish(flags, p, valid && i == 0, 2);
+  if (valid) r8::store(e_bar + v * bb, b, i, failed ? nan_row<T>() : Eb);
 }
 
 // info = -1 if a dataflow wait gave up
