@@ -86,6 +86,7 @@ struct JunctionPlanDev {
   int32_t *multi_tg = nullptr, *it_ptr = nullptr;
   int32_t *row_node = nullptr, *occ_ptr = nullptr, *occ_row = nullptr;
   int32_t *fdep_ptr = nullptr, *fdep = nullptr, *bdep_ptr = nullptr, *bdep = nullptr;
+  int32_t *part_off = nullptr, *split_off = nullptr, *part_chunk = nullptr;
 };
 
 }  // namespace selinv
@@ -103,6 +104,7 @@ struct selinv_junction_plan {
   std::vector<int64_t> it_ptr;     // first Schur work item of every target (ntg + 1)
   std::vector<int64_t> multi_off;  // range of multi-item targets of every level (levels + 1)
   int64_t max_slots = 0;           // partial-sum slots of the busiest level
+  int64_t nparts = 0, nsplit = 0;  // solve workgroups per (matrix, tile); parts of split chunks
   std::vector<int32_t> S_index;    // [2][nnz], host copy for the caller
   std::vector<int32_t> order;      // elimination order (labels)
   selinv::JunctionPlanDev dev;

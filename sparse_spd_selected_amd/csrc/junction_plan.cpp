@@ -122,6 +122,10 @@ struct HostTables {
   // sweep (fdep: those whose later rows hold its nodes) and in the backward
   // sweep (bdep: those that hold the nodes of its later rows)
   Vec fdep_ptr, fdep, bdep_ptr, bdep;
+  // ... and the workgroups ("parts") each chunk is split over: part_off
+  // (prefix over chunks), the chunk of every part, and the prefix over
+  // chunks of the parts of split chunks (slots for partial sums)
+  Vec part_off, part_chunk, split_off;
   std::vector<int64_t> fptr;
   // Schur-sum work items: each target's pair list cut into runs of at most
   // kItemPairs; targets with several items add partial sums (slots)
@@ -373,6 +377,23 @@ int analyze(int64_t n, int64_t m, const int32_t *edge_index_host, const int32_t 
       for (int32_t e = h.bdep_ptr[id]; e < h.bdep_ptr[id + 1]; ++e)
         h.fdep[next[h.bdep[e]]++] = static_cast<int32_t>(id);
   }
+  // Parts: a chunk whose nodes occur in many later rows (forward sum) or
+  // that has many later rows (backward sum) is split over up to kMaxParts
+  // workgroups, about kOccPerPart occurrences or kRowsPerPart rows each.
+  {
+    constexpr int64_t kMaxParts = 8, kOccPerPart = 64, kRowsPerPart = 16;
+    h.part_off.assign(nch + 1, 0);
+    h.split_off.assign(nch + 1, 0);
+    for (int64_t id = 0; id < nch; ++id) {
+      const int64_t occ = h.occ_ptr[h.ch_cptr[id] + h.ch_s[id]] - h.occ_ptr[h.ch_cptr[id]];
+      const int64_t P = std::min<int64_t>(
+          kMaxParts, std::max<int64_t>({1, (occ + kOccPerPart - 1) / kOccPerPart,
+                                        (h.ch_n[id] + kRowsPerPart - 1) / kRowsPerPart}));
+      h.part_off[id + 1] = h.part_off[id] + static_cast<int32_t>(P);
+      h.split_off[id + 1] = h.split_off[id] + static_cast<int32_t>(P > 1 ? P : 0);
+      for (int64_t q = 0; q < P; ++q) h.part_chunk.push_back(static_cast<int32_t>(id));
+    }
+  }
   // ---- forward targets: every panel block (r >= col), chunk by chunk
   const int64_t ntg = h.ch_tptr[nch];
   h.tg_chunk.resize(ntg);
@@ -538,6 +559,8 @@ extern "C" int selinv_junction_plan_create(int64_t n, int64_t m, const int32_t *
   plan->it_ptr = h.it_ptr;
   plan->multi_off = h.multi_off;
   plan->max_slots = h.max_slots;
+  plan->nparts = h.part_off[h.nch];
+  plan->nsplit = h.split_off[h.nch];
   plan->S_index.swap(h.S_index);
   plan->order.swap(h.order);
 
@@ -553,7 +576,8 @@ extern "C" int selinv_junction_plan_create(int64_t n, int64_t m, const int32_t *
                        align_up(h.npanel * i4) + 4 * align_up(h.nitems * i4) +
                        align_up(h.multi_tg.size() * i4) + align_up((h.ntg + 1) * i4) +
                        2 * align_up(h.nrows * i4) + align_up((n + 1) * i4) +
-                       2 * align_up((h.nch + 1) * i4) + 2 * align_up(h.bdep.size() * i4) + 4096;
+                       2 * align_up((h.nch + 1) * i4) + 2 * align_up(h.bdep.size() * i4) +
+                       2 * align_up((h.nch + 1) * i4) + align_up(h.part_chunk.size() * i4) + 4096;
   if (hipMalloc(&plan->dev_block, bytes) != hipSuccess) {
     delete plan;
     return SELINV_ERR_HIP;
@@ -593,6 +617,9 @@ extern "C" int selinv_junction_plan_create(int64_t n, int64_t m, const int32_t *
   dv.fdep = cv.take<int32_t>(h.fdep.size());
   dv.bdep_ptr = cv.take<int32_t>(h.nch + 1);
   dv.bdep = cv.take<int32_t>(h.bdep.size());
+  dv.part_off = cv.take<int32_t>(h.nch + 1);
+  dv.split_off = cv.take<int32_t>(h.nch + 1);
+  dv.part_chunk = cv.take<int32_t>(h.part_chunk.size());
   std::vector<int32_t> itptr32(h.ntg + 1);
   for (int64_t t = 0; t <= h.ntg; ++t) itptr32[t] = static_cast<int32_t>(h.it_ptr[t]);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -633,6 +660,9 @@ extern "C" int selinv_junction_plan_create(int64_t n, int64_t m, const int32_t *
   up(dv.fdep, h.fdep.data(), h.fdep.size() * i4);
   up(dv.bdep_ptr, h.bdep_ptr.data(), (h.nch + 1) * i4);
   up(dv.bdep, h.bdep.data(), h.bdep.size() * i4);
+  up(dv.part_off, h.part_off.data(), (h.nch + 1) * i4);
+  up(dv.split_off, h.split_off.data(), (h.nch + 1) * i4);
+  up(dv.part_chunk, h.part_chunk.data(), h.part_chunk.size() * i4);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) {
     selinv_junction_plan_destroy(plan);

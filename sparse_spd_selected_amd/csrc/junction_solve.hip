@@ -47,8 +47,14 @@
 // have completed.  Rows and x that cross workgroups are written and read with
 // device-coherent accesses, and every wait is bounded, as in dataflow.h; a
 // call whose wait gives up writes NaN into every x entry computed after that.
-// Its workspace is the row buffer [B][rows][b][k], then the two sweeps' flags
-// and the give-up word.  The sample has no workspace: it runs the backward
+// With four or more right-hand sides per tile, a chunk with long sums (many
+// occurrences or later rows; the plan fixes its number of parts) is split
+// over several workgroups: each part adds every P-th term into a slot of
+// its own, and the part that arrives last at the chunk's counter adds the
+// slots in part order and finishes the chunk (results stay deterministic;
+// no part waits for another).  Its workspace is the row buffer
+// [B][rows][b][k], then the flags and counters, the give-up word and the
+// parts' slots.  The sample has no workspace: it runs the backward
 // sweep as one launch per chunk level (levels downward), which orders the
 // chunks by kernel boundaries instead.
 #include <hip/hip_runtime.h>
@@ -63,11 +69,14 @@ namespace {
 
 constexpr int kST = 256;   // threads per workgroup
 constexpr int kIdx = 1024;  // row indices per LDS staging batch
+constexpr int kSplitMinCols = 4;  // right-hand sides per tile from which chunks are split
 
 struct SDims {
   int64_t n, npanel, nrinv, nrows, k;
   int kt, b;
   int64_t nch, B, nkt;  // chunks, matrices, tiles of right-hand sides
+  int64_t nparts;       // parts of all chunks (split chunks count several)
+  bool split;           // single-launch sweeps: one workgroup per part, else per chunk
 };
 
 // Reads of a region that other workgroups of the same launch write (kDF:
@@ -112,22 +121,56 @@ __device__ inline void wait_deps(const int32_t *flags, const int32_t *dep, int32
   df::acquire();
 }
 
-// The workgroup's (chunk id, matrix, tile of right-hand sides): one launch
-// per level (blockIdx = (chunk in level, matrix, tile)), or one launch over
-// all chunks, chunk-major, ascending (forward) or descending (backward).
+// The workgroup's (chunk id, part, parts, matrix, tile of right-hand sides):
+// one launch per level (blockIdx = (chunk in level, matrix, tile), one part),
+// or one launch over all parts of all chunks, part-major, ascending (forward)
+// or descending (backward); the parts of a chunk are consecutive.
 template <bool kDF>
-__device__ inline void workgroup_item(const SDims &d, int64_t cbase, bool descending,
-                                      int64_t &id, int64_t &mat, int64_t &kz) {
+__device__ inline void workgroup_item(const JunctionPlanDev &P, const SDims &d, int64_t cbase,
+                                      bool descending, int64_t &id, int &part, int &nparts,
+                                      int64_t &mat, int64_t &kz) {
   if constexpr (kDF) {
     const int64_t per = d.B * d.nkt, w = blockIdx.x, c = w / per, r = w - c * per;
-    id = descending ? d.nch - 1 - c : c;
+    if (d.split) {
+      const int64_t gp = descending ? d.nparts - 1 - c : c;
+      id = P.part_chunk[gp];
+      const int32_t p0 = P.part_off[id];
+      part = static_cast<int>(gp - p0);
+      nparts = P.part_off[id + 1] - p0;
+    } else {
+      id = descending ? d.nch - 1 - c : c;
+      part = 0;
+      nparts = 1;
+    }
     mat = r / d.nkt;
     kz = r - mat * d.nkt;
   } else {
     id = cbase + blockIdx.x;
+    part = 0;
+    nparts = 1;
     mat = blockIdx.y;
     kz = blockIdx.z;
   }
+}
+
+// A part of a split chunk hands over its partial sums (thread t < ne holds
+// entry t): it stores them in its slot at the point of coherence, and the
+// part that arrives last at the chunk's counter (when every other part's
+// slot is complete) goes on.  Returns true in that part.
+template <typename T>
+__device__ inline bool arrive_last(T *slot, T v, bool has, int32_t *cnt, int nparts,
+                                   int32_t *lds_word) {
+  if (has) df::store_coherent(slot + threadIdx.x, v);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);  // this wavefront's stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *lds_word = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                nparts - 1;
+  __syncthreads();
+  const bool last = *lds_word != 0;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  return last;
 }
 
 // dst[0 .. n) = src[0 .. n) by the workgroup, n >= 1: each thread issues up to
@@ -190,15 +233,16 @@ __global__ void __launch_bounds__(kST) js_forward(JunctionPlanDev P, SDims d, in
                                                   const T *__restrict__ W,
                                                   const T *__restrict__ RJ,
                                                   const T *__restrict__ y, T *z, T *U,
-                                                  int32_t *flags, int32_t *timeout,
-                                                  uint64_t ticks) {
+                                                  int32_t *flags, int32_t *cnt, T *slots,
+                                                  int32_t *timeout, uint64_t ticks) {
   extern __shared__ char smem_raw[];
   T *Ri = reinterpret_cast<T *>(smem_raw);
   const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
   int64_t id, mat, kz;
-  workgroup_item<kDF>(d, cbase, false, id, mat, kz);
+  int part, nparts;
+  workgroup_item<kDF>(P, d, cbase, false, id, part, nparts, mat, kz);
   const Tile q = tile_setup<BC>(P, d, id, mat, kz);
-  T *part = Ri + q.sb * q.sb, *rs = part + kST;
+  T *part_s = Ri + q.sb * q.sb, *rs = part_s + kST;
   int32_t *idx = reinterpret_cast<int32_t *>(rs + kST);
   const int64_t k = d.k, k0 = q.koff - q.kc;
   const T *Um = U + q.mat * d.nrows * b * k;
@@ -225,22 +269,34 @@ __global__ void __launch_bounds__(kST) js_forward(JunctionPlanDev P, SDims d, in
       __syncthreads();  // the previous batch has been read
       stage(idx, P.occ_row + b0, b1 - b0);
       __syncthreads();
-      if (q.g < q.G) {
+      if (q.g < q.G) {  // this part's groups take every stride-th occurrence
         const int32_t lo = o0 > b0 ? o0 : b0, hi = o1 < b1 ? o1 : b1;
-        int32_t o = o0 + q.g;
-        if (o < lo) o += (lo - o + q.G - 1) / q.G * q.G;
+        const int32_t stride = nparts * q.G;
+        int32_t o = o0 + part * q.G + q.g;
+        if (o < lo) o += (lo - o + stride - 1) / stride * stride;
 #pragma unroll 8
-        for (; o < hi; o += q.G) acc += Ur[int64_t(idx[o - b0]) * b * k + ui];
+        for (; o < hi; o += stride) acc += Ur[int64_t(idx[o - b0]) * b * k + ui];
       }
     }
-    if (q.g < q.G) part[q.g * q.ne + (t - q.g * q.ne)] = acc;
+    if (q.g < q.G) part_s[q.g * q.ne + (t - q.g * q.ne)] = acc;
   }
   __syncthreads();
-  if (t < q.ne) {
-    T v = T(0);
-    for (int gg = 0; gg < q.G; ++gg) v += part[gg * q.ne + t];
-    rs[t] = yv - v;
+  T v = T(0);
+  if (t < q.ne)
+    for (int gg = 0; gg < q.G; ++gg) v += part_s[gg * q.ne + t];
+  if constexpr (kDF) {
+    if (nparts > 1) {  // the last part to arrive adds the parts' sums in order
+      const int64_t sl = P.split_off[q.id];
+      T *my = slots + ((sl + part) * per_ch + self) * kST;
+      if (!arrive_last(my, v, t < q.ne, cnt + q.id * per_ch + self, nparts, idx)) return;
+      const df::CoherentReader<T> sr(slots + sl * per_ch * kST,
+                                     int64_t(nparts) * per_ch * kST);
+      v = T(0);
+      if (t < q.ne)
+        for (int pp = 0; pp < nparts; ++pp) v += sr[(pp * per_ch + self) * kST + t];
+    }
   }
+  if (t < q.ne) rs[t] = yv - v;
   __syncthreads();
   T zv = T(0);
   if (t < q.ne) {
@@ -275,15 +331,16 @@ template <typename T, int BC, bool kDF>
 __global__ void __launch_bounds__(kST) js_backward(JunctionPlanDev P, SDims d, int64_t cbase,
                                                    const T *__restrict__ W,
                                                    const T *__restrict__ RJ, const T *v,
-                                                   T *x, int32_t *flags, int32_t *timeout,
-                                                   uint64_t ticks) {
+                                                   T *x, int32_t *flags, int32_t *cnt,
+                                                   T *slots, int32_t *timeout, uint64_t ticks) {
   extern __shared__ char smem_raw[];
   T *Ri = reinterpret_cast<T *>(smem_raw);
   const int b = BC ? BC : d.b, bb = b * b, t = threadIdx.x;
   int64_t id, mat, kz;
-  workgroup_item<kDF>(d, cbase, true, id, mat, kz);
+  int part, nparts;
+  workgroup_item<kDF>(P, d, cbase, true, id, part, nparts, mat, kz);
   const Tile q = tile_setup<BC>(P, d, id, mat, kz);
-  T *part = Ri + q.sb * q.sb, *rs = part + kST;
+  T *part_s = Ri + q.sb * q.sb, *rs = part_s + kST;
   int32_t *idx = reinterpret_cast<int32_t *>(rs + kST);
   const int64_t k = d.k;
   const int l = q.i;  // entry I = c b + l of the chunk's columns
@@ -307,11 +364,12 @@ __global__ void __launch_bounds__(kST) js_backward(JunctionPlanDev P, SDims d, i
       __syncthreads();  // the previous batch has been read
       stage(idx, P.row_node + rb + a0, a1 - a0);
       __syncthreads();
-      if (q.g < q.G) {
-        int a = q.g;
-        if (a < a0) a += (a0 - a + q.G - 1) / q.G * q.G;
+      if (q.g < q.G) {  // this part's groups take every stride-th row
+        const int stride = nparts * q.G;
+        int a = part * q.G + q.g;
+        if (a < a0) a += (a0 - a + stride - 1) / stride * stride;
 #pragma unroll 4
-        for (; a < a1; a += q.G) {
+        for (; a < a1; a += stride) {
           const T *Wb = Wc + int64_t(a) * q.s * bb;
           const int64_t xw = int64_t(idx[a - a0]) * b * k + q.koff;
 #pragma unroll
@@ -319,14 +377,25 @@ __global__ void __launch_bounds__(kST) js_backward(JunctionPlanDev P, SDims d, i
         }
       }
     }
-    if (q.g < q.G) part[q.g * q.ne + (t - q.g * q.ne)] = acc;
+    if (q.g < q.G) part_s[q.g * q.ne + (t - q.g * q.ne)] = acc;
   }
   __syncthreads();
-  if (t < q.ne) {
-    T s = T(0);
-    for (int gg = 0; gg < q.G; ++gg) s += part[gg * q.ne + t];
-    rs[t] = vv - s;
+  T sum = T(0);
+  if (t < q.ne)
+    for (int gg = 0; gg < q.G; ++gg) sum += part_s[gg * q.ne + t];
+  if constexpr (kDF) {
+    if (nparts > 1) {  // the last part to arrive adds the parts' sums in order
+      const int64_t sl = P.split_off[q.id];
+      T *my = slots + ((sl + part) * per_ch + self) * kST;
+      if (!arrive_last(my, sum, t < q.ne, cnt + q.id * per_ch + self, nparts, idx)) return;
+      const df::CoherentReader<T> sr(slots + sl * per_ch * kST,
+                                     int64_t(nparts) * per_ch * kST);
+      sum = T(0);
+      if (t < q.ne)
+        for (int pp = 0; pp < nparts; ++pp) sum += sr[(pp * per_ch + self) * kST + t];
+    }
   }
+  if (t < q.ne) rs[t] = vv - sum;
   __syncthreads();
   if (t < q.ne) {
     T s = T(0);
@@ -346,22 +415,28 @@ inline void rhs_tiles(const selinv_junction_plan *plan, int64_t k, int &kt, int6
   nkt = (k + kt - 1) / kt;
 }
 
-// Workspace of a solve: the row buffer, then the flags of both sweeps
-// ([2][nch][B][nkt]) and the give-up word.
+// Workspace of a solve: the row buffer; the flags and the arrival counters
+// of both sweeps ([4][nch][B][nkt]: forward flags, backward flags, forward
+// counters, backward counters) and the give-up word; the partial-sum slots of
+// the split chunks' parts ([nsplit][B][nkt][kST] values).
 struct SolveWs {
-  size_t rows, flags, total;
+  size_t rows, words, slots, total;
+  int64_t per;  // B nkt
 };
 
 inline SolveWs solve_ws(const selinv_junction_plan *plan, int64_t B, int64_t k) {
-  if (B <= 0 || k <= 0) return SolveWs{0, 0, 0};
+  if (B <= 0 || k <= 0) return SolveWs{0, 0, 0, 0, 0};
   int kt;
   int64_t nkt;
   rhs_tiles(plan, k, kt, nkt);
   SolveWs o;
+  o.per = B * nkt;
   o.rows = align_up(size_t(B) * plan->rows_ptr[plan->nch] * plan->b * size_t(k) *
                     plan->dtype_bytes);
-  o.flags = 2 * size_t(plan->nch) * size_t(B) * size_t(nkt);
-  o.total = o.rows + align_up((o.flags + 1) * sizeof(int32_t));
+  o.words = 4 * size_t(plan->nch) * size_t(o.per);
+  o.slots = size_t(plan->nsplit) * size_t(o.per) * kST;
+  o.total = o.rows + align_up((o.words + 1) * sizeof(int32_t)) +
+            align_up(o.slots * plan->dtype_bytes);
   return o;
 }
 
@@ -374,8 +449,11 @@ hipError_t apply_run(const selinv_junction_plan *plan, int64_t B, const T *facto
   int64_t nkt;
   rhs_tiles(plan, k, kt, nkt);
   if (nkt > 65535) return hipErrorInvalidValue;
+  // Split chunks pay a handshake between their parts, which only the longer
+  // sums of several right-hand sides per tile repay.
+  const bool split = kt >= kSplitMinCols;
   const SDims d{plan->n,  plan->npanel, plan->nrinv, plan->rows_ptr[plan->nch], k, kt, b,
-                plan->nch, B,           nkt};
+                plan->nch, B,           nkt,         plan->nparts, split};
   const T *W = factor, *RJ = factor + B * plan->npanel * int64_t(b) * b;
   const size_t lds = sizeof(T) * (size_t(sbm) * sbm + 2 * kST) + sizeof(int32_t) * kIdx;
   const auto &lo = plan->level_off;
@@ -384,26 +462,32 @@ hipError_t apply_run(const selinv_junction_plan *plan, int64_t B, const T *facto
     for (int32_t l = plan->levels - 1; l >= 0; --l)
       js_backward<T, BC, false><<<dim3(static_cast<unsigned>(lo[l + 1] - lo[l]), By, Z),
                                   dim3(kST), lds, s>>>(plan->dev, d, lo[l], W, RJ, in, out,
-                                                       nullptr, nullptr, 0);
+                                                       nullptr, nullptr, nullptr, nullptr, 0);
     return hipGetLastError();
   }
-  const int64_t grid = plan->nch * B * nkt;
-  if (grid > INT32_MAX) return hipErrorInvalidValue;
-  // a matrix's row buffer and vector are read through 32-bit buffer offsets
-  const int64_t span = std::max(d.nrows, d.n) * b * k * int64_t(sizeof(T));
-  if (span >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const SolveWs o = solve_ws(plan, B, k);
-  T *U = static_cast<T *>(ws);
-  int32_t *flags = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + o.rows);
-  int32_t *fflags = flags, *bflags = flags + o.flags / 2, *timeout = flags + o.flags;
-  hipError_t e = df::launch_init(static_cast<int64_t>(o.flags), flags, nullptr, timeout, s);
+  const int64_t grid = (split ? plan->nparts : plan->nch) * o.per;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  // a matrix's row buffer and vector, and the slots, are read through 32-bit
+  // buffer offsets
+  const int64_t span = std::max(d.nrows, d.n) * b * k * int64_t(sizeof(T));
+  if (span >= (int64_t(1) << 31) || o.slots * sizeof(T) >= (size_t(1) << 31))
+    return hipErrorInvalidValue;
+  char *base = static_cast<char *>(ws);
+  T *U = reinterpret_cast<T *>(base);
+  int32_t *words = reinterpret_cast<int32_t *>(base + o.rows);
+  const size_t nw = size_t(plan->nch) * size_t(o.per);
+  int32_t *fflags = words, *bflags = words + nw, *fcnt = words + 2 * nw, *bcnt = words + 3 * nw;
+  int32_t *timeout = words + o.words;
+  T *slots = reinterpret_cast<T *>(base + o.rows + align_up((o.words + 1) * sizeof(int32_t)));
+  hipError_t e = df::launch_init(static_cast<int64_t>(o.words), words, nullptr, timeout, s);
   if (e != hipSuccess) return e;
   const uint64_t wt = wait_limit_ticks();
   const unsigned G = static_cast<unsigned>(grid);
   js_forward<T, BC, true><<<dim3(G), dim3(kST), lds, s>>>(plan->dev, d, 0, W, RJ, in, out, U,
-                                                          fflags, timeout, wt);
+                                                          fflags, fcnt, slots, timeout, wt);
   js_backward<T, BC, true><<<dim3(G), dim3(kST), lds, s>>>(plan->dev, d, 0, W, RJ, out, out,
-                                                           bflags, timeout, wt);
+                                                           bflags, bcnt, slots, timeout, wt);
   return hipGetLastError();
 }
 
