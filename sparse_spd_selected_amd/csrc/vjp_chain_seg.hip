@@ -27,6 +27,14 @@
 //          the Dbar map's R per segment
 //   scan:  one workgroup per chain, Dbar at every segment end (from P_{L-1})
 //   out:   Dbar_i and lower_bar_i = G_{i+1,i+1} Z_i - 2 Dbar_{i+1} X_i, descending
+// Decay.  Phi and Pi_i are products of the X's from the segment start; on a
+// diagonally dominant chain they shrink geometrically (2^-3.6 per block on
+// the b = 32 workload), as the forward's fill block does.  Once every entry
+// of Phi (prep) or Pi_i (mid) is at most 2^-100 (both start as I), it is set
+// to zero and no longer updated: what is lost is Pi_d^T R' Pi_d (R' the map of
+// the rest of the segment) in R, and the corresponding Phi_d GG_a Phi_d^T
+// term in the GG map, 2^-200 relative to terms of the same shape.  A product
+// that does not decay is never dropped.
 #include <algorithm>
 #include <climits>
 
@@ -216,6 +224,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     S = f32t::sub(sl.get_sym(tA), f32t::mm(GLa, T2, f32t::zero<T>()));
   }
   Blk<T> Ph = identity32<T>(g, j), Cm = f32t::zero<T>();
+  bool decayed = false;  // Phi dropped
   for (int64_t i = r.a0; i < r.a1; ++i) {
     if (i > r.a0 || s == 0) f32t::gj_inverse(S, col, g, j, pl);  // S <- Sinv_i
     f16::wave_sync();
@@ -240,7 +249,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     const Blk<T> GLtn = f32t::neg(io.blk_t());                   // -O(gl_i^T)
     io.stage(nGd);
     const Blk<T> c = io.symmetrize(f32t::mm(GLtn, XT, io.blk()));
-    Ph = f32t::mm(XT, Ph, f32t::zero<T>());                      // Phi <- X_i Phi
+    if (!decayed) {
+      Ph = f32t::mm(XT, Ph, f32t::zero<T>());                    // Phi <- X_i Phi
+      if (f32t::all_below(Ph, T(0x1p-100))) {
+        decayed = true;
+        Ph = f32t::zero<T>();
+      }
+    }
     const Blk<T> W = f32t::mm(Cm, XT, f32t::zero<T>());          // Cm X^T
     Cm = f32t::mm(XT, W, c);                                     // X Cm X^T + c
   }
@@ -268,6 +283,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   const T *gdm = gd + m * L * kBB32, *glm = gl + m * (L - 1) * kBB32, *GDm = Gd + m * L * kBB32;
   io.stage(gg_start + (m * P + s) * kBB32, true);
   Blk<T> GG = io.blk(), Pi = identity32<T>(g, j), R = f32t::zero<T>();
+  bool decayed = false;  // Pi dropped
   for (int64_t i = rg.a0; i < rg.a1; ++i) {
     // the step's input blocks, loaded together (the last block has only Sinv)
     const bool more = i < L - 1;
@@ -303,9 +319,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     const Blk<T> Vn = f32t::neg(f32t::mm(io.blk_t(), Z, f32t::zero<T>()));  // -G Z
     const Blk<T> rr = io.symmetrize(f32t::mm(Xo, Vn, Pf));
     // R += Pi^T r Pi, Pi <- X_i Pi
-    const Blk<T> A2 = f32t::mm(rr, Pi, f32t::zero<T>());         // r Pi
-    R = f32t::mm(Pi, A2, R);
-    Pi = f32t::mm(XT, Pi, f32t::zero<T>());
+    if (!decayed) {
+      const Blk<T> A2 = f32t::mm(rr, Pi, f32t::zero<T>());       // r Pi
+      R = f32t::mm(Pi, A2, R);
+      Pi = f32t::mm(XT, Pi, f32t::zero<T>());
+      decayed = f32t::all_below(Pi, T(0x1p-100));
+    }
   }
   io.store(rmap + (m * P + s) * kBB32, R, true);
 }

@@ -132,6 +132,34 @@ def test_chain_vjp_workload_b32_long(ssa):
         del Od, Ol
 
 
+def test_chain_vjp_slow_decay_maps_kept(ssa):
+    """D_i = (2 + 0.01) M, C_i = -M (M SPD, b = 32), 2 chains of 2048 blocks
+    (16 segments of 128 blocks): the products of the X's shrink only by
+    about 0.905 per block, so the segment maps are carried to every
+    segment's end (on the workload they are dropped after about 28 blocks);
+    every chain matches the oracle."""
+    rng = np.random.default_rng(22)
+    B, L, b = 2, 2048, 32
+    d = np.empty((B, L, b, b))
+    l = np.empty((B, L - 1, b, b))
+    for m in range(B):
+        M = pins.random_spd(b, rng, load=1.0)
+        d[m] = 2.01 * M
+        l[m] = -M
+    gd = spdgen.cotangent(d.shape, seed=22, k=0)
+    gl = spdgen.cotangent(l.shape, seed=22, k=1)
+    lb = spdgen.cotangent((B,), seed=22, k=2)
+    db, lbar, info = ssa.chain_vjp(_to(d, torch.float64), _to(l, torch.float64),
+                                   _to(gd, torch.float64), _to(gl, torch.float64),
+                                   torch.from_numpy(lb).to(DEV), return_info=True)
+    torch.cuda.synchronize()
+    assert int(info.abs().sum()) == 0
+    Od, Ol, st = oracle.chain_vjp(d, l, gd, gl, lb)
+    assert (st == 0).all()
+    e = max(_cmp("diag_bar", db, Od, torch.float64), _cmp("lower_bar", lbar, Ol, torch.float64))
+    say("  worst rel err %.2e" % e)
+
+
 def test_chain_vjp_segments_not_pd(ssa):
     d, l, gd, gl, lb = chain_case(2, 600, 32, seed=4)
     d[1, 300] = -np.eye(32)
