@@ -266,47 +266,72 @@ __device__ inline void gather_lds(T *dst, int tot, F src) {
   }
 }
 
+// Cholesky step sequence of chol_inverse for n <= NM on one wavefront (lane i
+// holds row i of the matrix padded to NM x NM with the identity, so that the
+// code is straight-line with static register indices; padded pivots are 1 and
+// leave the rest unchanged).  Column j is broadcast through LDS with
+// wavefront-scope ordering only.  On return row i of S (LDS, n x n) holds, for
+// l <= i, entry (i, l) as it was at pivot step l.  Returns 0 or 1 + the first
+// column whose pivot is not > 0 (the same in every lane); the steps after a
+// failure run on, their results unused.
+template <int NM, typename T>
+__device__ __forceinline__ int chol_wave(T *S, int n) {
+  __shared__ T colbuf[64];
+  const int t = threadIdx.x;
+  T r[NM];
+#pragma unroll
+  for (int l = 0; l < NM; ++l)
+    r[l] = (t < n && l < n) ? (l <= t ? S[t * n + l] : T(0)) : (l == t ? T(1) : T(0));
+  int fail = 0;
+#pragma unroll
+  for (int j = 0; j < NM; ++j) {
+    colbuf[t] = r[j];  // column j (lanes below j hold S_ij; the rest is unused)
+    f16::wave_sync();
+    const T dj = colbuf[j];
+    if (fail == 0 && !(dj > T(0))) fail = j + 1;
+    const T sj = r[j] * f16::rcp<T>(dj);
+#pragma unroll
+    for (int l = j + 1; l < NM; ++l) r[l] -= sj * colbuf[l];
+    f16::wave_sync();
+  }
+#pragma unroll
+  for (int l = 0; l < NM; ++l)
+    if (t < n && l < n && l <= t) S[t * n + l] = r[l];
+  return fail;
+}
+
 // S (LDS, n x n with n = s b; lower triangle read) = R R^T: R overwrites
 // the lower triangle of S, and X (LDS) receives R^-1 (lower, zero above);
 // tmp is LDS scratch of n b entries.  Returns 0, or 1 + the first column
 // whose pivot is not > 0 (NaN included), uniformly; *logdet = ln det S.
-// Cholesky: right-looking on unscaled columns, one barrier per column
-// (S_il -= S_ij S_lj / d_j for j < l <= i), scaled at the end.  Inverse:
+// Cholesky: right-looking on unscaled columns (S_il -= S_ij S_lj / d_j for
+// j < l <= i), scaled at the end.  For n <= 48 (always the case for chunks)
+// one wavefront runs it (chol_wave); larger n: one barrier per column.
+// Inverse:
 // block forward substitution with b x b blocks -- the diagonal blocks'
 // inverses, then one block diagonal of R^-1 at a time,
 // X_ik = -X_ii sum_{k <= q < i} R_iq X_qk.
 template <typename T>
-__device__ inline int chol_inverse(T *S, T *X, T *tmp, int n, int b, double *logdet) {
+__device__ __forceinline__ int chol_inverse(T *S, T *X, T *tmp, int n, int b, double *logdet) {
   const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
   if (n <= 48) {
-    // the trailing matrix in registers (n^2 <= 9 kJT entries, entry t + kJT u
-    // per thread); step j reads column j from LDS and writes back column
-    // j + 1, so LDS ends with every column as it was at its pivot step
-    constexpr int kU = 48 * 48 / kJT;
-    T r[kU];
-    int ri[kU], rl[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int e = t + kJT * u;
-      ri[u] = e < n * n ? e / n : -1;
-      rl[u] = e < n * n ? e - ri[u] * n : 0;
-      r[u] = e < n * n ? S[e] : T(0);
-    }
-    for (int j = 0; j < n; ++j) {
-      __syncthreads();
-      const T dj = S[j * n + j];
-      if (!(dj > T(0))) return j + 1;
-      const T inv = T(1) / dj;
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int i = ri[u], l = rl[u];
-        if (l > j && i >= l) {
-          r[u] -= S[i * n + j] * inv * S[l * n + j];
-          if (l == j + 1) S[i * n + l] = r[u];
-        }
-      }
+    __shared__ int fail_s;
+    if (t < 64) {  // the first wavefront; lane i holds row i
+      int fail;
+      if (n <= 8)
+        fail = chol_wave<8>(S, n);
+      else if (n <= 16)
+        fail = chol_wave<16>(S, n);
+      else if (n <= 24)
+        fail = chol_wave<24>(S, n);
+      else if (n <= 32)
+        fail = chol_wave<32>(S, n);
+      else
+        fail = chol_wave<48>(S, n);
+      if (t == 0) fail_s = fail;
     }
     __syncthreads();
+    if (fail_s) return fail_s;
   } else {
     for (int j = 0; j < n; ++j) {
       const T dj = S[j * n + j];
