@@ -343,6 +343,8 @@ __global__ __launch_bounds__(64) void chain16_solve_narrow(int L, int64_t k,
 // (upper-lower) Cholesky, columns 15 down to 0: u_jj = sqrt(a_jj),
 // u_rj = a_rj / u_jj (r < j), then a_rl -= u_rj u_lj for r, l < j.  Column j
 // is broadcast through LDS.  Dot products use the same strided column sets.
+// Any k: workgroup (m, grp) takes columns 4 grp .. 4 grp + 3 of chain m
+// (grid B ceil(k / 4)); every group forms its chain's U_i itself.
 template <typename T>
 __global__ __launch_bounds__(64) void chain16_sample_narrow(int L, int64_t k,
                                                            const T *__restrict__ lower,
@@ -356,13 +358,14 @@ __global__ __launch_bounds__(64) void chain16_sample_narrow(int L, int64_t k,
   __shared__ __align__(16) T sP[kPB];
   __shared__ __align__(16) T sC[256];
   const int lane = threadIdx.x, r = lane & 15, q = lane >> 4;
-  const int64_t m = blockIdx.x;
-  const int kc = static_cast<int>(k);
+  const int64_t ngrp = (k + kNarrow - 1) / kNarrow;
+  const int64_t m = blockIdx.x / ngrp, k0 = (blockIdx.x - m * ngrp) * kNarrow;
+  const int kc = static_cast<int>(k - k0 < kNarrow ? k - k0 : kNarrow);
   const T *F = factor + m * L * kPB;
   const T *C = L > 1 ? lower + m * (L - 1) * 256 : nullptr;  // none for one block
   const int lc = L > 1 ? L - 2 : 0;
-  auto vrow = [&](const T *base, int i) { return base + ((m * L + i) * 16 + r) * k; };
-  auto vrow_w = [&](T *base, int i) { return base + ((m * L + i) * 16 + r) * k; };
+  auto vrow = [&](const T *base, int i) { return base + ((m * L + i) * 16 + r) * k + k0; };
+  auto vrow_w = [&](T *base, int i) { return base + ((m * L + i) * 16 + r) * k + k0; };
   auto coupling = [&](int i) -> const T * {
     return C ? C + int64_t(min(max(i, 0), lc)) * 256 : nullptr;
   };
@@ -456,7 +459,9 @@ template <typename T>
 hipError_t chain16_sample_launch(int64_t B, int64_t L, int64_t k, const T *lower,
                                  const T *factor, const T *z, T *x, hipStream_t s) {
   if (B == 0 || k == 0) return hipSuccess;
-  hipLaunchKernelGGL(chain16_sample_narrow<T>, dim3(static_cast<unsigned>(B)), dim3(64), 0, s,
+  const int64_t groups = B * ((k + kNarrow - 1) / kNarrow);
+  if (groups > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(chain16_sample_narrow<T>, dim3(static_cast<unsigned>(groups)), dim3(64), 0, s,
                      static_cast<int>(L), k, lower, factor, z, x);
   return hipGetLastError();
 }

@@ -463,8 +463,7 @@ hipError_t chain_apply_launch(int64_t B, int64_t L, int32_t b, int64_t k, bool s
                               hipStream_t s) {
   if (B == 0 || k == 0) return hipSuccess;
   if (!sample && b == 16) return chain16_solve_launch<T>(B, L, k, lower, factor, in, out, s);
-  if (sample && b == 16 && k <= 4)
-    return chain16_sample_launch<T>(B, L, k, lower, factor, in, out, s);
+  if (sample && b == 16) return chain16_sample_launch<T>(B, L, k, lower, factor, in, out, s);
   const int nch = nchunks(k);
   const dim3 grid(static_cast<unsigned>(B * nch));
   const size_t shm = apply_smem(b) * sizeof(T);
