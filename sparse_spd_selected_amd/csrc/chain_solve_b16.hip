@@ -210,6 +210,9 @@ __global__ __launch_bounds__(64) void chain16_solve(int L, int64_t k, int nch,
 // the row's result.  That reads 4 (not 16) entries of each matrix row and of
 // each vector column from LDS per product.
 constexpr int kNarrow = 4;
+// the solve runs column groups up to this k (measured: two groups beat the
+// chunked kernel, four lose to it), the chunked kernel beyond
+constexpr int64_t kGroupedMax = 8;
 
 template <typename T>
 __device__ __forceinline__ T row_sum(T v) {
@@ -229,13 +232,15 @@ __global__ __launch_bounds__(64) void chain16_solve_narrow(int L, int64_t k,
   __shared__ __align__(16) T sP[kPB];
   __shared__ __align__(16) T sC[256];
   const int lane = threadIdx.x, r = lane & 15, q = lane >> 4;
-  const int64_t m = blockIdx.x;
-  const int kc = static_cast<int>(k);
+  // workgroup (m, grp) takes columns 4 grp .. 4 grp + 3 of chain m
+  const int64_t ngrp = (k + kNarrow - 1) / kNarrow;
+  const int64_t m = blockIdx.x / ngrp, k0 = (blockIdx.x - m * ngrp) * kNarrow;
+  const int kc = static_cast<int>(k - k0 < kNarrow ? k - k0 : kNarrow);
   const T *F = factor + m * L * kPB;
   const T *C = L > 1 ? lower + m * (L - 1) * 256 : nullptr;  // none for one block
   const int lc = L > 1 ? L - 2 : 0;
-  auto vrow = [&](const T *base, int i) { return base + ((m * L + i) * 16 + r) * k; };
-  auto vrow_w = [&](T *base, int i) { return base + ((m * L + i) * 16 + r) * k; };
+  auto vrow = [&](const T *base, int i) { return base + ((m * L + i) * 16 + r) * k + k0; };
+  auto vrow_w = [&](T *base, int i) { return base + ((m * L + i) * 16 + r) * k + k0; };
   auto coupling = [&](int i) -> const T * {
     return C ? C + int64_t(min(max(i, 0), lc)) * 256 : nullptr;
   };
@@ -477,9 +482,10 @@ template <typename T>
 hipError_t chain16_solve_launch(int64_t B, int64_t L, int64_t k, const T *lower, const T *factor,
                                 const T *y, T *x, hipStream_t s) {
   if (B == 0 || k == 0) return hipSuccess;
-  if (k <= kNarrow) {
-    hipLaunchKernelGGL(chain16_solve_narrow<T>, dim3(static_cast<unsigned>(B)), dim3(64), 0, s,
-                       static_cast<int>(L), k, lower, factor, y, x);
+  if (k <= kGroupedMax) {  // groups of four columns on the one-wavefront kernel
+    const int64_t groups = B * ((k + kNarrow - 1) / kNarrow);
+    hipLaunchKernelGGL(chain16_solve_narrow<T>, dim3(static_cast<unsigned>(groups)), dim3(64), 0,
+                       s, static_cast<int>(L), k, lower, factor, y, x);
     return hipGetLastError();
   }
   const int nch = static_cast<int>((k + kCols - 1) / kCols);
