@@ -37,6 +37,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -625,21 +626,28 @@ def peak_probe():
 def compact(workload, dtname, steps, warmup):
     """Event-timed forward calls of another workload: median and min call
     time, nominal GFLOP/s, block-rows/s and the HBM roofline fraction on
-    compulsory bytes (median call)."""
+    compulsory bytes (median call), with the number of calls sized by time
+    (the call count is reported)."""
     import spdgen
     import torch
     cfg = dict(spdgen.WORKLOADS[workload])
     kind = cfg.pop("kind")
     cfg.pop("dtypes")
     w = 8 if dtname == "f64" else 4
-    res = run_gpu(kind, cfg, dtname, max(steps, 20), max(warmup, 3))
+    # Short calls are timed in steady state: a probe estimates the call time,
+    # then at least ~20 ms of warm-up and ~50 ms of timed calls (at most 500).
+    probe = run_gpu(kind, cfg, dtname, 3, 1)
+    t_ms = max(min(probe["ev_ms"]), 1e-3)
+    warm = max(warmup, 3, int(math.ceil(20.0 / t_ms)))
+    n = max(steps, 20, min(500, int(math.ceil(50.0 / t_ms))))
+    res = run_gpu(kind, cfg, dtname, n, min(warm, 500))
     torch.cuda.empty_cache()
     ev = sorted(res["ev_ms"])
     med = ev[len(ev) // 2]
     F = nominal_flops(kind, cfg)
     nbytes = compulsory_bytes(kind, cfg, w)
     peak_t = FP64_PEAK_TFLOPS if dtname == "f64" else FP32_PEAK_TFLOPS
-    return {"ms_median": round(med, 4), "ms_min": round(ev[0], 4),
+    return {"ms_median": round(med, 4), "ms_min": round(ev[0], 4), "calls": n,
             "gflops": round(F / (med * 1e-3) / 1e9, 3),
             "block_rows_per_s": round(block_rows(kind, cfg) / (med * 1e-3), 1),
             "hbm_frac": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
