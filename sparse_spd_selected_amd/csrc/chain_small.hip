@@ -265,24 +265,29 @@ __global__ __launch_bounds__(64) void chain_dense32_kernel(
   const T *D = diag + m * L * bb;
   const T *C = lower + m * (L - 1) * bb;
   // A(R, c): D_k (lower triangle mirrored) on the diagonal blocks, C_k below
-  // them, C_k^T above, the identity past n; 16 independent loads per lane
+  // them, C_k^T above, the identity past n. Every lane issues its 16 loads
+  // unconditionally (an entry outside the band reads D_0 and discards it), so
+  // they are all in flight together instead of one per branch.
   T v[16];
+  bool use[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int e = lane + 64 * u, R = e >> 5, c = e & 31;
     const int kr = R / b, kc = c / b, r = R - kr * b, cc = c - kc * b;
-    T x = R == c ? T(1) : T(0);
-    if (R < n && c < n) {
-      if (kr == kc)
-        x = r >= cc ? D[kr * bb + r * b + cc] : D[kr * bb + cc * b + r];
-      else if (kr == kc + 1)
-        x = C[kc * bb + r * b + cc];
-      else if (kc == kr + 1)
-        x = C[kr * bb + cc * b + r];
-      else
-        x = T(0);
-    }
-    v[u] = x;
+    const bool in = R < n && c < n;
+    const bool dg = in && kr == kc, lo = in && kr == kc + 1, up = in && kc == kr + 1;
+    const int off = dg ? kr * bb + (r >= cc ? r * b + cc : cc * b + r)
+                  : lo ? kc * bb + r * b + cc
+                  : up ? kr * bb + cc * b + r : 0;
+    const T *src = (lo || up) ? C : D;
+    v[u] = src[off];
+    use[u] = dg || lo || up;
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int e = lane + 64 * u, R = e >> 5, c = e & 31;
+    const T id = (R == c && !(R < n)) ? T(1) : T(0);
+    v[u] = use[u] ? v[u] : id;
   }
 #pragma unroll
   for (int u = 0; u < 16; ++u) Al[lane + 64 * u] = v[u];
