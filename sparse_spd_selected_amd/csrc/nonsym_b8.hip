@@ -172,10 +172,7 @@ __global__ __launch_bounds__(64) void nstree8_distribute(
   const r8::Row<T> Si = valid ? r8::load8(st_sinv + p * 64, i) : r8::zero<T>();
   const r8::Row<T> U = valid ? r8::load(up + v * bb, b, i) : r8::zero<T>();
   const r8::Row<T> Dn = valid ? r8::load(down + v * bb, b, i) : r8::zero<T>();
-  if (valid && i == 0) df::wait_flags(flags, q, q + 1, 2, 0, 1, timeout, deadline);
-  df::acquire();
-  const bool failed = *first_fail != INT_MAX || df::timed_out(timeout);
-  const r8::Row<T> G = valid ? df::load_interleaved(st_m + q * 64, i) : r8::zero<T>();
+  // the products that do not involve the parent are formed before the wait
   sa.put(s, i, Si);
   sb.put(s, i, Dn);
   f16::wave_sync();
@@ -183,6 +180,10 @@ __global__ __launch_bounds__(64) void nstree8_distribute(
   const r8::Row<T> Bm = r8::mul(Si, sb, s, r8::zero<T>());  // Sinv_v down_v
   f16::wave_sync();
   sa.put(s, i, A);
+  if (valid && i == 0) df::wait_flags(flags, q, q + 1, 2, 0, 1, timeout, deadline);
+  df::acquire();
+  const bool failed = *first_fail != INT_MAX || df::timed_out(timeout);
+  const r8::Row<T> G = valid ? df::load_interleaved(st_m + q * 64, i) : r8::zero<T>();
   sb.put(s, i, G);
   f16::wave_sync();
   const r8::Row<T> V = r8::mul(G, sa, s, r8::zero<T>());    // G_pp A = -G_{p,v}

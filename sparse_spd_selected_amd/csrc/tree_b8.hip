@@ -153,15 +153,15 @@ __global__ __launch_bounds__(64) void tree8_distribute(
   }
   const r8::Row<T> Si = valid ? r8::load8(st_sinv + p * 64, i) : r8::zero<T>();
   const r8::Row<T> E = valid ? r8::load(edge + v * bb, b, i) : r8::zero<T>();
-  if (valid && i == 0) df::wait_flags(flags, pp, pp + 1, 2, 0, 1, timeout, deadline);
-  df::acquire();
-  const bool failed = *first_fail != INT_MAX || df::timed_out(timeout);
-  const r8::Row<T> G = valid ? df::load_transposed(G_diag + u * bb, b, i) : r8::zero<T>();
+  // X_v does not depend on the parent: formed before the wait
   sa.put(s, i, Si);
   f16::wave_sync();
   const r8::Row<T> X = r8::mul(E, sa, s, r8::zero<T>());  // E_v Sinv_v
   sb.put(s, i, X);
-  f16::wave_sync();
+  if (valid && i == 0) df::wait_flags(flags, pp, pp + 1, 2, 0, 1, timeout, deadline);
+  df::acquire();
+  const bool failed = *first_fail != INT_MAX || df::timed_out(timeout);
+  const r8::Row<T> G = valid ? df::load_transposed(G_diag + u * bb, b, i) : r8::zero<T>();
   const r8::Row<T> V = r8::mul(G, sb, s, r8::zero<T>());  // G_pp X_v
   f16::wave_sync();
   sa.put(s, i, V);

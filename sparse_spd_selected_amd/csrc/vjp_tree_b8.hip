@@ -224,13 +224,12 @@ __global__ __launch_bounds__(64) void tree8_vjp_distribute(
   const r8::Row<T> Z = r8::load8(arr(kZ) + pp * 64, i);
   const r8::Row<T> P = r8::load8(arr(kP) + pp * 64, i);
   const r8::Row<T> Si = r8::load8(arr(kSinv) + pp * 64, i);
+  sa.put(s, i, X);  // staged before the wait (the acquire orders them)
+  sb.put(s, i, Z);
   if (valid && i == 0) df::wait_flags(flags, q, q + 1, 2, 0, 1, timeout, deadline);
   df::acquire();
   const r8::Row<T> G = df::load_interleaved(arr(kM) + q * 64, i);  // G of the parent
   const r8::Row<T> Db = df::load_transposed(d_bar + u * bb, b, i);
-  sa.put(s, i, X);
-  sb.put(s, i, Z);
-  f16::wave_sync();
   const r8::Row<T> T2 = r8::mul(Db, sa, s, r8::zero<T>());  // Dbar_u X
   const r8::Row<T> V = r8::mul(G, sa, s, r8::zero<T>());    // G_uu X
   const r8::Row<T> Q = axpby(T(1), r8::mul(G, sb, s, r8::zero<T>()), T(-1), T2);

@@ -329,6 +329,15 @@ def test_tree_small(ssa, topo, n, b, dt):
 
 
 @pytest.mark.parametrize("dt", ["f64", "f32"])
+@pytest.mark.parametrize("n,b", [(16383, 8), (32767, 5)])
+def test_tree_wide_and_narrow_levels(ssa, n, b, dt):
+    """Balanced binary trees whose deepest levels (8192 and 16384 nodes) are
+    handed over by flags and whose upper levels by ready words: both kinds of
+    handshake, and the change between them, in one call."""
+    run_tree(ssa, spdgen.balanced_tree(n, 2), b, DT[dt], seed=n)
+
+
+@pytest.mark.parametrize("dt", ["f64", "f32"])
 def test_tree_workload_b8_random(ssa, dt):
     """Random recursive tree of 262144 nodes (seed 1), b = 8, full oracle."""
     run_tree(ssa, spdgen.random_recursive_tree(262144, 1), 8, DT[dt], seed=1)
