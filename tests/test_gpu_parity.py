@@ -331,9 +331,9 @@ def test_tree_small(ssa, topo, n, b, dt):
 @pytest.mark.parametrize("dt", ["f64", "f32"])
 @pytest.mark.parametrize("n,b", [(16383, 8), (32767, 5)])
 def test_tree_wide_and_narrow_levels(ssa, n, b, dt):
-    """Balanced binary trees whose deepest levels (8192 and 16384 nodes) are
-    handed over by flags and whose upper levels by ready words: both kinds of
-    handshake, and the change between them, in one call."""
+    """Balanced binary trees (levels of 1 up to 8192 and 16384 nodes): every
+    parent has two children, so every handshake of the single-launch schedule
+    has two producers, from one-tile levels to levels of thousands of tiles."""
     run_tree(ssa, spdgen.balanced_tree(n, 2), b, DT[dt], seed=n)
 
 
