@@ -42,9 +42,9 @@ using df::store_coherent;
 // kFactor: the collect pass of the shared factor: the packed lower triangle
 // of Sinv_v (wg-style layout, packed_entries(b) per position) goes to
 // st_sinv, which may be null (log det only); G_diag, G_edge are unused.
-template <typename T, bool kFactor>
+template <typename T, bool kFactor, bool kFull>
 __global__ __launch_bounds__(64) void tree8_collect(
-    int32_t tiles, int b, const int32_t *__restrict__ tile_lo, const int32_t *__restrict__ tile_hi,
+    int32_t tiles, int b_arg, const int32_t *__restrict__ tile_lo, const int32_t *__restrict__ tile_hi,
     const int32_t *__restrict__ node_at, const int32_t *__restrict__ child_beg,
     const int32_t *__restrict__ child_end, const int32_t *__restrict__ fail_rank,
     const T *__restrict__ diag, const T *__restrict__ edge, T *__restrict__ st_sinv,
@@ -56,6 +56,7 @@ __global__ __launch_bounds__(64) void tree8_collect(
   const int lane = threadIdx.x;
   const int s = lane >> 3, i = lane & 7;
   const r8::Stage<T> sa{lds[0]}, sb{lds[1]};
+  const int b = kFull ? 8 : b_arg;  // compiled for b = 8 on its own
   const int32_t t = tiles - 1 - static_cast<int32_t>(blockIdx.x);
   const int64_t p = tile_lo[t] + s;
   const bool valid = p < tile_hi[t];
@@ -127,9 +128,9 @@ __global__ __launch_bounds__(64) void tree8_collect(
 // Distribute of one tile; grid = tiles - 1, workgroup w takes tile w + 1
 // (root level first; the root's tile is finished by the collect).  Waits for
 // flags[parent] == 2, reads the parent's G_diag block, sets flags[p] = 2.
-template <typename T>
+template <typename T, bool kFull>
 __global__ __launch_bounds__(64) void tree8_distribute(
-    int b, const int32_t *__restrict__ tile_lo, const int32_t *__restrict__ tile_hi,
+    int b_arg, const int32_t *__restrict__ tile_lo, const int32_t *__restrict__ tile_hi,
     const int32_t *__restrict__ node_at, const int32_t *__restrict__ parent_pos,
     const int32_t *__restrict__ parent_node, const T *__restrict__ edge,
     const T *__restrict__ st_sinv, const int32_t *__restrict__ first_fail,
@@ -140,6 +141,7 @@ __global__ __launch_bounds__(64) void tree8_distribute(
   const int lane = threadIdx.x;
   const int s = lane >> 3, i = lane & 7;
   const r8::Stage<T> sa{lds[0]}, sb{lds[1]};
+  const int b = kFull ? 8 : b_arg;  // compiled for b = 8 on its own
   const int32_t t = static_cast<int32_t>(blockIdx.x) + 1;
   const int64_t p = tile_lo[t] + s;
   const bool valid = p < tile_hi[t];
@@ -401,13 +403,15 @@ hipError_t tree8_launch(const selinv_tree_plan *plan, const T *diag, const T *ed
   const uint64_t wt = wait_limit_ticks();
   hipError_t e = df::launch_init(n, flags, first_fail, timeout, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((tree8_collect<T, false>), dim3(tiles), dim3(64), 0, s, tiles, b, d.tile_lo,
-                     d.tile_hi, d.node_at, d.child_beg, d.child_end, d.fail_rank, diag, edge,
-                     st_sinv, st_m, st_ld, st_fail, first_fail, G_diag, G_edge, flags, timeout, wt);
+  auto collect = b == 8 ? tree8_collect<T, false, true> : tree8_collect<T, false, false>;
+  auto distribute = b == 8 ? tree8_distribute<T, true> : tree8_distribute<T, false>;
+  hipLaunchKernelGGL(collect, dim3(tiles), dim3(64), 0, s, tiles, b, d.tile_lo, d.tile_hi,
+                     d.node_at, d.child_beg, d.child_end, d.fail_rank, diag, edge, st_sinv, st_m,
+                     st_ld, st_fail, first_fail, G_diag, G_edge, flags, timeout, wt);
   if (tiles > 1)
-    hipLaunchKernelGGL(tree8_distribute<T>, dim3(tiles - 1), dim3(64), 0, s, b, d.tile_lo,
-                       d.tile_hi, d.node_at, d.parent_pos, d.parent_node, edge, st_sinv,
-                       first_fail, G_diag, G_edge, flags, timeout, wt);
+    hipLaunchKernelGGL(distribute, dim3(tiles - 1), dim3(64), 0, s, b, d.tile_lo, d.tile_hi,
+                       d.node_at, d.parent_pos, d.parent_node, edge, st_sinv, first_fail, G_diag,
+                       G_edge, flags, timeout, wt);
   const int64_t chunk = (n + kFinishGroups - 1) / kFinishGroups;
   hipLaunchKernelGGL(tree8_ld_partial, dim3(kFinishGroups), dim3(1024), 0, s, n, chunk, st_ld,
                      partial);
@@ -441,7 +445,8 @@ hipError_t tree8_factor_launch(const selinv_tree_plan *plan, const T *diag, cons
   const int32_t tiles = static_cast<int32_t>(plan->tiles);
   hipError_t e = df::launch_init(n, flags, first_fail, timeout, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((tree8_collect<T, true>), dim3(tiles), dim3(64), 0, s, tiles, b, d.tile_lo,
+  auto collect = b == 8 ? tree8_collect<T, true, true> : tree8_collect<T, true, false>;
+  hipLaunchKernelGGL(collect, dim3(tiles), dim3(64), 0, s, tiles, b, d.tile_lo,
                      d.tile_hi, d.node_at, d.child_beg, d.child_end, d.fail_rank, diag, edge,
                      factor, st_m, st_ld, st_fail, first_fail, nullptr, nullptr, flags, timeout,
                      wait_limit_ticks());
