@@ -402,8 +402,11 @@ SELINV_API int selinv_star_sample_f32(int64_t B, int64_t K, int32_t b, const flo
                            void *stream);
 
 /* tree: vectors [n][b][k] by node index.  For b <= 8 the solve runs both
- * sweeps as single launches with bounded waits (see selinv_tree_f64); a solve
- * whose wait gives up returns NaN in x. */
+ * sweeps, and the sampler its one parents-first sweep, as single launches with
+ * bounded waits (see selinv_tree_f64); a call whose wait gives up returns NaN
+ * in x.  Solve and sample take a workspace of selinv_tree_solve_workspace_bytes
+ * (plan, k) bytes (device, caller-owned, 256-byte aligned, contents need not
+ * be initialised; none is needed for the sampler when b > 8: pass NULL, 0). */
 SELINV_API size_t selinv_tree_factor_bytes(const selinv_tree_plan *plan);
 SELINV_API size_t selinv_tree_factor_workspace_bytes(const selinv_tree_plan *plan);
 SELINV_API size_t selinv_tree_solve_workspace_bytes(const selinv_tree_plan *plan, int64_t k);
@@ -421,10 +424,10 @@ SELINV_API int selinv_tree_solve_f32(const selinv_tree_plan *plan, const float *
                           void *workspace, size_t workspace_bytes, void *stream);
 SELINV_API int selinv_tree_sample_f64(const selinv_tree_plan *plan, const double *edge,
                            const double *factor, int64_t k, const double *z, double *x,
-                           void *stream);
+                           void *workspace, size_t workspace_bytes, void *stream);
 SELINV_API int selinv_tree_sample_f32(const selinv_tree_plan *plan, const float *edge,
                            const float *factor, int64_t k, const float *z, float *x,
-                           void *stream);
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------ non-symmetric ladder
  * (gabp-sparse-inv 0.3.2, "Implemented and tested kernels", items

@@ -152,7 +152,7 @@ def lib():
             "star_sample": [i64, i64, i32, vp, vp, i64, vp, vp, vp, vp, vp],
             "tree_factor": [vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "tree_solve": [vp, vp, vp, i64, vp, vp, vp, sz, vp],
-            "tree_sample": [vp, vp, vp, i64, vp, vp, vp]}
+            "tree_sample": [vp, vp, vp, i64, vp, vp, vp, sz, vp]}
     for name, args in sigs.items():
         for sfx in ("f64", "f32"):
             f = getattr(L, "selinv_%s_%s" % (name, sfx))
@@ -929,16 +929,11 @@ class TreeFactor:
         x = torch.empty_like(v)
         sfx = _sfx(self.factor)
         with torch.cuda.device(dev):
-            if sample:
-                rc = getattr(lib(), "selinv_tree_sample_" + sfx)(
-                    self.plan.handle, _ptr(self.edge), _ptr(self.factor), k, _ptr(v), _ptr(x),
-                    _stream(dev))
-            else:
-                nb = int(lib().selinv_tree_solve_workspace_bytes(self.plan.handle, k))
-                ws = _workspace(nb, dev)
-                rc = getattr(lib(), "selinv_tree_solve_" + sfx)(
-                    self.plan.handle, _ptr(self.edge), _ptr(self.factor), k, _ptr(v), _ptr(x),
-                    _ptr(ws), nb, _stream(dev))
+            nb = int(lib().selinv_tree_solve_workspace_bytes(self.plan.handle, k))
+            ws = _workspace(nb, dev)
+            rc = getattr(lib(), "selinv_tree_%s_%s" % ("sample" if sample else "solve", sfx))(
+                self.plan.handle, _ptr(self.edge), _ptr(self.factor), k, _ptr(v), _ptr(x),
+                _ptr(ws), nb, _stream(dev))
         _status(rc, "selinv_tree_%s_%s" % ("sample" if sample else "solve", sfx))
         return x
 

@@ -276,7 +276,8 @@ int tree_apply_entry(const selinv_tree_plan *plan, const T *edge, const T *facto
   if (k == 0) return SELINV_OK;
   if (!edge || !factor || !in || !out) return SELINV_ERR_INVALID_ARG;
   if (misaligned(edge) || misaligned(factor)) return SELINV_ERR_INVALID_ARG;
-  const size_t need = sample ? 0 : selinv::tree_apply_workspace_bytes(plan, k);
+  // the b > 8 sampler runs per-level launches and needs no workspace
+  const size_t need = (sample && plan->b > 8) ? 0 : selinv::tree_apply_workspace_bytes(plan, k);
   if (ws_bytes < need || (need && !ws) || (need && misaligned_ws(ws)))
     return SELINV_ERR_INVALID_ARG;
   const hipError_t e = selinv::tree_apply_launch<T>(plan, k, sample, edge, factor, in, out, ws,
@@ -741,8 +742,10 @@ int selinv_tree_solve_f64(const selinv_tree_plan *plan, const double *edge, cons
 }
 
 int selinv_tree_sample_f64(const selinv_tree_plan *plan, const double *edge, const double *factor,
-                           int64_t k, const double *z, double *x, void *stream) {
-  return tree_apply_entry<double>(plan, edge, factor, k, z, x, nullptr, 0, true, stream);
+                           int64_t k, const double *z, double *x, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  return tree_apply_entry<double>(plan, edge, factor, k, z, x, workspace, workspace_bytes, true,
+                              stream);
 }
 
 int selinv_chain_factor_f32(int64_t B, int64_t L, int32_t b, const float *diag,
@@ -797,8 +800,10 @@ int selinv_tree_solve_f32(const selinv_tree_plan *plan, const float *edge, const
 }
 
 int selinv_tree_sample_f32(const selinv_tree_plan *plan, const float *edge, const float *factor,
-                           int64_t k, const float *z, float *x, void *stream) {
-  return tree_apply_entry<float>(plan, edge, factor, k, z, x, nullptr, 0, true, stream);
+                           int64_t k, const float *z, float *x, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  return tree_apply_entry<float>(plan, edge, factor, k, z, x, workspace, workspace_bytes, true,
+                              stream);
 }
 
 size_t selinv_bidiag_workspace_bytes(int64_t B) {

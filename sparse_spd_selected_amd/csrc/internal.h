@@ -286,11 +286,15 @@ template <typename T>
 hipError_t star32_apply_launch(int64_t B, int64_t K, int64_t k, bool sample, const T *coupling,
                                const T *factor, const T *in_center, const T *in_leaves,
                                T *x_center, T *x_leaves, void *ws, hipStream_t s);
-// b <= 8 solve on the single-launch schedule (tree_b8.hip)
+// b <= 8 solve and sampling on the single-launch schedule (tree_b8.hip);
+// both take the workspace of tree8_solve_workspace_bytes
 size_t tree8_solve_workspace_bytes(const selinv_tree_plan *plan, int64_t k);
 template <typename T>
 hipError_t tree8_solve_launch(const selinv_tree_plan *plan, int64_t k, const T *edge,
                               const T *factor, const T *y, T *x, void *ws, hipStream_t s);
+template <typename T>
+hipError_t tree8_sample_launch(const selinv_tree_plan *plan, int64_t k, const T *edge,
+                               const T *factor, const T *z, T *x, void *ws, hipStream_t s);
 template <typename T>
 hipError_t tree_apply_launch(const selinv_tree_plan *plan, int64_t k, bool sample, const T *edge,
                              const T *factor, const T *in, T *out, void *ws, hipStream_t s);

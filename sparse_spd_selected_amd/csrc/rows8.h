@@ -204,5 +204,31 @@ __device__ __forceinline__ bool gj_inverse(Row<T> &a, const Stage<T> &st, int s,
   return bad;
 }
 
+// U with U U^T = A and a positive diagonal, U upper triangular, for the
+// symmetric positive definite b x b block A of each slot (row i per lane;
+// rows and columns from b on are left zero): the Cholesky factorisation in
+// reversed index order, k = b-1 .. 0, each step taking u_kk = sqrt(a_kk),
+// u_ik = a_ik / u_kk (i < k) and a_ij -= u_ik u_jk (i, j < k).  Row k is
+// broadcast through `st`.  For A = S^-1 with S = R R^T, U = R^-T.
+template <typename T>
+__device__ __forceinline__ Row<T> rev_cholesky(Row<T> a, const Stage<T> &st, int s, int i, int b) {
+  Row<T> u = zero<T>();
+#pragma unroll
+  for (int k = 7; k >= 0; --k) {
+    if (k < b) {
+      if (i == k) st.put(s, k, a);
+      f16::wave_sync();
+      const Row<T> rk = st.row(s, k);
+      f16::wave_sync();
+      const T d = __builtin_sqrt(rk.v[k]);
+      const T uk = i == k ? d : (i < k ? a.v[k] / d : T(0));  // u_ik
+      u.v[k] = uk;
+#pragma unroll
+      for (int j = 0; j < k; ++j) a.v[j] -= uk * (rk.v[j] / d);  // u_jk = a_kj / d
+    }
+  }
+  return u;
+}
+
 }  // namespace r8
 }  // namespace selinv

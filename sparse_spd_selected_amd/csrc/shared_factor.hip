@@ -597,6 +597,7 @@ hipError_t tree_apply_launch(const selinv_tree_plan *plan, int64_t k, bool sampl
                              const T *factor, const T *in, T *out, void *ws, hipStream_t s) {
   if (k == 0) return hipSuccess;
   if (!sample && plan->b <= 8) return tree8_solve_launch<T>(plan, k, edge, factor, in, out, ws, s);
+  if (sample && plan->b <= 8) return tree8_sample_launch<T>(plan, k, edge, factor, in, out, ws, s);
   const int b = plan->b;
   const int nch = nchunks(k);
   const int nt = sf_threads(b);

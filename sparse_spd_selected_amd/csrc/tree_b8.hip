@@ -286,13 +286,16 @@ __global__ __launch_bounds__(64) void tree8_solve_fwd(
   df::publish(fl, p, valid && i == 0, 1);
 }
 
-template <typename T>
+// kSample: x = L^-T D^-1/2 z instead, w_v = U_v z_v (U_v U_v^T = Sinv_v, U_v
+// upper triangular) formed from z before the wait; no forward pass.
+template <typename T, bool kSample>
 __global__ __launch_bounds__(64) void tree8_solve_bwd(
     int nch, int64_t n, int64_t k, int kw, const int32_t *__restrict__ tile_lo,
     const int32_t *__restrict__ tile_hi, int b, const int32_t *__restrict__ node_at,
     const int32_t *__restrict__ parent_pos, const int32_t *__restrict__ parent_node,
-    const T *__restrict__ edge, const T *__restrict__ factor, T *__restrict__ x,
-    int32_t *__restrict__ flags, int32_t *__restrict__ timeout, uint64_t wait_ticks) {
+    const T *__restrict__ edge, const T *__restrict__ factor, const T *__restrict__ z,
+    T *__restrict__ x, int32_t *__restrict__ flags, int32_t *__restrict__ timeout,
+    uint64_t wait_ticks) {
   __shared__ __align__(32) T lds[2][kSlots * 64];
   const uint64_t deadline = df::deadline_after(wait_ticks);
   const int lane = threadIdx.x;
@@ -313,13 +316,23 @@ __global__ __launch_bounds__(64) void tree8_solve_bwd(
     q = parent_pos[p];
   }
   const r8::Row<T> Si = valid ? packed_row(factor + p * pk, b, i) : r8::zero<T>();
-  const r8::Row<T> W = valid ? load_cols<T, false>(x, v, b, k, c0, kc, i) : r8::zero<T>();
+  r8::Row<T> W;
+  if constexpr (kSample) {  // w_v = U_v z_v
+    const r8::Row<T> Zr = valid ? load_cols<T, false>(z, v, b, k, c0, kc, i) : r8::zero<T>();
+    const r8::Row<T> U = r8::rev_cholesky(Si, sa, s, i, b);
+    sb.put(s, i, Zr);
+    f16::wave_sync();
+    W = r8::mul(U, sb, s, r8::zero<T>());
+    f16::wave_sync();
+  } else {
+    W = valid ? load_cols<T, false>(x, v, b, k, c0, kc, i) : r8::zero<T>();
+  }
   const r8::Row<T> E = has_parent ? r8::load(edge + v * bb, b, i) : r8::zero<T>();
+  sa.put(s, i, E);  // staged before the wait (the acquire orders it)
   int32_t *fl = flags + chunk * n;
   if (has_parent && i == 0) df::wait_flags(fl, q, q + 1, 2, 0, 1, timeout, deadline);
   df::acquire();
   const r8::Row<T> Xp = has_parent ? load_cols<T, true>(x, u, b, k, c0, kc, i) : r8::zero<T>();
-  sa.put(s, i, E);
   sb.put(s, i, Xp);
   f16::wave_sync();
   const r8::Row<T> Tt = r8::mul_tn(sa, sb, s, i, r8::zero<T>());  // E_v^T x_parent
@@ -487,11 +500,44 @@ hipError_t tree8_solve_launch(const selinv_tree_plan *plan, int64_t k, const T *
   hipLaunchKernelGGL(tree8_solve_fwd<T>, dim3(grid), dim3(64), 0, s, tiles, nch, n, k, kw,
                      d.tile_lo, d.tile_hi, b, d.node_at, d.child_beg, d.child_end, edge, factor,
                      y, x, msg, flags, timeout, wt);
-  hipLaunchKernelGGL(tree8_solve_bwd<T>, dim3(grid), dim3(64), 0, s, nch, n, k, kw, d.tile_lo,
-                     d.tile_hi, b, d.node_at, d.parent_pos, d.parent_node, edge, factor, x, flags,
-                     timeout, wt);
+  hipLaunchKernelGGL((tree8_solve_bwd<T, false>), dim3(grid), dim3(64), 0, s, nch, n, k, kw,
+                     d.tile_lo, d.tile_hi, b, d.node_at, d.parent_pos, d.parent_node, edge, factor,
+                     static_cast<const T *>(nullptr), x, flags, timeout, wt);
   return hipGetLastError();
 }
+
+// Sampling on the same single-launch parents-first schedule (no forward
+// pass); the workspace is the solve's.
+template <typename T>
+hipError_t tree8_sample_launch(const selinv_tree_plan *plan, int64_t k, const T *edge,
+                               const T *factor, const T *z, T *x, void *ws, hipStream_t s) {
+  if (k <= 0) return hipSuccess;
+  if (!ws) return hipErrorInvalidValue;  // the flags live in the workspace
+  const int64_t n = plan->n;
+  const int b = plan->b;
+  const int nch = static_cast<int>((k + kSolveCols - 1) / kSolveCols);
+  const int kw = static_cast<int>(std::min<int64_t>(k, kSolveCols));
+  Carve cv(ws);
+  (void)cv.take<T>(int64_t(nch) * n * 8 * kw);  // the solve's messages: unused
+  int32_t *flags = cv.take<int32_t>(int64_t(nch) * n);
+  int32_t *timeout = cv.take<int32_t>(1);
+  const TreePlanDev &d = plan->dev;
+  const int32_t tiles = static_cast<int32_t>(plan->tiles);
+  hipError_t e = df::launch_init(int64_t(nch) * n, flags, nullptr, timeout, s);
+  if (e != hipSuccess) return e;
+  const unsigned grid = static_cast<unsigned>(int64_t(tiles) * nch);
+  hipLaunchKernelGGL((tree8_solve_bwd<T, true>), dim3(grid), dim3(64), 0, s, nch, n, k, kw,
+                     d.tile_lo, d.tile_hi, b, d.node_at, d.parent_pos, d.parent_node, edge, factor,
+                     z, x, flags, timeout, wait_limit_ticks());
+  return hipGetLastError();
+}
+
+template hipError_t tree8_sample_launch<float>(const selinv_tree_plan *, int64_t, const float *,
+                                               const float *, const float *, float *, void *,
+                                               hipStream_t);
+template hipError_t tree8_sample_launch<double>(const selinv_tree_plan *, int64_t,
+                                                const double *, const double *, const double *,
+                                                double *, void *, hipStream_t);
 
 template hipError_t tree8_solve_launch<float>(const selinv_tree_plan *, int64_t, const float *,
                                               const float *, const float *, float *, void *,

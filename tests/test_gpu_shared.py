@@ -266,6 +266,27 @@ def test_tree_solve_wait_limit_gives_nan(ssa):
     _cmp_vec("solve", x[None], Ox[None], torch.float64)
 
 
+def test_tree_sample_wait_limit_gives_nan(ssa):
+    """The sampler runs on the same single-launch parents-first schedule:
+    with a zero wait bound on a path tree it gives up and leaves NaN in x;
+    with the bound restored the same draw matches the oracle."""
+    p = spdgen.path_tree(2000)
+    d, e = spdgen.tree(p, 4, seed=8)
+    z = spdgen.cotangent((2000, 4, 3), seed=8, k=1)
+    f = ssa.tree_factor(p, _to(d, torch.float64), _to(e, torch.float64))
+    old = ssa.wait_limit()
+    try:
+        ssa.set_wait_limit(0)
+        x = f.sample(z=_to(z, torch.float64))
+        torch.cuda.synchronize()
+    finally:
+        ssa.set_wait_limit(old)
+    assert torch.isnan(x).any()
+    x = f.sample(z=_to(z, torch.float64))
+    Ox = oracle.tree_apply(p, d, e, z, "sample")
+    _cmp_vec("sample", x[None], Ox[None], torch.float64)
+
+
 def test_tree_factor_not_pd(ssa):
     p = spdgen.random_recursive_tree(40, 1)
     d, e = spdgen.tree(p, 3)
