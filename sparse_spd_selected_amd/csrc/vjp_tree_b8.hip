@@ -76,9 +76,11 @@ __device__ __forceinline__ r8::Row<T> sym_rows(const r8::Row<T> &r, const r8::St
 }
 
 // Collect of one tile; workgroup w takes tile tiles - 1 - w (deepest level
-// first); flags[p] becomes 1 (2 for the root).
+// first); flags[p] becomes 1 (2 for the root).  The messages M, N are formed
+// and published first; P and Z, read only by the distribute launch, after the
+// flag.  Two wavefronts per SIMD (f64: 256 VGPRs, a few spilled) beat one.
 template <typename T>
-__global__ __launch_bounds__(64) void tree8_vjp_collect(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void tree8_vjp_collect(
     int32_t tiles, const int32_t *__restrict__ tile_lo, const int32_t *__restrict__ tile_hi,
     int b, const int32_t *__restrict__ node_at,
     const int32_t *__restrict__ child_beg, const int32_t *__restrict__ child_end,
@@ -141,19 +143,11 @@ __global__ __launch_bounds__(64) void tree8_vjp_collect(
     df::store_coherent(st_fail + p, (bad || child_failed) ? int32_t(1) : int32_t(0));
     if (bad && !child_failed) atomicMin(first_fail, fail_rank[p]);
   }
-  // P = sym(lb Sinv - Sinv (GG Sinv))
+  // messages to the parent first (they are on the chain of every level)
   f16::wave_sync();
   sa.put(s, i, S);
   f16::wave_sync();
-  const r8::Row<T> U = r8::mul(GG, sa, s, r8::zero<T>());  // row i of GG Sinv
-  f16::wave_sync();
-  sb.put(s, i, U);
-  f16::wave_sync();
-  const r8::Row<T> P =
-      sym_rows(axpby(lb, S, T(-1), r8::mul(S, sb, s, r8::zero<T>())), sb, s, i);
-  // messages to the parent; sa still holds Sinv
   const r8::Row<T> X = r8::mul(E, sa, s, r8::zero<T>());  // E Sinv
-  f16::wave_sync();
   sb.put(s, i, E);
   f16::wave_sync();
   const r8::Row<T> M = r8::mul_t(X, sb, s, r8::zero<T>());  // X E^T
@@ -162,11 +156,10 @@ __global__ __launch_bounds__(64) void tree8_vjp_collect(
   f16::wave_sync();
   const r8::Row<T> W = r8::mul(X, sb, s, r8::zero<T>());  // X GG
   const r8::Row<T> Y1 = axpby(T(1), W, T(-1), Ge);
-  const r8::Row<T> Z = r8::mul(axpby(T(1), W, T(1), Y1), sa, s, r8::zero<T>());  // (2W - Ge) Sinv
   f16::wave_sync();
   sb.put(s, i, X);
   f16::wave_sync();
-  const r8::Row<T> N = sym_rows(r8::mul_t(Y1, sb, s, r8::zero<T>()), sa, s, i);  // sym(Y1 X^T)
+  const r8::Row<T> N = sym_rows(r8::mul_t(Y1, sb, s, r8::zero<T>()), sb, s, i);  // sym(Y1 X^T)
   // what the parent reads in this launch goes before the flag (which waits
   // for every store issued so far), what only later launches read after it
   if (valid && p != 0) {
@@ -174,6 +167,15 @@ __global__ __launch_bounds__(64) void tree8_vjp_collect(
     df::store_interleaved(arr(kN) + p * 64, i, N);
   }
   df::publish(flags, p, valid && i == 0, p == 0 ? 2 : 1);
+  // for the distribute (sa still holds Sinv): Z = (2 W - Ge) Sinv and
+  // P = sym(lb Sinv - Sinv (GG Sinv))
+  const r8::Row<T> Z = r8::mul(axpby(T(1), W, T(1), Y1), sa, s, r8::zero<T>());
+  const r8::Row<T> U = r8::mul(GG, sa, s, r8::zero<T>());  // row i of GG Sinv
+  f16::wave_sync();
+  sb.put(s, i, U);
+  f16::wave_sync();
+  const r8::Row<T> P =
+      sym_rows(axpby(lb, S, T(-1), r8::mul(S, sb, s, r8::zero<T>())), sb, s, i);
   if (valid) {
     r8::store8(arr(kSinv) + p * 64, i, S);
     r8::store8(arr(kP) + p * 64, i, P);
