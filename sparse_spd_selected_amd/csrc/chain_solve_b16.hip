@@ -350,16 +350,79 @@ __global__ __launch_bounds__(64) void chain16_solve_narrow(int L, int64_t k,
 // is broadcast through LDS.  Dot products use the same strided column sets.
 // Any k: workgroup (m, grp) takes columns 4 grp .. 4 grp + 3 of chain m
 // (grid B ceil(k / 4)); every group forms its chain's U_i itself.
+// Sampling, x = L^-T D^-1/2 z with D^-1/2_i = U_i (U_i U_i^T = Sinv_i, U_i
+// upper triangular), in two launches.  First w_i = U_i z_i for every block at
+// once (one wavefront per block: U_i by the reversed Cholesky of Sinv_i,
+// columns 15 down to 0, each broadcast through LDS, then the columns of z_i
+// in groups of four), written to x; then the sequential backward sweep
+// x_i = w_i - Sinv_i C_i^T x_{i+1}, which reads w_i from x and overwrites it.
 template <typename T>
-__global__ __launch_bounds__(64) void chain16_sample_narrow(int L, int64_t k,
-                                                           const T *__restrict__ lower,
-                                                           const T *__restrict__ factor,
-                                                           const T *__restrict__ z,
-                                                           T *__restrict__ x) {
+__global__ __launch_bounds__(64) void chain16_sample_w(int64_t k, const T *__restrict__ factor,
+                                                       const T *__restrict__ z,
+                                                       T *__restrict__ x) {
   __shared__ __align__(16) T bufA[16 * kNarrow];
+  __shared__ __align__(16) T colj[16];
+  __shared__ __align__(16) T sP[kPB];
+  const int lane = threadIdx.x, r = lane & 15, q = lane >> 4;
+  const int64_t blk = blockIdx.x;
+  const T *P = factor + blk * kPB;
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+    if (lane + 64 * t < kPB) sP[lane + 64 * t] = P[lane + 64 * t];
+  f16::wave_sync();
+  T u[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int c = q + 4 * t;
+    u[t] = sP[c <= r ? r * (r + 1) / 2 + c : c * (c + 1) / 2 + r];
+  }
+  // reversed Cholesky of Sinv_i into u (entries (r, q + 4t) of U_i): column
+  // j = sqrt(a_jj) on the diagonal, a_rj / u_jj above it; one reciprocal per
+  // column
+#pragma unroll
+  for (int j = 15; j >= 0; --j) {
+    const int tj = j >> 2;
+    if ((j & 3) == q) colj[r] = u[tj];  // column j, current values
+    f16::wave_sync();
+    const T ujj = sqrt(colj[j]);
+    const T inv = f16::rcp<T>(ujj);
+    const T urj = colj[r] * inv;
+    const T f = urj * inv;  // u_rj / u_jj: a_cj u_rj / u_jj = u_rj u_cj
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = q + 4 * t;
+      if (c < j && r < j) u[t] -= f * colj[c];
+    }
+    if ((j & 3) == q) u[tj] = r < j ? urj : (r == j ? ujj : T(0));
+    f16::wave_sync();
+  }
+  // w = U_i z_i, columns in groups of four: this lane's quarter of row r,
+  // summed over the row's lanes
+  const int64_t row = (blk * 16 + r) * k;
+  for (int64_t k0 = 0; k0 < k; k0 += kNarrow) {
+    const int kc = static_cast<int>(k - k0 < kNarrow ? k - k0 : kNarrow);
+    if (q == 0)
+#pragma unroll
+      for (int c = 0; c < kNarrow; ++c) bufA[r * kNarrow + c] = c < kc ? z[row + k0 + c] : T(0);
+    f16::wave_sync();
+#pragma unroll
+    for (int c = 0; c < kNarrow; ++c) {
+      T acc = T(0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc += u[t] * bufA[(q + 4 * t) * kNarrow + c];
+      acc = row_sum(acc);
+      if (q == 0 && c < kc) x[row + k0 + c] = acc;
+    }
+    f16::wave_sync();
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void chain16_sample_bwd(int L, int64_t k,
+                                                         const T *__restrict__ lower,
+                                                         const T *__restrict__ factor, T *x) {
   __shared__ __align__(16) T bufB[16 * kNarrow];
   __shared__ __align__(16) T bufC[16 * kNarrow];
-  __shared__ __align__(16) T colj[16];
   __shared__ __align__(16) T sP[kPB];
   __shared__ __align__(16) T sC[256];
   const int lane = threadIdx.x, r = lane & 15, q = lane >> 4;
@@ -369,8 +432,7 @@ __global__ __launch_bounds__(64) void chain16_sample_narrow(int L, int64_t k,
   const T *F = factor + m * L * kPB;
   const T *C = L > 1 ? lower + m * (L - 1) * 256 : nullptr;  // none for one block
   const int lc = L > 1 ? L - 2 : 0;
-  auto vrow = [&](const T *base, int i) { return base + ((m * L + i) * 16 + r) * k + k0; };
-  auto vrow_w = [&](T *base, int i) { return base + ((m * L + i) * 16 + r) * k + k0; };
+  auto vrow = [&](int i) { return x + ((m * L + i) * 16 + r) * k + k0; };
   auto coupling = [&](int i) -> const T * {
     return C ? C + int64_t(min(max(i, 0), lc)) * 256 : nullptr;
   };
@@ -393,57 +455,29 @@ __global__ __launch_bounds__(64) void chain16_sample_narrow(int L, int64_t k,
 #pragma unroll
     for (int c = 0; c < kNarrow; ++c) o[c] = c < kc ? row[c] : T(0);
   };
-  auto store_row = [&](T *row, const T (&v)[kNarrow]) {
-    if (q == 0)
-#pragma unroll
-      for (int c = 0; c < kNarrow; ++c)
-        if (c < kc) row[c] = v[c];
-  };
 
   Raw<T> nx;
   load_raw(nx, F + int64_t(L - 1) * kPB, coupling(L - 1), lane);
-  T zn[kNarrow];
-  load_row(zn, vrow(z, L - 1));
+  T wn[kNarrow];
+  load_row(wn, vrow(L - 1));
   for (int i = L - 1; i >= 0; --i) {
     put_raw(sP, sC, nx, lane);
-    T zi[kNarrow];
+    T w[kNarrow];
 #pragma unroll
-    for (int c = 0; c < kNarrow; ++c) zi[c] = zn[c];
-    if (i > 0) {
+    for (int c = 0; c < kNarrow; ++c) w[c] = wn[c];
+    if (i > 0) {  // the next step's blocks and w (row i - 1, not written yet)
       load_raw(nx, F + int64_t(i - 1) * kPB, coupling(i - 1), lane);
-      load_row(zn, vrow(z, i - 1));
+      load_row(wn, vrow(i - 1));
     }
-    put_row(bufA, zi);
     f16::wave_sync();
-    T si[4], u[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int c = q + 4 * t;
-      si[t] = sP[c <= r ? r * (r + 1) / 2 + c : c * (c + 1) / 2 + r];
-      u[t] = si[t];
-    }
-    // reversed Cholesky of Sinv_i into u (entries (r, q + 4t) of U_i)
-#pragma unroll
-    for (int j = 15; j >= 0; --j) {
-      const int tj = j >> 2;
-      if ((j & 3) == q) colj[r] = u[tj];  // column j, current values
-      f16::wave_sync();
-      const T ujj = sqrt(colj[j]);
-      const T urj = colj[r] / ujj;
+    if (i < L - 1) {  // x_i = w_i - Sinv_i C_i^T x_{i+1}, x_{i+1} in bufB
+      T si[4], cc[4], t2[kNarrow];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int c = q + 4 * t;
-        if (c < j && r < j) u[t] -= urj * (colj[c] / ujj);
+        si[t] = sP[c <= r ? r * (r + 1) / 2 + c : c * (c + 1) / 2 + r];
+        cc[t] = sC[c * 16 + r];
       }
-      if ((j & 3) == q) u[tj] = r < j ? urj : (r == j ? ujj : T(0));
-      f16::wave_sync();
-    }
-    T w[kNarrow];
-    dot(w, u, bufA);  // U_i z_i
-    if (i < L - 1) {  // x_i = w_i - Sinv_i C_i^T x_{i+1}, x_{i+1} in bufB
-      T cc[4], t2[kNarrow];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) cc[t] = sC[(q + 4 * t) * 16 + r];
       dot(t2, cc, bufB);
       put_row(bufC, t2);
       f16::wave_sync();
@@ -452,7 +486,10 @@ __global__ __launch_bounds__(64) void chain16_sample_narrow(int L, int64_t k,
 #pragma unroll
       for (int c = 0; c < kNarrow; ++c) w[c] -= v[c];
     }
-    store_row(vrow_w(x, i), w);
+    if (q == 0)
+#pragma unroll
+      for (int c = 0; c < kNarrow; ++c)
+        if (c < kc) vrow(i)[c] = w[c];
     put_row(bufB, w);
     f16::wave_sync();
   }
@@ -466,8 +503,11 @@ hipError_t chain16_sample_launch(int64_t B, int64_t L, int64_t k, const T *lower
   if (B == 0 || k == 0) return hipSuccess;
   const int64_t groups = B * ((k + kNarrow - 1) / kNarrow);
   if (groups > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(chain16_sample_narrow<T>, dim3(static_cast<unsigned>(groups)), dim3(64), 0, s,
-                     static_cast<int>(L), k, lower, factor, z, x);
+  if (B * L > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(chain16_sample_w<T>, dim3(static_cast<unsigned>(B * L)), dim3(64), 0, s, k,
+                     factor, z, x);
+  hipLaunchKernelGGL(chain16_sample_bwd<T>, dim3(static_cast<unsigned>(groups)), dim3(64), 0, s,
+                     static_cast<int>(L), k, lower, factor, x);
   return hipGetLastError();
 }
 

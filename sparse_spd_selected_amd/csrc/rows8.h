@@ -221,10 +221,12 @@ __device__ __forceinline__ Row<T> rev_cholesky(Row<T> a, const Stage<T> &st, int
       const Row<T> rk = st.row(s, k);
       f16::wave_sync();
       const T d = __builtin_sqrt(rk.v[k]);
-      const T uk = i == k ? d : (i < k ? a.v[k] / d : T(0));  // u_ik
+      const T inv = f16::rcp<T>(d);
+      const T uk = i == k ? d : (i < k ? a.v[k] * inv : T(0));  // u_ik
       u.v[k] = uk;
+      const T f = uk * inv;
 #pragma unroll
-      for (int j = 0; j < k; ++j) a.v[j] -= uk * (rk.v[j] / d);  // u_jk = a_kj / d
+      for (int j = 0; j < k; ++j) a.v[j] -= f * rk.v[j];  // u_ik u_jk, u_jk = a_kj / d
     }
   }
   return u;
