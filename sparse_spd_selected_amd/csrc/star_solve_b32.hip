@@ -77,11 +77,13 @@ struct Lane {
       if ((j & 1) == h) colj[r] = u[tj];
       f16::wave_sync();
       const T ujj = sqrt(colj[j]);
-      const T urj = colj[r] / ujj;
+      const T inv = f16::rcp<T>(ujj);  // one reciprocal per column
+      const T urj = colj[r] * inv;
+      const T f = urj * inv;  // a_cj u_rj / u_jj = u_rj u_cj
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         const int c = h + 2 * t;
-        if (c < j && r < j) u[t] -= urj * (colj[c] / ujj);
+        if (c < j && r < j) u[t] -= f * colj[c];
       }
       if ((j & 1) == h) u[tj] = r < j ? urj : (r == j ? ujj : T(0));
       f16::wave_sync();
