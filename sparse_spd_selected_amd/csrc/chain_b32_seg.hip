@@ -92,9 +92,11 @@ __device__ __forceinline__ Blk<T> load_image(const T *P, int lane) {
 // seg32_plain continues with the plain sweep to the separator.  The plain
 // sweep holds no fill state, so it fits in half the registers and runs two
 // wavefronts per SIMD, which hides much of its dependent latency; the fill
-// phase is short (about 28 blocks per segment on the b = 32 workload).
+// phase is short (about 28 blocks per segment on the b = 32 workload).  The
+// fill kernel is held to two wavefronts per SIMD (a few registers spill), so
+// that 2048 segments run in one round rather than two.
 template <typename T>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void seg32_fill(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void seg32_fill(
     int L, int P, const T *__restrict__ diag, const T *__restrict__ lower,
     T *__restrict__ st_sinv, T *__restrict__ st_f, T *__restrict__ r_F, T *__restrict__ r_U,
     T *__restrict__ st_hand, double *__restrict__ seg_ld, int32_t *__restrict__ seg_fail,

@@ -287,9 +287,12 @@ __global__ __launch_bounds__(64) void tree8_solve_fwd(
 }
 
 // kSample: x = L^-T D^-1/2 z instead, w_v = U_v z_v (U_v U_v^T = Sinv_v, U_v
-// upper triangular) formed from z before the wait; no forward pass.
+// upper triangular) formed from z before the wait; no forward pass.  Held to
+// two wavefronts per SIMD: the f64 sampler would otherwise take one (its
+// unrolled reversed Cholesky needs ~300 registers; two with some spilled are
+// faster).
 template <typename T, bool kSample>
-__global__ __launch_bounds__(64) void tree8_solve_bwd(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void tree8_solve_bwd(
     int nch, int64_t n, int64_t k, int kw, const int32_t *__restrict__ tile_lo,
     const int32_t *__restrict__ tile_hi, int b, const int32_t *__restrict__ node_at,
     const int32_t *__restrict__ parent_pos, const int32_t *__restrict__ parent_node,
