@@ -377,15 +377,15 @@ __global__ __launch_bounds__(64) void chain16_sample_w(int64_t k, const T *__res
     u[t] = sP[c <= r ? r * (r + 1) / 2 + c : c * (c + 1) / 2 + r];
   }
   // reversed Cholesky of Sinv_i into u (entries (r, q + 4t) of U_i): column
-  // j = sqrt(a_jj) on the diagonal, a_rj / u_jj above it; one reciprocal per
-  // column
+  // j = sqrt(a_jj) on the diagonal, a_rj / u_jj above it; one reciprocal
+  // square root per column
 #pragma unroll
   for (int j = 15; j >= 0; --j) {
     const int tj = j >> 2;
     if ((j & 3) == q) colj[r] = u[tj];  // column j, current values
     f16::wave_sync();
-    const T ujj = sqrt(colj[j]);
-    const T inv = f16::rcp<T>(ujj);
+    const T inv = f16::rsqrt<T>(colj[j]);  // 1 / u_jj
+    const T ujj = colj[j] * inv;
     const T urj = colj[r] * inv;
     const T f = urj * inv;  // u_rj / u_jj: a_cj u_rj / u_jj = u_rj u_cj
 #pragma unroll

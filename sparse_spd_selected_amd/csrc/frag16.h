@@ -196,6 +196,26 @@ __device__ __forceinline__ float rcp<float>(float d) {
   return __builtin_fmaf(x, e, x);
 }
 
+// 1/sqrt(d) for d > 0: the hardware estimate refined by Newton-Raphson steps
+// for the reciprocal square root, y <- y (3/2 - (d/2) y^2), each of which
+// doubles the correct bits (two steps for double, one for float).
+template <typename T>
+__device__ __forceinline__ T rsqrt(T d);
+
+template <>
+__device__ __forceinline__ double rsqrt<double>(double d) {
+  double y = __builtin_amdgcn_rsq(d);
+  const double h = 0.5 * d;
+  y = y * __builtin_fma(-h * y, y, 1.5);
+  return y * __builtin_fma(-h * y, y, 1.5);
+}
+
+template <>
+__device__ __forceinline__ float rsqrt<float>(float d) {
+  const float y = __builtin_amdgcn_rsqf(d);
+  return y * __builtin_fmaf(-0.5f * d * y, y, 1.5f);
+}
+
 // Running product of pivots kept as mantissa * 2^exponent.  Pivots are
 // multiplied in groups of four and renormalised once per group, so any four
 // consecutive pivots with magnitudes in [2^-255, 2^255] are safe; ln of the

@@ -76,8 +76,8 @@ struct Lane {
       const int tj = j >> 1;
       if ((j & 1) == h) colj[r] = u[tj];
       f16::wave_sync();
-      const T ujj = sqrt(colj[j]);
-      const T inv = f16::rcp<T>(ujj);  // one reciprocal per column
+      const T inv = f16::rsqrt<T>(colj[j]);  // 1 / u_jj, one per column
+      const T ujj = colj[j] * inv;
       const T urj = colj[r] * inv;
       const T f = urj * inv;  // a_cj u_rj / u_jj = u_rj u_cj
 #pragma unroll
